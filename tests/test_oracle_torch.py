@@ -1,0 +1,104 @@
+"""Cross-check of the oracle against PyTorch library routines on the CPU, fp64.
+
+PyTorch's own LayerNorm, tanh-GELU, causal scaled-dot-product attention,
+cross-entropy, autograd, clip_grad_norm_ and AdamW (the routines the pages'
+recipes call) are an independent implementation of the same definitions.
+They share no code with the oracle or the HIP path.
+"""
+
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as F
+
+from gpt2_inputs import ModelShape, init_params, micro_batches, uniform_tokens
+from oracle import gpt2 as ref
+
+
+def torch_loss(P, x, y, n_head):
+    B, T = x.shape
+    C = P["wte"].shape[1]
+    L = P["qkv_w"].shape[0]
+    h = P["wte"][x] + P["wpe"][:T]
+    for l in range(L):
+        a = F.layer_norm(h, (C,), P["ln1_w"][l], P["ln1_b"][l], eps=1e-5)
+        qkv = F.linear(a, P["qkv_w"][l], P["qkv_b"][l])
+        q, k, v = qkv.split(C, dim=-1)
+        q, k, v = (t.view(B, T, n_head, C // n_head).transpose(1, 2) for t in (q, k, v))
+        o = F.scaled_dot_product_attention(q, k, v, is_causal=True)
+        o = o.transpose(1, 2).reshape(B, T, C)
+        h = h + F.linear(o, P["proj_w"][l], P["proj_b"][l])
+        a = F.layer_norm(h, (C,), P["ln2_w"][l], P["ln2_b"][l], eps=1e-5)
+        u = F.gelu(F.linear(a, P["fc_w"][l], P["fc_b"][l]), approximate="tanh")
+        h = h + F.linear(u, P["fcproj_w"][l], P["fcproj_b"][l])
+    h = F.layer_norm(h, (C,), P["lnf_w"], P["lnf_b"], eps=1e-5)
+    z = h @ P["wte"].T
+    return F.cross_entropy(z.reshape(B * T, -1), y.reshape(-1))
+
+
+def _setup(seed=0, L=2, NH=4, C=32, T=16, V=29, B=3):
+    s = ModelShape("xcheck", L, NH, C, T, V, V)
+    p = init_params(s, seed)
+    rng = np.random.default_rng(seed + 100)
+    for n in p:  # exercise biases and LN parameters
+        if n.endswith("_b") or n.startswith("ln"):
+            p[n] = (p[n] + 0.05 * rng.standard_normal(p[n].shape)).astype(np.float32)
+    (x, y), = micro_batches(uniform_tokens(B * T + 1, V, seed + 1), 1, B, T)
+    return s, p, x, y
+
+
+def test_forward_and_gradients_match_torch_autograd():
+    s, p, x, y = _setup()
+    P = {n: torch.tensor(a, dtype=torch.float64, requires_grad=True) for n, a in p.items()}
+    lt = torch_loss(P, torch.tensor(x, dtype=torch.long), torch.tensor(y, dtype=torch.long),
+                    s.n_head)
+    lt.backward()
+    lo, go = ref.loss_and_grads(p, x, y, s.n_head)
+    assert abs(lo - lt.item()) < 1e-12
+    for n in p:
+        want = P[n].grad.numpy()
+        err = np.linalg.norm(go[n] - want) / max(np.linalg.norm(want), 1e-300)
+        assert err < 1e-10, (n, err)
+
+
+@pytest.mark.parametrize("max_norm_mode", ["clip", "noclip"])
+def test_clip_and_adamw_match_torch(max_norm_mode):
+    s, p, x, y = _setup(seed=3)
+    lo, go = ref.loss_and_grads(p, x, y, s.n_head)
+    n = ref.global_norm(go)
+    max_norm = 0.5 * n if max_norm_mode == "clip" else 2.0 * n
+    lr, wd = 1e-3, 0.1
+
+    # torch: parameters per tensor (one per block and name), groups by rank
+    tensors, names = [], []
+    for name, a in p.items():
+        if name in ref.BLOCK_NAMES:
+            for l in range(a.shape[0]):
+                tensors.append(torch.tensor(a[l], dtype=torch.float64))
+                names.append((name, l))
+        else:
+            tensors.append(torch.tensor(a, dtype=torch.float64))
+            names.append((name, None))
+    for t, (name, l) in zip(tensors, names):
+        g = go[name] if l is None else go[name][l]
+        t.grad = torch.tensor(g, dtype=torch.float64)
+    tn = torch.nn.utils.clip_grad_norm_(tensors, max_norm)
+    groups = [{"params": [t for t in tensors if t.dim() >= 2], "weight_decay": wd},
+              {"params": [t for t in tensors if t.dim() < 2], "weight_decay": 0.0}]
+    opt = torch.optim.AdamW(groups, lr=lr, betas=(0.9, 0.95), eps=1e-8, foreach=False)
+    # two optimizer steps on the same gradients exercise the moments and t = 2
+    opt.step()
+    for t in tensors:
+        t.grad = t.grad.clone()
+    opt.step()
+
+    norm, clipped, cg = ref.clip_by_global_norm(go, max_norm)
+    assert abs(norm - tn.item()) < 1e-12 * norm
+    assert clipped == (max_norm_mode == "clip")
+    zero = {k: np.zeros(a.shape) for k, a in p.items()}
+    P1, M1, V1 = ref.adamw(p, cg, zero, zero, 1, lr, 0.9, 0.95, 1e-8, wd)
+    P2, _, _ = ref.adamw(P1, cg, M1, V1, 2, lr, 0.9, 0.95, 1e-8, wd)
+    for t, (name, l) in zip(tensors, names):
+        want = t.detach().numpy()
+        got = P2[name] if l is None else P2[name][l]
+        assert np.max(np.abs(got - want)) < 1e-13, name
