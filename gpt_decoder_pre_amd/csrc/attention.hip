@@ -1,0 +1,518 @@
+// Causal multi-head attention, forward and backward.
+//
+// bf16 path (head dim 64): flash attention on v_mfma_f32_32x32x16_bf16.  A
+// workgroup owns 128 queries (four waves of 32); keys and values stream
+// through LDS in tiles of 64.  Scores are computed transposed, S^T = K Q^T,
+// so that every lane owns one query: the online-softmax statistics (running
+// max and sum, in the exp2 domain) are per-lane registers, and a row max needs
+// a single exchange with the lane 32 apart.  The probabilities are fed back
+// to the MFMA as the B operand of O^T = V^T P^T with the key order permuted
+// to match the accumulator layout (the contraction order is free), so P never
+// leaves registers; V is stored transposed in LDS for that product.
+// Backward recomputes P from the saved log-sum-exp: one kernel per key tile
+// accumulates dK and dV over query tiles, one per query tile accumulates dQ
+// over key tiles (no atomics).
+//
+// fp32 path: one wavefront per query (forward, dQ) or key (dK, dV) row with the
+// scores of the row in LDS; plain fp32 arithmetic for the exact-mode step.
+#include "common.h"
+#include "kernels.h"
+
+namespace gpt2k {
+
+constexpr int HD = 64;
+constexpr int LD = 72;  // bf16 elements per LDS row (64 + 8 padding)
+
+DEVI bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+// 8 bf16 from an LDS row: elements [o, o+4) and [o+8, o+12) -- the key order
+// that matches the accumulator rows 4*hl + {0..3} and 8 + 4*hl + {0..3}.
+DEVI bf16x8 lds_pair4(const bf16* p) {
+  const u32x2 a = *reinterpret_cast<const u32x2*>(p);
+  const u32x2 b = *reinterpret_cast<const u32x2*>(p + 8);
+  u32x4 r = {a[0], a[1], b[0], b[1]};
+  return as_bf16x8(r);
+}
+
+DEVI bf16x8 pack8(const f32x16& v, int base) {
+  bf16x8 r;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) r[e] = (bf16)v[base + e];
+  return r;
+}
+
+// Loads a 64 x 64 bf16 tile (rows r0.., row stride ld, rows >= rmax zero) into
+// LDS [64][LD] as is (natural) -- all 256 threads, two 16-byte chunks each.
+DEVI void tile_natural(const bf16* g, int64_t ld, int r0, int rmax, bf16* s, int tid) {
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int c = tid + 256 * i;
+    const int r = c >> 3, ch = (c & 7) * 8;
+    *reinterpret_cast<u32x4*>(s + r * LD + ch) =
+        ld16_or_zero(g + (int64_t)(r0 + r) * ld + ch, r0 + r < rmax);
+  }
+}
+// Same tile stored transposed, s[col][row]; 64 threads, an 8 x 8 block each.
+DEVI void tile_transposed(const bf16* g, int64_t ld, int r0, int rmax, bf16* s, int t64) {
+  const int rb = t64 >> 3, cb = t64 & 7;
+  u32x4 in[8], out[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int r = r0 + rb * 8 + j;
+    in[j] = ld16_or_zero(g + (int64_t)r * ld + cb * 8, r < rmax);
+  }
+  transpose8x8(in, out);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) *reinterpret_cast<u32x4*>(s + (cb * 8 + e) * LD + rb * 8) = out[e];
+}
+
+// ------------------------------------------------------------------ forward ----
+__global__ __launch_bounds__(256) void flash_fwd_kernel(const bf16* __restrict__ qkv, bf16* __restrict__ y,
+                                                        float* __restrict__ lse, int T, int NH, int C,
+                                                        float sl2) {
+  __shared__ __attribute__((aligned(16))) bf16 Ks[64 * LD];
+  __shared__ __attribute__((aligned(16))) bf16 Vt[64 * LD];
+  const int qt = gridDim.x - 1 - blockIdx.x;  // longest rows first
+  const int h = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, lc = lane & 31, hl = lane >> 5;
+  const int q0 = qt * 128;
+  const int myq = q0 + wave * 32 + lc;
+  const int64_t ld = 3 * (int64_t)C;
+  const bf16* Q = qkv + (int64_t)b * T * ld + h * HD;
+  const bf16* K = Q + C;
+  const bf16* V = Q + 2 * C;
+
+  bf16x8 qf[4];
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) qf[kk] = as_bf16x8(ld16_or_zero(Q + (int64_t)myq * ld + kk * 16 + hl * 8, myq < T));
+
+  f32x16 o[2];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) o[0][r] = o[1][r] = 0.f;
+  float mrow = -INFINITY, lrow = 0.f;
+  const int kv_end = min(T, q0 + 128);
+  for (int k0 = 0; k0 < kv_end; k0 += 64) {
+    __syncthreads();
+    tile_natural(K, ld, k0, T, Ks, tid);
+    if (tid < 64) tile_transposed(V, ld, k0, T, Vt, tid);
+    __syncthreads();
+
+    f32x16 s[2];
+#pragma unroll
+    for (int js = 0; js < 2; ++js) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[js][r] = 0.f;
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(Ks + (js * 32 + lc) * LD + kk * 16 + hl * 8);
+        s[js] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[kk], s[js], 0, 0, 0);
+      }
+    }
+    // s[js][r]: key k0 + 32 js + 8 (r/4) + 4 hl + r%4, query myq
+    float mx = -INFINITY;
+#pragma unroll
+    for (int js = 0; js < 2; ++js)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = k0 + js * 32 + 8 * (r >> 2) + 4 * hl + (r & 3);
+        const float v = (key <= myq && key < T) ? s[js][r] * sl2 : -INFINITY;
+        s[js][r] = v;
+        mx = fmaxf(mx, v);
+      }
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    const float mnew = fmaxf(mrow, mx);
+    const float mu = (mnew == -INFINITY) ? 0.f : mnew;
+    const float alpha = exp2_fast(mrow - mu);
+    float ls = 0.f;
+#pragma unroll
+    for (int js = 0; js < 2; ++js)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float p = exp2_fast(s[js][r] - mu);
+        s[js][r] = p;
+        ls += p;
+      }
+    lrow = lrow * alpha + ls;
+    mrow = mnew;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      o[0][r] *= alpha;
+      o[1][r] *= alpha;
+    }
+    // O^T += V^T P^T over four 16-key steps
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+      const bf16x8 pf = pack8(s[st >> 1], 8 * (st & 1));
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const bf16x8 va = lds_pair4(Vt + (i * 32 + lc) * LD + st * 16 + 4 * hl);
+        o[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pf, o[i], 0, 0, 0);
+      }
+    }
+  }
+  const float ltot = lrow + __shfl_xor(lrow, 32, 64);
+  if (myq < T) {
+    const float inv = 1.0f / ltot;
+    bf16* yr = y + ((int64_t)b * T + myq) * C + h * HD;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        float v[4] = {o[i][4 * q] * inv, o[i][4 * q + 1] * inv, o[i][4 * q + 2] * inv, o[i][4 * q + 3] * inv};
+        store4(yr + i * 32 + 8 * q + 4 * hl, v);
+      }
+    if (hl == 0) lse[((int64_t)b * NH + h) * T + myq] = (mrow + log2f(ltot)) * kLn2;
+  }
+}
+
+// D[b][h][t] = sum_d dO[b,t,h,d] O[b,t,h,d]
+__global__ void attn_rowdot_kernel(const bf16* __restrict__ y, const bf16* __restrict__ dy, float* __restrict__ D,
+                                   int B, int T, int NH, int C) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;  // over B*T*NH
+  if (i >= (int64_t)B * T * NH) return;
+  const int h = (int)(i % NH);
+  const int64_t m = i / NH;  // b*T + t
+  const bf16* a = y + m * C + h * HD;
+  const bf16* g = dy + m * C + h * HD;
+  float s = 0.f;
+#pragma unroll
+  for (int d = 0; d < HD; d += 4) {
+    float u[4], v[4];
+    load4(a + d, u);
+    load4(g + d, v);
+    s += u[0] * v[0] + u[1] * v[1] + u[2] * v[2] + u[3] * v[3];
+  }
+  const int b = (int)(m / T), t = (int)(m % T);
+  D[((int64_t)b * NH + h) * T + t] = s;
+}
+
+// ---------------------------------------------------------- backward: dK, dV ----
+__global__ __launch_bounds__(256) void flash_bwd_dkdv_kernel(const bf16* __restrict__ qkv,
+                                                             const bf16* __restrict__ dy,
+                                                             const float* __restrict__ lse,
+                                                             const float* __restrict__ Dd, bf16* __restrict__ dqkv,
+                                                             int T, int NH, int C, float sl2, float scale) {
+  __shared__ __attribute__((aligned(16))) bf16 Qs[64 * LD];
+  __shared__ __attribute__((aligned(16))) bf16 Qt[64 * LD];
+  __shared__ __attribute__((aligned(16))) bf16 Gs[64 * LD];
+  __shared__ __attribute__((aligned(16))) bf16 Gt[64 * LD];
+  __shared__ float lse_s[64], D_s[64];
+  const int h = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, lc = lane & 31, hl = lane >> 5;
+  const int key0 = blockIdx.x * 128;  // tile 0 has the most queries and is scheduled first
+  const int mykey = key0 + wave * 32 + lc;
+  const int64_t ld = 3 * (int64_t)C;
+  const bf16* Q = qkv + (int64_t)b * T * ld + h * HD;
+  const bf16* K = Q + C;
+  const bf16* V = Q + 2 * C;
+  const bf16* G = dy + (int64_t)b * T * C + h * HD;
+  const float* lse_b = lse + ((int64_t)b * NH + h) * T;
+  const float* D_b = Dd + ((int64_t)b * NH + h) * T;
+
+  bf16x8 kf[4], vf[4];
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) {
+    kf[kk] = as_bf16x8(ld16_or_zero(K + (int64_t)mykey * ld + kk * 16 + hl * 8, mykey < T));
+    vf[kk] = as_bf16x8(ld16_or_zero(V + (int64_t)mykey * ld + kk * 16 + hl * 8, mykey < T));
+  }
+  f32x16 dk[2], dv[2];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) dk[0][r] = dk[1][r] = dv[0][r] = dv[1][r] = 0.f;
+
+  for (int q0 = key0; q0 < T; q0 += 64) {
+    __syncthreads();
+    tile_natural(Q, ld, q0, T, Qs, tid);
+    tile_natural(G, C, q0, T, Gs, tid);
+    if (tid < 64) tile_transposed(Q, ld, q0, T, Qt, tid);
+    else if (tid < 128) tile_transposed(G, C, q0, T, Gt, tid - 64);
+    else if (tid < 192) {
+      const int t = tid - 128, q = q0 + t;
+      lse_s[t] = q < T ? lse_b[q] * kLog2e : 0.f;
+      D_s[t] = q < T ? D_b[q] : 0.f;
+    }
+    __syncthreads();
+    f32x16 P[2], dS[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      f32x16 sv, dp;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sv[r] = dp[r] = 0.f;
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        const bf16x8 qa = *reinterpret_cast<const bf16x8*>(Qs + (i * 32 + lc) * LD + kk * 16 + hl * 8);
+        const bf16x8 ga = *reinterpret_cast<const bf16x8*>(Gs + (i * 32 + lc) * LD + kk * 16 + hl * 8);
+        sv = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kf[kk], sv, 0, 0, 0);
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ga, vf[kk], dp, 0, 0, 0);
+      }
+      // sv[r]: query q0 + 32 i + 8 (r/4) + 4 hl + r%4, key mykey
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int ql = i * 32 + 8 * (r >> 2) + 4 * hl + (r & 3);
+        const int q = q0 + ql;
+        const float p = (mykey <= q && q < T) ? exp2_fast(sv[r] * sl2 - lse_s[ql]) : 0.f;
+        P[i][r] = p;
+        dS[i][r] = p * (dp[r] - D_s[ql]);
+      }
+    }
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+      const bf16x8 pb = pack8(P[st >> 1], 8 * (st & 1));
+      const bf16x8 sb = pack8(dS[st >> 1], 8 * (st & 1));
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const bf16x8 ga = lds_pair4(Gt + (t * 32 + lc) * LD + st * 16 + 4 * hl);
+        const bf16x8 qa = lds_pair4(Qt + (t * 32 + lc) * LD + st * 16 + 4 * hl);
+        dv[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ga, pb, dv[t], 0, 0, 0);
+        dk[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, sb, dk[t], 0, 0, 0);
+      }
+    }
+  }
+  if (mykey < T) {
+    bf16* o = dqkv + ((int64_t)b * T + mykey) * ld + h * HD;
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        float a[4] = {dk[t][4 * q] * scale, dk[t][4 * q + 1] * scale, dk[t][4 * q + 2] * scale,
+                      dk[t][4 * q + 3] * scale};
+        float c[4] = {dv[t][4 * q], dv[t][4 * q + 1], dv[t][4 * q + 2], dv[t][4 * q + 3]};
+        store4(o + C + t * 32 + 8 * q + 4 * hl, a);
+        store4(o + 2 * C + t * 32 + 8 * q + 4 * hl, c);
+      }
+  }
+}
+
+// --------------------------------------------------------------- backward: dQ ----
+__global__ __launch_bounds__(256) void flash_bwd_dq_kernel(const bf16* __restrict__ qkv, const bf16* __restrict__ dy,
+                                                           const float* __restrict__ lse,
+                                                           const float* __restrict__ Dd, bf16* __restrict__ dqkv,
+                                                           int T, int NH, int C, float sl2, float scale) {
+  __shared__ __attribute__((aligned(16))) bf16 Ks[64 * LD];
+  __shared__ __attribute__((aligned(16))) bf16 Kt[64 * LD];
+  __shared__ __attribute__((aligned(16))) bf16 Vs[64 * LD];
+  const int qt = gridDim.x - 1 - blockIdx.x;
+  const int h = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, lc = lane & 31, hl = lane >> 5;
+  const int q0 = qt * 128;
+  const int myq = q0 + wave * 32 + lc;
+  const int64_t ld = 3 * (int64_t)C;
+  const bf16* Q = qkv + (int64_t)b * T * ld + h * HD;
+  const bf16* K = Q + C;
+  const bf16* V = Q + 2 * C;
+  const bf16* G = dy + (int64_t)b * T * C + h * HD;
+  const bool qok = myq < T;
+  const float lse2 = qok ? lse[((int64_t)b * NH + h) * T + myq] * kLog2e : 0.f;
+  const float Dq = qok ? Dd[((int64_t)b * NH + h) * T + myq] : 0.f;
+
+  bf16x8 qf[4], gf[4];
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) {
+    qf[kk] = as_bf16x8(ld16_or_zero(Q + (int64_t)myq * ld + kk * 16 + hl * 8, qok));
+    gf[kk] = as_bf16x8(ld16_or_zero(G + (int64_t)myq * C + kk * 16 + hl * 8, qok));
+  }
+  f32x16 dq[2];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) dq[0][r] = dq[1][r] = 0.f;
+  const int kv_end = min(T, q0 + 128);
+  for (int k0 = 0; k0 < kv_end; k0 += 64) {
+    __syncthreads();
+    tile_natural(K, ld, k0, T, Ks, tid);
+    tile_natural(V, ld, k0, T, Vs, tid);
+    if (tid < 64) tile_transposed(K, ld, k0, T, Kt, tid);
+    __syncthreads();
+    f32x16 dS[2];
+#pragma unroll
+    for (int js = 0; js < 2; ++js) {
+      f32x16 sv, dp;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sv[r] = dp[r] = 0.f;
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        const bf16x8 ka = *reinterpret_cast<const bf16x8*>(Ks + (js * 32 + lc) * LD + kk * 16 + hl * 8);
+        const bf16x8 va = *reinterpret_cast<const bf16x8*>(Vs + (js * 32 + lc) * LD + kk * 16 + hl * 8);
+        sv = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[kk], sv, 0, 0, 0);
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, gf[kk], dp, 0, 0, 0);
+      }
+      // sv[r]: key k0 + 32 js + 8 (r/4) + 4 hl + r%4, query myq
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = k0 + js * 32 + 8 * (r >> 2) + 4 * hl + (r & 3);
+        const float p = (key <= myq && qok) ? exp2_fast(sv[r] * sl2 - lse2) : 0.f;
+        dS[js][r] = p * (dp[r] - Dq);
+      }
+    }
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+      const bf16x8 sb = pack8(dS[st >> 1], 8 * (st & 1));
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const bf16x8 ka = lds_pair4(Kt + (t * 32 + lc) * LD + st * 16 + 4 * hl);
+        dq[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, sb, dq[t], 0, 0, 0);
+      }
+    }
+  }
+  if (qok) {
+    bf16* o = dqkv + ((int64_t)b * T + myq) * ld + h * HD;
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        float a[4] = {dq[t][4 * q] * scale, dq[t][4 * q + 1] * scale, dq[t][4 * q + 2] * scale,
+                      dq[t][4 * q + 3] * scale};
+        store4(o + t * 32 + 8 * q + 4 * hl, a);
+      }
+  }
+}
+
+void attn_fwd_bf16(const void* qkv, void* y, float* lse, int B, int T, int NH, int C, hipStream_t s) {
+  const float scale = 1.0f / sqrtf((float)HD);
+  dim3 grid((T + 127) / 128, NH, B);
+  flash_fwd_kernel<<<grid, 256, 0, s>>>(reinterpret_cast<const bf16*>(qkv), reinterpret_cast<bf16*>(y), lse, T, NH,
+                                        C, scale * kLog2e);
+}
+
+void attn_bwd_bf16(const void* qkv, const void* y, const void* dy, const float* lse, float* Dbuf, void* dqkv, int B,
+                   int T, int NH, int C, hipStream_t s) {
+  const float scale = 1.0f / sqrtf((float)HD);
+  const int64_t rows = (int64_t)B * T * NH;
+  attn_rowdot_kernel<<<(unsigned)((rows + 255) / 256), 256, 0, s>>>(
+      reinterpret_cast<const bf16*>(y), reinterpret_cast<const bf16*>(dy), Dbuf, B, T, NH, C);
+  dim3 grid((T + 127) / 128, NH, B);
+  flash_bwd_dkdv_kernel<<<grid, 256, 0, s>>>(reinterpret_cast<const bf16*>(qkv), reinterpret_cast<const bf16*>(dy),
+                                             lse, Dbuf, reinterpret_cast<bf16*>(dqkv), T, NH, C, scale * kLog2e,
+                                             scale);
+  flash_bwd_dq_kernel<<<grid, 256, 0, s>>>(reinterpret_cast<const bf16*>(qkv), reinterpret_cast<const bf16*>(dy),
+                                           lse, Dbuf, reinterpret_cast<bf16*>(dqkv), T, NH, C, scale * kLog2e, scale);
+}
+
+// ------------------------------------------------------------------ fp32 path ----
+// One wavefront per (query, head, sequence); scores of the row in LDS.
+__global__ __launch_bounds__(64) void attn_fwd_f32_kernel(const float* __restrict__ qkv, float* __restrict__ y,
+                                                          float* __restrict__ lse, int T, int NH, int C) {
+  extern __shared__ float sc[];
+  const int i = blockIdx.x, h = blockIdx.y, b = blockIdx.z, lane = threadIdx.x;
+  const int hd = C / NH;
+  const int64_t ld = 3 * (int64_t)C;
+  const float* base = qkv + (int64_t)b * T * ld + h * hd;
+  const float* q = base + (int64_t)i * ld;
+  const float scale = 1.0f / sqrtf((float)hd);
+  float mx = -INFINITY;
+  for (int j = lane; j <= i; j += 64) {
+    const float* k = base + C + (int64_t)j * ld;
+    float s = 0.f;
+    for (int d = 0; d < hd; ++d) s = fmaf(q[d], k[d], s);
+    s *= scale;
+    sc[j] = s;
+    mx = fmaxf(mx, s);
+  }
+  mx = wave_max(mx);
+  float sum = 0.f;
+  for (int j = lane; j <= i; j += 64) {
+    const float p = expf(sc[j] - mx);
+    sc[j] = p;
+    sum += p;
+  }
+  sum = wave_sum(sum);
+  __syncthreads();
+  for (int d = lane; d < hd; d += 64) {
+    float acc = 0.f;
+    for (int j = 0; j <= i; ++j) acc = fmaf(sc[j], base[2 * C + (int64_t)j * ld + d], acc);
+    y[((int64_t)b * T + i) * C + h * hd + d] = acc / sum;
+  }
+  if (lane == 0) lse[((int64_t)b * NH + h) * T + i] = mx + logf(sum);
+}
+
+// dQ for query i, and D_i = dO_i . O_i kept for the dK/dV kernel.
+__global__ __launch_bounds__(64) void attn_bwd_dq_f32_kernel(const float* __restrict__ qkv,
+                                                             const float* __restrict__ y,
+                                                             const float* __restrict__ dy,
+                                                             const float* __restrict__ lse, float* __restrict__ Dd,
+                                                             float* __restrict__ dqkv, int T, int NH, int C) {
+  extern __shared__ float sc[];
+  const int i = blockIdx.x, h = blockIdx.y, b = blockIdx.z, lane = threadIdx.x;
+  const int hd = C / NH;
+  const int64_t ld = 3 * (int64_t)C;
+  const float* base = qkv + (int64_t)b * T * ld + h * hd;
+  const float* q = base + (int64_t)i * ld;
+  const float* g = dy + ((int64_t)b * T + i) * C + h * hd;
+  const float* o = y + ((int64_t)b * T + i) * C + h * hd;
+  const float scale = 1.0f / sqrtf((float)hd);
+  float dsum = 0.f;
+  for (int d = lane; d < hd; d += 64) dsum = fmaf(g[d], o[d], dsum);
+  const float Di = wave_sum(dsum);
+  const float L = lse[((int64_t)b * NH + h) * T + i];
+  for (int j = lane; j <= i; j += 64) {
+    const float* k = base + C + (int64_t)j * ld;
+    const float* v = base + 2 * C + (int64_t)j * ld;
+    float s = 0.f, dp = 0.f;
+    for (int d = 0; d < hd; ++d) {
+      s = fmaf(q[d], k[d], s);
+      dp = fmaf(g[d], v[d], dp);
+    }
+    const float p = expf(s * scale - L);
+    sc[j] = p * (dp - Di);
+  }
+  __syncthreads();
+  for (int d = lane; d < hd; d += 64) {
+    float acc = 0.f;
+    for (int j = 0; j <= i; ++j) acc = fmaf(sc[j], base[C + (int64_t)j * ld + d], acc);
+    dqkv[((int64_t)b * T + i) * ld + h * hd + d] = acc * scale;
+  }
+  if (lane == 0) Dd[((int64_t)b * NH + h) * T + i] = Di;
+}
+
+// dK, dV for key j.
+__global__ __launch_bounds__(64) void attn_bwd_dkdv_f32_kernel(const float* __restrict__ qkv,
+                                                               const float* __restrict__ dy,
+                                                               const float* __restrict__ lse,
+                                                               const float* __restrict__ Dd,
+                                                               float* __restrict__ dqkv, int T, int NH, int C) {
+  extern __shared__ float sc[];  // [2][T]
+  const int j = blockIdx.x, h = blockIdx.y, b = blockIdx.z, lane = threadIdx.x;
+  const int hd = C / NH;
+  const int64_t ld = 3 * (int64_t)C;
+  const float* base = qkv + (int64_t)b * T * ld + h * hd;
+  const float* k = base + C + (int64_t)j * ld;
+  const float* v = base + 2 * C + (int64_t)j * ld;
+  const float scale = 1.0f / sqrtf((float)hd);
+  float* P = sc;
+  float* S = sc + T;
+  for (int i = j + lane; i < T; i += 64) {
+    const float* q = base + (int64_t)i * ld;
+    const float* g = dy + ((int64_t)b * T + i) * C + h * hd;
+    float s = 0.f, dp = 0.f;
+    for (int d = 0; d < hd; ++d) {
+      s = fmaf(q[d], k[d], s);
+      dp = fmaf(g[d], v[d], dp);
+    }
+    const int64_t r = ((int64_t)b * NH + h) * T + i;
+    const float p = expf(s * scale - lse[r]);
+    P[i] = p;
+    S[i] = p * (dp - Dd[r]);
+  }
+  __syncthreads();
+  for (int d = lane; d < hd; d += 64) {
+    float a = 0.f, c = 0.f;
+    for (int i = j; i < T; ++i) {
+      a = fmaf(S[i], base[(int64_t)i * ld + d], a);
+      c = fmaf(P[i], dy[((int64_t)b * T + i) * C + h * hd + d], c);
+    }
+    float* out = dqkv + ((int64_t)b * T + j) * ld + h * hd + d;
+    out[C] = a * scale;
+    out[2 * C] = c;
+  }
+}
+
+void attn_fwd_f32(const float* qkv, float* y, float* lse, int B, int T, int NH, int C, hipStream_t s) {
+  dim3 grid(T, NH, B);
+  attn_fwd_f32_kernel<<<grid, 64, T * sizeof(float), s>>>(qkv, y, lse, T, NH, C);
+}
+
+void attn_bwd_f32(const float* qkv, const float* y, const float* dy, const float* lse, float* Dbuf, float* dqkv,
+                  int B, int T, int NH, int C, hipStream_t s) {
+  dim3 grid(T, NH, B);
+  attn_bwd_dq_f32_kernel<<<grid, 64, T * sizeof(float), s>>>(qkv, y, dy, lse, Dbuf, dqkv, T, NH, C);
+  attn_bwd_dkdv_f32_kernel<<<grid, 64, 2 * T * sizeof(float), s>>>(qkv, dy, lse, Dbuf, dqkv, T, NH, C);
+}
+
+}  // namespace gpt2k

@@ -1,0 +1,125 @@
+// Device helpers shared by the gfx950 kernels of the GPT-2 step.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+#define GPT2_WAVE 64
+#define DEVI __device__ __forceinline__
+
+// ---- conversions -----------------------------------------------------------
+DEVI float to_f32(float x) { return x; }
+DEVI float to_f32(bf16 x) { return (float)x; }
+template <typename T> DEVI T from_f32(float x);
+template <> DEVI float from_f32<float>(float x) { return x; }
+template <> DEVI bf16 from_f32<bf16>(float x) { return (bf16)x; }  // RNE (v_cvt_pk_bf16_f32)
+
+// Load / store four consecutive elements as fp32.
+DEVI void load4(const float* p, float v[4]) {
+  f32x4 t = *reinterpret_cast<const f32x4*>(p);
+  v[0] = t[0]; v[1] = t[1]; v[2] = t[2]; v[3] = t[3];
+}
+DEVI void load4(const bf16* p, float v[4]) {
+  bf16x4 t = *reinterpret_cast<const bf16x4*>(p);
+  v[0] = (float)t[0]; v[1] = (float)t[1]; v[2] = (float)t[2]; v[3] = (float)t[3];
+}
+DEVI void store4(float* p, const float v[4]) {
+  f32x4 t = {v[0], v[1], v[2], v[3]};
+  *reinterpret_cast<f32x4*>(p) = t;
+}
+DEVI void store4(bf16* p, const float v[4]) {
+  bf16x4 t = {(bf16)v[0], (bf16)v[1], (bf16)v[2], (bf16)v[3]};
+  *reinterpret_cast<bf16x4*>(p) = t;
+}
+
+// ---- math --------------------------------------------------------------------
+constexpr float kLog2e = 1.4426950408889634f;   // log2(e)
+constexpr float kLn2 = 0.6931471805599453f;     // ln(2)
+
+DEVI float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+DEVI float exp_fast(float x) { return __builtin_amdgcn_exp2f(x * kLog2e); }
+
+// tanh(a) = 1 - 2 / (e^{2a} + 1): exact limits +-1 for large |a|.
+DEVI float tanh_fast(float a) { return 1.0f - 2.0f / (exp_fast(2.0f * a) + 1.0f); }
+
+// tanh-form GELU and its derivative: u -> 0.5 u (1 + tanh(k (u + 0.044715 u^3))).
+constexpr float kGeluK = 0.7978845608028654f;  // sqrt(2 / pi)
+constexpr float kGeluA = 0.044715f;
+DEVI float gelu_f(float u) {
+  float t = tanh_fast(kGeluK * (u + kGeluA * u * u * u));
+  return 0.5f * u * (1.0f + t);
+}
+DEVI float gelu_grad_f(float u) {
+  float t = tanh_fast(kGeluK * (u + kGeluA * u * u * u));
+  return 0.5f * (1.0f + t) + 0.5f * u * (1.0f - t * t) * kGeluK * (1.0f + 3.0f * kGeluA * u * u);
+}
+
+// ---- wave / block reductions ---------------------------------------------------
+DEVI float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+DEVI float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+DEVI double wave_sum_d(double v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+// Block-wide sum (blockDim.x a multiple of 64, at most 1024); every thread gets the result.
+template <typename T>
+DEVI T block_sum(T v, T* scratch /* >= 16 entries */) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  if constexpr (sizeof(T) == 8) v = wave_sum_d(v); else v = wave_sum(v);
+  __syncthreads();
+  if (lane == 0) scratch[w] = v;
+  __syncthreads();
+  T r = 0;
+  for (int i = 0; i < nw; ++i) r += scratch[i];  // fixed order
+  return r;
+}
+DEVI float block_max(float v, float* scratch) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  v = wave_max(v);
+  __syncthreads();
+  if (lane == 0) scratch[w] = v;
+  __syncthreads();
+  float r = -INFINITY;
+  for (int i = 0; i < nw; ++i) r = fmaxf(r, scratch[i]);
+  return r;
+}
+
+// ---- 8x8 bf16 transpose in registers ------------------------------------------
+// in[j] holds 8 bf16 of row j (elements 0..7 of that row).  out[e] receives
+// the 8 bf16 of column e (element j from row j).
+DEVI void transpose8x8(const u32x4 in[8], u32x4 out[8]) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      // low half from row 2d, high half from row 2d+1
+      out[e][d] = __builtin_amdgcn_perm(in[2 * d + 1][e >> 1], in[2 * d][e >> 1], sel);
+    }
+  }
+}
+
+// 16-byte global load with zero fill when the predicate is false.
+DEVI u32x4 ld16_or_zero(const void* p, bool ok) {
+  u32x4 z = {0u, 0u, 0u, 0u};
+  return ok ? *reinterpret_cast<const u32x4*>(p) : z;
+}

@@ -1,0 +1,217 @@
+// Token + position embedding: forward gather and deterministic backward scatter.
+//
+// Backward: the (id, position) pairs are sorted by id with a stable LSD radix
+// sort (4-bit digits, one workgroup), so the gradient of every wte row is the
+// sum of its positions' rows in position order.  The sum is split into runs of
+// at most 64 sorted entries (one block each) and the runs of a segment are
+// then added in order: no atomics, the same bits on every run.
+#include "common.h"
+#include "kernels.h"
+
+namespace gpt2k {
+
+__global__ void embed_fwd_kernel(const int32_t* __restrict__ idx, const float* __restrict__ wte,
+                                 const float* __restrict__ wpe, float* __restrict__ x, int32_t* __restrict__ ids_out,
+                                 int M, int T, int C, int vocab, int* __restrict__ err) {
+  const int C4 = C >> 2;
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= (int64_t)M * C4) return;
+  const int m = (int)(i / C4), c = (int)(i % C4) * 4;
+  int id = idx[m];
+  if (id < 0 || id >= vocab) {
+    *err = 1;
+    id = 0;
+  }
+  if (c == 0) ids_out[m] = id;
+  float a[4], b[4];
+  load4(wte + (int64_t)id * C + c, a);
+  load4(wpe + (int64_t)(m % T) * C + c, b);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) a[e] += b[e];
+  store4(x + (int64_t)m * C + c, a);
+}
+
+void embed_fwd(const int32_t* idx, const float* wte, const float* wpe, float* x, int32_t* ids_out, int M, int T,
+               int C, int vocab, int* err, hipStream_t s) {
+  const int64_t n = (int64_t)M * (C / 4);
+  embed_fwd_kernel<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(idx, wte, wpe, x, ids_out, M, T, C, vocab, err);
+}
+
+// Stable LSD radix sort of (key = idx[m], value = m).  Thread t owns the
+// contiguous range [t*chunk, (t+1)*chunk) of the input order, which keeps the
+// scatter stable.  Out-of-range ids are sorted as id 0 (the forward already
+// flagged them).
+__global__ __launch_bounds__(256) void radix_sort_kernel(const int32_t* __restrict__ idx, int M, int vocab,
+                                                         int passes, int32_t* ka, int32_t* va, int32_t* kb,
+                                                         int32_t* vb) {
+  __shared__ int hist[16][256];
+  __shared__ int tsum[256];
+  const int t = threadIdx.x;
+  const int chunk = (M + 255) / 256;
+  const int lo = min(M, t * chunk), hi = min(M, lo + chunk);
+  for (int pass = 0; pass < passes; ++pass) {
+    const int32_t* kin = (pass & 1) ? ka : kb;
+    const int32_t* vin = (pass & 1) ? va : vb;
+    int32_t* kout = (pass & 1) ? kb : ka;
+    int32_t* vout = (pass & 1) ? vb : va;
+    const int shift = 4 * pass;
+    int cnt[16];
+#pragma unroll
+    for (int d = 0; d < 16; ++d) cnt[d] = 0;
+    for (int i = lo; i < hi; ++i) {
+      int key;
+      if (pass == 0) {
+        key = idx[i];
+        if (key < 0 || key >= vocab) key = 0;
+      } else {
+        key = kin[i];
+      }
+      ++cnt[(key >> shift) & 15];
+    }
+#pragma unroll
+    for (int d = 0; d < 16; ++d) hist[d][t] = cnt[d];
+    __syncthreads();
+    // exclusive scan in (digit, thread) order; thread t scans flat entries [16t, 16t+16)
+    const int dd = t >> 4, t0 = (t & 15) * 16;
+    int loc[16], s = 0;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      loc[j] = hist[dd][t0 + j];
+      s += loc[j];
+    }
+    tsum[t] = s;
+    __syncthreads();
+    if (t == 0) {
+      int run = 0;
+      for (int i = 0; i < 256; ++i) {
+        const int v = tsum[i];
+        tsum[i] = run;
+        run += v;
+      }
+    }
+    __syncthreads();
+    int run = tsum[t];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      hist[dd][t0 + j] = run;
+      run += loc[j];
+    }
+    __syncthreads();
+    int off[16];
+#pragma unroll
+    for (int d = 0; d < 16; ++d) off[d] = hist[d][t];
+    for (int i = lo; i < hi; ++i) {
+      int key, val;
+      if (pass == 0) {
+        key = idx[i];
+        if (key < 0 || key >= vocab) key = 0;
+        val = i;
+      } else {
+        key = kin[i];
+        val = vin[i];
+      }
+      const int d = (key >> shift) & 15;
+      const int dst = off[d]++;
+      kout[dst] = key;
+      vout[dst] = val;
+    }
+    __threadfence();
+    __syncthreads();
+  }
+}
+
+void embed_sort(const int32_t* idx, int M, int vocab, int id_bits, int32_t* keys_a, int32_t* vals_a,
+                int32_t* keys_b, int32_t* vals_b, hipStream_t s) {
+  const int passes = (id_bits + 3) / 4;
+  radix_sort_kernel<<<1, 256, 0, s>>>(idx, M, vocab, passes, keys_a, vals_a, keys_b, vals_b);
+}
+
+constexpr int kRun = 64;
+
+// Runs: within each chunk of 64 sorted entries, consecutive equal ids form a run;
+// the run's row sum is stored at the index of its first entry.
+__global__ __launch_bounds__(256) void run_sum_kernel(const int32_t* __restrict__ sid,
+                                                      const int32_t* __restrict__ spos,
+                                                      const float* __restrict__ dx, float* __restrict__ runs,
+                                                      int M, int C) {
+  const int base = blockIdx.x * kRun, end = min(M, base + kRun);
+  const int C4 = C >> 2;
+  for (int c4 = threadIdx.x; c4 < C4; c4 += blockDim.x) {
+    float acc[4] = {0.f, 0.f, 0.f, 0.f};
+    int start = base;
+    for (int i = base; i < end; ++i) {
+      float v[4];
+      load4(dx + (int64_t)spos[i] * C + 4 * c4, v);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[e] += v[e];
+      if (i + 1 == end || sid[i + 1] != sid[i]) {
+        store4(runs + (int64_t)start * C + 4 * c4, acc);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[e] = 0.f;
+        start = i + 1;
+      }
+    }
+  }
+}
+
+// One wavefront per sorted entry; entries that start a segment add the
+// segment's runs (in order) into their wte row.
+__global__ __launch_bounds__(256) void segment_add_kernel(const int32_t* __restrict__ sid,
+                                                          const float* __restrict__ runs, float* __restrict__ dwte,
+                                                          int M, int C) {
+  const int i = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (i >= M) return;
+  const int id = sid[i];
+  if (i > 0 && sid[i - 1] == id) return;
+  const int C4 = C >> 2;
+  for (int c4 = lane; c4 < C4; c4 += 64) {
+    float s[4];
+    load4(runs + (int64_t)i * C + 4 * c4, s);
+    for (int j = (i / kRun + 1) * kRun; j < M && sid[j] == id; j += kRun) {
+      float v[4];
+      load4(runs + (int64_t)j * C + 4 * c4, v);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) s[e] += v[e];
+    }
+    float* o = dwte + (int64_t)id * C + 4 * c4;
+    float a[4];
+    load4(o, a);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) a[e] += s[e];
+    store4(o, a);
+  }
+}
+
+void embed_scatter(const int32_t* sorted_ids, const int32_t* sorted_pos, const float* dx, float* run_sums,
+                   float* dwte, int M, int C, hipStream_t s) {
+  run_sum_kernel<<<(M + kRun - 1) / kRun, 256, 0, s>>>(sorted_ids, sorted_pos, dx, run_sums, M, C);
+  segment_add_kernel<<<(M + 3) / 4, 256, 0, s>>>(sorted_ids, run_sums, dwte, M, C);
+}
+
+__global__ void wpe_grad_kernel(const float* __restrict__ dx, float* __restrict__ dwpe, int B, int T, int C) {
+  const int C4 = C >> 2;
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= (int64_t)T * C4) return;
+  const int t = (int)(i / C4), c = (int)(i % C4) * 4;
+  float s[4] = {0.f, 0.f, 0.f, 0.f};
+  for (int b = 0; b < B; ++b) {
+    float v[4];
+    load4(dx + ((int64_t)b * T + t) * C + c, v);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) s[e] += v[e];
+  }
+  float* o = dwpe + (int64_t)t * C + c;
+  float a[4];
+  load4(o, a);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) a[e] += s[e];
+  store4(o, a);
+}
+
+void embed_wpe_grad(const float* dx, float* dwpe, int B, int T, int C, hipStream_t s) {
+  const int64_t n = (int64_t)T * (C / 4);
+  wpe_grad_kernel<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(dx, dwpe, B, T, C);
+}
+
+}  // namespace gpt2k

@@ -1,0 +1,376 @@
+// GEMMs of the GPT-2 step: C = A B with fused epilogues.
+//
+// bf16 path: v_mfma_f32_32x32x16_bf16 on LDS-staged tiles.  Both operand
+// tiles are kept in LDS with k contiguous per row, so every MFMA fragment is a
+// single 16-byte LDS read; operands stored with k strided in HBM (the
+// transposed operands of the backward GEMMs) are transposed in registers
+// (8x8 bf16 blocks, v_perm_b32) between the coalesced global load and the
+// LDS store.  Global loads of tile k+1 are in flight while tile k is
+// multiplied (two LDS buffers, one barrier per k-tile).
+//
+// fp32 path: LDS-tiled FMA GEMM (64x64 tile, 4x4 outputs per thread).
+#include "common.h"
+#include "kernels.h"
+
+namespace gpt2k {
+
+// ---------------------------------------------------------------- epilogue ----
+template <int EPI, typename TA>
+DEVI void epi_store4(const GemmArgs& p, int m, int n, float v[4], int split) {
+  const int64_t off = (int64_t)m * p.ldc + n;
+  if constexpr (EPI == EPI_ACT) {
+    if (p.bias) {
+      float b[4];
+      load4(p.bias + n, b);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v[i] += b[i];
+    }
+    store4(reinterpret_cast<TA*>(p.C) + off, v);
+  } else if constexpr (EPI == EPI_F32) {
+    store4(reinterpret_cast<float*>(p.C) + off, v);
+  } else if constexpr (EPI == EPI_F32_ACC) {
+    float o[4];
+    float* c = reinterpret_cast<float*>(p.C) + off;
+    load4(c, o);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] += o[i];
+    store4(c, v);
+  } else if constexpr (EPI == EPI_RESID) {
+    float r[4], b[4];
+    load4(p.resid + off, r);
+    load4(p.bias + n, b);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = r[i] + (v[i] + b[i]);
+    store4(reinterpret_cast<float*>(p.C) + off, v);
+  } else if constexpr (EPI == EPI_GELU) {
+    float b[4], g[4];
+    load4(p.bias + n, b);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[i] += b[i];
+      g[i] = gelu_f(v[i]);
+    }
+    store4(reinterpret_cast<TA*>(p.C) + off, v);
+    store4(reinterpret_cast<TA*>(p.C2) + off, g);
+  } else if constexpr (EPI == EPI_GELU_BWD) {
+    float u[4];
+    load4(reinterpret_cast<const TA*>(p.aux) + off, u);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] *= gelu_grad_f(u[i]);
+    store4(reinterpret_cast<TA*>(p.C) + off, v);
+  } else {  // EPI_PARTIAL
+    store4(reinterpret_cast<float*>(p.C) + (int64_t)split * p.split_stride + off, v);
+  }
+}
+
+// One element (fp32 path, shapes that are not multiples of four).
+template <int EPI, typename TA>
+DEVI void epi_store1(const GemmArgs& p, int m, int n, float v, int split) {
+  const int64_t off = (int64_t)m * p.ldc + n;
+  if constexpr (EPI == EPI_ACT) {
+    reinterpret_cast<TA*>(p.C)[off] = from_f32<TA>(p.bias ? v + p.bias[n] : v);
+  } else if constexpr (EPI == EPI_F32) {
+    reinterpret_cast<float*>(p.C)[off] = v;
+  } else if constexpr (EPI == EPI_F32_ACC) {
+    reinterpret_cast<float*>(p.C)[off] += v;
+  } else if constexpr (EPI == EPI_RESID) {
+    reinterpret_cast<float*>(p.C)[off] = p.resid[off] + (v + p.bias[n]);
+  } else if constexpr (EPI == EPI_GELU) {
+    const float u = v + p.bias[n];
+    reinterpret_cast<TA*>(p.C)[off] = from_f32<TA>(u);
+    reinterpret_cast<TA*>(p.C2)[off] = from_f32<TA>(gelu_f(u));
+  } else if constexpr (EPI == EPI_GELU_BWD) {
+    reinterpret_cast<TA*>(p.C)[off] = from_f32<TA>(v * gelu_grad_f(to_f32(reinterpret_cast<const TA*>(p.aux)[off])));
+  } else {
+    reinterpret_cast<float*>(p.C)[(int64_t)split * p.split_stride + off] = v;
+  }
+}
+
+// ------------------------------------------------------------ bf16 MFMA GEMM ----
+// Stages an R x BK operand tile (rows r0.., k in [k0, kend)) through registers
+// into LDS laid out [R][BK + 8] (k contiguous, 16-byte row padding).
+template <bool KMAJ, int R, int BK>
+struct TileLoader {
+  static constexpr int LDS = BK + 8;
+  static constexpr int NCH = KMAJ ? (R * BK / 8) : (R * BK / 64);
+  static constexpr int PER = (NCH + 255) / 256;
+  static constexpr int REGS = KMAJ ? PER : PER * 8;
+  u32x4 r[REGS];
+
+  DEVI void load(const bf16* g, int64_t ld, int r0, int rmax, int k0, int kend, int tid) {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int c = tid + i * 256;
+      if (NCH % 256 == 0 || c < NCH) {
+        if constexpr (KMAJ) {
+          // g is [rows][k]: 16-byte chunks along k
+          const int row = c / (BK / 8), kc = (c % (BK / 8)) * 8;
+          const bool ok = (r0 + row < rmax) && (k0 + kc < kend);
+          r[i] = ld16_or_zero(g + (int64_t)(r0 + row) * ld + k0 + kc, ok);
+        } else {
+          // g is [k][rows]: an 8 (k) x 8 (rows) block
+          const int rb = c % (R / 8), kb = c / (R / 8);
+          const int rr = r0 + rb * 8;
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            const int k = k0 + kb * 8 + j;
+            r[i * 8 + j] = ld16_or_zero(g + (int64_t)k * ld + rr, (k < kend) && (rr < rmax));
+          }
+        }
+      }
+    }
+  }
+  DEVI void store(bf16* s, int tid) {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int c = tid + i * 256;
+      if (NCH % 256 == 0 || c < NCH) {
+        if constexpr (KMAJ) {
+          const int row = c / (BK / 8), kc = (c % (BK / 8)) * 8;
+          *reinterpret_cast<u32x4*>(s + row * LDS + kc) = r[i];
+        } else {
+          const int rb = c % (R / 8), kb = c / (R / 8);
+          u32x4 t[8];
+          transpose8x8(&r[i * 8], t);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) *reinterpret_cast<u32x4*>(s + (rb * 8 + e) * LDS + kb * 8) = t[e];
+        }
+      }
+    }
+  }
+};
+
+template <bool A_K, bool B_K, int BM, int BN, int BK, int WGM, int WGN, int EPI>
+__global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs p) {
+  static_assert(WGM * WGN == 4, "four waves");
+  constexpr int LDS = BK + 8;
+  constexpr int WTM = BM / WGM, WTN = BN / WGN;
+  constexpr int FM = WTM / 32, FN = WTN / 32;
+  __shared__ __attribute__((aligned(16))) bf16 smem[2 * (BM + BN) * LDS];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / WGN, wn = wave % WGN;
+  const int lc = lane & 31, hl = lane >> 5;
+  const int tiles_n = (p.N + BN - 1) / BN;
+  const int m0 = (blockIdx.x / tiles_n) * BM, n0 = (blockIdx.x % tiles_n) * BN;
+  const int split = blockIdx.y;
+  const int kbeg = split * p.k_per_split;
+  const int kend = min(p.K, kbeg + p.k_per_split);
+  const int nkt = kend > kbeg ? (kend - kbeg + BK - 1) / BK : 0;
+  const bf16* A = reinterpret_cast<const bf16*>(p.A);
+  const bf16* B = reinterpret_cast<const bf16*>(p.B);
+
+  bf16* sA0 = smem;
+  bf16* sB0 = smem + BM * LDS;
+  bf16* sA1 = smem + (BM + BN) * LDS;
+  bf16* sB1 = sA1 + BM * LDS;
+
+  f32x16 acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  TileLoader<A_K, BM, BK> la;
+  TileLoader<B_K, BN, BK> lb;
+  if (nkt > 0) {
+    la.load(A, p.lda, m0, p.M, kbeg, kend, tid);
+    lb.load(B, p.ldb, n0, p.N, kbeg, kend, tid);
+    la.store(sA0, tid);
+    lb.store(sB0, tid);
+  }
+  __syncthreads();
+
+  for (int kt = 0; kt < nkt; ++kt) {
+    const bool more = kt + 1 < nkt;
+    if (more) {
+      la.load(A, p.lda, m0, p.M, kbeg + (kt + 1) * BK, kend, tid);
+      lb.load(B, p.ldb, n0, p.N, kbeg + (kt + 1) * BK, kend, tid);
+    }
+    const bf16* a_s = (kt & 1) ? sA1 : sA0;
+    const bf16* b_s = (kt & 1) ? sB1 : sB0;
+#pragma unroll
+    for (int kk = 0; kk < BK / 16; ++kk) {
+      bf16x8 af[FM], bfr[FN];
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+        af[i] = *reinterpret_cast<const bf16x8*>(a_s + (wm * WTM + i * 32 + lc) * LDS + kk * 16 + hl * 8);
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+        bfr[j] = *reinterpret_cast<const bf16x8*>(b_s + (wn * WTN + j * 32 + lc) * LDS + kk * 16 + hl * 8);
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+          // first operand supplies the output rows (n), second the columns (m)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[j], af[i], acc[i][j], 0, 0, 0);
+    }
+    if (more) {
+      la.store((kt & 1) ? sA0 : sA1, tid);
+      lb.store((kt & 1) ? sB0 : sB1, tid);
+    }
+    __syncthreads();
+  }
+
+  // acc[i][j][4q + e] is C[m][n] with m = .. + lc, n = .. + 8q + 4hl + e
+#pragma unroll
+  for (int i = 0; i < FM; ++i) {
+    const int m = m0 + wm * WTM + i * 32 + lc;
+    if (m >= p.M) continue;
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int n = n0 + wn * WTN + j * 32 + 8 * q + 4 * hl;
+        if (n < p.N) {
+          float v[4] = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+          epi_store4<EPI, bf16>(p, m, n, v, split);
+        }
+      }
+    }
+  }
+}
+
+// -------------------------------------------------------------- fp32 GEMM ----
+template <bool A_K, bool B_K, int EPI>
+__global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs p) {
+  constexpr int BT = 64, BK = 16;
+  __shared__ float As[BK][BT + 4];
+  __shared__ float Bs[BK][BT + 4];
+  const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
+  const int tiles_n = (p.N + BT - 1) / BT;
+  const int m0 = (blockIdx.x / tiles_n) * BT, n0 = (blockIdx.x % tiles_n) * BT;
+  const int split = blockIdx.y;
+  const int kbeg = split * p.k_per_split;
+  const int kend = min(p.K, kbeg + p.k_per_split);
+  const float* A = reinterpret_cast<const float*>(p.A);
+  const float* B = reinterpret_cast<const float*>(p.B);
+  float acc[4][4] = {};
+  for (int k0 = kbeg; k0 < kend; k0 += BK) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int e = tid + 256 * r;
+      int mm, kk, nn, kb;
+      if (A_K) { mm = e / BK; kk = e % BK; } else { mm = e % BT; kk = e / BT; }
+      const int gm = m0 + mm, gk = k0 + kk;
+      float av = 0.f;
+      if (gm < p.M && gk < kend) av = A_K ? A[(int64_t)gm * p.lda + gk] : A[(int64_t)gk * p.lda + gm];
+      As[kk][mm] = av;
+      if (B_K) { nn = e / BK; kb = e % BK; } else { nn = e % BT; kb = e / BT; }
+      const int gn = n0 + nn, gk2 = k0 + kb;
+      float bv = 0.f;
+      if (gn < p.N && gk2 < kend) bv = B_K ? B[(int64_t)gn * p.ldb + gk2] : B[(int64_t)gk2 * p.ldb + gn];
+      Bs[kb][nn] = bv;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < BK; ++kk) {
+      float a[4], b[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) a[i] = As[kk][ty * 4 + i];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) b[j] = Bs[kk][tx * 4 + j];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(a[i], b[j], acc[i][j]);
+    }
+    __syncthreads();
+  }
+  const bool vec = (p.ldc % 4 == 0) && (p.N % 4 == 0);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int m = m0 + ty * 4 + i, n = n0 + tx * 4;
+    if (m >= p.M || n >= p.N) continue;
+    if (vec) {
+      epi_store4<EPI, float>(p, m, n, acc[i], split);
+    } else {
+      for (int j = 0; j < 4 && n + j < p.N; ++j) epi_store1<EPI, float>(p, m, n + j, acc[i][j], split);
+    }
+  }
+}
+
+// ----------------------------------------------------------- split-K reduce ----
+__global__ void splitk_reduce_kernel(float* out, const float* part, int splits, int64_t stride, int64_t n4) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n4) return;
+  float a[4];
+  load4(out + 4 * i, a);
+  float s[4] = {0.f, 0.f, 0.f, 0.f};
+  for (int k = 0; k < splits; ++k) {
+    float t[4];
+    load4(part + k * stride + 4 * i, t);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) s[e] += t[e];
+  }
+#pragma unroll
+  for (int e = 0; e < 4; ++e) a[e] += s[e];
+  store4(out + 4 * i, a);
+}
+
+void splitk_reduce_add(float* out, const float* part, int splits, int64_t stride, int64_t count,
+                       hipStream_t s) {
+  const int64_t n4 = count / 4;
+  splitk_reduce_kernel<<<(unsigned)((n4 + 255) / 256), 256, 0, s>>>(out, part, splits, stride, n4);
+}
+
+// ---------------------------------------------------------------- dispatch ----
+namespace {
+constexpr int kBM = 128, kBN = 128, kBK = 64;
+
+template <bool A_K, bool B_K, int EPI>
+void launch_bf16(const GemmArgs& a, hipStream_t s) {
+  const int tiles = ((a.M + kBM - 1) / kBM) * ((a.N + kBN - 1) / kBN);
+  dim3 grid(tiles, a.splits);
+  gemm_bf16_kernel<A_K, B_K, kBM, kBN, kBK, 2, 2, EPI><<<grid, 256, 0, s>>>(a);
+}
+template <bool A_K, bool B_K, int EPI>
+void launch_f32(const GemmArgs& a, hipStream_t s) {
+  const int tiles = ((a.M + 63) / 64) * ((a.N + 63) / 64);
+  dim3 grid(tiles, a.splits);
+  gemm_f32_kernel<A_K, B_K, EPI><<<grid, 256, 0, s>>>(a);
+}
+template <bool A_K, bool B_K, int EPI>
+void launch(bool bf16_mode, const GemmArgs& a, hipStream_t s) {
+  if (bf16_mode) launch_bf16<A_K, B_K, EPI>(a, s);
+  else launch_f32<A_K, B_K, EPI>(a, s);
+}
+}  // namespace
+
+bool gemm(GemmLayout layout, GemmEpilogue epi, bool bf16_mode, const GemmArgs& a0, hipStream_t s) {
+  GemmArgs a = a0;
+  if (a.M <= 0 || a.N <= 0 || a.K <= 0) return false;
+  if (a.splits < 1) a.splits = 1;
+  if (a.splits == 1) a.k_per_split = a.K;
+  if (a.splits > 1 && (a.k_per_split % kBK) != 0) return false;
+  if (bf16_mode) {
+    // 16-byte operand accesses: k-contiguous and transposed dims are multiples of 8;
+    // the epilogue writes four columns at a time.
+    if (a.K % 8 || a.N % 8 || a.ldc % 4 || a.lda % 8 || a.ldb % 8) return false;
+    if (layout == LAYOUT_TN && a.M % 8) return false;
+  }
+  switch (layout) {
+    case LAYOUT_NT:
+      if (epi == EPI_ACT) launch<true, true, EPI_ACT>(bf16_mode, a, s);
+      else if (epi == EPI_RESID) launch<true, true, EPI_RESID>(bf16_mode, a, s);
+      else if (epi == EPI_GELU) launch<true, true, EPI_GELU>(bf16_mode, a, s);
+      else return false;
+      break;
+    case LAYOUT_NN:
+      if (epi == EPI_F32) launch<true, false, EPI_F32>(bf16_mode, a, s);
+      else if (epi == EPI_GELU_BWD) launch<true, false, EPI_GELU_BWD>(bf16_mode, a, s);
+      else if (epi == EPI_ACT) launch<true, false, EPI_ACT>(bf16_mode, a, s);
+      else return false;
+      break;
+    case LAYOUT_TN:
+      if (epi == EPI_PARTIAL) launch<false, false, EPI_PARTIAL>(bf16_mode, a, s);
+      else if (epi == EPI_F32_ACC) launch<false, false, EPI_F32_ACC>(bf16_mode, a, s);
+      else return false;
+      break;
+  }
+  return true;
+}
+
+}  // namespace gpt2k

@@ -1,0 +1,706 @@
+// C ABI of the GPT-2 step: workspace plan, launch sequence of the forward,
+// backward, accumulation and clip + AdamW, and the helpers declared in gpt2.h.
+#include "gpt2.h"
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "common.h"
+#include "kernels.h"
+
+using namespace gpt2k;
+
+namespace {
+
+enum TensorId {
+  T_WTE = 0, T_WPE, T_LN1W, T_LN1B, T_QKVW, T_QKVB, T_PROJW, T_PROJB,
+  T_LN2W, T_LN2B, T_FCW, T_FCB, T_FCPW, T_FCPB, T_LNFW, T_LNFB, T_COUNT
+};
+const char* const kTensorNames[T_COUNT] = {"wte", "wpe", "ln1_w", "ln1_b", "qkv_w", "qkv_b", "proj_w", "proj_b",
+                                           "ln2_w", "ln2_b", "fc_w", "fc_b", "fcproj_w", "fcproj_b", "lnf_w",
+                                           "lnf_b"};
+
+struct TensorDesc {
+  int64_t off, numel, per_layer;  // per_layer: elements of one block's tensor (numel if global)
+  int ndim;
+  int64_t dims[3];
+  bool decay;
+};
+
+bool config_ok(const gpt2_config& c) {
+  if (c.n_layer < 1 || c.n_head < 1 || c.n_embd < 8 || c.block_size < 1 || c.vocab_size < 1) return false;
+  if (c.n_embd % c.n_head || c.n_embd % 8 || c.n_embd > 2048) return false;
+  if (c.padded_vocab_size < c.vocab_size || c.max_batch < 1) return false;
+  if (c.precision != GPT2_FP32 && c.precision != GPT2_BF16) return false;
+  if (c.precision == GPT2_BF16 && (c.n_embd / c.n_head != 64 || c.padded_vocab_size % 8)) return false;
+  if (c.precision == GPT2_FP32 && c.n_embd / c.n_head > 256) return false;
+  if ((int64_t)c.max_batch * c.block_size > (1 << 26)) return false;
+  return true;
+}
+
+void tensor_table(const gpt2_config& c, TensorDesc t[T_COUNT]) {
+  const int64_t C = c.n_embd, L = c.n_layer, Vp = c.padded_vocab_size;
+  struct S { int ndim; int64_t d0, d1; bool layer; } sh[T_COUNT] = {
+      {2, Vp, C, false},    {2, c.block_size, C, false}, {1, C, 0, true},     {1, C, 0, true},
+      {2, 3 * C, C, true},  {1, 3 * C, 0, true},         {2, C, C, true},     {1, C, 0, true},
+      {1, C, 0, true},      {1, C, 0, true},             {2, 4 * C, C, true}, {1, 4 * C, 0, true},
+      {2, C, 4 * C, true},  {1, C, 0, true},             {1, C, 0, false},    {1, C, 0, false}};
+  int64_t off = 0;
+  for (int i = 0; i < T_COUNT; ++i) {
+    const int64_t per = sh[i].ndim == 2 ? sh[i].d0 * sh[i].d1 : sh[i].d0;
+    TensorDesc& d = t[i];
+    d.off = off;
+    d.per_layer = per;
+    d.numel = sh[i].layer ? per * L : per;
+    d.decay = sh[i].ndim >= 2;  // weight decay on tensors of two or more dimensions
+    if (sh[i].layer) {
+      d.ndim = sh[i].ndim + 1;
+      d.dims[0] = L;
+      d.dims[1] = sh[i].d0;
+      d.dims[2] = sh[i].d1;
+    } else {
+      d.ndim = sh[i].ndim;
+      d.dims[0] = sh[i].d0;
+      d.dims[1] = sh[i].d1;
+      d.dims[2] = 0;
+    }
+    off += d.numel;
+  }
+}
+
+int64_t total_params(const TensorDesc t[T_COUNT]) { return t[T_COUNT - 1].off + t[T_COUNT - 1].numel; }
+
+// Workspace plan: a list of 256-byte aligned regions.
+struct Plan {
+  int64_t bytes = 0;
+  int64_t take(int64_t n) {
+    const int64_t o = bytes;
+    bytes += (n + 255) / 256 * 256;
+    return o;
+  }
+};
+
+}  // namespace
+
+struct gpt2_ctx {
+  gpt2_config cfg;
+  gpt2_buffers buf;
+  hipStream_t stream;
+  TensorDesc t[T_COUNT];
+  int64_t n_params;
+  bool bf16;
+  int64_t act;  // bytes per activation element
+  int64_t Mmax;
+  int L, C, NH, Vp, V;
+  int id_bits;
+
+  // workspace regions
+  float* res;
+  char* ln1;
+  float *ln1_mean, *ln1_rstd;
+  char* qkv;
+  char* atty;
+  float* lse;
+  char* ln2;
+  float *ln2_mean, *ln2_rstd;
+  char* fcu;
+  char* fcg;
+  char* lnf;
+  float *lnf_mean, *lnf_rstd;
+  char* logits;
+  float* row_loss;
+  int32_t* ids;
+  float* dres;
+  char* dres_act;
+  float* dh;
+  char* dbig;
+  char* dqkv;
+  char* dy;
+  float* attnD;
+  float* splitk;
+  int64_t splitk_elems;
+  float* colpart;
+  int32_t *sort_ka, *sort_va, *sort_kb, *sort_vb;
+  float* run_sums;
+  double* norm_part;
+  float* clip_scale;
+  int* err_flag;
+
+  // state
+  bool have_fwd = false;
+  int B = 0, T = 0;
+  int64_t step = 0;
+
+  // timing
+  std::string site;
+  bool timing = false;
+  std::vector<hipEvent_t> ev;
+  std::vector<double> ev_flops, ev_bytes;
+  size_t ev_used = 0;
+  bool ev_overflow = false;
+
+  // helpers
+  int64_t MC() const { return Mmax * C; }
+  char* layer_act(char* base, int l, int64_t cols) const { return base + (int64_t)l * Mmax * cols * act; }
+  const void* W(int id, int l = 0) const {
+    const int64_t o = t[id].off + (int64_t)l * t[id].per_layer;
+    return bf16 ? (const void*)((const char*)buf.params_bf16 + o * 2) : (const void*)(buf.params + o);
+  }
+  const float* P(int id, int l = 0) const { return buf.params + t[id].off + (int64_t)l * t[id].per_layer; }
+  float* G(int id, int l = 0) const { return buf.grads + t[id].off + (int64_t)l * t[id].per_layer; }
+  float* resid(int i) const { return res + (int64_t)i * MC(); }
+};
+
+namespace {
+
+// Brackets one launch with HIP events when its site matches the enabled prefix.
+struct Timed {
+  gpt2_ctx* c;
+  bool on = false;
+  size_t slot = 0;
+  Timed(gpt2_ctx* ctx, const char* site, double flops, double bytes) : c(ctx) {
+    if (!c->timing || strncmp(site, c->site.c_str(), c->site.size()) != 0) return;
+    if (c->ev_used * 2 + 2 > c->ev.size()) {
+      if (c->ev.size() >= 2 * 8192) {
+        c->ev_overflow = true;
+        return;
+      }
+      for (int i = 0; i < 256; ++i) {
+        hipEvent_t e;
+        if (hipEventCreate(&e) != hipSuccess) return;
+        c->ev.push_back(e);
+      }
+    }
+    slot = c->ev_used++;
+    c->ev_flops.resize(c->ev_used);
+    c->ev_bytes.resize(c->ev_used);
+    c->ev_flops[slot] = flops;
+    c->ev_bytes[slot] = bytes;
+    (void)hipEventRecord(c->ev[2 * slot], c->stream);
+    on = true;
+  }
+  ~Timed() {
+    if (on) (void)hipEventRecord(c->ev[2 * slot + 1], c->stream);
+  }
+};
+
+bool gemm_site(gpt2_ctx* c, const char* site, GemmLayout lay, GemmEpilogue epi, const GemmArgs& a, double bytes) {
+  Timed tm(c, site, 2.0 * a.M * (double)a.N * a.K, bytes);
+  return gemm(lay, epi, c->bf16, a, c->stream);
+}
+
+GemmArgs gargs(const void* A, int64_t lda, const void* B, int64_t ldb, int M, int N, int K, void* C, int64_t ldc) {
+  GemmArgs a;
+  memset(&a, 0, sizeof(a));
+  a.A = A;
+  a.B = B;
+  a.lda = lda;
+  a.ldb = ldb;
+  a.M = M;
+  a.N = N;
+  a.K = K;
+  a.C = C;
+  a.ldc = ldc;
+  a.splits = 1;
+  a.k_per_split = K;
+  return a;
+}
+
+// Weight gradient: out[Mo][N] += A^T B with A stored [K][Mo], B stored [K][N];
+// deterministic split-K over the token dimension when the tile grid is small.
+bool weight_grad(gpt2_ctx* c, const char* site, float* out, const void* A, int64_t lda, const void* B, int64_t ldb,
+                 int Mo, int N, int K) {
+  const int tile = c->bf16 ? 128 : 64;
+  const int64_t tiles = (int64_t)((Mo + tile - 1) / tile) * ((N + tile - 1) / tile);
+  int splits = (int)std::min<int64_t>(16, std::max<int64_t>(1, (512 + tiles - 1) / tiles));
+  int kps = (K + splits - 1) / splits;
+  kps = (kps + 63) / 64 * 64;
+  splits = (K + kps - 1) / kps;
+  const int64_t outn = (int64_t)Mo * N;
+  if (splits > 1 && splits * outn > c->splitk_elems) splits = 1;
+  GemmArgs a = gargs(A, lda, B, ldb, Mo, N, K, out, N);
+  const double bytes = (double)c->act * ((double)K * Mo + (double)K * N) + 8.0 * outn;
+  if (splits == 1) return gemm_site(c, site, LAYOUT_TN, EPI_F32_ACC, a, bytes);
+  a.C = c->splitk;
+  a.splits = splits;
+  a.k_per_split = kps;
+  a.split_stride = outn;
+  if (!gemm_site(c, site, LAYOUT_TN, EPI_PARTIAL, a, bytes)) return false;
+  splitk_reduce_add(out, c->splitk, splits, outn, outn, c->stream);
+  return true;
+}
+
+int hip_status() {
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) {
+    fprintf(stderr, "gpt2: HIP error: %s\n", hipGetErrorString(e));
+    return GPT2_ERR_HIP;
+  }
+  return GPT2_OK;
+}
+
+template <typename TA>
+int forward_impl(gpt2_ctx* c, const int32_t* d_idx, const int32_t* d_tgt, int B, int T, float loss_scale,
+                 float* d_loss, bool accumulate) {
+  hipStream_t s = c->stream;
+  const int M = B * T, C = c->C, L = c->L, Vp = c->Vp;
+  const double a = (double)c->act;
+  embed_fwd(d_idx, c->P(T_WTE), c->P(T_WPE), c->resid(0), c->ids, M, T, C, c->V, c->err_flag, s);
+  for (int l = 0; l < L; ++l) {
+    float* x_in = c->resid(2 * l);
+    float* x_mid = c->resid(2 * l + 1);
+    float* x_out = c->resid(2 * l + 2);
+    TA* ln1 = (TA*)c->layer_act(c->ln1, l, C);
+    TA* qkv = (TA*)c->layer_act(c->qkv, l, 3 * C);
+    TA* atty = (TA*)c->layer_act(c->atty, l, C);
+    TA* ln2 = (TA*)c->layer_act(c->ln2, l, C);
+    TA* fcu = (TA*)c->layer_act(c->fcu, l, 4 * C);
+    TA* fcg = (TA*)c->layer_act(c->fcg, l, 4 * C);
+    float* lse = c->lse + (int64_t)l * c->Mmax * c->NH;
+    {
+      Timed tm(c, "ln.fwd", 0, (double)M * C * (4 + a) + 8.0 * M);
+      layernorm_fwd<TA>(x_in, c->P(T_LN1W, l), c->P(T_LN1B, l), ln1, c->ln1_mean + (int64_t)l * c->Mmax,
+                        c->ln1_rstd + (int64_t)l * c->Mmax, M, C, s);
+    }
+    GemmArgs g = gargs(ln1, C, c->W(T_QKVW, l), C, M, 3 * C, C, qkv, 3 * C);
+    g.bias = c->P(T_QKVB, l);
+    if (!gemm_site(c, "gemm.fwd.qkv", LAYOUT_NT, EPI_ACT, g, a * ((double)M * C + 3.0 * C * C + 3.0 * M * C)))
+      return GPT2_ERR_ARG;
+    {
+      Timed tm(c, "attn.fwd", 4.0 * B * c->NH * ((double)T * (T + 1) / 2) * (C / c->NH),
+               a * (4.0 * M * C) + 4.0 * M * c->NH);
+      if (c->bf16) attn_fwd_bf16(qkv, atty, lse, B, T, c->NH, C, s);
+      else attn_fwd_f32((const float*)qkv, (float*)atty, lse, B, T, c->NH, C, s);
+    }
+    g = gargs(atty, C, c->W(T_PROJW, l), C, M, C, C, x_mid, C);
+    g.bias = c->P(T_PROJB, l);
+    g.resid = x_in;
+    if (!gemm_site(c, "gemm.fwd.proj", LAYOUT_NT, EPI_RESID, g, a * ((double)M * C + (double)C * C) + 8.0 * M * C))
+      return GPT2_ERR_ARG;
+    {
+      Timed tm(c, "ln.fwd", 0, (double)M * C * (4 + a) + 8.0 * M);
+      layernorm_fwd<TA>(x_mid, c->P(T_LN2W, l), c->P(T_LN2B, l), ln2, c->ln2_mean + (int64_t)l * c->Mmax,
+                        c->ln2_rstd + (int64_t)l * c->Mmax, M, C, s);
+    }
+    g = gargs(ln2, C, c->W(T_FCW, l), C, M, 4 * C, C, fcu, 4 * C);
+    g.bias = c->P(T_FCB, l);
+    g.C2 = fcg;
+    if (!gemm_site(c, "gemm.fwd.fc", LAYOUT_NT, EPI_GELU, g, a * ((double)M * C + 4.0 * C * C + 8.0 * M * C)))
+      return GPT2_ERR_ARG;
+    g = gargs(fcg, 4 * C, c->W(T_FCPW, l), 4 * C, M, C, 4 * C, x_out, C);
+    g.bias = c->P(T_FCPB, l);
+    g.resid = x_mid;
+    if (!gemm_site(c, "gemm.fwd.fcproj", LAYOUT_NT, EPI_RESID, g,
+                   a * (4.0 * M * C + 4.0 * C * C) + 8.0 * M * C))
+      return GPT2_ERR_ARG;
+  }
+  {
+    Timed tm(c, "ln.fwd", 0, (double)M * C * (4 + a) + 8.0 * M);
+    layernorm_fwd<TA>(c->resid(2 * L), c->P(T_LNFW), c->P(T_LNFB), (TA*)c->lnf, c->lnf_mean, c->lnf_rstd, M, C, s);
+  }
+  GemmArgs g = gargs(c->lnf, C, c->W(T_WTE), C, M, Vp, C, c->logits, Vp);
+  if (!gemm_site(c, "gemm.fwd.lmhead", LAYOUT_NT, EPI_ACT, g, a * ((double)M * C + (double)Vp * C + (double)M * Vp)))
+    return GPT2_ERR_ARG;
+  {
+    Timed tm(c, "xent", 0, 2.0 * a * M * Vp + 8.0 * M);
+    xent_fwd_bwd<TA>((TA*)c->logits, d_tgt, c->row_loss, M, Vp, c->V, loss_scale / (float)M, c->err_flag, s);
+  }
+  loss_reduce(c->row_loss, M, loss_scale / (float)M, accumulate, d_loss, s);
+  c->have_fwd = true;
+  c->B = B;
+  c->T = T;
+  return hip_status();
+}
+
+template <typename TA>
+int backward_impl(gpt2_ctx* c) {
+  hipStream_t s = c->stream;
+  const int B = c->B, T = c->T, M = B * T, C = c->C, L = c->L, Vp = c->Vp;
+  const double a = (double)c->act;
+  float* part = c->colpart;
+  // lm_head (tied): dlnf = dz wte; dwte += dz^T lnf
+  GemmArgs g = gargs(c->logits, Vp, c->W(T_WTE), C, M, C, Vp, c->dh, C);
+  if (!gemm_site(c, "gemm.bwd.lmhead.dx", LAYOUT_NN, EPI_F32, g, a * ((double)M * Vp + (double)Vp * C) + 4.0 * M * C))
+    return GPT2_ERR_ARG;
+  if (!weight_grad(c, "gemm.bwd.lmhead.dw", c->G(T_WTE), c->logits, Vp, c->lnf, C, Vp, C, M)) return GPT2_ERR_ARG;
+  int ch;
+  {
+    Timed tm(c, "ln.bwd", 0, (double)M * C * (12 + a) + 8.0 * M);
+    ch = layernorm_bwd<TA>(c->dh, c->resid(2 * L), c->lnf_mean, c->lnf_rstd, c->P(T_LNFW), c->dres, false,
+                           (TA*)c->dres_act, part, M, C, s);
+  }
+  colpart_reduce_add(c->G(T_LNFW), part, ch, C, C, s);
+  colpart_reduce_add(c->G(T_LNFB), part + (int64_t)ch * C, ch, C, C, s);
+  colpart_reduce_add(c->G(T_FCPB, L - 1), part + 2 * (int64_t)ch * C, ch, C, C, s);
+
+  for (int l = L - 1; l >= 0; --l) {
+    TA* ln1 = (TA*)c->layer_act(c->ln1, l, C);
+    TA* qkv = (TA*)c->layer_act(c->qkv, l, 3 * C);
+    TA* atty = (TA*)c->layer_act(c->atty, l, C);
+    TA* ln2 = (TA*)c->layer_act(c->ln2, l, C);
+    TA* fcu = (TA*)c->layer_act(c->fcu, l, 4 * C);
+    TA* fcg = (TA*)c->layer_act(c->fcg, l, 4 * C);
+    float* lse = c->lse + (int64_t)l * c->Mmax * c->NH;
+    TA* dres_act = (TA*)c->dres_act;
+    TA* dbig = (TA*)c->dbig;
+    TA* dqkv = (TA*)c->dqkv;
+    TA* dy = (TA*)c->dy;
+
+    // MLP output projection: x_out = x_mid + g Wfp^T + bfp
+    if (!weight_grad(c, "gemm.bwd.fcproj.dw", c->G(T_FCPW, l), dres_act, C, fcg, 4 * C, C, 4 * C, M))
+      return GPT2_ERR_ARG;
+    g = gargs(dres_act, C, c->W(T_FCPW, l), 4 * C, M, 4 * C, C, dbig, 4 * C);
+    g.aux = fcu;
+    if (!gemm_site(c, "gemm.bwd.fcproj.dx", LAYOUT_NN, EPI_GELU_BWD, g, a * ((double)M * C + 4.0 * C * C + 8.0 * M * C)))
+      return GPT2_ERR_ARG;
+    ch = colsum_partials<TA>(dbig, M, 4 * C, part, s);
+    colpart_reduce_add(c->G(T_FCB, l), part, ch, 4 * C, 4 * C, s);
+    // MLP input projection: u = LN2(x_mid) Wfc^T + bfc
+    if (!weight_grad(c, "gemm.bwd.fc.dw", c->G(T_FCW, l), dbig, 4 * C, ln2, C, 4 * C, C, M)) return GPT2_ERR_ARG;
+    g = gargs(dbig, 4 * C, c->W(T_FCW, l), C, M, C, 4 * C, c->dh, C);
+    if (!gemm_site(c, "gemm.bwd.fc.dx", LAYOUT_NN, EPI_F32, g, a * (4.0 * M * C + 4.0 * C * C) + 4.0 * M * C))
+      return GPT2_ERR_ARG;
+    {
+      Timed tm(c, "ln.bwd", 0, (double)M * C * (16 + a) + 8.0 * M);
+      ch = layernorm_bwd<TA>(c->dh, c->resid(2 * l + 1), c->ln2_mean + (int64_t)l * c->Mmax,
+                             c->ln2_rstd + (int64_t)l * c->Mmax, c->P(T_LN2W, l), c->dres, true, dres_act, part, M,
+                             C, s);
+    }
+    colpart_reduce_add(c->G(T_LN2W, l), part, ch, C, C, s);
+    colpart_reduce_add(c->G(T_LN2B, l), part + (int64_t)ch * C, ch, C, C, s);
+    colpart_reduce_add(c->G(T_PROJB, l), part + 2 * (int64_t)ch * C, ch, C, C, s);
+    // attention output projection: x_mid = x_in + y Wp^T + bp
+    if (!weight_grad(c, "gemm.bwd.proj.dw", c->G(T_PROJW, l), dres_act, C, atty, C, C, C, M)) return GPT2_ERR_ARG;
+    g = gargs(dres_act, C, c->W(T_PROJW, l), C, M, C, C, dy, C);
+    if (!gemm_site(c, "gemm.bwd.proj.dx", LAYOUT_NN, EPI_ACT, g, a * (2.0 * M * C + (double)C * C)))
+      return GPT2_ERR_ARG;
+    {
+      Timed tm(c, "attn.bwd", 10.0 * B * c->NH * ((double)T * (T + 1) / 2) * (C / c->NH),
+               a * (9.0 * M * C) + 8.0 * M * c->NH);
+      if (c->bf16) attn_bwd_bf16(qkv, atty, dy, lse, c->attnD, dqkv, B, T, c->NH, C, s);
+      else attn_bwd_f32((const float*)qkv, (const float*)atty, (const float*)dy, lse, c->attnD, (float*)dqkv, B, T,
+                        c->NH, C, s);
+    }
+    ch = colsum_partials<TA>(dqkv, M, 3 * C, part, s);
+    colpart_reduce_add(c->G(T_QKVB, l), part, ch, 3 * C, 3 * C, s);
+    // QKV projection: qkv = LN1(x_in) Wqkv^T + bqkv
+    if (!weight_grad(c, "gemm.bwd.qkv.dw", c->G(T_QKVW, l), dqkv, 3 * C, ln1, C, 3 * C, C, M)) return GPT2_ERR_ARG;
+    g = gargs(dqkv, 3 * C, c->W(T_QKVW, l), C, M, C, 3 * C, c->dh, C);
+    if (!gemm_site(c, "gemm.bwd.qkv.dx", LAYOUT_NN, EPI_F32, g, a * (3.0 * M * C + 3.0 * C * C) + 4.0 * M * C))
+      return GPT2_ERR_ARG;
+    {
+      Timed tm(c, "ln.bwd", 0, (double)M * C * (16 + a) + 8.0 * M);
+      ch = layernorm_bwd<TA>(c->dh, c->resid(2 * l), c->ln1_mean + (int64_t)l * c->Mmax,
+                             c->ln1_rstd + (int64_t)l * c->Mmax, c->P(T_LN1W, l), c->dres, true, dres_act, part, M,
+                             C, s);
+    }
+    colpart_reduce_add(c->G(T_LN1W, l), part, ch, C, C, s);
+    colpart_reduce_add(c->G(T_LN1B, l), part + (int64_t)ch * C, ch, C, C, s);
+    if (l > 0) colpart_reduce_add(c->G(T_FCPB, l - 1), part + 2 * (int64_t)ch * C, ch, C, C, s);
+  }
+  // embedding: x0 = wte[idx] + wpe[t]
+  {
+    Timed tm(c, "embed.bwd", 0, 12.0 * M * C);
+    embed_wpe_grad(c->dres, c->G(T_WPE), B, T, C, s);
+    embed_sort(c->ids, M, c->Vp, c->id_bits, c->sort_ka, c->sort_va, c->sort_kb, c->sort_vb, s);
+    const bool in_a = ((c->id_bits + 3) / 4) % 2 == 1;
+    embed_scatter(in_a ? c->sort_ka : c->sort_kb, in_a ? c->sort_va : c->sort_vb, c->dres, c->run_sums,
+                  c->G(T_WTE), M, C, s);
+  }
+  c->have_fwd = false;
+  return hip_status();
+}
+
+int check_bt(const gpt2_ctx* c, int B, int T) {
+  if (T > c->cfg.block_size) return GPT2_ERR_SEQ_TOO_LONG;
+  if (B < 1 || T < 1 || B > c->cfg.max_batch) return GPT2_ERR_BATCH;
+  return GPT2_OK;
+}
+
+int64_t plan_workspace(gpt2_ctx* c, Plan& p, bool assign) {
+  const int64_t M = c->Mmax, C = c->C, L = c->L, A = c->act, Vp = c->Vp, NH = c->NH;
+  char* base = (char*)c->buf.workspace;
+  auto at = [&](int64_t bytes) -> char* {
+    const int64_t o = p.take(bytes);
+    return assign ? base + o : nullptr;
+  };
+  c->res = (float*)at((2 * L + 1) * M * C * 4);
+  c->ln1 = at(L * M * C * A);
+  c->ln1_mean = (float*)at(L * M * 4);
+  c->ln1_rstd = (float*)at(L * M * 4);
+  c->qkv = at(L * M * 3 * C * A);
+  c->atty = at(L * M * C * A);
+  c->lse = (float*)at(L * M * NH * 4);
+  c->ln2 = at(L * M * C * A);
+  c->ln2_mean = (float*)at(L * M * 4);
+  c->ln2_rstd = (float*)at(L * M * 4);
+  c->fcu = at(L * M * 4 * C * A);
+  c->fcg = at(L * M * 4 * C * A);
+  c->lnf = at(M * C * A);
+  c->lnf_mean = (float*)at(M * 4);
+  c->lnf_rstd = (float*)at(M * 4);
+  c->logits = at(M * Vp * A);
+  c->row_loss = (float*)at(M * 4);
+  c->ids = (int32_t*)at(M * 4);
+  c->dres = (float*)at(M * C * 4);
+  c->dres_act = at(M * C * A);
+  c->dh = (float*)at(M * C * 4);
+  c->dbig = at(M * 4 * C * A);
+  c->dqkv = at(M * 3 * C * A);
+  c->dy = at(M * C * A);
+  c->attnD = (float*)at(M * NH * 4);
+  c->splitk_elems = 16 * 4 * C * C;
+  c->splitk = (float*)at(c->splitk_elems * 4);
+  const int64_t col_elems = std::max<int64_t>(3 * ((M + 31) / 32) * C, ((M + 63) / 64) * 4 * C);
+  c->colpart = (float*)at(col_elems * 4);
+  c->sort_ka = (int32_t*)at(M * 4);
+  c->sort_va = (int32_t*)at(M * 4);
+  c->sort_kb = (int32_t*)at(M * 4);
+  c->sort_vb = (int32_t*)at(M * 4);
+  c->run_sums = (float*)at(M * C * 4);
+  c->norm_part = (double*)at(1024 * 8);
+  c->clip_scale = (float*)at(256);
+  c->err_flag = (int*)at(256);
+  return p.bytes;
+}
+
+void fill_layout(gpt2_ctx* c, const gpt2_config& cfg) {
+  c->cfg = cfg;
+  tensor_table(cfg, c->t);
+  c->n_params = total_params(c->t);
+  c->bf16 = cfg.precision == GPT2_BF16;
+  c->act = c->bf16 ? 2 : 4;
+  c->Mmax = (int64_t)cfg.max_batch * cfg.block_size;
+  c->L = cfg.n_layer;
+  c->C = cfg.n_embd;
+  c->NH = cfg.n_head;
+  c->Vp = cfg.padded_vocab_size;
+  c->V = cfg.vocab_size;
+  int bits = 1;
+  while ((1 << bits) < cfg.padded_vocab_size) ++bits;
+  c->id_bits = bits;
+}
+
+}  // namespace
+
+extern "C" {
+
+int gpt2_init(const gpt2_config* cfg, const gpt2_buffers* bufs, void* hip_stream, gpt2_sizes* sizes,
+              gpt2_ctx** out) {
+  if (!cfg || !config_ok(*cfg)) return GPT2_ERR_ARG;
+  gpt2_ctx probe;
+  fill_layout(&probe, *cfg);
+  Plan plan;
+  const int64_t ws = plan_workspace(&probe, plan, false);
+  if (sizes) {
+    sizes->n_params = probe.n_params;
+    sizes->workspace_bytes = ws;
+    sizes->params_bf16_bytes = probe.bf16 ? probe.n_params * 2 : 0;
+  }
+  if (!bufs) return GPT2_OK;
+  if (!out || !bufs->params || !bufs->grads || !bufs->adam_m || !bufs->adam_v || !bufs->workspace)
+    return GPT2_ERR_ARG;
+  if (probe.bf16 && !bufs->params_bf16) return GPT2_ERR_ARG;
+  if (((uintptr_t)bufs->workspace) % 256) return GPT2_ERR_ARG;
+  gpt2_ctx* c = new gpt2_ctx();
+  fill_layout(c, *cfg);
+  c->buf = *bufs;
+  if (!c->bf16) c->buf.params_bf16 = nullptr;
+  c->stream = (hipStream_t)hip_stream;
+  Plan p2;
+  plan_workspace(c, p2, true);
+  fill_f32(c->buf.grads, c->n_params, 0.f, c->stream);
+  fill_f32(c->buf.adam_m, c->n_params, 0.f, c->stream);
+  fill_f32(c->buf.adam_v, c->n_params, 0.f, c->stream);
+  fill_f32((float*)c->err_flag, 1, 0.f, c->stream);
+  if (c->bf16) to_bf16(c->buf.params, c->buf.params_bf16, c->n_params, c->stream);
+  const int st = hip_status();
+  if (st != GPT2_OK) {
+    delete c;
+    return st;
+  }
+  *out = c;
+  return GPT2_OK;
+}
+
+int gpt2_forward_loss(gpt2_ctx* c, const int32_t* d_idx, const int32_t* d_targets, int B, int T, float loss_scale,
+                      float* d_loss) {
+  if (!c || !d_idx || !d_targets || !d_loss) return GPT2_ERR_ARG;
+  const int e = check_bt(c, B, T);
+  if (e != GPT2_OK) return e;
+  return c->bf16 ? forward_impl<bf16>(c, d_idx, d_targets, B, T, loss_scale, d_loss, false)
+                 : forward_impl<float>(c, d_idx, d_targets, B, T, loss_scale, d_loss, false);
+}
+
+int gpt2_backward(gpt2_ctx* c) {
+  if (!c) return GPT2_ERR_ARG;
+  if (!c->have_fwd) return GPT2_ERR_STATE;
+  return c->bf16 ? backward_impl<bf16>(c) : backward_impl<float>(c);
+}
+
+int gpt2_accumulate(gpt2_ctx* c, const int32_t* d_idx, const int32_t* d_targets, int k, int B, int T,
+                    float* d_mean_loss) {
+  if (!c || !d_idx || !d_targets || !d_mean_loss) return GPT2_ERR_ARG;
+  if (k < 1) return GPT2_ERR_BATCH;
+  int e = check_bt(c, B, T);
+  if (e != GPT2_OK) return e;
+  fill_f32(c->buf.grads, c->n_params, 0.f, c->stream);
+  const int64_t stride = (int64_t)B * T;
+  for (int i = 0; i < k; ++i) {
+    e = c->bf16 ? forward_impl<bf16>(c, d_idx + i * stride, d_targets + i * stride, B, T, 1.0f / k, d_mean_loss,
+                                     i > 0)
+                : forward_impl<float>(c, d_idx + i * stride, d_targets + i * stride, B, T, 1.0f / k, d_mean_loss,
+                                      i > 0);
+    if (e != GPT2_OK) return e;
+    e = gpt2_backward(c);
+    if (e != GPT2_OK) return e;
+  }
+  return GPT2_OK;
+}
+
+int gpt2_clip_adamw_step(gpt2_ctx* c, float lr, float beta1, float beta2, float eps, float weight_decay,
+                         float max_norm, float* d_norm, int32_t* d_clipped) {
+  if (!c || !d_norm || !d_clipped) return GPT2_ERR_ARG;
+  hipStream_t s = c->stream;
+  {
+    Timed tm(c, "norm", 0, 4.0 * c->n_params);
+    const int nblk = sumsq_partials(c->buf.grads, c->n_params, c->norm_part, s);
+    clip_finalize(c->norm_part, nblk, max_norm, d_norm, d_clipped, c->clip_scale, s);
+  }
+  c->step += 1;
+  const double bc1 = 1.0 - std::pow((double)beta1, (double)c->step);
+  const double bc2 = 1.0 - std::pow((double)beta2, (double)c->step);
+  DecaySegments seg;
+  memset(&seg, 0, sizeof(seg));
+  for (int i = 0; i < T_COUNT; ++i) {
+    if (seg.n == 0 || seg.decay[seg.n - 1] != (int)c->t[i].decay) {
+      seg.start[seg.n] = c->t[i].off;
+      seg.decay[seg.n] = c->t[i].decay;
+      ++seg.n;
+    }
+  }
+  seg.start[seg.n] = c->n_params;
+  {
+    Timed tm(c, "adamw", 0, (c->bf16 ? 30.0 : 28.0) * c->n_params);
+    adamw(c->buf.params, c->buf.grads, c->buf.adam_m, c->buf.adam_v, c->buf.params_bf16, c->n_params, seg,
+          c->clip_scale, lr, beta1, beta2, eps, weight_decay, (float)(1.0 / bc1), (float)(1.0 / bc2), s);
+  }
+  return hip_status();
+}
+
+void gpt2_destroy(gpt2_ctx* c) {
+  if (!c) return;
+  for (hipEvent_t e : c->ev) (void)hipEventDestroy(e);
+  delete c;
+}
+
+int gpt2_sync_status(gpt2_ctx* c) {
+  if (!c) return GPT2_ERR_ARG;
+  if (hipStreamSynchronize(c->stream) != hipSuccess) return GPT2_ERR_HIP;
+  int flag = 0;
+  if (hipMemcpy(&flag, c->err_flag, sizeof(int), hipMemcpyDeviceToHost) != hipSuccess) return GPT2_ERR_HIP;
+  if (flag) {
+    fill_f32((float*)c->err_flag, 1, 0.f, c->stream);
+    if (hipStreamSynchronize(c->stream) != hipSuccess) return GPT2_ERR_HIP;
+    return GPT2_ERR_TOKEN;
+  }
+  return hip_status();
+}
+
+int gpt2_sync_params(gpt2_ctx* c) {
+  if (!c) return GPT2_ERR_ARG;
+  if (c->bf16) to_bf16(c->buf.params, c->buf.params_bf16, c->n_params, c->stream);
+  return hip_status();
+}
+
+int64_t gpt2_get_step(const gpt2_ctx* c) { return c ? c->step : -1; }
+
+int gpt2_set_step(gpt2_ctx* c, int64_t t) {
+  if (!c || t < 0) return GPT2_ERR_ARG;
+  c->step = t;
+  return GPT2_OK;
+}
+
+int gpt2_tensor_info(const gpt2_config* cfg, int index, const char** name, int64_t* offset, int64_t* numel,
+                     int32_t* ndim, int64_t* dims) {
+  if (!cfg || !config_ok(*cfg) || index < 0 || index >= T_COUNT) return GPT2_ERR_ARG;
+  TensorDesc t[T_COUNT];
+  tensor_table(*cfg, t);
+  if (name) *name = kTensorNames[index];
+  if (offset) *offset = t[index].off;
+  if (numel) *numel = t[index].numel;
+  if (ndim) *ndim = t[index].ndim;
+  if (dims)
+    for (int i = 0; i < 3; ++i) dims[i] = i < t[index].ndim ? t[index].dims[i] : 0;
+  return GPT2_OK;
+}
+
+int gpt2_activation(gpt2_ctx* c, const char* name, int layer, void** ptr, int64_t* numel, int32_t* dtype) {
+  if (!c || !name || !ptr || !numel || !dtype) return GPT2_ERR_ARG;
+  const int64_t M = (int64_t)c->B * c->T, C = c->C;
+  const int32_t at = c->bf16 ? 1 : 0;
+  const bool lay_ok = layer >= 0 && layer < c->L;
+  auto ret = [&](void* p, int64_t n, int32_t d) {
+    *ptr = p;
+    *numel = n;
+    *dtype = d;
+    return GPT2_OK;
+  };
+  const std::string n(name);
+  if (n == "resid" && layer >= 0 && layer <= 2 * c->L) return ret(c->resid(layer), M * C, 0);
+  if (n == "lnf") return ret(c->lnf, M * C, at);
+  if (n == "logits") return ret(c->logits, M * c->Vp, at);
+  if (n == "row_loss") return ret(c->row_loss, M, 0);
+  if (n == "dresid") return ret(c->dres, M * C, 0);
+  const bool in_a = ((c->id_bits + 3) / 4) % 2 == 1;
+  if (n == "emb_sorted_ids") return ret(in_a ? c->sort_ka : c->sort_kb, M, 2);
+  if (n == "emb_sorted_pos") return ret(in_a ? c->sort_va : c->sort_vb, M, 2);
+  if (!lay_ok) return GPT2_ERR_ARG;
+  if (n == "ln1") return ret(c->layer_act(c->ln1, layer, C), M * C, at);
+  if (n == "ln1_mean") return ret(c->ln1_mean + (int64_t)layer * c->Mmax, M, 0);
+  if (n == "ln1_rstd") return ret(c->ln1_rstd + (int64_t)layer * c->Mmax, M, 0);
+  if (n == "qkv") return ret(c->layer_act(c->qkv, layer, 3 * C), M * 3 * C, at);
+  if (n == "atty") return ret(c->layer_act(c->atty, layer, C), M * C, at);
+  if (n == "lse") return ret(c->lse + (int64_t)layer * c->Mmax * c->NH, M * c->NH, 0);
+  if (n == "ln2") return ret(c->layer_act(c->ln2, layer, C), M * C, at);
+  if (n == "fcu") return ret(c->layer_act(c->fcu, layer, 4 * C), M * 4 * C, at);
+  if (n == "fcg") return ret(c->layer_act(c->fcg, layer, 4 * C), M * 4 * C, at);
+  return GPT2_ERR_ARG;
+}
+
+int gpt2_timing_enable(gpt2_ctx* c, const char* site) {
+  if (!c) return GPT2_ERR_ARG;
+  c->ev_used = 0;
+  c->ev_overflow = false;
+  c->ev_flops.clear();
+  c->ev_bytes.clear();
+  c->timing = site != nullptr;
+  c->site = site ? site : "";
+  return GPT2_OK;
+}
+
+int gpt2_timing_read(gpt2_ctx* c, double* total_ms, int64_t* launches, double* flops, double* bytes) {
+  if (!c || !total_ms || !launches || !flops || !bytes) return GPT2_ERR_ARG;
+  if (hipStreamSynchronize(c->stream) != hipSuccess) return GPT2_ERR_HIP;
+  double ms = 0, f = 0, b = 0;
+  for (size_t i = 0; i < c->ev_used; ++i) {
+    float t = 0.f;
+    if (hipEventElapsedTime(&t, c->ev[2 * i], c->ev[2 * i + 1]) != hipSuccess) return GPT2_ERR_HIP;
+    ms += t;
+    f += c->ev_flops[i];
+    b += c->ev_bytes[i];
+  }
+  *total_ms = ms;
+  *launches = (int64_t)c->ev_used;
+  *flops = f;
+  *bytes = b;
+  return c->ev_overflow ? GPT2_ERR_ARG : GPT2_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,111 @@
+// Host-side launchers of the gfx950 kernels of the GPT-2 step.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gpt2k {
+
+// ---- GEMM ---------------------------------------------------------------------
+// C[m][n] = sum_k A(m, k) B(k, n), fp32 accumulation, then an epilogue.
+enum GemmLayout {
+  LAYOUT_NT = 0,  // A stored [M][K], B stored [N][K]   (forward: x W^T)
+  LAYOUT_NN = 1,  // A stored [M][K], B stored [K][N]   (input gradient: dY W)
+  LAYOUT_TN = 2,  // A stored [K][M], B stored [K][N]   (weight gradient: dY^T X)
+};
+enum GemmEpilogue {
+  EPI_ACT = 0,       // C (activation type) = acc (+ bias[n] if bias)
+  EPI_F32 = 1,       // C (fp32) = acc
+  EPI_F32_ACC = 2,   // C (fp32) += acc
+  EPI_RESID = 3,     // C (fp32) = resid + acc + bias[n]
+  EPI_GELU = 4,      // u = acc + bias[n] -> C (act), gelu(u) -> C2 (act)
+  EPI_GELU_BWD = 5,  // C (act) = acc * gelu'(aux[m][n])
+  EPI_PARTIAL = 6,   // C (fp32) + split * split_stride = acc (split-K partial)
+};
+struct GemmArgs {
+  const void* A;
+  const void* B;
+  int M, N, K;
+  int64_t lda, ldb, ldc;
+  void* C;
+  void* C2;
+  const float* bias;
+  const float* resid;
+  const void* aux;
+  int splits;
+  int k_per_split;
+  int64_t split_stride;
+};
+// Returns false if the shape breaks a kernel precondition.
+bool gemm(GemmLayout layout, GemmEpilogue epi, bool bf16_mode, const GemmArgs& a, hipStream_t s);
+// out[i] += sum_{s < splits} part[s * stride + i], i < count (fixed order).
+void splitk_reduce_add(float* out, const float* part, int splits, int64_t stride, int64_t count,
+                       hipStream_t s);
+
+// ---- embedding ---------------------------------------------------------------
+// x[m][:] = wte[idx[m]][:] + wpe[m % T][:]; out-of-range ids set *err and use row 0;
+// ids_out[m] receives the id used.
+void embed_fwd(const int32_t* idx, const float* wte, const float* wpe, float* x, int32_t* ids_out, int M, int T,
+               int C, int vocab, int* err, hipStream_t s);
+// Stable sort of (idx[m], m) by id: LSD radix, 4-bit digits, one workgroup.
+void embed_sort(const int32_t* idx, int M, int vocab, int id_bits, int32_t* keys_a, int32_t* vals_a,
+                int32_t* keys_b, int32_t* vals_b, hipStream_t s);
+// dwte[id] += sum over positions with that id of dx[pos] (in position order);
+// run_sums: M x C fp32 scratch.
+void embed_scatter(const int32_t* sorted_ids, const int32_t* sorted_pos, const float* dx, float* run_sums,
+                   float* dwte, int M, int C, hipStream_t s);
+// dwpe[t] += sum_b dx[b * T + t].
+void embed_wpe_grad(const float* dx, float* dwpe, int B, int T, int C, hipStream_t s);
+
+// ---- LayerNorm -------------------------------------------------------------------
+template <typename TA>
+void layernorm_fwd(const float* x, const float* w, const float* b, TA* y, float* mean, float* rstd, int M,
+                   int C, hipStream_t s);
+// dres (fp32, in place) = (dres_in ? dres : 0) + dx;  dres_act = dres as TA.
+// Partial column sums per row chunk: part[0][chunk][C] = sum dy*xhat, part[1] = sum dy,
+// part[2] = sum dres_out.  Returns the number of chunks.
+template <typename TA>
+int layernorm_bwd(const float* dy, const float* x, const float* mean, const float* rstd, const float* w,
+                  float* dres, bool dres_in, TA* dres_act, float* part, int M, int C, hipStream_t s);
+// out[n] += sum_c part[c * ld + n], c < chunks, n < N.
+void colpart_reduce_add(float* out, const float* part, int chunks, int64_t ld, int N, hipStream_t s);
+// Column sums of an activation matrix (M x N, row-major) into partials [chunks][N];
+// returns the number of chunks.
+template <typename TA>
+int colsum_partials(const TA* x, int M, int N, float* part, hipStream_t s);
+
+// ---- attention ---------------------------------------------------------------------
+// qkv: [B*T][3C]; y: [B*T][C]; lse: [B][NH][T] (natural log).
+void attn_fwd_bf16(const void* qkv, void* y, float* lse, int B, int T, int NH, int C, hipStream_t s);
+void attn_bwd_bf16(const void* qkv, const void* y, const void* dy, const float* lse, float* Dbuf, void* dqkv,
+                   int B, int T, int NH, int C, hipStream_t s);
+void attn_fwd_f32(const float* qkv, float* y, float* lse, int B, int T, int NH, int C, hipStream_t s);
+void attn_bwd_f32(const float* qkv, const float* y, const float* dy, const float* lse, float* Dbuf,
+                  float* dqkv, int B, int T, int NH, int C, hipStream_t s);
+
+// ---- cross-entropy ---------------------------------------------------------------
+// Per row: loss_row = logsumexp(z) - z[y]; z <- (softmax(z) - onehot(y)) * grad_scale in place.
+template <typename TA>
+void xent_fwd_bwd(TA* logits, const int32_t* targets, float* row_loss, int M, int V, int vocab,
+                  float grad_scale, int* err, hipStream_t s);
+// *out = (accumulate ? *out : 0) + scale * sum(row_loss[0..M)) (fixed order).
+void loss_reduce(const float* row_loss, int M, float scale, bool accumulate, float* out, hipStream_t s);
+
+// ---- optimizer ---------------------------------------------------------------------
+void fill_f32(float* p, int64_t n, float v, hipStream_t s);
+void to_bf16(const float* src, void* dst, int64_t n, hipStream_t s);
+// Sum of squares into nblk fp64 partials; returns nblk.
+int sumsq_partials(const float* g, int64_t n, double* part, hipStream_t s);
+// norm = sqrt(sum part); coef = max_norm / (norm + 1e-6); clipped = coef < 1.
+void clip_finalize(const double* part, int nblk, float max_norm, float* d_norm, int32_t* d_clipped,
+                   float* scale_out, hipStream_t s);
+struct DecaySegments {
+  int n;
+  int64_t start[24];  // segment i covers [start[i], start[i+1]) (start[n] = total)
+  int decay[24];
+};
+void adamw(float* p, const float* g, float* m, float* v, void* p_bf16, int64_t n, const DecaySegments& seg,
+           const float* grad_scale, float lr, float beta1, float beta2, float eps, float wd, float inv_bc1,
+           float inv_bc2, hipStream_t s);
+
+}  // namespace gpt2k

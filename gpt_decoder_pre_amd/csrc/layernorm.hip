@@ -1,0 +1,230 @@
+// LayerNorm forward / backward and column-sum reductions (HBM-bound).
+//
+// One wavefront per row: the row stays in registers (float4 per lane, up to
+// C = 2048), mean and variance are wavefront-shuffle reductions, biased
+// variance, eps = 1e-5.  Column sums (gain / shift / bias gradients) are
+// deterministic: fixed row chunks per block write partial rows, a second
+// kernel adds the partials in chunk order.
+#include "common.h"
+#include "kernels.h"
+
+namespace gpt2k {
+
+constexpr float kLnEps = 1e-5f;
+constexpr int kMaxV = 8;  // float4 chunks per lane: C <= 64 * 4 * 8
+
+template <typename TA>
+__global__ __launch_bounds__(256) void ln_fwd_kernel(const float* __restrict__ x, const float* __restrict__ w,
+                                                     const float* __restrict__ b, TA* __restrict__ y,
+                                                     float* __restrict__ mean, float* __restrict__ rstd, int M,
+                                                     int C) {
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= M) return;
+  const int C4 = C >> 2;
+  const float* xr = x + (int64_t)row * C;
+  float v[kMaxV][4];
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < kMaxV; ++i) {
+    const int c4 = lane + i * 64;
+    if (c4 < C4) {
+      load4(xr + 4 * c4, v[i]);
+      s += (v[i][0] + v[i][1]) + (v[i][2] + v[i][3]);
+    }
+  }
+  const float mu = wave_sum(s) / (float)C;
+  float q = 0.f;
+#pragma unroll
+  for (int i = 0; i < kMaxV; ++i) {
+    const int c4 = lane + i * 64;
+    if (c4 < C4) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float d = v[i][e] - mu;
+        q += d * d;
+      }
+    }
+  }
+  const float var = wave_sum(q) / (float)C;
+  const float rs = 1.0f / sqrtf(var + kLnEps);
+  TA* yr = y + (int64_t)row * C;
+#pragma unroll
+  for (int i = 0; i < kMaxV; ++i) {
+    const int c4 = lane + i * 64;
+    if (c4 < C4) {
+      float ww[4], bb[4], o[4];
+      load4(w + 4 * c4, ww);
+      load4(b + 4 * c4, bb);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) o[e] = (v[i][e] - mu) * rs * ww[e] + bb[e];
+      store4(yr + 4 * c4, o);
+    }
+  }
+  if (lane == 0) {
+    mean[row] = mu;
+    rstd[row] = rs;
+  }
+}
+
+template <typename TA>
+void layernorm_fwd(const float* x, const float* w, const float* b, TA* y, float* mean, float* rstd, int M,
+                   int C, hipStream_t s) {
+  ln_fwd_kernel<TA><<<(M + 3) / 4, 256, 0, s>>>(x, w, b, y, mean, rstd, M, C);
+}
+template void layernorm_fwd<float>(const float*, const float*, const float*, float*, float*, float*, int, int,
+                                   hipStream_t);
+template void layernorm_fwd<bf16>(const float*, const float*, const float*, bf16*, float*, float*, int, int,
+                                  hipStream_t);
+
+// dx = rstd (dxhat - mean(dxhat) - xhat mean(dxhat xhat)), dxhat = dy w.
+template <typename TA>
+__global__ __launch_bounds__(256) void ln_bwd_kernel(const float* __restrict__ dy, const float* __restrict__ x,
+                                                     const float* __restrict__ mean,
+                                                     const float* __restrict__ rstd,
+                                                     const float* __restrict__ w, float* __restrict__ dres,
+                                                     int dres_in, TA* __restrict__ dres_act,
+                                                     float* __restrict__ part, int M, int C, int rows_per_block,
+                                                     int chunks) {
+  __shared__ float red[3][2048];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int C4 = C >> 2;
+  const int r0 = blockIdx.x * rows_per_block;
+  const int r1 = min(M, r0 + rows_per_block);
+  float aw[kMaxV][4], ab[kMaxV][4], ar[kMaxV][4], ww[kMaxV][4];
+#pragma unroll
+  for (int i = 0; i < kMaxV; ++i) {
+    const int c4 = lane + i * 64;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) aw[i][e] = ab[i][e] = ar[i][e] = 0.f;
+    if (c4 < C4) load4(w + 4 * c4, ww[i]);
+  }
+  for (int row = r0 + wave; row < r1; row += 4) {
+    const float mu = mean[row], rs = rstd[row];
+    const float* dyr = dy + (int64_t)row * C;
+    const float* xr = x + (int64_t)row * C;
+    float g[kMaxV][4], xh[kMaxV][4];
+    float s1 = 0.f, s2 = 0.f;
+#pragma unroll
+    for (int i = 0; i < kMaxV; ++i) {
+      const int c4 = lane + i * 64;
+      if (c4 < C4) {
+        float xv[4];
+        load4(dyr + 4 * c4, g[i]);
+        load4(xr + 4 * c4, xv);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          xh[i][e] = (xv[e] - mu) * rs;
+          const float d = g[i][e] * ww[i][e];
+          s1 += d;
+          s2 += d * xh[i][e];
+          aw[i][e] += g[i][e] * xh[i][e];
+          ab[i][e] += g[i][e];
+        }
+      }
+    }
+    const float m1 = wave_sum(s1) / (float)C, m2 = wave_sum(s2) / (float)C;
+    float* dr = dres + (int64_t)row * C;
+    TA* da = dres_act + (int64_t)row * C;
+#pragma unroll
+    for (int i = 0; i < kMaxV; ++i) {
+      const int c4 = lane + i * 64;
+      if (c4 < C4) {
+        float o[4] = {0.f, 0.f, 0.f, 0.f};
+        if (dres_in) load4(dr + 4 * c4, o);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          o[e] += rs * (g[i][e] * ww[i][e] - m1 - xh[i][e] * m2);
+          ar[i][e] += o[e];
+        }
+        store4(dr + 4 * c4, o);
+        store4(da + 4 * c4, o);
+      }
+    }
+  }
+  // combine the four waves in a fixed order
+  for (int wv = 0; wv < 4; ++wv) {
+    if (wave == wv) {
+#pragma unroll
+      for (int i = 0; i < kMaxV; ++i) {
+        const int c4 = lane + i * 64;
+        if (c4 < C4) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int c = 4 * c4 + e;
+            if (wv == 0) {
+              red[0][c] = aw[i][e];
+              red[1][c] = ab[i][e];
+              red[2][c] = ar[i][e];
+            } else {
+              red[0][c] += aw[i][e];
+              red[1][c] += ab[i][e];
+              red[2][c] += ar[i][e];
+            }
+          }
+        }
+      }
+    }
+    __syncthreads();
+  }
+  for (int c = threadIdx.x; c < C; c += blockDim.x) {
+#pragma unroll
+    for (int k = 0; k < 3; ++k) part[((int64_t)k * chunks + blockIdx.x) * C + c] = red[k][c];
+  }
+}
+
+template <typename TA>
+int layernorm_bwd(const float* dy, const float* x, const float* mean, const float* rstd, const float* w,
+                  float* dres, bool dres_in, TA* dres_act, float* part, int M, int C, hipStream_t s) {
+  const int rpb = 32;
+  const int chunks = (M + rpb - 1) / rpb;
+  ln_bwd_kernel<TA><<<chunks, 256, 0, s>>>(dy, x, mean, rstd, w, dres, dres_in ? 1 : 0, dres_act, part, M, C,
+                                           rpb, chunks);
+  return chunks;
+}
+template int layernorm_bwd<float>(const float*, const float*, const float*, const float*, const float*, float*,
+                                  bool, float*, float*, int, int, hipStream_t);
+template int layernorm_bwd<bf16>(const float*, const float*, const float*, const float*, const float*, float*,
+                                 bool, bf16*, float*, int, int, hipStream_t);
+
+__global__ void colpart_reduce_kernel(float* out, const float* part, int chunks, int64_t ld, int N) {
+  const int n = blockIdx.x * blockDim.x + threadIdx.x;
+  if (n >= N) return;
+  float s = 0.f;
+  for (int c = 0; c < chunks; ++c) s += part[c * ld + n];
+  out[n] += s;
+}
+
+void colpart_reduce_add(float* out, const float* part, int chunks, int64_t ld, int N, hipStream_t s) {
+  colpart_reduce_kernel<<<(N + 255) / 256, 256, 0, s>>>(out, part, chunks, ld, N);
+}
+
+// Partial column sums: block (cb, chunk) covers 1024 columns x rows_per_chunk rows.
+template <typename TA>
+__global__ __launch_bounds__(256) void colsum_kernel(const TA* __restrict__ x, int M, int N, int rows_per_chunk,
+                                                     float* __restrict__ part) {
+  const int c = (blockIdx.x * 256 + threadIdx.x) * 4;
+  if (c >= N) return;
+  const int r0 = blockIdx.y * rows_per_chunk, r1 = min(M, r0 + rows_per_chunk);
+  float s[4] = {0.f, 0.f, 0.f, 0.f};
+  for (int r = r0; r < r1; ++r) {
+    float v[4];
+    load4(x + (int64_t)r * N + c, v);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) s[e] += v[e];
+  }
+  store4(part + (int64_t)blockIdx.y * N + c, s);
+}
+
+template <typename TA>
+int colsum_partials(const TA* x, int M, int N, float* part, hipStream_t s) {
+  const int rpc = 64;
+  const int chunks = (M + rpc - 1) / rpc;
+  dim3 grid((N / 4 + 255) / 256, chunks);
+  colsum_kernel<TA><<<grid, 256, 0, s>>>(x, M, N, rpc, part);
+  return chunks;
+}
+template int colsum_partials<float>(const float*, int, int, float*, hipStream_t);
+template int colsum_partials<bf16>(const bf16*, int, int, float*, hipStream_t);
+
+}  // namespace gpt2k

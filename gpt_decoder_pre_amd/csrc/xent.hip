@@ -1,0 +1,99 @@
+// Softmax cross-entropy over the padded vocabulary, fused with its gradient.
+//
+// One workgroup per row of logits.  Pass 1 keeps a running (max, sum of
+// exponentials) per thread (fp32, online softmax), combines them across the
+// block and forms the row's log-sum-exp; pass 2 overwrites the logits with
+// (softmax - onehot(target)) * grad_scale.  Max and sums stay in fp32 even
+// when the logits are bf16.
+#include "common.h"
+#include "kernels.h"
+
+namespace gpt2k {
+
+template <typename TA, int VEC>
+__global__ __launch_bounds__(256) void xent_kernel(TA* __restrict__ logits, const int32_t* __restrict__ targets,
+                                                   float* __restrict__ row_loss, int V, int vocab,
+                                                   float grad_scale, int* __restrict__ err) {
+  __shared__ float red[16];
+  __shared__ float red2[16];
+  const int row = blockIdx.x;
+  TA* z = logits + (int64_t)row * V;
+  int y = targets[row];
+  if (y < 0 || y >= vocab) {
+    if (threadIdx.x == 0) *err = 1;
+    y = 0;
+  }
+  float m = -INFINITY, s = 0.f;
+  const int nv = V / VEC;
+  for (int i = threadIdx.x; i < nv; i += blockDim.x) {
+    float v[VEC];
+    if constexpr (VEC == 8) {
+      load4(z + i * 8, v);
+      load4(z + i * 8 + 4, v + 4);
+    } else {
+      v[0] = to_f32(z[i]);
+    }
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) {
+      if (v[e] > m) {
+        s = s * exp_fast(m - v[e]) + 1.f;
+        m = v[e];
+      } else {
+        s += exp_fast(v[e] - m);
+      }
+    }
+  }
+  const float M = block_max(m, red);
+  const float S = block_sum(m == -INFINITY ? 0.f : s * exp_fast(m - M), red2);
+  const float lse = M + logf(S);
+  const float zy = to_f32(z[y]);
+  if (threadIdx.x == 0) row_loss[row] = lse - zy;
+  __syncthreads();
+  for (int i = threadIdx.x; i < nv; i += blockDim.x) {
+    float v[VEC];
+    if constexpr (VEC == 8) {
+      load4(z + i * 8, v);
+      load4(z + i * 8 + 4, v + 4);
+    } else {
+      v[0] = to_f32(z[i]);
+    }
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) {
+      const int col = i * VEC + e;
+      v[e] = (exp_fast(v[e] - lse) - (col == y ? 1.f : 0.f)) * grad_scale;
+    }
+    if constexpr (VEC == 8) {
+      store4(z + i * 8, v);
+      store4(z + i * 8 + 4, v + 4);
+    } else {
+      z[i] = from_f32<TA>(v[0]);
+    }
+  }
+}
+
+template <typename TA>
+void xent_fwd_bwd(TA* logits, const int32_t* targets, float* row_loss, int M, int V, int vocab, float grad_scale,
+                  int* err, hipStream_t s) {
+  if (V % 8 == 0) xent_kernel<TA, 8><<<M, 256, 0, s>>>(logits, targets, row_loss, V, vocab, grad_scale, err);
+  else xent_kernel<TA, 1><<<M, 256, 0, s>>>(logits, targets, row_loss, V, vocab, grad_scale, err);
+}
+template void xent_fwd_bwd<float>(float*, const int32_t*, float*, int, int, int, float, int*, hipStream_t);
+template void xent_fwd_bwd<bf16>(bf16*, const int32_t*, float*, int, int, int, float, int*, hipStream_t);
+
+__global__ __launch_bounds__(256) void loss_reduce_kernel(const float* __restrict__ row_loss, int M, float scale,
+                                                          int accumulate, float* out) {
+  __shared__ double red[16];
+  double s = 0.0;
+  for (int i = threadIdx.x; i < M; i += blockDim.x) s += (double)row_loss[i];
+  s = block_sum(s, red);
+  if (threadIdx.x == 0) {
+    const float v = (float)(s * (double)scale);
+    *out = accumulate ? *out + v : v;
+  }
+}
+
+void loss_reduce(const float* row_loss, int M, float scale, bool accumulate, float* out, hipStream_t s) {
+  loss_reduce_kernel<<<1, 256, 0, s>>>(row_loss, M, scale, accumulate ? 1 : 0, out);
+}
+
+}  // namespace gpt2k

@@ -1,0 +1,202 @@
+/*
+ * gpt2.h -- C ABI of one GPT-2 pre-training step on one AMD Instinct MI355X
+ * (gfx950).  Every step of the path runs in hand-written HIP kernels; the
+ * caller (e.g. PyTorch) owns every device buffer and the stream.
+ *
+ * What the step computes (the pages are GPT-2 pre-training write-ups):
+ *   - the pre-LN decoder: token + position embedding, N blocks of
+ *     [LayerNorm -> causal multi-head self-attention -> residual add;
+ *      LayerNorm -> MLP C->4C (tanh GELU) -> 4C->C -> residual add],
+ *     final LayerNorm, lm_head tied to the token embedding
+ *     (hanzo gpt LLM.md, "GPT Model Architecture"; Genesis model card,
+ *     "Architecture"; AxonLM README, "Key Features": weight tying);
+ *   - mean softmax cross-entropy over every position, the softmax taken over
+ *     the whole padded vocabulary (GPT From Scratch, "Key decisions":
+ *     50,257 padded to 50,304);
+ *   - gradient accumulation over equal micro-batches, each loss scaled by 1/k
+ *     (AxonLM README, "Key Features"; GPT From Scratch, "Key decisions");
+ *   - global-norm gradient clipping and AdamW with decoupled weight decay on
+ *     tensors of two or more dimensions only, betas (0.9, 0.95)
+ *     (AxonLM README, "Training Recipe").
+ *
+ * Conventions for every call:
+ *   - Pointers named d_* and every pointer inside gpt2_buffers are DEVICE
+ *     pointers; gpt2_config / gpt2_sizes pointers are HOST pointers.
+ *   - All work is queued on the stream given to gpt2_init (a hipStream_t, or
+ *     NULL for the default stream) and is asynchronous: a return of GPT2_OK
+ *     means the work was queued.  Scalar results land in caller device memory.
+ *   - The library never allocates device memory: activations and scratch
+ *     live in the caller's workspace buffer.
+ *   - One context per stream; a context is not thread-safe.
+ *
+ * Parameter layout: one flat fp32 vector, tensors in this order, each
+ * row-major; weights are (out, in) so that y = x W^T.  Per-block tensors are
+ * stored for all L blocks contiguously ([L, ...]):
+ *   wte (Vp, C); wpe (block_size, C);
+ *   ln1_w [L, C]; ln1_b [L, C]; qkv_w [L, 3C, C]; qkv_b [L, 3C];
+ *   proj_w [L, C, C]; proj_b [L, C]; ln2_w [L, C]; ln2_b [L, C];
+ *   fc_w [L, 4C, C]; fc_b [L, 4C]; fcproj_w [L, C, 4C]; fcproj_b [L, C];
+ *   lnf_w (C); lnf_b (C).
+ * grads, adam_m and adam_v share this layout.  gpt2_tensor_info enumerates it.
+ * Weight decay applies to wte, wpe, qkv_w, proj_w, fc_w and fcproj_w.
+ */
+#ifndef GPT2_H
+#define GPT2_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* return codes */
+#define GPT2_OK                0
+#define GPT2_ERR_ARG          -1  /* bad config or argument, NULL pointer      */
+#define GPT2_ERR_SEQ_TOO_LONG -2  /* T > block_size                            */
+#define GPT2_ERR_BATCH        -3  /* B < 1, B > max_batch, k < 1               */
+#define GPT2_ERR_STATE        -4  /* backward without a matching forward       */
+#define GPT2_ERR_TOKEN        -5  /* an id or target outside [0, vocab_size)   */
+#define GPT2_ERR_HIP          -6  /* a HIP call or kernel launch failed        */
+
+/* precision modes */
+#define GPT2_FP32 0  /* every tensor fp32                                        */
+#define GPT2_BF16 1  /* bf16 GEMM/attention operands and activations, fp32
+                        residual stream, statistics, loss, grads, master
+                        weights and AdamW moments                              */
+
+typedef struct {
+  int32_t n_layer;            /* L                                             */
+  int32_t n_head;             /* NH; C % NH == 0                               */
+  int32_t n_embd;             /* C; C % 8 == 0                                 */
+  int32_t block_size;         /* largest T (rows of wpe)                       */
+  int32_t vocab_size;         /* ids and targets lie in [0, vocab_size)        */
+  int32_t padded_vocab_size;  /* Vp >= vocab_size: rows of wte, softmax width;
+                                 Vp % 8 == 0 in BF16 mode                      */
+  int32_t precision;          /* GPT2_FP32 or GPT2_BF16; BF16 needs C/NH == 64 */
+  int32_t max_batch;          /* largest micro-batch B the workspace holds     */
+} gpt2_config;
+
+typedef struct {
+  float *params;      /* n_params fp32 master weights (caller writes them)    */
+  float *grads;       /* n_params fp32                                         */
+  float *adam_m;      /* n_params fp32                                         */
+  float *adam_v;      /* n_params fp32                                         */
+  void  *params_bf16; /* n_params bf16 copy of params (BF16 mode; else NULL)   */
+  void  *workspace;   /* workspace_bytes, 256-byte aligned                     */
+} gpt2_buffers;
+
+typedef struct {
+  int64_t n_params;         /* elements of params / grads / adam_m / adam_v    */
+  int64_t workspace_bytes;  /* bytes of workspace for this config              */
+  int64_t params_bf16_bytes;/* bytes of params_bf16 (0 in FP32 mode)           */
+} gpt2_sizes;
+
+typedef struct gpt2_ctx gpt2_ctx;  /* opaque host-side context */
+
+/*
+ * Size query and set-up.
+ *   bufs == NULL: validate *cfg and fill *sizes only (no HIP call; *out is
+ *   left untouched).  Otherwise bind the caller's buffers, zero grads, adam_m
+ *   and adam_v on the stream, build the bf16 copy of params (BF16 mode), set
+ *   the AdamW step counter to 0 and return a context in *out.
+ * Errors: GPT2_ERR_ARG for an invalid config (C % NH != 0, C % 8 != 0,
+ *   Vp < vocab_size, BF16 with C/NH != 64, non-positive sizes) or a NULL
+ *   buffer; GPT2_ERR_HIP if a launch fails.
+ */
+int gpt2_init(const gpt2_config *cfg, const gpt2_buffers *bufs, void *hip_stream,
+              gpt2_sizes *sizes, gpt2_ctx **out);
+
+/*
+ * Forward pass of B sequences of T tokens and the mean cross-entropy.
+ *   d_idx, d_targets: int32 device arrays (B, T), row-major.  The position of
+ *   token (b, t) is t.  d_idx must stay valid until the matching backward.
+ *   *d_loss (device fp32) = loss_scale * mean over the B*T positions of
+ *   logsumexp(logits) - logit[target], the softmax over all Vp columns.
+ * Saves activations in the workspace for gpt2_backward (one forward is kept;
+ * a new forward replaces it).
+ * Errors: GPT2_ERR_SEQ_TOO_LONG if T > block_size; GPT2_ERR_BATCH if B < 1 or
+ *   B > max_batch or T < 1; GPT2_ERR_ARG for NULL pointers.  An id or target
+ *   outside [0, vocab_size) sets a sticky device flag (row 0 / class 0 is used
+ *   in its place) that gpt2_sync_status reports as GPT2_ERR_TOKEN.
+ */
+int gpt2_forward_loss(gpt2_ctx *ctx, const int32_t *d_idx, const int32_t *d_targets,
+                      int B, int T, float loss_scale, float *d_loss);
+
+/*
+ * Backward of the last forward: ADDS loss_scale * d(loss)/d(param) into grads
+ * (the tied wte receives both its lm_head and its embedding gradient).
+ * Deterministic: no floating-point atomics; fixed-order reductions.
+ * Errors: GPT2_ERR_STATE if no forward is pending.
+ */
+int gpt2_backward(gpt2_ctx *ctx);
+
+/*
+ * One accumulation: zero grads, then for i < k a forward with loss_scale 1/k
+ * on micro-batch i (d_idx + i*B*T, d_targets + i*B*T) followed by its
+ * backward.  *d_mean_loss (device fp32) = sum_i loss_i / k.
+ * Errors: as gpt2_forward_loss; GPT2_ERR_BATCH if k < 1.
+ */
+int gpt2_accumulate(gpt2_ctx *ctx, const int32_t *d_idx, const int32_t *d_targets,
+                    int k, int B, int T, float *d_mean_loss);
+
+/*
+ * Global-norm clip and one AdamW step (the step counter t becomes t + 1):
+ *   n = ||grads||_2 over every parameter (wte counted once);
+ *   c = max_norm / (n + 1e-6); the gradients are scaled by c iff c < 1;
+ *   m = beta1 m + (1 - beta1) g;  v = beta2 v + (1 - beta2) g^2;
+ *   p = p (1 - lr weight_decay) for decayed tensors, then
+ *   p = p - lr (m / (1 - beta1^t)) / (sqrt(v / (1 - beta2^t)) + eps);
+ *   and the bf16 copy of params is refreshed (BF16 mode).
+ * *d_norm (device fp32) receives n; *d_clipped (device int32) 1 iff scaled.
+ * grads are left unscaled.
+ * Errors: GPT2_ERR_ARG for NULL pointers.
+ */
+int gpt2_clip_adamw_step(gpt2_ctx *ctx, float lr, float beta1, float beta2, float eps,
+                         float weight_decay, float max_norm, float *d_norm,
+                         int32_t *d_clipped);
+
+/* Frees the host context (no device memory is owned). */
+void gpt2_destroy(gpt2_ctx *ctx);
+
+/* ---- helpers beyond the step itself --------------------------------------*/
+
+/* Synchronise the stream; return GPT2_ERR_TOKEN (and clear the flag) if a
+   kernel met an out-of-range id or target since the last call, GPT2_ERR_HIP on
+   a HIP error, else GPT2_OK. */
+int gpt2_sync_status(gpt2_ctx *ctx);
+
+/* After the caller rewrote params on the device: rebuild the bf16 copy. */
+int gpt2_sync_params(gpt2_ctx *ctx);
+
+/* Read / set the AdamW step counter (to resume from saved p, m, v). */
+int64_t gpt2_get_step(const gpt2_ctx *ctx);
+int gpt2_set_step(gpt2_ctx *ctx, int64_t t);
+
+/* Enumerate the parameter tensors in layout order: index in [0, 16); fills the
+   name, element offset into the flat vector, element count, rank and the
+   dims (at most 3).  Host only.  Returns GPT2_ERR_ARG past the last tensor. */
+int gpt2_tensor_info(const gpt2_config *cfg, int index, const char **name,
+                     int64_t *offset, int64_t *numel, int32_t *ndim, int64_t *dims);
+
+/* Device address of a saved activation of the last forward (for tests):
+   name in {"resid", "ln1", "ln1_mean", "ln1_rstd", "qkv", "atty", "lse",
+   "ln2", "fcu", "fcg", "lnf", "logits", "row_loss", "emb_sorted_ids",
+   "emb_sorted_pos", "dresid"}; layer selects the block (for "resid", the
+   index 0..2L of the residual stream).  dtype: 0 fp32, 1 bf16, 2 int32. */
+int gpt2_activation(gpt2_ctx *ctx, const char *name, int layer, void **ptr,
+                    int64_t *numel, int32_t *dtype);
+
+/* Per-launch timing with HIP events on the context's stream.  site: a prefix
+   of launch-site names (e.g. "gemm.fwd.lmhead", "attn.fwd", "gemm"), or NULL
+   to stop.  Enabling clears the record.  gpt2_timing_read synchronises and
+   returns the summed kernel time, the launch count and the summed
+   algorithmic flops and bytes of the matched launches. */
+int gpt2_timing_enable(gpt2_ctx *ctx, const char *site);
+int gpt2_timing_read(gpt2_ctx *ctx, double *total_ms, int64_t *launches,
+                     double *flops, double *bytes);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GPT2_H */

@@ -1,0 +1,101 @@
+"""The C ABI library on the CPU: it loads, exports every function the header
+declares, and its host-only queries (sizes, parameter layout, config checks)
+agree with the independent shape table.  No kernel is launched here."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from gpt2_inputs import SHAPES, ModelShape, n_params, param_shapes
+from gpt_decoder_pre_amd import lib as L
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gpt2.h")
+
+
+def header_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(gpt2_[a-z_0-9]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(L.LIB_PATH):
+        from gpt_decoder_pre_amd import build
+        build.build()
+    return L.load_library()
+
+
+def test_library_exports_every_declared_function(lib):
+    names = header_functions()
+    assert "gpt2_init" in names and "gpt2_clip_adamw_step" in names
+    assert sorted(names) == sorted(L.EXPORTS)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+@pytest.mark.parametrize("name", list(SHAPES))
+def test_size_query_and_layout_match_shape_table(lib, name):
+    s = SHAPES[name]
+    prec = "fp32" if name == "toy" else "bf16"
+    cfg = L.make_config(s, prec, 2)
+    sz = L.query_sizes(cfg)
+    assert sz.n_params == n_params(s)
+    assert sz.params_bf16_bytes == (2 * sz.n_params if prec == "bf16" else 0)
+    assert sz.workspace_bytes > 0
+    lay = L.tensor_layout(cfg)
+    shapes = param_shapes(s)
+    assert list(lay) == list(shapes)
+    off = 0
+    for n, (o, shp) in lay.items():
+        assert o == off, n
+        assert tuple(shp) == tuple(shapes[n]), n
+        k = 1
+        for d in shp:
+            k *= d
+        off += k
+    assert off == sz.n_params
+
+
+def test_workspace_grows_with_batch(lib):
+    s = SHAPES["gpt2-124m"]
+    a = L.query_sizes(L.make_config(s, "bf16", 1)).workspace_bytes
+    b = L.query_sizes(L.make_config(s, "bf16", 16)).workspace_bytes
+    assert b > 10 * a // 2
+    assert b < 64 * 2 ** 30  # fits easily in 288 GB of HBM
+
+
+@pytest.mark.parametrize("bad", [
+    dict(n_embd=100),                        # C % NH != 0 with NH = 12 ... and C % 8 != 0
+    dict(n_head=7),                          # 768 % 7 != 0
+    dict(padded_vocab_size=50000),           # padded < vocab
+    dict(max_batch=0),
+    dict(precision=7),
+])
+def test_invalid_config_is_rejected(lib, bad):
+    s = SHAPES["gpt2-124m"]
+    cfg = L.make_config(s, "bf16", 2)
+    for k, v in bad.items():
+        setattr(cfg, k, v)
+    sz = L.gpt2_sizes()
+    assert lib.gpt2_init(ctypes.byref(cfg), None, None, ctypes.byref(sz), None) == L.GPT2_ERR_ARG
+
+
+def test_bf16_mode_needs_head_dim_64(lib):
+    cfg = L.make_config(ModelShape("x", 2, 4, 128, 64, 65, 72), "bf16", 1)  # head dim 32
+    sz = L.gpt2_sizes()
+    assert lib.gpt2_init(ctypes.byref(cfg), None, None, ctypes.byref(sz), None) == L.GPT2_ERR_ARG
+    cfg.precision = L.GPT2_FP32
+    assert lib.gpt2_init(ctypes.byref(cfg), None, None, ctypes.byref(sz), None) == L.GPT2_OK
+
+
+def test_null_arguments_are_rejected_without_touching_the_gpu(lib):
+    assert lib.gpt2_forward_loss(None, None, None, 1, 1, 1.0, None) == L.GPT2_ERR_ARG
+    assert lib.gpt2_backward(None) == L.GPT2_ERR_ARG
+    assert lib.gpt2_accumulate(None, None, None, 1, 1, 1, None) == L.GPT2_ERR_ARG
+    assert lib.gpt2_clip_adamw_step(None, 1e-3, 0.9, 0.95, 1e-8, 0.1, 1.0, None, None) == L.GPT2_ERR_ARG
+    assert lib.gpt2_get_step(None) == -1
+    lib.gpt2_destroy(None)

@@ -1,0 +1,285 @@
+"""GPU parity: the HIP path through the C ABI against the fp64 oracle on the
+same seeded inputs.
+
+Tolerances (written from the arithmetic of each mode):
+  fp32 mode: loss, every gradient tensor and the parameter update within 1e-4
+  relative (L2) of the oracle;
+  bf16 mode: loss within 2e-2 absolute, per-tensor gradient cosine >= 0.99,
+  relative L2 error of the parameter update <= 2e-2 (from a warm AdamW state:
+  at t = 1 the update is g / |g| per element, a sign that bf16 rounding can
+  flip for near-zero components, so the cold update is reported, not gated).
+Index work (embedding gather, the sort behind the scatter) and the clip
+decision are compared bit for bit.
+"""
+
+import math
+
+import numpy as np
+import pytest
+
+from gpt2_inputs import SHAPES, init_params, param_shapes
+from oracle import gpt2 as ref
+from tests.gpu_helpers import (BF16_GRAD_COS, BF16_LOSS_ABS, BF16_UPDATE_REL, FP32_REL, batches_for, cos,
+                               gpu_step, host, rel, say, shape, to_dev, warm_state)
+
+pytestmark = pytest.mark.gpu
+
+
+def _oracle_step(params, batches, n_head, m, v, t, lr, wd=0.1, max_norm=1.0):
+    return ref.train_step(params, m, v, t, batches, n_head, lr=lr, weight_decay=wd, max_norm=max_norm)
+
+
+def _run(s, precision, params, batches, warm=None, lr=1e-3, max_norm=1.0):
+    """Returns (loss, grads, norm, clipped, new params) from the GPU."""
+    import torch
+    B = batches[0][0].shape[0]
+    st = gpu_step(s, precision, B, params)
+    if warm is not None:
+        m, v, t = warm
+        st.load_state(m, v, t)
+    x, y = to_dev(batches)
+    loss = st.accumulate(x, y)
+    torch.cuda.synchronize()
+    grads = host(st.to_dict(st.grads))
+    norm, clipped = st.clip_adamw_step(lr, 0.9, 0.95, 1e-8, 0.1, max_norm)
+    torch.cuda.synchronize()
+    assert st.sync_status() == 0
+    out = (float(loss.item()), grads, float(norm.item()), int(clipped.item()), host(st.to_dict(st.params)))
+    st.close()
+    return out
+
+
+# ------------------------------------------------------------------ fp32 toy ----
+
+def test_toy_fp32_forward_activations_match_oracle():
+    import torch
+    s = SHAPES["toy"]
+    say("toy fp32 forward activations")
+    p = init_params(s, 0)
+    (x, y), = batches_for(s, 4, 64, 1, kind="uniform")
+    st = gpu_step(s, "fp32", 4, p)
+    xd, yd = to_dev([(x, y)])
+    st.forward_loss(xd[0], yd[0], 1.0)
+    torch.cuda.synchronize()
+    loss_ref, cache = ref.forward(p, x, y, s.n_head)
+    M, C = 4 * 64, s.n_embd
+    for l in range(s.n_layer):
+        lc = cache["layers"][l]
+        checks = {
+            ("resid", 2 * l): lc["x_in"], ("ln1", l): lc["h1"], ("qkv", l): lc["qkv"],
+            ("atty", l): lc["y"], ("resid", 2 * l + 1): lc["x_mid"], ("ln2", l): lc["h2"],
+            ("fcu", l): lc["u"], ("fcg", l): lc["g"],
+        }
+        for (name, idx), want in checks.items():
+            got = st.activation(name, idx).float().cpu().numpy().reshape(want.shape)
+            assert rel(got, want) < 1e-5, (name, idx, rel(got, want))
+    got = st.activation("row_loss").cpu().numpy()
+    assert rel(got, cache["per_token_loss"].ravel()) < 1e-5
+    assert abs(st.d_loss.item() - loss_ref) / loss_ref < 1e-6
+    st.close()
+
+
+@pytest.mark.parametrize("B,T,k", [(4, 64, 1), (3, 37, 2)])
+def test_toy_fp32_full_step_matches_oracle(B, T, k):
+    s = SHAPES["toy"]
+    say(f"toy fp32 step B={B} T={T} k={k}")
+    p = init_params(s, 0)
+    batches = batches_for(s, B, T, k, kind="uniform")
+    loss_r, g_r = ref.accumulate(p, batches, s.n_head)
+    m0, v0 = warm_state(g_r)
+    r = _oracle_step(p, batches, s.n_head, m0, v0, 4, lr=1e-3)
+    loss, grads, norm, clipped, p_new = _run(s, "fp32", p, batches, warm=(m0, v0, 3), lr=1e-3)
+    assert abs(loss - r["loss"]) / r["loss"] < FP32_REL
+    for n in p:
+        assert rel(grads[n], r["grads"][n]) < FP32_REL, (n, rel(grads[n], r["grads"][n]))
+    assert abs(norm - r["norm"]) / r["norm"] < 1e-5
+    assert bool(clipped) == r["clipped"]
+    for n in p:
+        d_gpu = p_new[n] - p[n]
+        d_ref = r["params"][n] - p[n]
+        assert rel(d_gpu, d_ref) < FP32_REL, (n, rel(d_gpu, d_ref))
+
+
+# ------------------------------------------------------------- bf16 GPT-2 ----
+
+def _bf16_case(s, B, T, k, seed_w=0, lr=6e-4):
+    say(f"bf16 step {s.name}: L={s.n_layer} C={s.n_embd} NH={s.n_head} B={B} T={T} k={k}")
+    p = init_params(s, seed_w)
+    batches = batches_for(s, B, T, k, kind="zipf")
+    loss_r, g_r = ref.accumulate(p, batches, s.n_head)
+    m0, v0 = warm_state(g_r)
+    r = _oracle_step(p, batches, s.n_head, m0, v0, 11, lr=lr)
+    loss, grads, norm, clipped, p_new = _run(s, "bf16", p, batches, warm=(m0, v0, 10), lr=lr)
+    say(f"  loss gpu {loss:.6f} ref {r['loss']:.6f}; norm gpu {norm:.5f} ref {r['norm']:.5f}")
+    assert abs(loss - r["loss"]) < BF16_LOSS_ABS
+    worst = min((cos(grads[n], r["grads"][n]), n) for n in p)
+    say(f"  worst gradient cosine {worst[0]:.5f} ({worst[1]})")
+    for n in p:
+        assert cos(grads[n], r["grads"][n]) >= BF16_GRAD_COS, (n, cos(grads[n], r["grads"][n]))
+    assert abs(norm - r["norm"]) / r["norm"] < 2e-2
+    assert bool(clipped) == r["clipped"]
+    worst_u = max((rel(p_new[n] - p[n], r["params"][n] - p[n]), n) for n in p)
+    say(f"  worst update rel err {worst_u[0]:.5f} ({worst_u[1]})")
+    for n in p:
+        e = rel(p_new[n] - p[n], r["params"][n] - p[n])
+        assert e <= BF16_UPDATE_REL, (n, e)
+
+
+def test_bf16_gpt2_small_width_two_layers():
+    s = shape("gpt2-124m-L2", 2, 12, 768, 1024, 50257, 50304)
+    _bf16_case(s, 1, 1024, 2)
+
+
+def test_bf16_ragged_sequence_length():
+    s = shape("gpt2-124m-L1", 1, 12, 768, 1024, 50257, 50304)
+    _bf16_case(s, 2, 200, 1)
+
+
+def test_bf16_xl_width():
+    # C = 1600 and NH = 25 are not multiples of the 128-wide GEMM tiles
+    s = shape("gpt2-1558m-L1", 1, 25, 1600, 1024, 50257, 50304)
+    _bf16_case(s, 1, 256, 2)
+
+
+def test_bf16_full_gpt2_small_one_sequence():
+    s = SHAPES["gpt2-124m"]
+    _bf16_case(s, 1, 1024, 1)
+
+
+# ---------------------------------------------------------------- bit-exact ----
+
+def test_embedding_gather_and_sort_are_exact():
+    import torch
+    s = shape("gpt2-124m-L1", 1, 12, 768, 1024, 50257, 50304)
+    say("embedding gather / sort bit-exact")
+    p = init_params(s, 0)
+    p["wpe"][:] = 0
+    (x, y), = batches_for(s, 4, 512, 1, kind="zipf", seed=5)
+    st = gpu_step(s, "bf16", 4, p)
+    xd, yd = to_dev([(x, y)])
+    st.forward_loss(xd[0], yd[0], 1.0)
+    st.backward()
+    torch.cuda.synchronize()
+    x0 = st.activation("resid", 0).cpu().numpy().reshape(x.size, -1)
+    assert np.array_equal(x0, p["wte"][x.ravel()])
+    sid = st.activation("emb_sorted_ids").cpu().numpy()
+    spos = st.activation("emb_sorted_pos").cpu().numpy()
+    order = np.argsort(x.ravel(), kind="stable")
+    assert np.array_equal(spos, order)
+    assert np.array_equal(sid, x.ravel()[order])
+    st.close()
+
+
+@pytest.mark.parametrize("mode", ["clip", "noclip"])
+def test_clip_decision_matches_oracle(mode):
+    s = SHAPES["toy"]
+    say(f"clip decision {mode}")
+    p = init_params(s, 0)
+    batches = batches_for(s, 4, 64, 1, kind="uniform")
+    _, g = ref.accumulate(p, batches, s.n_head)
+    n = ref.global_norm(g)
+    max_norm = 0.5 * n if mode == "clip" else 2.0 * n
+    loss, grads, norm, clipped, _ = _run(s, "fp32", p, batches, max_norm=max_norm)
+    assert clipped == (1 if mode == "clip" else 0)
+    assert abs(norm - n) / n < 1e-5
+
+
+# ------------------------------------------------------------- properties ----
+
+def test_step_is_deterministic():
+    import torch
+    s = shape("gpt2-124m-L2", 2, 12, 768, 1024, 50257, 50304)
+    say("determinism")
+    p = init_params(s, 0)
+    batches = batches_for(s, 2, 512, 2, kind="zipf", seed=3)
+    outs = []
+    for _ in range(2):
+        st = gpu_step(s, "bf16", 2, p)
+        x, y = to_dev(batches)
+        for _ in range(2):
+            st.accumulate(x, y)
+            st.clip_adamw_step(6e-4)
+        torch.cuda.synchronize()
+        outs.append((st.params.clone(), st.m.clone(), st.v.clone(), st.grads.clone()))
+        st.close()
+    for a, b in zip(outs[0], outs[1]):
+        assert torch.equal(a, b)
+
+
+def test_accumulation_matches_one_large_batch_on_gpu():
+    import torch
+    s = SHAPES["toy"]
+    say("accumulation vs one batch (fp32)")
+    p = init_params(s, 0)
+    batches = batches_for(s, 2, 64, 3, kind="uniform", seed=9)
+    st = gpu_step(s, "fp32", 6, p)
+    x, y = to_dev(batches)
+    la = st.accumulate(x, y).item()
+    ga = st.grads.clone()
+    xb = x.reshape(1, 6, 64).contiguous()
+    yb = y.reshape(1, 6, 64).contiguous()
+    lb = st.accumulate(xb, yb).item()
+    gb = st.grads.clone()
+    torch.cuda.synchronize()
+    assert abs(la - lb) < 1e-5
+    assert (ga - gb).abs().max().item() < 1e-5 * max(1.0, gb.abs().max().item())
+    st.close()
+
+
+def test_error_codes():
+    import torch
+    from gpt_decoder_pre_amd.lib import GPT2_ERR_BATCH, GPT2_ERR_SEQ_TOO_LONG, GPT2_ERR_STATE, GPT2_ERR_TOKEN
+    from gpt_decoder_pre_amd.lib import Gpt2Error
+    s = SHAPES["toy"]
+    say("error codes")
+    p = init_params(s, 0)
+    st = gpu_step(s, "fp32", 2, p)
+    with pytest.raises(Gpt2Error) as e:
+        st.backward()
+    assert e.value.code == GPT2_ERR_STATE
+    long = torch.zeros(1, 65, dtype=torch.int32, device="cuda")
+    with pytest.raises(Gpt2Error) as e:
+        st.forward_loss(long, long)
+    assert e.value.code == GPT2_ERR_SEQ_TOO_LONG
+    big = torch.zeros(3, 8, dtype=torch.int32, device="cuda")
+    with pytest.raises(Gpt2Error) as e:
+        st.forward_loss(big, big)
+    assert e.value.code == GPT2_ERR_BATCH
+    bad = torch.full((1, 8), 65, dtype=torch.int32, device="cuda")  # id == vocab_size
+    ok = torch.zeros(1, 8, dtype=torch.int32, device="cuda")
+    st.forward_loss(bad, ok)
+    assert st.sync_status() == GPT2_ERR_TOKEN
+    assert st.sync_status() == 0  # the flag is cleared once reported
+    st.forward_loss(ok, bad)
+    assert st.sync_status() == GPT2_ERR_TOKEN
+    st.close()
+
+
+def test_full_bench_config_sampled_rows():
+    """GPT-2 124M at micro-batch 16 x 1024 (the benchmarked launch shapes):
+    every sequence is independent, so the oracle recomputes one sampled
+    sequence and the GPU's per-position losses for it must match."""
+    import torch
+    s = SHAPES["gpt2-124m"]
+    say("124M B=16 T=1024 sampled rows")
+    p = init_params(s, 0)
+    (x, y), = batches_for(s, 16, 1024, 1, kind="zipf")
+    st = gpu_step(s, "bf16", 16, p)
+    xd, yd = to_dev([(x, y)])
+    loss = st.forward_loss(xd[0], yd[0], 1.0).item()
+    rows = st.activation("row_loss").cpu().numpy().reshape(16, 1024)
+    st.backward()
+    torch.cuda.synchronize()
+    assert st.sync_status() == 0
+    g = st.grads
+    assert torch.isfinite(g).all().item()
+    b = 11
+    lr_, cache = ref.forward(p, x[b:b + 1], y[b:b + 1], s.n_head)
+    want = cache["per_token_loss"].ravel()
+    say(f"  mean |row loss err| {np.mean(np.abs(rows[b] - want)):.2e}, max {np.max(np.abs(rows[b] - want)):.2e}")
+    assert np.mean(np.abs(rows[b] - want)) < BF16_LOSS_ABS
+    assert abs(rows[b].mean() - lr_) < BF16_LOSS_ABS
+    assert abs(loss - rows.mean()) < 1e-4
+    # initial loss sits near ln(V) (+ C * 0.02^2 / 2 from the random lm_head)
+    assert abs(loss - math.log(50304)) < 0.3
+    st.close()
