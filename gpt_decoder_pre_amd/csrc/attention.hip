@@ -21,18 +21,13 @@
 namespace gpt2k {
 
 constexpr int HD = 64;
-constexpr int LD = 72;  // bf16 elements per LDS row (64 + 8 padding)
+constexpr int LD = 72;      // bf16 elements per LDS row (64 + 8 padding)
+constexpr int TILE = 64 * LD;
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
 DEVI bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
-
-// 8 bf16 from an LDS row: elements [o, o+4) and [o+8, o+12) -- the key order
-// that matches the accumulator rows 4*hl + {0..3} and 8 + 4*hl + {0..3}.
-DEVI bf16x8 lds_pair4(const bf16* p) {
-  const u32x2 a = *reinterpret_cast<const u32x2*>(p);
-  const u32x2 b = *reinterpret_cast<const u32x2*>(p + 8);
-  u32x4 r = {a[0], a[1], b[0], b[1]};
-  return as_bf16x8(r);
-}
 
 DEVI bf16x8 pack8(const f32x16& v, int base) {
   bf16x8 r;
@@ -41,42 +36,62 @@ DEVI bf16x8 pack8(const f32x16& v, int base) {
   return r;
 }
 
-// Loads a 64 x 64 bf16 tile (rows r0.., row stride ld, rows >= rmax zero) into
-// LDS [64][LD] as is (natural) -- all 256 threads, two 16-byte chunks each.
-DEVI void tile_natural(const bf16* g, int64_t ld, int r0, int rmax, bf16* s, int tid) {
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int c = tid + 256 * i;
-    const int r = c >> 3, ch = (c & 7) * 8;
-    *reinterpret_cast<u32x4*>(s + r * LD + ch) =
-        ld16_or_zero(g + (int64_t)(r0 + r) * ld + ch, r0 + r < rmax);
-  }
-}
-// Same tile stored transposed, s[col][row]; 64 threads, an 8 x 8 block each.
-DEVI void tile_transposed(const bf16* g, int64_t ld, int r0, int rmax, bf16* s, int t64) {
-  const int rb = t64 >> 3, cb = t64 & 7;
-  u32x4 in[8], out[8];
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int r = r0 + rb * 8 + j;
-    in[j] = ld16_or_zero(g + (int64_t)r * ld + cb * 8, r < rmax);
-  }
-  transpose8x8(in, out);
-#pragma unroll
-  for (int e = 0; e < 8; ++e) *reinterpret_cast<u32x4*>(s + (cb * 8 + e) * LD + rb * 8) = out[e];
+// MFMA A operand from an LDS tile stored [k][m] (m contiguous, row stride LD):
+// rows m = mbase + lane%32, and the eight k of the permuted 16-k step kbase:
+// kbase + 4 hl + {0..3} and kbase + 8 + 4 hl + {0..3}.  ds_read_b64_tr_b16
+// hands lane j of each 16-lane group element i of source lane 4i + j/4's
+// 8-byte row, so source lane 4i + q points at (k0 + i, m16 + 4q).
+DEVI bf16x8 lds_tr_frag(const bf16* tile, int kbase, int mbase, int lane) {
+  const int g = lane >> 4, s = lane & 15;
+  const int k = kbase + 4 * (g >> 1) + (s >> 2);
+  const int m = mbase + 16 * (g & 1) + 4 * (s & 3);
+  const bf16* p = tile + k * LD + m;
+  const i16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p));
+  const i16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p + 8 * LD));
+  const u32x2 ua = __builtin_bit_cast(u32x2, a), ub = __builtin_bit_cast(u32x2, b);
+  u32x4 r = {ua[0], ua[1], ub[0], ub[1]};
+  return as_bf16x8(r);
 }
 
+// MFMA operand rows from an LDS tile stored [row][k] (k contiguous).
+DEVI bf16x8 lds_row_frag(const bf16* tile, int row, int k) {
+  return *reinterpret_cast<const bf16x8*>(tile + row * LD + k);
+}
+
+// A 64-row x 64-column bf16 tile in flight: two 16-byte chunks per thread.
+struct TileRegs {
+  u32x4 r[2];
+  DEVI void load(const bf16* g, int64_t ld, int r0, int rmax, int tid) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int c = tid + 256 * i;
+      const int row = c >> 3, ch = (c & 7) * 8;
+      r[i] = ld16_or_zero(g + (int64_t)(r0 + row) * ld + ch, r0 + row < rmax);
+    }
+  }
+  DEVI void store(bf16* s, int tid) const {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int c = tid + 256 * i;
+      *reinterpret_cast<u32x4*>(s + (c >> 3) * LD + (c & 7) * 8) = r[i];
+    }
+  }
+};
+
 // ------------------------------------------------------------------ forward ----
-__global__ __launch_bounds__(256) void flash_fwd_kernel(const bf16* __restrict__ qkv, bf16* __restrict__ y,
-                                                        float* __restrict__ lse, int T, int NH, int C,
-                                                        float sl2) {
-  __shared__ __attribute__((aligned(16))) bf16 Ks[64 * LD];
-  __shared__ __attribute__((aligned(16))) bf16 Vt[64 * LD];
+// Workgroup: 128 queries of one (sequence, head); wave w owns queries
+// q0 + 32 w + lane%32.  K and V tiles of 64 keys are double-buffered in LDS;
+// the next tile's loads are in flight while the current one is used.
+__global__ __launch_bounds__(256, 2) void flash_fwd_kernel(const bf16* __restrict__ qkv, bf16* __restrict__ y,
+                                                           float* __restrict__ lse, int T, int NH, int C,
+                                                           float sl2) {
+  __shared__ __attribute__((aligned(16))) bf16 smem[4 * TILE];  // [stage][K | V]
   const int qt = gridDim.x - 1 - blockIdx.x;  // longest rows first
   const int h = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, lc = lane & 31, hl = lane >> 5;
   const int q0 = qt * 128;
-  const int myq = q0 + wave * 32 + lc;
+  const int wq0 = q0 + wave * 32;
+  const int myq = wq0 + lc;
   const int64_t ld = 3 * (int64_t)C;
   const bf16* Q = qkv + (int64_t)b * T * ld + h * HD;
   const bf16* K = Q + C;
@@ -91,64 +106,89 @@ __global__ __launch_bounds__(256) void flash_fwd_kernel(const bf16* __restrict__
   for (int r = 0; r < 16; ++r) o[0][r] = o[1][r] = 0.f;
   float mrow = -INFINITY, lrow = 0.f;
   const int kv_end = min(T, q0 + 128);
-  for (int k0 = 0; k0 < kv_end; k0 += 64) {
-    __syncthreads();
-    tile_natural(K, ld, k0, T, Ks, tid);
-    if (tid < 64) tile_transposed(V, ld, k0, T, Vt, tid);
-    __syncthreads();
-
-    f32x16 s[2];
-#pragma unroll
-    for (int js = 0; js < 2; ++js) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) s[js][r] = 0.f;
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(Ks + (js * 32 + lc) * LD + kk * 16 + hl * 8);
-        s[js] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[kk], s[js], 0, 0, 0);
-      }
+  const int nkt = (kv_end + 63) / 64;
+  TileRegs tk, tv;
+  tk.load(K, ld, 0, T, tid);
+  tv.load(V, ld, 0, T, tid);
+  tk.store(smem, tid);
+  tv.store(smem + TILE, tid);
+  __syncthreads();
+  for (int kt = 0; kt < nkt; ++kt) {
+    const int k0 = kt * 64;
+    const bool more = kt + 1 < nkt;
+    if (more) {
+      tk.load(K, ld, k0 + 64, T, tid);
+      tv.load(V, ld, k0 + 64, T, tid);
     }
-    // s[js][r]: key k0 + 32 js + 8 (r/4) + 4 hl + r%4, query myq
-    float mx = -INFINITY;
+    const bf16* Ks = smem + (kt & 1) * 2 * TILE;
+    const bf16* Vs = Ks + TILE;
+    if (k0 <= wq0 + 31) {  // some key of the tile is visible to this wave
+      f32x16 s[2];
 #pragma unroll
-    for (int js = 0; js < 2; ++js)
+      for (int js = 0; js < 2; ++js) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[js][r] = 0.f;
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk)
+          s[js] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_row_frag(Ks, js * 32 + lc, kk * 16 + hl * 8), qf[kk],
+                                                          s[js], 0, 0, 0);
+      }
+      // s[js][r]: key k0 + 32 js + 8 (r/4) + 4 hl + r%4, query myq
+      float mx = -INFINITY;
+      if (k0 + 63 > wq0 || k0 + 64 > T) {
+#pragma unroll
+        for (int js = 0; js < 2; ++js)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = k0 + js * 32 + 8 * (r >> 2) + 4 * hl + (r & 3);
+            const float v = (key <= myq && key < T) ? s[js][r] * sl2 : -INFINITY;
+            s[js][r] = v;
+            mx = fmaxf(mx, v);
+          }
+      } else {
+#pragma unroll
+        for (int js = 0; js < 2; ++js)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            s[js][r] *= sl2;
+            mx = fmaxf(mx, s[js][r]);
+          }
+      }
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      const float mnew = fmaxf(mrow, mx);
+      const float mu = (mnew == -INFINITY) ? 0.f : mnew;
+      const float alpha = exp2_fast(mrow - mu);
+      float ls = 0.f;
+#pragma unroll
+      for (int js = 0; js < 2; ++js)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float p = exp2_fast(s[js][r] - mu);
+          s[js][r] = p;
+          ls += p;
+        }
+      lrow = lrow * alpha + ls;
+      mrow = mnew;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int key = k0 + js * 32 + 8 * (r >> 2) + 4 * hl + (r & 3);
-        const float v = (key <= myq && key < T) ? s[js][r] * sl2 : -INFINITY;
-        s[js][r] = v;
-        mx = fmaxf(mx, v);
+        o[0][r] *= alpha;
+        o[1][r] *= alpha;
       }
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    const float mnew = fmaxf(mrow, mx);
-    const float mu = (mnew == -INFINITY) ? 0.f : mnew;
-    const float alpha = exp2_fast(mrow - mu);
-    float ls = 0.f;
+      // O^T += V^T P^T over four 16-key steps (V^T read transposed from V)
 #pragma unroll
-    for (int js = 0; js < 2; ++js)
+      for (int st = 0; st < 4; ++st) {
+        const bf16x8 pf = pack8(s[st >> 1], 8 * (st & 1));
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float p = exp2_fast(s[js][r] - mu);
-        s[js][r] = p;
-        ls += p;
-      }
-    lrow = lrow * alpha + ls;
-    mrow = mnew;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      o[0][r] *= alpha;
-      o[1][r] *= alpha;
-    }
-    // O^T += V^T P^T over four 16-key steps
-#pragma unroll
-    for (int st = 0; st < 4; ++st) {
-      const bf16x8 pf = pack8(s[st >> 1], 8 * (st & 1));
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const bf16x8 va = lds_pair4(Vt + (i * 32 + lc) * LD + st * 16 + 4 * hl);
-        o[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pf, o[i], 0, 0, 0);
+        for (int i = 0; i < 2; ++i)
+          o[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_tr_frag(Vs, st * 16, i * 32, lane), pf, o[i], 0, 0, 0);
       }
     }
+    if (more) {
+      bf16* nxt = smem + ((kt + 1) & 1) * 2 * TILE;
+      tk.store(nxt, tid);
+      tv.store(nxt + TILE, tid);
+    }
+    __syncthreads();
   }
   const float ltot = lrow + __shfl_xor(lrow, 32, 64);
   if (myq < T) {
@@ -176,31 +216,36 @@ __global__ void attn_rowdot_kernel(const bf16* __restrict__ y, const bf16* __res
   const bf16* g = dy + m * C + h * HD;
   float s = 0.f;
 #pragma unroll
-  for (int d = 0; d < HD; d += 4) {
-    float u[4], v[4];
+  for (int d = 0; d < HD; d += 8) {
+    float u[4], v[4], u2[4], v2[4];
     load4(a + d, u);
     load4(g + d, v);
-    s += u[0] * v[0] + u[1] * v[1] + u[2] * v[2] + u[3] * v[3];
+    load4(a + d + 4, u2);
+    load4(g + d + 4, v2);
+    s += u[0] * v[0] + u[1] * v[1] + u[2] * v[2] + u[3] * v[3] + u2[0] * v2[0] + u2[1] * v2[1] + u2[2] * v2[2] +
+         u2[3] * v2[3];
   }
   const int b = (int)(m / T), t = (int)(m % T);
   D[((int64_t)b * NH + h) * T + t] = s;
 }
 
 // ---------------------------------------------------------- backward: dK, dV ----
-__global__ __launch_bounds__(256) void flash_bwd_dkdv_kernel(const bf16* __restrict__ qkv,
-                                                             const bf16* __restrict__ dy,
-                                                             const float* __restrict__ lse,
-                                                             const float* __restrict__ Dd, bf16* __restrict__ dqkv,
-                                                             int T, int NH, int C, float sl2, float scale) {
-  __shared__ __attribute__((aligned(16))) bf16 Qs[64 * LD];
-  __shared__ __attribute__((aligned(16))) bf16 Qt[64 * LD];
-  __shared__ __attribute__((aligned(16))) bf16 Gs[64 * LD];
-  __shared__ __attribute__((aligned(16))) bf16 Gt[64 * LD];
-  __shared__ float lse_s[64], D_s[64];
+// Workgroup: 128 keys of one (sequence, head); wave w owns keys key0 + 32 w +
+// lane%32 and accumulates dK^T and dV^T over the query tiles (64 queries,
+// double-buffered) that can see them.
+__global__ __launch_bounds__(256, 2) void flash_bwd_dkdv_kernel(const bf16* __restrict__ qkv,
+                                                                const bf16* __restrict__ dy,
+                                                                const float* __restrict__ lse,
+                                                                const float* __restrict__ Dd,
+                                                                bf16* __restrict__ dqkv, int T, int NH, int C,
+                                                                float sl2, float scale) {
+  __shared__ __attribute__((aligned(16))) bf16 smem[4 * TILE];  // [stage][Q | dO]
+  __shared__ float rowv[2][2][64];                              // [stage][lse*log2e | D]
   const int h = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, lc = lane & 31, hl = lane >> 5;
   const int key0 = blockIdx.x * 128;  // tile 0 has the most queries and is scheduled first
-  const int mykey = key0 + wave * 32 + lc;
+  const int wk0 = key0 + wave * 32;
+  const int mykey = wk0 + lc;
   const int64_t ld = 3 * (int64_t)C;
   const bf16* Q = qkv + (int64_t)b * T * ld + h * HD;
   const bf16* K = Q + C;
@@ -219,53 +264,76 @@ __global__ __launch_bounds__(256) void flash_bwd_dkdv_kernel(const bf16* __restr
 #pragma unroll
   for (int r = 0; r < 16; ++r) dk[0][r] = dk[1][r] = dv[0][r] = dv[1][r] = 0.f;
 
-  for (int q0 = key0; q0 < T; q0 += 64) {
+  const int nqt = (T - key0 + 63) / 64;
+  TileRegs tq, tg;
+  float rv = 0.f;
+  auto fetch = [&](int q0) {
+    tq.load(Q, ld, q0, T, tid);
+    tg.load(G, C, q0, T, tid);
+    if (tid < 128) {
+      const int q = q0 + (tid & 63);
+      rv = q < T ? (tid < 64 ? lse_b[q] * kLog2e : D_b[q]) : 0.f;
+    }
+  };
+  auto put = [&](int stage) {
+    tq.store(smem + stage * 2 * TILE, tid);
+    tg.store(smem + stage * 2 * TILE + TILE, tid);
+    if (tid < 128) rowv[stage][tid >> 6][tid & 63] = rv;
+  };
+  fetch(key0);
+  put(0);
+  __syncthreads();
+  for (int it = 0; it < nqt; ++it) {
+    const int q0 = key0 + it * 64;
+    const bool more = it + 1 < nqt;
+    if (more) fetch(q0 + 64);
+    const int stg = it & 1;
+    const bf16* Qs = smem + stg * 2 * TILE;
+    const bf16* Gs = Qs + TILE;
+    const float* ls = rowv[stg][0];
+    const float* Ds = rowv[stg][1];
+    if (q0 + 63 >= wk0) {  // some query of the tile sees a key of this wave
+      const bool diag = q0 < wk0 + 31 || q0 + 64 > T;
+      f32x16 P[2], dS[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        f32x16 sv, dp;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sv[r] = dp[r] = 0.f;
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+          sv = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_row_frag(Qs, i * 32 + lc, kk * 16 + hl * 8), kf[kk], sv, 0,
+                                                       0, 0);
+          dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_row_frag(Gs, i * 32 + lc, kk * 16 + hl * 8), vf[kk], dp, 0,
+                                                       0, 0);
+        }
+        // sv[r]: query q0 + 32 i + 8 (r/4) + 4 hl + r%4, key mykey
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int ql = i * 32 + 8 * (r >> 2) + 4 * hl + (r & 3);
+          float p = exp2_fast(sv[r] * sl2 - ls[ql]);
+          if (diag) {
+            const int q = q0 + ql;
+            p = (mykey <= q && q < T) ? p : 0.f;
+          }
+          P[i][r] = p;
+          dS[i][r] = p * (dp[r] - Ds[ql]);
+        }
+      }
+      // dV^T += dO^T P, dK^T += Q^T dS (transposed operands read from the natural tiles)
+#pragma unroll
+      for (int st = 0; st < 4; ++st) {
+        const bf16x8 pb = pack8(P[st >> 1], 8 * (st & 1));
+        const bf16x8 sb = pack8(dS[st >> 1], 8 * (st & 1));
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          dv[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_tr_frag(Gs, st * 16, t * 32, lane), pb, dv[t], 0, 0, 0);
+          dk[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_tr_frag(Qs, st * 16, t * 32, lane), sb, dk[t], 0, 0, 0);
+        }
+      }
+    }
+    if (more) put(stg ^ 1);
     __syncthreads();
-    tile_natural(Q, ld, q0, T, Qs, tid);
-    tile_natural(G, C, q0, T, Gs, tid);
-    if (tid < 64) tile_transposed(Q, ld, q0, T, Qt, tid);
-    else if (tid < 128) tile_transposed(G, C, q0, T, Gt, tid - 64);
-    else if (tid < 192) {
-      const int t = tid - 128, q = q0 + t;
-      lse_s[t] = q < T ? lse_b[q] * kLog2e : 0.f;
-      D_s[t] = q < T ? D_b[q] : 0.f;
-    }
-    __syncthreads();
-    f32x16 P[2], dS[2];
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      f32x16 sv, dp;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) sv[r] = dp[r] = 0.f;
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        const bf16x8 qa = *reinterpret_cast<const bf16x8*>(Qs + (i * 32 + lc) * LD + kk * 16 + hl * 8);
-        const bf16x8 ga = *reinterpret_cast<const bf16x8*>(Gs + (i * 32 + lc) * LD + kk * 16 + hl * 8);
-        sv = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kf[kk], sv, 0, 0, 0);
-        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ga, vf[kk], dp, 0, 0, 0);
-      }
-      // sv[r]: query q0 + 32 i + 8 (r/4) + 4 hl + r%4, key mykey
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int ql = i * 32 + 8 * (r >> 2) + 4 * hl + (r & 3);
-        const int q = q0 + ql;
-        const float p = (mykey <= q && q < T) ? exp2_fast(sv[r] * sl2 - lse_s[ql]) : 0.f;
-        P[i][r] = p;
-        dS[i][r] = p * (dp[r] - D_s[ql]);
-      }
-    }
-#pragma unroll
-    for (int st = 0; st < 4; ++st) {
-      const bf16x8 pb = pack8(P[st >> 1], 8 * (st & 1));
-      const bf16x8 sb = pack8(dS[st >> 1], 8 * (st & 1));
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        const bf16x8 ga = lds_pair4(Gt + (t * 32 + lc) * LD + st * 16 + 4 * hl);
-        const bf16x8 qa = lds_pair4(Qt + (t * 32 + lc) * LD + st * 16 + 4 * hl);
-        dv[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ga, pb, dv[t], 0, 0, 0);
-        dk[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, sb, dk[t], 0, 0, 0);
-      }
-    }
   }
   if (mykey < T) {
     bf16* o = dqkv + ((int64_t)b * T + mykey) * ld + h * HD;
@@ -283,18 +351,20 @@ __global__ __launch_bounds__(256) void flash_bwd_dkdv_kernel(const bf16* __restr
 }
 
 // --------------------------------------------------------------- backward: dQ ----
-__global__ __launch_bounds__(256) void flash_bwd_dq_kernel(const bf16* __restrict__ qkv, const bf16* __restrict__ dy,
-                                                           const float* __restrict__ lse,
-                                                           const float* __restrict__ Dd, bf16* __restrict__ dqkv,
-                                                           int T, int NH, int C, float sl2, float scale) {
-  __shared__ __attribute__((aligned(16))) bf16 Ks[64 * LD];
-  __shared__ __attribute__((aligned(16))) bf16 Kt[64 * LD];
-  __shared__ __attribute__((aligned(16))) bf16 Vs[64 * LD];
+// Workgroup: 128 queries; wave w owns queries q0 + 32 w + lane%32 and
+// accumulates dQ^T over the key tiles (64 keys, double-buffered) it sees.
+__global__ __launch_bounds__(256, 2) void flash_bwd_dq_kernel(const bf16* __restrict__ qkv,
+                                                              const bf16* __restrict__ dy,
+                                                              const float* __restrict__ lse,
+                                                              const float* __restrict__ Dd, bf16* __restrict__ dqkv,
+                                                              int T, int NH, int C, float sl2, float scale) {
+  __shared__ __attribute__((aligned(16))) bf16 smem[4 * TILE];  // [stage][K | V]
   const int qt = gridDim.x - 1 - blockIdx.x;
   const int h = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, lc = lane & 31, hl = lane >> 5;
   const int q0 = qt * 128;
-  const int myq = q0 + wave * 32 + lc;
+  const int wq0 = q0 + wave * 32;
+  const int myq = wq0 + lc;
   const int64_t ld = 3 * (int64_t)C;
   const bf16* Q = qkv + (int64_t)b * T * ld + h * HD;
   const bf16* K = Q + C;
@@ -314,42 +384,62 @@ __global__ __launch_bounds__(256) void flash_bwd_dq_kernel(const bf16* __restric
 #pragma unroll
   for (int r = 0; r < 16; ++r) dq[0][r] = dq[1][r] = 0.f;
   const int kv_end = min(T, q0 + 128);
-  for (int k0 = 0; k0 < kv_end; k0 += 64) {
-    __syncthreads();
-    tile_natural(K, ld, k0, T, Ks, tid);
-    tile_natural(V, ld, k0, T, Vs, tid);
-    if (tid < 64) tile_transposed(K, ld, k0, T, Kt, tid);
-    __syncthreads();
-    f32x16 dS[2];
+  const int nkt = (kv_end + 63) / 64;
+  TileRegs tk, tv;
+  tk.load(K, ld, 0, T, tid);
+  tv.load(V, ld, 0, T, tid);
+  tk.store(smem, tid);
+  tv.store(smem + TILE, tid);
+  __syncthreads();
+  for (int kt = 0; kt < nkt; ++kt) {
+    const int k0 = kt * 64;
+    const bool more = kt + 1 < nkt;
+    if (more) {
+      tk.load(K, ld, k0 + 64, T, tid);
+      tv.load(V, ld, k0 + 64, T, tid);
+    }
+    const bf16* Ks = smem + (kt & 1) * 2 * TILE;
+    const bf16* Vs = Ks + TILE;
+    if (k0 <= wq0 + 31) {
+      const bool diag = k0 + 63 > wq0 || k0 + 64 > T;
+      f32x16 dS[2];
 #pragma unroll
-    for (int js = 0; js < 2; ++js) {
-      f32x16 sv, dp;
+      for (int js = 0; js < 2; ++js) {
+        f32x16 sv, dp;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) sv[r] = dp[r] = 0.f;
+        for (int r = 0; r < 16; ++r) sv[r] = dp[r] = 0.f;
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        const bf16x8 ka = *reinterpret_cast<const bf16x8*>(Ks + (js * 32 + lc) * LD + kk * 16 + hl * 8);
-        const bf16x8 va = *reinterpret_cast<const bf16x8*>(Vs + (js * 32 + lc) * LD + kk * 16 + hl * 8);
-        sv = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[kk], sv, 0, 0, 0);
-        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, gf[kk], dp, 0, 0, 0);
+        for (int kk = 0; kk < 4; ++kk) {
+          sv = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_row_frag(Ks, js * 32 + lc, kk * 16 + hl * 8), qf[kk], sv, 0,
+                                                       0, 0);
+          dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_row_frag(Vs, js * 32 + lc, kk * 16 + hl * 8), gf[kk], dp, 0,
+                                                       0, 0);
+        }
+        // sv[r]: key k0 + 32 js + 8 (r/4) + 4 hl + r%4, query myq
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          float p = exp2_fast(sv[r] * sl2 - lse2);
+          if (diag) {
+            const int key = k0 + js * 32 + 8 * (r >> 2) + 4 * hl + (r & 3);
+            p = (key <= myq && qok) ? p : 0.f;
+          }
+          dS[js][r] = p * (dp[r] - Dq);
+        }
       }
-      // sv[r]: key k0 + 32 js + 8 (r/4) + 4 hl + r%4, query myq
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int key = k0 + js * 32 + 8 * (r >> 2) + 4 * hl + (r & 3);
-        const float p = (key <= myq && qok) ? exp2_fast(sv[r] * sl2 - lse2) : 0.f;
-        dS[js][r] = p * (dp[r] - Dq);
+      for (int st = 0; st < 4; ++st) {
+        const bf16x8 sb = pack8(dS[st >> 1], 8 * (st & 1));
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+          dq[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_tr_frag(Ks, st * 16, t * 32, lane), sb, dq[t], 0, 0, 0);
       }
     }
-#pragma unroll
-    for (int st = 0; st < 4; ++st) {
-      const bf16x8 sb = pack8(dS[st >> 1], 8 * (st & 1));
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        const bf16x8 ka = lds_pair4(Kt + (t * 32 + lc) * LD + st * 16 + 4 * hl);
-        dq[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, sb, dq[t], 0, 0, 0);
-      }
+    if (more) {
+      bf16* nxt = smem + ((kt + 1) & 1) * 2 * TILE;
+      tk.store(nxt, tid);
+      tv.store(nxt + TILE, tid);
     }
+    __syncthreads();
   }
   if (qok) {
     bf16* o = dqkv + ((int64_t)b * T + myq) * ld + h * HD;

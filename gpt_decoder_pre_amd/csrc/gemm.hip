@@ -9,6 +9,8 @@
 // multiplied (two LDS buffers, one barrier per k-tile).
 //
 // fp32 path: LDS-tiled FMA GEMM (64x64 tile, 4x4 outputs per thread).
+#include <cmath>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -88,28 +90,31 @@ DEVI void epi_store1(const GemmArgs& p, int m, int n, float v, int split) {
 
 // ------------------------------------------------------------ bf16 MFMA GEMM ----
 // Stages an R x BK operand tile (rows r0.., k in [k0, kend)) through registers
-// into LDS laid out [R][BK + 8] (k contiguous, 16-byte row padding).
-template <bool KMAJ, int R, int BK>
+// into LDS laid out [R][BK + 8] (k contiguous, 16-byte row padding: the
+// fragment reads of eight consecutive rows hit distinct banks).
+template <bool KMAJ, int R, int BK, int NT>
 struct TileLoader {
   static constexpr int LDS = BK + 8;
   static constexpr int NCH = KMAJ ? (R * BK / 8) : (R * BK / 64);
-  static constexpr int PER = (NCH + 255) / 256;
+  static constexpr int PER = (NCH + NT - 1) / NT;
   static constexpr int REGS = KMAJ ? PER : PER * 8;
   u32x4 r[REGS];
 
   DEVI void load(const bf16* g, int64_t ld, int r0, int rmax, int k0, int kend, int tid) {
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
-      const int c = tid + i * 256;
-      if (NCH % 256 == 0 || c < NCH) {
+      const int c = tid + i * NT;
+      if (NCH % NT == 0 || c < NCH) {
         if constexpr (KMAJ) {
-          // g is [rows][k]: 16-byte chunks along k
+          // g is [rows][k]: 16-byte chunks along k, eight lanes per 128-byte row
           const int row = c / (BK / 8), kc = (c % (BK / 8)) * 8;
           const bool ok = (r0 + row < rmax) && (k0 + kc < kend);
           r[i] = ld16_or_zero(g + (int64_t)(r0 + row) * ld + k0 + kc, ok);
         } else {
-          // g is [k][rows]: an 8 (k) x 8 (rows) block
-          const int rb = c % (R / 8), kb = c / (R / 8);
+          // g is [k][rows]: an 8 (k) x 8 (rows) block; consecutive lanes take
+          // consecutive k blocks so that the transposed LDS rows they write
+          // are contiguous
+          const int kb = c % (BK / 8), rb = c / (BK / 8);
           const int rr = r0 + rb * 8;
 #pragma unroll
           for (int j = 0; j < 8; ++j) {
@@ -123,13 +128,13 @@ struct TileLoader {
   DEVI void store(bf16* s, int tid) {
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
-      const int c = tid + i * 256;
-      if (NCH % 256 == 0 || c < NCH) {
+      const int c = tid + i * NT;
+      if (NCH % NT == 0 || c < NCH) {
         if constexpr (KMAJ) {
           const int row = c / (BK / 8), kc = (c % (BK / 8)) * 8;
           *reinterpret_cast<u32x4*>(s + row * LDS + kc) = r[i];
         } else {
-          const int rb = c % (R / 8), kb = c / (R / 8);
+          const int kb = c % (BK / 8), rb = c / (BK / 8);
           u32x4 t[8];
           transpose8x8(&r[i * 8], t);
 #pragma unroll
@@ -140,19 +145,40 @@ struct TileLoader {
   }
 };
 
+// Tile order: blocks are dealt round-robin to the eight XCDs (each with its
+// own L2), so block b is first renumbered to make every XCD own a contiguous
+// range of tiles; tiles are then walked in groups of GM tile-rows so that
+// neighbouring tiles share A rows and B columns in that XCD's L2.
+DEVI void tile_coords(int b, int nblk, int tiles_m, int tiles_n, int& tm, int& tn) {
+  constexpr int NX = 8, GM = 8;
+  const int xcd = b % NX, idx = b / NX;
+  const int q = nblk / NX, rem = nblk % NX;
+  const int t = xcd * q + min(xcd, rem) + idx;
+  const int per_group = GM * tiles_n;
+  const int g = t / per_group;
+  const int first_m = g * GM;
+  const int gm = min(GM, tiles_m - first_m);
+  const int w = t - g * per_group;
+  tm = first_m + w % gm;
+  tn = w / gm;
+}
+
 template <bool A_K, bool B_K, int BM, int BN, int BK, int WGM, int WGN, int EPI>
-__global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs p) {
-  static_assert(WGM * WGN == 4, "four waves");
+__global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_bf16_kernel(GemmArgs p) {
+  constexpr int NT = 64 * WGM * WGN;
   constexpr int LDS = BK + 8;
   constexpr int WTM = BM / WGM, WTN = BN / WGN;
   constexpr int FM = WTM / 32, FN = WTN / 32;
+  static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile is a multiple of 32");
   __shared__ __attribute__((aligned(16))) bf16 smem[2 * (BM + BN) * LDS];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / WGN, wn = wave % WGN;
   const int lc = lane & 31, hl = lane >> 5;
-  const int tiles_n = (p.N + BN - 1) / BN;
-  const int m0 = (blockIdx.x / tiles_n) * BM, n0 = (blockIdx.x % tiles_n) * BN;
+  const int tiles_m = (p.M + BM - 1) / BM, tiles_n = (p.N + BN - 1) / BN;
+  int tm, tn;
+  tile_coords(blockIdx.x, gridDim.x, tiles_m, tiles_n, tm, tn);
+  const int m0 = tm * BM, n0 = tn * BN;
   const int split = blockIdx.y;
   const int kbeg = split * p.k_per_split;
   const int kend = min(p.K, kbeg + p.k_per_split);
@@ -173,8 +199,8 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs p) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  TileLoader<A_K, BM, BK> la;
-  TileLoader<B_K, BN, BK> lb;
+  TileLoader<A_K, BM, BK, NT> la;
+  TileLoader<B_K, BN, BK, NT> lb;
   if (nkt > 0) {
     la.load(A, p.lda, m0, p.M, kbeg, kend, tid);
     lb.load(B, p.ldb, n0, p.N, kbeg, kend, tid);
@@ -189,17 +215,15 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs p) {
       la.load(A, p.lda, m0, p.M, kbeg + (kt + 1) * BK, kend, tid);
       lb.load(B, p.ldb, n0, p.N, kbeg + (kt + 1) * BK, kend, tid);
     }
-    const bf16* a_s = (kt & 1) ? sA1 : sA0;
-    const bf16* b_s = (kt & 1) ? sB1 : sB0;
+    const bf16* a_s = ((kt & 1) ? sA1 : sA0) + (wm * WTM + lc) * LDS + hl * 8;
+    const bf16* b_s = ((kt & 1) ? sB1 : sB0) + (wn * WTN + lc) * LDS + hl * 8;
 #pragma unroll
     for (int kk = 0; kk < BK / 16; ++kk) {
       bf16x8 af[FM], bfr[FN];
 #pragma unroll
-      for (int i = 0; i < FM; ++i)
-        af[i] = *reinterpret_cast<const bf16x8*>(a_s + (wm * WTM + i * 32 + lc) * LDS + kk * 16 + hl * 8);
+      for (int i = 0; i < FM; ++i) af[i] = *reinterpret_cast<const bf16x8*>(a_s + i * 32 * LDS + kk * 16);
 #pragma unroll
-      for (int j = 0; j < FN; ++j)
-        bfr[j] = *reinterpret_cast<const bf16x8*>(b_s + (wn * WTN + j * 32 + lc) * LDS + kk * 16 + hl * 8);
+      for (int j = 0; j < FN; ++j) bfr[j] = *reinterpret_cast<const bf16x8*>(b_s + j * 32 * LDS + kk * 16);
 #pragma unroll
       for (int i = 0; i < FM; ++i)
 #pragma unroll
@@ -318,14 +342,32 @@ void splitk_reduce_add(float* out, const float* part, int splits, int64_t stride
 
 // ---------------------------------------------------------------- dispatch ----
 namespace {
-constexpr int kBM = 128, kBN = 128, kBK = 64;
+constexpr int kBK = 64;
 
+// Tile configurations (block tile BM x BN, wave grid WGM x WGN).
 template <bool A_K, bool B_K, int EPI>
-void launch_bf16(const GemmArgs& a, hipStream_t s) {
-  const int tiles = ((a.M + kBM - 1) / kBM) * ((a.N + kBN - 1) / kBN);
-  dim3 grid(tiles, a.splits);
-  gemm_bf16_kernel<A_K, B_K, kBM, kBN, kBK, 2, 2, EPI><<<grid, 256, 0, s>>>(a);
+void launch_bf16_cfg(int cfg, const GemmArgs& a, hipStream_t s) {
+#define GPT2_GEMM_CFG(ID, BM, BN, WGM, WGN)                                                     \
+  case ID: {                                                                                   \
+    const int tiles = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);                           \
+    gemm_bf16_kernel<A_K, B_K, BM, BN, kBK, WGM, WGN, EPI><<<dim3(tiles, a.splits), 64 * WGM * WGN, 0, s>>>(a); \
+    break;                                                                                     \
+  }
+  switch (cfg) {
+    GPT2_GEMM_CFG(0, 128, 128, 2, 2)
+    GPT2_GEMM_CFG(1, 256, 128, 2, 2)
+    GPT2_GEMM_CFG(2, 256, 256, 2, 2)
+    GPT2_GEMM_CFG(3, 256, 192, 2, 2)
+    GPT2_GEMM_CFG(4, 256, 256, 2, 4)
+    GPT2_GEMM_CFG(5, 128, 256, 2, 2)
+    default: break;
+  }
+#undef GPT2_GEMM_CFG
 }
+constexpr int kNumCfg = 6;
+const int kCfgBM[kNumCfg] = {128, 256, 256, 256, 256, 128};
+const int kCfgBN[kNumCfg] = {128, 128, 256, 192, 256, 256};
+
 template <bool A_K, bool B_K, int EPI>
 void launch_f32(const GemmArgs& a, hipStream_t s) {
   const int tiles = ((a.M + 63) / 64) * ((a.N + 63) / 64);
@@ -333,13 +375,49 @@ void launch_f32(const GemmArgs& a, hipStream_t s) {
   gemm_f32_kernel<A_K, B_K, EPI><<<grid, 256, 0, s>>>(a);
 }
 template <bool A_K, bool B_K, int EPI>
-void launch(bool bf16_mode, const GemmArgs& a, hipStream_t s) {
-  if (bf16_mode) launch_bf16<A_K, B_K, EPI>(a, s);
+void launch(bool bf16_mode, int cfg, const GemmArgs& a, hipStream_t s) {
+  if (bf16_mode) launch_bf16_cfg<A_K, B_K, EPI>(cfg, a, s);
   else launch_f32<A_K, B_K, EPI>(a, s);
+}
+
+// Picks the tile configuration with the least modelled time: a sustained
+// rate per configuration (measured on MI355X for these kernels) scaled by the
+// fill of the last wave of blocks over the 256 CUs and by the padding of
+// partial tiles.
+double model_time(int c, const GemmArgs& a, bool transposed_a) {
+  static const double tf_k[kNumCfg] = {560, 480, 650, 720, 750, 500};   // A stored k-contiguous
+  static const double tf_t[kNumCfg] = {450, 460, 660, 560, 640, 380};   // A stored transposed
+  const int64_t tm = (a.M + kCfgBM[c] - 1) / kCfgBM[c], tn = (a.N + kCfgBN[c] - 1) / kCfgBN[c];
+  const double waves = (double)(tm * tn * a.splits) / 256.0;
+  const double fill = waves / std::ceil(waves);
+  const double used = (double)a.M * a.N / ((double)tm * kCfgBM[c] * tn * kCfgBN[c]);
+  const double flops = 2.0 * a.M * (double)a.N * a.K;
+  return flops / ((transposed_a ? tf_t[c] : tf_k[c]) * 1e12 * fill * used);
+}
+int choose_cfg(const GemmArgs& a, bool transposed_a) {
+  int pick = 0;
+  double best = 1e30;
+  for (int c = 0; c < kNumCfg; ++c) {
+    const double t = model_time(c, a, transposed_a);
+    if (t < best) {
+      best = t;
+      pick = c;
+    }
+  }
+  return pick;
 }
 }  // namespace
 
-bool gemm(GemmLayout layout, GemmEpilogue epi, bool bf16_mode, const GemmArgs& a0, hipStream_t s) {
+int gemm_pick_config(const GemmArgs& a, bool transposed_a) { return choose_cfg(a, transposed_a); }
+
+double gemm_model_time(int cfg, const GemmArgs& a, bool transposed_a) { return model_time(cfg, a, transposed_a); }
+
+void gemm_config_tile(int cfg, int* bm, int* bn) {
+  *bm = (cfg >= 0 && cfg < kNumCfg) ? kCfgBM[cfg] : 128;
+  *bn = (cfg >= 0 && cfg < kNumCfg) ? kCfgBN[cfg] : 128;
+}
+
+bool gemm_cfg(int cfg, GemmLayout layout, GemmEpilogue epi, bool bf16_mode, const GemmArgs& a0, hipStream_t s) {
   GemmArgs a = a0;
   if (a.M <= 0 || a.N <= 0 || a.K <= 0) return false;
   if (a.splits < 1) a.splits = 1;
@@ -350,27 +428,35 @@ bool gemm(GemmLayout layout, GemmEpilogue epi, bool bf16_mode, const GemmArgs& a
     // the epilogue writes four columns at a time.
     if (a.K % 8 || a.N % 8 || a.ldc % 4 || a.lda % 8 || a.ldb % 8) return false;
     if (layout == LAYOUT_TN && a.M % 8) return false;
+    if (cfg < 0) cfg = choose_cfg(a, layout == LAYOUT_TN);
+    if (cfg >= kNumCfg) return false;
   }
   switch (layout) {
     case LAYOUT_NT:
-      if (epi == EPI_ACT) launch<true, true, EPI_ACT>(bf16_mode, a, s);
-      else if (epi == EPI_RESID) launch<true, true, EPI_RESID>(bf16_mode, a, s);
-      else if (epi == EPI_GELU) launch<true, true, EPI_GELU>(bf16_mode, a, s);
+      if (epi == EPI_ACT) launch<true, true, EPI_ACT>(bf16_mode, cfg, a, s);
+      else if (epi == EPI_RESID) launch<true, true, EPI_RESID>(bf16_mode, cfg, a, s);
+      else if (epi == EPI_GELU) launch<true, true, EPI_GELU>(bf16_mode, cfg, a, s);
+      else if (epi == EPI_F32) launch<true, true, EPI_F32>(bf16_mode, cfg, a, s);
       else return false;
       break;
     case LAYOUT_NN:
-      if (epi == EPI_F32) launch<true, false, EPI_F32>(bf16_mode, a, s);
-      else if (epi == EPI_GELU_BWD) launch<true, false, EPI_GELU_BWD>(bf16_mode, a, s);
-      else if (epi == EPI_ACT) launch<true, false, EPI_ACT>(bf16_mode, a, s);
+      if (epi == EPI_F32) launch<true, false, EPI_F32>(bf16_mode, cfg, a, s);
+      else if (epi == EPI_GELU_BWD) launch<true, false, EPI_GELU_BWD>(bf16_mode, cfg, a, s);
+      else if (epi == EPI_ACT) launch<true, false, EPI_ACT>(bf16_mode, cfg, a, s);
       else return false;
       break;
     case LAYOUT_TN:
-      if (epi == EPI_PARTIAL) launch<false, false, EPI_PARTIAL>(bf16_mode, a, s);
-      else if (epi == EPI_F32_ACC) launch<false, false, EPI_F32_ACC>(bf16_mode, a, s);
+      if (epi == EPI_PARTIAL) launch<false, false, EPI_PARTIAL>(bf16_mode, cfg, a, s);
+      else if (epi == EPI_F32_ACC) launch<false, false, EPI_F32_ACC>(bf16_mode, cfg, a, s);
+      else if (epi == EPI_F32) launch<false, false, EPI_F32>(bf16_mode, cfg, a, s);
       else return false;
       break;
   }
   return true;
+}
+
+bool gemm(GemmLayout layout, GemmEpilogue epi, bool bf16_mode, const GemmArgs& a, hipStream_t s) {
+  return gemm_cfg(-1, layout, epi, bf16_mode, a, s);
 }
 
 }  // namespace gpt2k

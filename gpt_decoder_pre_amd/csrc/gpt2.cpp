@@ -212,27 +212,60 @@ GemmArgs gargs(const void* A, int64_t lda, const void* B, int64_t ldb, int M, in
   return a;
 }
 
-// Weight gradient: out[Mo][N] += A^T B with A stored [K][Mo], B stored [K][N];
-// deterministic split-K over the token dimension when the tile grid is small.
+// Weight gradient: out[Mo][N] += A^T B with A stored [K][Mo], B stored [K][N].
+// The token dimension K is split when the output has too few tiles to fill
+// the chip; the splits write fp32 partials that a second kernel adds in split
+// order (deterministic).  Tile configuration and split count minimise the
+// modelled GEMM time plus the partials' HBM traffic.
 bool weight_grad(gpt2_ctx* c, const char* site, float* out, const void* A, int64_t lda, const void* B, int64_t ldb,
                  int Mo, int N, int K) {
-  const int tile = c->bf16 ? 128 : 64;
-  const int64_t tiles = (int64_t)((Mo + tile - 1) / tile) * ((N + tile - 1) / tile);
-  int splits = (int)std::min<int64_t>(16, std::max<int64_t>(1, (512 + tiles - 1) / tiles));
-  int kps = (K + splits - 1) / splits;
-  kps = (kps + 63) / 64 * 64;
-  splits = (K + kps - 1) / kps;
   const int64_t outn = (int64_t)Mo * N;
-  if (splits > 1 && splits * outn > c->splitk_elems) splits = 1;
   GemmArgs a = gargs(A, lda, B, ldb, Mo, N, K, out, N);
+  int best_cfg = -1, best_splits = 1, best_kps = K;
+  if (c->bf16) {
+    double best = 1e30;
+    for (int cfg = 0; cfg < kGemmConfigs; ++cfg) {
+      for (int sp = 1; sp <= 16; sp *= 2) {
+        int kps = (K + sp - 1) / sp;
+        kps = (kps + 63) / 64 * 64;
+        const int splits = (K + kps - 1) / kps;
+        if (splits > 1 && (int64_t)splits * outn > c->splitk_elems) continue;
+        GemmArgs t = a;
+        t.splits = splits;
+        t.k_per_split = kps;
+        double time = gemm_model_time(cfg, t, true);
+        if (splits > 1) time += (2.0 * splits + 2.0) * outn * 4.0 / 4.0e12;
+        if (time < best) {
+          best = time;
+          best_cfg = cfg;
+          best_splits = splits;
+          best_kps = kps;
+        }
+      }
+    }
+  } else {
+    const int64_t tiles = (int64_t)((Mo + 63) / 64) * ((N + 63) / 64);
+    int sp = (int)std::min<int64_t>(16, std::max<int64_t>(1, (512 + tiles - 1) / tiles));
+    int kps = ((K + sp - 1) / sp + 63) / 64 * 64;
+    sp = (K + kps - 1) / kps;
+    if (sp > 1 && sp * outn > c->splitk_elems) sp = 1;
+    best_splits = sp;
+    best_kps = sp > 1 ? kps : K;
+  }
   const double bytes = (double)c->act * ((double)K * Mo + (double)K * N) + 8.0 * outn;
-  if (splits == 1) return gemm_site(c, site, LAYOUT_TN, EPI_F32_ACC, a, bytes);
+  if (best_splits == 1) {
+    Timed tm(c, site, 2.0 * a.M * (double)a.N * a.K, bytes);
+    return gemm_cfg(best_cfg, LAYOUT_TN, EPI_F32_ACC, c->bf16, a, c->stream);
+  }
   a.C = c->splitk;
-  a.splits = splits;
-  a.k_per_split = kps;
+  a.splits = best_splits;
+  a.k_per_split = best_kps;
   a.split_stride = outn;
-  if (!gemm_site(c, site, LAYOUT_TN, EPI_PARTIAL, a, bytes)) return false;
-  splitk_reduce_add(out, c->splitk, splits, outn, outn, c->stream);
+  {
+    Timed tm(c, site, 2.0 * a.M * (double)a.N * a.K, bytes);
+    if (!gemm_cfg(best_cfg, LAYOUT_TN, EPI_PARTIAL, c->bf16, a, c->stream)) return false;
+  }
+  splitk_reduce_add(out, c->splitk, best_splits, outn, outn, c->stream);
   return true;
 }
 
@@ -335,9 +368,7 @@ int backward_impl(gpt2_ctx* c) {
     ch = layernorm_bwd<TA>(c->dh, c->resid(2 * L), c->lnf_mean, c->lnf_rstd, c->P(T_LNFW), c->dres, false,
                            (TA*)c->dres_act, part, M, C, s);
   }
-  colpart_reduce_add(c->G(T_LNFW), part, ch, C, C, s);
-  colpart_reduce_add(c->G(T_LNFB), part + (int64_t)ch * C, ch, C, C, s);
-  colpart_reduce_add(c->G(T_FCPB, L - 1), part + 2 * (int64_t)ch * C, ch, C, C, s);
+  colpart_reduce_add(c->G(T_LNFW), c->G(T_LNFB), c->G(T_FCPB, L - 1), part, ch, C, s);
 
   for (int l = L - 1; l >= 0; --l) {
     TA* ln1 = (TA*)c->layer_act(c->ln1, l, C);
@@ -360,7 +391,7 @@ int backward_impl(gpt2_ctx* c) {
     if (!gemm_site(c, "gemm.bwd.fcproj.dx", LAYOUT_NN, EPI_GELU_BWD, g, a * ((double)M * C + 4.0 * C * C + 8.0 * M * C)))
       return GPT2_ERR_ARG;
     ch = colsum_partials<TA>(dbig, M, 4 * C, part, s);
-    colpart_reduce_add(c->G(T_FCB, l), part, ch, 4 * C, 4 * C, s);
+    colpart_reduce_add(c->G(T_FCB, l), nullptr, nullptr, part, ch, 4 * C, s);
     // MLP input projection: u = LN2(x_mid) Wfc^T + bfc
     if (!weight_grad(c, "gemm.bwd.fc.dw", c->G(T_FCW, l), dbig, 4 * C, ln2, C, 4 * C, C, M)) return GPT2_ERR_ARG;
     g = gargs(dbig, 4 * C, c->W(T_FCW, l), C, M, C, 4 * C, c->dh, C);
@@ -372,9 +403,7 @@ int backward_impl(gpt2_ctx* c) {
                              c->ln2_rstd + (int64_t)l * c->Mmax, c->P(T_LN2W, l), c->dres, true, dres_act, part, M,
                              C, s);
     }
-    colpart_reduce_add(c->G(T_LN2W, l), part, ch, C, C, s);
-    colpart_reduce_add(c->G(T_LN2B, l), part + (int64_t)ch * C, ch, C, C, s);
-    colpart_reduce_add(c->G(T_PROJB, l), part + 2 * (int64_t)ch * C, ch, C, C, s);
+    colpart_reduce_add(c->G(T_LN2W, l), c->G(T_LN2B, l), c->G(T_PROJB, l), part, ch, C, s);
     // attention output projection: x_mid = x_in + y Wp^T + bp
     if (!weight_grad(c, "gemm.bwd.proj.dw", c->G(T_PROJW, l), dres_act, C, atty, C, C, C, M)) return GPT2_ERR_ARG;
     g = gargs(dres_act, C, c->W(T_PROJW, l), C, M, C, C, dy, C);
@@ -388,7 +417,7 @@ int backward_impl(gpt2_ctx* c) {
                         c->NH, C, s);
     }
     ch = colsum_partials<TA>(dqkv, M, 3 * C, part, s);
-    colpart_reduce_add(c->G(T_QKVB, l), part, ch, 3 * C, 3 * C, s);
+    colpart_reduce_add(c->G(T_QKVB, l), nullptr, nullptr, part, ch, 3 * C, s);
     // QKV projection: qkv = LN1(x_in) Wqkv^T + bqkv
     if (!weight_grad(c, "gemm.bwd.qkv.dw", c->G(T_QKVW, l), dqkv, 3 * C, ln1, C, 3 * C, C, M)) return GPT2_ERR_ARG;
     g = gargs(dqkv, 3 * C, c->W(T_QKVW, l), C, M, C, 3 * C, c->dh, C);
@@ -400,9 +429,7 @@ int backward_impl(gpt2_ctx* c) {
                              c->ln1_rstd + (int64_t)l * c->Mmax, c->P(T_LN1W, l), c->dres, true, dres_act, part, M,
                              C, s);
     }
-    colpart_reduce_add(c->G(T_LN1W, l), part, ch, C, C, s);
-    colpart_reduce_add(c->G(T_LN1B, l), part + (int64_t)ch * C, ch, C, C, s);
-    if (l > 0) colpart_reduce_add(c->G(T_FCPB, l - 1), part + 2 * (int64_t)ch * C, ch, C, C, s);
+    colpart_reduce_add(c->G(T_LN1W, l), c->G(T_LN1B, l), l > 0 ? c->G(T_FCPB, l - 1) : nullptr, part, ch, C, s);
   }
   // embedding: x0 = wte[idx] + wpe[t]
   {
@@ -455,7 +482,7 @@ int64_t plan_workspace(gpt2_ctx* c, Plan& p, bool assign) {
   c->dqkv = at(M * 3 * C * A);
   c->dy = at(M * C * A);
   c->attnD = (float*)at(M * NH * 4);
-  c->splitk_elems = 16 * 4 * C * C;
+  c->splitk_elems = std::max<int64_t>(16 * 4 * C * C, 2 * Vp * C);
   c->splitk = (float*)at(c->splitk_elems * 4);
   const int64_t col_elems = std::max<int64_t>(3 * ((M + 31) / 32) * C, ((M + 63) / 64) * 4 * C);
   c->colpart = (float*)at(col_elems * 4);

@@ -38,6 +38,15 @@ struct GemmArgs {
 };
 // Returns false if the shape breaks a kernel precondition.
 bool gemm(GemmLayout layout, GemmEpilogue epi, bool bf16_mode, const GemmArgs& a, hipStream_t s);
+// Same with an explicit bf16 tile configuration (cfg < 0: automatic choice).
+bool gemm_cfg(int cfg, GemmLayout layout, GemmEpilogue epi, bool bf16_mode, const GemmArgs& a, hipStream_t s);
+// The tile configuration the automatic choice takes for these shapes, and the
+// modelled time of a configuration (seconds).
+int gemm_pick_config(const GemmArgs& a, bool transposed_a);
+double gemm_model_time(int cfg, const GemmArgs& a, bool transposed_a);
+constexpr int kGemmConfigs = 6;
+// Block tile of a configuration.
+void gemm_config_tile(int cfg, int* bm, int* bn);
 // out[i] += sum_{s < splits} part[s * stride + i], i < count (fixed order).
 void splitk_reduce_add(float* out, const float* part, int splits, int64_t stride, int64_t count,
                        hipStream_t s);
@@ -67,8 +76,10 @@ void layernorm_fwd(const float* x, const float* w, const float* b, TA* y, float*
 template <typename TA>
 int layernorm_bwd(const float* dy, const float* x, const float* mean, const float* rstd, const float* w,
                   float* dres, bool dres_in, TA* dres_act, float* part, int M, int C, hipStream_t s);
-// out[n] += sum_c part[c * ld + n], c < chunks, n < N.
-void colpart_reduce_add(float* out, const float* part, int chunks, int64_t ld, int N, hipStream_t s);
+// out_k[n] += sum_c part[(k * chunks + c) * N + n], c < chunks, n < N, for each non-null
+// out_k (k = 0, 1, 2; out1 / out2 may be null), summed in a fixed order.
+void colpart_reduce_add(float* out0, float* out1, float* out2, const float* part, int chunks, int N,
+                        hipStream_t s);
 // Column sums of an activation matrix (M x N, row-major) into partials [chunks][N];
 // returns the number of chunks.
 template <typename TA>

@@ -187,16 +187,37 @@ template int layernorm_bwd<float>(const float*, const float*, const float*, cons
 template int layernorm_bwd<bf16>(const float*, const float*, const float*, const float*, const float*, float*,
                                  bool, bf16*, float*, int, int, hipStream_t);
 
-__global__ void colpart_reduce_kernel(float* out, const float* part, int chunks, int64_t ld, int N) {
-  const int n = blockIdx.x * blockDim.x + threadIdx.x;
-  if (n >= N) return;
+// out_k[n] += sum_c part[(k * chunks + c) * N + n] for the arrays k < nout.
+// A block owns 64 columns of one array; its 16 thread groups sum interleaved
+// chunks, then the group sums are added in group order (fixed order).
+__global__ __launch_bounds__(1024) void colpart_reduce_kernel(float* out0, float* out1, float* out2,
+                                                              const float* __restrict__ part, int chunks, int N) {
+  __shared__ float red[16][64];
+  const int k = blockIdx.y;
+  float* out = k == 0 ? out0 : (k == 1 ? out1 : out2);
+  const int col = threadIdx.x & 63, grp = threadIdx.x >> 6;
+  const int n = blockIdx.x * 64 + col;
+  const float* p = part + (int64_t)k * chunks * N;
   float s = 0.f;
-  for (int c = 0; c < chunks; ++c) s += part[c * ld + n];
-  out[n] += s;
+  if (n < N) {
+#pragma unroll 8
+    for (int c = grp; c < chunks; c += 16) s += p[(int64_t)c * N + n];
+  }
+  red[grp][col] = s;
+  __syncthreads();
+  if (grp == 0 && n < N) {
+    float t = 0.f;
+#pragma unroll
+    for (int g = 0; g < 16; ++g) t += red[g][col];
+    out[n] += t;
+  }
 }
 
-void colpart_reduce_add(float* out, const float* part, int chunks, int64_t ld, int N, hipStream_t s) {
-  colpart_reduce_kernel<<<(N + 255) / 256, 256, 0, s>>>(out, part, chunks, ld, N);
+void colpart_reduce_add(float* out0, float* out1, float* out2, const float* part, int chunks, int N,
+                        hipStream_t s) {
+  const int nout = out2 ? 3 : (out1 ? 2 : 1);
+  dim3 grid((N + 63) / 64, nout);
+  colpart_reduce_kernel<<<grid, 1024, 0, s>>>(out0, out1, out2, part, chunks, N);
 }
 
 // Partial column sums: block (cb, chunk) covers 1024 columns x rows_per_chunk rows.
