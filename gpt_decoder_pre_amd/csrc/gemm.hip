@@ -10,6 +10,7 @@
 //
 // fp32 path: LDS-tiled FMA GEMM (64x64 tile, 4x4 outputs per thread).
 #include <cmath>
+#include <type_traits>
 
 #include "common.h"
 #include "kernels.h"
@@ -257,6 +258,239 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_bf16_kernel(GemmArgs p
   }
 }
 
+// --------------------------------------------- bf16 MFMA GEMM, LDS-direct ----
+// Operand tiles go from HBM to LDS with global_load_lds_dwordx4 (each lane
+// moves 16 bytes; a wave instruction fills 1 KB of LDS), NST stages deep, so
+// tiles kt+1 .. kt+NST-2 are in flight while tile kt is multiplied and no
+// VGPRs or LDS-store instructions are spent on staging.
+//   * k-contiguous operand: LDS rows of BK elements; the 16-byte chunks of a
+//     row are XOR-swizzled by the row so that the ds_read_b128 fragment reads
+//     of 16 consecutive rows hit distinct banks;
+//   * transposed operand (stored [k][rows] in HBM): LDS rows are k, laid out
+//     as in HBM (chunks swizzled by 2 (k mod 4)); fragments come from pairs of
+//     ds_read_b64_tr_b16, which hand each lane four consecutive k of one row.
+// Tiles are not zero-filled: rows past M or N are clamped to the last row
+// (their outputs are discarded), so K must be a multiple of BK.
+
+typedef short i16x4g __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4g lds_i16x4g;
+typedef __attribute__((address_space(3))) void lds_void;
+
+template <int BK>
+DEVI int kswz(int r) {
+  if constexpr (BK == 32) return ((r >> 1) ^ (r >> 3)) & 3;
+  else return (r ^ (r >> 3)) & 7;
+}
+DEVI int tswz(int k) { return 2 * (k & 3); }
+
+// Workgroup barrier without the release fence of __syncthreads (which would
+// drain every outstanding global->LDS load): ordering of LDS data across waves
+// comes from each wave's own vmcnt wait before the barrier, and the memory
+// clobber keeps the compiler from moving LDS accesses across it.
+DEVI void lds_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+// One global_load_lds_dwordx4: each lane moves 16 bytes from gptr to LDS
+// address m0 + 16 * lane (m0 = lds_base, wave-uniform).  Written as inline asm
+// so that the compiler does not treat it as an LDS store it must wait for
+// before every LDS read (it cannot tell the pipeline stages apart); the
+// kernel orders it with explicit vmcnt waits.  The instruction has no output
+// registers; its address registers are read at issue.
+DEVI void dma16(const void* gptr, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds_base), "v"(gptr) : "memory", "m0");
+}
+
+// vmcnt(n) with expcnt and lgkmcnt left alone (gfx9 encoding).
+template <int N>
+DEVI void wait_vmcnt() {
+  static_assert(N < 64, "vmcnt field");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// This wave's share of the direct loads of one R x BK operand tile.  The
+// per-lane source addresses are formed once; each k-tile adds its offset.
+template <bool KMAJ, int R, int BK, int NW>
+struct DirectLoader {
+  static constexpr int BYTES = R * BK * 2;
+  static constexpr int INSTR = BYTES / 1024;         // wave instructions per tile
+  static constexpr int PER_WAVE = INSTR / NW;
+  static_assert(INSTR % NW == 0, "tile splits evenly over the waves");
+  const bf16* src[PER_WAVE];
+  uint32_t lds[PER_WAVE];
+  int64_t kstep;  // elements between consecutive k-tiles
+
+  DEVI void init(const bf16* g, int64_t ld, int r0, int rmax, int kbeg, const bf16* lds_tile, int wave, int lane) {
+#pragma unroll
+    for (int j = 0; j < PER_WAVE; ++j) {
+      const int J = wave * PER_WAVE + j;
+      const int byte = J * 1024 + lane * 16;
+      if constexpr (KMAJ) {
+        const int r = byte / (BK * 2), pc = (byte % (BK * 2)) / 16;
+        const int c = pc ^ kswz<BK>(r);
+        const int row = min(r0 + r, rmax - 1);
+        src[j] = g + (int64_t)row * ld + kbeg + 8 * c;
+      } else {
+        const int k = byte / (R * 2), pc = (byte % (R * 2)) / 16;
+        const int c = pc ^ tswz(k);
+        const int col = min(r0 + 8 * c, rmax - 8);
+        src[j] = g + (int64_t)(kbeg + k) * ld + col;
+      }
+      lds[j] = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void*)(lds_tile + J * 512));
+    }
+    kstep = KMAJ ? (int64_t)BK : (int64_t)BK * ld;
+  }
+  // loads k-tile kt into the stage whose LDS byte offset from stage 0 is stage_off
+  DEVI void issue(int kt, uint32_t stage_off) const {
+    const int64_t off = kt * kstep;
+#pragma unroll
+    for (int j = 0; j < PER_WAVE; ++j) dma16(src[j] + off, lds[j] + stage_off);
+  }
+};
+
+// Fragment (eight consecutive k of one row, rows = lane % 32) for the 16-k step kk.
+template <bool KMAJ, int R, int BK>
+DEVI bf16x8 frag(const bf16* tile, int row0, int kk, int lane) {
+  if constexpr (KMAJ) {
+    const int r = row0 + (lane & 31);
+    const int c = 2 * kk + (lane >> 5);
+    return *reinterpret_cast<const bf16x8*>(tile + r * BK + 8 * (c ^ kswz<BK>(r)));
+  } else {
+    const int g = lane >> 4, s = lane & 15;
+    const int k = 16 * kk + 8 * (g >> 1) + (s >> 2);
+    const int m = row0 + 16 * (g & 1) + 4 * (s & 3);
+    const int c = m >> 3, o = m & 7;
+    const bf16* p1 = tile + k * R + 8 * (c ^ tswz(k)) + o;
+    const bf16* p2 = tile + (k + 4) * R + 8 * (c ^ tswz(k + 4)) + o;
+    const i16x4g a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4g*)p1);
+    const i16x4g b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4g*)p2);
+    const u32x2 ua = __builtin_bit_cast(u32x2, a), ub = __builtin_bit_cast(u32x2, b);
+    u32x4 v = {ua[0], ua[1], ub[0], ub[1]};
+    return __builtin_bit_cast(bf16x8, v);
+  }
+}
+
+template <bool A_K, bool B_K, int BM, int BN, int BK, int WGM, int WGN, int NST, int EPI>
+__global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_lds_kernel(GemmArgs p) {
+  static_assert(NST >= 2 && NST <= 4, "two to four stages");
+  constexpr int NW = WGM * WGN;
+  constexpr int WTM = BM / WGM, WTN = BN / WGN;
+  constexpr int FM = WTM / 32, FN = WTN / 32;
+  constexpr int STAGE = (BM + BN) * BK;
+  using LA = DirectLoader<A_K, BM, BK, NW>;
+  using LB = DirectLoader<B_K, BN, BK, NW>;
+  constexpr int LPW = LA::PER_WAVE + LB::PER_WAVE;  // loads per wave per tile
+  // One array per stage: every LDS access names its stage at compile time, so
+  // the compiler can tell the reads of stage s from the loads into the others.
+  __shared__ __attribute__((aligned(1024))) bf16 st0[STAGE];
+  __shared__ __attribute__((aligned(1024))) bf16 st1[STAGE];
+  __shared__ __attribute__((aligned(1024))) bf16 st2[NST > 2 ? STAGE : 1];
+  __shared__ __attribute__((aligned(1024))) bf16 st3[NST > 3 ? STAGE : 1];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / WGN, wn = wave % WGN;
+  const int lc = lane & 31, hl = lane >> 5;
+  const int tiles_m = (p.M + BM - 1) / BM, tiles_n = (p.N + BN - 1) / BN;
+  int tm, tn;
+  tile_coords(blockIdx.x, gridDim.x, tiles_m, tiles_n, tm, tn);
+  const int m0 = tm * BM, n0 = tn * BN;
+  const int split = blockIdx.y;
+  const int kbeg = split * p.k_per_split;
+  const int kend = min(p.K, kbeg + p.k_per_split);
+  const int nkt = kend > kbeg ? (kend - kbeg) / BK : 0;
+  const bf16* A = reinterpret_cast<const bf16*>(p.A);
+  const bf16* B = reinterpret_cast<const bf16*>(p.B);
+
+  auto stage = [&](auto S) -> bf16* {
+    constexpr int s = decltype(S)::value;
+    if constexpr (s == 0) return st0;
+    else if constexpr (s == 1) return st1;
+    else if constexpr (s == 2) return st2;
+    else return st3;
+  };
+  LA la;
+  LB lb;
+  la.init(A, p.lda, m0, p.M, kbeg, st0, wave, lane);
+  lb.init(B, p.ldb, n0, p.N, kbeg, st0 + BM * BK, wave, lane);
+  const uint32_t base0 = (uint32_t)(uintptr_t)(lds_void*)st0;
+  auto issue = [&](auto S, int kt) {
+    const uint32_t off = (uint32_t)(uintptr_t)(lds_void*)stage(S) - base0;
+    la.issue(kt, off);
+    lb.issue(kt, off);
+  };
+
+  f32x16 acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  // one k-tile on stage S: wait for its loads, free the oldest stage, refill it, multiply
+  auto step = [&](auto S, int kt) {
+    constexpr int s = decltype(S)::value;
+    const int ahead = min(nkt - 1, kt + NST - 2) - kt;
+    if constexpr (NST >= 4) {
+      if (ahead >= 2) wait_vmcnt<2 * LPW>();
+      else if (ahead == 1) wait_vmcnt<LPW>();
+      else wait_vmcnt<0>();
+    } else if constexpr (NST == 3) {
+      if (ahead >= 1) wait_vmcnt<LPW>();
+      else wait_vmcnt<0>();
+    } else {
+      wait_vmcnt<0>();
+    }
+    lds_barrier();  // every wave's loads of tile kt landed; the stage of tile kt-1 is free
+    if (kt + NST - 1 < nkt) issue(std::integral_constant<int, (s + NST - 1) % NST>{}, kt + NST - 1);
+    const bf16* sa = stage(S);
+    const bf16* sb = sa + BM * BK;
+#pragma unroll
+    for (int kk = 0; kk < BK / 16; ++kk) {
+      bf16x8 af[FM], bfr[FN];
+#pragma unroll
+      for (int i = 0; i < FM; ++i) af[i] = frag<A_K, BM, BK>(sa, wm * WTM + i * 32, kk, lane);
+#pragma unroll
+      for (int j = 0; j < FN; ++j) bfr[j] = frag<B_K, BN, BK>(sb, wn * WTN + j * 32, kk, lane);
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[j], af[i], acc[i][j], 0, 0, 0);
+    }
+  };
+
+  if (0 < nkt) issue(std::integral_constant<int, 0>{}, 0);
+  if (1 < nkt && NST > 2) issue(std::integral_constant<int, 1>{}, 1);
+  if constexpr (NST > 3)
+    if (2 < nkt) issue(std::integral_constant<int, 2>{}, 2);
+
+  for (int kt = 0; kt < nkt; kt += NST) {
+    step(std::integral_constant<int, 0>{}, kt);
+    if (kt + 1 < nkt) step(std::integral_constant<int, 1>{}, kt + 1);
+    if constexpr (NST > 2)
+      if (kt + 2 < nkt) step(std::integral_constant<int, 2>{}, kt + 2);
+    if constexpr (NST > 3)
+      if (kt + 3 < nkt) step(std::integral_constant<int, 3>{}, kt + 3);
+  }
+
+#pragma unroll
+  for (int i = 0; i < FM; ++i) {
+    const int m = m0 + wm * WTM + i * 32 + lc;
+    if (m >= p.M) continue;
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int n = n0 + wn * WTN + j * 32 + 8 * q + 4 * hl;
+        if (n < p.N) {
+          float v[4] = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+          epi_store4<EPI, bf16>(p, m, n, v, split);
+        }
+      }
+    }
+  }
+}
+
 // -------------------------------------------------------------- fp32 GEMM ----
 template <bool A_K, bool B_K, int EPI>
 __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs p) {
@@ -363,10 +597,35 @@ void launch_bf16_cfg(int cfg, const GemmArgs& a, hipStream_t s) {
     default: break;
   }
 #undef GPT2_GEMM_CFG
+#define GPT2_GEMM_LDS(ID, BM, BN, BK, WGM, WGN, NST)                                            \
+  case ID: {                                                                                   \
+    const int tiles = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);                           \
+    gemm_lds_kernel<A_K, B_K, BM, BN, BK, WGM, WGN, NST, EPI><<<dim3(tiles, a.splits), 64 * WGM * WGN, 0, s>>>(a); \
+    break;                                                                                     \
+  }
+  switch (cfg) {
+    GPT2_GEMM_LDS(6, 256, 256, 32, 2, 2, 4)
+    GPT2_GEMM_LDS(7, 256, 256, 32, 2, 4, 4)
+    GPT2_GEMM_LDS(8, 256, 256, 64, 2, 4, 2)
+    GPT2_GEMM_LDS(9, 256, 128, 32, 2, 2, 4)
+    GPT2_GEMM_LDS(10, 128, 256, 32, 2, 2, 4)
+    GPT2_GEMM_LDS(11, 256, 192, 32, 2, 2, 4)
+    GPT2_GEMM_LDS(12, 128, 128, 32, 2, 2, 4)
+    GPT2_GEMM_LDS(13, 256, 256, 64, 2, 2, 2)
+    GPT2_GEMM_LDS(14, 256, 256, 32, 2, 4, 3)
+    GPT2_GEMM_LDS(15, 256, 192, 64, 4, 2, 2)
+    GPT2_GEMM_LDS(16, 256, 128, 64, 4, 2, 3)
+    GPT2_GEMM_LDS(17, 128, 256, 64, 2, 4, 3)
+    GPT2_GEMM_LDS(18, 256, 256, 64, 4, 2, 2)
+    default: break;
+  }
+#undef GPT2_GEMM_LDS
 }
-constexpr int kNumCfg = 6;
-const int kCfgBM[kNumCfg] = {128, 256, 256, 256, 256, 128};
-const int kCfgBN[kNumCfg] = {128, 128, 256, 192, 256, 256};
+constexpr int kNumCfg = 19;
+constexpr int kFirstLds = 6;
+const int kCfgBM[kNumCfg] = {128, 256, 256, 256, 256, 128, 256, 256, 256, 256, 128, 256, 128, 256, 256, 256, 256, 128, 256};
+const int kCfgBN[kNumCfg] = {128, 128, 256, 192, 256, 256, 256, 256, 256, 128, 256, 192, 128, 256, 256, 192, 128, 256, 256};
+const int kCfgBK[kNumCfg] = {64, 64, 64, 64, 64, 64, 32, 32, 64, 32, 32, 32, 32, 64, 32, 64, 64, 64, 64};
 
 template <bool A_K, bool B_K, int EPI>
 void launch_f32(const GemmArgs& a, hipStream_t s) {
@@ -385,8 +644,11 @@ void launch(bool bf16_mode, int cfg, const GemmArgs& a, hipStream_t s) {
 // fill of the last wave of blocks over the 256 CUs and by the padding of
 // partial tiles.
 double model_time(int c, const GemmArgs& a, bool transposed_a) {
-  static const double tf_k[kNumCfg] = {560, 480, 650, 720, 750, 500};   // A stored k-contiguous
-  static const double tf_t[kNumCfg] = {450, 460, 660, 560, 640, 380};   // A stored transposed
+  // sustained TFLOP/s at full waves; 13 spills registers and is never chosen
+  static const double tf_k[kNumCfg] = {560, 480, 650, 720, 750, 500, 750, 800, 880, 650, 650, 930, 820,
+                                        1, 820, 1020, 760, 760, 900};  // A k-contiguous
+  static const double tf_t[kNumCfg] = {450, 460, 660, 560, 640, 380, 860, 880, 950, 740, 740, 900, 820,
+                                        1, 950, 930, 850, 900, 930};   // A transposed
   const int64_t tm = (a.M + kCfgBM[c] - 1) / kCfgBM[c], tn = (a.N + kCfgBN[c] - 1) / kCfgBN[c];
   const double waves = (double)(tm * tn * a.splits) / 256.0;
   const double fill = waves / std::ceil(waves);
@@ -398,6 +660,7 @@ int choose_cfg(const GemmArgs& a, bool transposed_a) {
   int pick = 0;
   double best = 1e30;
   for (int c = 0; c < kNumCfg; ++c) {
+    if (!gemm_config_usable(c, a)) continue;
     const double t = model_time(c, a, transposed_a);
     if (t < best) {
       best = t;
@@ -409,6 +672,12 @@ int choose_cfg(const GemmArgs& a, bool transposed_a) {
 }  // namespace
 
 int gemm_pick_config(const GemmArgs& a, bool transposed_a) { return choose_cfg(a, transposed_a); }
+
+bool gemm_config_usable(int cfg, const GemmArgs& a) {
+  if (cfg < 0 || cfg >= kNumCfg || cfg == 13) return false;
+  if (cfg >= kFirstLds && (a.K % kCfgBK[cfg] || a.k_per_split % kCfgBK[cfg])) return false;
+  return true;
+}
 
 double gemm_model_time(int cfg, const GemmArgs& a, bool transposed_a) { return model_time(cfg, a, transposed_a); }
 
@@ -430,6 +699,11 @@ bool gemm_cfg(int cfg, GemmLayout layout, GemmEpilogue epi, bool bf16_mode, cons
     if (layout == LAYOUT_TN && a.M % 8) return false;
     if (cfg < 0) cfg = choose_cfg(a, layout == LAYOUT_TN);
     if (cfg >= kNumCfg) return false;
+    // the LDS-direct kernels need whole k-tiles and whole 8-column chunks
+    if (cfg >= kFirstLds) {
+      if (a.K % kCfgBK[cfg] || a.k_per_split % kCfgBK[cfg]) return false;
+      if (layout != LAYOUT_TN && a.M < 1) return false;
+    }
   }
   switch (layout) {
     case LAYOUT_NT:

@@ -232,14 +232,15 @@ bool weight_grad(gpt2_ctx* c, const char* site, float* out, const void* A, int64
         if (splits > 1 && (int64_t)splits * outn > c->splitk_elems) continue;
         GemmArgs t = a;
         t.splits = splits;
-        t.k_per_split = kps;
+        t.k_per_split = splits > 1 ? kps : K;
+        if (!gemm_config_usable(cfg, t)) continue;
         double time = gemm_model_time(cfg, t, true);
         if (splits > 1) time += (2.0 * splits + 2.0) * outn * 4.0 / 4.0e12;
         if (time < best) {
           best = time;
           best_cfg = cfg;
           best_splits = splits;
-          best_kps = kps;
+          best_kps = t.k_per_split;
         }
       }
     }

@@ -44,7 +44,9 @@ bool gemm_cfg(int cfg, GemmLayout layout, GemmEpilogue epi, bool bf16_mode, cons
 // modelled time of a configuration (seconds).
 int gemm_pick_config(const GemmArgs& a, bool transposed_a);
 double gemm_model_time(int cfg, const GemmArgs& a, bool transposed_a);
-constexpr int kGemmConfigs = 6;
+// Whether a configuration can run these shapes.
+bool gemm_config_usable(int cfg, const GemmArgs& a);
+constexpr int kGemmConfigs = 19;
 // Block tile of a configuration.
 void gemm_config_tile(int cfg, int* bm, int* bn);
 // out[i] += sum_{s < splits} part[s * stride + i], i < count (fixed order).
