@@ -42,7 +42,29 @@ def parse():
     ap.add_argument("--site", default=ROOFLINE_SITE, help="launch-site prefix timed for the roofline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--breakdown", action="store_true", help="also time every launch site (extra pass)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="first run a plain 1 GiB device-to-device copy (scale reference for HBM byte counters)")
     return ap.parse_args()
+
+
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_fwd_lmhead_124m_traffic.md")
+TRAFFIC_SOURCE = os.path.join(ROOT, "gpt_decoder_pre_amd", "csrc", "gemm.hip")
+
+
+def measured_traffic(site):
+    """HBM bytes per launch of the roofline kernel from the committed rocprofv3
+    FETCH_SIZE / WRITE_SIZE summary, or None if there is none for this site or
+    the kernel source changed since the counters were taken."""
+    import hashlib
+    try:
+        lines = open(TRAFFIC_FILE).read().splitlines()
+        rec = json.loads(next(l for l in lines if l.startswith("traffic: "))[len("traffic: "):])
+        sha = hashlib.sha256(open(TRAFFIC_SOURCE, "rb").read()).hexdigest()
+    except (OSError, StopIteration, ValueError):
+        return None
+    if rec.get("site") != site or rec.get("source_sha256") != sha:
+        return None
+    return float(rec["bytes_per_launch"])
 
 
 def flops_per_token(s, T):
@@ -107,6 +129,13 @@ def main():
         step.accumulate(xs[i % nb], ys[i % nb])
         step.clip_adamw_step(run.lr, run.beta1, run.beta2, run.eps, run.weight_decay, run.max_norm)
 
+    if args.copy_calibration:
+        src = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
     for i in range(args.warmup):
         one_step(i)
     torch.cuda.synchronize()
@@ -141,7 +170,8 @@ def main():
         if k_flops > 0:
             ach = (k_flops / k_n) / (avg_ms / 1e3) / 1e12
             roof = {"bound": "mfma", "achieved": round(ach, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                    "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": None}
+                    "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": measured_traffic(args.site)}
+            roof["algorithmic_bytes"] = round(k_bytes / k_n)
         else:
             ach = (k_bytes / k_n) / (avg_ms / 1e3) / 1e9
             roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",

@@ -21,7 +21,9 @@ namespace gpt2k {
 template <int EPI, typename TA>
 DEVI void epi_store4(const GemmArgs& p, int m, int n, float v[4], int split) {
   const int64_t off = (int64_t)m * p.ldc + n;
-  if constexpr (EPI == EPI_ACT) {
+  if constexpr (EPI == EPI_LOGITS) {
+    store4(reinterpret_cast<TA*>(p.C) + off, v);
+  } else if constexpr (EPI == EPI_ACT) {
     if (p.bias) {
       float b[4];
       load4(p.bias + n, b);
@@ -70,7 +72,9 @@ DEVI void epi_store4(const GemmArgs& p, int m, int n, float v[4], int split) {
 template <int EPI, typename TA>
 DEVI void epi_store1(const GemmArgs& p, int m, int n, float v, int split) {
   const int64_t off = (int64_t)m * p.ldc + n;
-  if constexpr (EPI == EPI_ACT) {
+  if constexpr (EPI == EPI_LOGITS) {
+    reinterpret_cast<TA*>(p.C)[off] = from_f32<TA>(v);
+  } else if constexpr (EPI == EPI_ACT) {
     reinterpret_cast<TA*>(p.C)[off] = from_f32<TA>(p.bias ? v + p.bias[n] : v);
   } else if constexpr (EPI == EPI_F32) {
     reinterpret_cast<float*>(p.C)[off] = v;
@@ -708,6 +712,7 @@ bool gemm_cfg(int cfg, GemmLayout layout, GemmEpilogue epi, bool bf16_mode, cons
   switch (layout) {
     case LAYOUT_NT:
       if (epi == EPI_ACT) launch<true, true, EPI_ACT>(bf16_mode, cfg, a, s);
+      else if (epi == EPI_LOGITS) launch<true, true, EPI_LOGITS>(bf16_mode, cfg, a, s);
       else if (epi == EPI_RESID) launch<true, true, EPI_RESID>(bf16_mode, cfg, a, s);
       else if (epi == EPI_GELU) launch<true, true, EPI_GELU>(bf16_mode, cfg, a, s);
       else if (epi == EPI_F32) launch<true, true, EPI_F32>(bf16_mode, cfg, a, s);

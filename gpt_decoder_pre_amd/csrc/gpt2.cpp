@@ -339,7 +339,7 @@ int forward_impl(gpt2_ctx* c, const int32_t* d_idx, const int32_t* d_tgt, int B,
     layernorm_fwd<TA>(c->resid(2 * L), c->P(T_LNFW), c->P(T_LNFB), (TA*)c->lnf, c->lnf_mean, c->lnf_rstd, M, C, s);
   }
   GemmArgs g = gargs(c->lnf, C, c->W(T_WTE), C, M, Vp, C, c->logits, Vp);
-  if (!gemm_site(c, "gemm.fwd.lmhead", LAYOUT_NT, EPI_ACT, g, a * ((double)M * C + (double)Vp * C + (double)M * Vp)))
+  if (!gemm_site(c, "gemm.fwd.lmhead", LAYOUT_NT, EPI_LOGITS, g, a * ((double)M * C + (double)Vp * C + (double)M * Vp)))
     return GPT2_ERR_ARG;
   {
     Timed tm(c, "xent", 0, 2.0 * a * M * Vp + 8.0 * M);

@@ -21,6 +21,7 @@ enum GemmEpilogue {
   EPI_GELU = 4,      // u = acc + bias[n] -> C (act), gelu(u) -> C2 (act)
   EPI_GELU_BWD = 5,  // C (act) = acc * gelu'(aux[m][n])
   EPI_PARTIAL = 6,   // C (fp32) + split * split_stride = acc (split-K partial)
+  EPI_LOGITS = 7,    // C (activation type) = acc; the lm_head product (its own kernel symbol)
 };
 struct GemmArgs {
   const void* A;
