@@ -150,15 +150,25 @@ struct TileLoader {
   }
 };
 
-// Tile order: blocks are dealt round-robin to the eight XCDs (each with its
-// own L2), so block b is first renumbered to make every XCD own a contiguous
-// range of tiles; tiles are then walked in groups of GM tile-rows so that
+// Tile order.  The dispatcher deals workgroups round-robin to the eight XCDs
+// (each with its own L2) in linear block order, so the linear id is first
+// renumbered to give every XCD a contiguous range; that range is walked
+// split by split, and within a split in groups of GM tile-rows so that
 // neighbouring tiles share A rows and B columns in that XCD's L2.
-DEVI void tile_coords(int b, int nblk, int tiles_m, int tiles_n, int& tm, int& tn) {
-  constexpr int NX = 8, GM = 8;
-  const int xcd = b % NX, idx = b / NX;
-  const int q = nblk / NX, rem = nblk % NX;
-  const int t = xcd * q + min(xcd, rem) + idx;
+DEVI void tile_coords(const GemmArgs& p, int tiles_m, int tiles_n, int& tm, int& tn, int& split) {
+  constexpr int NX = 8;
+  const int nblk = gridDim.x * gridDim.y;
+  const int b = blockIdx.x + blockIdx.y * gridDim.x;
+  int t = b;
+  if (!p.no_xcd_map) {
+    const int xcd = b % NX, idx = b / NX;
+    const int q = nblk / NX, rem = nblk % NX;
+    t = xcd * q + min(xcd, rem) + idx;
+  }
+  const int tiles = tiles_m * tiles_n;
+  split = t / tiles;
+  t -= split * tiles;
+  const int GM = p.group_m > 0 ? p.group_m : 8;
   const int per_group = GM * tiles_n;
   const int g = t / per_group;
   const int first_m = g * GM;
@@ -181,10 +191,9 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_bf16_kernel(GemmArgs p
   const int wm = wave / WGN, wn = wave % WGN;
   const int lc = lane & 31, hl = lane >> 5;
   const int tiles_m = (p.M + BM - 1) / BM, tiles_n = (p.N + BN - 1) / BN;
-  int tm, tn;
-  tile_coords(blockIdx.x, gridDim.x, tiles_m, tiles_n, tm, tn);
+  int tm, tn, split;
+  tile_coords(p, tiles_m, tiles_n, tm, tn, split);
   const int m0 = tm * BM, n0 = tn * BN;
-  const int split = blockIdx.y;
   const int kbeg = split * p.k_per_split;
   const int kend = min(p.K, kbeg + p.k_per_split);
   const int nkt = kend > kbeg ? (kend - kbeg + BK - 1) / BK : 0;
@@ -394,10 +403,9 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_lds_kernel(GemmArgs p)
   const int wm = wave / WGN, wn = wave % WGN;
   const int lc = lane & 31, hl = lane >> 5;
   const int tiles_m = (p.M + BM - 1) / BM, tiles_n = (p.N + BN - 1) / BN;
-  int tm, tn;
-  tile_coords(blockIdx.x, gridDim.x, tiles_m, tiles_n, tm, tn);
+  int tm, tn, split;
+  tile_coords(p, tiles_m, tiles_n, tm, tn, split);
   const int m0 = tm * BM, n0 = tn * BN;
-  const int split = blockIdx.y;
   const int kbeg = split * p.k_per_split;
   const int kend = min(p.K, kbeg + p.k_per_split);
   const int nkt = kend > kbeg ? (kend - kbeg) / BK : 0;

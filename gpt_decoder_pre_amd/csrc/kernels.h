@@ -36,6 +36,8 @@ struct GemmArgs {
   int splits;
   int k_per_split;
   int64_t split_stride;
+  int group_m;     // tile-rows walked together (0: default 8)
+  int no_xcd_map;  // 1: keep the hardware block order (no per-XCD renumbering)
 };
 // Returns false if the shape breaks a kernel precondition.
 bool gemm(GemmLayout layout, GemmEpilogue epi, bool bf16_mode, const GemmArgs& a, hipStream_t s);

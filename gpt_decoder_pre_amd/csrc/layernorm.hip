@@ -11,9 +11,9 @@
 namespace gpt2k {
 
 constexpr float kLnEps = 1e-5f;
-constexpr int kMaxV = 8;  // float4 chunks per lane: C <= 64 * 4 * 8
 
-template <typename TA>
+// NV = float4 chunks per lane (C <= 256 NV); the row lives in registers.
+template <typename TA, int NV>
 __global__ __launch_bounds__(256) void ln_fwd_kernel(const float* __restrict__ x, const float* __restrict__ w,
                                                      const float* __restrict__ b, TA* __restrict__ y,
                                                      float* __restrict__ mean, float* __restrict__ rstd, int M,
@@ -23,10 +23,10 @@ __global__ __launch_bounds__(256) void ln_fwd_kernel(const float* __restrict__ x
   if (row >= M) return;
   const int C4 = C >> 2;
   const float* xr = x + (int64_t)row * C;
-  float v[kMaxV][4];
+  float v[NV][4];
   float s = 0.f;
 #pragma unroll
-  for (int i = 0; i < kMaxV; ++i) {
+  for (int i = 0; i < NV; ++i) {
     const int c4 = lane + i * 64;
     if (c4 < C4) {
       load4(xr + 4 * c4, v[i]);
@@ -36,7 +36,7 @@ __global__ __launch_bounds__(256) void ln_fwd_kernel(const float* __restrict__ x
   const float mu = wave_sum(s) / (float)C;
   float q = 0.f;
 #pragma unroll
-  for (int i = 0; i < kMaxV; ++i) {
+  for (int i = 0; i < NV; ++i) {
     const int c4 = lane + i * 64;
     if (c4 < C4) {
 #pragma unroll
@@ -50,7 +50,7 @@ __global__ __launch_bounds__(256) void ln_fwd_kernel(const float* __restrict__ x
   const float rs = 1.0f / sqrtf(var + kLnEps);
   TA* yr = y + (int64_t)row * C;
 #pragma unroll
-  for (int i = 0; i < kMaxV; ++i) {
+  for (int i = 0; i < NV; ++i) {
     const int c4 = lane + i * 64;
     if (c4 < C4) {
       float ww[4], bb[4], o[4];
@@ -70,7 +70,18 @@ __global__ __launch_bounds__(256) void ln_fwd_kernel(const float* __restrict__ x
 template <typename TA>
 void layernorm_fwd(const float* x, const float* w, const float* b, TA* y, float* mean, float* rstd, int M,
                    int C, hipStream_t s) {
-  ln_fwd_kernel<TA><<<(M + 3) / 4, 256, 0, s>>>(x, w, b, y, mean, rstd, M, C);
+#define GPT2_LN_ARGS (M + 3) / 4, 256, 0, s>>>(x, w, b, y, mean, rstd, M, C
+  switch ((C / 4 + 63) / 64) {
+    case 1: ln_fwd_kernel<TA, 1><<<GPT2_LN_ARGS); break;
+    case 2: ln_fwd_kernel<TA, 2><<<GPT2_LN_ARGS); break;
+    case 3: ln_fwd_kernel<TA, 3><<<GPT2_LN_ARGS); break;
+    case 4: ln_fwd_kernel<TA, 4><<<GPT2_LN_ARGS); break;
+    case 5: ln_fwd_kernel<TA, 5><<<GPT2_LN_ARGS); break;
+    case 6: ln_fwd_kernel<TA, 6><<<GPT2_LN_ARGS); break;
+    case 7: ln_fwd_kernel<TA, 7><<<GPT2_LN_ARGS); break;
+    default: ln_fwd_kernel<TA, 8><<<GPT2_LN_ARGS); break;
+  }
+#undef GPT2_LN_ARGS
 }
 template void layernorm_fwd<float>(const float*, const float*, const float*, float*, float*, float*, int, int,
                                    hipStream_t);
@@ -78,7 +89,7 @@ template void layernorm_fwd<bf16>(const float*, const float*, const float*, bf16
                                   hipStream_t);
 
 // dx = rstd (dxhat - mean(dxhat) - xhat mean(dxhat xhat)), dxhat = dy w.
-template <typename TA>
+template <typename TA, int NV>
 __global__ __launch_bounds__(256) void ln_bwd_kernel(const float* __restrict__ dy, const float* __restrict__ x,
                                                      const float* __restrict__ mean,
                                                      const float* __restrict__ rstd,
@@ -86,32 +97,36 @@ __global__ __launch_bounds__(256) void ln_bwd_kernel(const float* __restrict__ d
                                                      int dres_in, TA* __restrict__ dres_act,
                                                      float* __restrict__ part, int M, int C, int rows_per_block,
                                                      int chunks) {
-  __shared__ float red[3][2048];
+  __shared__ float red[3][NV * 256];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int C4 = C >> 2;
   const int r0 = blockIdx.x * rows_per_block;
   const int r1 = min(M, r0 + rows_per_block);
-  float aw[kMaxV][4], ab[kMaxV][4], ar[kMaxV][4], ww[kMaxV][4];
+  float aw[NV][4], ab[NV][4], ar[NV][4], ww[NV][4];
 #pragma unroll
-  for (int i = 0; i < kMaxV; ++i) {
+  for (int i = 0; i < NV; ++i) {
     const int c4 = lane + i * 64;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) aw[i][e] = ab[i][e] = ar[i][e] = 0.f;
+    for (int e = 0; e < 4; ++e) aw[i][e] = ab[i][e] = ar[i][e] = ww[i][e] = 0.f;
     if (c4 < C4) load4(w + 4 * c4, ww[i]);
   }
   for (int row = r0 + wave; row < r1; row += 4) {
     const float mu = mean[row], rs = rstd[row];
     const float* dyr = dy + (int64_t)row * C;
     const float* xr = x + (int64_t)row * C;
-    float g[kMaxV][4], xh[kMaxV][4];
+    float* dr = dres + (int64_t)row * C;
+    float g[NV][4], xh[NV][4], o[NV][4];
     float s1 = 0.f, s2 = 0.f;
 #pragma unroll
-    for (int i = 0; i < kMaxV; ++i) {
+    for (int i = 0; i < NV; ++i) {
       const int c4 = lane + i * 64;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) o[i][e] = 0.f;
       if (c4 < C4) {
         float xv[4];
         load4(dyr + 4 * c4, g[i]);
         load4(xr + 4 * c4, xv);
+        if (dres_in) load4(dr + 4 * c4, o[i]);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           xh[i][e] = (xv[e] - mu) * rs;
@@ -124,21 +139,18 @@ __global__ __launch_bounds__(256) void ln_bwd_kernel(const float* __restrict__ d
       }
     }
     const float m1 = wave_sum(s1) / (float)C, m2 = wave_sum(s2) / (float)C;
-    float* dr = dres + (int64_t)row * C;
     TA* da = dres_act + (int64_t)row * C;
 #pragma unroll
-    for (int i = 0; i < kMaxV; ++i) {
+    for (int i = 0; i < NV; ++i) {
       const int c4 = lane + i * 64;
       if (c4 < C4) {
-        float o[4] = {0.f, 0.f, 0.f, 0.f};
-        if (dres_in) load4(dr + 4 * c4, o);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          o[e] += rs * (g[i][e] * ww[i][e] - m1 - xh[i][e] * m2);
-          ar[i][e] += o[e];
+          o[i][e] += rs * (g[i][e] * ww[i][e] - m1 - xh[i][e] * m2);
+          ar[i][e] += o[i][e];
         }
-        store4(dr + 4 * c4, o);
-        store4(da + 4 * c4, o);
+        store4(dr + 4 * c4, o[i]);
+        store4(da + 4 * c4, o[i]);
       }
     }
   }
@@ -146,7 +158,7 @@ __global__ __launch_bounds__(256) void ln_bwd_kernel(const float* __restrict__ d
   for (int wv = 0; wv < 4; ++wv) {
     if (wave == wv) {
 #pragma unroll
-      for (int i = 0; i < kMaxV; ++i) {
+      for (int i = 0; i < NV; ++i) {
         const int c4 = lane + i * 64;
         if (c4 < C4) {
 #pragma unroll
@@ -178,8 +190,18 @@ int layernorm_bwd(const float* dy, const float* x, const float* mean, const floa
                   float* dres, bool dres_in, TA* dres_act, float* part, int M, int C, hipStream_t s) {
   const int rpb = 32;
   const int chunks = (M + rpb - 1) / rpb;
-  ln_bwd_kernel<TA><<<chunks, 256, 0, s>>>(dy, x, mean, rstd, w, dres, dres_in ? 1 : 0, dres_act, part, M, C,
-                                           rpb, chunks);
+#define GPT2_LN_ARGS chunks, 256, 0, s>>>(dy, x, mean, rstd, w, dres, dres_in ? 1 : 0, dres_act, part, M, C, rpb, chunks
+  switch ((C / 4 + 63) / 64) {
+    case 1: ln_bwd_kernel<TA, 1><<<GPT2_LN_ARGS); break;
+    case 2: ln_bwd_kernel<TA, 2><<<GPT2_LN_ARGS); break;
+    case 3: ln_bwd_kernel<TA, 3><<<GPT2_LN_ARGS); break;
+    case 4: ln_bwd_kernel<TA, 4><<<GPT2_LN_ARGS); break;
+    case 5: ln_bwd_kernel<TA, 5><<<GPT2_LN_ARGS); break;
+    case 6: ln_bwd_kernel<TA, 6><<<GPT2_LN_ARGS); break;
+    case 7: ln_bwd_kernel<TA, 7><<<GPT2_LN_ARGS); break;
+    default: ln_bwd_kernel<TA, 8><<<GPT2_LN_ARGS); break;
+  }
+#undef GPT2_LN_ARGS
   return chunks;
 }
 template int layernorm_bwd<float>(const float*, const float*, const float*, const float*, const float*, float*,
@@ -220,28 +242,36 @@ void colpart_reduce_add(float* out0, float* out1, float* out2, const float* part
   colpart_reduce_kernel<<<grid, 1024, 0, s>>>(out0, out1, out2, part, chunks, N);
 }
 
-// Partial column sums: block (cb, chunk) covers 1024 columns x rows_per_chunk rows.
+// Partial column sums: block (cb, chunk) covers 256 x W columns (W = 16 bytes
+// of elements per thread) x rows_per_chunk rows.
 template <typename TA>
 __global__ __launch_bounds__(256) void colsum_kernel(const TA* __restrict__ x, int M, int N, int rows_per_chunk,
                                                      float* __restrict__ part) {
-  const int c = (blockIdx.x * 256 + threadIdx.x) * 4;
+  constexpr int W = 16 / sizeof(TA);
+  const int c = (blockIdx.x * 256 + threadIdx.x) * W;
   if (c >= N) return;
   const int r0 = blockIdx.y * rows_per_chunk, r1 = min(M, r0 + rows_per_chunk);
-  float s[4] = {0.f, 0.f, 0.f, 0.f};
-  for (int r = r0; r < r1; ++r) {
-    float v[4];
-    load4(x + (int64_t)r * N + c, v);
+  float s[W];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) s[e] += v[e];
+  for (int e = 0; e < W; ++e) s[e] = 0.f;
+#pragma unroll 4
+  for (int r = r0; r < r1; ++r) {
+    float v[W];
+    load4(x + (int64_t)r * N + c, v);
+    if constexpr (W == 8) load4(x + (int64_t)r * N + c + 4, v + 4);
+#pragma unroll
+    for (int e = 0; e < W; ++e) s[e] += v[e];
   }
   store4(part + (int64_t)blockIdx.y * N + c, s);
+  if constexpr (W == 8) store4(part + (int64_t)blockIdx.y * N + c + 4, s + 4);
 }
 
 template <typename TA>
 int colsum_partials(const TA* x, int M, int N, float* part, hipStream_t s) {
+  constexpr int W = 16 / sizeof(TA);
   const int rpc = 64;
   const int chunks = (M + rpc - 1) / rpc;
-  dim3 grid((N / 4 + 255) / 256, chunks);
+  dim3 grid((N / W + 255) / 256, chunks);
   colsum_kernel<TA><<<grid, 256, 0, s>>>(x, M, N, rpc, part);
   return chunks;
 }

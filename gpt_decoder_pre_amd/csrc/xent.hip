@@ -1,15 +1,16 @@
 // Softmax cross-entropy over the padded vocabulary, fused with its gradient.
 //
-// One workgroup per row of logits.  Pass 1 keeps a running (max, sum of
-// exponentials) per thread (fp32, online softmax), combines them across the
-// block and forms the row's log-sum-exp; pass 2 overwrites the logits with
-// (softmax - onehot(target)) * grad_scale.  Max and sums stay in fp32 even
-// when the logits are bf16.
+// One workgroup per row of logits.  The row's max and sum of exponentials are
+// combined across the block (fp32 even for bf16 logits) into its
+// log-sum-exp, and the logits are overwritten with
+// (softmax - onehot(target)) * grad_scale.  bf16 rows stay in registers
+// between the two uses (one HBM read, one write); other rows are read twice.
 #include "common.h"
 #include "kernels.h"
 
 namespace gpt2k {
 
+// General path (any V): two passes over the row.
 template <typename TA, int VEC>
 __global__ __launch_bounds__(256) void xent_kernel(TA* __restrict__ logits, const int32_t* __restrict__ targets,
                                                    float* __restrict__ row_loss, int V, int vocab,
@@ -71,9 +72,101 @@ __global__ __launch_bounds__(256) void xent_kernel(TA* __restrict__ logits, cons
   }
 }
 
+// bf16 rows of up to 1024 x NCH x 8 elements: the row is read once into
+// registers (16-byte chunks, NCH per thread), the statistics come from the
+// registers, and the gradient is written from them: one read, one write.
+template <int NCH>
+__global__ __launch_bounds__(1024) void xent_bf16_resident_kernel(bf16* __restrict__ logits,
+                                                                 const int32_t* __restrict__ targets,
+                                                                 float* __restrict__ row_loss, int V, int vocab,
+                                                                 float grad_scale, int* __restrict__ err) {
+  __shared__ float red[16];
+  __shared__ float red2[16];
+  const int row = blockIdx.x;
+  bf16* z = logits + (int64_t)row * V;
+  int y = targets[row];
+  if (y < 0 || y >= vocab) {
+    if (threadIdx.x == 0) *err = 1;
+    y = 0;
+  }
+  const int nchunk = V / 8;
+  u32x4 r[NCH];
+#pragma unroll
+  for (int i = 0; i < NCH; ++i) {
+    const int c = threadIdx.x + i * 1024;
+    r[i] = ld16_or_zero(z + 8 * c, c < nchunk);
+  }
+  float m = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < NCH; ++i) {
+    const int c = threadIdx.x + i * 1024;
+    if (c < nchunk) {
+      const bf16x8 v = __builtin_bit_cast(bf16x8, r[i]);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) m = fmaxf(m, (float)v[e]);
+    }
+  }
+  const float M = block_max(m, red);
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < NCH; ++i) {
+    const int c = threadIdx.x + i * 1024;
+    if (c < nchunk) {
+      const bf16x8 v = __builtin_bit_cast(bf16x8, r[i]);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) s += exp2_fast(((float)v[e] - M) * kLog2e);
+    }
+  }
+  const float S = block_sum(s, red2);
+  const float lse = M + logf(S);
+  if (threadIdx.x == (y / 8) % 1024) {
+    float zy = 0.f;
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      if (i == (y / 8) / 1024) {
+        const bf16x8 v = __builtin_bit_cast(bf16x8, r[i]);
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if (e == y % 8) zy = (float)v[e];
+      }
+    }
+    row_loss[row] = lse - zy;
+  }
+  const float l2 = lse * kLog2e;
+#pragma unroll
+  for (int i = 0; i < NCH; ++i) {
+    const int c = threadIdx.x + i * 1024;
+    if (c < nchunk) {
+      const bf16x8 v = __builtin_bit_cast(bf16x8, r[i]);
+      bf16x8 o;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float p = exp2_fast((float)v[e] * kLog2e - l2);
+        o[e] = (bf16)((p - (8 * c + e == y ? 1.f : 0.f)) * grad_scale);
+      }
+      *reinterpret_cast<bf16x8*>(z + 8 * c) = o;
+    }
+  }
+}
+
 template <typename TA>
 void xent_fwd_bwd(TA* logits, const int32_t* targets, float* row_loss, int M, int V, int vocab, float grad_scale,
                   int* err, hipStream_t s) {
+  if constexpr (sizeof(TA) == 2) {
+    if (V % 8 == 0 && V <= 1024 * 8 * 8) {
+      const int nch = (V / 8 + 1023) / 1024;
+      if (nch <= 2) {
+        xent_bf16_resident_kernel<2><<<M, 1024, 0, s>>>(logits, targets, row_loss, V, vocab, grad_scale, err);
+      } else if (nch <= 4) {
+        xent_bf16_resident_kernel<4><<<M, 1024, 0, s>>>(logits, targets, row_loss, V, vocab, grad_scale, err);
+      } else if (nch <= 7) {
+        xent_bf16_resident_kernel<7><<<M, 1024, 0, s>>>(logits, targets, row_loss, V, vocab, grad_scale, err);
+      } else {
+        xent_bf16_resident_kernel<8><<<M, 1024, 0, s>>>(logits, targets, row_loss, V, vocab, grad_scale, err);
+      }
+      return;
+    }
+  }
   if (V % 8 == 0) xent_kernel<TA, 8><<<M, 256, 0, s>>>(logits, targets, row_loss, V, vocab, grad_scale, err);
   else xent_kernel<TA, 1><<<M, 256, 0, s>>>(logits, targets, row_loss, V, vocab, grad_scale, err);
 }
