@@ -48,19 +48,26 @@ constexpr float kLn2 = 0.6931471805599453f;     // ln(2)
 DEVI float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 DEVI float exp_fast(float x) { return __builtin_amdgcn_exp2f(x * kLog2e); }
 
-// tanh(a) = 1 - 2 / (e^{2a} + 1): exact limits +-1 for large |a|.
-DEVI float tanh_fast(float a) { return 1.0f - 2.0f / (exp_fast(2.0f * a) + 1.0f); }
+DEVI float rcp_fast(float x) { return __builtin_amdgcn_rcpf(x); }  // v_rcp_f32
 
-// tanh-form GELU and its derivative: u -> 0.5 u (1 + tanh(k (u + 0.044715 u^3))).
+// tanh-form GELU, 0.5 u (1 + tanh(k (u + 0.044715 u^3))), k = sqrt(2/pi),
+// evaluated as u * sigmoid(z) with z = 2 k (u + 0.044715 u^3), because
+// 0.5 (1 + tanh(z / 2)) = sigmoid(z):  one exp2 and one reciprocal.
+// Large |u| saturate cleanly: exp2 -> inf gives sigmoid 0, exp2 -> 0 gives 1.
 constexpr float kGeluK = 0.7978845608028654f;  // sqrt(2 / pi)
 constexpr float kGeluA = 0.044715f;
-DEVI float gelu_f(float u) {
-  float t = tanh_fast(kGeluK * (u + kGeluA * u * u * u));
-  return 0.5f * u * (1.0f + t);
+constexpr float kGeluZ1 = -2.0f * kGeluK * kLog2e;           // -z / ln 2 per unit u
+constexpr float kGeluZ3 = -2.0f * kGeluK * kGeluA * kLog2e;  // ... per unit u^3
+DEVI float gelu_sigmoid(float u) {
+  const float t = u * u;
+  return rcp_fast(1.0f + exp2_fast(u * fmaf(kGeluZ3, t, kGeluZ1)));
 }
+DEVI float gelu_f(float u) { return u * gelu_sigmoid(u); }
+// d/du [u sigmoid(z)] = s + u s (1 - s) dz/du,  dz/du = 2 k (1 + 3 * 0.044715 u^2)
 DEVI float gelu_grad_f(float u) {
-  float t = tanh_fast(kGeluK * (u + kGeluA * u * u * u));
-  return 0.5f * (1.0f + t) + 0.5f * u * (1.0f - t * t) * kGeluK * (1.0f + 3.0f * kGeluA * u * u);
+  const float s = gelu_sigmoid(u);
+  const float dz = 2.0f * kGeluK * fmaf(3.0f * kGeluA, u * u, 1.0f);
+  return fmaf(u * s * (1.0f - s), dz, s);
 }
 
 // ---- wave / block reductions ---------------------------------------------------

@@ -155,10 +155,9 @@ struct TileLoader {
 // renumbered to give every XCD a contiguous range; that range is walked
 // split by split, and within a split in groups of GM tile-rows so that
 // neighbouring tiles share A rows and B columns in that XCD's L2.
-DEVI void tile_coords(const GemmArgs& p, int tiles_m, int tiles_n, int& tm, int& tn, int& split) {
+DEVI void tile_coords(const GemmArgs& p, int tiles_m, int tiles_n, int b, int nblk, int& tm, int& tn,
+                      int& split) {
   constexpr int NX = 8;
-  const int nblk = gridDim.x * gridDim.y;
-  const int b = blockIdx.x + blockIdx.y * gridDim.x;
   int t = b;
   if (!p.no_xcd_map) {
     const int xcd = b % NX, idx = b / NX;
@@ -192,7 +191,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_bf16_kernel(GemmArgs p
   const int lc = lane & 31, hl = lane >> 5;
   const int tiles_m = (p.M + BM - 1) / BM, tiles_n = (p.N + BN - 1) / BN;
   int tm, tn, split;
-  tile_coords(p, tiles_m, tiles_n, tm, tn, split);
+  tile_coords(p, tiles_m, tiles_n, blockIdx.x + blockIdx.y * gridDim.x, gridDim.x * gridDim.y, tm, tn, split);
   const int m0 = tm * BM, n0 = tn * BN;
   const int kbeg = split * p.k_per_split;
   const int kend = min(p.K, kbeg + p.k_per_split);
@@ -355,7 +354,7 @@ struct DirectLoader {
   DEVI void issue(int kt, uint32_t stage_off) const {
     const int64_t off = kt * kstep;
 #pragma unroll
-    for (int j = 0; j < PER_WAVE; ++j) dma16(src[j] + off, lds[j] + stage_off);
+    for (int j = 0; j < PER_WAVE; ++j) dma16(src[j] + off, __builtin_amdgcn_readfirstlane(lds[j] + stage_off));
   }
 };
 
@@ -404,7 +403,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_lds_kernel(GemmArgs p)
   const int lc = lane & 31, hl = lane >> 5;
   const int tiles_m = (p.M + BM - 1) / BM, tiles_n = (p.N + BN - 1) / BN;
   int tm, tn, split;
-  tile_coords(p, tiles_m, tiles_n, tm, tn, split);
+  tile_coords(p, tiles_m, tiles_n, blockIdx.x + blockIdx.y * gridDim.x, gridDim.x * gridDim.y, tm, tn, split);
   const int m0 = tm * BM, n0 = tn * BN;
   const int kbeg = split * p.k_per_split;
   const int kend = min(p.K, kbeg + p.k_per_split);
@@ -485,18 +484,94 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_lds_kernel(GemmArgs p)
       if (kt + 3 < nkt) step(std::integral_constant<int, 3>{}, kt + 3);
   }
 
+  // bf16 outputs are staged through LDS so that every store instruction
+  // writes whole row segments (16 bytes per lane along n) instead of 16 bytes
+  // into each of 32 rows; lines then reach L2 complete.
+  constexpr bool kBf16Out = EPI == EPI_ACT || EPI == EPI_LOGITS || EPI == EPI_GELU || EPI == EPI_GELU_BWD;
+  constexpr int SLD = WTN + 8;                       // staged row stride (elements)
+  constexpr int WPA = (NW + 1) / 2;                  // waves per stage array
+  constexpr bool kStage = kBf16Out && WPA * WTM * SLD <= STAGE;
+  if constexpr (kStage) {
+    __syncthreads();  // all waves are done reading the operand stages
+    bf16* region = (wave < WPA ? st0 : st1) + (wave % WPA) * WTM * SLD;
+    constexpr int NOUT = EPI == EPI_GELU ? 2 : 1;
+    constexpr int CPR = WTN / 8;  // 16-byte chunks per staged row
+    if constexpr (EPI == EPI_GELU_BWD) {
+      // the pre-activation tile u comes in whole row segments too
+      const bf16* aux = reinterpret_cast<const bf16*>(p.aux);
 #pragma unroll
-  for (int i = 0; i < FM; ++i) {
-    const int m = m0 + wm * WTM + i * 32 + lc;
-    if (m >= p.M) continue;
+      for (int it = 0; it < WTM * CPR / 64; ++it) {
+        const int q = it * 64 + lane;
+        const int r = q / CPR, c = q % CPR;
+        const int m = m0 + wm * WTM + r, n = n0 + wn * WTN + 8 * c;
+        *reinterpret_cast<u32x4*>(region + r * SLD + 8 * c) =
+            ld16_or_zero(aux + (int64_t)m * p.ldc + n, m < p.M && n < p.N);
+      }
+      __builtin_amdgcn_s_waitcnt(0xc07f);
+      __builtin_amdgcn_wave_barrier();
+    }
 #pragma unroll
-    for (int j = 0; j < FN; ++j) {
+    for (int o = 0; o < NOUT; ++o) {
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int n = n0 + wn * WTN + j * 32 + 8 * q + 4 * hl;
-        if (n < p.N) {
-          float v[4] = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
-          epi_store4<EPI, bf16>(p, m, n, v, split);
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int nl = j * 32 + 8 * q + 4 * hl;
+            const int n = n0 + wn * WTN + nl;
+            float v[4] = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+            if constexpr (EPI == EPI_ACT || EPI == EPI_GELU) {
+              if (p.bias && n < p.N) {
+                float bb[4];
+                load4(p.bias + n, bb);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) v[e] += bb[e];
+              }
+            }
+            if constexpr (EPI == EPI_GELU) {
+              if (o == 1) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) v[e] = gelu_f(v[e]);
+              }
+            }
+            if constexpr (EPI == EPI_GELU_BWD) {
+              float u[4];
+              load4(region + (i * 32 + lc) * SLD + nl, u);
+#pragma unroll
+              for (int e = 0; e < 4; ++e) v[e] *= gelu_grad_f(u[e]);
+            }
+            store4(region + (i * 32 + lc) * SLD + nl, v);
+          }
+      __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's LDS writes are done
+      __builtin_amdgcn_wave_barrier();
+      bf16* out = reinterpret_cast<bf16*>(o == 0 ? p.C : p.C2);
+#pragma unroll
+      for (int it = 0; it < WTM * CPR / 64; ++it) {
+        const int q = it * 64 + lane;
+        const int r = q / CPR, c = q % CPR;
+        const int m = m0 + wm * WTM + r, n = n0 + wn * WTN + 8 * c;
+        if (m < p.M && n < p.N)
+          *reinterpret_cast<u32x4*>(out + (int64_t)m * p.ldc + n) =
+              *reinterpret_cast<const u32x4*>(region + r * SLD + 8 * c);
+      }
+      __builtin_amdgcn_s_waitcnt(0xc07f);
+      __builtin_amdgcn_wave_barrier();
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      const int m = m0 + wm * WTM + i * 32 + lc;
+      if (m >= p.M) continue;
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int n = n0 + wn * WTN + j * 32 + 8 * q + 4 * hl;
+          if (n < p.N) {
+            float v[4] = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+            epi_store4<EPI, bf16>(p, m, n, v, split);
+          }
         }
       }
     }
@@ -687,7 +762,12 @@ int gemm_pick_config(const GemmArgs& a, bool transposed_a) { return choose_cfg(a
 
 bool gemm_config_usable(int cfg, const GemmArgs& a) {
   if (cfg < 0 || cfg >= kNumCfg || cfg == 13) return false;
-  if (cfg >= kFirstLds && (a.K % kCfgBK[cfg] || a.k_per_split % kCfgBK[cfg])) return false;
+  if (cfg >= kFirstLds) {
+    // whole k-tiles, and every split the same length (the persistent walk
+    // gives each tile the same number of k-steps)
+    if (a.K % kCfgBK[cfg] || a.k_per_split % kCfgBK[cfg]) return false;
+    if (a.splits > 1 && a.K != a.splits * a.k_per_split) return false;
+  }
   return true;
 }
 
@@ -710,12 +790,7 @@ bool gemm_cfg(int cfg, GemmLayout layout, GemmEpilogue epi, bool bf16_mode, cons
     if (a.K % 8 || a.N % 8 || a.ldc % 4 || a.lda % 8 || a.ldb % 8) return false;
     if (layout == LAYOUT_TN && a.M % 8) return false;
     if (cfg < 0) cfg = choose_cfg(a, layout == LAYOUT_TN);
-    if (cfg >= kNumCfg) return false;
-    // the LDS-direct kernels need whole k-tiles and whole 8-column chunks
-    if (cfg >= kFirstLds) {
-      if (a.K % kCfgBK[cfg] || a.k_per_split % kCfgBK[cfg]) return false;
-      if (layout != LAYOUT_TN && a.M < 1) return false;
-    }
+    if (!gemm_config_usable(cfg, a)) return false;
   }
   switch (layout) {
     case LAYOUT_NT:
