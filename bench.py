@@ -184,7 +184,10 @@ def main():
     if args.breakdown:
         breakdown = {}
         for site in ("gemm.fwd", "gemm.bwd", "attn.fwd", "attn.bwd", "ln.fwd", "ln.bwd", "xent", "embed.bwd",
-                     "norm", "adamw"):
+                     "norm", "adamw", "gemm.fwd.qkv", "gemm.fwd.proj", "gemm.fwd.fc", "gemm.fwd.fcproj",
+                     "gemm.fwd.lmhead", "gemm.bwd.lmhead.dx", "gemm.bwd.lmhead.dw", "gemm.bwd.fcproj.dx",
+                     "gemm.bwd.fcproj.dw", "gemm.bwd.fc.dx", "gemm.bwd.fc.dw", "gemm.bwd.proj.dx", "gemm.bwd.proj.dw",
+                     "gemm.bwd.qkv.dx", "gemm.bwd.qkv.dw"):
             step.timing_enable(site)
             one_step(0)
             sm, sn, sf, sb = step.timing_read()

@@ -17,6 +17,7 @@
 // scores of the row in LDS; plain fp32 arithmetic for the exact-mode step.
 #include "common.h"
 #include "kernels.h"
+#include "lds_tile.h"
 
 namespace gpt2k {
 
@@ -80,15 +81,126 @@ struct TileRegs {
 
 // ------------------------------------------------------------------ forward ----
 // Workgroup: 128 queries of one (sequence, head); wave w owns queries
-// q0 + 32 w + lane%32.  K and V tiles of 64 keys are double-buffered in LDS;
-// the next tile's loads are in flight while the current one is used.
-__global__ __launch_bounds__(256, 2) void flash_fwd_kernel(const bf16* __restrict__ qkv, bf16* __restrict__ y,
+// q0 + 32 w + lane%32.  K and V tiles of 64 keys go from HBM straight to LDS
+// (global_load_lds), three stages deep.  The scores of key tile j+1 are
+// multiplied while the softmax of tile j runs on the vector ALUs, and the
+// probabilities of tile j then feed the V product from registers.
+//
+// Softmax in the exp2 domain with a lazily updated running max: the max m is
+// raised only when a tile's max exceeds it by more than kLazy (then o and l
+// are rescaled), so exponents stay below 2^kLazy and most tiles skip the
+// rescale.  The result is the same up to rounding: o and l share the factor.
+
+constexpr int ATILE = 64 * 64;     // one 64 x 64 bf16 tile, swizzled, unpadded
+constexpr int ASTAGE = 2 * ATILE;  // K | V (or Q | dO)
+constexpr float kLazy = 8.0f;
+
+// This wave's two 1 KB loads of a 64-row tile of one head (rows r0.. of a
+// [T][ld] matrix): chunks swizzled by kswz (tile read row-wise) or tswz (tile
+// read transposed).  The per-lane byte offsets within a tile do not depend on
+// r0, so they are formed once; a tile adds the wave-uniform r0 * ld to the
+// scalar base.  Rows past T (only in a partial last tile) are clamped to T - 1.
+template <bool ROWWISE>
+struct AttnTileLoader {
+  uint32_t off[2];  // lane byte offsets of the two loads, relative to row r0
+  DEVI static void place(int wave, int lane, int j, int& r, int& c8) {
+    const int byte = (2 * wave + j) * 1024 + lane * 16;
+    r = byte >> 7;
+    const int pc = (byte >> 4) & 7;
+    c8 = 8 * (pc ^ (ROWWISE ? kswz<64>(r) : tswz(r)));
+  }
+  DEVI void init(int64_t ld, int wave, int lane) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      int r, c8;
+      place(wave, lane, j, r, c8);
+      off[j] = (uint32_t)(2 * ((int64_t)r * ld + c8));
+    }
+  }
+  DEVI void issue(const bf16* g, int64_t ld, int r0, int T, uint32_t lds_tile, int wave, int lane) const {
+    if (r0 + 64 <= T) {
+      const bf16* b = uniform_ptr(g + (int64_t)r0 * ld);
+#pragma unroll
+      for (int j = 0; j < 2; ++j) dma16s(b, off[j], lds_tile + (2 * wave + j) * 1024);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        int r, c8;
+        place(wave, lane, j, r, c8);
+        dma16(g + (int64_t)min(r0 + r, T - 1) * ld + c8, lds_tile + (2 * wave + j) * 1024);
+      }
+    }
+  }
+};
+
+// A operand of a product over keys from a tile stored [key][d] (tswz layout):
+// rows d = mbase + lane%32, and the eight keys of the 16-key step kbase in the
+// order the score accumulators hold them: kbase + 4 hl + {0..3} and
+// kbase + 8 + 4 hl + {0..3}.  ds_read_b64_tr_b16 hands lane j of each 16-lane
+// group element i of source lane 4i + j/4's 8-byte row, so source lane 4i + q
+// points at (key kb + i, d m16 + 4q).
+DEVI bf16x8 tr_frag_keys(const bf16* tile, int kbase, int mbase, int lane) {
+  const int g = lane >> 4, s = lane & 15;
+  const int k = kbase + 4 * (g >> 1) + (s >> 2);
+  const int m = mbase + 16 * (g & 1) + 4 * (s & 3);
+  const int c = m >> 3, o = m & 7;
+  const bf16* p = tile + k * 64 + 8 * (c ^ tswz(k)) + o;  // tswz(k + 8) == tswz(k)
+  const i16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p));
+  const i16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p + 8 * 64));
+  const u32x2 ua = __builtin_bit_cast(u32x2, a), ub = __builtin_bit_cast(u32x2, b);
+  u32x4 r = {ua[0], ua[1], ub[0], ub[1]};
+  return as_bf16x8(r);
+}
+
+// acc + the sum of eight bf16 values (four v_dot2c_f32_bf16 against ones)
+DEVI float sum_bf16x8(bf16x8 v, float acc) {
+  typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+  const bf16x2v one = {(bf16)1.0f, (bf16)1.0f};
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const bf16x2v pair = {v[2 * e], v[2 * e + 1]};
+    acc = __builtin_amdgcn_fdot2_f32_bf16(pair, one, acc, false);
+  }
+  return acc;
+}
+
+// Workgroups are dispatched to the eight XCDs round-robin in launch order,
+// and each XCD has its own L2.  Block b of a 1-D grid of n runs as logical
+// block (b % 8) (n / 8) + b / 8, so each XCD works through a contiguous range
+// of logical blocks: the tiles of one (sequence, head), which all re-read the
+// same K and V (or Q and dO), then share one L2.  Identity unless n % 8 == 0.
+DEVI int xcd_block(int b, int n) { return (n % 8 == 0) ? (b % 8) * (n / 8) + b / 8 : b; }
+
+// Logical block -> (tile index within the head, head, sequence); tiles of a
+// head are consecutive.
+DEVI void attn_block(int T, int NH, int& tile, int& h, int& b) {
+  const int nq = (T + 127) / 128;
+  const int L = xcd_block(blockIdx.x, gridDim.x);
+  const int bh = L / nq;
+  tile = L - bh * nq;
+  h = bh % NH;
+  b = bh / NH;
+}
+
+// max / sum of a value and its copy in the lane 32 apart (same query row)
+DEVI float halves_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+DEVI float halves_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+__global__ __launch_bounds__(256, 3) void flash_fwd_kernel(const bf16* __restrict__ qkv, bf16* __restrict__ y,
                                                            float* __restrict__ lse, int T, int NH, int C,
                                                            float sl2) {
-  __shared__ __attribute__((aligned(16))) bf16 smem[4 * TILE];  // [stage][K | V]
-  const int qt = gridDim.x - 1 - blockIdx.x;  // longest rows first
-  const int h = blockIdx.y, b = blockIdx.z;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, lc = lane & 31, hl = lane >> 5;
+  __shared__ __attribute__((aligned(1024))) bf16 smem[3 * ASTAGE];  // [stage][K | V]
+  int qt, h, b;
+  attn_block(T, NH, qt, h, b);
+  qt = (T + 127) / 128 - 1 - qt;  // longest rows first within a head
+  const int tid = threadIdx.x, lane = tid & 63, lc = lane & 31, hl = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int q0 = qt * 128;
   const int wq0 = q0 + wave * 32;
   const int myq = wq0 + lc;
@@ -96,101 +208,125 @@ __global__ __launch_bounds__(256, 2) void flash_fwd_kernel(const bf16* __restric
   const bf16* Q = qkv + (int64_t)b * T * ld + h * HD;
   const bf16* K = Q + C;
   const bf16* V = Q + 2 * C;
+  const uint32_t lds0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void*)smem);
+
+  const int nkt = (min(T, q0 + 128) + 63) / 64;            // key tiles of the workgroup
+  AttnTileLoader<true> lk;
+  AttnTileLoader<false> lv;
+  lk.init(ld, wave, lane);
+  lv.init(ld, wave, lane);
+  auto load = [&](int j, int stg) {
+    const uint32_t base = lds0 + stg * (ASTAGE * 2);
+    lk.issue(K, ld, j * 64, T, base, wave, lane);
+    lv.issue(V, ld, j * 64, T, base + ATILE * 2, wave, lane);
+  };
+  load(0, 0);
+  if (nkt > 1) load(1, 1);
 
   bf16x8 qf[4];
 #pragma unroll
   for (int kk = 0; kk < 4; ++kk) qf[kk] = as_bf16x8(ld16_or_zero(Q + (int64_t)myq * ld + kk * 16 + hl * 8, myq < T));
 
+  // S^T = K Q^T for tile j: s[js][r] is key 64 j + 32 js + 8 (r/4) + 4 hl + r%4, query myq
+  auto scores = [&](int stg, f32x16 (&s)[2]) {
+    const bf16* Ks = smem + stg * ASTAGE;
+#pragma unroll
+    for (int js = 0; js < 2; ++js) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[js][r] = 0.f;
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk)
+        s[js] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag<true, 64, 64>(Ks, js * 32, kk, lane), qf[kk], s[js], 0,
+                                                        0, 0);
+    }
+  };
+
+  // o: O^T (d 0..31, 32..63); lrow: this lane's share of the softmax
+  // denominator, summed from the bf16 probabilities the V product uses
   f32x16 o[2];
 #pragma unroll
   for (int r = 0; r < 16; ++r) o[0][r] = o[1][r] = 0.f;
   float mrow = -INFINITY, lrow = 0.f;
-  const int kv_end = min(T, q0 + 128);
-  const int nkt = (kv_end + 63) / 64;
-  TileRegs tk, tv;
-  tk.load(K, ld, 0, T, tid);
-  tv.load(V, ld, 0, T, tid);
-  tk.store(smem, tid);
-  tv.store(smem + TILE, tid);
-  __syncthreads();
-  for (int kt = 0; kt < nkt; ++kt) {
-    const int k0 = kt * 64;
-    const bool more = kt + 1 < nkt;
-    if (more) {
-      tk.load(K, ld, k0 + 64, T, tid);
-      tv.load(V, ld, k0 + 64, T, tid);
-    }
-    const bf16* Ks = smem + (kt & 1) * 2 * TILE;
-    const bf16* Vs = Ks + TILE;
-    if (k0 <= wq0 + 31) {  // some key of the tile is visible to this wave
-      f32x16 s[2];
+  const int qlim = min(myq, T - 1);  // last key this query sees
+
+  // Iteration j finishes tile j (scores in cur) and multiplies the scores of
+  // tile j+1 (into nxt) in between: mask, row max and (rarely) the rescale
+  // first, then one block in which the MFMAs of tile j+1 interleave with the
+  // exponentials of tile j, then O^T += V^T P^T.  Before that, tile j+1 is
+  // made resident (its loads waited for, then the barrier) and tile j+2 is
+  // loaded into the stage tile j-1 used (every wave is past iteration j-1).
+  // Waves whose queries see none of tile j compute it anyway: every score is
+  // masked, so it adds nothing.  Each wave issues four loads per tile.
+  auto iteration = [&](int j, int stg, f32x16 (&cur)[2], f32x16 (&nxt)[2]) {
+    const int stg1 = stg == 2 ? 0 : stg + 1, stg2 = stg1 == 2 ? 0 : stg1 + 1;
+    if (j + 1 < nkt) wait_vmcnt<0>();
+    lds_barrier();
+    if (j + 2 < nkt) load(j + 2, stg2);
+    const int k0 = j * 64;
+    if (k0 + 63 > wq0 || k0 + 64 > T) {
 #pragma unroll
       for (int js = 0; js < 2; ++js) {
+        const int lim = qlim - (k0 + 32 * js + 4 * hl);
 #pragma unroll
-        for (int r = 0; r < 16; ++r) s[js][r] = 0.f;
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk)
-          s[js] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_row_frag(Ks, js * 32 + lc, kk * 16 + hl * 8), qf[kk],
-                                                          s[js], 0, 0, 0);
+        for (int r = 0; r < 16; ++r) cur[js][r] = (8 * (r >> 2) + (r & 3) <= lim) ? cur[js][r] : -INFINITY;
       }
-      // s[js][r]: key k0 + 32 js + 8 (r/4) + 4 hl + r%4, query myq
-      float mx = -INFINITY;
-      if (k0 + 63 > wq0 || k0 + 64 > T) {
+    }
+    float mx = cur[0][0];
 #pragma unroll
-        for (int js = 0; js < 2; ++js)
+    for (int js = 0; js < 2; ++js)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = k0 + js * 32 + 8 * (r >> 2) + 4 * hl + (r & 3);
-            const float v = (key <= myq && key < T) ? s[js][r] * sl2 : -INFINITY;
-            s[js][r] = v;
-            mx = fmaxf(mx, v);
-          }
-      } else {
-#pragma unroll
-        for (int js = 0; js < 2; ++js)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            s[js][r] *= sl2;
-            mx = fmaxf(mx, s[js][r]);
-          }
-      }
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      const float mnew = fmaxf(mrow, mx);
-      const float mu = (mnew == -INFINITY) ? 0.f : mnew;
-      const float alpha = exp2_fast(mrow - mu);
-      float ls = 0.f;
-#pragma unroll
-      for (int js = 0; js < 2; ++js)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float p = exp2_fast(s[js][r] - mu);
-          s[js][r] = p;
-          ls += p;
-        }
-      lrow = lrow * alpha + ls;
-      mrow = mnew;
+      for (int r = (js == 0 ? 1 : 0); r < 16; ++r) mx = fmaxf(mx, cur[js][r]);
+    const float mx2 = halves_max(mx) * sl2;
+    const bool need = mx2 > mrow + kLazy;
+    if (__builtin_amdgcn_ballot_w64(need)) {
+      const float mnew = need ? mx2 : mrow;
+      const float alpha = exp2_fast(mrow - mnew);
+      lrow *= alpha;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         o[0][r] *= alpha;
         o[1][r] *= alpha;
       }
-      // O^T += V^T P^T over four 16-key steps (V^T read transposed from V)
-#pragma unroll
-      for (int st = 0; st < 4; ++st) {
-        const bf16x8 pf = pack8(s[st >> 1], 8 * (st & 1));
-#pragma unroll
-        for (int i = 0; i < 2; ++i)
-          o[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_tr_frag(Vs, st * 16, i * 32, lane), pf, o[i], 0, 0, 0);
-      }
+      mrow = mnew;
     }
-    if (more) {
-      bf16* nxt = smem + ((kt + 1) & 1) * 2 * TILE;
-      tk.store(nxt, tid);
-      tv.store(nxt + TILE, tid);
+    scores(stg1, nxt);  // past the last tile: stale data, never used
+#pragma unroll
+    for (int js = 0; js < 2; ++js)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) cur[js][r] = exp2_fast(fmaf(cur[js][r], sl2, -mrow));
+    const bf16* Vs = smem + stg * ASTAGE + ATILE;
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+      const bf16x8 pf = pack8(cur[st >> 1], 8 * (st & 1));
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+        o[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag_keys(Vs, st * 16, i * 32, lane), pf, o[i], 0, 0, 0);
+      lrow = sum_bf16x8(pf, lrow);
     }
-    __syncthreads();
+    // the eight score MFMAs of tile j+1 spread over the exponentials of tile j
+#pragma unroll
+    for (int g = 0; g < 8; ++g) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+      __builtin_amdgcn_sched_group_barrier(0x002, 12, 0);  // twelve VALU
+    }
+  };
+
+  if (nkt > 1) wait_vmcnt<4>();
+  else wait_vmcnt<0>();
+  lds_barrier();
+  f32x16 sa[2], sb[2];
+  scores(0, sa);
+  int stg = 0;
+  for (int j = 0; j < nkt; j += 2) {
+    iteration(j, stg, sa, sb);
+    stg = stg == 2 ? 0 : stg + 1;
+    if (j + 1 < nkt) {
+      iteration(j + 1, stg, sb, sa);
+      stg = stg == 2 ? 0 : stg + 1;
+    }
   }
-  const float ltot = lrow + __shfl_xor(lrow, 32, 64);
+
+  const float ltot = halves_sum(lrow);
   if (myq < T) {
     const float inv = 1.0f / ltot;
     bf16* yr = y + ((int64_t)b * T + myq) * C + h * HD;
@@ -241,9 +377,10 @@ __global__ __launch_bounds__(256, 2) void flash_bwd_dkdv_kernel(const bf16* __re
                                                                 float sl2, float scale) {
   __shared__ __attribute__((aligned(16))) bf16 smem[4 * TILE];  // [stage][Q | dO]
   __shared__ float rowv[2][2][64];                              // [stage][lse*log2e | D]
-  const int h = blockIdx.y, b = blockIdx.z;
+  int kt, h, b;
+  attn_block(T, NH, kt, h, b);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, lc = lane & 31, hl = lane >> 5;
-  const int key0 = blockIdx.x * 128;  // tile 0 has the most queries and is scheduled first
+  const int key0 = kt * 128;  // tile 0 has the most queries and is scheduled first
   const int wk0 = key0 + wave * 32;
   const int mykey = wk0 + lc;
   const int64_t ld = 3 * (int64_t)C;
@@ -359,8 +496,9 @@ __global__ __launch_bounds__(256, 2) void flash_bwd_dq_kernel(const bf16* __rest
                                                               const float* __restrict__ Dd, bf16* __restrict__ dqkv,
                                                               int T, int NH, int C, float sl2, float scale) {
   __shared__ __attribute__((aligned(16))) bf16 smem[4 * TILE];  // [stage][K | V]
-  const int qt = gridDim.x - 1 - blockIdx.x;
-  const int h = blockIdx.y, b = blockIdx.z;
+  int qt, h, b;
+  attn_block(T, NH, qt, h, b);
+  qt = (T + 127) / 128 - 1 - qt;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, lc = lane & 31, hl = lane >> 5;
   const int q0 = qt * 128;
   const int wq0 = q0 + wave * 32;
@@ -456,7 +594,7 @@ __global__ __launch_bounds__(256, 2) void flash_bwd_dq_kernel(const bf16* __rest
 
 void attn_fwd_bf16(const void* qkv, void* y, float* lse, int B, int T, int NH, int C, hipStream_t s) {
   const float scale = 1.0f / sqrtf((float)HD);
-  dim3 grid((T + 127) / 128, NH, B);
+  const unsigned grid = (unsigned)((T + 127) / 128 * NH * B);
   flash_fwd_kernel<<<grid, 256, 0, s>>>(reinterpret_cast<const bf16*>(qkv), reinterpret_cast<bf16*>(y), lse, T, NH,
                                         C, scale * kLog2e);
 }
@@ -467,7 +605,7 @@ void attn_bwd_bf16(const void* qkv, const void* y, const void* dy, const float* 
   const int64_t rows = (int64_t)B * T * NH;
   attn_rowdot_kernel<<<(unsigned)((rows + 255) / 256), 256, 0, s>>>(
       reinterpret_cast<const bf16*>(y), reinterpret_cast<const bf16*>(dy), Dbuf, B, T, NH, C);
-  dim3 grid((T + 127) / 128, NH, B);
+  const unsigned grid = (unsigned)((T + 127) / 128 * NH * B);
   flash_bwd_dkdv_kernel<<<grid, 256, 0, s>>>(reinterpret_cast<const bf16*>(qkv), reinterpret_cast<const bf16*>(dy),
                                              lse, Dbuf, reinterpret_cast<bf16*>(dqkv), T, NH, C, scale * kLog2e,
                                              scale);

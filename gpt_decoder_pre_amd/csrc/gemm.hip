@@ -14,6 +14,7 @@
 
 #include "common.h"
 #include "kernels.h"
+#include "lds_tile.h"
 
 namespace gpt2k {
 
@@ -284,48 +285,16 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_bf16_kernel(GemmArgs p
 // Tiles are not zero-filled: rows past M or N are clamped to the last row
 // (their outputs are discarded), so K must be a multiple of BK.
 
-typedef short i16x4g __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) i16x4g lds_i16x4g;
-typedef __attribute__((address_space(3))) void lds_void;
-
-template <int BK>
-DEVI int kswz(int r) {
-  if constexpr (BK == 32) return ((r >> 1) ^ (r >> 3)) & 3;
-  else return (r ^ (r >> 3)) & 7;
-}
-DEVI int tswz(int k) { return 2 * (k & 3); }
-
-// Workgroup barrier without the release fence of __syncthreads (which would
-// drain every outstanding global->LDS load): ordering of LDS data across waves
-// comes from each wave's own vmcnt wait before the barrier, and the memory
-// clobber keeps the compiler from moving LDS accesses across it.
-DEVI void lds_barrier() { asm volatile("s_barrier" ::: "memory"); }
-
-// One global_load_lds_dwordx4: each lane moves 16 bytes from gptr to LDS
-// address m0 + 16 * lane (m0 = lds_base, wave-uniform).  Written as inline asm
-// so that the compiler does not treat it as an LDS store it must wait for
-// before every LDS read (it cannot tell the pipeline stages apart); the
-// kernel orders it with explicit vmcnt waits.  The instruction has no output
-// registers; its address registers are read at issue.
-DEVI void dma16(const void* gptr, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds_base), "v"(gptr) : "memory", "m0");
-}
-
-// vmcnt(n) with expcnt and lgkmcnt left alone (gfx9 encoding).
-template <int N>
-DEVI void wait_vmcnt() {
-  static_assert(N < 64, "vmcnt field");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-
 // This wave's share of the direct loads of one R x BK operand tile.  The
 // per-lane source addresses are formed once; each k-tile adds its offset.
 template <bool KMAJ, int R, int BK, int NW>
 struct DirectLoader {
   static constexpr int BYTES = R * BK * 2;
   static constexpr int INSTR = BYTES / 1024;         // wave instructions per tile
-  static constexpr int PER_WAVE = INSTR / NW;
-  static_assert(INSTR % NW == 0, "tile splits evenly over the waves");
+  // every wave issues the same number of loads (the vmcnt accounting is per
+  // wave); surplus loads repeat the tile's last chunk (same bytes, same place)
+  static constexpr int PER_WAVE = (INSTR + NW - 1) / NW;
+  static_assert(BYTES % 1024 == 0, "whole 1 KB wave loads");
   const bf16* src[PER_WAVE];
   uint32_t lds[PER_WAVE];
   int64_t kstep;  // elements between consecutive k-tiles
@@ -333,7 +302,7 @@ struct DirectLoader {
   DEVI void init(const bf16* g, int64_t ld, int r0, int rmax, int kbeg, const bf16* lds_tile, int wave, int lane) {
 #pragma unroll
     for (int j = 0; j < PER_WAVE; ++j) {
-      const int J = wave * PER_WAVE + j;
+      const int J = min(wave * PER_WAVE + j, INSTR - 1);
       const int byte = J * 1024 + lane * 16;
       if constexpr (KMAJ) {
         const int r = byte / (BK * 2), pc = (byte % (BK * 2)) / 16;
@@ -358,25 +327,106 @@ struct DirectLoader {
   }
 };
 
-// Fragment (eight consecutive k of one row, rows = lane % 32) for the 16-k step kk.
-template <bool KMAJ, int R, int BK>
-DEVI bf16x8 frag(const bf16* tile, int row0, int kk, int lane) {
-  if constexpr (KMAJ) {
-    const int r = row0 + (lane & 31);
-    const int c = 2 * kk + (lane >> 5);
-    return *reinterpret_cast<const bf16x8*>(tile + r * BK + 8 * (c ^ kswz<BK>(r)));
+// ----------------------------------------------------------- epilogue ----
+// Writes one wave's FM x FN accumulator tiles (rows mb.., columns nb..).
+// acc[i][j][4q + e] holds C[mb + 32 i + lane % 32][nb + 32 j + 8 q + 4 (lane / 32) + e].
+// bf16 outputs are staged through this wave's LDS region (32 FM rows of
+// 32 FN + 8 elements) so that every store instruction writes whole row
+// segments (16 bytes per lane along n) instead of 16 bytes into each of 32
+// rows; lines then reach L2 complete.  Other outputs go straight from the
+// registers.
+template <int EPI>
+constexpr bool epi_staged() {
+  return EPI == EPI_ACT || EPI == EPI_LOGITS || EPI == EPI_GELU || EPI == EPI_GELU_BWD;
+}
+
+template <int EPI, int FM, int FN, bool STAGED>
+DEVI void gemm_epilogue(const GemmArgs& p, f32x16 (&acc)[FM][FN], bf16* region, int mb, int nb, int lane, int split) {
+  constexpr int WTM = 32 * FM, WTN = 32 * FN;
+  const int lc = lane & 31, hl = lane >> 5;
+  if constexpr (STAGED) {
+    constexpr int SLD = WTN + 8;  // staged row stride (elements)
+    constexpr int NOUT = EPI == EPI_GELU ? 2 : 1;
+    constexpr int CPR = WTN / 8;  // 16-byte chunks per staged row
+    if constexpr (EPI == EPI_GELU_BWD) {
+      // the pre-activation tile u comes in whole row segments too
+      const bf16* aux = reinterpret_cast<const bf16*>(p.aux);
+#pragma unroll
+      for (int it = 0; it < WTM * CPR / 64; ++it) {
+        const int q = it * 64 + lane;
+        const int r = q / CPR, c = q % CPR;
+        const int m = mb + r, n = nb + 8 * c;
+        *reinterpret_cast<u32x4*>(region + r * SLD + 8 * c) =
+            ld16_or_zero(aux + (int64_t)m * p.ldc + n, m < p.M && n < p.N);
+      }
+      __builtin_amdgcn_s_waitcnt(0xc07f);
+      __builtin_amdgcn_wave_barrier();
+    }
+#pragma unroll
+    for (int o = 0; o < NOUT; ++o) {
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int nl = j * 32 + 8 * q + 4 * hl;
+            const int n = nb + nl;
+            float v[4] = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+            if constexpr (EPI == EPI_ACT || EPI == EPI_GELU) {
+              if (p.bias && n < p.N) {
+                float bb[4];
+                load4(p.bias + n, bb);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) v[e] += bb[e];
+              }
+            }
+            if constexpr (EPI == EPI_GELU) {
+              if (o == 1) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) v[e] = gelu_f(v[e]);
+              }
+            }
+            if constexpr (EPI == EPI_GELU_BWD) {
+              float u[4];
+              load4(region + (i * 32 + lc) * SLD + nl, u);
+#pragma unroll
+              for (int e = 0; e < 4; ++e) v[e] *= gelu_grad_f(u[e]);
+            }
+            store4(region + (i * 32 + lc) * SLD + nl, v);
+          }
+      __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's LDS writes are done
+      __builtin_amdgcn_wave_barrier();
+      bf16* out = reinterpret_cast<bf16*>(o == 0 ? p.C : p.C2);
+#pragma unroll
+      for (int it = 0; it < WTM * CPR / 64; ++it) {
+        const int q = it * 64 + lane;
+        const int r = q / CPR, c = q % CPR;
+        const int m = mb + r, n = nb + 8 * c;
+        if (m < p.M && n < p.N)
+          *reinterpret_cast<u32x4*>(out + (int64_t)m * p.ldc + n) =
+              *reinterpret_cast<const u32x4*>(region + r * SLD + 8 * c);
+      }
+      __builtin_amdgcn_s_waitcnt(0xc07f);
+      __builtin_amdgcn_wave_barrier();
+    }
   } else {
-    const int g = lane >> 4, s = lane & 15;
-    const int k = 16 * kk + 8 * (g >> 1) + (s >> 2);
-    const int m = row0 + 16 * (g & 1) + 4 * (s & 3);
-    const int c = m >> 3, o = m & 7;
-    const bf16* p1 = tile + k * R + 8 * (c ^ tswz(k)) + o;
-    const bf16* p2 = tile + (k + 4) * R + 8 * (c ^ tswz(k + 4)) + o;
-    const i16x4g a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4g*)p1);
-    const i16x4g b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4g*)p2);
-    const u32x2 ua = __builtin_bit_cast(u32x2, a), ub = __builtin_bit_cast(u32x2, b);
-    u32x4 v = {ua[0], ua[1], ub[0], ub[1]};
-    return __builtin_bit_cast(bf16x8, v);
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      const int m = mb + i * 32 + lc;
+      if (m >= p.M) continue;
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int n = nb + j * 32 + 8 * q + 4 * hl;
+          if (n < p.N) {
+            float v[4] = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+            epi_store4<EPI, bf16>(p, m, n, v, split);
+          }
+        }
+      }
+    }
   }
 }
 
@@ -400,7 +450,6 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_lds_kernel(GemmArgs p)
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / WGN, wn = wave % WGN;
-  const int lc = lane & 31, hl = lane >> 5;
   const int tiles_m = (p.M + BM - 1) / BM, tiles_n = (p.N + BN - 1) / BN;
   int tm, tn, split;
   tile_coords(p, tiles_m, tiles_n, blockIdx.x + blockIdx.y * gridDim.x, gridDim.x * gridDim.y, tm, tn, split);
@@ -484,97 +533,14 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_lds_kernel(GemmArgs p)
       if (kt + 3 < nkt) step(std::integral_constant<int, 3>{}, kt + 3);
   }
 
-  // bf16 outputs are staged through LDS so that every store instruction
-  // writes whole row segments (16 bytes per lane along n) instead of 16 bytes
-  // into each of 32 rows; lines then reach L2 complete.
-  constexpr bool kBf16Out = EPI == EPI_ACT || EPI == EPI_LOGITS || EPI == EPI_GELU || EPI == EPI_GELU_BWD;
-  constexpr int SLD = WTN + 8;                       // staged row stride (elements)
-  constexpr int WPA = (NW + 1) / 2;                  // waves per stage array
-  constexpr bool kStage = kBf16Out && WPA * WTM * SLD <= STAGE;
-  if constexpr (kStage) {
+  constexpr int SLD = WTN + 8;
+  constexpr int WPA = (NW + 1) / 2;  // waves per stage array
+  if constexpr (epi_staged<EPI>() && WPA * WTM * SLD <= STAGE) {
     __syncthreads();  // all waves are done reading the operand stages
     bf16* region = (wave < WPA ? st0 : st1) + (wave % WPA) * WTM * SLD;
-    constexpr int NOUT = EPI == EPI_GELU ? 2 : 1;
-    constexpr int CPR = WTN / 8;  // 16-byte chunks per staged row
-    if constexpr (EPI == EPI_GELU_BWD) {
-      // the pre-activation tile u comes in whole row segments too
-      const bf16* aux = reinterpret_cast<const bf16*>(p.aux);
-#pragma unroll
-      for (int it = 0; it < WTM * CPR / 64; ++it) {
-        const int q = it * 64 + lane;
-        const int r = q / CPR, c = q % CPR;
-        const int m = m0 + wm * WTM + r, n = n0 + wn * WTN + 8 * c;
-        *reinterpret_cast<u32x4*>(region + r * SLD + 8 * c) =
-            ld16_or_zero(aux + (int64_t)m * p.ldc + n, m < p.M && n < p.N);
-      }
-      __builtin_amdgcn_s_waitcnt(0xc07f);
-      __builtin_amdgcn_wave_barrier();
-    }
-#pragma unroll
-    for (int o = 0; o < NOUT; ++o) {
-#pragma unroll
-      for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int j = 0; j < FN; ++j)
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const int nl = j * 32 + 8 * q + 4 * hl;
-            const int n = n0 + wn * WTN + nl;
-            float v[4] = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
-            if constexpr (EPI == EPI_ACT || EPI == EPI_GELU) {
-              if (p.bias && n < p.N) {
-                float bb[4];
-                load4(p.bias + n, bb);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) v[e] += bb[e];
-              }
-            }
-            if constexpr (EPI == EPI_GELU) {
-              if (o == 1) {
-#pragma unroll
-                for (int e = 0; e < 4; ++e) v[e] = gelu_f(v[e]);
-              }
-            }
-            if constexpr (EPI == EPI_GELU_BWD) {
-              float u[4];
-              load4(region + (i * 32 + lc) * SLD + nl, u);
-#pragma unroll
-              for (int e = 0; e < 4; ++e) v[e] *= gelu_grad_f(u[e]);
-            }
-            store4(region + (i * 32 + lc) * SLD + nl, v);
-          }
-      __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's LDS writes are done
-      __builtin_amdgcn_wave_barrier();
-      bf16* out = reinterpret_cast<bf16*>(o == 0 ? p.C : p.C2);
-#pragma unroll
-      for (int it = 0; it < WTM * CPR / 64; ++it) {
-        const int q = it * 64 + lane;
-        const int r = q / CPR, c = q % CPR;
-        const int m = m0 + wm * WTM + r, n = n0 + wn * WTN + 8 * c;
-        if (m < p.M && n < p.N)
-          *reinterpret_cast<u32x4*>(out + (int64_t)m * p.ldc + n) =
-              *reinterpret_cast<const u32x4*>(region + r * SLD + 8 * c);
-      }
-      __builtin_amdgcn_s_waitcnt(0xc07f);
-      __builtin_amdgcn_wave_barrier();
-    }
+    gemm_epilogue<EPI, FM, FN, true>(p, acc, region, m0 + wm * WTM, n0 + wn * WTN, lane, split);
   } else {
-#pragma unroll
-    for (int i = 0; i < FM; ++i) {
-      const int m = m0 + wm * WTM + i * 32 + lc;
-      if (m >= p.M) continue;
-#pragma unroll
-      for (int j = 0; j < FN; ++j) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int n = n0 + wn * WTN + j * 32 + 8 * q + 4 * hl;
-          if (n < p.N) {
-            float v[4] = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
-            epi_store4<EPI, bf16>(p, m, n, v, split);
-          }
-        }
-      }
-    }
+    gemm_epilogue<EPI, FM, FN, false>(p, acc, nullptr, m0 + wm * WTM, n0 + wn * WTN, lane, split);
   }
 }
 
@@ -743,12 +709,12 @@ double model_time(int c, const GemmArgs& a, bool transposed_a) {
   const double flops = 2.0 * a.M * (double)a.N * a.K;
   return flops / ((transposed_a ? tf_t[c] : tf_k[c]) * 1e12 * fill * used);
 }
-int choose_cfg(const GemmArgs& a, bool transposed_a) {
+int choose_cfg(const GemmArgs& a, GemmLayout layout) {
   int pick = 0;
   double best = 1e30;
   for (int c = 0; c < kNumCfg; ++c) {
-    if (!gemm_config_usable(c, a)) continue;
-    const double t = model_time(c, a, transposed_a);
+    if (!gemm_config_usable(c, layout, a)) continue;
+    const double t = model_time(c, a, layout == LAYOUT_TN);
     if (t < best) {
       best = t;
       pick = c;
@@ -758,9 +724,9 @@ int choose_cfg(const GemmArgs& a, bool transposed_a) {
 }
 }  // namespace
 
-int gemm_pick_config(const GemmArgs& a, bool transposed_a) { return choose_cfg(a, transposed_a); }
+int gemm_pick_config(const GemmArgs& a, GemmLayout layout) { return choose_cfg(a, layout); }
 
-bool gemm_config_usable(int cfg, const GemmArgs& a) {
+bool gemm_config_usable(int cfg, GemmLayout layout, const GemmArgs& a) {
   if (cfg < 0 || cfg >= kNumCfg || cfg == 13) return false;
   if (cfg >= kFirstLds) {
     // whole k-tiles, and every split the same length (the persistent walk
@@ -789,8 +755,8 @@ bool gemm_cfg(int cfg, GemmLayout layout, GemmEpilogue epi, bool bf16_mode, cons
     // the epilogue writes four columns at a time.
     if (a.K % 8 || a.N % 8 || a.ldc % 4 || a.lda % 8 || a.ldb % 8) return false;
     if (layout == LAYOUT_TN && a.M % 8) return false;
-    if (cfg < 0) cfg = choose_cfg(a, layout == LAYOUT_TN);
-    if (!gemm_config_usable(cfg, a)) return false;
+    if (cfg < 0) cfg = choose_cfg(a, layout);
+    if (!gemm_config_usable(cfg, layout, a)) return false;
   }
   switch (layout) {
     case LAYOUT_NT:

@@ -233,7 +233,7 @@ bool weight_grad(gpt2_ctx* c, const char* site, float* out, const void* A, int64
         GemmArgs t = a;
         t.splits = splits;
         t.k_per_split = splits > 1 ? kps : K;
-        if (!gemm_config_usable(cfg, t)) continue;
+        if (!gemm_config_usable(cfg, LAYOUT_TN, t)) continue;
         double time = gemm_model_time(cfg, t, true);
         if (splits > 1) time += (2.0 * splits + 2.0) * outn * 4.0 / 4.0e12;
         if (time < best) {

@@ -45,10 +45,10 @@ bool gemm(GemmLayout layout, GemmEpilogue epi, bool bf16_mode, const GemmArgs& a
 bool gemm_cfg(int cfg, GemmLayout layout, GemmEpilogue epi, bool bf16_mode, const GemmArgs& a, hipStream_t s);
 // The tile configuration the automatic choice takes for these shapes, and the
 // modelled time of a configuration (seconds).
-int gemm_pick_config(const GemmArgs& a, bool transposed_a);
+int gemm_pick_config(const GemmArgs& a, GemmLayout layout);
 double gemm_model_time(int cfg, const GemmArgs& a, bool transposed_a);
 // Whether a configuration can run these shapes.
-bool gemm_config_usable(int cfg, const GemmArgs& a);
+bool gemm_config_usable(int cfg, GemmLayout layout, const GemmArgs& a);
 constexpr int kGemmConfigs = 19;
 // Block tile of a configuration.
 void gemm_config_tile(int cfg, int* bm, int* bn);
