@@ -22,8 +22,6 @@
 namespace gpt2k {
 
 constexpr int HD = 64;
-constexpr int LD = 72;      // bf16 elements per LDS row (64 + 8 padding)
-constexpr int TILE = 64 * LD;
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
@@ -36,48 +34,6 @@ DEVI bf16x8 pack8(const f32x16& v, int base) {
   for (int e = 0; e < 8; ++e) r[e] = (bf16)v[base + e];
   return r;
 }
-
-// MFMA A operand from an LDS tile stored [k][m] (m contiguous, row stride LD):
-// rows m = mbase + lane%32, and the eight k of the permuted 16-k step kbase:
-// kbase + 4 hl + {0..3} and kbase + 8 + 4 hl + {0..3}.  ds_read_b64_tr_b16
-// hands lane j of each 16-lane group element i of source lane 4i + j/4's
-// 8-byte row, so source lane 4i + q points at (k0 + i, m16 + 4q).
-DEVI bf16x8 lds_tr_frag(const bf16* tile, int kbase, int mbase, int lane) {
-  const int g = lane >> 4, s = lane & 15;
-  const int k = kbase + 4 * (g >> 1) + (s >> 2);
-  const int m = mbase + 16 * (g & 1) + 4 * (s & 3);
-  const bf16* p = tile + k * LD + m;
-  const i16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p));
-  const i16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p + 8 * LD));
-  const u32x2 ua = __builtin_bit_cast(u32x2, a), ub = __builtin_bit_cast(u32x2, b);
-  u32x4 r = {ua[0], ua[1], ub[0], ub[1]};
-  return as_bf16x8(r);
-}
-
-// MFMA operand rows from an LDS tile stored [row][k] (k contiguous).
-DEVI bf16x8 lds_row_frag(const bf16* tile, int row, int k) {
-  return *reinterpret_cast<const bf16x8*>(tile + row * LD + k);
-}
-
-// A 64-row x 64-column bf16 tile in flight: two 16-byte chunks per thread.
-struct TileRegs {
-  u32x4 r[2];
-  DEVI void load(const bf16* g, int64_t ld, int r0, int rmax, int tid) {
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int c = tid + 256 * i;
-      const int row = c >> 3, ch = (c & 7) * 8;
-      r[i] = ld16_or_zero(g + (int64_t)(r0 + row) * ld + ch, r0 + row < rmax);
-    }
-  }
-  DEVI void store(bf16* s, int tid) const {
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int c = tid + 256 * i;
-      *reinterpret_cast<u32x4*>(s + (c >> 3) * LD + (c & 7) * 8) = r[i];
-    }
-  }
-};
 
 // ------------------------------------------------------------------ forward ----
 // Workgroup: 128 queries of one (sequence, head); wave w owns queries
@@ -95,21 +51,30 @@ constexpr int ATILE = 64 * 64;     // one 64 x 64 bf16 tile, swizzled, unpadded
 constexpr int ASTAGE = 2 * ATILE;  // K | V (or Q | dO)
 constexpr float kLazy = 8.0f;
 
-// This wave's two 1 KB loads of a 64-row tile of one head (rows r0.. of a
-// [T][ld] matrix): chunks swizzled by kswz (tile read row-wise) or tswz (tile
-// read transposed).  The per-lane byte offsets within a tile do not depend on
-// r0, so they are formed once; a tile adds the wave-uniform r0 * ld to the
-// scalar base.  Rows past T (only in a partial last tile) are clamped to T - 1.
-template <bool ROWWISE>
+// Every attention tile (64 rows of one head: keys or queries by 64 dims,
+// 128 bytes a row) is read both row-wise (ds_read_b128: eight dims of one row
+// per lane, 16 consecutive rows per 256-byte slice) and transposed
+// (ds_read_b64_tr_b16: four consecutive rows of one dim column).  Chunk c of
+// row r is stored at chunk c ^ bswz(r), bswz(r) = 4 r1 + 2 r2 + r3 (r_i the
+// bits of r): a bijection over bits 1..3 spreads the row-wise slices over all
+// banks, and rows r and r + 2 land in opposite chunk halves, which spreads the
+// transposed reads.
+DEVI int bswz(int r) { return (((r >> 1) & 1) << 2) | (((r >> 2) & 1) << 1) | ((r >> 3) & 1); }
+
+// This wave's two 1 KB loads of a tile (rows r0.. of a [T][ld] matrix).  The
+// per-lane byte offsets within a tile do not depend on r0, so they are formed
+// once; a tile adds the wave-uniform r0 * ld to the scalar base.  Rows past T
+// (only in a partial last tile) are clamped to T - 1.
 struct AttnTileLoader {
   uint32_t off[2];  // lane byte offsets of the two loads, relative to row r0
+  int64_t ld;       // row stride of the source (elements)
   DEVI static void place(int wave, int lane, int j, int& r, int& c8) {
     const int byte = (2 * wave + j) * 1024 + lane * 16;
     r = byte >> 7;
-    const int pc = (byte >> 4) & 7;
-    c8 = 8 * (pc ^ (ROWWISE ? kswz<64>(r) : tswz(r)));
+    c8 = 8 * (((byte >> 4) & 7) ^ bswz(r));
   }
-  DEVI void init(int64_t ld, int wave, int lane) {
+  DEVI void init(int64_t ld_, int wave, int lane) {
+    ld = ld_;
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       int r, c8;
@@ -117,7 +82,7 @@ struct AttnTileLoader {
       off[j] = (uint32_t)(2 * ((int64_t)r * ld + c8));
     }
   }
-  DEVI void issue(const bf16* g, int64_t ld, int r0, int T, uint32_t lds_tile, int wave, int lane) const {
+  DEVI void issue(const bf16* g, int r0, int T, uint32_t lds_tile, int wave, int lane) const {
     if (r0 + 64 <= T) {
       const bf16* b = uniform_ptr(g + (int64_t)r0 * ld);
 #pragma unroll
@@ -133,20 +98,27 @@ struct AttnTileLoader {
   }
 };
 
-// A operand of a product over keys from a tile stored [key][d] (tswz layout):
-// rows d = mbase + lane%32, and the eight keys of the 16-key step kbase in the
-// order the score accumulators hold them: kbase + 4 hl + {0..3} and
+// MFMA operand rows row0 + lane%32 of a tile, dims 16 kk + 8 hl .. + 7.
+DEVI bf16x8 row_frag(const bf16* tile, int row0, int kk, int lane) {
+  const int r = row0 + (lane & 31);
+  const int c = 2 * kk + (lane >> 5);
+  return *reinterpret_cast<const bf16x8*>(tile + r * 64 + 8 * (c ^ bswz(r)));
+}
+
+// A operand of a product over the tile's rows, read transposed: rows
+// (dims) mbase + lane%32, and the eight tile rows of the 16-row step kbase in
+// the order the score accumulators hold them: kbase + 4 hl + {0..3} and
 // kbase + 8 + 4 hl + {0..3}.  ds_read_b64_tr_b16 hands lane j of each 16-lane
 // group element i of source lane 4i + j/4's 8-byte row, so source lane 4i + q
-// points at (key kb + i, d m16 + 4q).
+// points at (row kb + i, dims m16 + 4q .. + 3).
 DEVI bf16x8 tr_frag_keys(const bf16* tile, int kbase, int mbase, int lane) {
   const int g = lane >> 4, s = lane & 15;
   const int k = kbase + 4 * (g >> 1) + (s >> 2);
   const int m = mbase + 16 * (g & 1) + 4 * (s & 3);
   const int c = m >> 3, o = m & 7;
-  const bf16* p = tile + k * 64 + 8 * (c ^ tswz(k)) + o;  // tswz(k + 8) == tswz(k)
-  const i16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p));
-  const i16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p + 8 * 64));
+  const i16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(tile + k * 64 + 8 * (c ^ bswz(k)) + o));
+  const i16x4 b =
+      __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(tile + (k + 8) * 64 + 8 * (c ^ bswz(k + 8)) + o));
   const u32x2 ua = __builtin_bit_cast(u32x2, a), ub = __builtin_bit_cast(u32x2, b);
   u32x4 r = {ua[0], ua[1], ub[0], ub[1]};
   return as_bf16x8(r);
@@ -211,14 +183,12 @@ __global__ __launch_bounds__(256, 3) void flash_fwd_kernel(const bf16* __restric
   const uint32_t lds0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void*)smem);
 
   const int nkt = (min(T, q0 + 128) + 63) / 64;            // key tiles of the workgroup
-  AttnTileLoader<true> lk;
-  AttnTileLoader<false> lv;
-  lk.init(ld, wave, lane);
-  lv.init(ld, wave, lane);
+  AttnTileLoader tl;
+  tl.init(ld, wave, lane);
   auto load = [&](int j, int stg) {
     const uint32_t base = lds0 + stg * (ASTAGE * 2);
-    lk.issue(K, ld, j * 64, T, base, wave, lane);
-    lv.issue(V, ld, j * 64, T, base + ATILE * 2, wave, lane);
+    tl.issue(K, j * 64, T, base, wave, lane);
+    tl.issue(V, j * 64, T, base + ATILE * 2, wave, lane);
   };
   load(0, 0);
   if (nkt > 1) load(1, 1);
@@ -236,8 +206,7 @@ __global__ __launch_bounds__(256, 3) void flash_fwd_kernel(const bf16* __restric
       for (int r = 0; r < 16; ++r) s[js][r] = 0.f;
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk)
-        s[js] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag<true, 64, 64>(Ks, js * 32, kk, lane), qf[kk], s[js], 0,
-                                                        0, 0);
+        s[js] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag(Ks, js * 32, kk, lane), qf[kk], s[js], 0, 0, 0);
     }
   };
 
@@ -367,19 +336,22 @@ __global__ void attn_rowdot_kernel(const bf16* __restrict__ y, const bf16* __res
 
 // ---------------------------------------------------------- backward: dK, dV ----
 // Workgroup: 128 keys of one (sequence, head); wave w owns keys key0 + 32 w +
-// lane%32 and accumulates dK^T and dV^T over the query tiles (64 queries,
-// double-buffered) that can see them.
+// lane%32 and accumulates dK^T and dV^T over the query tiles (64 queries)
+// that can see them.  Q and dO tiles stream from HBM straight into a
+// three-stage LDS ring; the tile's log-sum-exp (in the exp2 domain) and D
+// rows are staged beside them by waves 0 and 1 through registers.
 __global__ __launch_bounds__(256, 2) void flash_bwd_dkdv_kernel(const bf16* __restrict__ qkv,
                                                                 const bf16* __restrict__ dy,
                                                                 const float* __restrict__ lse,
                                                                 const float* __restrict__ Dd,
                                                                 bf16* __restrict__ dqkv, int T, int NH, int C,
                                                                 float sl2, float scale) {
-  __shared__ __attribute__((aligned(16))) bf16 smem[4 * TILE];  // [stage][Q | dO]
-  __shared__ float rowv[2][2][64];                              // [stage][lse*log2e | D]
+  __shared__ __attribute__((aligned(1024))) bf16 smem[3 * ASTAGE];  // [stage][Q | dO]
+  __shared__ __attribute__((aligned(16))) float rowv[3][2][64];     // [stage][lse log2e | D]
   int kt, h, b;
   attn_block(T, NH, kt, h, b);
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, lc = lane & 31, hl = lane >> 5;
+  const int tid = threadIdx.x, lane = tid & 63, lc = lane & 31, hl = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int key0 = kt * 128;  // tile 0 has the most queries and is scheduled first
   const int wk0 = key0 + wave * 32;
   const int mykey = wk0 + lc;
@@ -390,6 +362,27 @@ __global__ __launch_bounds__(256, 2) void flash_bwd_dkdv_kernel(const bf16* __re
   const bf16* G = dy + (int64_t)b * T * C + h * HD;
   const float* lse_b = lse + ((int64_t)b * NH + h) * T;
   const float* D_b = Dd + ((int64_t)b * NH + h) * T;
+  const uint32_t lds0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void*)smem);
+
+  const int nqt = (T - key0 + 63) / 64;
+  AttnTileLoader tlq, tlg;  // Q rows are 3C apart, dO rows C apart
+  tlq.init(ld, wave, lane);
+  tlg.init(C, wave, lane);
+  // waves 0 and 1 carry the lse / D rows of a query tile in a register
+  float rv = 0.f;
+  auto load = [&](int it, int stg) {
+    const int q0 = key0 + it * 64;
+    const uint32_t base = lds0 + stg * (ASTAGE * 2);
+    tlq.issue(Q, q0, T, base, wave, lane);
+    tlg.issue(G, q0, T, base + ATILE * 2, wave, lane);
+    if (wave < 2) {
+      const int q = min(q0 + lane, T - 1);
+      rv = wave == 0 ? lse_b[q] * kLog2e : D_b[q];
+    }
+  };
+  auto stage_rows = [&](int stg) {  // after the register loads landed
+    if (wave < 2) rowv[stg][wave][lane] = rv;
+  };
 
   bf16x8 kf[4], vf[4];
 #pragma unroll
@@ -401,34 +394,26 @@ __global__ __launch_bounds__(256, 2) void flash_bwd_dkdv_kernel(const bf16* __re
 #pragma unroll
   for (int r = 0; r < 16; ++r) dk[0][r] = dk[1][r] = dv[0][r] = dv[1][r] = 0.f;
 
-  const int nqt = (T - key0 + 63) / 64;
-  TileRegs tq, tg;
-  float rv = 0.f;
-  auto fetch = [&](int q0) {
-    tq.load(Q, ld, q0, T, tid);
-    tg.load(G, C, q0, T, tid);
-    if (tid < 128) {
-      const int q = q0 + (tid & 63);
-      rv = q < T ? (tid < 64 ? lse_b[q] * kLog2e : D_b[q]) : 0.f;
-    }
-  };
-  auto put = [&](int stage) {
-    tq.store(smem + stage * 2 * TILE, tid);
-    tg.store(smem + stage * 2 * TILE + TILE, tid);
-    if (tid < 128) rowv[stage][tid >> 6][tid & 63] = rv;
-  };
-  fetch(key0);
-  put(0);
-  __syncthreads();
+  // Prologue: tiles 0 and 1 in flight; tile 0's rows staged.
+  load(0, 0);
+  wait_vmcnt<0>();
+  stage_rows(0);
+  if (nqt > 1) load(1, 1);
+  // Iteration it: wait for tile it+1 and stage its rows, barrier (tile it
+  // complete everywhere, every wave past iteration it-1), load tile it+2 into
+  // the stage tile it-1 used, then use tile it.
+  int stg = 0;
   for (int it = 0; it < nqt; ++it) {
+    const int stg1 = stg == 2 ? 0 : stg + 1, stg2 = stg1 == 2 ? 0 : stg1 + 1;
+    if (it + 1 < nqt) {
+      wait_vmcnt<0>();
+      stage_rows(stg1);
+    }
+    __syncthreads();
+    if (it + 2 < nqt) load(it + 2, stg2);
     const int q0 = key0 + it * 64;
-    const bool more = it + 1 < nqt;
-    if (more) fetch(q0 + 64);
-    const int stg = it & 1;
-    const bf16* Qs = smem + stg * 2 * TILE;
-    const bf16* Gs = Qs + TILE;
-    const float* ls = rowv[stg][0];
-    const float* Ds = rowv[stg][1];
+    const bf16* Qs = smem + stg * ASTAGE;
+    const bf16* Gs = Qs + ATILE;
     if (q0 + 63 >= wk0) {  // some query of the tile sees a key of this wave
       const bool diag = q0 < wk0 + 31 || q0 + 64 > T;
       f32x16 P[2], dS[2];
@@ -439,22 +424,31 @@ __global__ __launch_bounds__(256, 2) void flash_bwd_dkdv_kernel(const bf16* __re
         for (int r = 0; r < 16; ++r) sv[r] = dp[r] = 0.f;
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
-          sv = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_row_frag(Qs, i * 32 + lc, kk * 16 + hl * 8), kf[kk], sv, 0,
-                                                       0, 0);
-          dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_row_frag(Gs, i * 32 + lc, kk * 16 + hl * 8), vf[kk], dp, 0,
-                                                       0, 0);
+          sv = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag(Qs, i * 32, kk, lane), kf[kk], sv, 0, 0, 0);
+          dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag(Gs, i * 32, kk, lane), vf[kk], dp, 0, 0, 0);
         }
-        // sv[r]: query q0 + 32 i + 8 (r/4) + 4 hl + r%4, key mykey
+        // sv[r]: query q0 + 32 i + 8 (r/4) + 4 hl + r%4, key mykey.  Queries
+        // before the key or past T get score -inf (probability exactly 0).
+        if (diag) {
+          const int lo = mykey - q0 - 4 * hl, span = T - q0 - 4 * hl - lo;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int ql = i * 32 + 8 * (r >> 2) + 4 * hl + (r & 3);
-          float p = exp2_fast(sv[r] * sl2 - ls[ql]);
-          if (diag) {
-            const int q = q0 + ql;
-            p = (mykey <= q && q < T) ? p : 0.f;
+          for (int r = 0; r < 16; ++r) {
+            const int c = i * 32 + 8 * (r >> 2) + (r & 3);
+            sv[r] = ((unsigned)(c - lo) < (unsigned)span) ? sv[r] : -INFINITY;
           }
-          P[i][r] = p;
-          dS[i][r] = p * (dp[r] - Ds[ql]);
+        }
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const int qg = i * 32 + 8 * g4 + 4 * hl;  // four consecutive queries
+          const f32x4 l4 = *reinterpret_cast<const f32x4*>(&rowv[stg][0][qg]);
+          const f32x4 d4 = *reinterpret_cast<const f32x4*>(&rowv[stg][1][qg]);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int r = 4 * g4 + e;
+            const float p = exp2_fast(fmaf(sv[r], sl2, -l4[e]));
+            P[i][r] = p;
+            dS[i][r] = p * (dp[r] - d4[e]);
+          }
         }
       }
       // dV^T += dO^T P, dK^T += Q^T dS (transposed operands read from the natural tiles)
@@ -464,13 +458,12 @@ __global__ __launch_bounds__(256, 2) void flash_bwd_dkdv_kernel(const bf16* __re
         const bf16x8 sb = pack8(dS[st >> 1], 8 * (st & 1));
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
-          dv[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_tr_frag(Gs, st * 16, t * 32, lane), pb, dv[t], 0, 0, 0);
-          dk[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_tr_frag(Qs, st * 16, t * 32, lane), sb, dk[t], 0, 0, 0);
+          dv[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag_keys(Gs, st * 16, t * 32, lane), pb, dv[t], 0, 0, 0);
+          dk[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag_keys(Qs, st * 16, t * 32, lane), sb, dk[t], 0, 0, 0);
         }
       }
     }
-    if (more) put(stg ^ 1);
-    __syncthreads();
+    stg = stg1;
   }
   if (mykey < T) {
     bf16* o = dqkv + ((int64_t)b * T + mykey) * ld + h * HD;
@@ -489,17 +482,19 @@ __global__ __launch_bounds__(256, 2) void flash_bwd_dkdv_kernel(const bf16* __re
 
 // --------------------------------------------------------------- backward: dQ ----
 // Workgroup: 128 queries; wave w owns queries q0 + 32 w + lane%32 and
-// accumulates dQ^T over the key tiles (64 keys, double-buffered) it sees.
+// accumulates dQ^T over the key tiles (64 keys) it sees; K and V tiles stream
+// into a three-stage LDS ring as in the forward kernel.
 __global__ __launch_bounds__(256, 2) void flash_bwd_dq_kernel(const bf16* __restrict__ qkv,
                                                               const bf16* __restrict__ dy,
                                                               const float* __restrict__ lse,
                                                               const float* __restrict__ Dd, bf16* __restrict__ dqkv,
                                                               int T, int NH, int C, float sl2, float scale) {
-  __shared__ __attribute__((aligned(16))) bf16 smem[4 * TILE];  // [stage][K | V]
+  __shared__ __attribute__((aligned(1024))) bf16 smem[3 * ASTAGE];  // [stage][K | V]
   int qt, h, b;
   attn_block(T, NH, qt, h, b);
   qt = (T + 127) / 128 - 1 - qt;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, lc = lane & 31, hl = lane >> 5;
+  const int tid = threadIdx.x, lane = tid & 63, lc = lane & 31, hl = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int q0 = qt * 128;
   const int wq0 = q0 + wave * 32;
   const int myq = wq0 + lc;
@@ -508,10 +503,21 @@ __global__ __launch_bounds__(256, 2) void flash_bwd_dq_kernel(const bf16* __rest
   const bf16* K = Q + C;
   const bf16* V = Q + 2 * C;
   const bf16* G = dy + (int64_t)b * T * C + h * HD;
+  const uint32_t lds0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void*)smem);
+  const int nkt = (min(T, q0 + 128) + 63) / 64;
+  AttnTileLoader tl;
+  tl.init(ld, wave, lane);
+  auto load = [&](int j, int stg) {
+    const uint32_t base = lds0 + stg * (ASTAGE * 2);
+    tl.issue(K, j * 64, T, base, wave, lane);
+    tl.issue(V, j * 64, T, base + ATILE * 2, wave, lane);
+  };
+  load(0, 0);
+  if (nkt > 1) load(1, 1);
+
   const bool qok = myq < T;
   const float lse2 = qok ? lse[((int64_t)b * NH + h) * T + myq] * kLog2e : 0.f;
   const float Dq = qok ? Dd[((int64_t)b * NH + h) * T + myq] : 0.f;
-
   bf16x8 qf[4], gf[4];
 #pragma unroll
   for (int kk = 0; kk < 4; ++kk) {
@@ -521,23 +527,18 @@ __global__ __launch_bounds__(256, 2) void flash_bwd_dq_kernel(const bf16* __rest
   f32x16 dq[2];
 #pragma unroll
   for (int r = 0; r < 16; ++r) dq[0][r] = dq[1][r] = 0.f;
-  const int kv_end = min(T, q0 + 128);
-  const int nkt = (kv_end + 63) / 64;
-  TileRegs tk, tv;
-  tk.load(K, ld, 0, T, tid);
-  tv.load(V, ld, 0, T, tid);
-  tk.store(smem, tid);
-  tv.store(smem + TILE, tid);
-  __syncthreads();
+  const int qlim = min(myq, T - 1);
+
+  int stg = 0;
   for (int kt = 0; kt < nkt; ++kt) {
+    const int stg1 = stg == 2 ? 0 : stg + 1, stg2 = stg1 == 2 ? 0 : stg1 + 1;
+    if (kt + 1 < nkt) wait_vmcnt<4>();  // this wave's loads of tile kt landed (tile kt+1's four may be in flight)
+    else wait_vmcnt<0>();
+    lds_barrier();
+    if (kt + 2 < nkt) load(kt + 2, stg2);
     const int k0 = kt * 64;
-    const bool more = kt + 1 < nkt;
-    if (more) {
-      tk.load(K, ld, k0 + 64, T, tid);
-      tv.load(V, ld, k0 + 64, T, tid);
-    }
-    const bf16* Ks = smem + (kt & 1) * 2 * TILE;
-    const bf16* Vs = Ks + TILE;
+    const bf16* Ks = smem + stg * ASTAGE;
+    const bf16* Vs = Ks + ATILE;
     if (k0 <= wq0 + 31) {
       const bool diag = k0 + 63 > wq0 || k0 + 64 > T;
       f32x16 dS[2];
@@ -548,36 +549,32 @@ __global__ __launch_bounds__(256, 2) void flash_bwd_dq_kernel(const bf16* __rest
         for (int r = 0; r < 16; ++r) sv[r] = dp[r] = 0.f;
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
-          sv = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_row_frag(Ks, js * 32 + lc, kk * 16 + hl * 8), qf[kk], sv, 0,
-                                                       0, 0);
-          dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_row_frag(Vs, js * 32 + lc, kk * 16 + hl * 8), gf[kk], dp, 0,
-                                                       0, 0);
+          sv = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag(Ks, js * 32, kk, lane), qf[kk], sv, 0, 0, 0);
+          dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag(Vs, js * 32, kk, lane), gf[kk], dp, 0, 0, 0);
         }
-        // sv[r]: key k0 + 32 js + 8 (r/4) + 4 hl + r%4, query myq
+        // sv[r]: key k0 + 32 js + 8 (r/4) + 4 hl + r%4, query myq; keys past
+        // the query get score -inf (probability exactly 0)
+        if (diag) {
+          const int lim = qlim - (k0 + 32 * js + 4 * hl);
+#pragma unroll
+          for (int r = 0; r < 16; ++r) sv[r] = (8 * (r >> 2) + (r & 3) <= lim) ? sv[r] : -INFINITY;
+        }
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          float p = exp2_fast(sv[r] * sl2 - lse2);
-          if (diag) {
-            const int key = k0 + js * 32 + 8 * (r >> 2) + 4 * hl + (r & 3);
-            p = (key <= myq && qok) ? p : 0.f;
-          }
+          const float p = exp2_fast(fmaf(sv[r], sl2, -lse2));
           dS[js][r] = p * (dp[r] - Dq);
         }
       }
+      // dQ^T += K^T dS^T (K read transposed, keys in the accumulator order)
 #pragma unroll
       for (int st = 0; st < 4; ++st) {
         const bf16x8 sb = pack8(dS[st >> 1], 8 * (st & 1));
 #pragma unroll
         for (int t = 0; t < 2; ++t)
-          dq[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_tr_frag(Ks, st * 16, t * 32, lane), sb, dq[t], 0, 0, 0);
+          dq[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag_keys(Ks, st * 16, t * 32, lane), sb, dq[t], 0, 0, 0);
       }
     }
-    if (more) {
-      bf16* nxt = smem + ((kt + 1) & 1) * 2 * TILE;
-      tk.store(nxt, tid);
-      tv.store(nxt + TILE, tid);
-    }
-    __syncthreads();
+    stg = stg1;
   }
   if (qok) {
     bf16* o = dqkv + ((int64_t)b * T + myq) * ld + h * HD;
