@@ -311,7 +311,7 @@ struct DirectLoader {
         src[j] = g + (int64_t)row * ld + kbeg + 8 * c;
       } else {
         const int k = byte / (R * 2), pc = (byte % (R * 2)) / 16;
-        const int c = pc ^ tswz(k);
+        const int c = pc ^ tswz<R>(k);
         const int col = min(r0 + 8 * c, rmax - 8);
         src[j] = g + (int64_t)(kbeg + k) * ld + col;
       }

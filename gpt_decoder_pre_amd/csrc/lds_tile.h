@@ -9,7 +9,7 @@
 //     so that the fragment reads of 16 consecutive rows hit distinct banks;
 //   * transposed tile (rows are k, R elements each, fragments read with
 //     ds_read_b64_tr_b16, which hands each lane four consecutive k of one
-//     column): chunks are XOR-swizzled by tswz(k) = 2 (k mod 4).
+//     column): chunks are XOR-swizzled by tswz<R>(k) (below).
 #pragma once
 
 #include "common.h"
@@ -25,7 +25,17 @@ DEVI int kswz(int r) {
   if constexpr (BK == 32) return ((r >> 1) ^ (r >> 3)) & 3;
   else return (r ^ (r >> 3)) & 7;
 }
-DEVI int tswz(int k) { return 2 * (k & 3); }
+// A transposed fragment read takes, per 256-byte slice, 4 consecutive k rows
+// x 4 consecutive chunks.  For rows of 128 or 256 elements (a whole number of
+// bank cycles) the 4 rows must land in 4 different chunk quads: XOR by
+// 4 (k mod 4).  For 192-element rows consecutive rows are already half a
+// bank cycle apart and XOR by 2 (k mod 4) suffices (a 12-wide XOR would also
+// leave the row's 24 chunks).
+template <int R>
+DEVI int tswz(int k) {
+  if constexpr (R % 128 == 0) return 4 * (k & 3);
+  else return 2 * (k & 3);
+}
 
 
 // Workgroup barrier without the release fence of __syncthreads (which would
@@ -79,8 +89,8 @@ DEVI bf16x8 frag(const bf16* tile, int row0, int kk, int lane) {
     const int k = 16 * kk + 8 * (g >> 1) + (s >> 2);
     const int m = row0 + 16 * (g & 1) + 4 * (s & 3);
     const int c = m >> 3, o = m & 7;
-    const bf16* p1 = tile + k * R + 8 * (c ^ tswz(k)) + o;
-    const bf16* p2 = tile + (k + 4) * R + 8 * (c ^ tswz(k + 4)) + o;
+    const bf16* p1 = tile + k * R + 8 * (c ^ tswz<R>(k)) + o;
+    const bf16* p2 = tile + (k + 4) * R + 8 * (c ^ tswz<R>(k + 4)) + o;
     const i16x4g a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4g*)p1);
     const i16x4g b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4g*)p2);
     const u32x2 ua = __builtin_bit_cast(u32x2, a), ub = __builtin_bit_cast(u32x2, b);
