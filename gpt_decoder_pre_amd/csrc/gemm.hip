@@ -777,7 +777,7 @@ bool gemm_cfg(int cfg, GemmLayout layout, GemmEpilogue epi, bool bf16_mode, cons
       // 128 x 192 tile at two workgroups per CU (config 19) lets one
       // workgroup's epilogue run beside the other's MFMA loop (measured
       // 3-10% faster than the 256 x 192 tile for these GEMMs on MI355X).
-      const bool heavy_epi = epi == EPI_ACT || epi == EPI_GELU || epi == EPI_GELU_BWD || epi == EPI_RESID;
+      const bool heavy_epi = (epi == EPI_ACT && a.bias) || epi == EPI_GELU || epi == EPI_GELU_BWD || epi == EPI_RESID;
       cfg = heavy_epi && gemm_config_usable(19, layout, a) ? 19 : choose_cfg(a, layout);
     }
     if (!gemm_config_usable(cfg, layout, a)) return false;

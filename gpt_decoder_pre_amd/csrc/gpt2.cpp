@@ -359,14 +359,17 @@ int backward_impl(gpt2_ctx* c) {
   const double a = (double)c->act;
   float* part = c->colpart;
   // lm_head (tied): dlnf = dz wte; dwte += dz^T lnf
-  GemmArgs g = gargs(c->logits, Vp, c->W(T_WTE), C, M, C, Vp, c->dh, C);
-  if (!gemm_site(c, "gemm.bwd.lmhead.dx", LAYOUT_NN, EPI_F32, g, a * ((double)M * Vp + (double)Vp * C) + 4.0 * M * C))
+  // dh: gradient at a LayerNorm output, in the activation type (bf16 in bf16
+  // mode, like every other matmul output of the mixed-precision step)
+  TA* dh = (TA*)c->dh;
+  GemmArgs g = gargs(c->logits, Vp, c->W(T_WTE), C, M, C, Vp, dh, C);
+  if (!gemm_site(c, "gemm.bwd.lmhead.dx", LAYOUT_NN, EPI_ACT, g, a * ((double)M * Vp + (double)Vp * C + (double)M * C)))
     return GPT2_ERR_ARG;
   if (!weight_grad(c, "gemm.bwd.lmhead.dw", c->G(T_WTE), c->logits, Vp, c->lnf, C, Vp, C, M)) return GPT2_ERR_ARG;
   int ch;
   {
-    Timed tm(c, "ln.bwd", 0, (double)M * C * (12 + a) + 8.0 * M);
-    ch = layernorm_bwd<TA>(c->dh, c->resid(2 * L), c->lnf_mean, c->lnf_rstd, c->P(T_LNFW), c->dres, false,
+    Timed tm(c, "ln.bwd", 0, (double)M * C * (8 + 2 * a) + 8.0 * M);
+    ch = layernorm_bwd<TA>(dh, c->resid(2 * L), c->lnf_mean, c->lnf_rstd, c->P(T_LNFW), c->dres, false,
                            (TA*)c->dres_act, part, M, C, s);
   }
   colpart_reduce_add(c->G(T_LNFW), c->G(T_LNFB), c->G(T_FCPB, L - 1), part, ch, C, s);
@@ -395,12 +398,12 @@ int backward_impl(gpt2_ctx* c) {
     colpart_reduce_add(c->G(T_FCB, l), nullptr, nullptr, part, ch, 4 * C, s);
     // MLP input projection: u = LN2(x_mid) Wfc^T + bfc
     if (!weight_grad(c, "gemm.bwd.fc.dw", c->G(T_FCW, l), dbig, 4 * C, ln2, C, 4 * C, C, M)) return GPT2_ERR_ARG;
-    g = gargs(dbig, 4 * C, c->W(T_FCW, l), C, M, C, 4 * C, c->dh, C);
-    if (!gemm_site(c, "gemm.bwd.fc.dx", LAYOUT_NN, EPI_F32, g, a * (4.0 * M * C + 4.0 * C * C) + 4.0 * M * C))
+    g = gargs(dbig, 4 * C, c->W(T_FCW, l), C, M, C, 4 * C, dh, C);
+    if (!gemm_site(c, "gemm.bwd.fc.dx", LAYOUT_NN, EPI_ACT, g, a * (4.0 * M * C + 4.0 * C * C + (double)M * C)))
       return GPT2_ERR_ARG;
     {
-      Timed tm(c, "ln.bwd", 0, (double)M * C * (16 + a) + 8.0 * M);
-      ch = layernorm_bwd<TA>(c->dh, c->resid(2 * l + 1), c->ln2_mean + (int64_t)l * c->Mmax,
+      Timed tm(c, "ln.bwd", 0, (double)M * C * (12 + 2 * a) + 8.0 * M);
+      ch = layernorm_bwd<TA>(dh, c->resid(2 * l + 1), c->ln2_mean + (int64_t)l * c->Mmax,
                              c->ln2_rstd + (int64_t)l * c->Mmax, c->P(T_LN2W, l), c->dres, true, dres_act, part, M,
                              C, s);
     }
@@ -421,12 +424,12 @@ int backward_impl(gpt2_ctx* c) {
     colpart_reduce_add(c->G(T_QKVB, l), nullptr, nullptr, part, ch, 3 * C, s);
     // QKV projection: qkv = LN1(x_in) Wqkv^T + bqkv
     if (!weight_grad(c, "gemm.bwd.qkv.dw", c->G(T_QKVW, l), dqkv, 3 * C, ln1, C, 3 * C, C, M)) return GPT2_ERR_ARG;
-    g = gargs(dqkv, 3 * C, c->W(T_QKVW, l), C, M, C, 3 * C, c->dh, C);
-    if (!gemm_site(c, "gemm.bwd.qkv.dx", LAYOUT_NN, EPI_F32, g, a * (3.0 * M * C + 3.0 * C * C) + 4.0 * M * C))
+    g = gargs(dqkv, 3 * C, c->W(T_QKVW, l), C, M, C, 3 * C, dh, C);
+    if (!gemm_site(c, "gemm.bwd.qkv.dx", LAYOUT_NN, EPI_ACT, g, a * (3.0 * M * C + 3.0 * C * C + (double)M * C)))
       return GPT2_ERR_ARG;
     {
-      Timed tm(c, "ln.bwd", 0, (double)M * C * (16 + a) + 8.0 * M);
-      ch = layernorm_bwd<TA>(c->dh, c->resid(2 * l), c->ln1_mean + (int64_t)l * c->Mmax,
+      Timed tm(c, "ln.bwd", 0, (double)M * C * (12 + 2 * a) + 8.0 * M);
+      ch = layernorm_bwd<TA>(dh, c->resid(2 * l), c->ln1_mean + (int64_t)l * c->Mmax,
                              c->ln1_rstd + (int64_t)l * c->Mmax, c->P(T_LN1W, l), c->dres, true, dres_act, part, M,
                              C, s);
     }

@@ -79,7 +79,7 @@ void layernorm_fwd(const float* x, const float* w, const float* b, TA* y, float*
 // Partial column sums per row chunk: part[0][chunk][C] = sum dy*xhat, part[1] = sum dy,
 // part[2] = sum dres_out.  Returns the number of chunks.
 template <typename TA>
-int layernorm_bwd(const float* dy, const float* x, const float* mean, const float* rstd, const float* w,
+int layernorm_bwd(const TA* dy, const float* x, const float* mean, const float* rstd, const float* w,
                   float* dres, bool dres_in, TA* dres_act, float* part, int M, int C, hipStream_t s);
 // out_k[n] += sum_c part[(k * chunks + c) * N + n], c < chunks, n < N, for each non-null
 // out_k (k = 0, 1, 2; out1 / out2 may be null), summed in a fixed order.

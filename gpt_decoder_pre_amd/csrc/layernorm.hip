@@ -90,7 +90,7 @@ template void layernorm_fwd<bf16>(const float*, const float*, const float*, bf16
 
 // dx = rstd (dxhat - mean(dxhat) - xhat mean(dxhat xhat)), dxhat = dy w.
 template <typename TA, int NV>
-__global__ __launch_bounds__(256) void ln_bwd_kernel(const float* __restrict__ dy, const float* __restrict__ x,
+__global__ __launch_bounds__(256) void ln_bwd_kernel(const TA* __restrict__ dy, const float* __restrict__ x,
                                                      const float* __restrict__ mean,
                                                      const float* __restrict__ rstd,
                                                      const float* __restrict__ w, float* __restrict__ dres,
@@ -112,7 +112,7 @@ __global__ __launch_bounds__(256) void ln_bwd_kernel(const float* __restrict__ d
   }
   for (int row = r0 + wave; row < r1; row += 4) {
     const float mu = mean[row], rs = rstd[row];
-    const float* dyr = dy + (int64_t)row * C;
+    const TA* dyr = dy + (int64_t)row * C;
     const float* xr = x + (int64_t)row * C;
     float* dr = dres + (int64_t)row * C;
     float g[NV][4], xh[NV][4], o[NV][4];
@@ -186,7 +186,7 @@ __global__ __launch_bounds__(256) void ln_bwd_kernel(const float* __restrict__ d
 }
 
 template <typename TA>
-int layernorm_bwd(const float* dy, const float* x, const float* mean, const float* rstd, const float* w,
+int layernorm_bwd(const TA* dy, const float* x, const float* mean, const float* rstd, const float* w,
                   float* dres, bool dres_in, TA* dres_act, float* part, int M, int C, hipStream_t s) {
   const int rpb = 32;
   const int chunks = (M + rpb - 1) / rpb;
@@ -206,7 +206,7 @@ int layernorm_bwd(const float* dy, const float* x, const float* mean, const floa
 }
 template int layernorm_bwd<float>(const float*, const float*, const float*, const float*, const float*, float*,
                                   bool, float*, float*, int, int, hipStream_t);
-template int layernorm_bwd<bf16>(const float*, const float*, const float*, const float*, const float*, float*,
+template int layernorm_bwd<bf16>(const bf16*, const float*, const float*, const float*, const float*, float*,
                                  bool, bf16*, float*, int, int, hipStream_t);
 
 // out_k[n] += sum_c part[(k * chunks + c) * N + n] for the arrays k < nout.
