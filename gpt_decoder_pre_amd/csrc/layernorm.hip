@@ -89,15 +89,47 @@ template void layernorm_fwd<bf16>(const float*, const float*, const float*, bf16
                                   hipStream_t);
 
 // dx = rstd (dxhat - mean(dxhat) - xhat mean(dxhat xhat)), dxhat = dy w.
+//
+// A block of W wavefronts owns rows_per_block consecutive rows; each
+// wavefront takes every W-th of them.  For rows of up to 768 columns W = 8 at
+// no more than 128 VGPRs, so two blocks (four rows per SIMD) are resident and
+// their row loads overlap; wider rows need more registers and use W = 4.  The
+// per-wavefront column sums (gain, shift, residual gradient) are combined by
+// a fixed pairwise tree in LDS, then written as the block's partial row.
+template <int NV> constexpr int ln_bwd_waves() { return NV <= 3 ? 8 : 4; }
+
 template <typename TA, int NV>
-__global__ __launch_bounds__(256) void ln_bwd_kernel(const TA* __restrict__ dy, const float* __restrict__ x,
-                                                     const float* __restrict__ mean,
-                                                     const float* __restrict__ rstd,
-                                                     const float* __restrict__ w, float* __restrict__ dres,
-                                                     int dres_in, TA* __restrict__ dres_act,
-                                                     float* __restrict__ part, int M, int C, int rows_per_block,
-                                                     int chunks) {
-  __shared__ float red[3][NV * 256];
+struct LnBwdRow {
+  float g[NV][4], xv[NV][4], o[NV][4];
+  float mu, rs;
+  DEVI void load(const TA* dy, const float* x, const float* dres, int dres_in, const float* mean,
+                 const float* rstd, int row, int lane, int C) {
+    const int C4 = C >> 2;
+    mu = mean[row];
+    rs = rstd[row];
+    const TA* dyr = dy + (int64_t)row * C;
+    const float* xr = x + (int64_t)row * C;
+    const float* dr = dres + (int64_t)row * C;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int c4 = lane + i * 64;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) g[i][e] = xv[i][e] = o[i][e] = 0.f;
+      if (c4 < C4) {
+        load4(dyr + 4 * c4, g[i]);
+        load4(xr + 4 * c4, xv[i]);
+        if (dres_in) load4(dr + 4 * c4, o[i]);
+      }
+    }
+  }
+};
+
+template <typename TA, int NV, int W = ln_bwd_waves<NV>()>
+__global__ __launch_bounds__(64 * W, W == 8 ? 4 : 1) void ln_bwd_kernel(
+    const TA* __restrict__ dy, const float* __restrict__ x, const float* __restrict__ mean,
+    const float* __restrict__ rstd, const float* __restrict__ w, float* __restrict__ dres, int dres_in,
+    TA* __restrict__ dres_act, float* __restrict__ part, int M, int C, int rows_per_block, int chunks) {
+  __shared__ float red[W / 2][3][NV * 256];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int C4 = C >> 2;
   const int r0 = blockIdx.x * rows_per_block;
@@ -110,78 +142,79 @@ __global__ __launch_bounds__(256) void ln_bwd_kernel(const TA* __restrict__ dy, 
     for (int e = 0; e < 4; ++e) aw[i][e] = ab[i][e] = ar[i][e] = ww[i][e] = 0.f;
     if (c4 < C4) load4(w + 4 * c4, ww[i]);
   }
-  for (int row = r0 + wave; row < r1; row += 4) {
-    const float mu = mean[row], rs = rstd[row];
-    const TA* dyr = dy + (int64_t)row * C;
-    const float* xr = x + (int64_t)row * C;
-    float* dr = dres + (int64_t)row * C;
-    float g[NV][4], xh[NV][4], o[NV][4];
+  for (int row = r0 + wave; row < r1; row += W) {
+    LnBwdRow<TA, NV> cur;
+    cur.load(dy, x, dres, dres_in, mean, rstd, row, lane, C);
+    float xh[NV][4];
     float s1 = 0.f, s2 = 0.f;
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
-      const int c4 = lane + i * 64;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) o[i][e] = 0.f;
-      if (c4 < C4) {
-        float xv[4];
-        load4(dyr + 4 * c4, g[i]);
-        load4(xr + 4 * c4, xv);
-        if (dres_in) load4(dr + 4 * c4, o[i]);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          xh[i][e] = (xv[e] - mu) * rs;
-          const float d = g[i][e] * ww[i][e];
-          s1 += d;
-          s2 += d * xh[i][e];
-          aw[i][e] += g[i][e] * xh[i][e];
-          ab[i][e] += g[i][e];
-        }
+      for (int e = 0; e < 4; ++e) {
+        xh[i][e] = (cur.xv[i][e] - cur.mu) * cur.rs;
+        const float d = cur.g[i][e] * ww[i][e];
+        s1 += d;
+        s2 += d * xh[i][e];
+        aw[i][e] += cur.g[i][e] * xh[i][e];
+        ab[i][e] += cur.g[i][e];
       }
     }
     const float m1 = wave_sum(s1) / (float)C, m2 = wave_sum(s2) / (float)C;
+    float* dr = dres + (int64_t)row * C;
     TA* da = dres_act + (int64_t)row * C;
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
       const int c4 = lane + i * 64;
       if (c4 < C4) {
+        float o[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          o[i][e] += rs * (g[i][e] * ww[i][e] - m1 - xh[i][e] * m2);
-          ar[i][e] += o[i][e];
+          o[e] = cur.o[i][e] + cur.rs * (cur.g[i][e] * ww[i][e] - m1 - xh[i][e] * m2);
+          ar[i][e] += o[e];
         }
-        store4(dr + 4 * c4, o[i]);
-        store4(da + 4 * c4, o[i]);
+        store4(dr + 4 * c4, o);
+        store4(da + 4 * c4, o);
       }
     }
   }
-  // combine the four waves in a fixed order
-  for (int wv = 0; wv < 4; ++wv) {
-    if (wave == wv) {
+  // fixed pairwise tree: wave w += wave w + h for h = W/2, ..., 2, 1
 #pragma unroll
-      for (int i = 0; i < NV; ++i) {
-        const int c4 = lane + i * 64;
-        if (c4 < C4) {
+  for (int h = W / 2; h >= 1; h >>= 1) {
+    if (wave >= h && wave < 2 * h) {
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int c = 4 * c4 + e;
-            if (wv == 0) {
-              red[0][c] = aw[i][e];
-              red[1][c] = ab[i][e];
-              red[2][c] = ar[i][e];
-            } else {
-              red[0][c] += aw[i][e];
-              red[1][c] += ab[i][e];
-              red[2][c] += ar[i][e];
-            }
-          }
+      for (int i = 0; i < NV; ++i)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int c = 4 * (lane + i * 64) + e;
+          red[wave - h][0][c] = aw[i][e];
+          red[wave - h][1][c] = ab[i][e];
+          red[wave - h][2][c] = ar[i][e];
         }
-      }
+    }
+    __syncthreads();
+    if (wave < h) {
+#pragma unroll
+      for (int i = 0; i < NV; ++i)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int c = 4 * (lane + i * 64) + e;
+          aw[i][e] += red[wave][0][c];
+          ab[i][e] += red[wave][1][c];
+          ar[i][e] += red[wave][2][c];
+        }
     }
     __syncthreads();
   }
-  for (int c = threadIdx.x; c < C; c += blockDim.x) {
+  if (wave == 0) {
 #pragma unroll
-    for (int k = 0; k < 3; ++k) part[((int64_t)k * chunks + blockIdx.x) * C + c] = red[k][c];
+    for (int i = 0; i < NV; ++i) {
+      const int c4 = lane + i * 64;
+      if (c4 < C4) {
+        store4(part + ((int64_t)0 * chunks + blockIdx.x) * C + 4 * c4, aw[i]);
+        store4(part + ((int64_t)1 * chunks + blockIdx.x) * C + 4 * c4, ab[i]);
+        store4(part + ((int64_t)2 * chunks + blockIdx.x) * C + 4 * c4, ar[i]);
+      }
+    }
   }
 }
 
@@ -190,18 +223,20 @@ int layernorm_bwd(const TA* dy, const float* x, const float* mean, const float* 
                   float* dres, bool dres_in, TA* dres_act, float* part, int M, int C, hipStream_t s) {
   const int rpb = 32;
   const int chunks = (M + rpb - 1) / rpb;
-#define GPT2_LN_ARGS chunks, 256, 0, s>>>(dy, x, mean, rstd, w, dres, dres_in ? 1 : 0, dres_act, part, M, C, rpb, chunks
+#define GPT2_LN_BWD(NV)                                                                          \
+  ln_bwd_kernel<TA, NV><<<chunks, 64 * ln_bwd_waves<NV>(), 0, s>>>(dy, x, mean, rstd, w, dres, dres_in ? 1 : 0, \
+                                                                   dres_act, part, M, C, rpb, chunks)
   switch ((C / 4 + 63) / 64) {
-    case 1: ln_bwd_kernel<TA, 1><<<GPT2_LN_ARGS); break;
-    case 2: ln_bwd_kernel<TA, 2><<<GPT2_LN_ARGS); break;
-    case 3: ln_bwd_kernel<TA, 3><<<GPT2_LN_ARGS); break;
-    case 4: ln_bwd_kernel<TA, 4><<<GPT2_LN_ARGS); break;
-    case 5: ln_bwd_kernel<TA, 5><<<GPT2_LN_ARGS); break;
-    case 6: ln_bwd_kernel<TA, 6><<<GPT2_LN_ARGS); break;
-    case 7: ln_bwd_kernel<TA, 7><<<GPT2_LN_ARGS); break;
-    default: ln_bwd_kernel<TA, 8><<<GPT2_LN_ARGS); break;
+    case 1: GPT2_LN_BWD(1); break;
+    case 2: GPT2_LN_BWD(2); break;
+    case 3: GPT2_LN_BWD(3); break;
+    case 4: GPT2_LN_BWD(4); break;
+    case 5: GPT2_LN_BWD(5); break;
+    case 6: GPT2_LN_BWD(6); break;
+    case 7: GPT2_LN_BWD(7); break;
+    default: GPT2_LN_BWD(8); break;
   }
-#undef GPT2_LN_ARGS
+#undef GPT2_LN_BWD
   return chunks;
 }
 template int layernorm_bwd<float>(const float*, const float*, const float*, const float*, const float*, float*,
