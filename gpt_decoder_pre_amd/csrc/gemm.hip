@@ -394,6 +394,9 @@ DEVI void gemm_epilogue(const GemmArgs& p, f32x16 (&acc)[FM][FN], bf16* region, 
               for (int e = 0; e < 4; ++e) v[e] *= gelu_grad_f(u[e]);
             }
             store4(region + (i * 32 + lc) * SLD + nl, v);
+            // one accumulator block at a time: the scheduler must not copy
+            // every accumulator out of the AGPRs at once
+            if (q == 3) __builtin_amdgcn_sched_barrier(0);
           }
       __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's LDS writes are done
       __builtin_amdgcn_wave_barrier();
@@ -425,6 +428,7 @@ DEVI void gemm_epilogue(const GemmArgs& p, f32x16 (&acc)[FM][FN], bf16* region, 
             epi_store4<EPI, bf16>(p, m, n, v, split);
           }
         }
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
   }
@@ -553,6 +557,190 @@ __global__ __launch_bounds__(64 * WGM * WGN, OCC) void gemm_lds_kernel(GemmArgs 
     __syncthreads();  // all waves are done reading the operand stages
     bf16* region = (wave < WPA ? st0 : st1) + (wave % WPA) * WTM * SLD;
     gemm_epilogue<EPI, FM, FN, true>(pe, acc, region, m0 + wm * WTM, n0 + wn * WTN, lane, split);
+  } else {
+    gemm_epilogue<EPI, FM, FN, false>(pe, acc, nullptr, m0 + wm * WTM, n0 + wn * WTN, lane, split);
+  }
+}
+
+// ------------------------------------------------------- one wave per SIMD ----
+// 2 x 2 waves, each owning a (BM/2) x (BN/2) accumulator tile (up to 256
+// accumulators, which live in AGPRs), BK = 64, two LDS stages filled by
+// global_load_lds.  With one wave per SIMD nothing hides a stall behind
+// another wave, so the k-loop is scheduled explicitly: after every MFMA the
+// wave issues at most one fragment read for the next 16-k step (double-
+// buffered fragment registers) and, in the last 16-k step of a k-tile, its
+// share of the direct loads of the k-tile after next.  A k-tile's only
+// barrier sits before its last 16-k step, once every wave holds that step's
+// fragments.  Measured on MI355X the loop runs at about 95% of the MFMA peak
+// without the operand loads; with them it is bound by the operand stream
+// (about 40-48 GB/s per CU from L2).
+
+// This wave's share of one R x 64 operand tile, in the SADDR form: a wave-
+// uniform base (advanced per k-tile) plus a 32-bit per-lane byte offset.
+template <bool KMAJ, int R, int NW>
+struct SaddrLoader {
+  static constexpr int INSTR = R * 64 * 2 / 1024;  // 1 KB wave instructions per k-tile
+  static constexpr int PER_WAVE = INSTR / NW;
+  static_assert(INSTR % NW == 0, "whole instructions per wave");
+  const bf16* base;
+  uint32_t voff[PER_WAVE];
+  uint32_t lds[PER_WAVE];
+  int64_t kstep;
+
+  // Rows past rmax are clamped to the last row (their outputs are discarded).
+  DEVI void init(const bf16* g, int64_t ld, int r0, int rmax, int kbeg, const bf16* lds_tile, int wave, int lane) {
+    base = uniform_ptr(KMAJ ? g + (int64_t)r0 * ld + kbeg : g + (int64_t)kbeg * ld + r0);
+#pragma unroll
+    for (int j = 0; j < PER_WAVE; ++j) {
+      const int J = wave * PER_WAVE + j;
+      const int byte = J * 1024 + lane * 16;
+      if constexpr (KMAJ) {
+        const int r = byte / 128, pc = (byte % 128) / 16;
+        const int c = pc ^ kswz<64>(r);
+        const int row = min(r0 + r, rmax - 1);
+        voff[j] = (uint32_t)(((int64_t)(row - r0) * ld + 8 * c) * 2);
+      } else {
+        const int k = byte / (R * 2), pc = (byte % (R * 2)) / 16;
+        const int c = pc ^ tswz<R>(k);
+        const int col = min(r0 + 8 * c, rmax - 8);
+        voff[j] = (uint32_t)(((int64_t)k * ld + (col - r0)) * 2);
+      }
+      lds[j] = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void*)(lds_tile + J * 512));
+    }
+    kstep = KMAJ ? (int64_t)64 : (int64_t)64 * ld;
+  }
+  DEVI void issue(int j, int kt, uint32_t stage_off) const {
+    dma16s(base + kt * kstep, voff[j], lds[j] + stage_off);
+  }
+};
+
+template <bool A_K, bool B_K, int BM, int BN, int EPI>
+__global__ __launch_bounds__(256, 1) void gemm_w4_kernel(GemmArgs p) {
+  constexpr int BK = 64, NW = 4;
+  constexpr int WTM = BM / 2, WTN = BN / 2;
+  constexpr int FM = WTM / 32, FN = WTN / 32;
+  constexpr int STAGE = (BM + BN) * BK;  // elements
+  constexpr int SLD = WTN + 8;           // staged epilogue row stride
+  constexpr int EPI_ELEMS = NW * WTM * SLD;
+  constexpr int LDS_ELEMS = 2 * STAGE > EPI_ELEMS ? 2 * STAGE : EPI_ELEMS;
+  using LA = SaddrLoader<A_K, BM, NW>;
+  using LB = SaddrLoader<B_K, BN, NW>;
+  constexpr int LPW = LA::PER_WAVE + LB::PER_WAVE;
+  constexpr int G = FM * FN;  // MFMAs per 16-k step
+  __shared__ __attribute__((aligned(1024))) bf16 smem[LDS_ELEMS];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+  const int tiles_m = (p.M + BM - 1) / BM, tiles_n = (p.N + BN - 1) / BN;
+  int tm, tn, split;
+  tile_coords(p, tiles_m, tiles_n, blockIdx.x + blockIdx.y * gridDim.x, gridDim.x * gridDim.y, tm, tn, split);
+  const int m0 = tm * BM, n0 = tn * BN;
+  const int kbeg = split * p.k_per_split;
+  const int kend = min(p.K, kbeg + p.k_per_split);
+  const int nkt = kend > kbeg ? (kend - kbeg) / BK : 0;
+
+  LA la;
+  LB lb;
+  la.init(reinterpret_cast<const bf16*>(p.A), p.lda, m0, p.M, kbeg, smem, wave, lane);
+  lb.init(reinterpret_cast<const bf16*>(p.B), p.ldb, n0, p.N, kbeg, smem + BM * BK, wave, lane);
+  constexpr uint32_t kStageBytes = STAGE * 2;
+  // direct load number d (A loads first) of k-tile kt into the stage at stage_off
+  auto dma = [&](int d, int kt, uint32_t stage_off) {
+    if (d < LA::PER_WAVE) la.issue(d, kt, stage_off);
+    else lb.issue(d - LA::PER_WAVE, kt, stage_off);
+  };
+
+  constexpr bool kBiasInit = EPI == EPI_ACT || EPI == EPI_GELU || EPI == EPI_RESID;
+  f32x16 acc[FM][FN];
+#pragma unroll
+  for (int j = 0; j < FN; ++j)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      float b[4] = {0.f, 0.f, 0.f, 0.f};
+      if constexpr (kBiasInit) {
+        const int n = n0 + wn * WTN + j * 32 + 8 * q + 4 * (lane >> 5);
+        if (p.bias && n < p.N && split == 0) load4(p.bias + n, b);
+      }
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[i][j][4 * q + e] = b[e];
+    }
+
+  bf16x8 fa[2][FM], fb[2][FN];
+  auto read_a = [&](int buf, int i, const bf16* st, int kk) {
+    fa[buf][i] = frag<A_K, BM, BK>(st, wm * WTM + i * 32, kk, lane);
+  };
+  auto read_b = [&](int buf, int j, const bf16* st, int kk) {
+    fb[buf][j] = frag<B_K, BN, BK>(st + BM * BK, wn * WTN + j * 32, kk, lane);
+  };
+
+  // One k-tile.  NEXT: k-tile kt + 1 exists (its fragments are read in the
+  // last 16-k step); LOAD: k-tile kt + 2 exists (it is loaded into this
+  // k-tile's stage once every wave is past the barrier).
+  auto ktile = [&](auto next_c, auto load_c, int kt) {
+    constexpr bool NEXT = decltype(next_c)::value, LOAD = decltype(load_c)::value;
+    const bf16* cur = smem + (kt & 1) * STAGE;
+    const bf16* nxt = smem + ((kt + 1) & 1) * STAGE;
+    const uint32_t cur_off = (kt & 1) * kStageBytes;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      const int cb = kk & 1;
+      if (kk == 3 && NEXT) {
+        // k-tile kt + 1 has landed for every wave, and every wave holds the
+        // fragments of this last 16-k step: the stage of k-tile kt is free
+        wait_vmcnt<0>();
+        __builtin_amdgcn_s_waitcnt(0xc07f);
+        lds_barrier();
+      }
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        const int i = g / FN, j = g % FN;
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[cb][j], fa[cb][i], acc[i][j], 0, 0, 0);
+        if (kk < 3) {
+          if (g < FM) read_a(cb ^ 1, g, cur, kk + 1);
+          else if (g < FM + FN) read_b(cb ^ 1, g - FM, cur, kk + 1);
+        } else if (NEXT) {
+          if (g < FM) read_a(cb ^ 1, g, nxt, 0);
+          else if (g < FM + FN) read_b(cb ^ 1, g - FM, nxt, 0);
+          if (LOAD) {
+            // the k-tile's direct loads spread evenly over this step's MFMAs
+#pragma unroll
+            for (int d = g * LPW / G; d < (g + 1) * LPW / G; ++d) dma(d, kt + 2, cur_off);
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  };
+
+  // every split has at least one k-tile (the host requires K = splits x
+  // k_per_split with k_per_split a positive multiple of 64)
+#pragma unroll
+  for (int d = 0; d < LPW; ++d) dma(d, 0, 0);
+  if (nkt > 1) {
+#pragma unroll
+    for (int d = 0; d < LPW; ++d) dma(d, 1, kStageBytes);
+    wait_vmcnt<LPW>();
+  } else {
+    wait_vmcnt<0>();
+  }
+  lds_barrier();
+#pragma unroll
+  for (int i = 0; i < FM; ++i) read_a(0, i, smem, 0);
+#pragma unroll
+  for (int j = 0; j < FN; ++j) read_b(0, j, smem, 0);
+  int kt = 0;
+  for (; kt + 2 < nkt; ++kt) ktile(std::true_type{}, std::true_type{}, kt);
+  if (kt + 1 < nkt) ktile(std::true_type{}, std::false_type{}, kt++);
+  ktile(std::false_type{}, std::false_type{}, kt);
+
+  GemmArgs pe = p;
+  if constexpr (kBiasInit) pe.bias = nullptr;  // already in the accumulators
+  if constexpr (epi_staged<EPI>()) {
+    __syncthreads();  // all waves are done reading the operand stages
+    gemm_epilogue<EPI, FM, FN, true>(pe, acc, smem + wave * WTM * SLD, m0 + wm * WTM, n0 + wn * WTN, lane, split);
   } else {
     gemm_epilogue<EPI, FM, FN, false>(pe, acc, nullptr, m0 + wm * WTM, n0 + wn * WTN, lane, split);
   }
@@ -689,12 +877,24 @@ void launch_bf16_cfg(int cfg, const GemmArgs& a, hipStream_t s) {
     default: break;
   }
 #undef GPT2_GEMM_LDS
+#define GPT2_GEMM_W4(ID, BM, BN)                                                                \
+  case ID: {                                                                                   \
+    const int tiles = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);                           \
+    gemm_w4_kernel<A_K, B_K, BM, BN, EPI><<<dim3(tiles, a.splits), 256, 0, s>>>(a);            \
+    break;                                                                                     \
+  }
+  switch (cfg) {
+    GPT2_GEMM_W4(20, 256, 256)
+    GPT2_GEMM_W4(21, 256, 192)
+    default: break;
+  }
+#undef GPT2_GEMM_W4
 }
-constexpr int kNumCfg = 20;
+constexpr int kNumCfg = 22;
 constexpr int kFirstLds = 6;
-const int kCfgBM[kNumCfg] = {128, 256, 256, 256, 256, 128, 256, 256, 256, 256, 128, 256, 128, 256, 256, 256, 256, 128, 256, 128};
-const int kCfgBN[kNumCfg] = {128, 128, 256, 192, 256, 256, 256, 256, 256, 128, 256, 192, 128, 256, 256, 192, 128, 256, 256, 192};
-const int kCfgBK[kNumCfg] = {64, 64, 64, 64, 64, 64, 32, 32, 64, 32, 32, 32, 32, 64, 32, 64, 64, 64, 64, 64};
+const int kCfgBM[kNumCfg] = {128, 256, 256, 256, 256, 128, 256, 256, 256, 256, 128, 256, 128, 256, 256, 256, 256, 128, 256, 128, 256, 256};
+const int kCfgBN[kNumCfg] = {128, 128, 256, 192, 256, 256, 256, 256, 256, 128, 256, 192, 128, 256, 256, 192, 128, 256, 256, 192, 256, 192};
+const int kCfgBK[kNumCfg] = {64, 64, 64, 64, 64, 64, 32, 32, 64, 32, 32, 32, 32, 64, 32, 64, 64, 64, 64, 64, 64, 64};
 
 template <bool A_K, bool B_K, int EPI>
 void launch_f32(const GemmArgs& a, hipStream_t s) {
@@ -715,9 +915,9 @@ void launch(bool bf16_mode, int cfg, const GemmArgs& a, hipStream_t s) {
 double model_time(int c, const GemmArgs& a, bool transposed_a) {
   // sustained TFLOP/s at full waves; 13 spills registers and is never chosen
   static const double tf_k[kNumCfg] = {560, 480, 650, 720, 750, 500, 750, 800, 880, 650, 650, 930, 820,
-                                        1, 820, 1020, 760, 760, 900, 1};  // A k-contiguous
+                                        1, 820, 1020, 760, 760, 900, 1, 1090, 1060};  // A k-contiguous
   static const double tf_t[kNumCfg] = {450, 460, 660, 560, 640, 380, 860, 880, 950, 740, 740, 900, 820,
-                                        1, 950, 930, 850, 900, 930, 1};   // A transposed
+                                        1, 950, 930, 850, 900, 930, 1, 1080, 1000};   // A transposed
   const int64_t tm = (a.M + kCfgBM[c] - 1) / kCfgBM[c], tn = (a.N + kCfgBN[c] - 1) / kCfgBN[c];
   const double waves = (double)(tm * tn * a.splits) / 256.0;
   const double fill = waves / std::ceil(waves);
@@ -772,13 +972,17 @@ bool gemm_cfg(int cfg, GemmLayout layout, GemmEpilogue epi, bool bf16_mode, cons
     if (a.K % 8 || a.N % 8 || a.ldc % 4 || a.lda % 8 || a.ldb % 8) return false;
     if (layout == LAYOUT_TN && a.M % 8) return false;
     if (cfg < 0) {
-      // Epilogues that do per-element work on bf16 / fp32 activations (bias,
-      // GELU, GELU', residual add) cost as much as a short-K main loop; the
-      // 128 x 192 tile at two workgroups per CU (config 19) lets one
-      // workgroup's epilogue run beside the other's MFMA loop (measured
-      // 3-10% faster than the 256 x 192 tile for these GEMMs on MI355X).
-      const bool heavy_epi = (epi == EPI_ACT && a.bias) || epi == EPI_GELU || epi == EPI_GELU_BWD || epi == EPI_RESID;
-      cfg = heavy_epi && gemm_config_usable(19, layout, a) ? 19 : choose_cfg(a, layout);
+      // Epilogues that do per-element work on bf16 activations (bias, GELU,
+      // GELU') cost as much as a short-K main loop; the 128 x 192 tile at two
+      // workgroups per CU (config 19) lets one workgroup's epilogue run beside
+      // the other's MFMA loop (measured 5-40% faster than the one-wave-per-SIMD
+      // tiles for these GEMMs on MI355X).  The residual add is cheaper per
+      // byte and takes the 256 x 192 one-wave-per-SIMD tile (config 21, 7%
+      // faster than config 19).
+      const bool heavy_epi = (epi == EPI_ACT && a.bias) || epi == EPI_GELU || epi == EPI_GELU_BWD;
+      if (heavy_epi && gemm_config_usable(19, layout, a)) cfg = 19;
+      else if (epi == EPI_RESID && gemm_config_usable(21, layout, a)) cfg = 21;
+      else cfg = choose_cfg(a, layout);
     }
     if (!gemm_config_usable(cfg, layout, a)) return false;
   }

@@ -159,13 +159,21 @@ struct gpt2_ctx {
 
 namespace {
 
+// True when `prefix` is `site` or a leading run of its dot-separated parts
+// ("gemm.fwd" matches "gemm.fwd.fc"; "gemm.fwd.fc" does not match "gemm.fwd.fcproj").
+bool site_matches(const char* site, const std::string& prefix) {
+  if (strncmp(site, prefix.c_str(), prefix.size()) != 0) return false;
+  const char next = site[prefix.size()];
+  return next == '\0' || next == '.' || prefix.empty();
+}
+
 // Brackets one launch with HIP events when its site matches the enabled prefix.
 struct Timed {
   gpt2_ctx* c;
   bool on = false;
   size_t slot = 0;
   Timed(gpt2_ctx* ctx, const char* site, double flops, double bytes) : c(ctx) {
-    if (!c->timing || strncmp(site, c->site.c_str(), c->site.size()) != 0) return;
+    if (!c->timing || !site_matches(site, c->site)) return;
     if (c->ev_used * 2 + 2 > c->ev.size()) {
       if (c->ev.size() >= 2 * 8192) {
         c->ev_overflow = true;

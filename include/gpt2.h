@@ -186,8 +186,9 @@ int gpt2_tensor_info(const gpt2_config *cfg, int index, const char **name,
 int gpt2_activation(gpt2_ctx *ctx, const char *name, int layer, void **ptr,
                     int64_t *numel, int32_t *dtype);
 
-/* Per-launch timing with HIP events on the context's stream.  site: a prefix
-   of launch-site names (e.g. "gemm.fwd.lmhead", "attn.fwd", "gemm"), or NULL
+/* Per-launch timing with HIP events on the context's stream.  site: a leading
+   run of the dot-separated parts of launch-site names (e.g. "gemm.fwd.lmhead",
+   "attn.fwd", "gemm"; "gemm.fwd.fc" does not match "gemm.fwd.fcproj"), or NULL
    to stop.  Enabling clears the record.  gpt2_timing_read synchronises and
    returns the summed kernel time, the launch count and the summed
    algorithmic flops and bytes of the matched launches. */
