@@ -62,12 +62,13 @@ DEVI float gelu_sigmoid(float u) {
   const float t = u * u;
   return rcp_fast(1.0f + exp2_fast(u * fmaf(kGeluZ3, t, kGeluZ1)));
 }
-DEVI float gelu_f(float u) { return u * gelu_sigmoid(u); }
+// gelu(u) and its derivative from one sigmoid:
 // d/du [u sigmoid(z)] = s + u s (1 - s) dz/du,  dz/du = 2 k (1 + 3 * 0.044715 u^2)
-DEVI float gelu_grad_f(float u) {
+DEVI void gelu_and_grad(float u, float& g, float& d) {
   const float s = gelu_sigmoid(u);
   const float dz = 2.0f * kGeluK * fmaf(3.0f * kGeluA, u * u, 1.0f);
-  return fmaf(u * s * (1.0f - s), dz, s);
+  g = u * s;
+  d = fmaf(g * (1.0f - s), dz, s);
 }
 
 // ---- wave / block reductions ---------------------------------------------------

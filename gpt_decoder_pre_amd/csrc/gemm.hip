@@ -49,20 +49,17 @@ DEVI void epi_store4(const GemmArgs& p, int m, int n, float v[4], int split) {
     for (int i = 0; i < 4; ++i) v[i] = r[i] + (v[i] + b[i]);
     store4(reinterpret_cast<float*>(p.C) + off, v);
   } else if constexpr (EPI == EPI_GELU) {
-    float b[4] = {0.f, 0.f, 0.f, 0.f}, g[4];
+    float b[4] = {0.f, 0.f, 0.f, 0.f}, g[4], d[4];
     if (p.bias) load4(p.bias + n, b);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      v[i] += b[i];
-      g[i] = gelu_f(v[i]);
-    }
-    store4(reinterpret_cast<TA*>(p.C) + off, v);
+    for (int i = 0; i < 4; ++i) gelu_and_grad(v[i] + b[i], g[i], d[i]);
+    store4(reinterpret_cast<TA*>(p.C) + off, d);
     store4(reinterpret_cast<TA*>(p.C2) + off, g);
   } else if constexpr (EPI == EPI_GELU_BWD) {
-    float u[4];
-    load4(reinterpret_cast<const TA*>(p.aux) + off, u);
+    float d[4];
+    load4(reinterpret_cast<const TA*>(p.aux) + off, d);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) v[i] *= gelu_grad_f(u[i]);
+    for (int i = 0; i < 4; ++i) v[i] *= d[i];
     store4(reinterpret_cast<TA*>(p.C) + off, v);
   } else {  // EPI_PARTIAL
     store4(reinterpret_cast<float*>(p.C) + (int64_t)split * p.split_stride + off, v);
@@ -84,11 +81,12 @@ DEVI void epi_store1(const GemmArgs& p, int m, int n, float v, int split) {
   } else if constexpr (EPI == EPI_RESID) {
     reinterpret_cast<float*>(p.C)[off] = p.resid[off] + (v + p.bias[n]);
   } else if constexpr (EPI == EPI_GELU) {
-    const float u = v + p.bias[n];
-    reinterpret_cast<TA*>(p.C)[off] = from_f32<TA>(u);
-    reinterpret_cast<TA*>(p.C2)[off] = from_f32<TA>(gelu_f(u));
+    float g, d;
+    gelu_and_grad(v + p.bias[n], g, d);
+    reinterpret_cast<TA*>(p.C)[off] = from_f32<TA>(d);
+    reinterpret_cast<TA*>(p.C2)[off] = from_f32<TA>(g);
   } else if constexpr (EPI == EPI_GELU_BWD) {
-    reinterpret_cast<TA*>(p.C)[off] = from_f32<TA>(v * gelu_grad_f(to_f32(reinterpret_cast<const TA*>(p.aux)[off])));
+    reinterpret_cast<TA*>(p.C)[off] = from_f32<TA>(v * to_f32(reinterpret_cast<const TA*>(p.aux)[off]));
   } else {
     reinterpret_cast<float*>(p.C)[(int64_t)split * p.split_stride + off] = v;
   }
@@ -349,7 +347,7 @@ DEVI void gemm_epilogue(const GemmArgs& p, f32x16 (&acc)[FM][FN], bf16* region, 
     constexpr int NOUT = EPI == EPI_GELU ? 2 : 1;
     constexpr int CPR = WTN / 8;  // 16-byte chunks per staged row
     if constexpr (EPI == EPI_GELU_BWD) {
-      // the pre-activation tile u comes in whole row segments too
+      // the gelu'(u) tile comes in whole row segments too
       const bf16* aux = reinterpret_cast<const bf16*>(p.aux);
 #pragma unroll
       for (int it = 0; it < WTM * CPR / 64; ++it) {
@@ -358,6 +356,7 @@ DEVI void gemm_epilogue(const GemmArgs& p, f32x16 (&acc)[FM][FN], bf16* region, 
         const int m = mb + r, n = nb + 8 * c;
         *reinterpret_cast<u32x4*>(region + r * SLD + 8 * c) =
             ld16_or_zero(aux + (int64_t)m * p.ldc + n, m < p.M && n < p.N);
+        if (it % 8 == 7) __builtin_amdgcn_sched_barrier(0);  // bounded loads in flight
       }
       __builtin_amdgcn_s_waitcnt(0xc07f);
       __builtin_amdgcn_wave_barrier();
@@ -374,7 +373,7 @@ DEVI void gemm_epilogue(const GemmArgs& p, f32x16 (&acc)[FM][FN], bf16* region, 
             const int n = nb + nl;
             float v[4] = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
             if constexpr (EPI == EPI_ACT || EPI == EPI_GELU) {
-              if (p.bias && n < p.N) {
+              if (o == 0 && p.bias && n < p.N) {
                 float bb[4];
                 load4(p.bias + n, bb);
 #pragma unroll
@@ -382,16 +381,22 @@ DEVI void gemm_epilogue(const GemmArgs& p, f32x16 (&acc)[FM][FN], bf16* region, 
               }
             }
             if constexpr (EPI == EPI_GELU) {
-              if (o == 1) {
+              // pass 0 writes gelu'(u) and leaves gelu(u) in the accumulators
+              // for pass 1: one sigmoid per element
+              if (o == 0) {
 #pragma unroll
-                for (int e = 0; e < 4; ++e) v[e] = gelu_f(v[e]);
+                for (int e = 0; e < 4; ++e) {
+                  float g;
+                  gelu_and_grad(v[e], g, v[e]);
+                  acc[i][j][4 * q + e] = g;
+                }
               }
             }
             if constexpr (EPI == EPI_GELU_BWD) {
-              float u[4];
-              load4(region + (i * 32 + lc) * SLD + nl, u);
+              float d[4];
+              load4(region + (i * 32 + lc) * SLD + nl, d);
 #pragma unroll
-              for (int e = 0; e < 4; ++e) v[e] *= gelu_grad_f(u[e]);
+              for (int e = 0; e < 4; ++e) v[e] *= d[e];
             }
             store4(region + (i * 32 + lc) * SLD + nl, v);
             // one accumulator block at a time: the scheduler must not copy

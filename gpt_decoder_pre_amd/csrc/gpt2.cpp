@@ -109,7 +109,7 @@ struct gpt2_ctx {
   float* lse;
   char* ln2;
   float *ln2_mean, *ln2_rstd;
-  char* fcu;
+  char* fcgd;  // gelu'(u) of the MLP pre-activation u, the only use of u in the backward
   char* fcg;
   char* lnf;
   float *lnf_mean, *lnf_rstd;
@@ -302,7 +302,7 @@ int forward_impl(gpt2_ctx* c, const int32_t* d_idx, const int32_t* d_tgt, int B,
     TA* qkv = (TA*)c->layer_act(c->qkv, l, 3 * C);
     TA* atty = (TA*)c->layer_act(c->atty, l, C);
     TA* ln2 = (TA*)c->layer_act(c->ln2, l, C);
-    TA* fcu = (TA*)c->layer_act(c->fcu, l, 4 * C);
+    TA* fcgd = (TA*)c->layer_act(c->fcgd, l, 4 * C);
     TA* fcg = (TA*)c->layer_act(c->fcg, l, 4 * C);
     float* lse = c->lse + (int64_t)l * c->Mmax * c->NH;
     {
@@ -330,7 +330,7 @@ int forward_impl(gpt2_ctx* c, const int32_t* d_idx, const int32_t* d_tgt, int B,
       layernorm_fwd<TA>(x_mid, c->P(T_LN2W, l), c->P(T_LN2B, l), ln2, c->ln2_mean + (int64_t)l * c->Mmax,
                         c->ln2_rstd + (int64_t)l * c->Mmax, M, C, s);
     }
-    g = gargs(ln2, C, c->W(T_FCW, l), C, M, 4 * C, C, fcu, 4 * C);
+    g = gargs(ln2, C, c->W(T_FCW, l), C, M, 4 * C, C, fcgd, 4 * C);
     g.bias = c->P(T_FCB, l);
     g.C2 = fcg;
     if (!gemm_site(c, "gemm.fwd.fc", LAYOUT_NT, EPI_GELU, g, a * ((double)M * C + 4.0 * C * C + 8.0 * M * C)))
@@ -387,7 +387,7 @@ int backward_impl(gpt2_ctx* c) {
     TA* qkv = (TA*)c->layer_act(c->qkv, l, 3 * C);
     TA* atty = (TA*)c->layer_act(c->atty, l, C);
     TA* ln2 = (TA*)c->layer_act(c->ln2, l, C);
-    TA* fcu = (TA*)c->layer_act(c->fcu, l, 4 * C);
+    TA* fcgd = (TA*)c->layer_act(c->fcgd, l, 4 * C);
     TA* fcg = (TA*)c->layer_act(c->fcg, l, 4 * C);
     float* lse = c->lse + (int64_t)l * c->Mmax * c->NH;
     TA* dres_act = (TA*)c->dres_act;
@@ -399,7 +399,7 @@ int backward_impl(gpt2_ctx* c) {
     if (!weight_grad(c, "gemm.bwd.fcproj.dw", c->G(T_FCPW, l), dres_act, C, fcg, 4 * C, C, 4 * C, M))
       return GPT2_ERR_ARG;
     g = gargs(dres_act, C, c->W(T_FCPW, l), 4 * C, M, 4 * C, C, dbig, 4 * C);
-    g.aux = fcu;
+    g.aux = fcgd;
     if (!gemm_site(c, "gemm.bwd.fcproj.dx", LAYOUT_NN, EPI_GELU_BWD, g, a * ((double)M * C + 4.0 * C * C + 8.0 * M * C)))
       return GPT2_ERR_ARG;
     ch = colsum_partials<TA>(dbig, M, 4 * C, part, s);
@@ -479,7 +479,7 @@ int64_t plan_workspace(gpt2_ctx* c, Plan& p, bool assign) {
   c->ln2 = at(L * M * C * A);
   c->ln2_mean = (float*)at(L * M * 4);
   c->ln2_rstd = (float*)at(L * M * 4);
-  c->fcu = at(L * M * 4 * C * A);
+  c->fcgd = at(L * M * 4 * C * A);
   c->fcg = at(L * M * 4 * C * A);
   c->lnf = at(M * C * A);
   c->lnf_mean = (float*)at(M * 4);
@@ -708,7 +708,7 @@ int gpt2_activation(gpt2_ctx* c, const char* name, int layer, void** ptr, int64_
   if (n == "atty") return ret(c->layer_act(c->atty, layer, C), M * C, at);
   if (n == "lse") return ret(c->lse + (int64_t)layer * c->Mmax * c->NH, M * c->NH, 0);
   if (n == "ln2") return ret(c->layer_act(c->ln2, layer, C), M * C, at);
-  if (n == "fcu") return ret(c->layer_act(c->fcu, layer, 4 * C), M * 4 * C, at);
+  if (n == "fcgd") return ret(c->layer_act(c->fcgd, layer, 4 * C), M * 4 * C, at);
   if (n == "fcg") return ret(c->layer_act(c->fcg, layer, 4 * C), M * 4 * C, at);
   return GPT2_ERR_ARG;
 }

@@ -18,8 +18,8 @@ enum GemmEpilogue {
   EPI_F32 = 1,       // C (fp32) = acc
   EPI_F32_ACC = 2,   // C (fp32) += acc
   EPI_RESID = 3,     // C (fp32) = resid + acc + bias[n]
-  EPI_GELU = 4,      // u = acc + bias[n] -> C (act), gelu(u) -> C2 (act)
-  EPI_GELU_BWD = 5,  // C (act) = acc * gelu'(aux[m][n])
+  EPI_GELU = 4,      // u = acc + bias[n]: gelu'(u) -> C (act), gelu(u) -> C2 (act)
+  EPI_GELU_BWD = 5,  // C (act) = acc * aux[m][n]  (aux = the stored gelu'(u))
   EPI_PARTIAL = 6,   // C (fp32) + split * split_stride = acc (split-K partial)
   EPI_LOGITS = 7,    // C (activation type) = acc; the lm_head product (its own kernel symbol)
 };

@@ -180,9 +180,11 @@ int gpt2_tensor_info(const gpt2_config *cfg, int index, const char **name,
 
 /* Device address of a saved activation of the last forward (for tests):
    name in {"resid", "ln1", "ln1_mean", "ln1_rstd", "qkv", "atty", "lse",
-   "ln2", "fcu", "fcg", "lnf", "logits", "row_loss", "emb_sorted_ids",
+   "ln2", "fcgd", "fcg", "lnf", "logits", "row_loss", "emb_sorted_ids",
    "emb_sorted_pos", "dresid"}; layer selects the block (for "resid", the
-   index 0..2L of the residual stream).  dtype: 0 fp32, 1 bf16, 2 int32. */
+   index 0..2L of the residual stream).  "fcgd" is gelu'(u) and "fcg" gelu(u)
+   for the MLP pre-activation u (u itself is not kept).  dtype: 0 fp32,
+   1 bf16, 2 int32. */
 int gpt2_activation(gpt2_ctx *ctx, const char *name, int layer, void **ptr,
                     int64_t *numel, int32_t *dtype);
 

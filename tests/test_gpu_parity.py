@@ -68,7 +68,7 @@ def test_toy_fp32_forward_activations_match_oracle():
         checks = {
             ("resid", 2 * l): lc["x_in"], ("ln1", l): lc["h1"], ("qkv", l): lc["qkv"],
             ("atty", l): lc["y"], ("resid", 2 * l + 1): lc["x_mid"], ("ln2", l): lc["h2"],
-            ("fcu", l): lc["u"], ("fcg", l): lc["g"],
+            ("fcgd", l): ref.gelu_grad(lc["u"]), ("fcg", l): lc["g"],
         }
         for (name, idx), want in checks.items():
             got = st.activation(name, idx).float().cpu().numpy().reshape(want.shape)

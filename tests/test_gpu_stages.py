@@ -69,12 +69,14 @@ def test_bf16_forward_stages_against_torch_fp32(C, NH, T, B):
         ln2 = act("ln2", l, C)
         ref = F.layer_norm(xmid, (C,), W["ln2_w"][l], W["ln2_b"][l], eps=1e-5)
         assert _max_rel(ln2, ref) < 1e-2, ("ln2", l)
-        u = act("fcu", l, 4 * C)
-        ref = ln2 @ Wb["fc_w"][l].T + W["fc_b"][l]
-        assert _max_rel(u, ref) < 1e-2, ("fc gemm", l, _max_rel(u, ref))
+        # the fc GEMM keeps gelu(u) and gelu'(u) of u = LN2 Wfc^T + bfc
+        u = (ln2 @ Wb["fc_w"][l].T + W["fc_b"][l]).requires_grad_(True)
+        gref = F.gelu(u, approximate="tanh")
+        (dref,) = torch.autograd.grad(gref.sum(), u)
         g = act("fcg", l, 4 * C)
-        ref = F.gelu(u, approximate="tanh")
-        assert _max_rel(g, ref) < 1e-2, ("gelu", l, _max_rel(g, ref))
+        assert _max_rel(g, gref.detach()) < 1e-2, ("fc gemm + gelu", l, _max_rel(g, gref.detach()))
+        d = act("fcgd", l, 4 * C)
+        assert _max_rel(d, dref) < 1e-2, ("fc gemm + gelu'", l, _max_rel(d, dref))
         xout = st.activation("resid", 2 * l + 2).reshape(M, C)
         ref = xmid + g @ Wb["fcproj_w"][l].T + W["fcproj_b"][l]
         assert _max_rel(xout, ref) < 1e-3, ("fcproj gemm + residual", l, _max_rel(xout, ref))
