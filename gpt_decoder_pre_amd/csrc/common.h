@@ -41,6 +41,26 @@ DEVI void store4(bf16* p, const float v[4]) {
   *reinterpret_cast<bf16x4*>(p) = t;
 }
 
+// Sixteen bytes as fp32 values: four floats, or eight bf16 (element 2i in the
+// low half of word i).
+template <typename T> DEVI void unpack16(u32x4 v, float* f);
+template <> DEVI void unpack16<float>(u32x4 v, float* f) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    // through a scalar: __builtin_bit_cast of a vector element subscript
+    // yields element 0 with this compiler
+    const uint32_t u = v[i];
+    f[i] = __builtin_bit_cast(float, u);
+  }
+}
+template <> DEVI void unpack16<bf16>(u32x4 v, float* f) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f[2 * i] = __builtin_bit_cast(float, v[i] << 16);
+    f[2 * i + 1] = __builtin_bit_cast(float, v[i] & 0xffff0000u);
+  }
+}
+
 // ---- math --------------------------------------------------------------------
 constexpr float kLog2e = 1.4426950408889634f;   // log2(e)
 constexpr float kLn2 = 0.6931471805599453f;     // ln(2)

@@ -50,10 +50,12 @@ __global__ __launch_bounds__(256) void radix_sort_kernel(const int32_t* __restri
   const int chunk = (M + 255) / 256;
   const int lo = min(M, t * chunk), hi = min(M, lo + chunk);
   for (int pass = 0; pass < passes; ++pass) {
-    const int32_t* kin = (pass & 1) ? ka : kb;
-    const int32_t* vin = (pass & 1) ? va : vb;
-    int32_t* kout = (pass & 1) ? kb : ka;
-    int32_t* vout = (pass & 1) ? vb : va;
+    // the last pass writes (ka, va)
+    const bool out_b = ((passes - 1 - pass) & 1) != 0;
+    const int32_t* kin = out_b ? ka : kb;
+    const int32_t* vin = out_b ? va : vb;
+    int32_t* kout = out_b ? kb : ka;
+    int32_t* vout = out_b ? vb : va;
     const int shift = 4 * pass;
     int cnt[16];
 #pragma unroll
@@ -120,8 +122,55 @@ __global__ __launch_bounds__(256) void radix_sort_kernel(const int32_t* __restri
   }
 }
 
+// The same order from one workgroup sorting in LDS: position m and id
+// idx[m] packed as (id << 16) | m are distinct words, so sorting the words
+// (a bitonic network over a power-of-two count, padded with all-ones words)
+// gives the stable order by id.  For M <= 32768 and ids below 65535.
+constexpr int kBitonicMax = 32768;
+__global__ __launch_bounds__(1024) void bitonic_sort_kernel(const int32_t* __restrict__ idx, int M, int vocab,
+                                                            int N, int32_t* __restrict__ keys,
+                                                            int32_t* __restrict__ vals) {
+  __shared__ uint32_t w[kBitonicMax];
+  const int tid = threadIdx.x;
+  for (int i = tid; i < N; i += blockDim.x) {
+    if (i < M) {
+      int key = idx[i];
+      if (key < 0 || key >= vocab) key = 0;
+      w[i] = ((uint32_t)key << 16) | (uint32_t)i;
+    } else {
+      w[i] = 0xffffffffu;
+    }
+  }
+  __syncthreads();
+  for (int k = 2; k <= N; k <<= 1) {
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      for (int t = tid; t < N / 2; t += blockDim.x) {
+        const int a = ((t & ~(j - 1)) << 1) | (t & (j - 1));  // bit j of a is clear
+        const int b = a | j;
+        const bool ascending = (a & k) == 0;
+        const uint32_t x = w[a], y = w[b];
+        if ((x > y) == ascending) {
+          w[a] = y;
+          w[b] = x;
+        }
+      }
+      __syncthreads();
+    }
+  }
+  for (int i = tid; i < M; i += blockDim.x) {
+    keys[i] = (int32_t)(w[i] >> 16);
+    vals[i] = (int32_t)(w[i] & 0xffffu);
+  }
+}
+
 void embed_sort(const int32_t* idx, int M, int vocab, int id_bits, int32_t* keys_a, int32_t* vals_a,
                 int32_t* keys_b, int32_t* vals_b, hipStream_t s) {
+  if (M <= kBitonicMax && vocab < 65535) {
+    int n = 2;
+    while (n < M) n <<= 1;
+    bitonic_sort_kernel<<<1, 1024, 0, s>>>(idx, M, vocab, n, keys_a, vals_a);
+    return;
+  }
   const int passes = (id_bits + 3) / 4;
   radix_sort_kernel<<<1, 256, 0, s>>>(idx, M, vocab, passes, keys_a, vals_a, keys_b, vals_b);
 }

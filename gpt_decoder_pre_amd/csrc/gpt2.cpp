@@ -448,9 +448,7 @@ int backward_impl(gpt2_ctx* c) {
     Timed tm(c, "embed.bwd", 0, 12.0 * M * C);
     embed_wpe_grad(c->dres, c->G(T_WPE), B, T, C, s);
     embed_sort(c->ids, M, c->Vp, c->id_bits, c->sort_ka, c->sort_va, c->sort_kb, c->sort_vb, s);
-    const bool in_a = ((c->id_bits + 3) / 4) % 2 == 1;
-    embed_scatter(in_a ? c->sort_ka : c->sort_kb, in_a ? c->sort_va : c->sort_vb, c->dres, c->run_sums,
-                  c->G(T_WTE), M, C, s);
+    embed_scatter(c->sort_ka, c->sort_va, c->dres, c->run_sums, c->G(T_WTE), M, C, s);
   }
   c->have_fwd = false;
   return hip_status();
@@ -459,6 +457,8 @@ int backward_impl(gpt2_ctx* c) {
 int check_bt(const gpt2_ctx* c, int B, int T) {
   if (T > c->cfg.block_size) return GPT2_ERR_SEQ_TOO_LONG;
   if (B < 1 || T < 1 || B > c->cfg.max_batch) return GPT2_ERR_BATCH;
+  // bf16 weight gradients contract over the B*T tokens in 16-byte rows
+  if (c->bf16 && ((int64_t)B * T) % 8) return GPT2_ERR_BATCH;
   return GPT2_OK;
 }
 
@@ -697,9 +697,8 @@ int gpt2_activation(gpt2_ctx* c, const char* name, int layer, void** ptr, int64_
   if (n == "logits") return ret(c->logits, M * c->Vp, at);
   if (n == "row_loss") return ret(c->row_loss, M, 0);
   if (n == "dresid") return ret(c->dres, M * C, 0);
-  const bool in_a = ((c->id_bits + 3) / 4) % 2 == 1;
-  if (n == "emb_sorted_ids") return ret(in_a ? c->sort_ka : c->sort_kb, M, 2);
-  if (n == "emb_sorted_pos") return ret(in_a ? c->sort_va : c->sort_vb, M, 2);
+  if (n == "emb_sorted_ids") return ret(c->sort_ka, M, 2);
+  if (n == "emb_sorted_pos") return ret(c->sort_va, M, 2);
   if (!lay_ok) return GPT2_ERR_ARG;
   if (n == "ln1") return ret(c->layer_act(c->ln1, layer, C), M * C, at);
   if (n == "ln1_mean") return ret(c->ln1_mean + (int64_t)layer * c->Mmax, M, 0);

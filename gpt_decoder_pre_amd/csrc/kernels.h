@@ -61,7 +61,9 @@ void splitk_reduce_add(float* out, const float* part, int splits, int64_t stride
 // ids_out[m] receives the id used.
 void embed_fwd(const int32_t* idx, const float* wte, const float* wpe, float* x, int32_t* ids_out, int M, int T,
                int C, int vocab, int* err, hipStream_t s);
-// Stable sort of (idx[m], m) by id: LSD radix, 4-bit digits, one workgroup.
+// Stable sort of (idx[m], m) by id into (keys_a, vals_a): a bitonic sort in
+// LDS for M <= 32768 and ids below 65535, else an LSD radix sort (4-bit
+// digits, one workgroup, keys_b / vals_b as the other buffer).
 void embed_sort(const int32_t* idx, int M, int vocab, int id_bits, int32_t* keys_a, int32_t* vals_a,
                 int32_t* keys_b, int32_t* vals_b, hipStream_t s);
 // dwte[id] += sum over positions with that id of dx[pos] (in position order);

@@ -5,6 +5,8 @@
 // variance, eps = 1e-5.  Column sums (gain / shift / bias gradients) are
 // deterministic: fixed row chunks per block write partial rows, a second
 // kernel adds the partials in chunk order.
+#include <algorithm>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -277,28 +279,41 @@ void colpart_reduce_add(float* out0, float* out1, float* out2, const float* part
   colpart_reduce_kernel<<<grid, 1024, 0, s>>>(out0, out1, out2, part, chunks, N);
 }
 
-// Partial column sums: block (cb, chunk) covers 256 x W columns (W = 16 bytes
-// of elements per thread) x rows_per_chunk rows.
+// Partial column sums: block `chunk` covers rows_per_chunk rows and all N
+// columns; each lane owns W = 16 bytes of consecutive columns (one 16-byte
+// load per row, eight rows in flight) and loops over column groups if the row
+// is wider than the block.
 template <typename TA>
-__global__ __launch_bounds__(256) void colsum_kernel(const TA* __restrict__ x, int M, int N, int rows_per_chunk,
-                                                     float* __restrict__ part) {
+__global__ __launch_bounds__(1024) void colsum_kernel(const TA* __restrict__ x, int M, int N, int rows_per_chunk,
+                                                      float* __restrict__ part) {
   constexpr int W = 16 / sizeof(TA);
-  const int c = (blockIdx.x * 256 + threadIdx.x) * W;
-  if (c >= N) return;
-  const int r0 = blockIdx.y * rows_per_chunk, r1 = min(M, r0 + rows_per_chunk);
-  float s[W];
+  const int r0 = blockIdx.x * rows_per_chunk, r1 = min(M, r0 + rows_per_chunk);
+  for (int c = threadIdx.x * W; c < N; c += blockDim.x * W) {
+    float s[W];
 #pragma unroll
-  for (int e = 0; e < W; ++e) s[e] = 0.f;
-#pragma unroll 4
-  for (int r = r0; r < r1; ++r) {
-    float v[W];
-    load4(x + (int64_t)r * N + c, v);
-    if constexpr (W == 8) load4(x + (int64_t)r * N + c + 4, v + 4);
+    for (int e = 0; e < W; ++e) s[e] = 0.f;
+    int r = r0;
+    for (; r + 8 <= r1; r += 8) {
+      u32x4 v[8];
 #pragma unroll
-    for (int e = 0; e < W; ++e) s[e] += v[e];
+      for (int k = 0; k < 8; ++k) v[k] = *reinterpret_cast<const u32x4*>(x + (int64_t)(r + k) * N + c);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        float f[W];
+        unpack16<TA>(v[k], f);
+#pragma unroll
+        for (int e = 0; e < W; ++e) s[e] += f[e];
+      }
+    }
+    for (; r < r1; ++r) {
+      float f[W];
+      unpack16<TA>(*reinterpret_cast<const u32x4*>(x + (int64_t)r * N + c), f);
+#pragma unroll
+      for (int e = 0; e < W; ++e) s[e] += f[e];
+    }
+#pragma unroll
+    for (int e = 0; e < W; e += 4) store4(part + (int64_t)blockIdx.x * N + c + e, s + e);
   }
-  store4(part + (int64_t)blockIdx.y * N + c, s);
-  if constexpr (W == 8) store4(part + (int64_t)blockIdx.y * N + c + 4, s + 4);
 }
 
 template <typename TA>
@@ -306,8 +321,9 @@ int colsum_partials(const TA* x, int M, int N, float* part, hipStream_t s) {
   constexpr int W = 16 / sizeof(TA);
   const int rpc = 64;
   const int chunks = (M + rpc - 1) / rpc;
-  dim3 grid((N / W + 255) / 256, chunks);
-  colsum_kernel<TA><<<grid, 256, 0, s>>>(x, M, N, rpc, part);
+  const int groups = N / W;
+  const int threads = std::min(1024, (groups + 63) / 64 * 64);
+  colsum_kernel<TA><<<chunks, threads, 0, s>>>(x, M, N, rpc, part);
   return chunks;
 }
 template int colsum_partials<float>(const float*, int, int, float*, hipStream_t);

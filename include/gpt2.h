@@ -53,7 +53,7 @@ extern "C" {
 #define GPT2_OK                0
 #define GPT2_ERR_ARG          -1  /* bad config or argument, NULL pointer      */
 #define GPT2_ERR_SEQ_TOO_LONG -2  /* T > block_size                            */
-#define GPT2_ERR_BATCH        -3  /* B < 1, B > max_batch, k < 1               */
+#define GPT2_ERR_BATCH        -3  /* B < 1, B > max_batch, k < 1, BF16 B*T % 8 */
 #define GPT2_ERR_STATE        -4  /* backward without a matching forward       */
 #define GPT2_ERR_TOKEN        -5  /* an id or target outside [0, vocab_size)   */
 #define GPT2_ERR_HIP          -6  /* a HIP call or kernel launch failed        */
@@ -115,7 +115,9 @@ int gpt2_init(const gpt2_config *cfg, const gpt2_buffers *bufs, void *hip_stream
  * Saves activations in the workspace for gpt2_backward (one forward is kept;
  * a new forward replaces it).
  * Errors: GPT2_ERR_SEQ_TOO_LONG if T > block_size; GPT2_ERR_BATCH if B < 1 or
- *   B > max_batch or T < 1; GPT2_ERR_ARG for NULL pointers.  An id or target
+ *   B > max_batch or T < 1, or in BF16 mode if B*T is not a multiple of 8 (the
+ *   weight-gradient GEMMs contract over tokens in 16-byte rows); GPT2_ERR_ARG
+ *   for NULL pointers.  An id or target
  *   outside [0, vocab_size) sets a sticky device flag (row 0 / class 0 is used
  *   in its place) that gpt2_sync_status reports as GPT2_ERR_TOKEN.
  */

@@ -148,14 +148,17 @@ def test_bf16_full_gpt2_small_one_sequence():
 
 # ---------------------------------------------------------------- bit-exact ----
 
-def test_embedding_gather_and_sort_are_exact():
+# bitonic sort in LDS (power-of-two and ragged token counts) and the radix
+# sort it falls back to above 32768 tokens
+@pytest.mark.parametrize("C,NH,B,T", [(768, 12, 4, 512), (768, 12, 3, 40), (64, 1, 33, 1024)])
+def test_embedding_gather_and_sort_are_exact(C, NH, B, T):
     import torch
-    s = shape("gpt2-124m-L1", 1, 12, 768, 1024, 50257, 50304)
-    say("embedding gather / sort bit-exact")
+    s = shape("emb", 1, NH, C, 1024, 50257, 50304)
+    say(f"embedding gather / sort bit-exact C={C} B={B} T={T}")
     p = init_params(s, 0)
     p["wpe"][:] = 0
-    (x, y), = batches_for(s, 4, 512, 1, kind="zipf", seed=5)
-    st = gpu_step(s, "bf16", 4, p)
+    (x, y), = batches_for(s, B, T, 1, kind="zipf", seed=5)
+    st = gpu_step(s, "bf16", B, p)
     xd, yd = to_dev([(x, y)])
     st.forward_loss(xd[0], yd[0], 1.0)
     st.backward()
@@ -252,6 +255,18 @@ def test_error_codes():
     assert st.sync_status() == 0  # the flag is cleared once reported
     st.forward_loss(ok, bad)
     assert st.sync_status() == GPT2_ERR_TOKEN
+    st.close()
+    # bf16: the token count must be a multiple of 8 (checked before any launch)
+    sb = shape("err-bf16", 1, 1, 64, 64, 65, 72)
+    st = gpu_step(sb, "bf16", 2, init_params(sb, 0))
+    odd = torch.zeros(1, 12, dtype=torch.int32, device="cuda")
+    with pytest.raises(Gpt2Error) as e:
+        st.forward_loss(odd, odd)
+    assert e.value.code == GPT2_ERR_BATCH
+    even = torch.zeros(2, 12, dtype=torch.int32, device="cuda")
+    st.forward_loss(even, even)
+    st.backward()
+    assert st.sync_status() == 0
     st.close()
 
 
