@@ -72,11 +72,13 @@ __global__ __launch_bounds__(256) void xent_kernel(TA* __restrict__ logits, cons
   }
 }
 
-// bf16 rows of up to 1024 x NCH x 8 elements: the row is read once into
+// bf16 rows of up to NT x NCH x 8 elements: the row is read once into
 // registers (16-byte chunks, NCH per thread), the statistics come from the
 // registers, and the gradient is written from them: one read, one write.
-template <int NCH>
-__global__ __launch_bounds__(1024) void xent_bf16_resident_kernel(bf16* __restrict__ logits,
+// The register budget (64 VGPRs) keeps two rows resident per CU, so one row's
+// loads overlap the other's arithmetic and stores.
+template <int NCH, int NT>
+__global__ __launch_bounds__(NT, 8 * NT / 1024) void xent_bf16_resident_kernel(bf16* __restrict__ logits,
                                                                  const int32_t* __restrict__ targets,
                                                                  float* __restrict__ row_loss, int V, int vocab,
                                                                  float grad_scale, int* __restrict__ err) {
@@ -93,13 +95,13 @@ __global__ __launch_bounds__(1024) void xent_bf16_resident_kernel(bf16* __restri
   u32x4 r[NCH];
 #pragma unroll
   for (int i = 0; i < NCH; ++i) {
-    const int c = threadIdx.x + i * 1024;
+    const int c = threadIdx.x + i * NT;
     r[i] = ld16_or_zero(z + 8 * c, c < nchunk);
   }
   float m = -INFINITY;
 #pragma unroll
   for (int i = 0; i < NCH; ++i) {
-    const int c = threadIdx.x + i * 1024;
+    const int c = threadIdx.x + i * NT;
     if (c < nchunk) {
       const bf16x8 v = __builtin_bit_cast(bf16x8, r[i]);
 #pragma unroll
@@ -110,7 +112,7 @@ __global__ __launch_bounds__(1024) void xent_bf16_resident_kernel(bf16* __restri
   float s = 0.f;
 #pragma unroll
   for (int i = 0; i < NCH; ++i) {
-    const int c = threadIdx.x + i * 1024;
+    const int c = threadIdx.x + i * NT;
     if (c < nchunk) {
       const bf16x8 v = __builtin_bit_cast(bf16x8, r[i]);
 #pragma unroll
@@ -119,11 +121,11 @@ __global__ __launch_bounds__(1024) void xent_bf16_resident_kernel(bf16* __restri
   }
   const float S = block_sum(s, red2);
   const float lse = M + logf(S);
-  if (threadIdx.x == (y / 8) % 1024) {
+  if (threadIdx.x == (y / 8) % NT) {
     float zy = 0.f;
 #pragma unroll
     for (int i = 0; i < NCH; ++i) {
-      if (i == (y / 8) / 1024) {
+      if (i == (y / 8) / NT) {
         const bf16x8 v = __builtin_bit_cast(bf16x8, r[i]);
 #pragma unroll
         for (int e = 0; e < 8; ++e)
@@ -135,7 +137,7 @@ __global__ __launch_bounds__(1024) void xent_bf16_resident_kernel(bf16* __restri
   const float l2 = lse * kLog2e;
 #pragma unroll
   for (int i = 0; i < NCH; ++i) {
-    const int c = threadIdx.x + i * 1024;
+    const int c = threadIdx.x + i * NT;
     if (c < nchunk) {
       const bf16x8 v = __builtin_bit_cast(bf16x8, r[i]);
       bf16x8 o;
@@ -156,13 +158,13 @@ void xent_fwd_bwd(TA* logits, const int32_t* targets, float* row_loss, int M, in
     if (V % 8 == 0 && V <= 1024 * 8 * 8) {
       const int nch = (V / 8 + 1023) / 1024;
       if (nch <= 2) {
-        xent_bf16_resident_kernel<2><<<M, 1024, 0, s>>>(logits, targets, row_loss, V, vocab, grad_scale, err);
+        xent_bf16_resident_kernel<2, 1024><<<M, 1024, 0, s>>>(logits, targets, row_loss, V, vocab, grad_scale, err);
       } else if (nch <= 4) {
-        xent_bf16_resident_kernel<4><<<M, 1024, 0, s>>>(logits, targets, row_loss, V, vocab, grad_scale, err);
+        xent_bf16_resident_kernel<4, 1024><<<M, 1024, 0, s>>>(logits, targets, row_loss, V, vocab, grad_scale, err);
       } else if (nch <= 7) {
-        xent_bf16_resident_kernel<7><<<M, 1024, 0, s>>>(logits, targets, row_loss, V, vocab, grad_scale, err);
+        xent_bf16_resident_kernel<7, 1024><<<M, 1024, 0, s>>>(logits, targets, row_loss, V, vocab, grad_scale, err);
       } else {
-        xent_bf16_resident_kernel<8><<<M, 1024, 0, s>>>(logits, targets, row_loss, V, vocab, grad_scale, err);
+        xent_bf16_resident_kernel<8, 1024><<<M, 1024, 0, s>>>(logits, targets, row_loss, V, vocab, grad_scale, err);
       }
       return;
     }
