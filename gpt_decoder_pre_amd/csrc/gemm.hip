@@ -619,8 +619,8 @@ struct SaddrLoader {
   }
 };
 
-template <bool A_K, bool B_K, int BM, int BN, int EPI>
-__global__ __launch_bounds__(256, 1) void gemm_w4_kernel(GemmArgs p) {
+template <bool A_K, bool B_K, int BM, int BN, int EPI, int OCC = 1>
+__global__ __launch_bounds__(256, OCC) void gemm_w4_kernel(GemmArgs p) {
   constexpr int BK = 64, NW = 4;
   constexpr int WTM = BM / 2, WTN = BN / 2;
   constexpr int FM = WTM / 32, FN = WTN / 32;
@@ -882,24 +882,25 @@ void launch_bf16_cfg(int cfg, const GemmArgs& a, hipStream_t s) {
     default: break;
   }
 #undef GPT2_GEMM_LDS
-#define GPT2_GEMM_W4(ID, BM, BN)                                                                \
+#define GPT2_GEMM_W4(ID, BM, BN, OCC)                                                           \
   case ID: {                                                                                   \
     const int tiles = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);                           \
-    gemm_w4_kernel<A_K, B_K, BM, BN, EPI><<<dim3(tiles, a.splits), 256, 0, s>>>(a);            \
+    gemm_w4_kernel<A_K, B_K, BM, BN, EPI, OCC><<<dim3(tiles, a.splits), 256, 0, s>>>(a);       \
     break;                                                                                     \
   }
   switch (cfg) {
-    GPT2_GEMM_W4(20, 256, 256)
-    GPT2_GEMM_W4(21, 256, 192)
+    GPT2_GEMM_W4(20, 256, 256, 1)
+    GPT2_GEMM_W4(21, 256, 192, 1)
+    GPT2_GEMM_W4(22, 128, 192, 2)  // two workgroups per CU
     default: break;
   }
 #undef GPT2_GEMM_W4
 }
-constexpr int kNumCfg = 22;
+constexpr int kNumCfg = 23;
 constexpr int kFirstLds = 6;
-const int kCfgBM[kNumCfg] = {128, 256, 256, 256, 256, 128, 256, 256, 256, 256, 128, 256, 128, 256, 256, 256, 256, 128, 256, 128, 256, 256};
-const int kCfgBN[kNumCfg] = {128, 128, 256, 192, 256, 256, 256, 256, 256, 128, 256, 192, 128, 256, 256, 192, 128, 256, 256, 192, 256, 192};
-const int kCfgBK[kNumCfg] = {64, 64, 64, 64, 64, 64, 32, 32, 64, 32, 32, 32, 32, 64, 32, 64, 64, 64, 64, 64, 64, 64};
+const int kCfgBM[kNumCfg] = {128, 256, 256, 256, 256, 128, 256, 256, 256, 256, 128, 256, 128, 256, 256, 256, 256, 128, 256, 128, 256, 256, 128};
+const int kCfgBN[kNumCfg] = {128, 128, 256, 192, 256, 256, 256, 256, 256, 128, 256, 192, 128, 256, 256, 192, 128, 256, 256, 192, 256, 192, 192};
+const int kCfgBK[kNumCfg] = {64, 64, 64, 64, 64, 64, 32, 32, 64, 32, 32, 32, 32, 64, 32, 64, 64, 64, 64, 64, 64, 64, 64};
 
 template <bool A_K, bool B_K, int EPI>
 void launch_f32(const GemmArgs& a, hipStream_t s) {
@@ -918,11 +919,14 @@ void launch(bool bf16_mode, int cfg, const GemmArgs& a, hipStream_t s) {
 // fill of the last wave of blocks over the 256 CUs and by the padding of
 // partial tiles.
 double model_time(int c, const GemmArgs& a, bool transposed_a) {
-  // sustained TFLOP/s at full waves; 13 spills registers and is never chosen
+  // sustained TFLOP/s at full waves; 13 spills registers and is never chosen;
+  // 22 is never chosen for weight gradients (measured slower in the step
+  // than in isolation: its split-K partials compete with the other
+  // workgroup on the CU)
   static const double tf_k[kNumCfg] = {560, 480, 650, 720, 750, 500, 750, 800, 880, 650, 650, 930, 820,
-                                        1, 820, 1020, 760, 760, 900, 1, 1090, 1060};  // A k-contiguous
+                                        1, 820, 1020, 760, 760, 900, 1, 1090, 1060, 1040};  // A k-contiguous
   static const double tf_t[kNumCfg] = {450, 460, 660, 560, 640, 380, 860, 880, 950, 740, 740, 900, 820,
-                                        1, 950, 930, 850, 900, 930, 1, 1080, 1000};   // A transposed
+                                        1, 950, 930, 850, 900, 930, 1, 1080, 1000, 1};   // A transposed
   const int64_t tm = (a.M + kCfgBM[c] - 1) / kCfgBM[c], tn = (a.N + kCfgBN[c] - 1) / kCfgBN[c];
   const double waves = (double)(tm * tn * a.splits) / 256.0;
   const double fill = waves / std::ceil(waves);
@@ -978,14 +982,17 @@ bool gemm_cfg(int cfg, GemmLayout layout, GemmEpilogue epi, bool bf16_mode, cons
     if (layout == LAYOUT_TN && a.M % 8) return false;
     if (cfg < 0) {
       // Epilogues that do per-element work on bf16 activations (bias, GELU,
-      // GELU') cost as much as a short-K main loop; the 128 x 192 tile at two
-      // workgroups per CU (config 19) lets one workgroup's epilogue run beside
-      // the other's MFMA loop (measured 5-40% faster than the one-wave-per-SIMD
-      // tiles for these GEMMs on MI355X).  The residual add is cheaper per
-      // byte and takes the 256 x 192 one-wave-per-SIMD tile (config 21, 7%
-      // faster than config 19).
+      // GELU') and short-K products (K <= 1024: a dozen k-tiles per output
+      // tile) are bound by the time outside the k-loop; the 128 x 192 tile at
+      // two workgroups per CU (config 22) lets one workgroup's prologue and
+      // epilogue run beside the other's k-loop (measured on MI355X: 3-10%
+      // faster than config 19 and 5-18% faster than the one-workgroup tiles
+      // for these GEMMs).  The lm_head product (K = C but 50k columns) and
+      // the long-K residual GEMM keep the one-workgroup tiles.
       const bool heavy_epi = (epi == EPI_ACT && a.bias) || epi == EPI_GELU || epi == EPI_GELU_BWD;
-      if (heavy_epi && gemm_config_usable(19, layout, a)) cfg = 19;
+      const bool short_k = a.K <= 1024 && epi != EPI_LOGITS;
+      if ((heavy_epi || short_k) && gemm_config_usable(22, layout, a)) cfg = 22;
+      else if (heavy_epi && gemm_config_usable(19, layout, a)) cfg = 19;
       else if (epi == EPI_RESID && gemm_config_usable(21, layout, a)) cfg = 21;
       else cfg = choose_cfg(a, layout);
     }

@@ -49,7 +49,7 @@ int gemm_pick_config(const GemmArgs& a, GemmLayout layout);
 double gemm_model_time(int cfg, const GemmArgs& a, bool transposed_a);
 // Whether a configuration can run these shapes.
 bool gemm_config_usable(int cfg, GemmLayout layout, const GemmArgs& a);
-constexpr int kGemmConfigs = 22;
+constexpr int kGemmConfigs = 23;
 // Block tile of a configuration.
 void gemm_config_tile(int cfg, int* bm, int* bn);
 // out[i] += sum_{s < splits} part[s * stride + i], i < count (fixed order).
