@@ -365,7 +365,18 @@ int backward_impl(gpt2_ctx* c) {
   hipStream_t s = c->stream;
   const int B = c->B, T = c->T, M = B * T, C = c->C, L = c->L, Vp = c->Vp;
   const double a = (double)c->act;
+  // Column partials (LayerNorm gain / shift and bias gradients): every
+  // producer writes its own region; one batched launch at the end of the
+  // pass reduces them all (each output has exactly one job).
   float* part = c->colpart;
+  std::vector<ColJob> jobs;
+  jobs.reserve(4 * L + 1);
+  // arrays: partial arrays the producer wrote (3 for LayerNorm, 1 for a sum)
+  auto defer = [&](float* o0, float* o1, float* o2, int chunks, int n, int arrays) {
+    const int nout = o2 ? 3 : (o1 ? 2 : 1);
+    jobs.push_back(ColJob{{o0, o1, o2}, part, chunks, n, nout});
+    part += (int64_t)arrays * chunks * n;
+  };
   // lm_head (tied): dlnf = dz wte; dwte += dz^T lnf
   // dh: gradient at a LayerNorm output, in the activation type (bf16 in bf16
   // mode, like every other matmul output of the mixed-precision step)
@@ -380,7 +391,7 @@ int backward_impl(gpt2_ctx* c) {
     ch = layernorm_bwd<TA>(dh, c->resid(2 * L), c->lnf_mean, c->lnf_rstd, c->P(T_LNFW), c->dres, false,
                            (TA*)c->dres_act, part, M, C, s);
   }
-  colpart_reduce_add(c->G(T_LNFW), c->G(T_LNFB), c->G(T_FCPB, L - 1), part, ch, C, s);
+  defer(c->G(T_LNFW), c->G(T_LNFB), c->G(T_FCPB, L - 1), ch, C, 3);
 
   for (int l = L - 1; l >= 0; --l) {
     TA* ln1 = (TA*)c->layer_act(c->ln1, l, C);
@@ -403,7 +414,7 @@ int backward_impl(gpt2_ctx* c) {
     if (!gemm_site(c, "gemm.bwd.fcproj.dx", LAYOUT_NN, EPI_GELU_BWD, g, a * ((double)M * C + 4.0 * C * C + 8.0 * M * C)))
       return GPT2_ERR_ARG;
     ch = colsum_partials<TA>(dbig, M, 4 * C, part, s);
-    colpart_reduce_add(c->G(T_FCB, l), nullptr, nullptr, part, ch, 4 * C, s);
+    defer(c->G(T_FCB, l), nullptr, nullptr, ch, 4 * C, 1);
     // MLP input projection: u = LN2(x_mid) Wfc^T + bfc
     if (!weight_grad(c, "gemm.bwd.fc.dw", c->G(T_FCW, l), dbig, 4 * C, ln2, C, 4 * C, C, M)) return GPT2_ERR_ARG;
     g = gargs(dbig, 4 * C, c->W(T_FCW, l), C, M, C, 4 * C, dh, C);
@@ -415,7 +426,7 @@ int backward_impl(gpt2_ctx* c) {
                              c->ln2_rstd + (int64_t)l * c->Mmax, c->P(T_LN2W, l), c->dres, true, dres_act, part, M,
                              C, s);
     }
-    colpart_reduce_add(c->G(T_LN2W, l), c->G(T_LN2B, l), c->G(T_PROJB, l), part, ch, C, s);
+    defer(c->G(T_LN2W, l), c->G(T_LN2B, l), c->G(T_PROJB, l), ch, C, 3);
     // attention output projection: x_mid = x_in + y Wp^T + bp
     if (!weight_grad(c, "gemm.bwd.proj.dw", c->G(T_PROJW, l), dres_act, C, atty, C, C, C, M)) return GPT2_ERR_ARG;
     g = gargs(dres_act, C, c->W(T_PROJW, l), C, M, C, C, dy, C);
@@ -429,7 +440,7 @@ int backward_impl(gpt2_ctx* c) {
                         c->NH, C, s);
     }
     ch = colsum_partials<TA>(dqkv, M, 3 * C, part, s);
-    colpart_reduce_add(c->G(T_QKVB, l), nullptr, nullptr, part, ch, 3 * C, s);
+    defer(c->G(T_QKVB, l), nullptr, nullptr, ch, 3 * C, 1);
     // QKV projection: qkv = LN1(x_in) Wqkv^T + bqkv
     if (!weight_grad(c, "gemm.bwd.qkv.dw", c->G(T_QKVW, l), dqkv, 3 * C, ln1, C, 3 * C, C, M)) return GPT2_ERR_ARG;
     g = gargs(dqkv, 3 * C, c->W(T_QKVW, l), C, M, C, 3 * C, dh, C);
@@ -441,8 +452,11 @@ int backward_impl(gpt2_ctx* c) {
                              c->ln1_rstd + (int64_t)l * c->Mmax, c->P(T_LN1W, l), c->dres, true, dres_act, part, M,
                              C, s);
     }
-    colpart_reduce_add(c->G(T_LN1W, l), c->G(T_LN1B, l), l > 0 ? c->G(T_FCPB, l - 1) : nullptr, part, ch, C, s);
+    // the shift's third output is the previous block's MLP output bias
+    if (l > 0) defer(c->G(T_LN1W, l), c->G(T_LN1B, l), c->G(T_FCPB, l - 1), ch, C, 3);
+    else defer(c->G(T_LN1W, l), c->G(T_LN1B, l), nullptr, ch, C, 3);
   }
+  colpart_reduce_batch(jobs.data(), (int)jobs.size(), s);
   // embedding: x0 = wte[idx] + wpe[t]
   {
     Timed tm(c, "embed.bwd", 0, 12.0 * M * C);
@@ -496,7 +510,10 @@ int64_t plan_workspace(gpt2_ctx* c, Plan& p, bool assign) {
   c->attnD = (float*)at(M * NH * 4);
   c->splitk_elems = std::max<int64_t>(16 * 4 * C * C, 2 * Vp * C);
   c->splitk = (float*)at(c->splitk_elems * 4);
-  const int64_t col_elems = std::max<int64_t>(3 * ((M + 31) / 32) * C, ((M + 63) / 64) * 4 * C);
+  // one region per column-partial producer of a backward pass: 2L + 1
+  // LayerNorm backwards (3 x M/32 rows of C) and the qkv and fc bias sums
+  // (M/64 rows of 3C and 4C)
+  const int64_t col_elems = (2 * L + 1) * 3 * ((M + 31) / 32) * C + L * ((M + 63) / 64) * 7 * C;
   c->colpart = (float*)at(col_elems * 4);
   c->sort_ka = (int32_t*)at(M * 4);
   c->sort_va = (int32_t*)at(M * 4);

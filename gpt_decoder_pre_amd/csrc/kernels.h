@@ -83,10 +83,22 @@ void layernorm_fwd(const float* x, const float* w, const float* b, TA* y, float*
 template <typename TA>
 int layernorm_bwd(const TA* dy, const float* x, const float* mean, const float* rstd, const float* w,
                   float* dres, bool dres_in, TA* dres_act, float* part, int M, int C, hipStream_t s);
-// out_k[n] += sum_c part[(k * chunks + c) * N + n], c < chunks, n < N, for each non-null
-// out_k (k = 0, 1, 2; out1 / out2 may be null), summed in a fixed order.
-void colpart_reduce_add(float* out0, float* out1, float* out2, const float* part, int chunks, int N,
-                        hipStream_t s);
+// A column-partial reduction deferred to one batched launch: out[k][n] +=
+// sum over the chunks of part[k][chunk][n] for k < nout (fixed chunk order).
+struct ColJob {
+  float* out[3];
+  const float* part;
+  int chunks, N, nout;
+};
+constexpr int kColJobsMax = 64;
+struct ColJobs {
+  ColJob job[kColJobsMax];
+  int first[kColJobsMax];  // first block of each job
+  int n;
+};
+static_assert(sizeof(ColJobs) <= 4096, "kernel argument size");
+// Launches the jobs (kColJobsMax per launch); each output is written by one job.
+void colpart_reduce_batch(const ColJob* jobs, int n, hipStream_t s);
 // Column sums of an activation matrix (M x N, row-major) into partials [chunks][N];
 // returns the number of chunks.
 template <typename TA>

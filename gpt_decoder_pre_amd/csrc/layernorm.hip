@@ -14,76 +14,102 @@ namespace gpt2k {
 
 constexpr float kLnEps = 1e-5f;
 
-// NV = float4 chunks per lane (C <= 256 NV); the row lives in registers.
-template <typename TA, int NV>
+// NV = float4 chunks per lane (C <= 256 NV); the rows live in registers.
+// Each wavefront normalises R rows together, so their loads are in flight at
+// once and their shuffle reductions interleave.
+template <typename TA, int NV, int R>
 __global__ __launch_bounds__(256) void ln_fwd_kernel(const float* __restrict__ x, const float* __restrict__ w,
                                                      const float* __restrict__ b, TA* __restrict__ y,
                                                      float* __restrict__ mean, float* __restrict__ rstd, int M,
                                                      int C) {
   const int lane = threadIdx.x & 63;
-  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (row >= M) return;
+  const int row0 = (blockIdx.x * 4 + (threadIdx.x >> 6)) * R;
   const int C4 = C >> 2;
-  const float* xr = x + (int64_t)row * C;
-  float v[NV][4];
-  float s = 0.f;
+  float v[R][NV][4];
+  float mu[R], rs[R];
 #pragma unroll
-  for (int i = 0; i < NV; ++i) {
-    const int c4 = lane + i * 64;
-    if (c4 < C4) {
-      load4(xr + 4 * c4, v[i]);
-      s += (v[i][0] + v[i][1]) + (v[i][2] + v[i][3]);
-    }
-  }
-  const float mu = wave_sum(s) / (float)C;
-  float q = 0.f;
+  for (int r = 0; r < R; ++r) {
+    const int row = row0 + r;
+    const float* xr = x + (int64_t)min(row, M - 1) * C;
+    float s = 0.f;
 #pragma unroll
-  for (int i = 0; i < NV; ++i) {
-    const int c4 = lane + i * 64;
-    if (c4 < C4) {
+    for (int i = 0; i < NV; ++i) {
+      const int c4 = lane + i * 64;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float d = v[i][e] - mu;
-        q += d * d;
+      for (int e = 0; e < 4; ++e) v[r][i][e] = 0.f;
+      if (c4 < C4) {
+        load4(xr + 4 * c4, v[r][i]);
+        s += (v[r][i][0] + v[r][i][1]) + (v[r][i][2] + v[r][i][3]);
       }
     }
+    mu[r] = s;
   }
-  const float var = wave_sum(q) / (float)C;
-  const float rs = 1.0f / sqrtf(var + kLnEps);
-  TA* yr = y + (int64_t)row * C;
+#pragma unroll
+  for (int r = 0; r < R; ++r) mu[r] = wave_sum(mu[r]) / (float)C;
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    float q = 0.f;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int c4 = lane + i * 64;
+      if (c4 < C4) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float d = v[r][i][e] - mu[r];
+          q += d * d;
+        }
+      }
+    }
+    rs[r] = q;
+  }
+#pragma unroll
+  for (int r = 0; r < R; ++r) rs[r] = 1.0f / sqrtf(wave_sum(rs[r]) / (float)C + kLnEps);
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
     const int c4 = lane + i * 64;
     if (c4 < C4) {
-      float ww[4], bb[4], o[4];
+      float ww[4], bb[4];
       load4(w + 4 * c4, ww);
       load4(b + 4 * c4, bb);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) o[e] = (v[i][e] - mu) * rs * ww[e] + bb[e];
-      store4(yr + 4 * c4, o);
+      for (int r = 0; r < R; ++r) {
+        const int row = row0 + r;
+        if (row < M) {
+          float o[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) o[e] = (v[r][i][e] - mu[r]) * rs[r] * ww[e] + bb[e];
+          store4(y + (int64_t)row * C + 4 * c4, o);
+        }
+      }
     }
   }
   if (lane == 0) {
-    mean[row] = mu;
-    rstd[row] = rs;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      if (row0 + r < M) {
+        mean[row0 + r] = mu[r];
+        rstd[row0 + r] = rs[r];
+      }
+    }
   }
 }
 
 template <typename TA>
 void layernorm_fwd(const float* x, const float* w, const float* b, TA* y, float* mean, float* rstd, int M,
                    int C, hipStream_t s) {
-#define GPT2_LN_ARGS (M + 3) / 4, 256, 0, s>>>(x, w, b, y, mean, rstd, M, C
+  // two rows per wavefront up to C = 1024, one beyond (register budget)
+#define GPT2_LN_FWD(NV, R) ln_fwd_kernel<TA, NV, R><<<(M + 4 * R - 1) / (4 * R), 256, 0, s>>>(x, w, b, y, mean, rstd, M, C)
   switch ((C / 4 + 63) / 64) {
-    case 1: ln_fwd_kernel<TA, 1><<<GPT2_LN_ARGS); break;
-    case 2: ln_fwd_kernel<TA, 2><<<GPT2_LN_ARGS); break;
-    case 3: ln_fwd_kernel<TA, 3><<<GPT2_LN_ARGS); break;
-    case 4: ln_fwd_kernel<TA, 4><<<GPT2_LN_ARGS); break;
-    case 5: ln_fwd_kernel<TA, 5><<<GPT2_LN_ARGS); break;
-    case 6: ln_fwd_kernel<TA, 6><<<GPT2_LN_ARGS); break;
-    case 7: ln_fwd_kernel<TA, 7><<<GPT2_LN_ARGS); break;
-    default: ln_fwd_kernel<TA, 8><<<GPT2_LN_ARGS); break;
+    case 1: GPT2_LN_FWD(1, 2); break;
+    case 2: GPT2_LN_FWD(2, 2); break;
+    case 3: GPT2_LN_FWD(3, 2); break;
+    case 4: GPT2_LN_FWD(4, 2); break;
+    case 5: GPT2_LN_FWD(5, 1); break;
+    case 6: GPT2_LN_FWD(6, 1); break;
+    case 7: GPT2_LN_FWD(7, 1); break;
+    default: GPT2_LN_FWD(8, 1); break;
   }
-#undef GPT2_LN_ARGS
+#undef GPT2_LN_FWD
 }
 template void layernorm_fwd<float>(const float*, const float*, const float*, float*, float*, float*, int, int,
                                    hipStream_t);
@@ -246,25 +272,29 @@ template int layernorm_bwd<float>(const float*, const float*, const float*, cons
 template int layernorm_bwd<bf16>(const bf16*, const float*, const float*, const float*, const float*, float*,
                                  bool, bf16*, float*, int, int, hipStream_t);
 
-// out_k[n] += sum_c part[(k * chunks + c) * N + n] for the arrays k < nout.
-// A block owns 64 columns of one array; its 16 thread groups sum interleaved
-// chunks, then the group sums are added in group order (fixed order).
-__global__ __launch_bounds__(1024) void colpart_reduce_kernel(float* out0, float* out1, float* out2,
-                                                              const float* __restrict__ part, int chunks, int N) {
+// Many column-partial reductions in one launch: block b belongs to the job j
+// with jobs.first[j] <= b < jobs.first[j + 1] and reduces that job's 64
+// columns the single-job kernel would (same fixed order).
+__global__ __launch_bounds__(1024) void colpart_reduce_batch_kernel(ColJobs jobs) {
   __shared__ float red[16][64];
-  const int k = blockIdx.y;
-  float* out = k == 0 ? out0 : (k == 1 ? out1 : out2);
+  int j = 0;
+  while (j + 1 < jobs.n && (int)blockIdx.x >= jobs.first[j + 1]) ++j;
+  const ColJob& job = jobs.job[j];
+  const int local = blockIdx.x - jobs.first[j];
+  const int cblocks = (job.N + 63) / 64;
+  const int k = local / cblocks;
+  float* out = job.out[k];
   const int col = threadIdx.x & 63, grp = threadIdx.x >> 6;
-  const int n = blockIdx.x * 64 + col;
-  const float* p = part + (int64_t)k * chunks * N;
-  float s = 0.f;
-  if (n < N) {
+  const int n = (local % cblocks) * 64 + col;
+  const float* p = job.part + (int64_t)k * job.chunks * job.N;
+  float sum = 0.f;
+  if (n < job.N) {
 #pragma unroll 8
-    for (int c = grp; c < chunks; c += 16) s += p[(int64_t)c * N + n];
+    for (int c = grp; c < job.chunks; c += 16) sum += p[(int64_t)c * job.N + n];
   }
-  red[grp][col] = s;
+  red[grp][col] = sum;
   __syncthreads();
-  if (grp == 0 && n < N) {
+  if (grp == 0 && n < job.N) {
     float t = 0.f;
 #pragma unroll
     for (int g = 0; g < 16; ++g) t += red[g][col];
@@ -272,11 +302,18 @@ __global__ __launch_bounds__(1024) void colpart_reduce_kernel(float* out0, float
   }
 }
 
-void colpart_reduce_add(float* out0, float* out1, float* out2, const float* part, int chunks, int N,
-                        hipStream_t s) {
-  const int nout = out2 ? 3 : (out1 ? 2 : 1);
-  dim3 grid((N + 63) / 64, nout);
-  colpart_reduce_kernel<<<grid, 1024, 0, s>>>(out0, out1, out2, part, chunks, N);
+void colpart_reduce_batch(const ColJob* jobs, int n, hipStream_t s) {
+  for (int j0 = 0; j0 < n; j0 += kColJobsMax) {
+    ColJobs b;
+    b.n = std::min(kColJobsMax, n - j0);
+    int blocks = 0;
+    for (int j = 0; j < b.n; ++j) {
+      b.job[j] = jobs[j0 + j];
+      b.first[j] = blocks;
+      blocks += (b.job[j].N + 63) / 64 * b.job[j].nout;
+    }
+    colpart_reduce_batch_kernel<<<blocks, 1024, 0, s>>>(b);
+  }
 }
 
 // Partial column sums: block `chunk` covers rows_per_chunk rows and all N
