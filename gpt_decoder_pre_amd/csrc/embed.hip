@@ -122,53 +122,98 @@ __global__ __launch_bounds__(256) void radix_sort_kernel(const int32_t* __restri
   }
 }
 
-// The same order from one workgroup sorting in LDS: position m and id
-// idx[m] packed as (id << 16) | m are distinct words, so sorting the words
-// (a bitonic network over a power-of-two count, padded with all-ones words)
-// gives the stable order by id.  For M <= 32768 and ids below 65535.
+// The same order from one workgroup: position m and id idx[m] packed as
+// (id << 16) | m are distinct words, so sorting the words (a bitonic network
+// over 1024 E words, padded with all-ones words) gives the stable order by
+// id.  Thread t holds the E consecutive words t E .. t E + E - 1: stages whose
+// partners are less than E apart run in registers, those within a wavefront
+// exchange by lane shuffles, and only the stages across wavefronts go through
+// LDS with barriers.  For M <= 32768 and ids below 65535.
 constexpr int kBitonicMax = 32768;
+template <int E>
 __global__ __launch_bounds__(1024) void bitonic_sort_kernel(const int32_t* __restrict__ idx, int M, int vocab,
-                                                            int N, int32_t* __restrict__ keys,
-                                                            int32_t* __restrict__ vals) {
-  __shared__ uint32_t w[kBitonicMax];
-  const int tid = threadIdx.x;
-  for (int i = tid; i < N; i += blockDim.x) {
+                                                            int32_t* __restrict__ keys, int32_t* __restrict__ vals) {
+  constexpr int N = 1024 * E;
+  __shared__ uint32_t w[N];
+  const int t = threadIdx.x;
+  uint32_t x[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const int i = t * E + e;
     if (i < M) {
       int key = idx[i];
       if (key < 0 || key >= vocab) key = 0;
-      w[i] = ((uint32_t)key << 16) | (uint32_t)i;
+      x[e] = ((uint32_t)key << 16) | (uint32_t)i;
     } else {
-      w[i] = 0xffffffffu;
+      x[e] = 0xffffffffu;
     }
   }
-  __syncthreads();
   for (int k = 2; k <= N; k <<= 1) {
-    for (int j = k >> 1; j > 0; j >>= 1) {
-      for (int t = tid; t < N / 2; t += blockDim.x) {
-        const int a = ((t & ~(j - 1)) << 1) | (t & (j - 1));  // bit j of a is clear
-        const int b = a | j;
-        const bool ascending = (a & k) == 0;
-        const uint32_t x = w[a], y = w[b];
-        if ((x > y) == ascending) {
-          w[a] = y;
-          w[b] = x;
+    // partners j >= E apart: in another thread
+    for (int j = k >> 1; j >= E; j >>= 1) {
+      const int m = j / E;  // partner thread = t ^ m
+      const bool low = (t & m) == 0;
+      if (m < 64) {
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          const uint32_t y = (uint32_t)__shfl_xor((int)x[e], m, 64);
+          const bool asc = ((t * E + e) & k) == 0;
+          x[e] = (asc == low) ? min(x[e], y) : max(x[e], y);
+        }
+      } else {
+        __syncthreads();  // the previous exchange's reads are done
+#pragma unroll
+        for (int e = 0; e < E; ++e) w[t * E + e] = x[e];
+        __syncthreads();
+        const int p = t ^ m;
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          const uint32_t y = w[p * E + e];
+          const bool asc = ((t * E + e) & k) == 0;
+          x[e] = (asc == low) ? min(x[e], y) : max(x[e], y);
         }
       }
-      __syncthreads();
+    }
+    // partners j < E apart: in this thread's registers
+#pragma unroll
+    for (int j = E / 2; j > 0; j >>= 1) {
+      if (j < k) {
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          if ((e & j) == 0) {
+            const bool asc = ((t * E + e) & k) == 0;
+            const uint32_t a = x[e], b = x[e | j];
+            if ((a > b) == asc) {
+              x[e] = b;
+              x[e | j] = a;
+            }
+          }
+        }
+      }
     }
   }
-  for (int i = tid; i < M; i += blockDim.x) {
-    keys[i] = (int32_t)(w[i] >> 16);
-    vals[i] = (int32_t)(w[i] & 0xffffu);
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const int i = t * E + e;
+    if (i < M) {
+      keys[i] = (int32_t)(x[e] >> 16);
+      vals[i] = (int32_t)(x[e] & 0xffffu);
+    }
   }
 }
 
 void embed_sort(const int32_t* idx, int M, int vocab, int id_bits, int32_t* keys_a, int32_t* vals_a,
                 int32_t* keys_b, int32_t* vals_b, hipStream_t s) {
   if (M <= kBitonicMax && vocab < 65535) {
-    int n = 2;
-    while (n < M) n <<= 1;
-    bitonic_sort_kernel<<<1, 1024, 0, s>>>(idx, M, vocab, n, keys_a, vals_a);
+    const int e = (M + 1023) / 1024;  // words per thread, rounded up to a power of two
+#define GPT2_BITONIC(E) bitonic_sort_kernel<E><<<1, 1024, 0, s>>>(idx, M, vocab, keys_a, vals_a)
+    if (e <= 1) GPT2_BITONIC(1);
+    else if (e <= 2) GPT2_BITONIC(2);
+    else if (e <= 4) GPT2_BITONIC(4);
+    else if (e <= 8) GPT2_BITONIC(8);
+    else if (e <= 16) GPT2_BITONIC(16);
+    else GPT2_BITONIC(32);
+#undef GPT2_BITONIC
     return;
   }
   const int passes = (id_bits + 3) / 4;

@@ -148,9 +148,10 @@ def test_bf16_full_gpt2_small_one_sequence():
 
 # ---------------------------------------------------------------- bit-exact ----
 
-# bitonic sort in LDS (power-of-two and ragged token counts) and the radix
-# sort it falls back to above 32768 tokens
-@pytest.mark.parametrize("C,NH,B,T", [(768, 12, 4, 512), (768, 12, 3, 40), (64, 1, 33, 1024)])
+# bitonic sort (1 to 32 words per thread: 120, 2048, 4096, 16384 and 24576
+# tokens) and the radix sort it falls back to above 32768 tokens
+@pytest.mark.parametrize("C,NH,B,T", [(768, 12, 4, 512), (768, 12, 3, 40), (64, 1, 4, 1024), (64, 1, 16, 1024),
+                                      (64, 1, 24, 1024), (64, 1, 33, 1024)])
 def test_embedding_gather_and_sort_are_exact(C, NH, B, T):
     import torch
     s = shape("emb", 1, NH, C, 1024, 50257, 50304)
