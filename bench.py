@@ -187,11 +187,13 @@ def main():
                      "norm", "adamw", "gemm.fwd.qkv", "gemm.fwd.proj", "gemm.fwd.fc", "gemm.fwd.fcproj",
                      "gemm.fwd.lmhead", "gemm.bwd.lmhead.dx", "gemm.bwd.lmhead.dw", "gemm.bwd.fcproj.dx",
                      "gemm.bwd.fcproj.dw", "gemm.bwd.fc.dx", "gemm.bwd.fc.dw", "gemm.bwd.proj.dx", "gemm.bwd.proj.dw",
-                     "gemm.bwd.qkv.dx", "gemm.bwd.qkv.dw"):
+                     "gemm.bwd.qkv.dx", "gemm.bwd.qkv.dw", "gemm.bwd.dw"):
             step.timing_enable(site)
             one_step(0)
             sm, sn, sf, sb = step.timing_read()
             step.timing_enable(None)
+            if sn == 0:  # e.g. per-site weight gradients when they run as one grouped launch
+                continue
             breakdown[site] = {"ms_per_step": round(sm, 3), "launches": int(sn),
                                "tflops": round(sf / max(sm, 1e-9) / 1e9, 1) if sf else None,
                                "gbs": round(sb / max(sm, 1e-9) / 1e6, 1)}

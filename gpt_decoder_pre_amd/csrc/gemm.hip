@@ -9,6 +9,7 @@
 // multiplied (two LDS buffers, one barrier per k-tile).
 //
 // fp32 path: LDS-tiled FMA GEMM (64x64 tile, 4x4 outputs per thread).
+#include <algorithm>
 #include <cmath>
 #include <type_traits>
 
@@ -619,27 +620,30 @@ struct SaddrLoader {
   }
 };
 
-template <bool A_K, bool B_K, int BM, int BN, int EPI, int OCC = 1>
-__global__ __launch_bounds__(256, OCC) void gemm_w4_kernel(GemmArgs p) {
+// LDS elements of the one-wave-per-SIMD tile (two operand stages, or the
+// staged epilogue if larger).
+template <int BM, int BN>
+constexpr int w4_lds_elems() {
+  constexpr int STAGE = (BM + BN) * 64, EPI_ELEMS = 4 * (BM / 2) * (BN / 2 + 8);
+  return 2 * STAGE > EPI_ELEMS ? 2 * STAGE : EPI_ELEMS;
+}
+
+// One BM x BN output tile (tile row tm, column tn, k-split `split`) of p.
+template <bool A_K, bool B_K, int BM, int BN, int EPI>
+DEVI void w4_tile(const GemmArgs& p, int tm, int tn, int split, bf16* smem) {
   constexpr int BK = 64, NW = 4;
   constexpr int WTM = BM / 2, WTN = BN / 2;
   constexpr int FM = WTM / 32, FN = WTN / 32;
   constexpr int STAGE = (BM + BN) * BK;  // elements
   constexpr int SLD = WTN + 8;           // staged epilogue row stride
-  constexpr int EPI_ELEMS = NW * WTM * SLD;
-  constexpr int LDS_ELEMS = 2 * STAGE > EPI_ELEMS ? 2 * STAGE : EPI_ELEMS;
   using LA = SaddrLoader<A_K, BM, NW>;
   using LB = SaddrLoader<B_K, BN, NW>;
   constexpr int LPW = LA::PER_WAVE + LB::PER_WAVE;
   constexpr int G = FM * FN;  // MFMAs per 16-k step
-  __shared__ __attribute__((aligned(1024))) bf16 smem[LDS_ELEMS];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
-  const int tiles_m = (p.M + BM - 1) / BM, tiles_n = (p.N + BN - 1) / BN;
-  int tm, tn, split;
-  tile_coords(p, tiles_m, tiles_n, blockIdx.x + blockIdx.y * gridDim.x, gridDim.x * gridDim.y, tm, tn, split);
   const int m0 = tm * BM, n0 = tn * BN;
   const int kbeg = split * p.k_per_split;
   const int kend = min(p.K, kbeg + p.k_per_split);
@@ -749,6 +753,53 @@ __global__ __launch_bounds__(256, OCC) void gemm_w4_kernel(GemmArgs p) {
   } else {
     gemm_epilogue<EPI, FM, FN, false>(pe, acc, nullptr, m0 + wm * WTM, n0 + wn * WTN, lane, split);
   }
+}
+
+template <bool A_K, bool B_K, int BM, int BN, int EPI, int OCC = 1>
+__global__ __launch_bounds__(256, OCC) void gemm_w4_kernel(GemmArgs p) {
+  __shared__ __attribute__((aligned(1024))) bf16 smem[w4_lds_elems<BM, BN>()];
+  const int tiles_m = (p.M + BM - 1) / BM, tiles_n = (p.N + BN - 1) / BN;
+  int tm, tn, split;
+  tile_coords(p, tiles_m, tiles_n, blockIdx.x + blockIdx.y * gridDim.x, gridDim.x * gridDim.y, tm, tn, split);
+  w4_tile<A_K, B_K, BM, BN, EPI>(p, tm, tn, split, smem);
+}
+
+// Many independent products in one launch (weight gradients of a whole
+// backward pass: fp32 C += A^T B, both operands stored [K][rows]).  The grid
+// is renumbered per XCD over all tiles, then tile t belongs to the problem
+// with first[j] <= t < first[j + 1]; within a problem tiles are walked as in
+// tile_coords (groups of GM tile-rows).
+__global__ __launch_bounds__(256, 1) void gemm_w4_group_kernel(GemmGroup grp) {
+  constexpr int BM = 256, BN = 192;
+  __shared__ __attribute__((aligned(1024))) bf16 smem[w4_lds_elems<BM, BN>()];
+  constexpr int NX = 8;
+  const int b = blockIdx.x, nblk = gridDim.x;
+  const int xcd = b % NX, idx = b / NX;
+  const int q = nblk / NX, rem = nblk % NX;
+  const int t = xcd * q + min(xcd, rem) + idx;
+  int j = 0;
+  while (j + 1 < grp.n && t >= grp.first[j + 1]) ++j;
+  const GemmProblem& pr = grp.prob[j];
+  GemmArgs p = {};
+  p.A = pr.A;
+  p.B = pr.B;
+  p.C = pr.C;
+  p.M = pr.M;
+  p.N = pr.N;
+  p.K = pr.K;
+  p.lda = pr.lda;
+  p.ldb = pr.ldb;
+  p.ldc = pr.ldc;
+  p.splits = 1;
+  p.k_per_split = pr.K;
+  const int tiles_m = (p.M + BM - 1) / BM, tiles_n = (p.N + BN - 1) / BN;
+  const int local = t - grp.first[j];
+  constexpr int GM = 8;
+  const int g = local / (GM * tiles_n);
+  const int first_m = g * GM;
+  const int gm = min(GM, tiles_m - first_m);
+  const int w = local - g * GM * tiles_n;
+  w4_tile<false, false, BM, BN, EPI_F32_ACC>(p, first_m + w % gm, w / gm, 0, smem);
 }
 
 // -------------------------------------------------------------- fp32 GEMM ----
@@ -948,6 +999,25 @@ int choose_cfg(const GemmArgs& a, GemmLayout layout) {
   return pick;
 }
 }  // namespace
+
+bool gemm_group_ok(const GemmProblem& p) {
+  return p.M > 0 && p.N > 0 && p.K > 0 && p.K % 64 == 0 && p.M % 8 == 0 && p.N % 8 == 0 && p.lda % 8 == 0 &&
+         p.ldb % 8 == 0;
+}
+
+void gemm_group_tn_acc(const GemmProblem* probs, int n, hipStream_t s) {
+  for (int j0 = 0; j0 < n; j0 += kGroupMax) {
+    GemmGroup g;
+    g.n = std::min(kGroupMax, n - j0);
+    int tiles = 0;
+    for (int j = 0; j < g.n; ++j) {
+      g.prob[j] = probs[j0 + j];
+      g.first[j] = tiles;
+      tiles += ((g.prob[j].M + 255) / 256) * ((g.prob[j].N + 191) / 192);
+    }
+    gemm_w4_group_kernel<<<tiles, 256, 0, s>>>(g);
+  }
+}
 
 int gemm_pick_config(const GemmArgs& a, GemmLayout layout) { return choose_cfg(a, layout); }
 

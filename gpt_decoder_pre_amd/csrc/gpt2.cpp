@@ -377,6 +377,28 @@ int backward_impl(gpt2_ctx* c) {
     jobs.push_back(ColJob{{o0, o1, o2}, part, chunks, n, nout});
     part += (int64_t)arrays * chunks * n;
   };
+  // Weight gradients: in bf16 mode with whole 64-token k-tiles they are
+  // collected and run as one grouped launch at the end of the pass (enough
+  // output tiles to fill the GPU without split-K); otherwise each runs here.
+  const bool group_dw = c->bf16 && M % 64 == 0;
+  std::vector<GemmProblem> dw;
+  auto wgrad = [&](const char* site, float* out, const void* A, int64_t lda, const void* Bop, int64_t ldb, int Mo,
+                   int N) -> bool {
+    if (group_dw) {
+      const GemmProblem pr{A, Bop, out, Mo, N, M, lda, ldb, (int64_t)N};
+      if (gemm_group_ok(pr)) {
+        dw.push_back(pr);
+        return true;
+      }
+    }
+    return weight_grad(c, site, out, A, lda, Bop, ldb, Mo, N, M);
+  };
+  // residual-gradient slots (bf16 copy): 2L + 1 is the lm_head side, 2l + 1
+  // the gradient at x_mid of block l, 2l the gradient at x_in of block l
+  const bool per_layer = c->bf16;
+  auto dres_slot = [&](int i) -> TA* {
+    return (TA*)(c->dres_act + (per_layer ? (int64_t)i * c->Mmax * C * c->act : 0));
+  };
   // lm_head (tied): dlnf = dz wte; dwte += dz^T lnf
   // dh: gradient at a LayerNorm output, in the activation type (bf16 in bf16
   // mode, like every other matmul output of the mixed-precision step)
@@ -384,12 +406,12 @@ int backward_impl(gpt2_ctx* c) {
   GemmArgs g = gargs(c->logits, Vp, c->W(T_WTE), C, M, C, Vp, dh, C);
   if (!gemm_site(c, "gemm.bwd.lmhead.dx", LAYOUT_NN, EPI_ACT, g, a * ((double)M * Vp + (double)Vp * C + (double)M * C)))
     return GPT2_ERR_ARG;
-  if (!weight_grad(c, "gemm.bwd.lmhead.dw", c->G(T_WTE), c->logits, Vp, c->lnf, C, Vp, C, M)) return GPT2_ERR_ARG;
+  if (!wgrad("gemm.bwd.lmhead.dw", c->G(T_WTE), c->logits, Vp, c->lnf, C, Vp, C)) return GPT2_ERR_ARG;
   int ch;
   {
     Timed tm(c, "ln.bwd", 0, (double)M * C * (8 + 2 * a) + 8.0 * M);
     ch = layernorm_bwd<TA>(dh, c->resid(2 * L), c->lnf_mean, c->lnf_rstd, c->P(T_LNFW), c->dres, false,
-                           (TA*)c->dres_act, part, M, C, s);
+                           dres_slot(2 * L), part, M, C, s);
   }
   defer(c->G(T_LNFW), c->G(T_LNFB), c->G(T_FCPB, L - 1), ch, C, 3);
 
@@ -401,35 +423,35 @@ int backward_impl(gpt2_ctx* c) {
     TA* fcgd = (TA*)c->layer_act(c->fcgd, l, 4 * C);
     TA* fcg = (TA*)c->layer_act(c->fcg, l, 4 * C);
     float* lse = c->lse + (int64_t)l * c->Mmax * c->NH;
-    TA* dres_act = (TA*)c->dres_act;
-    TA* dbig = (TA*)c->dbig;
-    TA* dqkv = (TA*)c->dqkv;
+    TA* dres_out = dres_slot(2 * l + 2);  // gradient at x_out of this block
+    TA* dres_mid = dres_slot(2 * l + 1);
+    TA* dbig = (TA*)(per_layer ? c->layer_act(c->dbig, l, 4 * C) : c->dbig);
+    TA* dqkv = (TA*)(per_layer ? c->layer_act(c->dqkv, l, 3 * C) : c->dqkv);
     TA* dy = (TA*)c->dy;
 
     // MLP output projection: x_out = x_mid + g Wfp^T + bfp
-    if (!weight_grad(c, "gemm.bwd.fcproj.dw", c->G(T_FCPW, l), dres_act, C, fcg, 4 * C, C, 4 * C, M))
-      return GPT2_ERR_ARG;
-    g = gargs(dres_act, C, c->W(T_FCPW, l), 4 * C, M, 4 * C, C, dbig, 4 * C);
+    if (!wgrad("gemm.bwd.fcproj.dw", c->G(T_FCPW, l), dres_out, C, fcg, 4 * C, C, 4 * C)) return GPT2_ERR_ARG;
+    g = gargs(dres_out, C, c->W(T_FCPW, l), 4 * C, M, 4 * C, C, dbig, 4 * C);
     g.aux = fcgd;
     if (!gemm_site(c, "gemm.bwd.fcproj.dx", LAYOUT_NN, EPI_GELU_BWD, g, a * ((double)M * C + 4.0 * C * C + 8.0 * M * C)))
       return GPT2_ERR_ARG;
     ch = colsum_partials<TA>(dbig, M, 4 * C, part, s);
     defer(c->G(T_FCB, l), nullptr, nullptr, ch, 4 * C, 1);
     // MLP input projection: u = LN2(x_mid) Wfc^T + bfc
-    if (!weight_grad(c, "gemm.bwd.fc.dw", c->G(T_FCW, l), dbig, 4 * C, ln2, C, 4 * C, C, M)) return GPT2_ERR_ARG;
+    if (!wgrad("gemm.bwd.fc.dw", c->G(T_FCW, l), dbig, 4 * C, ln2, C, 4 * C, C)) return GPT2_ERR_ARG;
     g = gargs(dbig, 4 * C, c->W(T_FCW, l), C, M, C, 4 * C, dh, C);
     if (!gemm_site(c, "gemm.bwd.fc.dx", LAYOUT_NN, EPI_ACT, g, a * (4.0 * M * C + 4.0 * C * C + (double)M * C)))
       return GPT2_ERR_ARG;
     {
       Timed tm(c, "ln.bwd", 0, (double)M * C * (12 + 2 * a) + 8.0 * M);
       ch = layernorm_bwd<TA>(dh, c->resid(2 * l + 1), c->ln2_mean + (int64_t)l * c->Mmax,
-                             c->ln2_rstd + (int64_t)l * c->Mmax, c->P(T_LN2W, l), c->dres, true, dres_act, part, M,
+                             c->ln2_rstd + (int64_t)l * c->Mmax, c->P(T_LN2W, l), c->dres, true, dres_mid, part, M,
                              C, s);
     }
     defer(c->G(T_LN2W, l), c->G(T_LN2B, l), c->G(T_PROJB, l), ch, C, 3);
     // attention output projection: x_mid = x_in + y Wp^T + bp
-    if (!weight_grad(c, "gemm.bwd.proj.dw", c->G(T_PROJW, l), dres_act, C, atty, C, C, C, M)) return GPT2_ERR_ARG;
-    g = gargs(dres_act, C, c->W(T_PROJW, l), C, M, C, C, dy, C);
+    if (!wgrad("gemm.bwd.proj.dw", c->G(T_PROJW, l), dres_mid, C, atty, C, C, C)) return GPT2_ERR_ARG;
+    g = gargs(dres_mid, C, c->W(T_PROJW, l), C, M, C, C, dy, C);
     if (!gemm_site(c, "gemm.bwd.proj.dx", LAYOUT_NN, EPI_ACT, g, a * (2.0 * M * C + (double)C * C)))
       return GPT2_ERR_ARG;
     {
@@ -442,14 +464,14 @@ int backward_impl(gpt2_ctx* c) {
     ch = colsum_partials<TA>(dqkv, M, 3 * C, part, s);
     defer(c->G(T_QKVB, l), nullptr, nullptr, ch, 3 * C, 1);
     // QKV projection: qkv = LN1(x_in) Wqkv^T + bqkv
-    if (!weight_grad(c, "gemm.bwd.qkv.dw", c->G(T_QKVW, l), dqkv, 3 * C, ln1, C, 3 * C, C, M)) return GPT2_ERR_ARG;
+    if (!wgrad("gemm.bwd.qkv.dw", c->G(T_QKVW, l), dqkv, 3 * C, ln1, C, 3 * C, C)) return GPT2_ERR_ARG;
     g = gargs(dqkv, 3 * C, c->W(T_QKVW, l), C, M, C, 3 * C, dh, C);
     if (!gemm_site(c, "gemm.bwd.qkv.dx", LAYOUT_NN, EPI_ACT, g, a * (3.0 * M * C + 3.0 * C * C + (double)M * C)))
       return GPT2_ERR_ARG;
     {
       Timed tm(c, "ln.bwd", 0, (double)M * C * (12 + 2 * a) + 8.0 * M);
       ch = layernorm_bwd<TA>(dh, c->resid(2 * l), c->ln1_mean + (int64_t)l * c->Mmax,
-                             c->ln1_rstd + (int64_t)l * c->Mmax, c->P(T_LN1W, l), c->dres, true, dres_act, part, M,
+                             c->ln1_rstd + (int64_t)l * c->Mmax, c->P(T_LN1W, l), c->dres, true, dres_slot(2 * l), part, M,
                              C, s);
     }
     // the shift's third output is the previous block's MLP output bias
@@ -457,6 +479,15 @@ int backward_impl(gpt2_ctx* c) {
     else defer(c->G(T_LN1W, l), c->G(T_LN1B, l), nullptr, ch, C, 3);
   }
   colpart_reduce_batch(jobs.data(), (int)jobs.size(), s);
+  if (!dw.empty()) {
+    double fl = 0.0, by = 0.0;
+    for (const GemmProblem& pr : dw) {
+      fl += 2.0 * pr.M * (double)pr.N * pr.K;
+      by += a * ((double)pr.K * pr.M + (double)pr.K * pr.N) + 8.0 * pr.M * (double)pr.N;
+    }
+    Timed tm(c, "gemm.bwd.dw", fl, by);
+    gemm_group_tn_acc(dw.data(), (int)dw.size(), s);
+  }
   // embedding: x0 = wte[idx] + wpe[t]
   {
     Timed tm(c, "embed.bwd", 0, 12.0 * M * C);
@@ -502,10 +533,14 @@ int64_t plan_workspace(gpt2_ctx* c, Plan& p, bool assign) {
   c->row_loss = (float*)at(M * 4);
   c->ids = (int32_t*)at(M * 4);
   c->dres = (float*)at(M * C * 4);
-  c->dres_act = at(M * C * A);
+  // bf16: the gradients the weight-gradient GEMMs read stay until the end of
+  // the backward pass (one grouped launch there): 2L + 1 residual-gradient
+  // slots, L slots of du and of dqkv.  fp32: one of each.
+  const int64_t slots = c->bf16 ? L : 1;
+  c->dres_act = at((2 * slots + 1) * M * C * A);
   c->dh = (float*)at(M * C * 4);
-  c->dbig = at(M * 4 * C * A);
-  c->dqkv = at(M * 3 * C * A);
+  c->dbig = at(slots * M * 4 * C * A);
+  c->dqkv = at(slots * M * 3 * C * A);
   c->dy = at(M * C * A);
   c->attnD = (float*)at(M * NH * 4);
   c->splitk_elems = std::max<int64_t>(16 * 4 * C * C, 2 * Vp * C);

@@ -39,6 +39,29 @@ struct GemmArgs {
   int group_m;     // tile-rows walked together (0: default 8)
   int no_xcd_map;  // 1: keep the hardware block order (no per-XCD renumbering)
 };
+// One product of a grouped launch: fp32 C[M][N] += A^T B with A stored
+// [K][M] (lda) and B stored [K][N] (ldb), bf16 operands.
+struct GemmProblem {
+  const void* A;
+  const void* B;
+  void* C;
+  int M, N, K;
+  int64_t lda, ldb, ldc;
+};
+constexpr int kGroupMax = 48;
+struct GemmGroup {
+  GemmProblem prob[kGroupMax];
+  int first[kGroupMax];  // first tile of each problem
+  int n;
+};
+static_assert(sizeof(GemmGroup) <= 4096, "kernel argument size");
+// Whether a problem can go into a grouped launch (K a multiple of 64, M and N
+// multiples of 8).
+bool gemm_group_ok(const GemmProblem& p);
+// All problems in one launch per kGroupMax problems (256 x 192 tiles, no
+// split-K: each tile adds its whole-K product into C).  Problems must not
+// overlap in C.
+void gemm_group_tn_acc(const GemmProblem* probs, int n, hipStream_t s);
 // Returns false if the shape breaks a kernel precondition.
 bool gemm(GemmLayout layout, GemmEpilogue epi, bool bf16_mode, const GemmArgs& a, hipStream_t s);
 // Same with an explicit bf16 tile configuration (cfg < 0: automatic choice).
