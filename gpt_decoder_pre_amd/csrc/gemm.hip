@@ -789,7 +789,7 @@ __global__ __launch_bounds__(256, 1) void gemm_w4_group_kernel(GemmGroup grp) {
   p.K = pr.K;
   p.lda = pr.lda;
   p.ldb = pr.ldb;
-  p.ldc = pr.ldc;
+  p.ldc = pr.N;
   p.splits = 1;
   p.k_per_split = pr.K;
   const int tiles_m = (p.M + BM - 1) / BM, tiles_n = (p.N + BN - 1) / BN;
@@ -1006,15 +1006,31 @@ bool gemm_group_ok(const GemmProblem& p) {
 }
 
 void gemm_group_tn_acc(const GemmProblem* probs, int n, hipStream_t s) {
-  for (int j0 = 0; j0 < n; j0 += kGroupMax) {
+  auto tiles_of = [](const GemmProblem& p) { return ((p.M + 255) / 256) * ((p.N + 191) / 192); };
+  int64_t total = 0;
+  for (int j = 0; j < n; ++j) total += tiles_of(probs[j]);
+  // launches of at most kGroupMax problems, each cut once its running tile
+  // count passes an equal share (a launch with a few tiles would idle most
+  // CUs) but never leaving more problems than the later launches can take
+  const int launches = (n + kGroupMax - 1) / kGroupMax;
+  int j0 = 0;
+  int64_t done = 0;
+  for (int li = 0; li < launches; ++li) {
+    const int64_t target = total * (li + 1) / launches;
+    const int min_count = std::max(1, (n - j0) - (launches - 1 - li) * kGroupMax);
+    const int max_count = std::min(kGroupMax, n - j0);
     GemmGroup g;
-    g.n = std::min(kGroupMax, n - j0);
+    g.n = 0;
     int tiles = 0;
-    for (int j = 0; j < g.n; ++j) {
-      g.prob[j] = probs[j0 + j];
-      g.first[j] = tiles;
-      tiles += ((g.prob[j].M + 255) / 256) * ((g.prob[j].N + 191) / 192);
+    while (g.n < max_count && (g.n < min_count || done < target || li == launches - 1)) {
+      g.prob[g.n] = probs[j0 + g.n];
+      g.first[g.n] = tiles;
+      tiles += tiles_of(probs[j0 + g.n]);
+      done += tiles_of(probs[j0 + g.n]);
+      ++g.n;
     }
+    j0 += g.n;
+    if (tiles == 0) break;
     gemm_w4_group_kernel<<<tiles, 256, 0, s>>>(g);
   }
 }

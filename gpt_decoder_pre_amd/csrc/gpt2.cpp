@@ -385,7 +385,7 @@ int backward_impl(gpt2_ctx* c) {
   auto wgrad = [&](const char* site, float* out, const void* A, int64_t lda, const void* Bop, int64_t ldb, int Mo,
                    int N) -> bool {
     if (group_dw) {
-      const GemmProblem pr{A, Bop, out, Mo, N, M, lda, ldb, (int64_t)N};
+      const GemmProblem pr{A, Bop, out, Mo, N, M, (int)lda, (int)ldb};
       if (gemm_group_ok(pr)) {
         dw.push_back(pr);
         return true;

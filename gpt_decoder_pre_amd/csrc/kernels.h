@@ -44,11 +44,11 @@ struct GemmArgs {
 struct GemmProblem {
   const void* A;
   const void* B;
-  void* C;
+  void* C;        // ldc = N
   int M, N, K;
-  int64_t lda, ldb, ldc;
+  int lda, ldb;
 };
-constexpr int kGroupMax = 48;
+constexpr int kGroupMax = 64;
 struct GemmGroup {
   GemmProblem prob[kGroupMax];
   int first[kGroupMax];  // first tile of each problem
@@ -58,9 +58,9 @@ static_assert(sizeof(GemmGroup) <= 4096, "kernel argument size");
 // Whether a problem can go into a grouped launch (K a multiple of 64, M and N
 // multiples of 8).
 bool gemm_group_ok(const GemmProblem& p);
-// All problems in one launch per kGroupMax problems (256 x 192 tiles, no
-// split-K: each tile adds its whole-K product into C).  Problems must not
-// overlap in C.
+// All problems in as few launches as kGroupMax allows, with about equal tile
+// counts per launch (256 x 192 tiles, no split-K: each tile adds its whole-K
+// product into C).  Problems must not overlap in C.
 void gemm_group_tn_acc(const GemmProblem* probs, int n, hipStream_t s);
 // Returns false if the shape breaks a kernel precondition.
 bool gemm(GemmLayout layout, GemmEpilogue epi, bool bf16_mode, const GemmArgs& a, hipStream_t s);
