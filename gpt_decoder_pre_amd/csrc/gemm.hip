@@ -769,8 +769,8 @@ __global__ __launch_bounds__(256, OCC) void gemm_w4_kernel(GemmArgs p) {
 // is renumbered per XCD over all tiles, then tile t belongs to the problem
 // with first[j] <= t < first[j + 1]; within a problem tiles are walked as in
 // tile_coords (groups of GM tile-rows).
+template <int BM, int BN>
 __global__ __launch_bounds__(256, 1) void gemm_w4_group_kernel(GemmGroup grp) {
-  constexpr int BM = 256, BN = 192;
   __shared__ __attribute__((aligned(1024))) bf16 smem[w4_lds_elems<BM, BN>()];
   constexpr int NX = 8;
   const int b = blockIdx.x, nblk = gridDim.x;
@@ -1005,8 +1005,14 @@ bool gemm_group_ok(const GemmProblem& p) {
          p.ldb % 8 == 0;
 }
 
+// 256 x 256 tiles: fewer operand bytes per flop than 256 x 192 (the stream
+// from L2 bounds these long-K products), at a slightly coarser last wave.
+constexpr int kGroupBM = 256, kGroupBN = 256;
+
 void gemm_group_tn_acc(const GemmProblem* probs, int n, hipStream_t s) {
-  auto tiles_of = [](const GemmProblem& p) { return ((p.M + 255) / 256) * ((p.N + 191) / 192); };
+  auto tiles_of = [](const GemmProblem& p) {
+    return ((p.M + kGroupBM - 1) / kGroupBM) * ((p.N + kGroupBN - 1) / kGroupBN);
+  };
   int64_t total = 0;
   for (int j = 0; j < n; ++j) total += tiles_of(probs[j]);
   // launches of at most kGroupMax problems, each cut once its running tile
@@ -1031,7 +1037,7 @@ void gemm_group_tn_acc(const GemmProblem* probs, int n, hipStream_t s) {
     }
     j0 += g.n;
     if (tiles == 0) break;
-    gemm_w4_group_kernel<<<tiles, 256, 0, s>>>(g);
+    gemm_w4_group_kernel<kGroupBM, kGroupBN><<<tiles, 256, 0, s>>>(g);
   }
 }
 

@@ -59,7 +59,7 @@ static_assert(sizeof(GemmGroup) <= 4096, "kernel argument size");
 // multiples of 8).
 bool gemm_group_ok(const GemmProblem& p);
 // All problems in as few launches as kGroupMax allows, with about equal tile
-// counts per launch (256 x 192 tiles, no split-K: each tile adds its whole-K
+// counts per launch (256 x 256 tiles, no split-K: each tile adds its whole-K
 // product into C).  Problems must not overlap in C.
 void gemm_group_tn_acc(const GemmProblem* probs, int n, hipStream_t s);
 // Returns false if the shape breaks a kernel precondition.
