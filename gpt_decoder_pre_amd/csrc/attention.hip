@@ -136,20 +136,21 @@ DEVI float sum_bf16x8(bf16x8 v, float acc) {
   return acc;
 }
 
-// Workgroups are dispatched to the eight XCDs round-robin in launch order,
-// and each XCD has its own L2.  Block b of a 1-D grid of n runs as logical
-// block (b % 8) (n / 8) + b / 8, so each XCD works through a contiguous range
-// of logical blocks: the tiles of one (sequence, head), which all re-read the
-// same K and V (or Q and dO), then share one L2.  Identity unless n % 8 == 0.
-DEVI int xcd_block(int b, int n) { return (n % 8 == 0) ? (b % 8) * (n / 8) + b / 8 : b; }
-
-// Logical block -> (tile index within the head, head, sequence); tiles of a
-// head are consecutive.
+// Block -> (tile index within the head, head, sequence).  Causal tiles carry
+// very different work (the first key tile of a head sees every query tile,
+// the last one a single one), so the tile index is the slowest-varying part
+// of the block index: every head's longest tile is dispatched first, then
+// every head's second longest, and so on.  Taken in this order, greedy
+// dispatch leaves a short tail; head by head, a long tile dispatched near
+// the end would run alone (about a third longer in all).  Workgroups go to
+// the eight XCDs round-robin in launch order, so when B NH is a multiple of 8
+// every tile of a head runs on the same XCD and shares its L2 (the tiles
+// re-read the same K and V, or Q and dO).
 DEVI void attn_block(int T, int NH, int& tile, int& h, int& b) {
   const int nq = (T + 127) / 128;
-  const int L = xcd_block(blockIdx.x, gridDim.x);
-  const int bh = L / nq;
-  tile = L - bh * nq;
+  const int bh_count = gridDim.x / nq;
+  tile = blockIdx.x / bh_count;
+  const int bh = blockIdx.x - tile * bh_count;
   h = bh % NH;
   b = bh / NH;
 }
@@ -170,7 +171,7 @@ __global__ __launch_bounds__(256, 3) void flash_fwd_kernel(const bf16* __restric
   __shared__ __attribute__((aligned(1024))) bf16 smem[3 * ASTAGE];  // [stage][K | V]
   int qt, h, b;
   attn_block(T, NH, qt, h, b);
-  qt = (T + 127) / 128 - 1 - qt;  // longest rows first within a head
+  qt = (T + 127) / 128 - 1 - qt;  // tile 0: the most key tiles
   const int tid = threadIdx.x, lane = tid & 63, lc = lane & 31, hl = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int q0 = qt * 128;
@@ -352,7 +353,7 @@ __global__ __launch_bounds__(256, 2) void flash_bwd_dkdv_kernel(const bf16* __re
   attn_block(T, NH, kt, h, b);
   const int tid = threadIdx.x, lane = tid & 63, lc = lane & 31, hl = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int key0 = kt * 128;  // tile 0 has the most queries and is scheduled first
+  const int key0 = kt * 128;  // tile 0: the most query tiles
   const int wk0 = key0 + wave * 32;
   const int mykey = wk0 + lc;
   const int64_t ld = 3 * (int64_t)C;
@@ -492,7 +493,7 @@ __global__ __launch_bounds__(256, 2) void flash_bwd_dq_kernel(const bf16* __rest
   __shared__ __attribute__((aligned(1024))) bf16 smem[3 * ASTAGE];  // [stage][K | V]
   int qt, h, b;
   attn_block(T, NH, qt, h, b);
-  qt = (T + 127) / 128 - 1 - qt;
+  qt = (T + 127) / 128 - 1 - qt;  // tile 0: the most key tiles
   const int tid = threadIdx.x, lane = tid & 63, lc = lane & 31, hl = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int q0 = qt * 128;
