@@ -9,9 +9,9 @@
 // to the MFMA as the B operand of O^T = V^T P^T with the key order permuted
 // to match the accumulator layout (the contraction order is free), so P never
 // leaves registers; V is stored transposed in LDS for that product.
-// Backward recomputes P from the saved log-sum-exp: one kernel per key tile
-// accumulates dK and dV over query tiles, one per query tile accumulates dQ
-// over key tiles (no atomics).
+// Backward recomputes P from the saved log-sum-exp: one kernel per query tile
+// computes D = rowsum(dO o O) and accumulates dQ over key tiles, then one per
+// key tile accumulates dK and dV over query tiles (no atomics).
 //
 // fp32 path: one wavefront per query (forward, dQ) or key (dK, dV) row with the
 // scores of the row in LDS; plain fp32 arithmetic for the exact-mode step.
@@ -311,30 +311,6 @@ __global__ __launch_bounds__(256, 3) void flash_fwd_kernel(const bf16* __restric
   }
 }
 
-// D[b][h][t] = sum_d dO[b,t,h,d] O[b,t,h,d]
-__global__ void attn_rowdot_kernel(const bf16* __restrict__ y, const bf16* __restrict__ dy, float* __restrict__ D,
-                                   int B, int T, int NH, int C) {
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;  // over B*T*NH
-  if (i >= (int64_t)B * T * NH) return;
-  const int h = (int)(i % NH);
-  const int64_t m = i / NH;  // b*T + t
-  const bf16* a = y + m * C + h * HD;
-  const bf16* g = dy + m * C + h * HD;
-  float s = 0.f;
-#pragma unroll
-  for (int d = 0; d < HD; d += 8) {
-    float u[4], v[4], u2[4], v2[4];
-    load4(a + d, u);
-    load4(g + d, v);
-    load4(a + d + 4, u2);
-    load4(g + d + 4, v2);
-    s += u[0] * v[0] + u[1] * v[1] + u[2] * v[2] + u[3] * v[3] + u2[0] * v2[0] + u2[1] * v2[1] + u2[2] * v2[2] +
-         u2[3] * v2[3];
-  }
-  const int b = (int)(m / T), t = (int)(m % T);
-  D[((int64_t)b * NH + h) * T + t] = s;
-}
-
 // ---------------------------------------------------------- backward: dK, dV ----
 // Workgroup: 128 keys of one (sequence, head); wave w owns keys key0 + 32 w +
 // lane%32 and accumulates dK^T and dV^T over the query tiles (64 queries)
@@ -482,14 +458,16 @@ __global__ __launch_bounds__(256, 2) void flash_bwd_dkdv_kernel(const bf16* __re
 }
 
 // --------------------------------------------------------------- backward: dQ ----
-// Workgroup: 128 queries; wave w owns queries q0 + 32 w + lane%32 and
+// Workgroup: 128 queries; wave w owns queries q0 + 32 w + lane%32, forms D
+// for them from the dO and O rows (and stores it for the dK / dV kernel), and
 // accumulates dQ^T over the key tiles (64 keys) it sees; K and V tiles stream
 // into a three-stage LDS ring as in the forward kernel.
 __global__ __launch_bounds__(256, 2) void flash_bwd_dq_kernel(const bf16* __restrict__ qkv,
+                                                              const bf16* __restrict__ y,
                                                               const bf16* __restrict__ dy,
-                                                              const float* __restrict__ lse,
-                                                              const float* __restrict__ Dd, bf16* __restrict__ dqkv,
-                                                              int T, int NH, int C, float sl2, float scale) {
+                                                              const float* __restrict__ lse, float* __restrict__ Dd,
+                                                              bf16* __restrict__ dqkv, int T, int NH, int C, float sl2,
+                                                              float scale) {
   __shared__ __attribute__((aligned(1024))) bf16 smem[3 * ASTAGE];  // [stage][K | V]
   int qt, h, b;
   attn_block(T, NH, qt, h, b);
@@ -518,13 +496,19 @@ __global__ __launch_bounds__(256, 2) void flash_bwd_dq_kernel(const bf16* __rest
 
   const bool qok = myq < T;
   const float lse2 = qok ? lse[((int64_t)b * NH + h) * T + myq] * kLog2e : 0.f;
-  const float Dq = qok ? Dd[((int64_t)b * NH + h) * T + myq] : 0.f;
   bf16x8 qf[4], gf[4];
+  float dsum = 0.f;  // this lane's half of D = sum_d dO O for its query
 #pragma unroll
   for (int kk = 0; kk < 4; ++kk) {
     qf[kk] = as_bf16x8(ld16_or_zero(Q + (int64_t)myq * ld + kk * 16 + hl * 8, qok));
     gf[kk] = as_bf16x8(ld16_or_zero(G + (int64_t)myq * C + kk * 16 + hl * 8, qok));
+    const bf16x8 of = as_bf16x8(ld16_or_zero(y + ((int64_t)b * T + myq) * C + h * HD + kk * 16 + hl * 8, qok));
+#pragma unroll
+    for (int e = 0; e < 8; ++e) dsum = fmaf((float)gf[kk][e], (float)of[e], dsum);
   }
+  // D for the dK / dV kernel (launched after this one) and for this one
+  const float Dq = halves_sum(dsum);
+  if (qok && hl == 0) Dd[((int64_t)b * NH + h) * T + myq] = Dq;
   f32x16 dq[2];
 #pragma unroll
   for (int r = 0; r < 16; ++r) dq[0][r] = dq[1][r] = 0.f;
@@ -600,15 +584,14 @@ void attn_fwd_bf16(const void* qkv, void* y, float* lse, int B, int T, int NH, i
 void attn_bwd_bf16(const void* qkv, const void* y, const void* dy, const float* lse, float* Dbuf, void* dqkv, int B,
                    int T, int NH, int C, hipStream_t s) {
   const float scale = 1.0f / sqrtf((float)HD);
-  const int64_t rows = (int64_t)B * T * NH;
-  attn_rowdot_kernel<<<(unsigned)((rows + 255) / 256), 256, 0, s>>>(
-      reinterpret_cast<const bf16*>(y), reinterpret_cast<const bf16*>(dy), Dbuf, B, T, NH, C);
   const unsigned grid = (unsigned)((T + 127) / 128 * NH * B);
+  // dQ first: it also writes D = rowsum(dO o O), which dK / dV reads
+  flash_bwd_dq_kernel<<<grid, 256, 0, s>>>(reinterpret_cast<const bf16*>(qkv), reinterpret_cast<const bf16*>(y),
+                                           reinterpret_cast<const bf16*>(dy), lse, Dbuf,
+                                           reinterpret_cast<bf16*>(dqkv), T, NH, C, scale * kLog2e, scale);
   flash_bwd_dkdv_kernel<<<grid, 256, 0, s>>>(reinterpret_cast<const bf16*>(qkv), reinterpret_cast<const bf16*>(dy),
                                              lse, Dbuf, reinterpret_cast<bf16*>(dqkv), T, NH, C, scale * kLog2e,
                                              scale);
-  flash_bwd_dq_kernel<<<grid, 256, 0, s>>>(reinterpret_cast<const bf16*>(qkv), reinterpret_cast<const bf16*>(dy),
-                                           lse, Dbuf, reinterpret_cast<bf16*>(dqkv), T, NH, C, scale * kLog2e, scale);
 }
 
 // ------------------------------------------------------------------ fp32 path ----
