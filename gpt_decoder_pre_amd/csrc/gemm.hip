@@ -419,6 +419,34 @@ DEVI void gemm_epilogue(const GemmArgs& p, f32x16 (&acc)[FM][FN], bf16* region, 
       __builtin_amdgcn_s_waitcnt(0xc07f);
       __builtin_amdgcn_wave_barrier();
     }
+    if constexpr (EPI == EPI_GELU_BWD && WTM % 64 == 0) {
+      // column sums of the staged (bf16) tile per 64-row chunk: the bias
+      // gradient of the layer whose pre-activation gradient this is.  Rows are
+      // added in ascending order, as a separate column-sum pass over C would.
+      if (p.colsum) {
+#pragma unroll
+        for (int c0 = 0; c0 < WTM / 64; ++c0) {
+          const int rows = min(64, p.M - (mb + 64 * c0));  // wave-uniform
+          if (rows <= 0) break;
+          for (int pc = lane; pc < WTN / 2; pc += 64) {
+            const bf16* col = region + 64 * c0 * SLD + 2 * pc;
+            float s0 = 0.f, s1 = 0.f;
+#pragma unroll 8
+            for (int r = 0; r < rows; ++r) {
+              const uint32_t w = *reinterpret_cast<const uint32_t*>(col + r * SLD);
+              s0 += __uint_as_float(w << 16);
+              s1 += __uint_as_float(w & 0xffff0000u);
+            }
+            const int n = nb + 2 * pc;
+            if (n < p.N) {
+              float* out = p.colsum + (int64_t)((mb >> 6) + c0) * p.N + n;
+              out[0] = s0;
+              out[1] = s1;
+            }
+          }
+        }
+      }
+    }
   } else if constexpr (EPI == EPI_RESID && FM * FN <= 6) {
     // the residual tile is loaded whole first (one round trip instead of FM)
     f32x4 rv[FM][FN][4];
@@ -1143,6 +1171,12 @@ bool gemm_cfg(int cfg, GemmLayout layout, GemmEpilogue epi, bool bf16_mode, cons
     }
     if (!gemm_config_usable(cfg, layout, a)) return false;
   }
+  // column-sum partials: formed in the epilogue by the one-wave-per-SIMD
+  // tiles (their wave tiles span whole 64-row chunks), else by a pass over C
+  float* const colsum = epi == EPI_GELU_BWD ? a.colsum : nullptr;
+  if (colsum && a.ldc != a.N) return false;
+  const bool fused_colsum = colsum && bf16_mode && cfg >= 20 && cfg <= 22;
+  if (!fused_colsum) a.colsum = nullptr;
   switch (layout) {
     case LAYOUT_NT:
       if (epi == EPI_ACT) launch<true, true, EPI_ACT>(bf16_mode, cfg, a, s);
@@ -1164,6 +1198,10 @@ bool gemm_cfg(int cfg, GemmLayout layout, GemmEpilogue epi, bool bf16_mode, cons
       else if (epi == EPI_F32) launch<false, false, EPI_F32>(bf16_mode, cfg, a, s);
       else return false;
       break;
+  }
+  if (colsum && !fused_colsum) {
+    if (bf16_mode) colsum_partials<bf16>(reinterpret_cast<const bf16*>(a.C), a.M, a.N, colsum, s);
+    else colsum_partials<float>(reinterpret_cast<const float*>(a.C), a.M, a.N, colsum, s);
   }
   return true;
 }

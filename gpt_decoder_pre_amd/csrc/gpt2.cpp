@@ -433,9 +433,10 @@ int backward_impl(gpt2_ctx* c) {
     if (!wgrad("gemm.bwd.fcproj.dw", c->G(T_FCPW, l), dres_out, C, fcg, 4 * C, C, 4 * C)) return GPT2_ERR_ARG;
     g = gargs(dres_out, C, c->W(T_FCPW, l), 4 * C, M, 4 * C, C, dbig, 4 * C);
     g.aux = fcgd;
+    g.colsum = part;  // fc bias gradient partials, 64 rows per chunk
     if (!gemm_site(c, "gemm.bwd.fcproj.dx", LAYOUT_NN, EPI_GELU_BWD, g, a * ((double)M * C + 4.0 * C * C + 8.0 * M * C)))
       return GPT2_ERR_ARG;
-    ch = colsum_partials<TA>(dbig, M, 4 * C, part, s);
+    ch = (M + 63) / 64;
     defer(c->G(T_FCB, l), nullptr, nullptr, ch, 4 * C, 1);
     // MLP input projection: u = LN2(x_mid) Wfc^T + bfc
     if (!wgrad("gemm.bwd.fc.dw", c->G(T_FCW, l), dbig, 4 * C, ln2, C, 4 * C, C)) return GPT2_ERR_ARG;

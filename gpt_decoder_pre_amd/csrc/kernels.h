@@ -38,6 +38,10 @@ struct GemmArgs {
   int64_t split_stride;
   int group_m;     // tile-rows walked together (0: default 8)
   int no_xcd_map;  // 1: keep the hardware block order (no per-XCD renumbering)
+  // EPI_GELU_BWD only (or null): column sums of C per 64-row chunk, fp32
+  // [ceil(M/64)][N] with ldc == N, each chunk's rows added in ascending order
+  // (formed in the epilogue where the tile allows it, else by a pass over C)
+  float* colsum;
 };
 // One product of a grouped launch: fp32 C[M][N] += A^T B with A stored
 // [K][M] (lda) and B stored [K][N] (ldb), bf16 operands.
