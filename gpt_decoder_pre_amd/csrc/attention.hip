@@ -155,6 +155,37 @@ DEVI void attn_block(int T, int NH, int& tile, int& h, int& b) {
   b = bh / NH;
 }
 
+// qkv bias gradient partials from a backward kernel's stored outputs (T a
+// multiple of 64).  Each wave holds a 64-dim x 32-token block (acc[t][r]:
+// dim 32 t + 8 (r/4) + 4 hl + r%4, token lane%32) of bf16-rounded values;
+// the block's four waves write theirs to LDS, then thread (c, d) of the
+// first 128 adds dim d over the 64 tokens of chunk c (waves 2c and 2c + 1,
+// tokens ascending) into out[chunk][d], out = colsum + column offset.  The
+// caller has synchronised so that red may be overwritten.
+DEVI void chunk_colsums(const f32x16 (&acc)[2], float scale, bool tok_ok, float* red, float* out, int64_t chunk0,
+                        int64_t ldo, int tok0, int T) {
+  const int tid = threadIdx.x, lane = tid & 63, lc = lane & 31, hl = lane >> 5, wave = tid >> 6;
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int d = t * 32 + 8 * (r >> 2) + 4 * hl + (r & 3);
+      red[(wave * 64 + d) * 33 + lc] = tok_ok ? (float)(bf16)(acc[t][r] * scale) : 0.f;
+    }
+  __syncthreads();
+  if (tid < 128) {
+    const int c = tid >> 6, d = tid & 63;
+    if (tok0 + 64 * c < T) {
+      float sum = 0.f;
+#pragma unroll
+      for (int w = 0; w < 2; ++w)
+#pragma unroll 8
+        for (int q = 0; q < 32; ++q) sum += red[((2 * c + w) * 64 + d) * 33 + q];
+      out[(chunk0 + c) * ldo + d] = sum;
+    }
+  }
+}
+
 // max / sum of a value and its copy in the lane 32 apart (same query row)
 DEVI float halves_max(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
@@ -322,7 +353,7 @@ __global__ __launch_bounds__(256, 2) void flash_bwd_dkdv_kernel(const bf16* __re
                                                                 const float* __restrict__ lse,
                                                                 const float* __restrict__ Dd,
                                                                 bf16* __restrict__ dqkv, int T, int NH, int C,
-                                                                float sl2, float scale) {
+                                                                float sl2, float scale, float* __restrict__ colsum) {
   __shared__ __attribute__((aligned(1024))) bf16 smem[3 * ASTAGE];  // [stage][Q | dO]
   __shared__ __attribute__((aligned(16))) float rowv[3][2][64];     // [stage][lse log2e | D]
   int kt, h, b;
@@ -455,6 +486,14 @@ __global__ __launch_bounds__(256, 2) void flash_bwd_dkdv_kernel(const bf16* __re
         store4(o + 2 * C + t * 32 + 8 * q + 4 * hl, c);
       }
   }
+  if (colsum) {  // K and V parts of the qkv bias gradient
+    float* red = reinterpret_cast<float*>(smem);
+    const int64_t chunk0 = ((int64_t)b * T + key0) / 64;
+    __syncthreads();  // every wave is done with the Q / dO stages
+    chunk_colsums(dk, scale, mykey < T, red, colsum + C + h * HD, chunk0, 3 * (int64_t)C, key0, T);
+    __syncthreads();
+    chunk_colsums(dv, 1.0f, mykey < T, red, colsum + 2 * C + h * HD, chunk0, 3 * (int64_t)C, key0, T);
+  }
 }
 
 // --------------------------------------------------------------- backward: dQ ----
@@ -462,12 +501,12 @@ __global__ __launch_bounds__(256, 2) void flash_bwd_dkdv_kernel(const bf16* __re
 // for them from the dO and O rows (and stores it for the dK / dV kernel), and
 // accumulates dQ^T over the key tiles (64 keys) it sees; K and V tiles stream
 // into a three-stage LDS ring as in the forward kernel.
-__global__ __launch_bounds__(256, 2) void flash_bwd_dq_kernel(const bf16* __restrict__ qkv,
+__global__ __launch_bounds__(256, 3) void flash_bwd_dq_kernel(const bf16* __restrict__ qkv,
                                                               const bf16* __restrict__ y,
                                                               const bf16* __restrict__ dy,
                                                               const float* __restrict__ lse, float* __restrict__ Dd,
                                                               bf16* __restrict__ dqkv, int T, int NH, int C, float sl2,
-                                                              float scale) {
+                                                              float scale, float* __restrict__ colsum) {
   __shared__ __attribute__((aligned(1024))) bf16 smem[3 * ASTAGE];  // [stage][K | V]
   int qt, h, b;
   attn_block(T, NH, qt, h, b);
@@ -572,6 +611,11 @@ __global__ __launch_bounds__(256, 2) void flash_bwd_dq_kernel(const bf16* __rest
         store4(o + t * 32 + 8 * q + 4 * hl, a);
       }
   }
+  if (colsum) {  // Q part of the qkv bias gradient
+    __syncthreads();  // every wave is done with the K / V stages
+    chunk_colsums(dq, scale, qok, reinterpret_cast<float*>(smem), colsum + h * HD, ((int64_t)b * T + q0) / 64,
+                  3 * (int64_t)C, q0, T);
+  }
 }
 
 void attn_fwd_bf16(const void* qkv, void* y, float* lse, int B, int T, int NH, int C, hipStream_t s) {
@@ -581,17 +625,19 @@ void attn_fwd_bf16(const void* qkv, void* y, float* lse, int B, int T, int NH, i
                                         C, scale * kLog2e);
 }
 
-void attn_bwd_bf16(const void* qkv, const void* y, const void* dy, const float* lse, float* Dbuf, void* dqkv, int B,
-                   int T, int NH, int C, hipStream_t s) {
+bool attn_bwd_bf16(const void* qkv, const void* y, const void* dy, const float* lse, float* Dbuf, void* dqkv, int B,
+                   int T, int NH, int C, float* colsum, hipStream_t s) {
+  if (T % 64) colsum = nullptr;  // chunks would straddle sequences
   const float scale = 1.0f / sqrtf((float)HD);
   const unsigned grid = (unsigned)((T + 127) / 128 * NH * B);
   // dQ first: it also writes D = rowsum(dO o O), which dK / dV reads
   flash_bwd_dq_kernel<<<grid, 256, 0, s>>>(reinterpret_cast<const bf16*>(qkv), reinterpret_cast<const bf16*>(y),
                                            reinterpret_cast<const bf16*>(dy), lse, Dbuf,
-                                           reinterpret_cast<bf16*>(dqkv), T, NH, C, scale * kLog2e, scale);
+                                           reinterpret_cast<bf16*>(dqkv), T, NH, C, scale * kLog2e, scale, colsum);
   flash_bwd_dkdv_kernel<<<grid, 256, 0, s>>>(reinterpret_cast<const bf16*>(qkv), reinterpret_cast<const bf16*>(dy),
                                              lse, Dbuf, reinterpret_cast<bf16*>(dqkv), T, NH, C, scale * kLog2e,
-                                             scale);
+                                             scale, colsum);
+  return colsum != nullptr;
 }
 
 // ------------------------------------------------------------------ fp32 path ----

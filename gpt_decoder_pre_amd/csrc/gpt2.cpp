@@ -455,14 +455,17 @@ int backward_impl(gpt2_ctx* c) {
     g = gargs(dres_mid, C, c->W(T_PROJW, l), C, M, C, C, dy, C);
     if (!gemm_site(c, "gemm.bwd.proj.dx", LAYOUT_NN, EPI_ACT, g, a * (2.0 * M * C + (double)C * C)))
       return GPT2_ERR_ARG;
+    bool fused = false;
     {
       Timed tm(c, "attn.bwd", 10.0 * B * c->NH * ((double)T * (T + 1) / 2) * (C / c->NH),
                a * (9.0 * M * C) + 8.0 * M * c->NH);
-      if (c->bf16) attn_bwd_bf16(qkv, atty, dy, lse, c->attnD, dqkv, B, T, c->NH, C, s);
+      // the qkv bias gradient partials come from the attention kernels when
+      // they can form them (64-token chunks within a sequence)
+      if (c->bf16) fused = attn_bwd_bf16(qkv, atty, dy, lse, c->attnD, dqkv, B, T, c->NH, C, part, s);
       else attn_bwd_f32((const float*)qkv, (const float*)atty, (const float*)dy, lse, c->attnD, (float*)dqkv, B, T,
                         c->NH, C, s);
     }
-    ch = colsum_partials<TA>(dqkv, M, 3 * C, part, s);
+    ch = fused ? M / 64 : colsum_partials<TA>(dqkv, M, 3 * C, part, s);
     defer(c->G(T_QKVB, l), nullptr, nullptr, ch, 3 * C, 1);
     // QKV projection: qkv = LN1(x_in) Wqkv^T + bqkv
     if (!wgrad("gemm.bwd.qkv.dw", c->G(T_QKVW, l), dqkv, 3 * C, ln1, C, 3 * C, C)) return GPT2_ERR_ARG;
