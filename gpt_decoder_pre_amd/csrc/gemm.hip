@@ -339,8 +339,11 @@ constexpr bool epi_staged() {
   return EPI == EPI_ACT || EPI == EPI_LOGITS || EPI == EPI_GELU || EPI == EPI_GELU_BWD;
 }
 
+// aux_pre (EPI_GELU_BWD, staged, or null): this wave's aux tile already in
+// registers, chunk `it` of the staging loop below in aux_pre[it].
 template <int EPI, int FM, int FN, bool STAGED>
-DEVI void gemm_epilogue(const GemmArgs& p, f32x16 (&acc)[FM][FN], bf16* region, int mb, int nb, int lane, int split) {
+DEVI void gemm_epilogue(const GemmArgs& p, f32x16 (&acc)[FM][FN], bf16* region, int mb, int nb, int lane, int split,
+                        const u32x4* aux_pre = nullptr) {
   constexpr int WTM = 32 * FM, WTN = 32 * FN;
   const int lc = lane & 31, hl = lane >> 5;
   if constexpr (STAGED) {
@@ -356,7 +359,7 @@ DEVI void gemm_epilogue(const GemmArgs& p, f32x16 (&acc)[FM][FN], bf16* region, 
         const int r = q / CPR, c = q % CPR;
         const int m = mb + r, n = nb + 8 * c;
         *reinterpret_cast<u32x4*>(region + r * SLD + 8 * c) =
-            ld16_or_zero(aux + (int64_t)m * p.ldc + n, m < p.M && n < p.N);
+            aux_pre ? aux_pre[it] : ld16_or_zero(aux + (int64_t)m * p.ldc + n, m < p.M && n < p.N);
         if (it % 8 == 7) __builtin_amdgcn_sched_barrier(0);  // bounded loads in flight
       }
       __builtin_amdgcn_s_waitcnt(0xc07f);
@@ -750,6 +753,26 @@ DEVI void w4_tile(const GemmArgs& p, int tm, int tn, int split, bf16* smem) {
     fb[buf][j] = frag<B_K, BN, BK>(st + BM * BK, wn * WTN + j * 32, kk, lane);
   };
 
+  // GELU': the wave's gelu'(u) tile (read by the epilogue) is loaded into
+  // registers during the k-loop, a share after each k-tile barrier (which
+  // waits for the share before), so that its HBM reads overlap the MFMAs
+  // instead of following them.  Only where the registers allow it.
+  constexpr int CPR = WTN / 8, NA = WTM * CPR / 64;  // 16-byte loads per lane
+  constexpr bool kAuxPre = EPI == EPI_GELU_BWD && 4 * NA <= 48;
+  u32x4 auxr[kAuxPre ? NA : 1];
+  const int am0 = m0 + wm * WTM, an0 = n0 + wn * WTN;
+  auto aux_load = [&](int j) {
+    const int q = j * 64 + lane, r = q / CPR, c = q % CPR;
+    const int m = am0 + r, n = an0 + 8 * c;
+    auxr[j] = ld16_or_zero(reinterpret_cast<const bf16*>(p.aux) + (int64_t)m * p.ldc + n, m < p.M && n < p.N);
+  };
+  auto aux_share = [&](int kt) {  // k-tiles 0 .. nkt-2 each load their share
+    const int lo = kt * NA / (nkt - 1), hi = (kt + 1) * NA / (nkt - 1);
+#pragma unroll
+    for (int j = 0; j < NA; ++j)
+      if (j >= lo && j < hi) aux_load(j);
+  };
+
   // A k-tile's direct loads go out in S chunks: chunk 0 in the last 16-k step
   // of the k-tile two before it (its stage has just been freed), chunks 1..S-1
   // in the first S-1 16-k steps of the k-tile before it (before that k-tile's
@@ -797,6 +820,9 @@ DEVI void w4_tile(const GemmArgs& p, int tm, int tn, int split, bf16* smem) {
           if (g < FM) read_a(cb ^ 1, g, nxt, 0);
           else if (g < FM + FN) read_b(cb ^ 1, g - FM, nxt, 0);
           if (LOAD) dma_chunk(0, g, kt + 2, cur_off);
+          if constexpr (kAuxPre) {
+            if (g == G - 1) aux_share(kt);
+          }
         }
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -829,9 +855,17 @@ DEVI void w4_tile(const GemmArgs& p, int tm, int tn, int split, bf16* smem) {
   if constexpr (kBiasInit) pe.bias = nullptr;  // already in the accumulators
   if constexpr (epi_staged<EPI>()) {
     __syncthreads();  // all waves are done reading the operand stages
-    gemm_epilogue<EPI, FM, FN, true>(pe, acc, smem + wave * WTM * SLD, m0 + wm * WTM, n0 + wn * WTN, lane, split);
+    const u32x4* aux_pre = nullptr;
+    if constexpr (kAuxPre) {
+      if (nkt < 2) {  // no k-tile barrier to carry the loads
+#pragma unroll
+        for (int j = 0; j < NA; ++j) aux_load(j);
+      }
+      aux_pre = auxr;
+    }
+    gemm_epilogue<EPI, FM, FN, true>(pe, acc, smem + wave * WTM * SLD, am0, an0, lane, split, aux_pre);
   } else {
-    gemm_epilogue<EPI, FM, FN, false>(pe, acc, nullptr, m0 + wm * WTM, n0 + wn * WTN, lane, split);
+    gemm_epilogue<EPI, FM, FN, false>(pe, acc, nullptr, am0, an0, lane, split);
   }
 }
 
