@@ -49,7 +49,11 @@ DEVI void lds_barrier() { asm volatile("s_barrier" ::: "memory"); }
 // so that the compiler does not treat it as an LDS store it must wait for
 // before every LDS read (it cannot tell the pipeline stages apart); the
 // kernel orders it with explicit vmcnt waits.  The instruction has no output
-// registers; its address registers are read at issue.
+// registers; its address registers are read at issue.  m0 is set in the same
+// asm block as its one use; nothing else in these kernels reads m0 (the
+// compiler needs it on gfx950 only for LDS DMA builtins, message sends and
+// indexed register moves, none of which they use), so clobbering the
+// reserved register here is safe.
 DEVI void dma16(const void* gptr, uint32_t lds_base) {
   asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds_base), "v"(gptr) : "memory", "m0");
 }
