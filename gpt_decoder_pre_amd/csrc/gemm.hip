@@ -879,22 +879,18 @@ __global__ __launch_bounds__(256, OCC) void gemm_w4_kernel(GemmArgs p) {
 }
 
 // Many independent products in one launch (weight gradients of a whole
-// backward pass: fp32 C += A^T B, both operands stored [K][rows]).  The grid
-// is renumbered per XCD over all tiles, then tile t belongs to the problem
-// with first[j] <= t < first[j + 1]; within a problem tiles are walked as in
-// tile_coords (groups of GM tile-rows).
+// backward pass: fp32 C += A^T B, both operands stored [K][rows]).  Each XCD
+// works through a contiguous range of the tiles; tile t belongs to the
+// problem with first[j] <= t < first[j + 1].
+//
+// Tile t of a grouped launch: its problem's arguments and tile coordinates
+// (within a problem, tiles walk groups of GM tile-rows as in tile_coords).
 template <int BM, int BN>
-__global__ __launch_bounds__(256, 1) void gemm_w4_group_kernel(GemmGroup grp) {
-  __shared__ __attribute__((aligned(1024))) bf16 smem[w4_lds_elems<BM, BN>()];
-  constexpr int NX = 8;
-  const int b = blockIdx.x, nblk = gridDim.x;
-  const int xcd = b % NX, idx = b / NX;
-  const int q = nblk / NX, rem = nblk % NX;
-  const int t = xcd * q + min(xcd, rem) + idx;
+DEVI void group_tile(const GemmGroup& grp, int t, GemmArgs& p, int& tm, int& tn) {
   int j = 0;
   while (j + 1 < grp.n && t >= grp.first[j + 1]) ++j;
   const GemmProblem& pr = grp.prob[j];
-  GemmArgs p = {};
+  p = {};
   p.A = pr.A;
   p.B = pr.B;
   p.C = pr.C;
@@ -913,7 +909,61 @@ __global__ __launch_bounds__(256, 1) void gemm_w4_group_kernel(GemmGroup grp) {
   const int first_m = g * GM;
   const int gm = min(GM, tiles_m - first_m);
   const int w = local - g * GM * tiles_n;
-  w4_tile<false, false, BM, BN, EPI_F32_ACC>(p, first_m + w % gm, w / gm, 0, smem);
+  tm = first_m + w % gm;
+  tn = w / gm;
+}
+
+template <int BM, int BN>
+__global__ __launch_bounds__(256, 1) void gemm_w4_group_kernel(GemmGroup grp) {
+  __shared__ __attribute__((aligned(1024))) bf16 smem[w4_lds_elems<BM, BN>()];
+  // block b runs on XCD b % 8 as that XCD's idx-th workgroup: its whole
+  // tiles first, then the K halves of its split tail tiles
+  const int x = blockIdx.x % kGroupXcds, idx = blockIdx.x / kGroupXcds;
+  const int whole = grp.xcount[x] - grp.xsplit[x];
+  GemmArgs p;
+  int tm, tn;
+  if (idx < whole) {
+    group_tile<BM, BN>(grp, grp.xstart[x] + idx, p, tm, tn);
+    w4_tile<false, false, BM, BN, EPI_F32_ACC>(p, tm, tn, 0, smem);
+  } else if (idx < whole + 2 * grp.xsplit[x]) {
+    const int u = idx - whole, half = u & 1;
+    group_tile<BM, BN>(grp, grp.xstart[x] + whole + (u >> 1), p, tm, tn);
+    // the half's partial goes to a dense BM x BN block of its slot
+    const int64_t slot = (int64_t)x * kGroupTailMax + (u >> 1);
+    p.splits = 2;
+    p.k_per_split = p.K / 2;
+    p.ldc = BN;
+    p.split_stride = (int64_t)BM * BN;
+    p.C = grp.part + slot * 2 * BM * BN - ((int64_t)tm * BM * BN + (int64_t)tn * BN);
+    w4_tile<false, false, BM, BN, EPI_PARTIAL>(p, tm, tn, half, smem);
+  }
+}
+
+// C += first half + second half, for every split tail tile (fixed order)
+template <int BM, int BN>
+__global__ __launch_bounds__(256) void group_tail_reduce_kernel(GemmGroup grp) {
+  const int x = blockIdx.x / kGroupTailMax, i = blockIdx.x % kGroupTailMax;
+  if (i >= grp.xsplit[x]) return;
+  GemmArgs p;
+  int tm, tn;
+  group_tile<BM, BN>(grp, grp.xstart[x] + grp.xcount[x] - grp.xsplit[x] + i, p, tm, tn);
+  const float* p0 = grp.part + ((int64_t)x * kGroupTailMax + i) * 2 * BM * BN;
+  const float* p1 = p0 + BM * BN;
+  float* c = reinterpret_cast<float*>(p.C);
+  for (int e = threadIdx.x; e < BM * BN / 4; e += blockDim.x) {
+    const int r = e / (BN / 4), c4 = (e % (BN / 4)) * 4;
+    const int m = tm * BM + r, n = tn * BN + c4;
+    if (m < p.M && n < p.N) {
+      float a[4], b[4], o[4];
+      load4(p0 + r * BN + c4, a);
+      load4(p1 + r * BN + c4, b);
+      float* cp = c + (int64_t)m * p.N + n;
+      load4(cp, o);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) o[k] += a[k] + b[k];
+      store4(cp, o);
+    }
+  }
 }
 
 // -------------------------------------------------------------- fp32 GEMM ----
@@ -1123,12 +1173,27 @@ bool gemm_group_ok(const GemmProblem& p) {
 // from L2 bounds these long-K products), at a slightly coarser last wave.
 constexpr int kGroupBM = 256, kGroupBN = 256;
 
-void gemm_group_tn_acc(const GemmProblem* probs, int n, hipStream_t s) {
+// CUs per XCD of the current device (256 CUs in 8 XCDs on MI355X)
+static int cus_per_xcd() {
+  static int v = 0;
+  if (v == 0) {
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      cus = 256;
+    v = std::max(1, cus / kGroupXcds);
+  }
+  return v;
+}
+
+void gemm_group_tn_acc(const GemmProblem* probs, int n, float* part, int64_t part_elems, hipStream_t s) {
   auto tiles_of = [](const GemmProblem& p) {
     return ((p.M + kGroupBM - 1) / kGroupBM) * ((p.N + kGroupBN - 1) / kGroupBN);
   };
   int64_t total = 0;
   for (int j = 0; j < n; ++j) total += tiles_of(probs[j]);
+  const int cpx = cus_per_xcd();
+  const int64_t tail_cap = part ? part_elems / (2LL * kGroupBM * kGroupBN) / kGroupXcds : 0;
+  const int tail_max = (int)std::min<int64_t>(kGroupTailMax, tail_cap);
   // launches of at most kGroupMax problems, each cut once its running tile
   // count passes an equal share (a launch with a few tiles would idle most
   // CUs) but never leaving more problems than the later launches can take
@@ -1142,16 +1207,32 @@ void gemm_group_tn_acc(const GemmProblem* probs, int n, hipStream_t s) {
     GemmGroup g;
     g.n = 0;
     int tiles = 0;
+    bool halves_ok = true;  // every K splits into two whole-k-tile halves
     while (g.n < max_count && (g.n < min_count || done < target || li == launches - 1)) {
       g.prob[g.n] = probs[j0 + g.n];
       g.first[g.n] = tiles;
       tiles += tiles_of(probs[j0 + g.n]);
       done += tiles_of(probs[j0 + g.n]);
+      halves_ok = halves_ok && probs[j0 + g.n].K % (2 * kBK) == 0;
       ++g.n;
     }
     j0 += g.n;
     if (tiles == 0) break;
-    gemm_w4_group_kernel<kGroupBM, kGroupBN><<<tiles, 256, 0, s>>>(g);
+    // each XCD takes a contiguous range of tiles; a last round of r <= cpx/2
+    // tiles becomes 2r K halves, which finish in about half a round
+    g.part = part;
+    int per_xcd = 0;
+    bool any_split = false;
+    for (int x = 0; x < kGroupXcds; ++x) {
+      g.xstart[x] = x * (tiles / kGroupXcds) + std::min(x, tiles % kGroupXcds);
+      g.xcount[x] = tiles / kGroupXcds + (x < tiles % kGroupXcds ? 1 : 0);
+      const int r = g.xcount[x] % cpx;
+      g.xsplit[x] = (halves_ok && r > 0 && 2 * r <= cpx && r <= tail_max) ? r : 0;
+      any_split = any_split || g.xsplit[x] > 0;
+      per_xcd = std::max(per_xcd, g.xcount[x] + g.xsplit[x]);
+    }
+    gemm_w4_group_kernel<kGroupBM, kGroupBN><<<per_xcd * kGroupXcds, 256, 0, s>>>(g);
+    if (any_split) group_tail_reduce_kernel<kGroupBM, kGroupBN><<<kGroupXcds * kGroupTailMax, 256, 0, s>>>(g);
   }
 }
 

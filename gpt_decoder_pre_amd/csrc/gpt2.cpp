@@ -490,7 +490,7 @@ int backward_impl(gpt2_ctx* c) {
       by += a * ((double)pr.K * pr.M + (double)pr.K * pr.N) + 8.0 * pr.M * (double)pr.N;
     }
     Timed tm(c, "gemm.bwd.dw", fl, by);
-    gemm_group_tn_acc(dw.data(), (int)dw.size(), s);
+    gemm_group_tn_acc(dw.data(), (int)dw.size(), c->splitk, c->splitk_elems, s);  // split-K scratch is free here
   }
   // embedding: x0 = wte[idx] + wpe[t]
   {

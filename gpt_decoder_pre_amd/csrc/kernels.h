@@ -53,19 +53,29 @@ struct GemmProblem {
   int lda, ldb;
 };
 constexpr int kGroupMax = 64;
+constexpr int kGroupXcds = 8;     // workgroups are dealt to the XCDs round-robin
+constexpr int kGroupTailMax = 16;  // split tail tiles per XCD
 struct GemmGroup {
   GemmProblem prob[kGroupMax];
   int first[kGroupMax];  // first tile of each problem
   int n;
+  // per XCD: its contiguous range of tiles, and how many of the last ones
+  // are computed as two K halves into part (slot x * kGroupTailMax + i, two
+  // 256 x 256 fp32 blocks each) and added into C by a second kernel
+  int xstart[kGroupXcds], xcount[kGroupXcds], xsplit[kGroupXcds];
+  float* part;
 };
 static_assert(sizeof(GemmGroup) <= 4096, "kernel argument size");
 // Whether a problem can go into a grouped launch (K a multiple of 64, M and N
 // multiples of 8).
 bool gemm_group_ok(const GemmProblem& p);
 // All problems in as few launches as kGroupMax allows, with about equal tile
-// counts per launch (256 x 256 tiles, no split-K: each tile adds its whole-K
-// product into C).  Problems must not overlap in C.
-void gemm_group_tn_acc(const GemmProblem* probs, int n, hipStream_t s);
+// counts per launch (256 x 256 tiles; each tile adds its whole-K product into
+// C).  Problems must not overlap in C.  Where an XCD's last round of tiles
+// would leave most of its CUs idle, those tiles run as two K halves into
+// scratch (part, part_elems fp32; null: never) and a fixed-order pass adds
+// both halves into C, so the result stays deterministic.
+void gemm_group_tn_acc(const GemmProblem* probs, int n, float* part, int64_t part_elems, hipStream_t s);
 // Returns false if the shape breaks a kernel precondition.
 bool gemm(GemmLayout layout, GemmEpilogue epi, bool bf16_mode, const GemmArgs& a, hipStream_t s);
 // Same with an explicit bf16 tile configuration (cfg < 0: automatic choice).
