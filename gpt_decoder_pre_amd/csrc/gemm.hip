@@ -939,10 +939,13 @@ __global__ __launch_bounds__(256, 1) void gemm_w4_group_kernel(GemmGroup grp) {
   }
 }
 
-// C += first half + second half, for every split tail tile (fixed order)
+// C += first half + second half, for every split tail tile (fixed order);
+// kTailRowBlocks workgroups per tile, each a band of rows
+constexpr int kTailRowBlocks = 8;
 template <int BM, int BN>
 __global__ __launch_bounds__(256) void group_tail_reduce_kernel(GemmGroup grp) {
-  const int x = blockIdx.x / kGroupTailMax, i = blockIdx.x % kGroupTailMax;
+  const int band = blockIdx.x % kTailRowBlocks, slot = blockIdx.x / kTailRowBlocks;
+  const int x = slot / kGroupTailMax, i = slot % kGroupTailMax;
   if (i >= grp.xsplit[x]) return;
   GemmArgs p;
   int tm, tn;
@@ -950,8 +953,9 @@ __global__ __launch_bounds__(256) void group_tail_reduce_kernel(GemmGroup grp) {
   const float* p0 = grp.part + ((int64_t)x * kGroupTailMax + i) * 2 * BM * BN;
   const float* p1 = p0 + BM * BN;
   float* c = reinterpret_cast<float*>(p.C);
-  for (int e = threadIdx.x; e < BM * BN / 4; e += blockDim.x) {
-    const int r = e / (BN / 4), c4 = (e % (BN / 4)) * 4;
+  constexpr int ROWS = BM / kTailRowBlocks;
+  for (int e = threadIdx.x; e < ROWS * BN / 4; e += blockDim.x) {
+    const int r = band * ROWS + e / (BN / 4), c4 = (e % (BN / 4)) * 4;
     const int m = tm * BM + r, n = tn * BN + c4;
     if (m < p.M && n < p.N) {
       float a[4], b[4], o[4];
@@ -1232,7 +1236,8 @@ void gemm_group_tn_acc(const GemmProblem* probs, int n, float* part, int64_t par
       per_xcd = std::max(per_xcd, g.xcount[x] + g.xsplit[x]);
     }
     gemm_w4_group_kernel<kGroupBM, kGroupBN><<<per_xcd * kGroupXcds, 256, 0, s>>>(g);
-    if (any_split) group_tail_reduce_kernel<kGroupBM, kGroupBN><<<kGroupXcds * kGroupTailMax, 256, 0, s>>>(g);
+    if (any_split)
+      group_tail_reduce_kernel<kGroupBM, kGroupBN><<<kGroupXcds * kGroupTailMax * kTailRowBlocks, 256, 0, s>>>(g);
   }
 }
 
