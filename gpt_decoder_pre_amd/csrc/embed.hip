@@ -128,7 +128,8 @@ __global__ __launch_bounds__(256) void radix_sort_kernel(const int32_t* __restri
 // id.  Thread t holds the E consecutive words t E .. t E + E - 1: stages whose
 // partners are less than E apart run in registers, those within a wavefront
 // exchange by lane shuffles, and only the stages across wavefronts go through
-// LDS with barriers.  For M <= 32768 and ids below 65535.
+// LDS with barriers.  For M <= 32768 and ids below 65535.  Workgroup b sorts
+// the b-th of several independent arrays of M ids (b M .. b M + M - 1).
 constexpr int kBitonicMax = 32768;
 template <int E>
 __global__ __launch_bounds__(1024) void bitonic_sort_kernel(const int32_t* __restrict__ idx, int M, int vocab,
@@ -136,6 +137,9 @@ __global__ __launch_bounds__(1024) void bitonic_sort_kernel(const int32_t* __res
   constexpr int N = 1024 * E;
   __shared__ uint32_t w[N];
   const int t = threadIdx.x;
+  idx += (int64_t)blockIdx.x * M;
+  keys += (int64_t)blockIdx.x * M;
+  vals += (int64_t)blockIdx.x * M;
   uint32_t x[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) {
@@ -200,6 +204,20 @@ __global__ __launch_bounds__(1024) void bitonic_sort_kernel(const int32_t* __res
       vals[i] = (int32_t)(x[e] & 0xffffu);
     }
   }
+}
+
+bool embed_sort_batch(const int32_t* idx, int M, int nb, int vocab, int32_t* keys, int32_t* vals, hipStream_t s) {
+  if (M > kBitonicMax || vocab >= 65535 || nb < 1) return false;
+  const int e = (M + 1023) / 1024;
+#define GPT2_BITONIC(E) bitonic_sort_kernel<E><<<nb, 1024, 0, s>>>(idx, M, vocab, keys, vals)
+  if (e <= 1) GPT2_BITONIC(1);
+  else if (e <= 2) GPT2_BITONIC(2);
+  else if (e <= 4) GPT2_BITONIC(4);
+  else if (e <= 8) GPT2_BITONIC(8);
+  else if (e <= 16) GPT2_BITONIC(16);
+  else GPT2_BITONIC(32);
+#undef GPT2_BITONIC
+  return true;
 }
 
 void embed_sort(const int32_t* idx, int M, int vocab, int id_bits, int32_t* keys_a, int32_t* vals_a,

@@ -18,6 +18,10 @@ using namespace gpt2k;
 
 namespace {
 
+// micro-batches whose ids gpt2_accumulate sorts in one launch (the sort
+// buffers hold this many)
+constexpr int kSortBatch = 4;
+
 enum TensorId {
   T_WTE = 0, T_WPE, T_LN1W, T_LN1B, T_QKVW, T_QKVB, T_PROJW, T_PROJB,
   T_LN2W, T_LN2B, T_FCW, T_FCB, T_FCPW, T_FCPB, T_LNFW, T_LNFB, T_COUNT
@@ -123,6 +127,9 @@ struct gpt2_ctx {
   char* dqkv;
   char* dy;
   float* attnD;
+  // gpt2_accumulate sorts the ids of up to kSortBatch micro-batches in one
+  // launch; presorted >= 0: the backward's sorted ids are slice presorted
+  int presorted = -1;
   float* splitk;
   int64_t splitk_elems;
   float* colpart;
@@ -496,8 +503,15 @@ int backward_impl(gpt2_ctx* c) {
   {
     Timed tm(c, "embed.bwd", 0, 12.0 * M * C);
     embed_wpe_grad(c->dres, c->G(T_WPE), B, T, C, s);
-    embed_sort(c->ids, M, c->Vp, c->id_bits, c->sort_ka, c->sort_va, c->sort_kb, c->sort_vb, s);
-    embed_scatter(c->sort_ka, c->sort_va, c->dres, c->run_sums, c->G(T_WTE), M, C, s);
+    int32_t* keys = c->sort_ka;
+    int32_t* vals = c->sort_va;
+    if (c->presorted >= 0) {
+      keys += (int64_t)c->presorted * M;
+      vals += (int64_t)c->presorted * M;
+    } else {
+      embed_sort(c->ids, M, c->Vp, c->id_bits, c->sort_ka, c->sort_va, c->sort_kb, c->sort_vb, s);
+    }
+    embed_scatter(keys, vals, c->dres, c->run_sums, c->G(T_WTE), M, C, s);
   }
   c->have_fwd = false;
   return hip_status();
@@ -554,8 +568,8 @@ int64_t plan_workspace(gpt2_ctx* c, Plan& p, bool assign) {
   // (M/64 rows of 3C and 4C)
   const int64_t col_elems = (2 * L + 1) * 3 * ((M + 31) / 32) * C + L * ((M + 63) / 64) * 7 * C;
   c->colpart = (float*)at(col_elems * 4);
-  c->sort_ka = (int32_t*)at(M * 4);
-  c->sort_va = (int32_t*)at(M * 4);
+  c->sort_ka = (int32_t*)at(kSortBatch * M * 4);
+  c->sort_va = (int32_t*)at(kSortBatch * M * 4);
   c->sort_kb = (int32_t*)at(M * 4);
   c->sort_vb = (int32_t*)at(M * 4);
   c->run_sums = (float*)at(M * C * 4);
@@ -647,13 +661,23 @@ int gpt2_accumulate(gpt2_ctx* c, const int32_t* d_idx, const int32_t* d_targets,
   if (e != GPT2_OK) return e;
   fill_f32(c->buf.grads, c->n_params, 0.f, c->stream);
   const int64_t stride = (int64_t)B * T;
+  bool batched = false;
   for (int i = 0; i < k; ++i) {
+    // the embedding gradient's sort of the ids, for kSortBatch micro-batches
+    // at a time (one workgroup each, side by side, instead of one per backward)
+    if (i % kSortBatch == 0) {
+      Timed tm(c, "embed.bwd", 0, 8.0 * stride * std::min(kSortBatch, k - i));
+      batched = embed_sort_batch(d_idx + i * stride, (int)stride, std::min(kSortBatch, k - i), c->V, c->sort_ka,
+                                 c->sort_va, c->stream);
+    }
     e = c->bf16 ? forward_impl<bf16>(c, d_idx + i * stride, d_targets + i * stride, B, T, 1.0f / k, d_mean_loss,
                                      i > 0)
                 : forward_impl<float>(c, d_idx + i * stride, d_targets + i * stride, B, T, 1.0f / k, d_mean_loss,
                                       i > 0);
     if (e != GPT2_OK) return e;
+    c->presorted = batched ? i % kSortBatch : -1;
     e = gpt2_backward(c);
+    c->presorted = -1;
     if (e != GPT2_OK) return e;
   }
   return GPT2_OK;

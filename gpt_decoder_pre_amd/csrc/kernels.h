@@ -103,6 +103,11 @@ void embed_fwd(const int32_t* idx, const float* wte, const float* wpe, float* x,
 // digits, one workgroup, keys_b / vals_b as the other buffer).
 void embed_sort(const int32_t* idx, int M, int vocab, int id_bits, int32_t* keys_a, int32_t* vals_a,
                 int32_t* keys_b, int32_t* vals_b, hipStream_t s);
+// The bitonic sort of nb independent arrays of M ids at once (array b at
+// idx + b M into keys / vals + b M; out-of-range ids sort as id 0), one
+// workgroup each.  Returns false (nothing launched) where the bitonic sort
+// does not apply.
+bool embed_sort_batch(const int32_t* idx, int M, int nb, int vocab, int32_t* keys, int32_t* vals, hipStream_t s);
 // dwte[id] += sum over positions with that id of dx[pos] (in position order);
 // run_sums: M x C fp32 scratch.
 void embed_scatter(const int32_t* sorted_ids, const int32_t* sorted_pos, const float* dx, float* run_sums,

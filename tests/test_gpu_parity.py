@@ -174,6 +174,30 @@ def test_embedding_gather_and_sort_are_exact(C, NH, B, T):
     st.close()
 
 
+@pytest.mark.parametrize("k", [4, 5])
+def test_accumulate_sorts_each_micro_batch_exactly(k):
+    """gpt2_accumulate sorts the ids of four micro-batches per launch; the
+    sorted ids left in the first slot are those of micro-batch 0 (k = 4) or
+    of micro-batch 4, the first of the second launch (k = 5)."""
+    import torch
+    B, T = 4, 512
+    s = shape("emb", 1, 12, 768, 1024, 50257, 50304)
+    say(f"accumulate sort k={k} B={B} T={T}")
+    p = init_params(s, 0)
+    batches = batches_for(s, B, T, k, kind="zipf", seed=7)
+    st = gpu_step(s, "bf16", B, p)
+    xs = torch.tensor(np.stack([b[0] for b in batches]), dtype=torch.int32, device="cuda")
+    ys = torch.tensor(np.stack([b[1] for b in batches]), dtype=torch.int32, device="cuda")
+    st.accumulate(xs, ys)
+    torch.cuda.synchronize()
+    assert st.sync_status() == 0
+    x = batches[0 if k == 4 else 4][0].ravel()
+    order = np.argsort(x, kind="stable")
+    assert np.array_equal(st.activation("emb_sorted_pos").cpu().numpy(), order)
+    assert np.array_equal(st.activation("emb_sorted_ids").cpu().numpy(), x[order])
+    st.close()
+
+
 @pytest.mark.parametrize("mode", ["clip", "noclip"])
 def test_clip_decision_matches_oracle(mode):
     s = SHAPES["toy"]
