@@ -280,11 +280,24 @@ __global__ __launch_bounds__(256) void segment_add_kernel(const int32_t* __restr
   for (int c4 = lane; c4 < C4; c4 += 64) {
     float s[4];
     load4(runs + (int64_t)i * C + 4 * c4, s);
-    for (int j = (i / kRun + 1) * kRun; j < M && sid[j] == id; j += kRun) {
-      float v[4];
-      load4(runs + (int64_t)j * C + 4 * c4, v);
+    // the segment's later runs, four at a time (loads together, adds in order)
+    int j = (i / kRun + 1) * kRun;
+    while (j < M && sid[j] == id) {
+      float v[4][4];
+      bool in[4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) s[e] += v[e];
+      for (int u = 0; u < 4; ++u) {
+        const int jj = j + u * kRun;
+        in[u] = jj < M && sid[jj] == id && (u == 0 || in[u - 1]);
+        if (in[u]) load4(runs + (int64_t)jj * C + 4 * c4, v[u]);
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        if (in[u]) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) s[e] += v[u][e];
+        }
+      j += 4 * kRun;
     }
     float* o = dwte + (int64_t)id * C + 4 * c4;
     float a[4];

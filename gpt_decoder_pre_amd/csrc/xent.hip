@@ -175,11 +175,20 @@ void xent_fwd_bwd(TA* logits, const int32_t* targets, float* row_loss, int M, in
 template void xent_fwd_bwd<float>(float*, const int32_t*, float*, int, int, int, float, int*, hipStream_t);
 template void xent_fwd_bwd<bf16>(bf16*, const int32_t*, float*, int, int, int, float, int*, hipStream_t);
 
-__global__ __launch_bounds__(256) void loss_reduce_kernel(const float* __restrict__ row_loss, int M, float scale,
-                                                          int accumulate, float* out) {
+__global__ __launch_bounds__(1024) void loss_reduce_kernel(const float* __restrict__ row_loss, int M, float scale,
+                                                           int accumulate, float* out) {
   __shared__ double red[16];
-  double s = 0.0;
-  for (int i = threadIdx.x; i < M; i += blockDim.x) s += (double)row_loss[i];
+  // four independent partial sums per thread (loads in flight together),
+  // combined in a fixed order
+  double s4[4] = {0.0, 0.0, 0.0, 0.0};
+  const int step = 4 * blockDim.x;
+  int i = threadIdx.x;
+  for (; i + 3 * (int)blockDim.x < M; i += step) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) s4[u] += (double)row_loss[i + u * blockDim.x];
+  }
+  for (int u = 0; i < M; i += blockDim.x, ++u) s4[u] += (double)row_loss[i];
+  double s = (s4[0] + s4[1]) + (s4[2] + s4[3]);
   s = block_sum(s, red);
   if (threadIdx.x == 0) {
     const float v = (float)(s * (double)scale);
@@ -188,7 +197,7 @@ __global__ __launch_bounds__(256) void loss_reduce_kernel(const float* __restric
 }
 
 void loss_reduce(const float* row_loss, int M, float scale, bool accumulate, float* out, hipStream_t s) {
-  loss_reduce_kernel<<<1, 256, 0, s>>>(row_loss, M, scale, accumulate ? 1 : 0, out);
+  loss_reduce_kernel<<<1, 1024, 0, s>>>(row_loss, M, scale, accumulate ? 1 : 0, out);
 }
 
 }  // namespace gpt2k
