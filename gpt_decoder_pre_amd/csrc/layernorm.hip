@@ -1,8 +1,9 @@
 // LayerNorm forward / backward and column-sum reductions (HBM-bound).
 //
-// One wavefront per row: the row stays in registers (float4 per lane, up to
-// C = 2048), mean and variance are wavefront-shuffle reductions, biased
-// variance, eps = 1e-5.  Column sums (gain / shift / bias gradients) are
+// Rows stay in registers (up to C = 2048): the forward takes one or two rows
+// per wavefront in chunks of eight values, the backward one row per
+// wavefront in float4s; mean and variance are wavefront-shuffle reductions,
+// biased variance, eps = 1e-5.  Column sums (gain / shift / bias gradients) are
 // deterministic: fixed row chunks per block write partial rows, a second
 // kernel adds the partials in chunk order.
 #include <algorithm>
@@ -14,73 +15,94 @@ namespace gpt2k {
 
 constexpr float kLnEps = 1e-5f;
 
-// NV = float4 chunks per lane (C <= 256 NV); the rows live in registers.
-// Each wavefront normalises R rows together, so their loads are in flight at
-// once and their shuffle reductions interleave.
-template <typename TA, int NV, int R>
+// Eight consecutive values of a row: two float4 loads; eight outputs in one
+// 16-byte store (bf16) or two (fp32).
+DEVI void store8(float* p, const float o[8]) {
+  store4(p, o);
+  store4(p + 4, o + 4);
+}
+DEVI void store8(bf16* p, const float o[8]) {
+  bf16x8 t;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) t[e] = (bf16)o[e];
+  *reinterpret_cast<bf16x8*>(p) = t;
+}
+
+// Each wavefront normalises R rows together (their loads in flight at once,
+// their shuffle reductions interleaved), the rows in registers.  The R rows
+// are taken end to end as R C / 8 chunks of eight values; lane l holds
+// chunks l, l + 64, ..., NP of them, so every lane reads 32 bytes and writes
+// one 16-byte bf16 group per chunk.  C % 8 == 0.
+template <typename TA, int NP, int R>
 __global__ __launch_bounds__(256) void ln_fwd_kernel(const float* __restrict__ x, const float* __restrict__ w,
                                                      const float* __restrict__ b, TA* __restrict__ y,
                                                      float* __restrict__ mean, float* __restrict__ rstd, int M,
                                                      int C) {
   const int lane = threadIdx.x & 63;
   const int row0 = (blockIdx.x * 4 + (threadIdx.x >> 6)) * R;
-  const int C4 = C >> 2;
-  float v[R][NV][4];
+  const int P = C >> 3;  // chunks per row
+  float v[NP][8];
+  int rk[NP];  // which of the R rows chunk k belongs to (-1: past them)
   float mu[R], rs[R];
 #pragma unroll
-  for (int r = 0; r < R; ++r) {
-    const int row = row0 + r;
-    const float* xr = x + (int64_t)min(row, M - 1) * C;
-    float s = 0.f;
+  for (int r = 0; r < R; ++r) mu[r] = 0.f;
 #pragma unroll
-    for (int i = 0; i < NV; ++i) {
-      const int c4 = lane + i * 64;
+  for (int k = 0; k < NP; ++k) {
+    const int p = lane + 64 * k;
+    const int r = p / P;
+    rk[k] = p < R * P ? r : -1;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) v[r][i][e] = 0.f;
-      if (c4 < C4) {
-        load4(xr + 4 * c4, v[r][i]);
-        s += (v[r][i][0] + v[r][i][1]) + (v[r][i][2] + v[r][i][3]);
-      }
+    for (int e = 0; e < 8; ++e) v[k][e] = 0.f;
+    if (rk[k] >= 0) {
+      const float* xr = x + (int64_t)min(row0 + r, M - 1) * C + 8 * (p - r * P);
+      load4(xr, v[k]);
+      load4(xr + 4, v[k] + 4);
+      const float t = ((v[k][0] + v[k][1]) + (v[k][2] + v[k][3])) + ((v[k][4] + v[k][5]) + (v[k][6] + v[k][7]));
+#pragma unroll
+      for (int rr = 0; rr < R; ++rr)
+        if (rr == r) mu[rr] += t;
     }
-    mu[r] = s;
   }
 #pragma unroll
-  for (int r = 0; r < R; ++r) mu[r] = wave_sum(mu[r]) / (float)C;
-#pragma unroll
   for (int r = 0; r < R; ++r) {
-    float q = 0.f;
+    mu[r] = wave_sum(mu[r]) / (float)C;
+    rs[r] = 0.f;
+  }
 #pragma unroll
-    for (int i = 0; i < NV; ++i) {
-      const int c4 = lane + i * 64;
-      if (c4 < C4) {
+  for (int k = 0; k < NP; ++k) {
+    if (rk[k] >= 0) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float d = v[r][i][e] - mu[r];
-          q += d * d;
+      for (int rr = 0; rr < R; ++rr)
+        if (rr == rk[k]) {
+          float q = 0.f;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const float d = v[k][e] - mu[rr];
+            q += d * d;
+          }
+          rs[rr] += q;
         }
-      }
     }
-    rs[r] = q;
   }
 #pragma unroll
   for (int r = 0; r < R; ++r) rs[r] = 1.0f / sqrtf(wave_sum(rs[r]) / (float)C + kLnEps);
 #pragma unroll
-  for (int i = 0; i < NV; ++i) {
-    const int c4 = lane + i * 64;
-    if (c4 < C4) {
-      float ww[4], bb[4];
-      load4(w + 4 * c4, ww);
-      load4(b + 4 * c4, bb);
+  for (int k = 0; k < NP; ++k) {
+    const int r = rk[k];
+    if (r >= 0 && row0 + r < M) {
+      const int c = 8 * (lane + 64 * k - r * P);
+      float ww[8], bb[8], o[8];
+      load4(w + c, ww);
+      load4(w + c + 4, ww + 4);
+      load4(b + c, bb);
+      load4(b + c + 4, bb + 4);
+      float m = mu[0], sd = rs[0];
 #pragma unroll
-      for (int r = 0; r < R; ++r) {
-        const int row = row0 + r;
-        if (row < M) {
-          float o[4];
+      for (int rr = 1; rr < R; ++rr)
+        if (rr == r) m = mu[rr], sd = rs[rr];
 #pragma unroll
-          for (int e = 0; e < 4; ++e) o[e] = (v[r][i][e] - mu[r]) * rs[r] * ww[e] + bb[e];
-          store4(y + (int64_t)row * C + 4 * c4, o);
-        }
-      }
+      for (int e = 0; e < 8; ++e) o[e] = (v[k][e] - m) * sd * ww[e] + bb[e];
+      store8(y + (int64_t)(row0 + r) * C + c, o);
     }
   }
   if (lane == 0) {
@@ -97,17 +119,16 @@ __global__ __launch_bounds__(256) void ln_fwd_kernel(const float* __restrict__ x
 template <typename TA>
 void layernorm_fwd(const float* x, const float* w, const float* b, TA* y, float* mean, float* rstd, int M,
                    int C, hipStream_t s) {
-  // two rows per wavefront up to C = 1024, one beyond (register budget)
-#define GPT2_LN_FWD(NV, R) ln_fwd_kernel<TA, NV, R><<<(M + 4 * R - 1) / (4 * R), 256, 0, s>>>(x, w, b, y, mean, rstd, M, C)
-  switch ((C / 4 + 63) / 64) {
-    case 1: GPT2_LN_FWD(1, 2); break;
-    case 2: GPT2_LN_FWD(2, 2); break;
-    case 3: GPT2_LN_FWD(3, 2); break;
-    case 4: GPT2_LN_FWD(4, 2); break;
-    case 5: GPT2_LN_FWD(5, 1); break;
-    case 6: GPT2_LN_FWD(6, 1); break;
-    case 7: GPT2_LN_FWD(7, 1); break;
-    default: GPT2_LN_FWD(8, 1); break;
+  // two rows per wavefront up to C = 1024, one beyond (register budget);
+  // NP = chunks of eight per lane over those rows
+#define GPT2_LN_FWD(NP, R) ln_fwd_kernel<TA, NP, R><<<(M + 4 * R - 1) / (4 * R), 256, 0, s>>>(x, w, b, y, mean, rstd, M, C)
+  const int R = C <= 1024 ? 2 : 1;
+  switch ((R * (C / 8) + 63) / 64) {
+    case 1: if (R == 2) GPT2_LN_FWD(1, 2); else GPT2_LN_FWD(1, 1); break;
+    case 2: if (R == 2) GPT2_LN_FWD(2, 2); else GPT2_LN_FWD(2, 1); break;
+    case 3: if (R == 2) GPT2_LN_FWD(3, 2); else GPT2_LN_FWD(3, 1); break;
+    case 4: if (R == 2) GPT2_LN_FWD(4, 2); else GPT2_LN_FWD(4, 1); break;
+    default: GPT2_LN_FWD(4, 1); break;  // C <= 2048
   }
 #undef GPT2_LN_FWD
 }
