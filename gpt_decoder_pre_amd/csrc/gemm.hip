@@ -928,14 +928,20 @@ __global__ __launch_bounds__(256, 1) void gemm_w4_group_kernel(GemmGroup grp) {
   } else if (idx < whole + 2 * grp.xsplit[x]) {
     const int u = idx - whole, half = u & 1;
     group_tile<BM, BN>(grp, grp.xstart[x] + whole + (u >> 1), p, tm, tn);
-    // the half's partial goes to a dense BM x BN block of its slot
+    // the tile as tile (0, 0) of the BM x BN problem at its origin (both
+    // operands are stored [K][rows]), its half's partial into a dense
+    // BM x BN block of its slot
     const int64_t slot = (int64_t)x * kGroupTailMax + (u >> 1);
+    p.A = reinterpret_cast<const bf16*>(p.A) + (int64_t)tm * BM;
+    p.B = reinterpret_cast<const bf16*>(p.B) + (int64_t)tn * BN;
+    p.M = min(BM, p.M - tm * BM);
+    p.N = min(BN, p.N - tn * BN);
     p.splits = 2;
     p.k_per_split = p.K / 2;
     p.ldc = BN;
     p.split_stride = (int64_t)BM * BN;
-    p.C = grp.part + slot * 2 * BM * BN - ((int64_t)tm * BM * BN + (int64_t)tn * BN);
-    w4_tile<false, false, BM, BN, EPI_PARTIAL>(p, tm, tn, half, smem);
+    p.C = grp.part + slot * 2 * BM * BN;
+    w4_tile<false, false, BM, BN, EPI_PARTIAL>(p, 0, 0, half, smem);
   }
 }
 
