@@ -140,6 +140,7 @@ struct ColJobs {
 };
 static_assert(sizeof(ColJobs) <= 4096, "kernel argument size");
 // Launches the jobs (kColJobsMax per launch); each output is written by one job.
+// N a multiple of 4, part and the outputs 16-byte aligned.
 void colpart_reduce_batch(const ColJob* jobs, int n, hipStream_t s);
 // Column sums of an activation matrix (M x N, row-major) into partials [chunks][N];
 // returns the number of chunks.

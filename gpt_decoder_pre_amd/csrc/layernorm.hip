@@ -294,32 +294,35 @@ template int layernorm_bwd<bf16>(const bf16*, const float*, const float*, const 
                                  bool, bf16*, float*, int, int, hipStream_t);
 
 // Many column-partial reductions in one launch: block b belongs to the job j
-// with jobs.first[j] <= b < jobs.first[j + 1] and reduces that job's 64
-// columns the single-job kernel would (same fixed order).
+// with jobs.first[j] <= b < jobs.first[j + 1] and reduces 256 of that job's
+// columns, four per lane (16-byte accesses).  Each of 16 lane groups adds
+// every 16th chunk in chunk order, then the groups are added in order: a
+// fixed order for every column.
 __global__ __launch_bounds__(1024) void colpart_reduce_batch_kernel(ColJobs jobs) {
-  __shared__ float red[16][64];
+  __shared__ f32x4 red[16][64];
   int j = 0;
   while (j + 1 < jobs.n && (int)blockIdx.x >= jobs.first[j + 1]) ++j;
   const ColJob& job = jobs.job[j];
   const int local = blockIdx.x - jobs.first[j];
-  const int cblocks = (job.N + 63) / 64;
+  const int cblocks = (job.N + 255) / 256;  // 256 columns per block, four per lane
   const int k = local / cblocks;
   float* out = job.out[k];
   const int col = threadIdx.x & 63, grp = threadIdx.x >> 6;
-  const int n = (local % cblocks) * 64 + col;
+  const int n = (local % cblocks) * 256 + 4 * col;
   const float* p = job.part + (int64_t)k * job.chunks * job.N;
-  float sum = 0.f;
+  f32x4 sum = {0.f, 0.f, 0.f, 0.f};
   if (n < job.N) {
 #pragma unroll 8
-    for (int c = grp; c < job.chunks; c += 16) sum += p[(int64_t)c * job.N + n];
+    for (int c = grp; c < job.chunks; c += 16) sum += *reinterpret_cast<const f32x4*>(p + (int64_t)c * job.N + n);
   }
   red[grp][col] = sum;
   __syncthreads();
   if (grp == 0 && n < job.N) {
-    float t = 0.f;
+    f32x4 t = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int g = 0; g < 16; ++g) t += red[g][col];
-    out[n] += t;
+    f32x4* o = reinterpret_cast<f32x4*>(out + n);
+    *o += t;
   }
 }
 
@@ -331,7 +334,7 @@ void colpart_reduce_batch(const ColJob* jobs, int n, hipStream_t s) {
     for (int j = 0; j < b.n; ++j) {
       b.job[j] = jobs[j0 + j];
       b.first[j] = blocks;
-      blocks += (b.job[j].N + 63) / 64 * b.job[j].nout;
+      blocks += (b.job[j].N + 255) / 256 * b.job[j].nout;
     }
     colpart_reduce_batch_kernel<<<blocks, 1024, 0, s>>>(b);
   }
