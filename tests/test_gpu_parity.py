@@ -141,6 +141,14 @@ def test_bf16_xl_width():
     _bf16_case(s, 1, 256, 2)
 
 
+def test_bf16_narrow_width_single_k_tile():
+    # C = 64: every product over C is a single 64-wide k-tile (the GELU'
+    # epilogue then loads gelu'(u) after the k-loop), and 256 tokens put every
+    # grouped weight-gradient tile on the split-K tail path
+    s = shape("narrow-L1", 1, 1, 64, 1024, 50257, 50304)
+    _bf16_case(s, 2, 128, 1)
+
+
 def test_bf16_full_gpt2_small_one_sequence():
     s = SHAPES["gpt2-124m"]
     _bf16_case(s, 1, 1024, 1)
