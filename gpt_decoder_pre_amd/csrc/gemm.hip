@@ -1285,12 +1285,12 @@ bool gemm_cfg(int cfg, GemmLayout layout, GemmEpilogue epi, bool bf16_mode, cons
       // two workgroups per CU (config 22) lets one workgroup's prologue and
       // epilogue run beside the other's k-loop (measured on MI355X: 3-10%
       // faster than config 19 and 5-18% faster than the one-workgroup tiles
-      // for these GEMMs).  The residual add (fp32 in and out) takes it at
-      // any K (measured 0.3% faster per step than the 256 x 192 tile for
-      // the K = 4C residual GEMM).  The lm_head product (K = C but 50k
-      // columns) keeps the one-workgroup tiles.
+      // for these GEMMs).  The residual add with K = 4C goes to the rate
+      // model (measured on MI355X: 0.3% faster per step than the 128 x 192
+      // tile).  The lm_head product (K = C but 50k columns) keeps the
+      // one-workgroup tiles.
       const bool heavy_epi = (epi == EPI_ACT && a.bias) || epi == EPI_GELU || epi == EPI_GELU_BWD;
-      const bool short_k = (a.K <= 1024 && epi != EPI_LOGITS) || epi == EPI_RESID;
+      const bool short_k = a.K <= 1024 && epi != EPI_LOGITS;
       if ((heavy_epi || short_k) && gemm_config_usable(22, layout, a)) cfg = 22;
       else if (heavy_epi && gemm_config_usable(19, layout, a)) cfg = 19;
       else cfg = choose_cfg(a, layout);
