@@ -1267,36 +1267,43 @@ void gemm_config_tile(int cfg, int* bm, int* bn) {
   *bn = (cfg >= 0 && cfg < kNumCfg) ? kCfgBN[cfg] : 128;
 }
 
-bool gemm_cfg(int cfg, GemmLayout layout, GemmEpilogue epi, bool bf16_mode, const GemmArgs& a0, hipStream_t s) {
+int gemm_resolve_config(int cfg, GemmLayout layout, GemmEpilogue epi, bool bf16_mode, const GemmArgs& a0) {
   GemmArgs a = a0;
-  if (a.M <= 0 || a.N <= 0 || a.K <= 0) return false;
+  if (a.M <= 0 || a.N <= 0 || a.K <= 0) return -1;
   if (a.splits < 1) a.splits = 1;
   if (a.splits == 1) a.k_per_split = a.K;
-  if (a.splits > 1 && (a.k_per_split % kBK) != 0) return false;
-  if (bf16_mode) {
-    // 16-byte operand accesses: k-contiguous and transposed dims are multiples of 8;
-    // the epilogue writes four columns at a time.
-    if (a.K % 8 || a.N % 8 || a.ldc % 4 || a.lda % 8 || a.ldb % 8) return false;
-    if (layout == LAYOUT_TN && a.M % 8) return false;
-    if (cfg < 0) {
-      // Epilogues that do per-element work on bf16 activations (bias, GELU,
-      // GELU') and short-K products (K <= 1024: a dozen k-tiles per output
-      // tile) are bound by the time outside the k-loop; the 128 x 192 tile at
-      // two workgroups per CU (config 22) lets one workgroup's prologue and
-      // epilogue run beside the other's k-loop (measured on MI355X: 3-10%
-      // faster than config 19 and 5-18% faster than the one-workgroup tiles
-      // for these GEMMs).  The residual add with K = 4C goes to the rate
-      // model (measured on MI355X: 0.3% faster per step than the 128 x 192
-      // tile).  The lm_head product (K = C but 50k columns) keeps the
-      // one-workgroup tiles.
-      const bool heavy_epi = (epi == EPI_ACT && a.bias) || epi == EPI_GELU || epi == EPI_GELU_BWD;
-      const bool short_k = a.K <= 1024 && epi != EPI_LOGITS;
-      if ((heavy_epi || short_k) && gemm_config_usable(22, layout, a)) cfg = 22;
-      else if (heavy_epi && gemm_config_usable(19, layout, a)) cfg = 19;
-      else cfg = choose_cfg(a, layout);
-    }
-    if (!gemm_config_usable(cfg, layout, a)) return false;
+  if (a.splits > 1 && (a.k_per_split % kBK) != 0) return -1;
+  if (!bf16_mode) return kGemmCfgF32;
+  // 16-byte operand accesses: k-contiguous and transposed dims are multiples of 8;
+  // the epilogue writes four columns at a time.
+  if (a.K % 8 || a.N % 8 || a.ldc % 4 || a.lda % 8 || a.ldb % 8) return -1;
+  if (layout == LAYOUT_TN && a.M % 8) return -1;
+  if (cfg < 0) {
+    // Epilogues that do per-element work on bf16 activations (bias, GELU,
+    // GELU') and short-K products (K <= 1024: a dozen k-tiles per output
+    // tile) are bound by the time outside the k-loop; the 128 x 192 tile at
+    // two workgroups per CU (config 22) lets one workgroup's prologue and
+    // epilogue run beside the other's k-loop (measured on MI355X: 3-10%
+    // faster than config 19 and 5-18% faster than the one-workgroup tiles
+    // for these GEMMs).  The residual add with K = 4C goes to the rate
+    // model (measured on MI355X: 0.3% faster per step than the 128 x 192
+    // tile).  The lm_head product (K = C but 50k columns) keeps the
+    // one-workgroup tiles.
+    const bool heavy_epi = (epi == EPI_ACT && a.bias) || epi == EPI_GELU || epi == EPI_GELU_BWD;
+    const bool short_k = a.K <= 1024 && epi != EPI_LOGITS;
+    if ((heavy_epi || short_k) && gemm_config_usable(22, layout, a)) cfg = 22;
+    else if (heavy_epi && gemm_config_usable(19, layout, a)) cfg = 19;
+    else cfg = choose_cfg(a, layout);
   }
+  return gemm_config_usable(cfg, layout, a) ? cfg : -1;
+}
+
+bool gemm_cfg(int cfg, GemmLayout layout, GemmEpilogue epi, bool bf16_mode, const GemmArgs& a0, hipStream_t s) {
+  cfg = gemm_resolve_config(cfg, layout, epi, bf16_mode, a0);
+  if (cfg < 0) return false;
+  GemmArgs a = a0;
+  if (a.splits < 1) a.splits = 1;
+  if (a.splits == 1) a.k_per_split = a.K;
   // column-sum partials: formed in the epilogue by the one-wave-per-SIMD
   // tiles (their wave tiles span whole 64-row chunks), else by a pass over C
   float* const colsum = epi == EPI_GELU_BWD ? a.colsum : nullptr;

@@ -149,6 +149,8 @@ struct gpt2_ctx {
   bool timing = false;
   std::vector<hipEvent_t> ev;
   std::vector<double> ev_flops, ev_bytes;
+  std::vector<const char*> ev_site;  // launch-site name of each bracketed launch
+  std::vector<int> ev_cfg;           // its GEMM tile configuration (-1: not a GEMM)
   size_t ev_used = 0;
   bool ev_overflow = false;
 
@@ -174,12 +176,16 @@ bool site_matches(const char* site, const std::string& prefix) {
   return next == '\0' || next == '.' || prefix.empty();
 }
 
+// GEMM tile configuration recorded for the grouped weight-gradient launch
+constexpr int kCfgGrouped = -2;
+
 // Brackets one launch with HIP events when its site matches the enabled prefix.
+// site must be a string literal (its address is kept).
 struct Timed {
   gpt2_ctx* c;
   bool on = false;
   size_t slot = 0;
-  Timed(gpt2_ctx* ctx, const char* site, double flops, double bytes) : c(ctx) {
+  Timed(gpt2_ctx* ctx, const char* site, double flops, double bytes, int cfg = -1) : c(ctx) {
     if (!c->timing || !site_matches(site, c->site)) return;
     if (c->ev_used * 2 + 2 > c->ev.size()) {
       if (c->ev.size() >= 2 * 8192) {
@@ -195,8 +201,12 @@ struct Timed {
     slot = c->ev_used++;
     c->ev_flops.resize(c->ev_used);
     c->ev_bytes.resize(c->ev_used);
+    c->ev_site.resize(c->ev_used);
+    c->ev_cfg.resize(c->ev_used);
     c->ev_flops[slot] = flops;
     c->ev_bytes[slot] = bytes;
+    c->ev_site[slot] = site;
+    c->ev_cfg[slot] = cfg;
     (void)hipEventRecord(c->ev[2 * slot], c->stream);
     on = true;
   }
@@ -206,7 +216,8 @@ struct Timed {
 };
 
 bool gemm_site(gpt2_ctx* c, const char* site, GemmLayout lay, GemmEpilogue epi, const GemmArgs& a, double bytes) {
-  Timed tm(c, site, 2.0 * a.M * (double)a.N * a.K, bytes);
+  Timed tm(c, site, 2.0 * a.M * (double)a.N * a.K, bytes,
+           c->timing ? gemm_resolve_config(-1, lay, epi, c->bf16, a) : -1);
   return gemm(lay, epi, c->bf16, a, c->stream);
 }
 
@@ -269,8 +280,9 @@ bool weight_grad(gpt2_ctx* c, const char* site, float* out, const void* A, int64
     best_kps = sp > 1 ? kps : K;
   }
   const double bytes = (double)c->act * ((double)K * Mo + (double)K * N) + 8.0 * outn;
+  if (!c->bf16) best_cfg = kGemmCfgF32;
   if (best_splits == 1) {
-    Timed tm(c, site, 2.0 * a.M * (double)a.N * a.K, bytes);
+    Timed tm(c, site, 2.0 * a.M * (double)a.N * a.K, bytes, best_cfg);
     return gemm_cfg(best_cfg, LAYOUT_TN, EPI_F32_ACC, c->bf16, a, c->stream);
   }
   a.C = c->splitk;
@@ -278,7 +290,7 @@ bool weight_grad(gpt2_ctx* c, const char* site, float* out, const void* A, int64
   a.k_per_split = best_kps;
   a.split_stride = outn;
   {
-    Timed tm(c, site, 2.0 * a.M * (double)a.N * a.K, bytes);
+    Timed tm(c, site, 2.0 * a.M * (double)a.N * a.K, bytes, best_cfg);
     if (!gemm_cfg(best_cfg, LAYOUT_TN, EPI_PARTIAL, c->bf16, a, c->stream)) return false;
   }
   splitk_reduce_add(out, c->splitk, best_splits, outn, outn, c->stream);
@@ -496,7 +508,7 @@ int backward_impl(gpt2_ctx* c) {
       fl += 2.0 * pr.M * (double)pr.N * pr.K;
       by += a * ((double)pr.K * pr.M + (double)pr.K * pr.N) + 8.0 * pr.M * (double)pr.N;
     }
-    Timed tm(c, "gemm.bwd.dw", fl, by);
+    Timed tm(c, "gemm.bwd.dw", fl, by, kCfgGrouped);
     gemm_group_tn_acc(dw.data(), (int)dw.size(), c->splitk, c->splitk_elems, s);  // split-K scratch is free here
   }
   // embedding: x0 = wte[idx] + wpe[t]
@@ -798,6 +810,8 @@ int gpt2_timing_enable(gpt2_ctx* c, const char* site) {
   c->ev_overflow = false;
   c->ev_flops.clear();
   c->ev_bytes.clear();
+  c->ev_site.clear();
+  c->ev_cfg.clear();
   c->timing = site != nullptr;
   c->site = site ? site : "";
   return GPT2_OK;
@@ -819,6 +833,53 @@ int gpt2_timing_read(gpt2_ctx* c, double* total_ms, int64_t* launches, double* f
   *flops = f;
   *bytes = b;
   return c->ev_overflow ? GPT2_ERR_ARG : GPT2_OK;
+}
+
+int gpt2_embedding_backward(gpt2_ctx* c, const int32_t* d_idx, const float* d_dx0, int B, int T) {
+  if (!c || !d_idx || !d_dx0) return GPT2_ERR_ARG;
+  if (T > c->cfg.block_size) return GPT2_ERR_SEQ_TOO_LONG;
+  if (B < 1 || T < 1 || B > c->cfg.max_batch) return GPT2_ERR_BATCH;
+  hipStream_t s = c->stream;
+  const int M = B * T;
+  Timed tm(c, "embed.bwd", 0, 12.0 * M * c->C);
+  embed_wpe_grad(d_dx0, c->G(T_WPE), B, T, c->C, s);
+  embed_sort(d_idx, M, c->Vp, c->id_bits, c->sort_ka, c->sort_va, c->sort_kb, c->sort_vb, s);
+  embed_scatter(c->sort_ka, c->sort_va, d_dx0, c->run_sums, c->G(T_WTE), M, c->C, s);
+  return hip_status();
+}
+
+int gpt2_timing_site(gpt2_ctx* c, int index, const char** site, double* total_ms, int64_t* launches,
+                     double* flops, double* bytes, int32_t* gemm_cfg) {
+  if (!c || index < 0 || !site || !total_ms || !launches || !flops || !bytes || !gemm_cfg) return GPT2_ERR_ARG;
+  if (hipStreamSynchronize(c->stream) != hipSuccess) return GPT2_ERR_HIP;
+  // distinct sites in order of first launch
+  std::vector<const char*> names;
+  for (size_t i = 0; i < c->ev_used; ++i) {
+    bool seen = false;
+    for (const char* n : names) seen = seen || strcmp(n, c->ev_site[i]) == 0;
+    if (!seen) names.push_back(c->ev_site[i]);
+  }
+  if ((size_t)index >= names.size()) return GPT2_ERR_ARG;
+  double ms = 0, f = 0, b = 0;
+  int64_t n = 0;
+  int cfg = -1;
+  for (size_t i = 0; i < c->ev_used; ++i) {
+    if (strcmp(names[index], c->ev_site[i]) != 0) continue;
+    float t = 0.f;
+    if (hipEventElapsedTime(&t, c->ev[2 * i], c->ev[2 * i + 1]) != hipSuccess) return GPT2_ERR_HIP;
+    ms += t;
+    f += c->ev_flops[i];
+    b += c->ev_bytes[i];
+    cfg = c->ev_cfg[i];
+    ++n;
+  }
+  *site = names[index];
+  *total_ms = ms;
+  *launches = n;
+  *flops = f;
+  *bytes = b;
+  *gemm_cfg = cfg;
+  return GPT2_OK;
 }
 
 }  // extern "C"

@@ -76,6 +76,11 @@ bool gemm_group_ok(const GemmProblem& p);
 // scratch (part, part_elems fp32; null: never) and a fixed-order pass adds
 // both halves into C, so the result stays deterministic.
 void gemm_group_tn_acc(const GemmProblem* probs, int n, float* part, int64_t part_elems, hipStream_t s);
+// The tile configuration gemm_cfg launches for these arguments (cfg < 0:
+// the automatic choice), kGemmCfgF32 in fp32 mode, or -1 if the shape breaks
+// a kernel precondition.
+constexpr int kGemmCfgF32 = 100;
+int gemm_resolve_config(int cfg, GemmLayout layout, GemmEpilogue epi, bool bf16_mode, const GemmArgs& a);
 // Returns false if the shape breaks a kernel precondition.
 bool gemm(GemmLayout layout, GemmEpilogue epi, bool bf16_mode, const GemmArgs& a, hipStream_t s);
 // Same with an explicit bf16 tile configuration (cfg < 0: automatic choice).

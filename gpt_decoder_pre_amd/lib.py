@@ -34,7 +34,8 @@ ERROR_NAMES = {
 # Every function the header declares.
 EXPORTS = ("gpt2_init", "gpt2_forward_loss", "gpt2_backward", "gpt2_accumulate", "gpt2_clip_adamw_step",
            "gpt2_destroy", "gpt2_sync_status", "gpt2_sync_params", "gpt2_get_step", "gpt2_set_step",
-           "gpt2_tensor_info", "gpt2_activation", "gpt2_timing_enable", "gpt2_timing_read")
+           "gpt2_tensor_info", "gpt2_activation", "gpt2_timing_enable", "gpt2_timing_read", "gpt2_timing_site",
+           "gpt2_embedding_backward")
 
 
 class Gpt2Error(RuntimeError):
@@ -92,6 +93,10 @@ def load_library() -> ctypes.CDLL:
         "gpt2_timing_enable": (I, [P, ctypes.c_char_p]),
         "gpt2_timing_read": (I, [P, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(I64),
                                  ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_double)]),
+        "gpt2_embedding_backward": (I, [P, P, P, I, I]),
+        "gpt2_timing_site": (I, [P, I, ctypes.POINTER(ctypes.c_char_p), ctypes.POINTER(ctypes.c_double),
+                                 ctypes.POINTER(I64), ctypes.POINTER(ctypes.c_double),
+                                 ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int32)]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -163,6 +168,9 @@ class GPT2Step:
         self.bufs = gpt2_buffers(self.params.data_ptr(), self.grads.data_ptr(), self.m.data_ptr(),
                                  self.v.data_ptr(),
                                  self.params_bf16.data_ptr() if self.params_bf16 is not None else None, ws_ptr)
+        if dev.type == "cuda" and dev.index is None:
+            dev = torch.device("cuda", torch.cuda.current_device())
+            self.device = dev
         self.stream = torch.cuda.current_stream(dev)
         ctx = ctypes.c_void_p()
         _check(self.lib.gpt2_init(ctypes.byref(self.cfg), ctypes.byref(self.bufs),
@@ -199,7 +207,27 @@ class GPT2Step:
         return OrderedDict((n, self._flat_view(flat, n)) for n in self.layout)
 
     # ---- the C ABI ----
+    def _check_tokens(self, idx, targets, ndim: int, what: str) -> None:
+        """The C ABI reads int32 (.., T) row-major device arrays: anything else
+        (torch's default int64 ids, a strided view, host memory) would be read
+        as different tokens, so it is refused here."""
+        torch = self.torch
+        for name, t in (("idx", idx), ("targets", targets)):
+            if not isinstance(t, torch.Tensor):
+                raise TypeError(f"{what}: {name} must be a torch tensor")
+            if t.dtype != torch.int32:
+                raise TypeError(f"{what}: {name} must be int32, got {t.dtype}")
+            if t.dim() != ndim:
+                raise ValueError(f"{what}: {name} must have {ndim} dimensions, got shape {tuple(t.shape)}")
+            if not t.is_contiguous():
+                raise ValueError(f"{what}: {name} must be contiguous")
+            if t.device != self.device:
+                raise ValueError(f"{what}: {name} is on {t.device}, the context is on {self.device}")
+        if idx.shape != targets.shape:
+            raise ValueError(f"{what}: idx {tuple(idx.shape)} and targets {tuple(targets.shape)} differ in shape")
+
     def forward_loss(self, idx, targets, loss_scale: float = 1.0):
+        self._check_tokens(idx, targets, 2, "forward_loss")
         B, T = idx.shape
         _check(self.lib.gpt2_forward_loss(self.ctx, ctypes.c_void_p(idx.data_ptr()),
                                           ctypes.c_void_p(targets.data_ptr()), B, T, loss_scale,
@@ -211,6 +239,7 @@ class GPT2Step:
 
     def accumulate(self, idx, targets):
         """idx, targets: int32 device tensors (k, B, T)."""
+        self._check_tokens(idx, targets, 3, "accumulate")
         k, B, T = idx.shape
         _check(self.lib.gpt2_accumulate(self.ctx, ctypes.c_void_p(idx.data_ptr()),
                                         ctypes.c_void_p(targets.data_ptr()), k, B, T,
@@ -222,6 +251,18 @@ class GPT2Step:
                                              ctypes.c_void_p(self.d_norm.data_ptr()),
                                              ctypes.c_void_p(self.d_clipped.data_ptr())), "gpt2_clip_adamw_step")
         return self.d_norm, self.d_clipped
+
+    def embedding_backward(self, idx, dx0) -> None:
+        """idx: int32 (B, T), dx0: fp32 (B, T, C) device tensors; adds the
+        embedding gradient of dx0 into grads (wte and wpe)."""
+        torch = self.torch
+        self._check_tokens(idx, idx, 2, "embedding_backward")
+        B, T = idx.shape
+        if dx0.dtype != torch.float32 or not dx0.is_contiguous() or dx0.device != self.device or \
+                tuple(dx0.shape) != (B, T, self.shape.n_embd):
+            raise ValueError("embedding_backward: dx0 must be a contiguous fp32 (B, T, C) tensor on the device")
+        _check(self.lib.gpt2_embedding_backward(self.ctx, ctypes.c_void_p(idx.data_ptr()),
+                                                ctypes.c_void_p(dx0.data_ptr()), B, T), "gpt2_embedding_backward")
 
     def sync_status(self) -> int:
         return self.lib.gpt2_sync_status(self.ctx)
@@ -252,6 +293,25 @@ class GPT2Step:
         _check(self.lib.gpt2_timing_read(self.ctx, ctypes.byref(ms), ctypes.byref(n), ctypes.byref(fl),
                                          ctypes.byref(by)), "gpt2_timing_read")
         return ms.value, n.value, fl.value, by.value
+
+    def timing_sites(self):
+        """Per-site totals of the recorded launches: list of dicts with the
+        site name, summed ms, launch count, flops, bytes and the GEMM tile
+        configuration of its last launch."""
+        out = []
+        i = 0
+        while True:
+            name, ms, n = ctypes.c_char_p(), ctypes.c_double(), ctypes.c_int64()
+            fl, by, cfg = ctypes.c_double(), ctypes.c_double(), ctypes.c_int32()
+            code = self.lib.gpt2_timing_site(self.ctx, i, ctypes.byref(name), ctypes.byref(ms), ctypes.byref(n),
+                                             ctypes.byref(fl), ctypes.byref(by), ctypes.byref(cfg))
+            if code == GPT2_ERR_ARG:
+                break
+            _check(code, "gpt2_timing_site")
+            out.append({"site": name.value.decode(), "ms": ms.value, "launches": n.value, "flops": fl.value,
+                        "bytes": by.value, "gemm_cfg": cfg.value})
+            i += 1
+        return out
 
     def close(self) -> None:
         if getattr(self, "ctx", None):

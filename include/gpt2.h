@@ -94,7 +94,10 @@ typedef struct {
 typedef struct gpt2_ctx gpt2_ctx;  /* opaque host-side context */
 
 /*
- * Size query and set-up.
+ * Size query and set-up.  The config is the model description of the pages'
+ * GPTConfig (GPT From Scratch, "Problem": GPTConfig() is the 124M shape, the
+ * toy is 4 layers, 4 heads, 128 dims, block 64; AxonLM README, "Model
+ * Scales": the four GPT-2 scales).
  *   bufs == NULL: validate *cfg and fill *sizes only (no HIP call; *out is
  *   left untouched).  Otherwise bind the caller's buffers, zero grads, adam_m
  *   and adam_v on the stream, build the bf16 copy of params (BF16 mode), set
@@ -107,7 +110,11 @@ int gpt2_init(const gpt2_config *cfg, const gpt2_buffers *bufs, void *hip_stream
               gpt2_sizes *sizes, gpt2_ctx **out);
 
 /*
- * Forward pass of B sequences of T tokens and the mean cross-entropy.
+ * Forward pass of B sequences of T tokens and the mean cross-entropy
+ * (hanzo gpt LLM.md, "GPT Model Architecture" and "Transformer Blocks": token
+ * + position embedding, pre-LN blocks, final LayerNorm, tied head; GPT From
+ * Scratch, "Key decisions": tanh-GELU MLP with 4x expansion and the vocabulary
+ * padded to 50,304; "Results": the initial loss sits near ln V).
  *   d_idx, d_targets: int32 device arrays (B, T), row-major.  The position of
  *   token (b, t) is t.  d_idx must stay valid until the matching backward.
  *   *d_loss (device fp32) = loss_scale * mean over the B*T positions of
@@ -125,7 +132,9 @@ int gpt2_forward_loss(gpt2_ctx *ctx, const int32_t *d_idx, const int32_t *d_targ
                       int B, int T, float loss_scale, float *d_loss);
 
 /*
- * Backward of the last forward: ADDS loss_scale * d(loss)/d(param) into grads
+ * Backward of the last forward (the closed-form gradients of every step of
+ * gpt2_forward_loss; the tied head of AxonLM README, "Key Features", makes
+ * wte one tensor with one gradient): ADDS loss_scale * d(loss)/d(param) into grads
  * (the tied wte receives both its lm_head and its embedding gradient).
  * Deterministic: no floating-point atomics; fixed-order reductions.
  * Errors: GPT2_ERR_STATE if no forward is pending.
@@ -133,16 +142,22 @@ int gpt2_forward_loss(gpt2_ctx *ctx, const int32_t *d_idx, const int32_t *d_targ
 int gpt2_backward(gpt2_ctx *ctx);
 
 /*
- * One accumulation: zero grads, then for i < k a forward with loss_scale 1/k
- * on micro-batch i (d_idx + i*B*T, d_targets + i*B*T) followed by its
- * backward.  *d_mean_loss (device fp32) = sum_i loss_i / k.
+ * Gradient accumulation over k equal micro-batches (AxonLM README, "Key
+ * Features": total batch / micro-batch; GPT From Scratch, "Key decisions": it
+ * matches one large batch).  One accumulation: zero grads, then for i < k
+ * a forward with loss_scale 1/k on micro-batch i (d_idx + i*B*T,
+ * d_targets + i*B*T) followed by its backward.  *d_mean_loss (device fp32) = sum_i loss_i / k.
  * Errors: as gpt2_forward_loss; GPT2_ERR_BATCH if k < 1.
  */
 int gpt2_accumulate(gpt2_ctx *ctx, const int32_t *d_idx, const int32_t *d_targets,
                     int k, int B, int T, float *d_mean_loss);
 
 /*
- * Global-norm clip and one AdamW step (the step counter t becomes t + 1):
+ * Global-norm clip and one AdamW step (AxonLM README, "Training Recipe":
+ * clip 1.0, betas 0.9 / 0.95, weight decay 0.1 on 2-D tensors only; GPT From
+ * Scratch, "Key decisions": decay only on parameters of two or more
+ * dimensions; Genesis model card, "Training Features": clip_grad_norm_ at
+ * 1.0) (the step counter t becomes t + 1):
  *   n = ||grads||_2 over every parameter (wte counted once);
  *   c = max_norm / (n + 1e-6); the gradients are scaled by c iff c < 1;
  *   m = beta1 m + (1 - beta1) g;  v = beta2 v + (1 - beta2) g^2;
@@ -190,6 +205,19 @@ int gpt2_tensor_info(const gpt2_config *cfg, int index, const char **name,
 int gpt2_activation(gpt2_ctx *ctx, const char *name, int layer, void **ptr,
                     int64_t *numel, int32_t *dtype);
 
+/* The embedding part of the backward on its own: ADDS to grads
+     wte[idx[b, t]] += dx0[b, t, :]   (summed per id in position order) and
+     wpe[t]        += sum_b dx0[b, t, :]
+   for d_idx int32 (B, T) and d_dx0 fp32 (B, T, C) device arrays, with the
+   same sort and fixed-order segment sums that gpt2_backward uses (the
+   gradient of x0 = wte[idx] + wpe[t]; hanzo gpt LLM.md, "GPT Model
+   Architecture": token + position embeddings).  Ids must lie in
+   [0, vocab_size) (gpt2_forward_loss checks them; this call does not).
+   Errors: GPT2_ERR_ARG, GPT2_ERR_SEQ_TOO_LONG, GPT2_ERR_BATCH as for
+   gpt2_forward_loss. */
+int gpt2_embedding_backward(gpt2_ctx *ctx, const int32_t *d_idx, const float *d_dx0,
+                            int B, int T);
+
 /* Per-launch timing with HIP events on the context's stream.  site: a leading
    run of the dot-separated parts of launch-site names (e.g. "gemm.fwd.lmhead",
    "attn.fwd", "gemm"; "gemm.fwd.fc" does not match "gemm.fwd.fcproj"), or NULL
@@ -199,6 +227,15 @@ int gpt2_activation(gpt2_ctx *ctx, const char *name, int layer, void **ptr,
 int gpt2_timing_enable(gpt2_ctx *ctx, const char *site);
 int gpt2_timing_read(gpt2_ctx *ctx, double *total_ms, int64_t *launches,
                      double *flops, double *bytes);
+
+/* The same record split by launch site: index enumerates the distinct sites
+   of the recorded launches in order of first launch (GPT2_ERR_ARG past the
+   last).  Synchronises the stream.  *site is a static string; *gemm_cfg is
+   the GEMM tile configuration of the site's last launch (0..22 for the bf16
+   tiles, 100 for the fp32 GEMM, -2 for the grouped weight-gradient launch,
+   -1 for a launch that is not a GEMM). */
+int gpt2_timing_site(gpt2_ctx *ctx, int index, const char **site, double *total_ms,
+                     int64_t *launches, double *flops, double *bytes, int32_t *gemm_cfg);
 
 #ifdef __cplusplus
 }

@@ -351,10 +351,12 @@ def adamw(params, grads, m, v, t, lr, beta1=0.9, beta2=0.95, eps=1e-8, weight_de
 
 
 def train_step(params, m, v, t, batches, n_head, lr, beta1=0.9, beta2=0.95, eps=1e-8,
-               weight_decay=0.1, max_norm=1.0):
+               weight_decay=0.1, max_norm=1.0, accumulated=None):
     """Accumulate over the micro-batches, clip, AdamW (t is the new step
-    number).  Returns dict with loss, norm, clipped, grads, params, m, v."""
-    loss, grads = accumulate(params, batches, n_head)
+    number).  Returns dict with loss, norm, clipped, grads, params, m, v.
+    accumulated: an already computed (mean loss, grads) of the same
+    micro-batches (batches is then unused)."""
+    loss, grads = accumulate(params, batches, n_head) if accumulated is None else accumulated
     norm, clipped, cg = clip_by_global_norm(grads, max_norm)
     P, M, Vv = adamw(params, cg, m, v, t, lr, beta1, beta2, eps, weight_decay)
     return {"loss": loss, "norm": norm, "clipped": clipped, "grads": grads,

@@ -71,3 +71,71 @@ def warm_state(grads_ref, seed=7):
         m[n] = (0.5 * r * rng.standard_normal(g.shape)).astype(np.float32)
         v[n] = ((r * r) * (1.0 + rng.random(g.shape))).astype(np.float32)
     return m, v
+
+
+# ---------------------------------------------------------------- per tensor ----
+
+def per_tensor(d):
+    """(name, layer) -> array: one entry per tensor as the model defines them
+    (the stacked per-block arrays split by layer; layer None for the global
+    tensors), so that a gate over one layer is not diluted by the others."""
+    from oracle.gpt2 import BLOCK_NAMES
+    out = {}
+    for n, a in d.items():
+        if n in BLOCK_NAMES:
+            for l in range(a.shape[0]):
+                out[(n, l)] = a[l]
+        else:
+            out[(n, None)] = a
+    return out
+
+
+# ---------------------------------------------------- oracle on many threads ----
+
+def oracle_accumulate_per_sequence(params, x, y, n_head, workers=None):
+    """The oracle's accumulation with every sequence of the (B, T) batch as its
+    own micro-batch (loss scale 1/B): equal to the one batch of B sequences
+    (the accumulation pin).  The sequences run on a thread pool (numpy
+    releases the GIL inside its loops and BLAS calls) with BLAS limited to a
+    share of the cores each; the sums are taken in sequence order.
+    Returns (mean loss, grads)."""
+    import os
+    from concurrent.futures import ThreadPoolExecutor
+
+    from threadpoolctl import threadpool_limits
+
+    from oracle import gpt2 as ref
+    B = x.shape[0]
+    cpus = min(16, len(os.sched_getaffinity(0)))
+    workers = workers or max(1, min(8, B, cpus))
+    with threadpool_limits(max(1, cpus // workers)):
+        with ThreadPoolExecutor(max_workers=workers) as ex:
+            results = list(ex.map(lambda b: ref.loss_and_grads(params, x[b:b + 1], y[b:b + 1], n_head,
+                                                               loss_scale=1.0 / B), range(B)))
+    total = 0.0
+    grads = None
+    for loss, g in results:  # fixed order: sequence 0, 1, ...
+        total += loss
+        if grads is None:
+            grads = g
+        else:
+            for n in grads:
+                grads[n] += g[n]
+    return total, grads
+
+
+def oracle_warm_state(params, s, B, T, steps=10, seed=101, lr=6e-4, kind="zipf"):
+    """A warm AdamW state from the oracle itself: `steps` fp64 oracle training
+    steps from m = v = 0 on other seeded batches.  Returns (params, m, v, t)
+    cast to fp32, to be loaded identically into both paths."""
+    from oracle import gpt2 as ref
+    p = {n: np.asarray(a, np.float64) for n, a in params.items()}
+    m = {n: np.zeros(a.shape) for n, a in p.items()}
+    v = {n: np.zeros(a.shape) for n, a in p.items()}
+    stream = token_stream(kind, steps * B * T + 1, s.vocab_size, seed)
+    for t in range(1, steps + 1):
+        (bx, by), = micro_batches(stream[(t - 1) * B * T:t * B * T + 1], 1, B, T)
+        r = ref.train_step(p, m, v, t, [(bx, by)], s.n_head, lr=lr)
+        p, m, v = r["params"], r["m"], r["v"]
+    f32 = lambda d: {n: np.asarray(a, np.float32) for n, a in d.items()}  # noqa: E731
+    return f32(p), f32(m), f32(v), steps

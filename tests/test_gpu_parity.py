@@ -20,17 +20,21 @@ import pytest
 from gpt2_inputs import SHAPES, init_params, param_shapes
 from oracle import gpt2 as ref
 from tests.gpu_helpers import (BF16_GRAD_COS, BF16_LOSS_ABS, BF16_UPDATE_REL, FP32_REL, batches_for, cos,
-                               gpu_step, host, rel, say, shape, to_dev, warm_state)
+                               gpu_step, host, oracle_accumulate_per_sequence, oracle_warm_state, per_tensor, rel,
+                               say, shape, to_dev, warm_state)
 
 pytestmark = pytest.mark.gpu
 
 
-def _oracle_step(params, batches, n_head, m, v, t, lr, wd=0.1, max_norm=1.0):
-    return ref.train_step(params, m, v, t, batches, n_head, lr=lr, weight_decay=wd, max_norm=max_norm)
+def _oracle_step(params, batches, n_head, m, v, t, lr, wd=0.1, max_norm=1.0, accumulated=None):
+    return ref.train_step(params, m, v, t, batches, n_head, lr=lr, weight_decay=wd, max_norm=max_norm,
+                          accumulated=accumulated)
 
 
-def _run(s, precision, params, batches, warm=None, lr=1e-3, max_norm=1.0):
-    """Returns (loss, grads, norm, clipped, new params) from the GPU."""
+def _run(s, precision, params, batches, warm=None, lr=1e-3, max_norm=1.0, cold=False, sites=False):
+    """Returns a dict with loss, grads, norm, clipped and the new params from
+    the GPU (and, with cold, the params after the same step from m = v = 0
+    at t = 1; with sites, the per-site launch record of the accumulation)."""
     import torch
     B = batches[0][0].shape[0]
     st = gpu_step(s, precision, B, params)
@@ -38,15 +42,73 @@ def _run(s, precision, params, batches, warm=None, lr=1e-3, max_norm=1.0):
         m, v, t = warm
         st.load_state(m, v, t)
     x, y = to_dev(batches)
+    if sites:
+        st.timing_enable("")
     loss = st.accumulate(x, y)
     torch.cuda.synchronize()
-    grads = host(st.to_dict(st.grads))
+    out = {"sites": {r["site"]: r for r in st.timing_sites()} if sites else None}
+    st.timing_enable(None)
+    out["grads"] = host(st.to_dict(st.grads))
     norm, clipped = st.clip_adamw_step(lr, 0.9, 0.95, 1e-8, 0.1, max_norm)
     torch.cuda.synchronize()
     assert st.sync_status() == 0
-    out = (float(loss.item()), grads, float(norm.item()), int(clipped.item()), host(st.to_dict(st.params)))
+    out.update(loss=float(loss.item()), norm=float(norm.item()), clipped=int(clipped.item()),
+               params=host(st.to_dict(st.params)))
+    if cold:  # same gradients (clip + AdamW leave grads untouched), fresh moments
+        st.load_params(params)
+        st.m.zero_()
+        st.v.zero_()
+        st.lib.gpt2_set_step(st.ctx, 0)
+        st.clip_adamw_step(lr, 0.9, 0.95, 1e-8, 0.1, max_norm)
+        torch.cuda.synchronize()
+        out["cold_params"] = host(st.to_dict(st.params))
     st.close()
     return out
+
+
+def _gate_fp32(p, r, g):
+    """fp32 mode: loss, every gradient tensor (per layer) and its update within
+    FP32_REL relative L2 of the oracle."""
+    assert abs(g["loss"] - r["loss"]) / r["loss"] < FP32_REL
+    G, RG = per_tensor(g["grads"]), per_tensor(r["grads"])
+    worst = max((rel(G[k], RG[k]), k) for k in G)
+    say(f"  worst gradient rel err {worst[0]:.2e} {worst[1]}")
+    for k in G:
+        assert rel(G[k], RG[k]) < FP32_REL, (k, rel(G[k], RG[k]))
+    assert abs(g["norm"] - r["norm"]) / r["norm"] < 1e-5
+    assert bool(g["clipped"]) == r["clipped"]
+    P0, P1, R1 = per_tensor(p), per_tensor(g["params"]), per_tensor(r["params"])
+    worst = max((rel(P1[k] - P0[k], R1[k] - P0[k]), k) for k in P0)
+    say(f"  worst update rel err {worst[0]:.2e} {worst[1]}")
+    for k in P0:
+        e = rel(P1[k] - P0[k], R1[k] - P0[k])
+        assert e < FP32_REL, (k, e)
+
+
+def _gate_bf16(p, r, g, cold_ref=None):
+    """bf16 mode: loss within BF16_LOSS_ABS, gradient cosine >= BF16_GRAD_COS
+    and update relative L2 <= BF16_UPDATE_REL for every tensor (per layer for
+    the block tensors); the clip decision equal."""
+    say(f"  loss gpu {g['loss']:.6f} ref {r['loss']:.6f}; norm gpu {g['norm']:.5f} ref {r['norm']:.5f}")
+    assert abs(g["loss"] - r["loss"]) < BF16_LOSS_ABS
+    G, RG = per_tensor(g["grads"]), per_tensor(r["grads"])
+    worst = min((cos(G[k], RG[k]), k) for k in G)
+    say(f"  worst gradient cosine {worst[0]:.5f} {worst[1]} over {len(G)} tensors")
+    for k in G:
+        assert cos(G[k], RG[k]) >= BF16_GRAD_COS, (k, cos(G[k], RG[k]))
+    assert abs(g["norm"] - r["norm"]) / r["norm"] < 2e-2
+    assert bool(g["clipped"]) == r["clipped"]
+    P0, P1, R1 = per_tensor(p), per_tensor(g["params"]), per_tensor(r["params"])
+    worst = max((rel(P1[k] - P0[k], R1[k] - P0[k]), k) for k in P0)
+    say(f"  worst update rel err {worst[0]:.5f} {worst[1]}")
+    for k in P0:
+        e = rel(P1[k] - P0[k], R1[k] - P0[k])
+        assert e <= BF16_UPDATE_REL, (k, e)
+    if cold_ref is not None and "cold_params" in g:
+        # reported, not gated: at t = 1 the update is a sign per element
+        C1, RC = per_tensor(g["cold_params"]), per_tensor(cold_ref)
+        worst = max((rel(C1[k] - P0[k], RC[k] - P0[k]), k) for k in P0)
+        say(f"  cold t=1 update: worst rel err {worst[0]:.4f} {worst[1]} (reported only)")
 
 
 # ------------------------------------------------------------------ fp32 toy ----
@@ -62,7 +124,6 @@ def test_toy_fp32_forward_activations_match_oracle():
     st.forward_loss(xd[0], yd[0], 1.0)
     torch.cuda.synchronize()
     loss_ref, cache = ref.forward(p, x, y, s.n_head)
-    M, C = 4 * 64, s.n_embd
     for l in range(s.n_layer):
         lc = cache["layers"][l]
         checks = {
@@ -87,42 +148,45 @@ def test_toy_fp32_full_step_matches_oracle(B, T, k):
     batches = batches_for(s, B, T, k, kind="uniform")
     loss_r, g_r = ref.accumulate(p, batches, s.n_head)
     m0, v0 = warm_state(g_r)
-    r = _oracle_step(p, batches, s.n_head, m0, v0, 4, lr=1e-3)
-    loss, grads, norm, clipped, p_new = _run(s, "fp32", p, batches, warm=(m0, v0, 3), lr=1e-3)
-    assert abs(loss - r["loss"]) / r["loss"] < FP32_REL
-    for n in p:
-        assert rel(grads[n], r["grads"][n]) < FP32_REL, (n, rel(grads[n], r["grads"][n]))
-    assert abs(norm - r["norm"]) / r["norm"] < 1e-5
-    assert bool(clipped) == r["clipped"]
-    for n in p:
-        d_gpu = p_new[n] - p[n]
-        d_ref = r["params"][n] - p[n]
-        assert rel(d_gpu, d_ref) < FP32_REL, (n, rel(d_gpu, d_ref))
+    r = _oracle_step(p, batches, s.n_head, m0, v0, 4, lr=1e-3, accumulated=(loss_r, g_r))
+    g = _run(s, "fp32", p, batches, warm=(m0, v0, 3), lr=1e-3)
+    _gate_fp32(p, r, g)
+
+
+def test_fp32_gpt2_small_width_one_layer():
+    """fp32 mode at GPT-2 width: C = 768, NH = 12 (head dim 64), the padded
+    50,304 vocabulary; one layer, one 64-token sequence."""
+    s = shape("gpt2-124m-L1", 1, 12, 768, 1024, 50257, 50304)
+    say("fp32 step at GPT-2 width L=1 B=1 T=64")
+    p = init_params(s, 0)
+    batches = batches_for(s, 1, 64, 1, kind="zipf")
+    loss_r, g_r = ref.accumulate(p, batches, s.n_head)
+    m0, v0 = warm_state(g_r)
+    r = _oracle_step(p, batches, s.n_head, m0, v0, 4, lr=6e-4, accumulated=(loss_r, g_r))
+    g = _run(s, "fp32", p, batches, warm=(m0, v0, 3), lr=6e-4)
+    _gate_fp32(p, r, g)
 
 
 # ------------------------------------------------------------- bf16 GPT-2 ----
 
-def _bf16_case(s, B, T, k, seed_w=0, lr=6e-4):
-    say(f"bf16 step {s.name}: L={s.n_layer} C={s.n_embd} NH={s.n_head} B={B} T={T} k={k}")
+def _bf16_case(s, B, T, k, seed_w=0, lr=6e-4, warm="synthetic"):
+    """One bf16 step against the oracle.  warm: "synthetic" (moments drawn from
+    the oracle gradient's scale, t = 10) or "oracle" (parameters and moments
+    after 10 fp64 oracle steps on other seeded batches)."""
+    say(f"bf16 step {s.name}: L={s.n_layer} C={s.n_embd} NH={s.n_head} B={B} T={T} k={k} warm={warm}")
     p = init_params(s, seed_w)
+    if warm == "oracle":
+        p, m0, v0, t0 = oracle_warm_state(p, s, B, T, steps=10, lr=lr)
     batches = batches_for(s, B, T, k, kind="zipf")
     loss_r, g_r = ref.accumulate(p, batches, s.n_head)
-    m0, v0 = warm_state(g_r)
-    r = _oracle_step(p, batches, s.n_head, m0, v0, 11, lr=lr)
-    loss, grads, norm, clipped, p_new = _run(s, "bf16", p, batches, warm=(m0, v0, 10), lr=lr)
-    say(f"  loss gpu {loss:.6f} ref {r['loss']:.6f}; norm gpu {norm:.5f} ref {r['norm']:.5f}")
-    assert abs(loss - r["loss"]) < BF16_LOSS_ABS
-    worst = min((cos(grads[n], r["grads"][n]), n) for n in p)
-    say(f"  worst gradient cosine {worst[0]:.5f} ({worst[1]})")
-    for n in p:
-        assert cos(grads[n], r["grads"][n]) >= BF16_GRAD_COS, (n, cos(grads[n], r["grads"][n]))
-    assert abs(norm - r["norm"]) / r["norm"] < 2e-2
-    assert bool(clipped) == r["clipped"]
-    worst_u = max((rel(p_new[n] - p[n], r["params"][n] - p[n]), n) for n in p)
-    say(f"  worst update rel err {worst_u[0]:.5f} ({worst_u[1]})")
-    for n in p:
-        e = rel(p_new[n] - p[n], r["params"][n] - p[n])
-        assert e <= BF16_UPDATE_REL, (n, e)
+    if warm == "synthetic":
+        m0, v0 = warm_state(g_r)
+        t0 = 10
+    r = _oracle_step(p, batches, s.n_head, m0, v0, t0 + 1, lr=lr, accumulated=(loss_r, g_r))
+    zero = {n: np.zeros(a.shape) for n, a in p.items()}
+    cold = _oracle_step(p, batches, s.n_head, zero, zero, 1, lr=lr, accumulated=(loss_r, g_r))["params"]
+    g = _run(s, "bf16", p, batches, warm=(m0, v0, t0), lr=lr, cold=True)
+    _gate_bf16(p, r, g, cold_ref=cold)
 
 
 def test_bf16_gpt2_small_width_two_layers():
@@ -133,6 +197,11 @@ def test_bf16_gpt2_small_width_two_layers():
 def test_bf16_ragged_sequence_length():
     s = shape("gpt2-124m-L1", 1, 12, 768, 1024, 50257, 50304)
     _bf16_case(s, 2, 200, 1)
+
+
+def test_bf16_ragged_sequence_length_oracle_warm_state():
+    s = shape("gpt2-124m-L1", 1, 12, 768, 1024, 50257, 50304)
+    _bf16_case(s, 1, 200, 1, warm="oracle")
 
 
 def test_bf16_xl_width():
@@ -149,9 +218,61 @@ def test_bf16_narrow_width_single_k_tile():
     _bf16_case(s, 2, 128, 1)
 
 
+def test_bf16_narrow_width_oracle_warm_state():
+    s = shape("narrow-L1", 1, 1, 64, 1024, 50257, 50304)
+    _bf16_case(s, 2, 128, 1, warm="oracle")
+
+
 def test_bf16_full_gpt2_small_one_sequence():
     s = SHAPES["gpt2-124m"]
     _bf16_case(s, 1, 1024, 1)
+
+
+# GEMM tile configurations the benchmarked step runs at M = 16,384 tokens
+# (gemm_resolve_config): 20 = 256 x 256 and 21 = 256 x 192 one-wave-per-SIMD
+# tiles, 22 = 128 x 192 at two workgroups per CU, -2 = the grouped
+# weight-gradient launch.
+BENCH_SITE_CONFIGS = {
+    "gemm.fwd.lmhead": 20, "gemm.bwd.lmhead.dx": 21, "gemm.bwd.fc.dx": 21, "gemm.bwd.qkv.dx": 21,
+    "gemm.fwd.fcproj": 21, "gemm.fwd.qkv": 22, "gemm.fwd.fc": 22, "gemm.fwd.proj": 22,
+    "gemm.bwd.fcproj.dx": 22, "gemm.bwd.proj.dx": 22, "gemm.bwd.dw": -2,
+}
+
+
+def test_bf16_bench_launch_shape_two_layers():
+    """The benchmarked launch shapes (micro-batch 16 x 1024 tokens at GPT-2
+    124M width, vocabulary 50,304), two layers, one micro-batch: every GEMM
+    runs the tile configuration of the benchmark (asserted from the launch
+    record), and the gradients and the update are gated per layer and tensor
+    against the oracle (accumulated sequence by sequence, equal to one batch)."""
+    s = shape("gpt2-124m-L2", 2, 12, 768, 1024, 50257, 50304)
+    B, T, lr = 16, 1024, 6e-4
+    say(f"bf16 bench launch shape: L=2 C=768 B={B} T={T}")
+    p = init_params(s, 0)
+    batches = batches_for(s, B, T, 1, kind="zipf")
+    g = _run(s, "bf16", p, batches, warm=None, lr=lr, sites=True)
+    for site, want in BENCH_SITE_CONFIGS.items():
+        got = g["sites"][site]["gemm_cfg"]
+        say(f"  {site}: config {got}")
+        assert got == want, (site, got, want)
+    x, y = batches[0]
+    loss_r, g_r = oracle_accumulate_per_sequence(p, x, y, s.n_head)
+    m0, v0 = warm_state(g_r)
+    # the GPU step ran from zero moments: rerun its update from the warm state
+    import torch
+    st = gpu_step(s, "bf16", B, p)
+    st.load_state(m0, v0, 10)
+    for n, a in st.to_dict(st.grads).items():
+        a.copy_(torch.as_tensor(g["grads"][n], dtype=torch.float32))
+    st.clip_adamw_step(lr, 0.9, 0.95, 1e-8, 0.1, 1.0)
+    torch.cuda.synchronize()
+    assert st.sync_status() == 0
+    g["params"] = host(st.to_dict(st.params))
+    g["norm"] = float(st.d_norm.item())
+    g["clipped"] = int(st.d_clipped.item())
+    st.close()
+    r = _oracle_step(p, None, s.n_head, m0, v0, 11, lr=lr, accumulated=(loss_r, g_r))
+    _gate_bf16(p, r, g)
 
 
 # ---------------------------------------------------------------- bit-exact ----
@@ -215,9 +336,9 @@ def test_clip_decision_matches_oracle(mode):
     _, g = ref.accumulate(p, batches, s.n_head)
     n = ref.global_norm(g)
     max_norm = 0.5 * n if mode == "clip" else 2.0 * n
-    loss, grads, norm, clipped, _ = _run(s, "fp32", p, batches, max_norm=max_norm)
-    assert clipped == (1 if mode == "clip" else 0)
-    assert abs(norm - n) / n < 1e-5
+    g = _run(s, "fp32", p, batches, max_norm=max_norm)
+    assert g["clipped"] == (1 if mode == "clip" else 0)
+    assert abs(g["norm"] - n) / n < 1e-5
 
 
 # ------------------------------------------------------------- properties ----
@@ -330,4 +451,112 @@ def test_full_bench_config_sampled_rows():
     assert abs(loss - rows.mean()) < 1e-4
     # initial loss sits near ln(V) (+ C * 0.02^2 / 2 from the random lm_head)
     assert abs(loss - math.log(50304)) < 0.3
+    st.close()
+
+
+# ------------------------------------------------------- kernels on their own ----
+
+@pytest.mark.parametrize("B,T", [(16, 1024), (3, 40)])
+def test_embedding_scatter_alone(B, T):
+    """The embedding backward fed dx0 directly (gpt2_embedding_backward):
+    with dx0 = 1 every wte row receives exactly its token count (integers
+    below 2^24 are exact in fp32) and every wpe row exactly B; with a random
+    dx0 the rows match the fp64 sums."""
+    import torch
+    s = shape("emb", 1, 12, 768, 1024, 50257, 50304)
+    say(f"embedding scatter alone B={B} T={T}")
+    p = init_params(s, 0)
+    (x, _), = batches_for(s, B, T, 1, kind="zipf", seed=13)
+    st = gpu_step(s, "bf16", B, p)
+    xd = torch.tensor(x, dtype=torch.int32, device="cuda")
+    ones = torch.ones(B, T, s.n_embd, dtype=torch.float32, device="cuda")
+    st.grads.zero_()
+    st.embedding_backward(xd, ones)
+    torch.cuda.synchronize()
+    assert st.sync_status() == 0
+    G = host(st.to_dict(st.grads))
+    hist = np.bincount(x.ravel(), minlength=s.padded_vocab_size).astype(np.float64)
+    assert np.array_equal(G["wte"], np.repeat(hist[:, None], s.n_embd, axis=1))
+    want_wpe = np.zeros((s.block_size, s.n_embd))
+    want_wpe[:T] = B
+    assert np.array_equal(G["wpe"], want_wpe)
+    for n in G:
+        if n not in ("wte", "wpe"):
+            assert not G[n].any(), n
+    rng = np.random.default_rng(3)
+    dx = rng.standard_normal((B, T, s.n_embd)).astype(np.float32)
+    st.grads.zero_()
+    st.embedding_backward(xd, torch.tensor(dx, device="cuda"))
+    torch.cuda.synchronize()
+    G = host(st.to_dict(st.grads))
+    want = np.zeros((s.padded_vocab_size, s.n_embd))
+    np.add.at(want, x.ravel(), dx.reshape(-1, s.n_embd).astype(np.float64))
+    assert rel(G["wte"], want) < 1e-6
+    want_wpe = np.zeros((s.block_size, s.n_embd))
+    want_wpe[:T] = dx.astype(np.float64).sum(axis=0)
+    assert rel(G["wpe"], want_wpe) < 1e-6
+    st.close()
+
+
+@pytest.mark.parametrize("mode", ["clip", "noclip"])
+def test_adamw_kernel_alone_matches_oracle(mode):
+    """Clip + AdamW alone on identical fp32 (p, g, m, v) at t = 11: m and v
+    within 1e-6 relative of the fp64 oracle per tensor; the update p' - p
+    within 1e-5 (fp32's own rounding of p', about 2^-24 |p| per element, is
+    already ~1e-6 of an update of size lr)."""
+    import torch
+    s = shape("gpt2-124m-L2", 2, 12, 768, 1024, 50257, 50304)
+    say(f"clip + AdamW alone ({mode})")
+    p = init_params(s, 0)
+    rng = np.random.default_rng(21)
+    g = {n: (1e-3 * rng.standard_normal(a.shape)).astype(np.float32) for n, a in p.items()}
+    m0, v0 = warm_state(g, seed=22)
+    n = ref.global_norm(g)
+    max_norm = 0.5 * n if mode == "clip" else 2.0 * n
+    lr = 6e-4
+    st = gpu_step(s, "bf16", 1, p)
+    st.load_state(m0, v0, 10)
+    for name, a in st.to_dict(st.grads).items():
+        a.copy_(torch.as_tensor(g[name]))
+    st.clip_adamw_step(lr, 0.9, 0.95, 1e-8, 0.1, max_norm)
+    torch.cuda.synchronize()
+    assert st.sync_status() == 0
+    P1, M1, V1 = (host(st.to_dict(t)) for t in (st.params, st.m, st.v))
+    assert int(st.d_clipped.item()) == (1 if mode == "clip" else 0)
+    assert abs(float(st.d_norm.item()) - n) / n < 1e-6
+    r = ref.train_step(p, m0, v0, 11, None, s.n_head, lr=lr, max_norm=max_norm, accumulated=(0.0, g))
+    st.close()
+    worst = [0.0, 0.0, 0.0]
+    P0, RP = per_tensor(p), per_tensor(r["params"])
+    for k, (gm, gv) in {k: (per_tensor(M1)[k], per_tensor(V1)[k]) for k in P0}.items():
+        em, ev = rel(gm, per_tensor(r["m"])[k]), rel(gv, per_tensor(r["v"])[k])
+        eu = rel(per_tensor(P1)[k] - P0[k], RP[k] - P0[k])
+        worst = [max(worst[0], em), max(worst[1], ev), max(worst[2], eu)]
+        assert em <= 1e-6 and ev <= 1e-6, (k, em, ev)
+        assert eu <= 1e-5, (k, eu)
+    say(f"  worst rel err: m {worst[0]:.2e}, v {worst[1]:.2e}, update {worst[2]:.2e}")
+
+
+@pytest.mark.parametrize("precision", ["fp32", "bf16"])
+def test_non_finite_values_show_in_the_device_scalars(precision):
+    """A NaN in the weights is not an error: the loss and the gradient norm
+    come back non-finite in the caller's device scalars, as in PyTorch, and
+    the step reports no error code."""
+    import torch
+    if precision == "fp32":
+        s, B, T = SHAPES["toy"], 2, 64
+    else:
+        s, B, T = shape("gpt2-124m-L1", 1, 12, 768, 1024, 50257, 50304), 1, 128
+    say(f"non-finite loss and norm ({precision})")
+    p = init_params(s, 0)
+    p["lnf_w"][3] = np.nan
+    batches = batches_for(s, B, T, 1, kind="uniform" if precision == "fp32" else "zipf")
+    st = gpu_step(s, precision, B, p)
+    x, y = to_dev(batches)
+    loss = float(st.accumulate(x, y).item())
+    st.clip_adamw_step(1e-3)
+    torch.cuda.synchronize()
+    assert st.sync_status() == 0
+    assert not math.isfinite(loss)
+    assert not math.isfinite(float(st.d_norm.item()))
     st.close()

@@ -80,7 +80,7 @@ def test_bf16_forward_stages_against_torch_fp32(C, NH, T, B):
         xout = st.activation("resid", 2 * l + 2).reshape(M, C)
         ref = xmid + g @ Wb["fcproj_w"][l].T + W["fcproj_b"][l]
         assert _max_rel(xout, ref) < 1e-3, ("fcproj gemm + residual", l, _max_rel(xout, ref))
-    lnf = act("lnf", 0, C) if False else st.activation("lnf").float().reshape(M, C)
+    lnf = st.activation("lnf").float().reshape(M, C)
     ref = F.layer_norm(st.activation("resid", 4).reshape(M, C), (C,), W["lnf_w"], W["lnf_b"], eps=1e-5)
     assert _max_rel(lnf, ref) < 1e-2, "lnf"
     # after the forward the logits buffer holds (softmax - onehot) / M

@@ -61,6 +61,7 @@ def _run_all_pins():
     checks = [
         xcheck.test_forward_and_gradients_match_torch_autograd,
         lambda: xcheck.test_clip_and_adamw_match_torch("clip"),
+        lambda: xcheck.test_train_step_matches_torch_accumulate_clip_adamw("clip"),
         pins.test_attention_masked_equals_online_softmax_form,
         pins.test_causality_future_tokens_do_not_change_past_logits,
         pins.test_initial_loss_toy_near_ln65,
@@ -116,4 +117,28 @@ def test_planted_transposed_operand_in_attention_backward_is_caught(monkeypatch)
 def test_planted_sign_error_in_gelu_derivative_is_caught(monkeypatch):
     orig = ref.gelu_grad
     monkeypatch.setattr(ref, "gelu_grad", lambda u: orig(u) - 2 * 0.5 * u * 0 - 0.01 * u)
+    assert not _run_all_pins()
+
+
+def _train_step_unclipped(params, m, v, t, batches, n_head, lr, beta1=0.9, beta2=0.95, eps=1e-8,
+                          weight_decay=0.1, max_norm=1.0, accumulated=None):
+    """Plausible slip: AdamW fed the accumulated gradients instead of the clipped ones."""
+    loss, grads = ref.accumulate(params, batches, n_head) if accumulated is None else accumulated
+    norm, clipped, cg = ref.clip_by_global_norm(grads, max_norm)
+    P, M, Vv = ref.adamw(params, grads, m, v, t, lr, beta1, beta2, eps, weight_decay)
+    return {"loss": loss, "norm": norm, "clipped": clipped, "grads": grads, "params": P, "m": M, "v": Vv}
+
+
+def _train_step_stale_t(params, m, v, t, batches, n_head, lr, beta1=0.9, beta2=0.95, eps=1e-8,
+                        weight_decay=0.1, max_norm=1.0, accumulated=None):
+    """Plausible slip: bias correction with the previous step number."""
+    loss, grads = ref.accumulate(params, batches, n_head) if accumulated is None else accumulated
+    norm, clipped, cg = ref.clip_by_global_norm(grads, max_norm)
+    P, M, Vv = ref.adamw(params, cg, m, v, t - 1, lr, beta1, beta2, eps, weight_decay)
+    return {"loss": loss, "norm": norm, "clipped": clipped, "grads": grads, "params": P, "m": M, "v": Vv}
+
+
+@pytest.mark.parametrize("bad", [_train_step_unclipped, _train_step_stale_t])
+def test_planted_mistake_in_train_step_wiring_is_caught(monkeypatch, bad):
+    monkeypatch.setattr(ref, "train_step", bad)
     assert not _run_all_pins()

@@ -102,3 +102,80 @@ def test_clip_and_adamw_match_torch(max_norm_mode):
         want = t.detach().numpy()
         got = P2[name] if l is None else P2[name][l]
         assert np.max(np.abs(got - want)) < 1e-13, name
+
+
+def _torch_tensors(p):
+    """One fp64 torch tensor per block and name (the per-tensor view the
+    optimizer groups act on), with the (name, layer) key of each."""
+    tensors, names = [], []
+    for name, a in p.items():
+        if name in ref.BLOCK_NAMES:
+            for l in range(a.shape[0]):
+                tensors.append(torch.tensor(a[l], dtype=torch.float64))
+                names.append((name, l))
+        else:
+            tensors.append(torch.tensor(a, dtype=torch.float64))
+            names.append((name, None))
+    return tensors, names
+
+
+def _pick(d, name, l):
+    return d[name] if l is None else d[name][l]
+
+
+@pytest.mark.parametrize("max_norm_mode", ["clip", "noclip"])
+def test_train_step_matches_torch_accumulate_clip_adamw(max_norm_mode):
+    """The whole oracle step (accumulate over two micro-batches, clip, AdamW
+    from a warm state at t = 4) against torch autograd + clip_grad_norm_ +
+    AdamW with per-tensor parameter groups.  With max_norm = 0.5 n the clip
+    fires, so AdamW fed the unclipped gradients or a wrong t would differ."""
+    s, p, x, y = _setup(seed=5, B=4)
+    batches = [(x[:2], y[:2]), (x[2:], y[2:])]
+    _, g_probe = ref.accumulate(p, batches, s.n_head)
+    n = ref.global_norm(g_probe)
+    max_norm = 0.5 * n if max_norm_mode == "clip" else 2.0 * n
+    lr, wd, t_prev = 1e-3, 0.1, 3
+    rng = np.random.default_rng(11)
+    m0 = {k: 0.1 * rng.standard_normal(a.shape) * np.sqrt(np.mean(g_probe[k] ** 2)) for k, a in p.items()}
+    v0 = {k: (1.0 + rng.random(a.shape)) * np.mean(g_probe[k] ** 2) for k, a in p.items()}
+
+    r = ref.train_step(p, m0, v0, t_prev + 1, batches, s.n_head, lr=lr, weight_decay=wd, max_norm=max_norm)
+    # the same step from a precomputed accumulation takes the same path after it
+    r2 = ref.train_step(p, m0, v0, t_prev + 1, None, s.n_head, lr=lr, weight_decay=wd, max_norm=max_norm,
+                        accumulated=ref.accumulate(p, batches, s.n_head))
+    for k in ("params", "m", "v"):
+        for name in p:
+            assert np.array_equal(r[k][name], r2[k][name]), (k, name)
+
+    # torch: loss of each micro-batch / k through autograd, summed gradients
+    P = {k: torch.tensor(a, dtype=torch.float64, requires_grad=True) for k, a in p.items()}
+    total = 0.0
+    for bx, by in batches:
+        lt = torch_loss(P, torch.tensor(bx, dtype=torch.long), torch.tensor(by, dtype=torch.long),
+                        s.n_head) / len(batches)
+        lt.backward()
+        total += lt.item()
+    grads = {k: P[k].grad.numpy() for k in p}
+    tensors, names = _torch_tensors(p)
+    for tt, (name, l) in zip(tensors, names):
+        tt.grad = torch.tensor(_pick(grads, name, l), dtype=torch.float64)
+    tn = torch.nn.utils.clip_grad_norm_(tensors, max_norm)
+    groups = [{"params": [tt for tt in tensors if tt.dim() >= 2], "weight_decay": wd},
+              {"params": [tt for tt in tensors if tt.dim() < 2], "weight_decay": 0.0}]
+    opt = torch.optim.AdamW(groups, lr=lr, betas=(0.9, 0.95), eps=1e-8, foreach=False)
+    for tt, (name, l) in zip(tensors, names):
+        opt.state[tt] = {"step": torch.tensor(float(t_prev)),
+                         "exp_avg": torch.tensor(_pick(m0, name, l), dtype=torch.float64),
+                         "exp_avg_sq": torch.tensor(_pick(v0, name, l), dtype=torch.float64)}
+    opt.step()
+
+    assert abs(r["loss"] - total) < 1e-12
+    assert abs(r["norm"] - tn.item()) < 1e-12 * r["norm"]
+    assert r["clipped"] == (max_norm_mode == "clip")
+    for tt, (name, l) in zip(tensors, names):
+        st = opt.state[tt]
+        assert np.max(np.abs(_pick(r["params"], name, l) - tt.detach().numpy())) < 1e-13, (name, l)
+        assert np.max(np.abs(_pick(r["m"], name, l) - st["exp_avg"].numpy())) < 1e-13, (name, l)
+        assert np.max(np.abs(_pick(r["v"], name, l) - st["exp_avg_sq"].numpy())) < 1e-15, (name, l)
+        # the returned gradients are the accumulated (pre-clip) ones
+        assert np.max(np.abs(_pick(r["grads"], name, l) - _pick(grads, name, l))) < 1e-13, (name, l)
