@@ -28,9 +28,9 @@ PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 METRIC = "train tokens/s + MFU (% bf16 MFMA peak), GPT-2 124M T=1024, 1 MI355X"
 
-# Dominant kernel for the roofline object: the launch site whose kernel takes
-# the most time per step (from the rocprofv3 kernel trace of this command).
-ROOFLINE_SITE = "gemm.fwd.lmhead"
+# Launch sites of one step (gpt2_timing_site names them); the roofline object
+# describes the one that takes the most time per step, ranked from a
+# per-site HIP-event record of one untimed step of this run.
 
 
 def parse():
@@ -39,62 +39,107 @@ def parse():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", default="gpt2-124m")
-    ap.add_argument("--site", default=ROOFLINE_SITE, help="launch-site prefix timed for the roofline")
+    ap.add_argument("--site", default=None, help="launch site timed for the roofline (default: the one that "
+                    "takes the most time per step in a per-site record of one untimed step)")
+    ap.add_argument("--cpu-toy", action="store_true", help="also time the oracle on the toy step")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--breakdown", action="store_true", help="also time every launch site (extra pass)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run a plain 1 GiB device-to-device copy (scale reference for HBM byte counters)")
     return ap.parse_args()
 
 
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_fwd_lmhead_124m_traffic.md")
-TRAFFIC_SOURCE = os.path.join(ROOT, "gpt_decoder_pre_amd", "csrc", "gemm.hip")
+PROFILES = os.path.join(ROOT, "profiles")
+CSRC = os.path.join(ROOT, "gpt_decoder_pre_amd", "csrc")
 
 
 def measured_traffic(site):
-    """HBM bytes per launch of the roofline kernel from the committed rocprofv3
-    FETCH_SIZE / WRITE_SIZE summary, or None if there is none for this site or
-    the kernel source changed since the counters were taken."""
+    """HBM bytes per launch of a launch site's kernel from a committed
+    rocprofv3 FETCH_SIZE / WRITE_SIZE summary (a `traffic: {json}` line in
+    profiles/*_traffic.md), or None if there is none for this site or the
+    kernel source it names changed since the counters were taken."""
+    import glob
     import hashlib
-    try:
-        lines = open(TRAFFIC_FILE).read().splitlines()
-        rec = json.loads(next(l for l in lines if l.startswith("traffic: "))[len("traffic: "):])
-        sha = hashlib.sha256(open(TRAFFIC_SOURCE, "rb").read()).hexdigest()
-    except (OSError, StopIteration, ValueError):
-        return None
-    if rec.get("site") != site or rec.get("source_sha256") != sha:
-        return None
-    return float(rec["bytes_per_launch"])
+    for path in sorted(glob.glob(os.path.join(PROFILES, "*_traffic.md"))):
+        try:
+            lines = open(path).read().splitlines()
+            rec = json.loads(next(l for l in lines if l.startswith("traffic: "))[len("traffic: "):])
+            if rec.get("site") != site:
+                continue
+            sha = hashlib.sha256(open(os.path.join(CSRC, rec["source"]), "rb").read()).hexdigest()
+        except (OSError, StopIteration, ValueError, KeyError):
+            continue
+        if rec.get("source_sha256") == sha:
+            return float(rec["bytes_per_launch"])
+    return None
+
+
+def site_roofline(ms, n, flops, bytes_):
+    """Achieved rate of a site's launches against the MI355X peak that bounds
+    it: dense bf16 MFMA for products, HBM for the streaming kernels."""
+    avg_ms = ms / n
+    if flops > 0:
+        ach = (flops / n) / (avg_ms / 1e3) / 1e12
+        return {"bound": "mfma", "achieved": round(ach, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(ach / PEAK_BF16_TFLOPS, 4)}
+    ach = (bytes_ / n) / (avg_ms / 1e3) / 1e9
+    return {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": round(ach / PEAK_HBM_GBS, 4)}
 
 
 def flops_per_token(s, T):
     """Algorithmic training FLOPs per token: 6 N + 6 L C T (causal attention),
     N = parameters without wpe; and the 6 N + 12 L C T convention."""
     from gpt2_inputs import n_params
-    N = n_params(s) - s.block_size * s.n_embd
+    # wpe (and wte when the head is its own tensor) is a gather, not a product
+    N = n_params(s) - s.block_size * s.n_embd - (0 if s.tied else s.padded_vocab_size * s.n_embd)
     return 6 * N + 6 * s.n_layer * s.n_embd * T, 6 * N + 12 * s.n_layer * s.n_embd * T
 
 
-def cpu_baseline(run, s):
+def _cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(run, s, toy=False):
     """The fp64 oracle as it stands: one full step (forward, backward, clip,
-    AdamW) on one sequence of T tokens of the same workload."""
+    AdamW) on one sequence of T tokens of the same workload (and, with toy,
+    the whole char-level toy step)."""
     import numpy as np
     from threadpoolctl import threadpool_info
 
-    from gpt2_inputs import init_params, micro_batches, token_stream
+    from gpt2_inputs import RUNS, init_params, micro_batches, token_stream
     from oracle import gpt2 as ref
 
+    def one(r, shape, B, T, k):
+        p = init_params(shape, r.seed_weights)
+        b = micro_batches(token_stream(r.tokens, k * B * T + 1, shape.vocab_size, r.seed_tokens), k, B, T)
+        z = {n: np.zeros(a.shape) for n, a in p.items()}
+        t0 = time.perf_counter()
+        ref.train_step(p, z, z, 1, b, shape.n_head, lr=r.lr, weight_decay=r.weight_decay, max_norm=r.max_norm)
+        return time.perf_counter() - t0
+
     T = run.seq_len
-    p = init_params(s, run.seed_weights)
-    b = micro_batches(token_stream(run.tokens, T + 1, s.vocab_size, run.seed_tokens), 1, 1, T)
-    z = {n: np.zeros(a.shape) for n, a in p.items()}
-    t0 = time.perf_counter()
-    ref.train_step(p, z, z, 1, b, s.n_head, lr=run.lr, weight_decay=run.weight_decay, max_norm=run.max_norm)
-    dt = time.perf_counter() - t0
-    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    return {"value": round(T / dt, 2), "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"one fp64 oracle step (forward, backward, clip, AdamW) on 1 x {T} tokens of "
-                      f"{s.name}, {dt:.1f} s wall"}
+    dt = one(run, s, 1, T, 1)
+    info = threadpool_info()
+    threads = max([i.get("num_threads", 1) for i in info] or [1])
+    blas = ", ".join(sorted({f"{i.get('internal_api')} {i.get('version')}" for i in info if i.get("user_api") == "blas"}))
+    out = {"value": round(T / dt, 2), "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+           "sample": f"one fp64 oracle step (forward, backward, clip, AdamW) on 1 x {T} tokens of "
+                     f"{s.name}, {dt:.1f} s wall",
+           "cpu_model": _cpu_model(), "blas": blas or "unknown",
+           "affinity_cpus": len(os.sched_getaffinity(0))}
+    if toy:
+        tr = RUNS["toy"]
+        dtt = one(tr, tr.shape, tr.micro_batch, tr.seq_len, tr.grad_accum)
+        out["toy"] = {"value": round(tr.tokens_per_step / dtt, 1), "unit": "tokens/s",
+                      "sample": f"the whole toy step ({tr.micro_batch} x {tr.seq_len} tokens, fp64), "
+                                f"{dtt * 1e3:.0f} ms wall"}
+    return out
 
 
 def main():
@@ -142,7 +187,21 @@ def main():
     if step.sync_status() != 0:
         raise RuntimeError("device error during warm-up")
 
-    step.timing_enable(args.site)
+    # per-site record of one untimed step: ranks the sites by time per step
+    step.timing_enable("")
+    one_step(0)
+    sites = sorted(step.timing_sites(), key=lambda r: -r["ms"])
+    step.timing_enable(None)
+    site = args.site or sites[0]["site"]
+    step_ms = sum(r["ms"] for r in sites)
+    breakdown = []
+    for r in sites[:12]:
+        e = {"site": r["site"], "ms_per_step": round(r["ms"], 3), "share": round(r["ms"] / step_ms, 4),
+             "launches": r["launches"], "gemm_cfg": r["gemm_cfg"]}
+        e.update(site_roofline(r["ms"], r["launches"], r["flops"], r["bytes"]))
+        breakdown.append(e)
+
+    step.timing_enable(site)
     start = torch.cuda.Event(enable_timing=True)
     stop = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -166,37 +225,13 @@ def main():
 
     roof = None
     if k_n > 0 and k_ms > 0:
-        avg_ms = k_ms / k_n
-        if k_flops > 0:
-            ach = (k_flops / k_n) / (avg_ms / 1e3) / 1e12
-            roof = {"bound": "mfma", "achieved": round(ach, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                    "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": measured_traffic(args.site)}
-            roof["algorithmic_bytes"] = round(k_bytes / k_n)
-        else:
-            ach = (k_bytes / k_n) / (avg_ms / 1e3) / 1e9
-            roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                    "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": None}
-        roof["kernel"] = args.site
+        roof = site_roofline(k_ms, k_n, k_flops, k_bytes)
+        roof["traffic"] = measured_traffic(site)
+        roof["kernel"] = site
         roof["launches"] = int(k_n)
-        roof["avg_launch_us"] = round(1e3 * avg_ms, 2)
-
-    breakdown = None
-    if args.breakdown:
-        breakdown = {}
-        for site in ("gemm.fwd", "gemm.bwd", "attn.fwd", "attn.bwd", "ln.fwd", "ln.bwd", "xent", "embed.bwd",
-                     "norm", "adamw", "gemm.fwd.qkv", "gemm.fwd.proj", "gemm.fwd.fc", "gemm.fwd.fcproj",
-                     "gemm.fwd.lmhead", "gemm.bwd.lmhead.dx", "gemm.bwd.lmhead.dw", "gemm.bwd.fcproj.dx",
-                     "gemm.bwd.fcproj.dw", "gemm.bwd.fc.dx", "gemm.bwd.fc.dw", "gemm.bwd.proj.dx", "gemm.bwd.proj.dw",
-                     "gemm.bwd.qkv.dx", "gemm.bwd.qkv.dw", "gemm.bwd.dw"):
-            step.timing_enable(site)
-            one_step(0)
-            sm, sn, sf, sb = step.timing_read()
-            step.timing_enable(None)
-            if sn == 0:  # e.g. per-site weight gradients when they run as one grouped launch
-                continue
-            breakdown[site] = {"ms_per_step": round(sm, 3), "launches": int(sn),
-                               "tflops": round(sf / max(sm, 1e-9) / 1e9, 1) if sf else None,
-                               "gbs": round(sb / max(sm, 1e-9) / 1e6, 1)}
+        roof["avg_launch_us"] = round(1e3 * k_ms / k_n, 2)
+        roof["algorithmic_per_launch"] = (round(k_flops / k_n) if k_flops > 0 else round(k_bytes / k_n))
+        roof["algorithmic_unit"] = "flop" if k_flops > 0 else "byte"
 
     out = {
         "metric": METRIC,
@@ -212,7 +247,8 @@ def main():
         "dtype": "bf16" if run.precision == "bf16" else "f32",
         "data": "synthetic",
         "config": {"workload": f"{s.name} pre-training step: {s.n_layer} layers, {s.n_head} heads, "
-                               f"{s.n_embd} dims, vocab {s.padded_vocab_size} (tied), Zipf(1.1) token ids",
+                               f"{s.n_embd} dims, vocab {s.padded_vocab_size} "
+                               f"({'tied' if s.tied else 'untied head, no QKV bias'}), Zipf(1.1) token ids",
                    "micro_batch": B, "grad_accum": k, "seq_len": T, "tokens_per_step": k * B * T,
                    "precision": "bf16 compute, fp32 master weights and AdamW moments"},
         "mfu_pct": round(100 * mfu, 2),
@@ -220,12 +256,11 @@ def main():
         "flops_per_token": f_alg,
         "final_loss": round(loss, 5),
         "roofline": roof,
+        "breakdown": breakdown,
     }
-    if breakdown is not None:
-        out["breakdown"] = breakdown
     step.close()
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(run, s)
+        out["cpu_baseline"] = cpu_baseline(run, s, toy=args.cpu_toy or args.config == "gpt2-124m")
     print(json.dumps(out), flush=True)
 
 

@@ -27,6 +27,8 @@ class ModelShape:
     block_size: int
     vocab_size: int          # ids and targets lie in [0, vocab_size)
     padded_vocab_size: int   # rows of wte and width of the softmax
+    tied: bool = True        # lm_head is wte (False: its own (Vp, C) tensor "lm_head")
+    qkv_bias: bool = True    # the QKV projection has a bias
 
     @property
     def head_dim(self) -> int:
@@ -64,6 +66,9 @@ SHAPES = {
     "gpt2-355m": ModelShape("gpt2-355m", 24, 16, 1024, 1024, 50257, 50304),
     "gpt2-774m": ModelShape("gpt2-774m", 36, 20, 1280, 1024, 50257, 50304),
     "gpt2-1558m": ModelShape("gpt2-1558m", 48, 25, 1600, 1024, 50257, 50304),
+    # the untied variant of Genesis ("Model Specs": 163,009,536 parameters at
+    # vocab 50,257; its own lm_head and no QKV bias), vocabulary padded
+    "genesis-163m": ModelShape("genesis-163m", 12, 12, 768, 1024, 50257, 50304, tied=False, qkv_bias=False),
 }
 
 RUNS = {
@@ -72,6 +77,7 @@ RUNS = {
     "gpt2-355m": RunConfig("gpt2-355m", SHAPES["gpt2-355m"], 8, 8, 1024, "bf16", "zipf", 6e-4),
     "gpt2-774m": RunConfig("gpt2-774m", SHAPES["gpt2-774m"], 4, 8, 1024, "bf16", "zipf", 6e-4),
     "gpt2-1558m": RunConfig("gpt2-1558m", SHAPES["gpt2-1558m"], 4, 16, 1024, "bf16", "zipf", 6e-4),
+    "genesis-163m": RunConfig("genesis-163m", SHAPES["genesis-163m"], 16, 4, 1024, "bf16", "zipf", 6e-4),
 }
 
 _GLOBAL_FIRST = ("wte", "wpe")
@@ -99,9 +105,13 @@ def param_shapes(s: ModelShape) -> "OrderedDict[str, tuple]":
     out["wte"] = (s.padded_vocab_size, C)
     out["wpe"] = (s.block_size, C)
     for n in _PER_LAYER:
+        if n == "qkv_b" and not s.qkv_bias:
+            continue
         out[n] = (L,) + per[n]
     out["lnf_w"] = (C,)
     out["lnf_b"] = (C,)
+    if not s.tied:
+        out["lm_head"] = (s.padded_vocab_size, C)
     return out
 
 

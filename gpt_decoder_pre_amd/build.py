@@ -21,7 +21,8 @@ LIB_DIR = os.path.join(PKG, "_lib")
 LIB_PATH = os.path.join(LIB_DIR, "libgpt2.so")
 
 ARCH = "gfx950"
-SOURCES = ["gemm.hip", "attention.hip", "layernorm.hip", "embed.hip", "xent.hip", "optim.hip", "gpt2.cpp"]
+SOURCES = ["gemm.hip", "attention.hip", "layernorm.hip", "embed.hip", "xent.hip", "optim.hip", "infer.hip",
+           "gpt2.cpp", "train.cpp", "infer_ctx.cpp"]
 CXXFLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
     # no packed-fp32 instructions in device code
@@ -39,7 +40,7 @@ def _hipcc() -> str:
 
 
 def _compile(src: str, hipcc: str) -> str:
-    obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
+    obj = os.path.join(BUILD_DIR, src.replace(".", "_") + ".o")
     cmd = [hipcc, *CXXFLAGS, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:

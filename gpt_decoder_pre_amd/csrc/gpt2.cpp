@@ -4,6 +4,8 @@
 
 #include <hip/hip_runtime.h>
 
+#include <cstdint>
+
 #include <algorithm>
 #include <cmath>
 #include <cstdio>
@@ -12,6 +14,7 @@
 #include <vector>
 
 #include "common.h"
+#include "gpt2_train.h"
 #include "kernels.h"
 
 using namespace gpt2k;
@@ -21,20 +24,20 @@ namespace {
 // micro-batches whose ids gpt2_accumulate sorts in one launch (the sort
 // buffers hold this many)
 constexpr int kSortBatch = 4;
-
 enum TensorId {
   T_WTE = 0, T_WPE, T_LN1W, T_LN1B, T_QKVW, T_QKVB, T_PROJW, T_PROJB,
-  T_LN2W, T_LN2B, T_FCW, T_FCB, T_FCPW, T_FCPB, T_LNFW, T_LNFB, T_COUNT
+  T_LN2W, T_LN2B, T_FCW, T_FCB, T_FCPW, T_FCPB, T_LNFW, T_LNFB, T_LMHEAD, T_COUNT
 };
 const char* const kTensorNames[T_COUNT] = {"wte", "wpe", "ln1_w", "ln1_b", "qkv_w", "qkv_b", "proj_w", "proj_b",
                                            "ln2_w", "ln2_b", "fc_w", "fc_b", "fcproj_w", "fcproj_b", "lnf_w",
-                                           "lnf_b"};
+                                           "lnf_b", "lm_head"};
 
 struct TensorDesc {
   int64_t off, numel, per_layer;  // per_layer: elements of one block's tensor (numel if global)
   int ndim;
   int64_t dims[3];
   bool decay;
+  bool present;  // false: the variant has no such tensor (numel 0)
 };
 
 bool config_ok(const gpt2_config& c) {
@@ -42,6 +45,7 @@ bool config_ok(const gpt2_config& c) {
   if (c.n_embd % c.n_head || c.n_embd % 8 || c.n_embd > 2048) return false;
   if (c.padded_vocab_size < c.vocab_size || c.max_batch < 1) return false;
   if (c.precision != GPT2_FP32 && c.precision != GPT2_BF16) return false;
+  if (c.variant & ~(GPT2_UNTIED_HEAD | GPT2_NO_QKV_BIAS)) return false;
   if (c.precision == GPT2_BF16 && (c.n_embd / c.n_head != 64 || c.padded_vocab_size % 8)) return false;
   if (c.precision == GPT2_FP32 && c.n_embd / c.n_head > 256) return false;
   if ((int64_t)c.max_batch * c.block_size > (1 << 26)) return false;
@@ -54,14 +58,16 @@ void tensor_table(const gpt2_config& c, TensorDesc t[T_COUNT]) {
       {2, Vp, C, false},    {2, c.block_size, C, false}, {1, C, 0, true},     {1, C, 0, true},
       {2, 3 * C, C, true},  {1, 3 * C, 0, true},         {2, C, C, true},     {1, C, 0, true},
       {1, C, 0, true},      {1, C, 0, true},             {2, 4 * C, C, true}, {1, 4 * C, 0, true},
-      {2, C, 4 * C, true},  {1, C, 0, true},             {1, C, 0, false},    {1, C, 0, false}};
+      {2, C, 4 * C, true},  {1, C, 0, true},             {1, C, 0, false},    {1, C, 0, false},
+      {2, Vp, C, false}};
   int64_t off = 0;
   for (int i = 0; i < T_COUNT; ++i) {
     const int64_t per = sh[i].ndim == 2 ? sh[i].d0 * sh[i].d1 : sh[i].d0;
     TensorDesc& d = t[i];
+    d.present = !((i == T_QKVB && (c.variant & GPT2_NO_QKV_BIAS)) || (i == T_LMHEAD && !(c.variant & GPT2_UNTIED_HEAD)));
     d.off = off;
-    d.per_layer = per;
-    d.numel = sh[i].layer ? per * L : per;
+    d.per_layer = d.present ? per : 0;
+    d.numel = d.present ? (sh[i].layer ? per * L : per) : 0;
     d.decay = sh[i].ndim >= 2;  // weight decay on tensors of two or more dimensions
     if (sh[i].layer) {
       d.ndim = sh[i].ndim + 1;
@@ -103,6 +109,8 @@ struct gpt2_ctx {
   int64_t Mmax;
   int L, C, NH, Vp, V;
   int id_bits;
+  int head;        // tensor of the lm_head weight: T_WTE (tied) or T_LMHEAD
+  bool qkv_bias;   // the QKV projection has a bias
 
   // workspace regions
   float* res;
@@ -330,7 +338,7 @@ int forward_impl(gpt2_ctx* c, const int32_t* d_idx, const int32_t* d_tgt, int B,
                         c->ln1_rstd + (int64_t)l * c->Mmax, M, C, s);
     }
     GemmArgs g = gargs(ln1, C, c->W(T_QKVW, l), C, M, 3 * C, C, qkv, 3 * C);
-    g.bias = c->P(T_QKVB, l);
+    g.bias = c->qkv_bias ? c->P(T_QKVB, l) : nullptr;
     if (!gemm_site(c, "gemm.fwd.qkv", LAYOUT_NT, EPI_ACT, g, a * ((double)M * C + 3.0 * C * C + 3.0 * M * C)))
       return GPT2_ERR_ARG;
     {
@@ -365,7 +373,7 @@ int forward_impl(gpt2_ctx* c, const int32_t* d_idx, const int32_t* d_tgt, int B,
     Timed tm(c, "ln.fwd", 0, (double)M * C * (4 + a) + 8.0 * M);
     layernorm_fwd<TA>(c->resid(2 * L), c->P(T_LNFW), c->P(T_LNFB), (TA*)c->lnf, c->lnf_mean, c->lnf_rstd, M, C, s);
   }
-  GemmArgs g = gargs(c->lnf, C, c->W(T_WTE), C, M, Vp, C, c->logits, Vp);
+  GemmArgs g = gargs(c->lnf, C, c->W(c->head), C, M, Vp, C, c->logits, Vp);
   if (!gemm_site(c, "gemm.fwd.lmhead", LAYOUT_NT, EPI_LOGITS, g, a * ((double)M * C + (double)Vp * C + (double)M * Vp)))
     return GPT2_ERR_ARG;
   {
@@ -422,10 +430,10 @@ int backward_impl(gpt2_ctx* c) {
   // dh: gradient at a LayerNorm output, in the activation type (bf16 in bf16
   // mode, like every other matmul output of the mixed-precision step)
   TA* dh = (TA*)c->dh;
-  GemmArgs g = gargs(c->logits, Vp, c->W(T_WTE), C, M, C, Vp, dh, C);
+  GemmArgs g = gargs(c->logits, Vp, c->W(c->head), C, M, C, Vp, dh, C);
   if (!gemm_site(c, "gemm.bwd.lmhead.dx", LAYOUT_NN, EPI_ACT, g, a * ((double)M * Vp + (double)Vp * C + (double)M * C)))
     return GPT2_ERR_ARG;
-  if (!wgrad("gemm.bwd.lmhead.dw", c->G(T_WTE), c->logits, Vp, c->lnf, C, Vp, C)) return GPT2_ERR_ARG;
+  if (!wgrad("gemm.bwd.lmhead.dw", c->G(c->head), c->logits, Vp, c->lnf, C, Vp, C)) return GPT2_ERR_ARG;
   int ch;
   {
     Timed tm(c, "ln.bwd", 0, (double)M * C * (8 + 2 * a) + 8.0 * M);
@@ -480,12 +488,15 @@ int backward_impl(gpt2_ctx* c) {
                a * (9.0 * M * C) + 8.0 * M * c->NH);
       // the qkv bias gradient partials come from the attention kernels when
       // they can form them (64-token chunks within a sequence)
-      if (c->bf16) fused = attn_bwd_bf16(qkv, atty, dy, lse, c->attnD, dqkv, B, T, c->NH, C, part, s);
+      if (c->bf16)
+        fused = attn_bwd_bf16(qkv, atty, dy, lse, c->attnD, dqkv, B, T, c->NH, C, c->qkv_bias ? part : nullptr, s);
       else attn_bwd_f32((const float*)qkv, (const float*)atty, (const float*)dy, lse, c->attnD, (float*)dqkv, B, T,
                         c->NH, C, s);
     }
-    ch = fused ? M / 64 : colsum_partials<TA>(dqkv, M, 3 * C, part, s);
-    defer(c->G(T_QKVB, l), nullptr, nullptr, ch, 3 * C, 1);
+    if (c->qkv_bias) {
+      ch = fused ? M / 64 : colsum_partials<TA>(dqkv, M, 3 * C, part, s);
+      defer(c->G(T_QKVB, l), nullptr, nullptr, ch, 3 * C, 1);
+    }
     // QKV projection: qkv = LN1(x_in) Wqkv^T + bqkv
     if (!wgrad("gemm.bwd.qkv.dw", c->G(T_QKVW, l), dqkv, 3 * C, ln1, C, 3 * C, C)) return GPT2_ERR_ARG;
     g = gargs(dqkv, 3 * C, c->W(T_QKVW, l), C, M, C, 3 * C, dh, C);
@@ -606,6 +617,8 @@ void fill_layout(gpt2_ctx* c, const gpt2_config& cfg) {
   int bits = 1;
   while ((1 << bits) < cfg.padded_vocab_size) ++bits;
   c->id_bits = bits;
+  c->head = (cfg.variant & GPT2_UNTIED_HEAD) ? T_LMHEAD : T_WTE;
+  c->qkv_bias = !(cfg.variant & GPT2_NO_QKV_BIAS);
 }
 
 }  // namespace
@@ -695,33 +708,50 @@ int gpt2_accumulate(gpt2_ctx* c, const int32_t* d_idx, const int32_t* d_targets,
   return GPT2_OK;
 }
 
-int gpt2_clip_adamw_step(gpt2_ctx* c, float lr, float beta1, float beta2, float eps, float weight_decay,
-                         float max_norm, float* d_norm, int32_t* d_clipped) {
-  if (!c || !d_norm || !d_clipped) return GPT2_ERR_ARG;
-  hipStream_t s = c->stream;
-  {
-    Timed tm(c, "norm", 0, 4.0 * c->n_params);
-    const int nblk = sumsq_partials(c->buf.grads, c->n_params, c->norm_part, s);
-    clip_finalize(c->norm_part, nblk, max_norm, d_norm, d_clipped, c->clip_scale, s);
-  }
-  c->step += 1;
-  const double bc1 = 1.0 - std::pow((double)beta1, (double)c->step);
-  const double bc2 = 1.0 - std::pow((double)beta2, (double)c->step);
+namespace {
+
+DecaySegments decay_segments(const TensorDesc t[T_COUNT], int64_t n_params) {
   DecaySegments seg;
   memset(&seg, 0, sizeof(seg));
   for (int i = 0; i < T_COUNT; ++i) {
-    if (seg.n == 0 || seg.decay[seg.n - 1] != (int)c->t[i].decay) {
-      seg.start[seg.n] = c->t[i].off;
-      seg.decay[seg.n] = c->t[i].decay;
+    if (!t[i].present) continue;
+    if (seg.n == 0 || seg.decay[seg.n - 1] != (int)t[i].decay) {
+      seg.start[seg.n] = t[i].off;
+      seg.decay[seg.n] = t[i].decay;
       ++seg.n;
     }
   }
-  seg.start[seg.n] = c->n_params;
+  seg.start[seg.n] = n_params;
+  return seg;
+}
+
+// Norm, clip decision and AdamW at step t on the flat vectors of bufs, with
+// the norm partials and the clip factor in (norm_part, clip_scale).
+void clip_adamw_launch(gpt2_ctx* c, const gpt2_buffers& b, int64_t n_params, const DecaySegments& seg, int64_t t,
+                       double* norm_part, float* clip_scale, float lr, float beta1, float beta2, float eps,
+                       float weight_decay, float max_norm, float* d_norm, int32_t* d_clipped, hipStream_t s) {
   {
-    Timed tm(c, "adamw", 0, (c->bf16 ? 30.0 : 28.0) * c->n_params);
-    adamw(c->buf.params, c->buf.grads, c->buf.adam_m, c->buf.adam_v, c->buf.params_bf16, c->n_params, seg,
-          c->clip_scale, lr, beta1, beta2, eps, weight_decay, (float)(1.0 / bc1), (float)(1.0 / bc2), s);
+    Timed tm(c, "norm", 0, 4.0 * n_params);
+    const int nblk = sumsq_partials(b.grads, n_params, norm_part, s);
+    clip_finalize(norm_part, nblk, max_norm, d_norm, d_clipped, clip_scale, s);
   }
+  const double bc1 = 1.0 - std::pow((double)beta1, (double)t);
+  const double bc2 = 1.0 - std::pow((double)beta2, (double)t);
+  {
+    Timed tm(c, "adamw", 0, (b.params_bf16 ? 30.0 : 28.0) * n_params);
+    adamw(b.params, b.grads, b.adam_m, b.adam_v, b.params_bf16, n_params, seg, clip_scale, lr, beta1, beta2, eps,
+          weight_decay, (float)(1.0 / bc1), (float)(1.0 / bc2), s);
+  }
+}
+
+}  // namespace
+
+int gpt2_clip_adamw_step(gpt2_ctx* c, float lr, float beta1, float beta2, float eps, float weight_decay,
+                         float max_norm, float* d_norm, int32_t* d_clipped) {
+  if (!c || !d_norm || !d_clipped) return GPT2_ERR_ARG;
+  c->step += 1;
+  clip_adamw_launch(c, c->buf, c->n_params, decay_segments(c->t, c->n_params), c->step, c->norm_part, c->clip_scale,
+                    lr, beta1, beta2, eps, weight_decay, max_norm, d_norm, d_clipped, c->stream);
   return hip_status();
 }
 
@@ -760,15 +790,22 @@ int gpt2_set_step(gpt2_ctx* c, int64_t t) {
 
 int gpt2_tensor_info(const gpt2_config* cfg, int index, const char** name, int64_t* offset, int64_t* numel,
                      int32_t* ndim, int64_t* dims) {
-  if (!cfg || !config_ok(*cfg) || index < 0 || index >= T_COUNT) return GPT2_ERR_ARG;
+  if (!cfg || !config_ok(*cfg) || index < 0) return GPT2_ERR_ARG;
   TensorDesc t[T_COUNT];
   tensor_table(*cfg, t);
-  if (name) *name = kTensorNames[index];
-  if (offset) *offset = t[index].off;
-  if (numel) *numel = t[index].numel;
-  if (ndim) *ndim = t[index].ndim;
+  int id = -1;
+  for (int i = 0, k = 0; i < T_COUNT; ++i)
+    if (t[i].present && k++ == index) {
+      id = i;
+      break;
+    }
+  if (id < 0) return GPT2_ERR_ARG;
+  if (name) *name = kTensorNames[id];
+  if (offset) *offset = t[id].off;
+  if (numel) *numel = t[id].numel;
+  if (ndim) *ndim = t[id].ndim;
   if (dims)
-    for (int i = 0; i < 3; ++i) dims[i] = i < t[index].ndim ? t[index].dims[i] : 0;
+    for (int i = 0; i < 3; ++i) dims[i] = i < t[id].ndim ? t[id].dims[i] : 0;
   return GPT2_OK;
 }
 
@@ -833,6 +870,102 @@ int gpt2_timing_read(gpt2_ctx* c, double* total_ms, int64_t* launches, double* f
   *flops = f;
   *bytes = b;
   return c->ev_overflow ? GPT2_ERR_ARG : GPT2_OK;
+}
+
+// ---- checkpoints ------------------------------------------------------------------
+// File: "GPT2CKP1", the gpt2_config, int64 step, n_params, n_extra, the extra
+// words, then params, adam_m and adam_v as fp32 (little-endian, as in memory).
+namespace {
+constexpr char kCkptMagic[8] = {'G', 'P', 'T', '2', 'C', 'K', 'P', '1'};
+constexpr int kCkptExtraMax = 16;
+constexpr int64_t kCkptChunk = (int64_t)1 << 24;  // floats per staged copy
+
+bool same_model(const gpt2_config& a, const gpt2_config& b) {
+  return a.n_layer == b.n_layer && a.n_head == b.n_head && a.n_embd == b.n_embd && a.block_size == b.block_size &&
+         a.vocab_size == b.vocab_size && a.padded_vocab_size == b.padded_vocab_size && a.precision == b.precision &&
+         a.variant == b.variant;
+}
+}  // namespace
+
+int gpt2_checkpoint_save(gpt2_ctx* c, const char* path, const int64_t* extra, int n_extra) {
+  if (!c || !path || n_extra < 0 || n_extra > kCkptExtraMax || (n_extra > 0 && !extra)) return GPT2_ERR_ARG;
+  if (hipStreamSynchronize(c->stream) != hipSuccess) return GPT2_ERR_HIP;
+  const std::string tmp = std::string(path) + ".tmp";
+  FILE* f = fopen(tmp.c_str(), "wb");
+  if (!f) return GPT2_ERR_IO;
+  const int64_t head[3] = {c->step, c->n_params, (int64_t)n_extra};
+  bool ok = fwrite(kCkptMagic, 1, 8, f) == 8 && fwrite(&c->cfg, sizeof(gpt2_config), 1, f) == 1 &&
+            fwrite(head, sizeof(int64_t), 3, f) == 3 &&
+            (n_extra == 0 || fwrite(extra, sizeof(int64_t), n_extra, f) == (size_t)n_extra);
+  std::vector<float> stage((size_t)std::min<int64_t>(kCkptChunk, c->n_params));
+  const float* src[3] = {c->buf.params, c->buf.adam_m, c->buf.adam_v};
+  int err = GPT2_ERR_IO;
+  for (int a = 0; a < 3 && ok; ++a) {
+    for (int64_t o = 0; o < c->n_params && ok; o += kCkptChunk) {
+      const int64_t n = std::min<int64_t>(kCkptChunk, c->n_params - o);
+      if (hipMemcpy(stage.data(), src[a] + o, n * sizeof(float), hipMemcpyDeviceToHost) != hipSuccess) {
+        ok = false;
+        err = GPT2_ERR_HIP;
+        break;
+      }
+      ok = fwrite(stage.data(), sizeof(float), n, f) == (size_t)n;
+    }
+  }
+  ok = (fclose(f) == 0) && ok;
+  if (!ok || rename(tmp.c_str(), path) != 0) {
+    remove(tmp.c_str());
+    return ok ? GPT2_ERR_IO : err;
+  }
+  return GPT2_OK;
+}
+
+int gpt2_checkpoint_load(gpt2_ctx* c, const char* path, int64_t* extra, int* n_extra) {
+  if (!c || !path || !n_extra || *n_extra < 0 || (*n_extra > 0 && !extra)) return GPT2_ERR_ARG;
+  FILE* f = fopen(path, "rb");
+  if (!f) return GPT2_ERR_IO;
+  char magic[8];
+  gpt2_config cfg;
+  int64_t head[3];
+  if (fread(magic, 1, 8, f) != 8 || memcmp(magic, kCkptMagic, 8) != 0 || fread(&cfg, sizeof(cfg), 1, f) != 1 ||
+      fread(head, sizeof(int64_t), 3, f) != 3 || head[2] < 0 || head[2] > kCkptExtraMax || head[0] < 0) {
+    fclose(f);
+    return GPT2_ERR_IO;
+  }
+  if (!same_model(cfg, c->cfg) || head[1] != c->n_params) {
+    fclose(f);
+    return GPT2_ERR_ARG;
+  }
+  int64_t ex[kCkptExtraMax];
+  if (head[2] > 0 && fread(ex, sizeof(int64_t), head[2], f) != (size_t)head[2]) {
+    fclose(f);
+    return GPT2_ERR_IO;
+  }
+  if (hipStreamSynchronize(c->stream) != hipSuccess) {
+    fclose(f);
+    return GPT2_ERR_HIP;
+  }
+  std::vector<float> stage((size_t)std::min<int64_t>(kCkptChunk, c->n_params));
+  float* dst[3] = {c->buf.params, c->buf.adam_m, c->buf.adam_v};
+  for (int a = 0; a < 3; ++a) {
+    for (int64_t o = 0; o < c->n_params; o += kCkptChunk) {
+      const int64_t n = std::min<int64_t>(kCkptChunk, c->n_params - o);
+      if (fread(stage.data(), sizeof(float), n, f) != (size_t)n) {
+        fclose(f);
+        return GPT2_ERR_IO;
+      }
+      if (hipMemcpy(dst[a] + o, stage.data(), n * sizeof(float), hipMemcpyHostToDevice) != hipSuccess) {
+        fclose(f);
+        return GPT2_ERR_HIP;
+      }
+    }
+  }
+  fclose(f);
+  c->step = head[0];
+  const int nx = (int)std::min<int64_t>(head[2], *n_extra);
+  for (int i = 0; i < nx; ++i) extra[i] = ex[i];
+  *n_extra = nx;
+  if (c->bf16) to_bf16(c->buf.params, c->buf.params_bf16, c->n_params, c->stream);
+  return hip_status();
 }
 
 int gpt2_embedding_backward(gpt2_ctx* c, const int32_t* d_idx, const float* d_dx0, int B, int T) {

@@ -1,0 +1,293 @@
+// Autoregressive decoding on the step's kernels: the key / value cache, the
+// attention of one new query per sequence over its cached keys, and
+// temperature / top-k / top-p sampling.
+#include "common.h"
+#include "infer_kernels.h"
+
+namespace gpt2k {
+
+// cache[(b * Tmax + t0 + t)][0 : 2C] = qkv[b * T + t][C : 3C] (keys | values)
+template <typename TA>
+__global__ void kv_store_kernel(const TA* __restrict__ qkv, TA* __restrict__ cache, int B, int T, int t0, int Tmax,
+                                int C) {
+  constexpr int V = 16 / sizeof(TA);  // elements per 16-byte chunk
+  const int chunks = 2 * C / V;
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= (int64_t)B * T * chunks) return;
+  const int64_t row = i / chunks;
+  const int c = (int)(i % chunks) * V;
+  const int b = (int)(row / T), t = (int)(row % T);
+  const u32x4 v = *reinterpret_cast<const u32x4*>(qkv + row * 3 * C + C + c);
+  *reinterpret_cast<u32x4*>(cache + ((int64_t)b * Tmax + t0 + t) * 2 * C + c) = v;
+}
+
+template <typename TA>
+void kv_store(const TA* qkv, TA* cache, int B, int T, int t0, int Tmax, int C, hipStream_t s) {
+  const int64_t n = (int64_t)B * T * (2 * C / (16 / (int)sizeof(TA)));
+  kv_store_kernel<TA><<<(unsigned)((n + 255) / 256), 256, 0, s>>>(qkv, cache, B, T, t0, Tmax, C);
+}
+
+// dst[b] = src[b * T + T - 1] (the last position of every sequence)
+template <typename TA>
+__global__ void last_rows_kernel(const TA* __restrict__ src, TA* __restrict__ dst, int B, int T, int C) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= (int64_t)B * C) return;
+  const int b = (int)(i / C), c = (int)(i % C);
+  dst[i] = src[((int64_t)b * T + T - 1) * C + c];
+}
+
+template <typename TA>
+void last_rows(const TA* src, TA* dst, int B, int T, int C, hipStream_t s) {
+  const int64_t n = (int64_t)B * C;
+  last_rows_kernel<TA><<<(unsigned)((n + 255) / 256), 256, 0, s>>>(src, dst, B, T, C);
+}
+
+// One new query per sequence against its n_keys cached keys (the query's own
+// key and value are the last of them): workgroup (head, sequence).  The scores
+// of all keys go to LDS (one thread per key at a time), then their softmax;
+// then hd-wide groups of threads each sum the values of every G-th key and the
+// groups' sums are added in group order.
+template <typename TA>
+__global__ __launch_bounds__(256) void decode_attn_kernel(const TA* __restrict__ qkv, const TA* __restrict__ cache,
+                                                          TA* __restrict__ y, int n_keys, int Tmax, int C, int NH,
+                                                          float scale) {
+  extern __shared__ float sm[];  // [n_keys] scores, then [groups][hd] partial sums; q in red
+  __shared__ float red[16];
+  __shared__ float qs[256];
+  const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+  const int hd = C / NH;
+  const TA* q = qkv + (int64_t)b * 3 * C + h * hd;
+  for (int d = tid; d < hd; d += blockDim.x) qs[d] = to_f32(q[d]);
+  __syncthreads();
+  const TA* kb = cache + (int64_t)b * Tmax * 2 * C + h * hd;
+  float mx = -INFINITY;
+  for (int j = tid; j < n_keys; j += blockDim.x) {
+    const TA* k = kb + (int64_t)j * 2 * C;
+    float acc = 0.f;
+    for (int d = 0; d < hd; d += 4) {
+      float kv[4];
+      load4(k + d, kv);
+      acc = fmaf(qs[d], kv[0], acc);
+      acc = fmaf(qs[d + 1], kv[1], acc);
+      acc = fmaf(qs[d + 2], kv[2], acc);
+      acc = fmaf(qs[d + 3], kv[3], acc);
+    }
+    acc *= scale;
+    sm[j] = acc;
+    mx = fmaxf(mx, acc);
+  }
+  mx = block_max(mx, red);
+  float l = 0.f;
+  for (int j = tid; j < n_keys; j += blockDim.x) {
+    const float pj = expf(sm[j] - mx);
+    sm[j] = pj;
+    l += pj;
+  }
+  l = block_sum(l, red);  // ends with a barrier after the probabilities are written
+  __syncthreads();
+  const int groups = blockDim.x / hd;
+  const int g = tid / hd, d = tid % hd;
+  float* part = sm + n_keys;
+  if (g < groups) {
+    const TA* vb = kb + C + d;
+    float acc = 0.f;
+    for (int j = g; j < n_keys; j += groups) acc = fmaf(sm[j], to_f32(vb[(int64_t)j * 2 * C]), acc);
+    part[g * hd + d] = acc;
+  }
+  __syncthreads();
+  if (tid < hd) {
+    float acc = 0.f;
+    for (int i = 0; i < groups; ++i) acc += part[i * hd + tid];
+    y[(int64_t)b * C + h * hd + tid] = from_f32<TA>(acc / l);
+  }
+}
+
+template <typename TA>
+bool decode_attn(const TA* qkv, const TA* cache, TA* y, int B, int n_keys, int Tmax, int C, int NH, hipStream_t s) {
+  const int hd = C / NH;
+  if (hd > 256 || hd % 4 || n_keys < 1 || n_keys > Tmax) return false;
+  const int groups = 256 / hd;
+  const size_t lds = (size_t)(n_keys + groups * hd) * sizeof(float);
+  if (lds > 60 * 1024) return false;
+  decode_attn_kernel<TA><<<dim3(NH, B), 256, lds, s>>>(qkv, cache, y, n_keys, Tmax, C, NH,
+                                                       1.0f / sqrtf((float)hd));
+  return true;
+}
+
+// ---------------------------------------------------------------- sampling ----
+// One workgroup of 1024 threads per row; thread t holds the NPT consecutive
+// columns [t NPT, (t + 1) NPT) in registers.  Thresholds are found by a
+// bitwise search over ordered 32-bit keys (exact: 32 counting or summing
+// passes), so no sort is needed.
+constexpr int kSampleThreads = 1024;
+constexpr int kSampleNPT = 64;  // columns per thread: vocabularies up to 65,536
+
+// order-preserving map of a float to an unsigned key (-inf lowest)
+DEVI uint32_t order_key(float f) {
+  const uint32_t u = __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// block-wide integer sum (every thread gets it)
+DEVI int block_count(int v, int* scratch) {
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) scratch[threadIdx.x >> 6] = v;
+  __syncthreads();
+  int r = 0;
+  for (int w = 0; w < (int)(blockDim.x >> 6); ++w) r += scratch[w];
+  return r;
+}
+
+__global__ __launch_bounds__(kSampleThreads) void sample_kernel(const float* __restrict__ logits, int64_t ld, int V,
+                                                                float temperature, int top_k, float top_p,
+                                                                const float* __restrict__ uniform,
+                                                                int32_t* __restrict__ out) {
+  __shared__ float redf[16];
+  __shared__ int redi[16];
+  __shared__ float scan[kSampleThreads];
+  __shared__ int pick;
+  const int b = blockIdx.x, t = threadIdx.x;
+  const float* row = logits + (int64_t)b * ld;
+  const int c0 = t * kSampleNPT;
+  float z[kSampleNPT];
+#pragma unroll
+  for (int i = 0; i < kSampleNPT; ++i) z[i] = (c0 + i < V) ? row[c0 + i] : -INFINITY;
+
+  if (temperature <= 0.f || top_k == 1) {  // greedy: the first largest logit
+    float best = -INFINITY;
+    int bi = V;  // past the end: no candidate yet
+#pragma unroll
+    for (int i = 0; i < kSampleNPT; ++i)
+      if (c0 + i < V && (z[i] > best || bi == V)) {
+        best = z[i];
+        bi = c0 + i;
+      }
+    // block arg-max with the lowest index on ties
+    const float m = block_max(best, redf);
+    int cand = (best == m) ? bi : V;
+    for (int o = 32; o >= 1; o >>= 1) cand = min(cand, __shfl_xor(cand, o, 64));
+    __syncthreads();
+    if ((t & 63) == 0) redi[t >> 6] = cand;
+    __syncthreads();
+    if (t == 0) {
+      int r = V;
+      for (int w = 0; w < kSampleThreads / 64; ++w) r = min(r, redi[w]);
+      out[b] = r;
+    }
+    return;
+  }
+  const float inv_t = 1.0f / temperature;
+#pragma unroll
+  for (int i = 0; i < kSampleNPT; ++i) z[i] *= inv_t;
+  // top-k: the k-th largest key; columns below it drop out
+  uint32_t kth = 0;
+  if (top_k > 0 && top_k < V) {
+    for (int bit = 31; bit >= 0; --bit) {
+      const uint32_t cand = kth | (1u << bit);
+      int cnt = 0;
+#pragma unroll
+      for (int i = 0; i < kSampleNPT; ++i) cnt += order_key(z[i]) >= cand ? 1 : 0;
+      if (block_count(cnt, redi) >= top_k) kth = cand;
+    }
+  }
+  float mx = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < kSampleNPT; ++i) {
+    if (order_key(z[i]) < kth || c0 + i >= V) z[i] = -INFINITY;
+    mx = fmaxf(mx, z[i]);
+  }
+  mx = block_max(mx, redf);
+  // unnormalised probabilities e = exp(z - max) of the kept columns
+  float part = 0.f;
+#pragma unroll
+  for (int i = 0; i < kSampleNPT; ++i) {
+    z[i] = expf(z[i] - mx);
+    part += z[i];
+  }
+  const float Z = block_sum(part, redf);
+  // top-p: the largest e-threshold whose kept mass reaches top_p Z
+  if (top_p > 0.f && top_p < 1.f) {
+    const float need = top_p * Z;
+    uint32_t thr = 0;
+    for (int bit = 30; bit >= 0; --bit) {
+      const uint32_t cand = thr | (1u << bit);
+      const float c = __uint_as_float(cand);
+      float sp = 0.f;
+#pragma unroll
+      for (int i = 0; i < kSampleNPT; ++i) sp += z[i] >= c ? z[i] : 0.f;
+      if (block_sum(sp, redf) >= need) thr = cand;
+    }
+    const float c = __uint_as_float(thr);
+#pragma unroll
+    for (int i = 0; i < kSampleNPT; ++i) z[i] = z[i] >= c ? z[i] : 0.f;
+  }
+  // inverse CDF in column order: thread sums, an exclusive scan, then the
+  // thread whose range holds u * total walks its columns
+  float mine = 0.f;
+#pragma unroll
+  for (int i = 0; i < kSampleNPT; ++i) mine += z[i];
+  scan[t] = mine;
+  if (t == 0) pick = -1;
+  __syncthreads();
+  for (int o = 1; o < kSampleThreads; o <<= 1) {  // inclusive scan (Hillis-Steele)
+    const float add = t >= o ? scan[t - o] : 0.f;
+    __syncthreads();
+    scan[t] += add;
+    __syncthreads();
+  }
+  const float total = scan[kSampleThreads - 1];
+  const float target = uniform[b] * total;
+  const float before = t > 0 ? scan[t - 1] : 0.f;
+  if (mine > 0.f && target >= before && target < scan[t]) {
+    float c = before;
+    int sel = -1;
+#pragma unroll
+    for (int i = 0; i < kSampleNPT; ++i) {
+      if (z[i] > 0.f && sel < 0) {
+        c += z[i];
+        if (target < c) sel = c0 + i;
+      }
+    }
+    if (sel < 0) {  // rounding of the thread's own sum: its last kept column
+#pragma unroll
+      for (int i = 0; i < kSampleNPT; ++i)
+        if (z[i] > 0.f) sel = c0 + i;
+    }
+    pick = sel;
+  }
+  __syncthreads();
+  if (pick >= 0) {
+    if (t == 0) out[b] = pick;
+    return;
+  }
+  // the target fell at or past the rounded total: the last kept column
+  int last = -1;
+#pragma unroll
+  for (int i = 0; i < kSampleNPT; ++i)
+    if (z[i] > 0.f) last = c0 + i;
+  for (int o = 32; o >= 1; o >>= 1) last = max(last, __shfl_xor(last, o, 64));
+  if ((t & 63) == 0) redi[t >> 6] = last;
+  __syncthreads();
+  if (t == 0) {
+    int r = -1;
+    for (int w = 0; w < kSampleThreads / 64; ++w) r = max(r, redi[w]);
+    out[b] = r;
+  }
+}
+
+bool sample(const float* logits, int64_t ld, int B, int V, float temperature, int top_k, float top_p,
+            const float* uniform, int32_t* out, hipStream_t s) {
+  if (V < 1 || V > kSampleThreads * kSampleNPT || B < 1) return false;
+  sample_kernel<<<B, kSampleThreads, 0, s>>>(logits, ld, V, temperature, top_k, top_p, uniform, out);
+  return true;
+}
+
+template void kv_store<float>(const float*, float*, int, int, int, int, int, hipStream_t);
+template void kv_store<bf16>(const bf16*, bf16*, int, int, int, int, int, hipStream_t);
+template void last_rows<float>(const float*, float*, int, int, int, hipStream_t);
+template void last_rows<bf16>(const bf16*, bf16*, int, int, int, hipStream_t);
+template bool decode_attn<float>(const float*, const float*, float*, int, int, int, int, int, hipStream_t);
+template bool decode_attn<bf16>(const bf16*, const bf16*, bf16*, int, int, int, int, int, hipStream_t);
+
+}  // namespace gpt2k

@@ -1,0 +1,31 @@
+// Host-side launchers of the decoding kernels (infer.hip).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gpt2k {
+
+// cache[(b Tmax + t0 + t)][0 : 2C] = qkv[b T + t][C : 3C] (the keys and values of
+// rows (b, t) of a (B, T, 3C) QKV activation into a (B, Tmax, 2C) cache).
+template <typename TA>
+void kv_store(const TA* qkv, TA* cache, int B, int T, int t0, int Tmax, int C, hipStream_t s);
+// dst (B, C) = the rows (b, T - 1) of src (B, T, C).
+template <typename TA>
+void last_rows(const TA* src, TA* dst, int B, int T, int C, hipStream_t s);
+// y (B, C) = causal attention of the single query of each sequence (qkv
+// (B, 3C)) over keys and values 0 .. n_keys - 1 of its cache rows (the last
+// one its own).  Returns false for shapes the kernel does not take.
+template <typename TA>
+bool decode_attn(const TA* qkv, const TA* cache, TA* y, int B, int n_keys, int Tmax, int C, int NH, hipStream_t s);
+// out[b] = a column of logits row b (fp32, row stride ld) among [0, V):
+// temperature <= 0 or top_k == 1: the first largest; else z = logits / T,
+// columns below the k-th largest z dropped (top_k > 0), p = softmax(z),
+// columns outside the smallest most-probable set of mass >= top_p dropped
+// (0 < top_p < 1; ties at the threshold kept), and the column where the
+// running sum of the kept p in column order first exceeds uniform[b] times
+// their total.
+bool sample(const float* logits, int64_t ld, int B, int V, float temperature, int top_k, float top_p,
+            const float* uniform, int32_t* out, hipStream_t s);
+
+}  // namespace gpt2k

@@ -22,20 +22,27 @@ GPT2_ERR_BATCH = -3
 GPT2_ERR_STATE = -4
 GPT2_ERR_TOKEN = -5
 GPT2_ERR_HIP = -6
+GPT2_ERR_IO = -7
 GPT2_FP32 = 0
 GPT2_BF16 = 1
+GPT2_UNTIED_HEAD = 1
+GPT2_NO_QKV_BIAS = 2
 
 ERROR_NAMES = {
     GPT2_ERR_ARG: "GPT2_ERR_ARG", GPT2_ERR_SEQ_TOO_LONG: "GPT2_ERR_SEQ_TOO_LONG",
     GPT2_ERR_BATCH: "GPT2_ERR_BATCH", GPT2_ERR_STATE: "GPT2_ERR_STATE",
-    GPT2_ERR_TOKEN: "GPT2_ERR_TOKEN", GPT2_ERR_HIP: "GPT2_ERR_HIP",
+    GPT2_ERR_TOKEN: "GPT2_ERR_TOKEN", GPT2_ERR_HIP: "GPT2_ERR_HIP", GPT2_ERR_IO: "GPT2_ERR_IO",
 }
 
 # Every function the header declares.
 EXPORTS = ("gpt2_init", "gpt2_forward_loss", "gpt2_backward", "gpt2_accumulate", "gpt2_clip_adamw_step",
            "gpt2_destroy", "gpt2_sync_status", "gpt2_sync_params", "gpt2_get_step", "gpt2_set_step",
            "gpt2_tensor_info", "gpt2_activation", "gpt2_timing_enable", "gpt2_timing_read", "gpt2_timing_site",
-           "gpt2_embedding_backward")
+           "gpt2_embedding_backward",
+           "gpt2_lr_at", "gpt2_loader_open", "gpt2_loader_next", "gpt2_loader_next_host", "gpt2_loader_state",
+           "gpt2_loader_seek", "gpt2_loader_close", "gpt2_checkpoint_save", "gpt2_checkpoint_load",
+           "gpt2_infer_init", "gpt2_infer_prefill", "gpt2_infer_decode", "gpt2_infer_length", "gpt2_sample",
+           "gpt2_infer_sync_status", "gpt2_infer_destroy")
 
 
 class Gpt2Error(RuntimeError):
@@ -48,12 +55,21 @@ class gpt2_config(ctypes.Structure):
     _fields_ = [("n_layer", ctypes.c_int32), ("n_head", ctypes.c_int32), ("n_embd", ctypes.c_int32),
                 ("block_size", ctypes.c_int32), ("vocab_size", ctypes.c_int32),
                 ("padded_vocab_size", ctypes.c_int32), ("precision", ctypes.c_int32),
-                ("max_batch", ctypes.c_int32)]
+                ("max_batch", ctypes.c_int32), ("variant", ctypes.c_int32)]
 
 
 class gpt2_buffers(ctypes.Structure):
     _fields_ = [("params", ctypes.c_void_p), ("grads", ctypes.c_void_p), ("adam_m", ctypes.c_void_p),
                 ("adam_v", ctypes.c_void_p), ("params_bf16", ctypes.c_void_p), ("workspace", ctypes.c_void_p)]
+
+
+class gpt2_lr_schedule(ctypes.Structure):
+    _fields_ = [("max_lr", ctypes.c_double), ("min_lr", ctypes.c_double), ("warmup_steps", ctypes.c_int64),
+                ("max_steps", ctypes.c_int64)]
+
+
+class gpt2_infer_sizes(ctypes.Structure):
+    _fields_ = [("cache_bytes", ctypes.c_int64), ("workspace_bytes", ctypes.c_int64)]
 
 
 class gpt2_sizes(ctypes.Structure):
@@ -94,6 +110,16 @@ def load_library() -> ctypes.CDLL:
         "gpt2_timing_read": (I, [P, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(I64),
                                  ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_double)]),
         "gpt2_embedding_backward": (I, [P, P, P, I, I]),
+        "gpt2_lr_at": (ctypes.c_double, [ctypes.POINTER(gpt2_lr_schedule), I64]),
+        "gpt2_loader_open": (I, [ctypes.POINTER(ctypes.c_char_p), I, ctypes.c_int32, ctypes.c_int32, I, I, I,
+                                 ctypes.POINTER(P)]),
+        "gpt2_loader_next": (I, [P, P, P, P]),
+        "gpt2_loader_next_host": (I, [P, P, P]),
+        "gpt2_loader_state": (I, [P, ctypes.POINTER(I64), ctypes.POINTER(I64)]),
+        "gpt2_loader_seek": (I, [P, I64, I64]),
+        "gpt2_loader_close": (None, [P]),
+        "gpt2_checkpoint_save": (I, [P, ctypes.c_char_p, ctypes.POINTER(I64), I]),
+        "gpt2_checkpoint_load": (I, [P, ctypes.c_char_p, ctypes.POINTER(I64), ctypes.POINTER(ctypes.c_int)]),
         "gpt2_timing_site": (I, [P, I, ctypes.POINTER(ctypes.c_char_p), ctypes.POINTER(ctypes.c_double),
                                  ctypes.POINTER(I64), ctypes.POINTER(ctypes.c_double),
                                  ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int32)]),
@@ -112,8 +138,10 @@ def _check(code: int, what: str) -> None:
 
 
 def make_config(shape, precision: str, max_batch: int) -> gpt2_config:
+    variant = (0 if getattr(shape, "tied", True) else GPT2_UNTIED_HEAD) | \
+              (0 if getattr(shape, "qkv_bias", True) else GPT2_NO_QKV_BIAS)
     return gpt2_config(shape.n_layer, shape.n_head, shape.n_embd, shape.block_size, shape.vocab_size,
-                       shape.padded_vocab_size, GPT2_BF16 if precision == "bf16" else GPT2_FP32, max_batch)
+                       shape.padded_vocab_size, GPT2_BF16 if precision == "bf16" else GPT2_FP32, max_batch, variant)
 
 
 def query_sizes(cfg: gpt2_config) -> gpt2_sizes:
@@ -313,6 +341,20 @@ class GPT2Step:
             i += 1
         return out
 
+    def checkpoint_save(self, path: str, extra=()) -> None:
+        """Training state (params, AdamW moments, step counter, extra int64
+        words such as the loader position) to a file."""
+        ex = (ctypes.c_int64 * 16)(*extra)
+        _check(self.lib.gpt2_checkpoint_save(self.ctx, os.fsencode(path), ex, len(extra)), "gpt2_checkpoint_save")
+
+    def checkpoint_load(self, path: str):
+        """Restores a checkpoint; returns its extra words."""
+        ex = (ctypes.c_int64 * 16)()
+        n = ctypes.c_int(16)
+        _check(self.lib.gpt2_checkpoint_load(self.ctx, os.fsencode(path), ex, ctypes.byref(n)),
+               "gpt2_checkpoint_load")
+        return tuple(ex[i] for i in range(n.value))
+
     def close(self) -> None:
         if getattr(self, "ctx", None):
             self.lib.gpt2_destroy(self.ctx)
@@ -323,3 +365,155 @@ class GPT2Step:
             self.close()
         except Exception:
             pass
+
+
+def lr_at(max_lr: float, min_lr: float, warmup_steps: int, max_steps: int, step: int) -> float:
+    """The library's warmup + cosine learning rate for optimizer step `step`."""
+    lib = load_library()
+    sched = gpt2_lr_schedule(max_lr, min_lr, warmup_steps, max_steps)
+    return float(lib.gpt2_lr_at(ctypes.byref(sched), step))
+
+
+class TokenLoader:
+    """The library's sequential loader over token shard files (uint16 or
+    int32 ids): one call of next() gives one optimizer step of k micro-batches
+    of B x T tokens."""
+
+    def __init__(self, paths, vocab_size: int, k: int, B: int, T: int, dtype: str = "uint16"):
+        self.lib = load_library()
+        self.shape = (k, B, T)
+        arr = (ctypes.c_char_p * len(paths))(*[os.fsencode(p) for p in paths])
+        ld = ctypes.c_void_p()
+        _check(self.lib.gpt2_loader_open(arr, len(paths), 0 if dtype == "uint16" else 1, vocab_size, k, B, T,
+                                         ctypes.byref(ld)), "gpt2_loader_open")
+        self.ld = ld
+
+    def next_host(self):
+        import numpy as np
+        k, B, T = self.shape
+        x = np.empty((k, B, T), np.int32)
+        y = np.empty((k, B, T), np.int32)
+        _check(self.lib.gpt2_loader_next_host(self.ld, x.ctypes.data_as(ctypes.c_void_p),
+                                              y.ctypes.data_as(ctypes.c_void_p)), "gpt2_loader_next_host")
+        return x, y
+
+    def next_device(self, x, y, stream) -> None:
+        """Fills the int32 (k, B, T) device tensors x, y on `stream`."""
+        import torch
+        for t in (x, y):
+            if t.dtype != torch.int32 or not t.is_contiguous() or tuple(t.shape) != self.shape or not t.is_cuda:
+                raise ValueError("next_device: x and y must be contiguous int32 (k, B, T) device tensors")
+        _check(self.lib.gpt2_loader_next(self.ld, ctypes.c_void_p(x.data_ptr()), ctypes.c_void_p(y.data_ptr()),
+                                         ctypes.c_void_p(stream.cuda_stream)), "gpt2_loader_next")
+
+    def state(self):
+        sh, pos = ctypes.c_int64(), ctypes.c_int64()
+        _check(self.lib.gpt2_loader_state(self.ld, ctypes.byref(sh), ctypes.byref(pos)), "gpt2_loader_state")
+        return sh.value, pos.value
+
+    def seek(self, shard: int, pos: int) -> None:
+        _check(self.lib.gpt2_loader_seek(self.ld, shard, pos), "gpt2_loader_seek")
+
+    def close(self) -> None:
+        if getattr(self, "ld", None):
+            self.lib.gpt2_loader_close(self.ld)
+            self.ld = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+class Decoder:
+    """A decoding context of the C ABI (gpt2_infer.h) over the parameters of
+    a GPT2Step (read, not copied): prefill, one-token steps and sampling."""
+
+    def __init__(self, step: "GPT2Step", max_batch: int):
+        import torch
+        self.torch = torch
+        self.lib = load_library()
+        self.step = step
+        cfg = make_config(step.shape, step.precision, max_batch)
+        self.cfg = cfg
+        sz = gpt2_infer_sizes()
+        _check(self.lib.gpt2_infer_init(ctypes.byref(cfg), None, None, None, None, None, ctypes.byref(sz), None),
+               "gpt2_infer_init (size query)")
+        dev = step.device
+        self.cache = torch.empty(sz.cache_bytes + 256, dtype=torch.uint8, device=dev)
+        self.ws = torch.empty(sz.workspace_bytes + 256, dtype=torch.uint8, device=dev)
+        al = lambda t: (t.data_ptr() + 255) // 256 * 256  # noqa: E731
+        self.stream = step.stream
+        ctx = ctypes.c_void_p()
+        _check(self.lib.gpt2_infer_init(ctypes.byref(cfg), ctypes.c_void_p(step.params.data_ptr()),
+                                        ctypes.c_void_p(step.params_bf16.data_ptr()) if step.params_bf16 is not None
+                                        else None, ctypes.c_void_p(al(self.cache)), ctypes.c_void_p(al(self.ws)),
+                                        ctypes.c_void_p(self.stream.cuda_stream), None, ctypes.byref(ctx)),
+               "gpt2_infer_init")
+        self.ctx = ctx
+        self.vp = step.shape.padded_vocab_size
+        self.B = 0
+
+    def _logits(self, B):
+        return self.torch.empty((B, self.vp), dtype=self.torch.float32, device=self.step.device)
+
+    def prefill(self, idx):
+        """idx: int32 (B, T) device tensor; returns fp32 (B, Vp) logits of the last position."""
+        torch = self.torch
+        if idx.dtype != torch.int32 or idx.dim() != 2 or not idx.is_contiguous() or idx.device != self.step.device:
+            raise ValueError("prefill: idx must be a contiguous int32 (B, T) tensor on the device")
+        B, T = idx.shape
+        out = self._logits(B)
+        _check(self.lib.gpt2_infer_prefill(self.ctx, ctypes.c_void_p(idx.data_ptr()), B, T,
+                                           ctypes.c_void_p(out.data_ptr())), "gpt2_infer_prefill")
+        self.B = B
+        return out
+
+    def decode(self, tokens):
+        """tokens: int32 (B,) device tensor; returns fp32 (B, Vp) logits."""
+        torch = self.torch
+        if tokens.dtype != torch.int32 or tuple(tokens.shape) != (self.B,) or not tokens.is_contiguous() \
+                or tokens.device != self.step.device:
+            raise ValueError("decode: tokens must be a contiguous int32 (B,) tensor on the device")
+        out = self._logits(self.B)
+        _check(self.lib.gpt2_infer_decode(self.ctx, ctypes.c_void_p(tokens.data_ptr()),
+                                          ctypes.c_void_p(out.data_ptr())), "gpt2_infer_decode")
+        return out
+
+    def length(self) -> int:
+        return int(self.lib.gpt2_infer_length(self.ctx))
+
+    def sample(self, logits, uniform, temperature=1.0, top_k=0, top_p=1.0):
+        return sample(logits, uniform, self.step.shape.vocab_size, temperature, top_k, top_p, self.stream)
+
+    def sync_status(self) -> int:
+        return self.lib.gpt2_infer_sync_status(self.ctx)
+
+    def close(self) -> None:
+        if getattr(self, "ctx", None):
+            self.lib.gpt2_infer_destroy(self.ctx)
+            self.ctx = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def sample(logits, uniform, vocab_size, temperature=1.0, top_k=0, top_p=1.0, stream=None):
+    """gpt2_sample: logits fp32 (B, ld) and uniform fp32 (B,) device tensors;
+    returns int32 (B,) tokens."""
+    import torch
+    lib = load_library()
+    B, ld = logits.shape
+    if logits.dtype != torch.float32 or not logits.is_contiguous() or uniform.dtype != torch.float32 \
+            or tuple(uniform.shape) != (B,) or not uniform.is_contiguous():
+        raise ValueError("sample: logits fp32 (B, ld) and uniform fp32 (B,) contiguous device tensors")
+    out = torch.empty(B, dtype=torch.int32, device=logits.device)
+    st = stream if stream is not None else torch.cuda.current_stream(logits.device)
+    _check(lib.gpt2_sample(ctypes.c_void_p(logits.data_ptr()), ld, B, vocab_size, temperature, top_k, top_p,
+                           ctypes.c_void_p(uniform.data_ptr()), ctypes.c_void_p(out.data_ptr()),
+                           ctypes.c_void_p(st.cuda_stream)), "gpt2_sample")
+    return out

@@ -36,9 +36,10 @@
  *   ln1_w [L, C]; ln1_b [L, C]; qkv_w [L, 3C, C]; qkv_b [L, 3C];
  *   proj_w [L, C, C]; proj_b [L, C]; ln2_w [L, C]; ln2_b [L, C];
  *   fc_w [L, 4C, C]; fc_b [L, 4C]; fcproj_w [L, C, 4C]; fcproj_b [L, C];
- *   lnf_w (C); lnf_b (C).
+ *   lnf_w (C); lnf_b (C); and lm_head (Vp, C) in the untied variant (qkv_b
+ *   is absent from the layout without a QKV bias).
  * grads, adam_m and adam_v share this layout.  gpt2_tensor_info enumerates it.
- * Weight decay applies to wte, wpe, qkv_w, proj_w, fc_w and fcproj_w.
+ * Weight decay applies to wte, wpe, qkv_w, proj_w, fc_w, fcproj_w and lm_head.
  */
 #ifndef GPT2_H
 #define GPT2_H
@@ -58,6 +59,14 @@ extern "C" {
 #define GPT2_ERR_TOKEN        -5  /* an id or target outside [0, vocab_size)   */
 #define GPT2_ERR_HIP          -6  /* a HIP call or kernel launch failed        */
 
+/* model variants (gpt2_config.variant): the untied model of the Genesis
+   model card ("Model Specs": 163,009,536 parameters at vocab 50,257; the
+   lm_head kept separate from the token embedding, and no bias on the QKV
+   projection) is GPT2_UNTIED_HEAD | GPT2_NO_QKV_BIAS. */
+#define GPT2_UNTIED_HEAD 1  /* the lm_head is its own (Vp, C) tensor "lm_head",
+                               last in the layout, decayed                 */
+#define GPT2_NO_QKV_BIAS 2  /* the QKV projection has no bias (no qkv_b)   */
+
 /* precision modes */
 #define GPT2_FP32 0  /* every tensor fp32                                        */
 #define GPT2_BF16 1  /* bf16 GEMM/attention operands and activations, fp32
@@ -74,6 +83,8 @@ typedef struct {
                                  Vp % 8 == 0 in BF16 mode                      */
   int32_t precision;          /* GPT2_FP32 or GPT2_BF16; BF16 needs C/NH == 64 */
   int32_t max_batch;          /* largest micro-batch B the workspace holds     */
+  int32_t variant;            /* 0 (GPT-2), or GPT2_UNTIED_HEAD and/or
+                                 GPT2_NO_QKV_BIAS                              */
 } gpt2_config;
 
 typedef struct {
@@ -189,7 +200,7 @@ int gpt2_sync_params(gpt2_ctx *ctx);
 int64_t gpt2_get_step(const gpt2_ctx *ctx);
 int gpt2_set_step(gpt2_ctx *ctx, int64_t t);
 
-/* Enumerate the parameter tensors in layout order: index in [0, 16); fills the
+/* Enumerate the parameter tensors in layout order: index in [0, 15..17); fills the
    name, element offset into the flat vector, element count, rank and the
    dims (at most 3).  Host only.  Returns GPT2_ERR_ARG past the last tensor. */
 int gpt2_tensor_info(const gpt2_config *cfg, int index, const char **name,

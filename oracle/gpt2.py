@@ -43,7 +43,7 @@ GELU_K = math.sqrt(2.0 / math.pi)
 GELU_A = 0.044715
 CLIP_EPS = 1e-6
 
-GLOBAL_NAMES = ("wte", "wpe", "lnf_w", "lnf_b")
+GLOBAL_NAMES = ("wte", "wpe", "lnf_w", "lnf_b", "lm_head")
 BLOCK_NAMES = ("ln1_w", "ln1_b", "qkv_w", "qkv_b", "proj_w", "proj_b",
                "ln2_w", "ln2_b", "fc_w", "fc_b", "fcproj_w", "fcproj_b")
 
@@ -152,6 +152,13 @@ def _merge_heads(x):
 # forward + loss
 # --------------------------------------------------------------------------
 
+def head_name(params):
+    """The lm_head weight: wte when tied (AxonLM "Key Features": weight
+    tying), else the model's own "lm_head" (Genesis "Model Specs": the head
+    kept separate from the embedding)."""
+    return "lm_head" if "lm_head" in params else "wte"
+
+
 def _as64(params):
     return {n: np.asarray(a, dtype=np.float64) for n, a in params.items()}
 
@@ -177,7 +184,9 @@ def forward(params, idx, targets, n_head, loss_scale=1.0):
     for l in range(L):
         lc = {"x_in": x}
         h1, lc["ln1"] = layer_norm(x, p["ln1_w"][l], p["ln1_b"][l])
-        qkv = h1 @ p["qkv_w"][l].T + p["qkv_b"][l]
+        qkv = h1 @ p["qkv_w"][l].T
+        if "qkv_b" in p:
+            qkv = qkv + p["qkv_b"][l]
         q = _split_heads(qkv[..., 0:C], n_head)
         k = _split_heads(qkv[..., C:2 * C], n_head)
         v = _split_heads(qkv[..., 2 * C:3 * C], n_head)
@@ -193,7 +202,7 @@ def forward(params, idx, targets, n_head, loss_scale=1.0):
         cache["layers"].append(lc)
     cache["x_final"] = x
     hf, cache["lnf"] = layer_norm(x, p["lnf_w"], p["lnf_b"])
-    z = hf @ p["wte"].T
+    z = hf @ p[head_name(p)].T
     cache.update(hf=hf, logits=z)
 
     zmax = z.max(axis=-1, keepdims=True)
@@ -232,9 +241,10 @@ def backward(params, cache):
                       np.take_along_axis(dz, targets[..., None], axis=-1) - 1.0, axis=-1)
     dz *= cache["loss_scale"] / N
 
-    # tied lm_head: z = hf wte^T
-    dhf = dz @ p["wte"]
-    g["wte"] += dz.reshape(N, V).T @ cache["hf"].reshape(N, C)
+    # lm_head: z = hf W^T with W = wte (tied) or the model's own lm_head
+    head = head_name(p)
+    dhf = dz @ p[head]
+    g[head] += dz.reshape(N, V).T @ cache["hf"].reshape(N, C)
     dx, g["lnf_w"], g["lnf_b"] = layer_norm_backward(dhf, p["lnf_w"], cache["lnf"])
 
     for l in reversed(range(L)):
@@ -256,7 +266,8 @@ def backward(params, cache):
         dq, dk, dv = causal_attention_backward(_split_heads(dy, n_head), lc["q"], lc["k"],
                                                lc["v"], lc["P"])
         dqkv = np.concatenate([_merge_heads(dq), _merge_heads(dk), _merge_heads(dv)], axis=-1)
-        g["qkv_b"][l] = dqkv.reshape(N, 3 * C).sum(axis=0)
+        if "qkv_b" in g:
+            g["qkv_b"][l] = dqkv.reshape(N, 3 * C).sum(axis=0)
         g["qkv_w"][l] = dqkv.reshape(N, 3 * C).T @ lc["h1"].reshape(N, C)
         dh1 = dqkv @ p["qkv_w"][l]
         dln, g["ln1_w"][l], g["ln1_b"][l] = layer_norm_backward(dh1, p["ln1_w"][l], lc["ln1"])

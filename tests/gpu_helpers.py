@@ -92,35 +92,44 @@ def per_tensor(d):
 
 # ---------------------------------------------------- oracle on many threads ----
 
-def oracle_accumulate_per_sequence(params, x, y, n_head, workers=None):
+def _seq_loss_grads_dx0(params, x, y, n_head, scale):
+    from oracle import gpt2 as ref
+    loss, cache = ref.forward(params, x, y, n_head, loss_scale=scale)
+    g = ref.backward(params, cache)
+    return loss, g, cache["dx0"]
+
+
+def oracle_accumulate_per_sequence(params, x, y, n_head, workers=None, with_dx0=False):
     """The oracle's accumulation with every sequence of the (B, T) batch as its
     own micro-batch (loss scale 1/B): equal to the one batch of B sequences
     (the accumulation pin).  The sequences run on a thread pool (numpy
-    releases the GIL inside its loops and BLAS calls) with BLAS limited to a
-    share of the cores each; the sums are taken in sequence order.
+    releases the GIL inside its loops and BLAS calls) with single-threaded
+    BLAS: concurrent calls into a multi-threaded OpenBLAS from several
+    threads return corrupted products.  The sums are taken in sequence order.
     Returns (mean loss, grads)."""
     import os
     from concurrent.futures import ThreadPoolExecutor
 
     from threadpoolctl import threadpool_limits
 
-    from oracle import gpt2 as ref
     B = x.shape[0]
     cpus = min(16, len(os.sched_getaffinity(0)))
-    workers = workers or max(1, min(8, B, cpus))
-    with threadpool_limits(max(1, cpus // workers)):
+    workers = workers or max(1, min(B, cpus))
+    with threadpool_limits(1):
         with ThreadPoolExecutor(max_workers=workers) as ex:
-            results = list(ex.map(lambda b: ref.loss_and_grads(params, x[b:b + 1], y[b:b + 1], n_head,
-                                                               loss_scale=1.0 / B), range(B)))
+            results = list(ex.map(lambda b: _seq_loss_grads_dx0(params, x[b:b + 1], y[b:b + 1], n_head, 1.0 / B),
+                                  range(B)))
     total = 0.0
     grads = None
-    for loss, g in results:  # fixed order: sequence 0, 1, ...
+    for loss, g, _ in results:  # fixed order: sequence 0, 1, ...
         total += loss
         if grads is None:
             grads = g
         else:
             for n in grads:
                 grads[n] += g[n]
+    if with_dx0:
+        return total, grads, np.concatenate([r[2] for r in results], axis=0)
     return total, grads
 
 

@@ -12,13 +12,17 @@ from gpt2_inputs import SHAPES, ModelShape, n_params, param_shapes
 from gpt_decoder_pre_amd import lib as L
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "gpt2.h")
+HEADERS = [os.path.join(ROOT, "include", h) for h in sorted(os.listdir(os.path.join(ROOT, "include")))
+           if h.endswith(".h")]
 
 
 def header_functions():
-    src = open(HEADER).read()
-    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(gpt2_[a-z_0-9]+)\s*\(", src)))
+    names = set()
+    for h in HEADERS:
+        src = open(h).read()
+        src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+        names |= set(re.findall(r"\b(gpt2_[a-z_0-9]+)\s*\(", src))
+    return sorted(names)
 
 
 @pytest.fixture(scope="module")

@@ -60,6 +60,7 @@ def _run_all_pins():
     """Run the cheap pins; return True if every one passes."""
     checks = [
         xcheck.test_forward_and_gradients_match_torch_autograd,
+        xcheck.test_untied_variant_matches_torch_autograd,
         lambda: xcheck.test_clip_and_adamw_match_torch("clip"),
         lambda: xcheck.test_train_step_matches_torch_accumulate_clip_adamw("clip"),
         pins.test_attention_masked_equals_online_softmax_form,
@@ -141,4 +142,11 @@ def _train_step_stale_t(params, m, v, t, batches, n_head, lr, beta1=0.9, beta2=0
 @pytest.mark.parametrize("bad", [_train_step_unclipped, _train_step_stale_t])
 def test_planted_mistake_in_train_step_wiring_is_caught(monkeypatch, bad):
     monkeypatch.setattr(ref, "train_step", bad)
+    assert not _run_all_pins()
+
+
+def test_planted_tied_head_in_untied_backward_is_caught(monkeypatch):
+    """Plausible slip: the untied variant's backward still sends the head's
+    gradient to wte."""
+    monkeypatch.setattr(ref, "head_name", lambda params: "wte")
     assert not _run_all_pins()

@@ -45,6 +45,14 @@ def test_param_count_untied_163m_cross_check():
     assert untied == GOLDEN["params_untied_163m"]["value"]
 
 
+def test_param_count_of_the_untied_variant_matches_page():
+    # the variant's own tensor table (lm_head added, qkv_b removed) at vocab 50,257
+    s = ModelShape("x", 12, 12, 768, 1024, 50257, 50257, tied=False, qkv_bias=False)
+    assert n_params(s) == GOLDEN["params_untied_163m"]["value"]
+    names = list(param_shapes(s))
+    assert "qkv_b" not in names and names[-1] == "lm_head"
+
+
 @pytest.mark.parametrize("scale", ["small", "medium", "large", "xl"])
 def test_scale_param_counts_near_page_figures(scale):
     L, NH, C = GOLDEN["scales"]["value"][scale]

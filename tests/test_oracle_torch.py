@@ -22,7 +22,7 @@ def torch_loss(P, x, y, n_head):
     h = P["wte"][x] + P["wpe"][:T]
     for l in range(L):
         a = F.layer_norm(h, (C,), P["ln1_w"][l], P["ln1_b"][l], eps=1e-5)
-        qkv = F.linear(a, P["qkv_w"][l], P["qkv_b"][l])
+        qkv = F.linear(a, P["qkv_w"][l], P["qkv_b"][l] if "qkv_b" in P else None)
         q, k, v = qkv.split(C, dim=-1)
         q, k, v = (t.view(B, T, n_head, C // n_head).transpose(1, 2) for t in (q, k, v))
         o = F.scaled_dot_product_attention(q, k, v, is_causal=True)
@@ -32,12 +32,12 @@ def torch_loss(P, x, y, n_head):
         u = F.gelu(F.linear(a, P["fc_w"][l], P["fc_b"][l]), approximate="tanh")
         h = h + F.linear(u, P["fcproj_w"][l], P["fcproj_b"][l])
     h = F.layer_norm(h, (C,), P["lnf_w"], P["lnf_b"], eps=1e-5)
-    z = h @ P["wte"].T
+    z = h @ (P["lm_head"] if "lm_head" in P else P["wte"]).T
     return F.cross_entropy(z.reshape(B * T, -1), y.reshape(-1))
 
 
-def _setup(seed=0, L=2, NH=4, C=32, T=16, V=29, B=3):
-    s = ModelShape("xcheck", L, NH, C, T, V, V)
+def _setup(seed=0, L=2, NH=4, C=32, T=16, V=29, B=3, tied=True, qkv_bias=True):
+    s = ModelShape("xcheck", L, NH, C, T, V, V, tied=tied, qkv_bias=qkv_bias)
     p = init_params(s, seed)
     rng = np.random.default_rng(seed + 100)
     for n in p:  # exercise biases and LN parameters
@@ -48,7 +48,17 @@ def _setup(seed=0, L=2, NH=4, C=32, T=16, V=29, B=3):
 
 
 def test_forward_and_gradients_match_torch_autograd():
-    s, p, x, y = _setup()
+    _autograd_case(True, True)
+
+
+def test_untied_variant_matches_torch_autograd():
+    """The variant with its own lm_head and no QKV bias (Genesis "Model Specs")."""
+    _autograd_case(False, False)
+
+
+def _autograd_case(tied, qkv_bias):
+    s, p, x, y = _setup(tied=tied, qkv_bias=qkv_bias)
+    assert ("lm_head" in p) == (not tied) and ("qkv_b" in p) == qkv_bias
     P = {n: torch.tensor(a, dtype=torch.float64, requires_grad=True) for n, a in p.items()}
     lt = torch_loss(P, torch.tensor(x, dtype=torch.long), torch.tensor(y, dtype=torch.long),
                     s.n_head)
