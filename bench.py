@@ -42,6 +42,10 @@ def parse():
     ap.add_argument("--site", default=None, help="launch site timed for the roofline (default: the one that "
                     "takes the most time per step in a per-site record of one untimed step)")
     ap.add_argument("--cpu-toy", action="store_true", help="also time the oracle on the toy step")
+    ap.add_argument("--decode", action="store_true",
+                    help="instead of the training step, time cached decoding (prefill, then one token per "
+                         "sequence per step with top-k / top-p sampling) and print its own JSON line")
+    ap.add_argument("--prompt", type=int, default=128, help="prompt length for --decode")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run a plain 1 GiB device-to-device copy (scale reference for HBM byte counters)")
@@ -142,8 +146,68 @@ def cpu_baseline(run, s, toy=False):
     return out
 
 
+def decode_bench(args):
+    """Cached decoding of the micro-batch's sequences: per step one token per
+    sequence (lm_head logits, the sampler, then the next decode).  A decoding
+    step streams every weight once plus the cached keys and values, so its
+    roofline is HBM bandwidth."""
+    import numpy as np
+    import torch
+
+    from gpt2_inputs import RUNS, init_params, token_stream
+    from gpt_decoder_pre_amd.lib import Decoder, GPT2Step
+
+    run = RUNS[args.config]
+    s = run.shape
+    B, T0, n = run.micro_batch, args.prompt, args.steps
+    if T0 + args.warmup + n > s.block_size:
+        raise SystemExit("--prompt + --warmup + --steps exceeds the block size")
+    dev = torch.device("cuda:0")
+    st = GPT2Step(s, run.precision, max_batch=1, device="cuda:0")
+    st.load_params(init_params(s, run.seed_weights))
+    dec = Decoder(st, B)
+    prompt = torch.tensor(token_stream("zipf", B * T0, s.vocab_size, run.seed_tokens).reshape(B, T0),
+                          dtype=torch.int32, device=dev)
+    u = torch.rand((args.warmup + n, B), generator=torch.Generator(device=dev).manual_seed(1), device=dev)
+    z = dec.prefill(prompt)
+    for i in range(args.warmup):
+        z = dec.decode(dec.sample(z, u[i], 0.8, 40, 0.95))
+    torch.cuda.synchronize()
+    len0 = dec.length()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for i in range(n):
+        z = dec.decode(dec.sample(z, u[args.warmup + i], 0.8, 40, 0.95))
+    t1.record()
+    torch.cuda.synchronize()
+    if dec.sync_status() != 0:
+        raise RuntimeError("device error in decoding")
+    ms = t0.elapsed_time(t1) / n
+    from gpt2_inputs import n_params
+    w_bytes = 2 * (n_params(s) - s.block_size * s.n_embd)  # bf16 weights, each read once per step
+    kv = 2 * s.n_layer * B * (len0 + n / 2) * 2 * s.n_embd  # cached keys and values, mean length
+    byt = w_bytes + kv + 4 * B * s.padded_vocab_size
+    ach = byt / (ms / 1e3) / 1e9
+    out = {"metric": "decode tokens/s (cached, one token per sequence per step, top-k 40 / top-p 0.95)",
+           "value": round(B / (ms / 1e3), 1), "unit": "tokens/s", "n_gpus": 1, "steps": n, "warmup": args.warmup,
+           "ms_per_step": round(ms, 4), "higher_is_better": True, "dtype": "bf16", "data": "synthetic",
+           "config": {"workload": f"{s.name} decoding, {B} sequences, prompt {T0}, positions {len0}..{len0 + n}"},
+           "roofline": {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                        "frac": round(ach / PEAK_HBM_GBS, 4), "algorithmic_per_step": int(byt),
+                        "algorithmic_unit": "byte", "traffic": None}}
+    dec.close()
+    st.close()
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = parse()
+    if args.decode:
+        if args.gpus != 1:
+            print("bench.py runs on one GPU only", file=sys.stderr)
+            sys.exit(2)
+        decode_bench(args)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the data-parallel split across GPUs "
               f"is not part of this build", file=sys.stderr)

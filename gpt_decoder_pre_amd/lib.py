@@ -120,6 +120,14 @@ def load_library() -> ctypes.CDLL:
         "gpt2_loader_close": (None, [P]),
         "gpt2_checkpoint_save": (I, [P, ctypes.c_char_p, ctypes.POINTER(I64), I]),
         "gpt2_checkpoint_load": (I, [P, ctypes.c_char_p, ctypes.POINTER(I64), ctypes.POINTER(ctypes.c_int)]),
+        "gpt2_infer_init": (I, [ctypes.POINTER(gpt2_config), P, P, P, P, P, ctypes.POINTER(gpt2_infer_sizes),
+                                ctypes.POINTER(P)]),
+        "gpt2_infer_prefill": (I, [P, P, I, I, P]),
+        "gpt2_infer_decode": (I, [P, P, P]),
+        "gpt2_infer_length": (I, [P]),
+        "gpt2_sample": (I, [P, I64, I, I, F, I, F, P, P, P]),
+        "gpt2_infer_sync_status": (I, [P]),
+        "gpt2_infer_destroy": (None, [P]),
         "gpt2_timing_site": (I, [P, I, ctypes.POINTER(ctypes.c_char_p), ctypes.POINTER(ctypes.c_double),
                                  ctypes.POINTER(I64), ctypes.POINTER(ctypes.c_double),
                                  ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int32)]),

@@ -573,11 +573,12 @@ def test_embedding_scatter_alone(B, T):
 @pytest.mark.parametrize("mode", ["clip", "noclip"])
 def test_adamw_kernel_alone_matches_oracle(mode):
     """Clip + AdamW alone on identical fp32 (p, g, m, v) at t = 11: m and v
-    within 1e-6 relative (L2) of the fp64 oracle per tensor; the update
-    p' - p within 1e-5 of the oracle's p' rounded to fp32, with 99.9% of the
-    parameters within two fp32 spacings of it.  (The update is ~lr, so fp32's
-    spacing of p' alone is 1e-6..1e-4 of it, and an m' formed by cancellation
-    carries a large relative rounding error into its element's update.)"""
+    within 1e-6 relative (L2) of the fp64 oracle per tensor, the update
+    p' - p within 1e-5 of the oracle's p' rounded to fp32, and every new
+    parameter within the error bound of fp32 arithmetic: a few units of
+    2^-24 of the magnitudes each rounding acts on (p and p', the two terms of
+    m', and the Adam step).  A relative bound on p' alone cannot hold where
+    the Adam step nearly cancels or m' is itself a cancellation."""
     import torch
     s = shape("gpt2-124m-L2", 2, 12, 768, 1024, 50257, 50304)
     say(f"clip + AdamW alone ({mode})")
@@ -587,33 +588,38 @@ def test_adamw_kernel_alone_matches_oracle(mode):
     m0, v0 = warm_state(g, seed=22)
     n = ref.global_norm(g)
     max_norm = 0.5 * n if mode == "clip" else 2.0 * n
-    lr = 6e-4
+    lr, b1, b2, eps, t = 6e-4, 0.9, 0.95, 1e-8, 11
     st = gpu_step(s, "bf16", 1, p)
-    st.load_state(m0, v0, 10)
+    st.load_state(m0, v0, t - 1)
     for name, a in st.to_dict(st.grads).items():
         a.copy_(torch.as_tensor(g[name]))
-    st.clip_adamw_step(lr, 0.9, 0.95, 1e-8, 0.1, max_norm)
+    st.clip_adamw_step(lr, b1, b2, eps, 0.1, max_norm)
     torch.cuda.synchronize()
     assert st.sync_status() == 0
-    P1, M1, V1 = (per_tensor(host(st.to_dict(t))) for t in (st.params, st.m, st.v))
+    P1, M1, V1 = (per_tensor(host(st.to_dict(x))) for x in (st.params, st.m, st.v))
     assert int(st.d_clipped.item()) == (1 if mode == "clip" else 0)
     assert abs(float(st.d_norm.item()) - n) / n < 1e-6
-    r = ref.train_step(p, m0, v0, 11, None, s.n_head, lr=lr, max_norm=max_norm, accumulated=(0.0, g))
+    r = ref.train_step(p, m0, v0, t, None, s.n_head, lr=lr, max_norm=max_norm, accumulated=(0.0, g))
     st.close()
-    P0, RP, RM, RV = per_tensor(p), per_tensor(_f32(r["params"])), per_tensor(r["m"]), per_tensor(r["v"])
+    coef = min(1.0, max_norm / (n + 1e-6))
+    bc1, bc2 = 1 - b1 ** t, 1 - b2 ** t
+    P0, G0, Mw, RP = per_tensor(p), per_tensor(g), per_tensor(m0), per_tensor(r["params"])
+    RPf, RM, RV = per_tensor(_f32(r["params"])), per_tensor(r["m"]), per_tensor(r["v"])
     worst = [0.0, 0.0, 0.0, 0.0]
     for k in P0:
         em, ev = rel(M1[k], RM[k]), rel(V1[k], RV[k])
-        eu = rel(P1[k] - P0[k], RP[k] - P0[k])
-        big = np.maximum(np.abs(P0[k]), np.abs(RP[k])).astype(np.float32)
-        ulps = np.abs(P1[k] - RP[k]) / np.spacing(big).astype(np.float64)
-        q = float(np.quantile(ulps, 0.999))
-        worst = [max(worst[0], em), max(worst[1], ev), max(worst[2], eu), max(worst[3], q)]
+        eu = rel(P1[k] - P0[k], RPf[k] - P0[k])
+        den = np.sqrt(RV[k] / bc2) + eps
+        scale = (np.maximum(np.abs(P0[k]), np.abs(RP[k]))
+                 + lr * (b1 * np.abs(Mw[k]) + (1 - b1) * coef * np.abs(G0[k])) / bc1 / den
+                 + lr * np.abs(RM[k]) / bc1 / den)
+        ratio = float(np.max(np.abs(P1[k] - RP[k]) / (2.0 ** -22 * scale)))
+        worst = [max(worst[0], em), max(worst[1], ev), max(worst[2], eu), max(worst[3], ratio)]
         assert em <= 1e-6 and ev <= 1e-6, (k, em, ev)
         assert eu <= 1e-5, (k, eu)
-        assert q <= 2.0, (k, q)
+        assert ratio <= 1.0, (k, ratio)
     say(f"  worst: m rel {worst[0]:.2e}, v rel {worst[1]:.2e}, update rel {worst[2]:.2e}, "
-        f"99.9th percentile {worst[3]:.2f} fp32 spacings")
+        f"largest error / fp32 bound {worst[3]:.3f}")
 
 
 @pytest.mark.parametrize("precision", ["fp32", "bf16"])
