@@ -24,6 +24,10 @@ namespace {
 // micro-batches whose ids gpt2_accumulate sorts in one launch (the sort
 // buffers hold this many)
 constexpr int kSortBatch = 4;
+// parameters gpt2_clip_adamw_step_static takes at most (its AdamW grid of
+// n / 1024 workgroups stays within the 32-bit grid dimension)
+constexpr int64_t kStaticMaxParams = (int64_t)1 << 40;
+
 enum TensorId {
   T_WTE = 0, T_WPE, T_LN1W, T_LN1B, T_QKVW, T_QKVB, T_PROJW, T_PROJB,
   T_LN2W, T_LN2B, T_FCW, T_FCB, T_FCPW, T_FCPB, T_LNFW, T_LNFB, T_LMHEAD, T_COUNT
@@ -752,6 +756,33 @@ int gpt2_clip_adamw_step(gpt2_ctx* c, float lr, float beta1, float beta2, float 
   c->step += 1;
   clip_adamw_launch(c, c->buf, c->n_params, decay_segments(c->t, c->n_params), c->step, c->norm_part, c->clip_scale,
                     lr, beta1, beta2, eps, weight_decay, max_norm, d_norm, d_clipped, c->stream);
+  return hip_status();
+}
+
+int gpt2_clip_adamw_step_static(const gpt2_config* cfg, const gpt2_buffers* bufs, void* hip_stream, int64_t t,
+                                float lr, float beta1, float beta2, float eps, float weight_decay, float max_norm,
+                                float* d_norm, int32_t* d_clipped) {
+  if (!cfg || !config_ok(*cfg) || !bufs || !bufs->params || !bufs->grads || !bufs->adam_m || !bufs->adam_v ||
+      !d_norm || !d_clipped || t < 1)
+    return GPT2_ERR_ARG;
+  TensorDesc td[T_COUNT];
+  tensor_table(*cfg, td);
+  const int64_t n = total_params(td);
+  if (n > kStaticMaxParams) {
+    fprintf(stderr, "gpt2_clip_adamw_step_static: %lld parameters exceed the limit of %lld\n", (long long)n,
+            (long long)kStaticMaxParams);
+    return GPT2_ERR_ARG;
+  }
+  gpt2_buffers b = *bufs;
+  if (cfg->precision != GPT2_BF16) b.params_bf16 = nullptr;
+  else if (!b.params_bf16) return GPT2_ERR_ARG;
+  double* part = nullptr;
+  float* clip_scale = nullptr;
+  int nblk = 0;
+  if (static_scratch(&part, &clip_scale, &nblk) != 0) return GPT2_ERR_HIP;
+  gpt2_ctx none;  // no timing
+  clip_adamw_launch(&none, b, n, decay_segments(td, n), t, part, clip_scale, lr, beta1, beta2, eps, weight_decay,
+                    max_norm, d_norm, d_clipped, (hipStream_t)hip_stream);
   return hip_status();
 }
 

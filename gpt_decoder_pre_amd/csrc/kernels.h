@@ -185,6 +185,10 @@ struct DecaySegments {
   int64_t start[24];  // segment i covers [start[i], start[i+1]) (start[n] = total)
   int decay[24];
 };
+// The current device's copy of the library's static scratch: room for the
+// sumsq_partials of any n (nblk of them) and one clip factor.  Returns 0, or
+// -1 if the device address cannot be found.
+int static_scratch(double** partials, float** clip_scale, int* nblk);
 void adamw(float* p, const float* g, float* m, float* v, void* p_bf16, int64_t n, const DecaySegments& seg,
            const float* grad_scale, float lr, float beta1, float beta2, float eps, float wd, float inv_bc1,
            float inv_bc2, hipStream_t s);

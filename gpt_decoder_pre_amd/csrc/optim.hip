@@ -1,5 +1,8 @@
 // Global gradient norm, clip decision and one multi-tensor AdamW pass over the
 // flat fp32 parameter vector (HBM-bound).
+#include <cstdio>
+#include <mutex>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -129,6 +132,41 @@ void adamw(float* p, const float* g, float* m, float* v, void* p_bf16, int64_t n
   else
     adamw_kernel<false><<<grid, 256, 0, s>>>(p, g, m, v, nullptr, n4, seg, grad_scale, lr, beta1, beta2, eps, wd,
                                              inv_bc1, inv_bc2);
+}
+
+// ---- scratch in device memory that nothing allocates ----------------------------
+// The norm's fp64 partials (kNormBlocks) and the clip factor for callers that
+// cannot allocate.  Each device holds its own copy from module load until the
+// process ends; the host-side name of the array is not a device address, so
+// host code only ever uses the address hipGetSymbolAddress returns for the
+// current device.
+constexpr int kStaticScratchDoubles = kNormBlocks + 32;
+static __device__ __align__(256) double scratch[kStaticScratchDoubles];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+int static_scratch(double** partials, float** clip_scale, int* nblk) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return -1;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr) {
+      fprintf(stderr, "gpt2: hipGetSymbolAddress(scratch) failed on device %d: %s\n", dev, hipGetErrorString(e));
+      return -1;
+    }
+    g_scratch_ptr[dev] = ptr;
+  }
+  double* base = static_cast<double*>(g_scratch_ptr[dev]);
+  *partials = base;
+  *clip_scale = reinterpret_cast<float*>(base + kNormBlocks);
+  *nblk = kNormBlocks;
+  return 0;
 }
 
 }  // namespace gpt2k

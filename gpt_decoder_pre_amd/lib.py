@@ -38,7 +38,7 @@ ERROR_NAMES = {
 EXPORTS = ("gpt2_init", "gpt2_forward_loss", "gpt2_backward", "gpt2_accumulate", "gpt2_clip_adamw_step",
            "gpt2_destroy", "gpt2_sync_status", "gpt2_sync_params", "gpt2_get_step", "gpt2_set_step",
            "gpt2_tensor_info", "gpt2_activation", "gpt2_timing_enable", "gpt2_timing_read", "gpt2_timing_site",
-           "gpt2_embedding_backward",
+           "gpt2_embedding_backward", "gpt2_clip_adamw_step_static",
            "gpt2_lr_at", "gpt2_loader_open", "gpt2_loader_next", "gpt2_loader_next_host", "gpt2_loader_state",
            "gpt2_loader_seek", "gpt2_loader_close", "gpt2_checkpoint_save", "gpt2_checkpoint_load",
            "gpt2_infer_init", "gpt2_infer_prefill", "gpt2_infer_decode", "gpt2_infer_length", "gpt2_sample",
@@ -120,6 +120,8 @@ def load_library() -> ctypes.CDLL:
         "gpt2_loader_close": (None, [P]),
         "gpt2_checkpoint_save": (I, [P, ctypes.c_char_p, ctypes.POINTER(I64), I]),
         "gpt2_checkpoint_load": (I, [P, ctypes.c_char_p, ctypes.POINTER(I64), ctypes.POINTER(ctypes.c_int)]),
+        "gpt2_clip_adamw_step_static": (I, [ctypes.POINTER(gpt2_config), ctypes.POINTER(gpt2_buffers), P, I64,
+                                            F, F, F, F, F, F, P, P]),
         "gpt2_infer_init": (I, [ctypes.POINTER(gpt2_config), P, P, P, P, P, ctypes.POINTER(gpt2_infer_sizes),
                                 ctypes.POINTER(P)]),
         "gpt2_infer_prefill": (I, [P, P, I, I, P]),
@@ -299,6 +301,17 @@ class GPT2Step:
             raise ValueError("embedding_backward: dx0 must be a contiguous fp32 (B, T, C) tensor on the device")
         _check(self.lib.gpt2_embedding_backward(self.ctx, ctypes.c_void_p(idx.data_ptr()),
                                                 ctypes.c_void_p(dx0.data_ptr()), B, T), "gpt2_embedding_backward")
+
+    def clip_adamw_step_static(self, t, lr, beta1=0.9, beta2=0.95, eps=1e-8, weight_decay=0.1, max_norm=1.0):
+        """gpt2_clip_adamw_step_static on this object's buffers at step t (the
+        context's own step counter is not used or changed)."""
+        _check(self.lib.gpt2_clip_adamw_step_static(ctypes.byref(self.cfg), ctypes.byref(self.bufs),
+                                                    ctypes.c_void_p(self.stream.cuda_stream), t, lr, beta1, beta2,
+                                                    eps, weight_decay, max_norm,
+                                                    ctypes.c_void_p(self.d_norm.data_ptr()),
+                                                    ctypes.c_void_p(self.d_clipped.data_ptr())),
+               "gpt2_clip_adamw_step_static")
+        return self.d_norm, self.d_clipped
 
     def sync_status(self) -> int:
         return self.lib.gpt2_sync_status(self.ctx)

@@ -183,6 +183,27 @@ int gpt2_clip_adamw_step(gpt2_ctx *ctx, float lr, float beta1, float beta2, floa
                          float weight_decay, float max_norm, float *d_norm,
                          int32_t *d_clipped);
 
+/*
+ * gpt2_clip_adamw_step without a context or workspace, for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc).  The same kernels and the same
+ * arithmetic as gpt2_clip_adamw_step on the flat vectors of *bufs laid out
+ * for *cfg (params, grads, adam_m, adam_v, and params_bf16 in BF16 mode;
+ * workspace is ignored), with t the new AdamW step number (>= 1).  The
+ * norm's partial sums and the clip factor live in a static device array of
+ * the library (8,448 bytes on each GPU, held until the process ends) instead
+ * of a workspace; the call allocates nothing.  Calls that overlap on one GPU
+ * (two streams, or two threads) share that array and race: serialise them.
+ * The device current on the calling thread must be the stream's device.
+ * Errors: GPT2_ERR_ARG for an invalid config, NULL pointers, t < 1 or more
+ * than 2^40 parameters; GPT2_ERR_HIP if the scratch address cannot be found
+ * or a launch fails.
+ */
+int gpt2_clip_adamw_step_static(const gpt2_config *cfg, const gpt2_buffers *bufs,
+                                void *hip_stream, int64_t t, float lr, float beta1,
+                                float beta2, float eps, float weight_decay,
+                                float max_norm, float *d_norm, int32_t *d_clipped);
+
 /* Frees the host context (no device memory is owned). */
 void gpt2_destroy(gpt2_ctx *ctx);
 
