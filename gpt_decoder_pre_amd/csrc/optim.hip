@@ -42,11 +42,24 @@ void to_bf16(const float* src, void* dst, int64_t n, hipStream_t s) {
 
 constexpr int kNormBlocks = 1024;
 
+// Each thread keeps four 16-byte loads in flight per round (a read-only
+// stream needs that many bytes outstanding per CU to cover the HBM latency).
 __global__ __launch_bounds__(256) void sumsq_kernel(const float* __restrict__ g, int64_t n, double* part) {
   __shared__ double red[16];
   const int64_t n4 = n >> 2;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
   double acc = 0.0;
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += (int64_t)gridDim.x * blockDim.x) {
+  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  for (; i + 3 * stride < n4; i += 4 * stride) {
+    float v[4][4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) load4(g + 4 * (i + u * stride), v[u]);
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc += (double)v[u][e] * (double)v[u][e];
+  }
+  for (; i < n4; i += stride) {
     float v[4];
     load4(g + 4 * i, v);
 #pragma unroll
