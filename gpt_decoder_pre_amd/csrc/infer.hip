@@ -3,6 +3,7 @@
 // temperature / top-k / top-p sampling.
 #include "common.h"
 #include "infer_kernels.h"
+#include "kernels.h"
 
 namespace gpt2k {
 
@@ -43,38 +44,45 @@ void last_rows(const TA* src, TA* dst, int B, int T, int C, hipStream_t s) {
 }
 
 // One new query per sequence against its n_keys cached keys (the query's own
-// key and value are the last of them): workgroup (head, sequence).  The scores
-// of all keys go to LDS (one thread per key at a time), then their softmax;
-// then hd-wide groups of threads each sum the values of every G-th key and the
-// groups' sums are added in group order.
+// key and value are the last of them): workgroup (head, sequence).  A key's
+// row is read by TPK threads, 16 bytes each, so 256 / TPK keys are in flight
+// per pass: their scores go to LDS, then the block's softmax, then the same
+// threads sum p_j v_j for every KP-th key and the KP partial rows are added
+// in order.
 template <typename TA>
 __global__ __launch_bounds__(256) void decode_attn_kernel(const TA* __restrict__ qkv, const TA* __restrict__ cache,
                                                           TA* __restrict__ y, int n_keys, int Tmax, int C, int NH,
                                                           float scale) {
-  extern __shared__ float sm[];  // [n_keys] scores, then [groups][hd] partial sums; q in red
+  extern __shared__ float sm[];  // [n_keys] scores, then [KP][hd] partial rows
   __shared__ float red[16];
-  __shared__ float qs[256];
+  constexpr int V = 16 / sizeof(TA);  // elements per 16-byte chunk
   const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
   const int hd = C / NH;
-  const TA* q = qkv + (int64_t)b * 3 * C + h * hd;
-  for (int d = tid; d < hd; d += blockDim.x) qs[d] = to_f32(q[d]);
-  __syncthreads();
-  const TA* kb = cache + (int64_t)b * Tmax * 2 * C + h * hd;
+  const int tpk = hd / V;        // threads per key row (a power of two)
+  const int kp = 256 / tpk;      // keys per pass
+  const int sub = tid % tpk, kq = tid / tpk;
+  float q[V];
+  {
+    const TA* qr = qkv + (int64_t)b * 3 * C + h * hd + sub * V;
+    const u32x4 raw = *reinterpret_cast<const u32x4*>(qr);
+    unpack16<TA>(raw, q);
+  }
+  const TA* kb = cache + (int64_t)b * Tmax * 2 * C + h * hd + sub * V;
   float mx = -INFINITY;
-  for (int j = tid; j < n_keys; j += blockDim.x) {
-    const TA* k = kb + (int64_t)j * 2 * C;
-    float acc = 0.f;
-    for (int d = 0; d < hd; d += 4) {
-      float kv[4];
-      load4(k + d, kv);
-      acc = fmaf(qs[d], kv[0], acc);
-      acc = fmaf(qs[d + 1], kv[1], acc);
-      acc = fmaf(qs[d + 2], kv[2], acc);
-      acc = fmaf(qs[d + 3], kv[3], acc);
+  for (int j0 = 0; j0 < n_keys; j0 += kp) {
+    const int j = j0 + kq;
+    float part = 0.f;
+    if (j < n_keys) {
+      float k[V];
+      unpack16<TA>(*reinterpret_cast<const u32x4*>(kb + (int64_t)j * 2 * C), k);
+#pragma unroll
+      for (int e = 0; e < V; ++e) part = fmaf(q[e], k[e], part);
     }
-    acc *= scale;
-    sm[j] = acc;
-    mx = fmaxf(mx, acc);
+    for (int o = tpk / 2; o >= 1; o >>= 1) part += __shfl_xor(part, o, 64);
+    if (j < n_keys && sub == 0) {
+      sm[j] = part * scale;
+      mx = fmaxf(mx, part * scale);
+    }
   }
   mx = block_max(mx, red);
   float l = 0.f;
@@ -83,35 +91,129 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(const TA* __restrict__
     sm[j] = pj;
     l += pj;
   }
-  l = block_sum(l, red);  // ends with a barrier after the probabilities are written
+  l = block_sum(l, red);  // its barriers also order the writes of the probabilities
   __syncthreads();
-  const int groups = blockDim.x / hd;
-  const int g = tid / hd, d = tid % hd;
-  float* part = sm + n_keys;
-  if (g < groups) {
-    const TA* vb = kb + C + d;
-    float acc = 0.f;
-    for (int j = g; j < n_keys; j += groups) acc = fmaf(sm[j], to_f32(vb[(int64_t)j * 2 * C]), acc);
-    part[g * hd + d] = acc;
+  float acc[V];
+#pragma unroll
+  for (int e = 0; e < V; ++e) acc[e] = 0.f;
+  for (int j = kq; j < n_keys; j += kp) {
+    float v[V];
+    unpack16<TA>(*reinterpret_cast<const u32x4*>(kb + C + (int64_t)j * 2 * C), v);
+    const float pj = sm[j];
+#pragma unroll
+    for (int e = 0; e < V; ++e) acc[e] = fmaf(pj, v[e], acc[e]);
   }
+  float* part = sm + n_keys;
+#pragma unroll
+  for (int e = 0; e < V; ++e) part[kq * hd + sub * V + e] = acc[e];
   __syncthreads();
   if (tid < hd) {
-    float acc = 0.f;
-    for (int i = 0; i < groups; ++i) acc += part[i * hd + tid];
-    y[(int64_t)b * C + h * hd + tid] = from_f32<TA>(acc / l);
+    float sum = 0.f;
+    for (int i = 0; i < kp; ++i) sum += part[i * hd + tid];
+    y[(int64_t)b * C + h * hd + tid] = from_f32<TA>(sum / l);
   }
 }
 
 template <typename TA>
 bool decode_attn(const TA* qkv, const TA* cache, TA* y, int B, int n_keys, int Tmax, int C, int NH, hipStream_t s) {
   const int hd = C / NH;
-  if (hd > 256 || hd % 4 || n_keys < 1 || n_keys > Tmax) return false;
-  const int groups = 256 / hd;
-  const size_t lds = (size_t)(n_keys + groups * hd) * sizeof(float);
+  constexpr int V = 16 / sizeof(TA);
+  const int tpk = hd / V;
+  // 16-byte rows chunks: hd a multiple of V, tpk a power of two that fits a wavefront
+  if (hd % V || tpk < 1 || tpk > 64 || (tpk & (tpk - 1)) || C % V || n_keys < 1 || n_keys > Tmax) return false;
+  const int kp = 256 / tpk;
+  const size_t lds = (size_t)(n_keys + kp * hd) * sizeof(float);
   if (lds > 60 * 1024) return false;
   decode_attn_kernel<TA><<<dim3(NH, B), 256, lds, s>>>(qkv, cache, y, n_keys, Tmax, C, NH,
                                                        1.0f / sqrtf((float)hd));
   return true;
+}
+
+
+// ------------------------------------------------------------- skinny GEMM ----
+// C = epilogue(A B^T) for at most 32 rows (the one-token decoding step): A
+// (M x K, bf16, row stride lda), B (N x K, bf16, row stride ldb: a weight
+// matrix (out, in)).  A workgroup owns 32 output columns; its NW waves (4, or
+// 16 for long K) take every NW-th 16-wide k-step, one v_mfma_f32_32x32x16_bf16
+// each (rows past M and columns past N read as zero), then add their 32 x 32
+// partial products in LDS in wave order and apply the epilogue.  The weights
+// stream from HBM once; the rows of A stay in L2.
+template <int EPI, int NW>
+__global__ __launch_bounds__(64 * NW) void skinny_gemm_kernel(GemmArgs a) {
+  __shared__ float red[NW][32 * 33];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n0 = blockIdx.x * 32;
+  const int col = lane & 31, kh = lane >> 5;
+  const bf16* A = reinterpret_cast<const bf16*>(a.A);
+  const bf16* B = reinterpret_cast<const bf16*>(a.B);
+  const bool row_ok = col < a.M, col_ok = n0 + col < a.N;
+  const bf16* ar = A + (int64_t)(row_ok ? col : 0) * a.lda + 8 * kh;
+  const bf16* br = B + (int64_t)(col_ok ? n0 + col : 0) * a.ldb + 8 * kh;
+  f32x16 acc;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+  const int steps = a.K / 16;
+  int ks = wave;
+  for (; ks + 3 * NW < steps; ks += 4 * NW) {  // four steps per round, their loads first
+    bf16x8 af[4], bfr[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      af[u] = __builtin_bit_cast(bf16x8, ld16_or_zero(ar + 16 * (ks + NW * u), row_ok));
+      bfr[u] = __builtin_bit_cast(bf16x8, ld16_or_zero(br + 16 * (ks + NW * u), col_ok));
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[u], bfr[u], acc, 0, 0, 0);
+  }
+  for (; ks < steps; ks += NW) {
+    const bf16x8 af = __builtin_bit_cast(bf16x8, ld16_or_zero(ar + 16 * ks, row_ok));
+    const bf16x8 bfr = __builtin_bit_cast(bf16x8, ld16_or_zero(br + 16 * ks, col_ok));
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, bfr, acc, 0, 0, 0);
+  }
+  // acc[r] = partial C[row 8 (r / 4) + 4 kh + r % 4][column n0 + col]
+#pragma unroll
+  for (int r = 0; r < 16; ++r) red[wave][(8 * (r >> 2) + 4 * kh + (r & 3)) * 33 + col] = acc[r];
+  __syncthreads();
+  for (int o = tid; o < 32 * 32; o += 64 * NW) {
+    const int m = o >> 5, c = o & 31, n = n0 + c;
+    if (m >= a.M || n >= a.N) continue;
+    float v = red[0][m * 33 + c];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) v += red[w][m * 33 + c];
+    const float bias = a.bias ? a.bias[n] : 0.f;
+    const int64_t idx = (int64_t)m * a.ldc + n;
+    if constexpr (EPI == EPI_ACT) {
+      reinterpret_cast<bf16*>(a.C)[idx] = (bf16)(v + bias);
+    } else if constexpr (EPI == EPI_F32) {
+      reinterpret_cast<float*>(a.C)[idx] = v + bias;
+    } else if constexpr (EPI == EPI_RESID) {
+      reinterpret_cast<float*>(a.C)[idx] = a.resid[idx] + (v + bias);
+    } else if constexpr (EPI == EPI_GELU) {
+      float g, d;
+      gelu_and_grad(v + bias, g, d);
+      reinterpret_cast<bf16*>(a.C)[idx] = (bf16)d;
+      reinterpret_cast<bf16*>(a.C2)[idx] = (bf16)g;
+    }
+  }
+}
+
+template <int NW>
+bool skinny_launch(GemmEpilogue epi, const GemmArgs& a, hipStream_t s) {
+  const unsigned grid = (unsigned)((a.N + 31) / 32);
+  switch (epi) {
+    case EPI_ACT: skinny_gemm_kernel<EPI_ACT, NW><<<grid, 64 * NW, 0, s>>>(a); return true;
+    case EPI_F32: skinny_gemm_kernel<EPI_F32, NW><<<grid, 64 * NW, 0, s>>>(a); return true;
+    case EPI_RESID: skinny_gemm_kernel<EPI_RESID, NW><<<grid, 64 * NW, 0, s>>>(a); return true;
+    case EPI_GELU: skinny_gemm_kernel<EPI_GELU, NW><<<grid, 64 * NW, 0, s>>>(a); return true;
+    default: return false;
+  }
+}
+
+bool gemm_skinny(GemmEpilogue epi, const GemmArgs& a, hipStream_t s) {
+  if (a.M < 1 || a.M > 32 || a.N < 1 || a.K < 16 || a.K % 16 || a.lda % 8 || a.ldb % 8) return false;
+  // long K over few columns (the MLP's output projection): sixteen waves share
+  // the k-steps, so that a workgroup's chain of dependent steps stays short
+  if (a.K > 1024 && a.N <= 4096) return skinny_launch<16>(epi, a, s);
+  return skinny_launch<4>(epi, a, s);
 }
 
 // ---------------------------------------------------------------- sampling ----

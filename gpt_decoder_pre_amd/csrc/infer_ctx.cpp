@@ -96,6 +96,13 @@ int hip_ok() {
   return GPT2_OK;
 }
 
+// A product of the forward pass: the skinny kernel for the few rows of a
+// decoding step in bf16 mode, else the step's GEMM.
+bool product(gpt2_infer* c, GemmEpilogue epi, const GemmArgs& g, hipStream_t s) {
+  if (c->bf16 && g.M <= 32 && gemm_skinny(epi, g, s)) return true;
+  return gemm(LAYOUT_NT, epi, c->bf16, g, s);
+}
+
 // The blocks, final LayerNorm and lm_head over M = B T rows (prefill, T > 1
 // or len == 0) or B rows at position len (decode), from x0 (the embeddings).
 template <typename TA>
@@ -112,7 +119,7 @@ int forward(gpt2_infer* c, int B, int T, bool decode, float* d_logits) {
     layernorm_fwd<TA>(xa, c->P("ln1_w", l), c->P("ln1_b", l), ln, c->mean, c->rstd, M, C, s);
     GemmArgs g = args(ln, C, c->W("qkv_w", l), C, M, 3 * C, C, qkv, 3 * C);
     g.bias = c->has("qkv_b") ? c->P("qkv_b", l) : nullptr;
-    if (!gemm(LAYOUT_NT, EPI_ACT, bf, g, s)) return GPT2_ERR_ARG;
+    if (!product(c, EPI_ACT, g, s)) return GPT2_ERR_ARG;
     TA* cache = (TA*)c->cache_l(l);
     if (decode) {
       kv_store<TA>(qkv, cache, B, 1, c->len, c->Tmax, C, s);
@@ -125,16 +132,16 @@ int forward(gpt2_infer* c, int B, int T, bool decode, float* d_logits) {
     g = args(atty, C, c->W("proj_w", l), C, M, C, C, xb, C);
     g.bias = c->P("proj_b", l);
     g.resid = xa;
-    if (!gemm(LAYOUT_NT, EPI_RESID, bf, g, s)) return GPT2_ERR_ARG;
+    if (!product(c, EPI_RESID, g, s)) return GPT2_ERR_ARG;
     layernorm_fwd<TA>(xb, c->P("ln2_w", l), c->P("ln2_b", l), ln, c->mean, c->rstd, M, C, s);
     g = args(ln, C, c->W("fc_w", l), C, M, 4 * C, C, c->fcgd, 4 * C);
     g.bias = c->P("fc_b", l);
     g.C2 = c->fcg;
-    if (!gemm(LAYOUT_NT, EPI_GELU, bf, g, s)) return GPT2_ERR_ARG;
+    if (!product(c, EPI_GELU, g, s)) return GPT2_ERR_ARG;
     g = args(c->fcg, 4 * C, c->W("fcproj_w", l), 4 * C, M, C, 4 * C, xa, C);
     g.bias = c->P("fcproj_b", l);
     g.resid = xb;
-    if (!gemm(LAYOUT_NT, EPI_RESID, bf, g, s)) return GPT2_ERR_ARG;
+    if (!product(c, EPI_RESID, g, s)) return GPT2_ERR_ARG;
   }
   layernorm_fwd<TA>(xa, c->P("lnf_w"), c->P("lnf_b"), (TA*)c->lnf, c->mean, c->rstd, M, C, s);
   const void* hrows = c->lnf;
@@ -143,7 +150,7 @@ int forward(gpt2_infer* c, int B, int T, bool decode, float* d_logits) {
     hrows = c->last;
   }
   GemmArgs g = args(hrows, C, c->W(c->has("lm_head") ? "lm_head" : "wte"), C, B, c->Vp, C, d_logits, c->Vp);
-  if (!gemm(LAYOUT_NT, EPI_F32, bf, g, s)) return GPT2_ERR_ARG;
+  if (!product(c, EPI_F32, g, s)) return GPT2_ERR_ARG;
   return hip_ok();
 }
 

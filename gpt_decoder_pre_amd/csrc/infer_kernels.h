@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "kernels.h"
+
 namespace gpt2k {
 
 // cache[(b Tmax + t0 + t)][0 : 2C] = qkv[b T + t][C : 3C] (the keys and values of
@@ -18,6 +20,12 @@ void last_rows(const TA* src, TA* dst, int B, int T, int C, hipStream_t s);
 // one its own).  Returns false for shapes the kernel does not take.
 template <typename TA>
 bool decode_attn(const TA* qkv, const TA* cache, TA* y, int B, int n_keys, int Tmax, int C, int NH, hipStream_t s);
+// bf16 C = epilogue(A B^T) for M <= 32 rows with the weights read once (the
+// one-token decoding step); epilogues EPI_ACT, EPI_F32, EPI_RESID (C fp32 =
+// resid + acc + bias, resid with C's row stride) and EPI_GELU.  Returns false
+// (nothing launched) for shapes it does not take: M > 32, K % 16, unaligned
+// rows.
+bool gemm_skinny(GemmEpilogue epi, const GemmArgs& a, hipStream_t s);
 // out[b] = a column of logits row b (fp32, row stride ld) among [0, V):
 // temperature <= 0 or top_k == 1: the first largest; else z = logits / T,
 // columns below the k-th largest z dropped (top_k > 0), p = softmax(z),
