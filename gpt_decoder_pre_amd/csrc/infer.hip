@@ -224,10 +224,58 @@ bool gemm_skinny(GemmEpilogue epi, const GemmArgs& a, hipStream_t s) {
 constexpr int kSampleThreads = 1024;
 constexpr int kSampleNPT = 64;  // columns per thread: vocabularies up to 65,536
 
-// order-preserving map of a float to an unsigned key (-inf lowest)
+// block-wide integer sum with one barrier: consecutive calls alternate between
+// the two halves of scratch (32 entries), so a half is rewritten only after
+// every thread has passed the barrier of the call in between
+DEVI int block_count_alt(int v, int* scratch, int parity) {
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+  int* half = scratch + 16 * parity;
+  if ((threadIdx.x & 63) == 0) half[threadIdx.x >> 6] = v;
+  __syncthreads();
+  int r = 0;
+  for (int w = 0; w < (int)(blockDim.x >> 6); ++w) r += half[w];
+  return r;
+}
+
+// exclusive prefix sum over the block's threads in thread order (every
+// thread gets its own; blockDim.x a multiple of 64, at most 1024)
+DEVI int block_excl_scan(int v, int* scratch) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  int incl = v;
+  for (int o = 1; o < 64; o <<= 1) {
+    const int u = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += u;
+  }
+  __syncthreads();
+  if (lane == 63) scratch[w] = incl;
+  __syncthreads();
+  int off = 0;
+  for (int i = 0; i < w; ++i) off += scratch[i];
+  return off + incl - v;
+}
+
+// order-preserving map of a float to an unsigned key (-inf lowest), and back.
+// Without -0 and NaN among the values, key(x) >= K  <=>  x >= key_float(K) for
+// every K the threshold search visits.
 DEVI uint32_t order_key(float f) {
   const uint32_t u = __float_as_uint(f);
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+DEVI float key_float(uint32_t k) { return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k); }
+
+// inclusive prefix sum of a float over the block's threads in thread order
+DEVI float block_incl_scan(float v, float* scratch) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  for (int o = 1; o < 64; o <<= 1) {
+    const float u = __shfl_up(v, o, 64);
+    if (lane >= o) v += u;
+  }
+  __syncthreads();
+  if (lane == 63) scratch[w] = v;
+  __syncthreads();
+  float off = 0.f;
+  for (int i = 0; i < w; ++i) off += scratch[i];
+  return off + v;
 }
 
 // block-wide integer sum (every thread gets it)
@@ -247,6 +295,7 @@ __global__ __launch_bounds__(kSampleThreads) void sample_kernel(const float* __r
                                                                 int32_t* __restrict__ out) {
   __shared__ float redf[16];
   __shared__ int redi[16];
+  __shared__ int redi2[32];
   __shared__ float scan[kSampleThreads];
   __shared__ int pick;
   const int b = blockIdx.x, t = threadIdx.x;
@@ -281,22 +330,25 @@ __global__ __launch_bounds__(kSampleThreads) void sample_kernel(const float* __r
   }
   const float inv_t = 1.0f / temperature;
 #pragma unroll
-  for (int i = 0; i < kSampleNPT; ++i) z[i] *= inv_t;
+  for (int i = 0; i < kSampleNPT; ++i) z[i] = z[i] * inv_t + 0.0f;  // + 0 turns -0 into +0
   // top-k: the k-th largest key; columns below it drop out
   uint32_t kth = 0;
   if (top_k > 0 && top_k < V) {
+    __syncthreads();
     for (int bit = 31; bit >= 0; --bit) {
       const uint32_t cand = kth | (1u << bit);
+      const float cf = key_float(cand);
       int cnt = 0;
 #pragma unroll
-      for (int i = 0; i < kSampleNPT; ++i) cnt += order_key(z[i]) >= cand ? 1 : 0;
-      if (block_count(cnt, redi) >= top_k) kth = cand;
+      for (int i = 0; i < kSampleNPT; ++i) cnt += z[i] >= cf ? 1 : 0;
+      if (block_count_alt(cnt, redi2, bit & 1) >= top_k) kth = cand;
     }
   }
   float mx = -INFINITY;
+  const float kth_f = key_float(kth);
 #pragma unroll
   for (int i = 0; i < kSampleNPT; ++i) {
-    if (order_key(z[i]) < kth || c0 + i >= V) z[i] = -INFINITY;
+    if (z[i] < kth_f || c0 + i >= V) z[i] = -INFINITY;
     mx = fmaxf(mx, z[i]);
   }
   mx = block_max(mx, redf);
@@ -309,6 +361,35 @@ __global__ __launch_bounds__(kSampleThreads) void sample_kernel(const float* __r
   }
   const float Z = block_sum(part, redf);
   // top-p: the largest e-threshold whose kept mass reaches top_p Z
+  if (top_p > 0.f && top_p < 1.f) {
+    const float need = top_p * Z;
+    // few columns left (top-k): gather them in column order and give each
+    // its mass at or above it, S(e) = sum of the kept e' >= e; the threshold
+    // is the largest e with S(e) >= need
+    int mine_n = 0;
+#pragma unroll
+    for (int i = 0; i < kSampleNPT; ++i) mine_n += z[i] > 0.f ? 1 : 0;
+    const int nk = block_count(mine_n, redi);
+    if (nk <= kSampleThreads) {
+      int pos = block_excl_scan(mine_n, redi);
+#pragma unroll
+      for (int i = 0; i < kSampleNPT; ++i)
+        if (z[i] > 0.f) scan[pos++] = z[i];
+      __syncthreads();
+      float thr_e = 0.f;
+      if (t < nk) {
+        const float mine_e = scan[t];
+        float sum = 0.f;
+        for (int j = 0; j < nk; ++j) sum += scan[j] >= mine_e ? scan[j] : 0.f;
+        if (sum >= need) thr_e = mine_e;
+      }
+      const float c = block_max(thr_e, redf);
+#pragma unroll
+      for (int i = 0; i < kSampleNPT; ++i) z[i] = z[i] >= c ? z[i] : 0.f;
+      __syncthreads();  // scan[] is reused below
+      top_p = 1.f;      // done
+    }
+  }
   if (top_p > 0.f && top_p < 1.f) {
     const float need = top_p * Z;
     uint32_t thr = 0;
@@ -329,15 +410,9 @@ __global__ __launch_bounds__(kSampleThreads) void sample_kernel(const float* __r
   float mine = 0.f;
 #pragma unroll
   for (int i = 0; i < kSampleNPT; ++i) mine += z[i];
-  scan[t] = mine;
   if (t == 0) pick = -1;
+  scan[t] = block_incl_scan(mine, redf);
   __syncthreads();
-  for (int o = 1; o < kSampleThreads; o <<= 1) {  // inclusive scan (Hillis-Steele)
-    const float add = t >= o ? scan[t - o] : 0.f;
-    __syncthreads();
-    scan[t] += add;
-    __syncthreads();
-  }
   const float total = scan[kSampleThreads - 1];
   const float target = uniform[b] * total;
   const float before = t > 0 ? scan[t - 1] : 0.f;
