@@ -150,6 +150,19 @@ struct TileLoader {
   }
 };
 
+// Tile t of one k-split: groups of GM tile-rows are walked column by column,
+// so that neighbouring tiles share operand rows and columns.
+DEVI void tile_walk(const GemmArgs& p, int tiles_m, int tiles_n, int t, int& tm, int& tn) {
+  const int GM = p.group_m > 0 ? p.group_m : 8;
+  const int per_group = GM * tiles_n;
+  const int g = t / per_group;
+  const int first_m = g * GM;
+  const int gm = min(GM, tiles_m - first_m);
+  const int w = t - g * per_group;
+  tm = first_m + w % gm;
+  tn = w / gm;
+}
+
 // Tile order.  The dispatcher deals workgroups round-robin to the eight XCDs
 // (each with its own L2) in linear block order, so the linear id is first
 // renumbered to give every XCD a contiguous range; that range is walked
@@ -167,14 +180,7 @@ DEVI void tile_coords(const GemmArgs& p, int tiles_m, int tiles_n, int b, int nb
   const int tiles = tiles_m * tiles_n;
   split = t / tiles;
   t -= split * tiles;
-  const int GM = p.group_m > 0 ? p.group_m : 8;
-  const int per_group = GM * tiles_n;
-  const int g = t / per_group;
-  const int first_m = g * GM;
-  const int gm = min(GM, tiles_m - first_m);
-  const int w = t - g * per_group;
-  tm = first_m + w % gm;
-  tn = w / gm;
+  tile_walk(p, tiles_m, tiles_n, t, tm, tn);
 }
 
 template <bool A_K, bool B_K, int BM, int BN, int BK, int WGM, int WGN, int EPI>
@@ -329,11 +335,11 @@ struct DirectLoader {
 // ----------------------------------------------------------- epilogue ----
 // Writes one wave's FM x FN accumulator tiles (rows mb.., columns nb..).
 // acc[i][j][4q + e] holds C[mb + 32 i + lane % 32][nb + 32 j + 8 q + 4 (lane / 32) + e].
-// bf16 outputs are staged through this wave's LDS region (32 FM rows of
-// 32 FN + 8 elements) so that every store instruction writes whole row
-// segments (16 bytes per lane along n) instead of 16 bytes into each of 32
-// rows; lines then reach L2 complete.  Other outputs go straight from the
-// registers.
+// bf16 outputs are staged through this wave's LDS region (RB rows of
+// 32 FN + 8 elements: the whole wave tile, or one 32-row block of it at a
+// time) so that every store instruction writes whole row segments (16 bytes
+// per lane along n) instead of 16 bytes into each of 32 rows; lines then
+// reach L2 complete.  Other outputs go straight from the registers.
 template <int EPI>
 constexpr bool epi_staged() {
   return EPI == EPI_ACT || EPI == EPI_LOGITS || EPI == EPI_GELU || EPI == EPI_GELU_BWD;
@@ -341,113 +347,137 @@ constexpr bool epi_staged() {
 
 // aux_pre (EPI_GELU_BWD, staged, or null): this wave's aux tile already in
 // registers, chunk `it` of the staging loop below in aux_pre[it].
-template <int EPI, int FM, int FN, bool STAGED>
+template <int EPI, int FM, int FN, bool STAGED, int RB = 32 * FM>
 DEVI void gemm_epilogue(const GemmArgs& p, f32x16 (&acc)[FM][FN], bf16* region, int mb, int nb, int lane, int split,
                         const u32x4* aux_pre = nullptr) {
   constexpr int WTM = 32 * FM, WTN = 32 * FN;
   const int lc = lane & 31, hl = lane >> 5;
   if constexpr (STAGED) {
+    // RB rows of the wave tile per pass (the region holds RB rows of WTN + 8
+    // elements): the whole tile, or 32-row blocks where LDS is short.
     constexpr int SLD = WTN + 8;  // staged row stride (elements)
     constexpr int NOUT = EPI == EPI_GELU ? 2 : 1;
-    constexpr int CPR = WTN / 8;  // 16-byte chunks per staged row
-    if constexpr (EPI == EPI_GELU_BWD) {
-      // the gelu'(u) tile comes in whole row segments too
-      const bf16* aux = reinterpret_cast<const bf16*>(p.aux);
+    constexpr int CPR = WTN / 8;       // 16-byte chunks per staged row
+    constexpr int RBF = RB / 32;       // accumulator row blocks per pass
+    constexpr int ITB = RB * CPR / 64;  // 16-byte chunks per lane for one pass
+    static_assert(RB % 32 == 0 && WTM % RB == 0, "whole 32-row blocks per pass");
+    static_assert(WTN / 2 <= 64, "one column pair per lane for the column sums");
+    float cs0 = 0.f, cs1 = 0.f;  // GELU', 32-row passes: this lane's column pair, current 64-row chunk
 #pragma unroll
-      for (int it = 0; it < WTM * CPR / 64; ++it) {
-        const int q = it * 64 + lane;
-        const int r = q / CPR, c = q % CPR;
-        const int m = mb + r, n = nb + 8 * c;
-        *reinterpret_cast<u32x4*>(region + r * SLD + 8 * c) =
-            aux_pre ? aux_pre[it] : ld16_or_zero(aux + (int64_t)m * p.ldc + n, m < p.M && n < p.N);
-        if (it % 8 == 7) __builtin_amdgcn_sched_barrier(0);  // bounded loads in flight
+    for (int pb = 0; pb < WTM / RB; ++pb) {
+      const int mi = mb + RB * pb;
+      if constexpr (EPI == EPI_GELU_BWD) {
+        // the gelu'(u) rows come in whole row segments too
+        const bf16* aux = reinterpret_cast<const bf16*>(p.aux);
+#pragma unroll
+        for (int it = 0; it < ITB; ++it) {
+          const int q = it * 64 + lane;
+          const int r = q / CPR, c = q % CPR;
+          const int m = mi + r, n = nb + 8 * c;
+          *reinterpret_cast<u32x4*>(region + r * SLD + 8 * c) =
+              aux_pre ? aux_pre[pb * ITB + it] : ld16_or_zero(aux + (int64_t)m * p.ldc + n, m < p.M && n < p.N);
+          if (it % 8 == 7) __builtin_amdgcn_sched_barrier(0);  // bounded loads in flight
+        }
+        __builtin_amdgcn_s_waitcnt(0xc07f);
+        __builtin_amdgcn_wave_barrier();
       }
-      __builtin_amdgcn_s_waitcnt(0xc07f);
-      __builtin_amdgcn_wave_barrier();
-    }
 #pragma unroll
-    for (int o = 0; o < NOUT; ++o) {
+      for (int o = 0; o < NOUT; ++o) {
 #pragma unroll
-      for (int i = 0; i < FM; ++i)
+        for (int ib = 0; ib < RBF; ++ib) {
+          const int i = pb * RBF + ib;
+          const int rl = ib * 32 + lc;  // this lane's staged row
 #pragma unroll
-        for (int j = 0; j < FN; ++j)
+          for (int j = 0; j < FN; ++j)
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const int nl = j * 32 + 8 * q + 4 * hl;
-            const int n = nb + nl;
-            float v[4] = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
-            if constexpr (EPI == EPI_ACT || EPI == EPI_GELU) {
-              if (o == 0 && p.bias && n < p.N) {
-                float bb[4];
-                load4(p.bias + n, bb);
+            for (int q = 0; q < 4; ++q) {
+              const int nl = j * 32 + 8 * q + 4 * hl;
+              const int n = nb + nl;
+              float v[4] = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+              if constexpr (EPI == EPI_ACT || EPI == EPI_GELU) {
+                if (o == 0 && p.bias && n < p.N) {
+                  float bb[4];
+                  load4(p.bias + n, bb);
 #pragma unroll
-                for (int e = 0; e < 4; ++e) v[e] += bb[e];
-              }
-            }
-            if constexpr (EPI == EPI_GELU) {
-              // pass 0 writes gelu'(u) and leaves gelu(u) in the accumulators
-              // for pass 1: one sigmoid per element
-              if (o == 0) {
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                  float g;
-                  gelu_and_grad(v[e], g, v[e]);
-                  acc[i][j][4 * q + e] = g;
+                  for (int e = 0; e < 4; ++e) v[e] += bb[e];
                 }
               }
+              if constexpr (EPI == EPI_GELU) {
+                // pass 0 writes gelu'(u) and leaves gelu(u) in the accumulators
+                // for pass 1: one sigmoid per element
+                if (o == 0) {
+#pragma unroll
+                  for (int e = 0; e < 4; ++e) {
+                    float g;
+                    gelu_and_grad(v[e], g, v[e]);
+                    acc[i][j][4 * q + e] = g;
+                  }
+                }
+              }
+              if constexpr (EPI == EPI_GELU_BWD) {
+                float d[4];
+                load4(region + rl * SLD + nl, d);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) v[e] *= d[e];
+              }
+              store4(region + rl * SLD + nl, v);
+              // one accumulator block at a time: the scheduler must not copy
+              // every accumulator out of the AGPRs at once
+              if (q == 3) __builtin_amdgcn_sched_barrier(0);
             }
-            if constexpr (EPI == EPI_GELU_BWD) {
-              float d[4];
-              load4(region + (i * 32 + lc) * SLD + nl, d);
+        }
+        __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's LDS writes are done
+        __builtin_amdgcn_wave_barrier();
+        bf16* out = reinterpret_cast<bf16*>(o == 0 ? p.C : p.C2);
 #pragma unroll
-              for (int e = 0; e < 4; ++e) v[e] *= d[e];
-            }
-            store4(region + (i * 32 + lc) * SLD + nl, v);
-            // one accumulator block at a time: the scheduler must not copy
-            // every accumulator out of the AGPRs at once
-            if (q == 3) __builtin_amdgcn_sched_barrier(0);
-          }
-      __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's LDS writes are done
-      __builtin_amdgcn_wave_barrier();
-      bf16* out = reinterpret_cast<bf16*>(o == 0 ? p.C : p.C2);
-#pragma unroll
-      for (int it = 0; it < WTM * CPR / 64; ++it) {
-        const int q = it * 64 + lane;
-        const int r = q / CPR, c = q % CPR;
-        const int m = mb + r, n = nb + 8 * c;
-        if (m < p.M && n < p.N)
-          *reinterpret_cast<u32x4*>(out + (int64_t)m * p.ldc + n) =
-              *reinterpret_cast<const u32x4*>(region + r * SLD + 8 * c);
-      }
-      __builtin_amdgcn_s_waitcnt(0xc07f);
-      __builtin_amdgcn_wave_barrier();
-    }
-    if constexpr (EPI == EPI_GELU_BWD && WTM % 64 == 0) {
-      // column sums of the staged (bf16) tile per 64-row chunk: the bias
-      // gradient of the layer whose pre-activation gradient this is.  Rows are
-      // added in ascending order, as a separate column-sum pass over C would.
-      if (p.colsum) {
-#pragma unroll
-        for (int c0 = 0; c0 < WTM / 64; ++c0) {
-          const int rows = min(64, p.M - (mb + 64 * c0));  // wave-uniform
-          if (rows <= 0) break;
-          for (int pc = lane; pc < WTN / 2; pc += 64) {
-            const bf16* col = region + 64 * c0 * SLD + 2 * pc;
-            float s0 = 0.f, s1 = 0.f;
+        for (int it = 0; it < ITB; ++it) {
+          const int q = it * 64 + lane;
+          const int r = q / CPR, c = q % CPR;
+          const int m = mi + r, n = nb + 8 * c;
+          if (m < p.M && n < p.N)
+            *reinterpret_cast<u32x4*>(out + (int64_t)m * p.ldc + n) =
+                *reinterpret_cast<const u32x4*>(region + r * SLD + 8 * c);
+        }
+        if constexpr (EPI == EPI_GELU_BWD && WTM % 64 == 0) {
+          // column sums of the staged (bf16) rows per 64-row chunk: the bias
+          // gradient of the layer whose pre-activation gradient this is.  Rows
+          // are added in ascending order, as a separate column-sum pass over C
+          // would.
+          if (p.colsum && lane < WTN / 2) {
+            const int n = nb + 2 * lane;
+            auto sum_rows = [&](int r0, int rows) {
+              const bf16* col = region + r0 * SLD + 2 * lane;
 #pragma unroll 8
-            for (int r = 0; r < rows; ++r) {
-              const uint32_t w = *reinterpret_cast<const uint32_t*>(col + r * SLD);
-              s0 += __uint_as_float(w << 16);
-              s1 += __uint_as_float(w & 0xffff0000u);
-            }
-            const int n = nb + 2 * pc;
-            if (n < p.N) {
-              float* out = p.colsum + (int64_t)((mb >> 6) + c0) * p.N + n;
-              out[0] = s0;
-              out[1] = s1;
+              for (int r = 0; r < rows; ++r) {
+                const uint32_t w = *reinterpret_cast<const uint32_t*>(col + r * SLD);
+                cs0 += __uint_as_float(w << 16);
+                cs1 += __uint_as_float(w & 0xffff0000u);
+              }
+            };
+            auto flush = [&](int c0) {  // chunk of rows c0 .. c0 + 63
+              if (n < p.N) {
+                float* cp = p.colsum + (int64_t)(c0 >> 6) * p.N + n;
+                cp[0] = cs0;
+                cp[1] = cs1;
+              }
+              cs0 = cs1 = 0.f;
+            };
+            if constexpr (RB >= 64) {
+#pragma unroll
+              for (int c = 0; c < RB / 64; ++c) {
+                const int c0 = mi + 64 * c;
+                if (c0 >= p.M) break;  // wave-uniform
+                sum_rows(64 * c, min(64, p.M - c0));
+                flush(c0);
+              }
+            } else {
+              sum_rows(0, min(32, p.M - mi));  // wave-uniform; none past M
+              if ((pb & 1) && mi - 32 < p.M) flush(mi - 32);
             }
           }
         }
+        __builtin_amdgcn_s_waitcnt(0xc07f);
+        __builtin_amdgcn_wave_barrier();
       }
     }
   } else if constexpr (EPI == EPI_RESID && FM * FN <= 6) {
@@ -638,7 +668,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, OCC) void gemm_lds_kernel(GemmArgs 
 // another wave, so the k-loop is scheduled explicitly: after every MFMA the
 // wave issues at most one fragment read for the next 16-k step (double-
 // buffered fragment registers) and a share of the direct loads of a later
-// k-tile (the schedule is described in w4_tile).  A k-tile's only
+// k-tile (the schedule is described in w4_tiles).  A k-tile's only
 // barrier sits before its last 16-k step, once every wave holds that step's
 // fragments.  Measured on MI355X the loop runs at about 95% of the MFMA peak
 // without the operand loads; with them it is bound by the operand stream
@@ -688,39 +718,53 @@ struct SaddrLoader {
   }
 };
 
-// LDS elements of the one-wave-per-SIMD tile (two operand stages, or the
-// staged epilogue if larger).
-template <int BM, int BN>
+// LDS elements of the one-wave-per-SIMD tile: two operand stages; the staged
+// epilogue of a single tile takes the whole wave tile at once (over both
+// stages), that of a persistent workgroup 32-row blocks in the second stage
+// (the first is then receiving the next tile's loads).
+template <int BM, int BN, bool PERSIST>
 constexpr int w4_lds_elems() {
   constexpr int STAGE = (BM + BN) * 64, EPI_ELEMS = 4 * (BM / 2) * (BN / 2 + 8);
-  return 2 * STAGE > EPI_ELEMS ? 2 * STAGE : EPI_ELEMS;
+  return PERSIST || 2 * STAGE > EPI_ELEMS ? 2 * STAGE : EPI_ELEMS;
 }
 
-// One BM x BN output tile (tile row tm, column tn, k-split `split`) of p.
-template <bool A_K, bool B_K, int BM, int BN, int EPI>
-DEVI void w4_tile(const GemmArgs& p, int tm, int tn, int split, bf16* smem) {
+// A sequence of BM x BN output tiles of p, one after the other in this
+// workgroup: next(tm, tn, split) gives the coordinates of the next tile
+// (tile row tm, column tn, k-split split) or returns false.  Between two
+// tiles the loads of the next tile's first k-tile go out before the
+// epilogue of the current one (which stages through the other stage), so
+// that their latency is spent storing instead of waiting.
+template <bool A_K, bool B_K, int BM, int BN, int EPI, bool PERSIST, class Next>
+DEVI void w4_tiles(const GemmArgs& p, bf16* smem, Next next) {
   constexpr int BK = 64, NW = 4;
   constexpr int WTM = BM / 2, WTN = BN / 2;
   constexpr int FM = WTM / 32, FN = WTN / 32;
   constexpr int STAGE = (BM + BN) * BK;  // elements
   constexpr int SLD = WTN + 8;           // staged epilogue row stride
+  static_assert(!PERSIST || NW * 32 * SLD <= STAGE, "32-row staging fits in one stage");
   using LA = SaddrLoader<A_K, BM, NW>;
   using LB = SaddrLoader<B_K, BN, NW>;
   constexpr int LPW = LA::PER_WAVE + LB::PER_WAVE;
   constexpr int G = FM * FN;  // MFMAs per 16-k step
 
+  int tm, tn, split;
+  if (!next(tm, tn, split)) return;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
-  const int m0 = tm * BM, n0 = tn * BN;
-  const int kbeg = split * p.k_per_split;
-  const int kend = min(p.K, kbeg + p.k_per_split);
-  const int nkt = kend > kbeg ? (kend - kbeg) / BK : 0;
-
+  int m0, n0, kbeg, nkt;
   LA la;
   LB lb;
-  la.init(reinterpret_cast<const bf16*>(p.A), p.lda, m0, p.M, kbeg, smem, wave, lane);
-  lb.init(reinterpret_cast<const bf16*>(p.B), p.ldb, n0, p.N, kbeg, smem + BM * BK, wave, lane);
+  // operand loaders of tile (tm, tn, split)
+  auto setup = [&]() {
+    m0 = tm * BM;
+    n0 = tn * BN;
+    kbeg = split * p.k_per_split;
+    const int kend = min(p.K, kbeg + p.k_per_split);
+    nkt = kend > kbeg ? (kend - kbeg) / BK : 0;
+    la.init(reinterpret_cast<const bf16*>(p.A), p.lda, m0, p.M, kbeg, smem, wave, lane);
+    lb.init(reinterpret_cast<const bf16*>(p.B), p.ldb, n0, p.N, kbeg, smem + BM * BK, wave, lane);
+  };
   constexpr uint32_t kStageBytes = STAGE * 2;
   // direct load number d (A loads first) of k-tile kt into the stage at stage_off
   auto dma = [&](int d, int kt, uint32_t stage_off) {
@@ -730,21 +774,6 @@ DEVI void w4_tile(const GemmArgs& p, int tm, int tn, int split, bf16* smem) {
 
   constexpr bool kBiasInit = EPI == EPI_ACT || EPI == EPI_GELU || EPI == EPI_RESID;
   f32x16 acc[FM][FN];
-#pragma unroll
-  for (int j = 0; j < FN; ++j)
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      float b[4] = {0.f, 0.f, 0.f, 0.f};
-      if constexpr (kBiasInit) {
-        const int n = n0 + wn * WTN + j * 32 + 8 * q + 4 * (lane >> 5);
-        if (p.bias && n < p.N && split == 0) load4(p.bias + n, b);
-      }
-#pragma unroll
-      for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) acc[i][j][4 * q + e] = b[e];
-    }
-
   bf16x8 fa[2][FM], fb[2][FN];
   auto read_a = [&](int buf, int i, const bf16* st, int kk) {
     fa[buf][i] = frag<A_K, BM, BK>(st, wm * WTM + i * 32, kk, lane);
@@ -760,10 +789,9 @@ DEVI void w4_tile(const GemmArgs& p, int tm, int tn, int split, bf16* smem) {
   constexpr int CPR = WTN / 8, NA = WTM * CPR / 64;  // 16-byte loads per lane
   constexpr bool kAuxPre = EPI == EPI_GELU_BWD && 4 * NA <= 48;
   u32x4 auxr[kAuxPre ? NA : 1];
-  const int am0 = m0 + wm * WTM, an0 = n0 + wn * WTN;
   auto aux_load = [&](int j) {
     const int q = j * 64 + lane, r = q / CPR, c = q % CPR;
-    const int m = am0 + r, n = an0 + 8 * c;
+    const int m = m0 + wm * WTM + r, n = n0 + wn * WTN + 8 * c;
     auxr[j] = ld16_or_zero(reinterpret_cast<const bf16*>(p.aux) + (int64_t)m * p.ldc + n, m < p.M && n < p.N);
   };
   auto aux_share = [&](int kt) {  // k-tiles 0 .. nkt-2 each load their share
@@ -830,52 +858,129 @@ DEVI void w4_tile(const GemmArgs& p, int tm, int tn, int split, bf16* smem) {
   };
 
   // every split has at least one k-tile (the host requires K = splits x
-  // k_per_split with k_per_split a positive multiple of 64).  Prologue: k-tile
-  // 0 whole, chunk 0 of k-tile 1 (the rest follows in k-tile 0's steps).
+  // k_per_split with k_per_split a positive multiple of 64).  First tile:
+  // k-tile 0 whole, chunk 0 of k-tile 1 (the rest follows in k-tile 0's
+  // steps).
+  setup();
 #pragma unroll
   for (int d = 0; d < LPW; ++d) dma(d, 0, 0);
   if (nkt > 1) {
 #pragma unroll
     for (int d = 0; d < C0; ++d) dma(d, 1, kStageBytes);
-    wait_vmcnt<C0>();
-  } else {
-    wait_vmcnt<0>();
   }
-  lds_barrier();
+  for (;;) {
+    // k-tile 0 has landed (and the previous tile's stores have gone out)
+    if (nkt > 1) wait_vmcnt<C0>();
+    else wait_vmcnt<0>();
+    lds_barrier();
 #pragma unroll
-  for (int i = 0; i < FM; ++i) read_a(0, i, smem, 0);
+    for (int j = 0; j < FN; ++j)
 #pragma unroll
-  for (int j = 0; j < FN; ++j) read_b(0, j, smem, 0);
-  int kt = 0;
-  for (; kt + 2 < nkt; ++kt) ktile(std::true_type{}, std::true_type{}, kt);
-  if (kt + 1 < nkt) ktile(std::true_type{}, std::false_type{}, kt++);
-  ktile(std::false_type{}, std::false_type{}, kt);
+      for (int q = 0; q < 4; ++q) {
+        float b[4] = {0.f, 0.f, 0.f, 0.f};
+        if constexpr (kBiasInit) {
+          const int n = n0 + wn * WTN + j * 32 + 8 * q + 4 * (lane >> 5);
+          if (p.bias && n < p.N && split == 0) load4(p.bias + n, b);
+        }
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[i][j][4 * q + e] = b[e];
+      }
+#pragma unroll
+    for (int i = 0; i < FM; ++i) read_a(0, i, smem, 0);
+#pragma unroll
+    for (int j = 0; j < FN; ++j) read_b(0, j, smem, 0);
+    int kt = 0;
+    for (; kt + 2 < nkt; ++kt) ktile(std::true_type{}, std::true_type{}, kt);
+    if (kt + 1 < nkt) ktile(std::true_type{}, std::false_type{}, kt++);
+    ktile(std::false_type{}, std::false_type{}, kt);
 
-  GemmArgs pe = p;
-  if constexpr (kBiasInit) pe.bias = nullptr;  // already in the accumulators
-  if constexpr (epi_staged<EPI>()) {
+    GemmArgs pe = p;
+    if constexpr (kBiasInit) pe.bias = nullptr;  // already in the accumulators
+    const int am0 = m0 + wm * WTM, an0 = n0 + wn * WTN, esplit = split;
+    const bool more = next(tm, tn, split);
     __syncthreads();  // all waves are done reading the operand stages
-    const u32x4* aux_pre = nullptr;
     if constexpr (kAuxPre) {
-      if (nkt < 2) {  // no k-tile barrier to carry the loads
+      if (nkt < 2) {  // no k-tile barrier carried the loads
 #pragma unroll
         for (int j = 0; j < NA; ++j) aux_load(j);
       }
-      aux_pre = auxr;
     }
-    gemm_epilogue<EPI, FM, FN, true>(pe, acc, smem + wave * WTM * SLD, am0, an0, lane, split, aux_pre);
-  } else {
-    gemm_epilogue<EPI, FM, FN, false>(pe, acc, nullptr, am0, an0, lane, split);
+    if (more) {  // the next tile's first k-tile, into stage 0
+      setup();
+#pragma unroll
+      for (int d = 0; d < LPW; ++d) dma(d, 0, 0);
+    }
+    if constexpr (epi_staged<EPI>()) {
+      const u32x4* aux_pre = nullptr;
+      if constexpr (kAuxPre) aux_pre = auxr;
+      if constexpr (PERSIST)
+        gemm_epilogue<EPI, FM, FN, true, 32>(pe, acc, smem + STAGE + wave * 32 * SLD, am0, an0, lane, esplit, aux_pre);
+      else
+        gemm_epilogue<EPI, FM, FN, true>(pe, acc, smem + wave * WTM * SLD, am0, an0, lane, esplit, aux_pre);
+    } else {
+      gemm_epilogue<EPI, FM, FN, false>(pe, acc, nullptr, am0, an0, lane, esplit);
+    }
+    if (!more) break;
+    // the loaders again: the same values, but nothing of them stays live
+    // across the epilogue
+    setup();
+    if (nkt > 1) {
+      __syncthreads();  // every wave is done with its staging rows in stage 1
+#pragma unroll
+      for (int d = 0; d < C0; ++d) dma(d, 1, kStageBytes);
+    }
   }
 }
 
+// The single tile (tm, tn, split).
+struct OneTile {
+  int tm, tn, split;
+  bool done;
+  DEVI bool operator()(int& a, int& b, int& s) {
+    if (done) return false;
+    a = tm;
+    b = tn;
+    s = split;
+    done = true;
+    return true;
+  }
+};
+
 template <bool A_K, bool B_K, int BM, int BN, int EPI, int OCC = 1>
 __global__ __launch_bounds__(256, OCC) void gemm_w4_kernel(GemmArgs p) {
-  __shared__ __attribute__((aligned(1024))) bf16 smem[w4_lds_elems<BM, BN>()];
+  __shared__ __attribute__((aligned(1024))) bf16 smem[w4_lds_elems<BM, BN, false>()];
   const int tiles_m = (p.M + BM - 1) / BM, tiles_n = (p.N + BN - 1) / BN;
   int tm, tn, split;
   tile_coords(p, tiles_m, tiles_n, blockIdx.x + blockIdx.y * gridDim.x, gridDim.x * gridDim.y, tm, tn, split);
-  w4_tile<A_K, B_K, BM, BN, EPI>(p, tm, tn, split, smem);
+  w4_tiles<A_K, B_K, BM, BN, EPI, false>(p, smem, OneTile{tm, tn, split, false});
+}
+
+// Persistent form (one k-split): a grid of 8 n workgroups, n per XCD (they
+// are dealt to the XCDs round-robin).  XCD x owns the contiguous range of
+// tiles tile_coords gives it; its workgroup w takes the tiles w, w + n,
+// w + 2n, ... of that range, so that at any moment the XCD works on
+// neighbouring tiles as the one-tile-per-workgroup grid does.
+template <bool A_K, bool B_K, int BM, int BN, int EPI, int OCC = 1>
+__global__ __launch_bounds__(256, OCC) void gemm_w4p_kernel(GemmArgs p) {
+  __shared__ __attribute__((aligned(1024))) bf16 smem[w4_lds_elems<BM, BN, true>()];
+  const int tiles_m = (p.M + BM - 1) / BM, tiles_n = (p.N + BN - 1) / BN;
+  const int total = tiles_m * tiles_n;
+  constexpr int NX = 8;
+  const int x = blockIdx.x % NX, w = blockIdx.x / NX, nw = gridDim.x / NX;
+  const int start = x * (total / NX) + min(x, total % NX);
+  const int count = total / NX + (x < total % NX ? 1 : 0);
+  int j = 0;
+  auto next = [&](int& tm, int& tn, int& split) {
+    const int local = w + j * nw;
+    if (local >= count) return false;
+    ++j;
+    tile_walk(p, tiles_m, tiles_n, start + local, tm, tn);
+    split = 0;
+    return true;
+  };
+  w4_tiles<A_K, B_K, BM, BN, EPI, true>(p, smem, next);
 }
 
 // Many independent products in one launch (weight gradients of a whole
@@ -915,7 +1020,7 @@ DEVI void group_tile(const GemmGroup& grp, int t, GemmArgs& p, int& tm, int& tn)
 
 template <int BM, int BN>
 __global__ __launch_bounds__(256, 1) void gemm_w4_group_kernel(GemmGroup grp) {
-  __shared__ __attribute__((aligned(1024))) bf16 smem[w4_lds_elems<BM, BN>()];
+  __shared__ __attribute__((aligned(1024))) bf16 smem[w4_lds_elems<BM, BN, false>()];
   // block b runs on XCD b % 8 as that XCD's idx-th workgroup: its whole
   // tiles first, then the K halves of its split tail tiles
   const int x = blockIdx.x % kGroupXcds, idx = blockIdx.x / kGroupXcds;
@@ -924,7 +1029,7 @@ __global__ __launch_bounds__(256, 1) void gemm_w4_group_kernel(GemmGroup grp) {
   int tm, tn;
   if (idx < whole) {
     group_tile<BM, BN>(grp, grp.xstart[x] + idx, p, tm, tn);
-    w4_tile<false, false, BM, BN, EPI_F32_ACC>(p, tm, tn, 0, smem);
+    w4_tiles<false, false, BM, BN, EPI_F32_ACC, false>(p, smem, OneTile{tm, tn, 0, false});
   } else if (idx < whole + 2 * grp.xsplit[x]) {
     const int u = idx - whole, half = u & 1;
     group_tile<BM, BN>(grp, grp.xstart[x] + whole + (u >> 1), p, tm, tn);
@@ -941,7 +1046,7 @@ __global__ __launch_bounds__(256, 1) void gemm_w4_group_kernel(GemmGroup grp) {
     p.ldc = BN;
     p.split_stride = (int64_t)BM * BN;
     p.C = grp.part + slot * 2 * BM * BN;
-    w4_tile<false, false, BM, BN, EPI_PARTIAL>(p, 0, 0, half, smem);
+    w4_tiles<false, false, BM, BN, EPI_PARTIAL, false>(p, smem, OneTile{0, 0, half, false});
   }
 }
 
@@ -1064,6 +1169,33 @@ namespace {
 constexpr int kBK = 64;
 
 // Tile configurations (block tile BM x BN, wave grid WGM x WGN).
+#ifndef GPT2_W4_PERSIST
+#define GPT2_W4_PERSIST 1
+#endif
+// Workgroups per XCD of the persistent one-wave-per-SIMD launch (one per
+// resident slot: CUs per XCD x occupancy), or 0 for the one-tile-per-
+// workgroup grid: k-splits, the hardware block order, or fewer than two
+// tiles per workgroup (nothing to overlap).
+// Epilogues whose persistent form would spill registers (the GELU' tile
+// held for the epilogue; the residual add on the largest tile) keep the
+// one-tile grid.
+template <int EPI, int BM, int BN>
+constexpr bool w4_persist_ok() {
+  return EPI != EPI_GELU_BWD && !(EPI == EPI_RESID && BM * BN > 256 * 192);
+}
+int w4_persistent_per_xcd(int occ, int tiles, const GemmArgs& a) {
+  if (!GPT2_W4_PERSIST || a.splits != 1 || a.no_xcd_map) return 0;
+  static int cus = 0;
+  if (cus == 0) {
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      n = 256;
+    cus = n;
+  }
+  const int nw = std::max(1, cus / 8) * occ;
+  return tiles >= 2 * 8 * nw ? nw : 0;
+}
+
 template <bool A_K, bool B_K, int EPI>
 void launch_bf16_cfg(int cfg, const GemmArgs& a, hipStream_t s) {
 #define GPT2_GEMM_CFG(ID, BM, BN, WGM, WGN)                                                     \
@@ -1110,6 +1242,13 @@ void launch_bf16_cfg(int cfg, const GemmArgs& a, hipStream_t s) {
 #define GPT2_GEMM_W4(ID, BM, BN, OCC)                                                           \
   case ID: {                                                                                   \
     const int tiles = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);                           \
+    if constexpr (w4_persist_ok<EPI, BM, BN>()) {                                             \
+      const int nw = w4_persistent_per_xcd(OCC, tiles, a);                                    \
+      if (nw > 0) {                                                                            \
+        gemm_w4p_kernel<A_K, B_K, BM, BN, EPI, OCC><<<dim3(8 * nw), 256, 0, s>>>(a);           \
+        break;                                                                                 \
+      }                                                                                        \
+    }                                                                                          \
     gemm_w4_kernel<A_K, B_K, BM, BN, EPI, OCC><<<dim3(tiles, a.splits), 256, 0, s>>>(a);       \
     break;                                                                                     \
   }
