@@ -1176,9 +1176,10 @@ constexpr int kBK = 64;
 // resident slot: CUs per XCD x occupancy), or 0 for the one-tile-per-
 // workgroup grid: k-splits, the hardware block order, or fewer than two
 // tiles per workgroup (nothing to overlap).
-// Epilogues whose persistent form would spill registers (the GELU' tile
-// held for the epilogue; the residual add on the largest tile) keep the
-// one-tile grid.
+// The GELU' epilogue keeps the one-tile grid: its persistent form either
+// spills registers (gelu'(u) carried through the k-loop) or, loading those
+// rows in the epilogue, ran 6% slower on MI355X.  So does the residual add
+// on the largest tile (it spills).
 template <int EPI, int BM, int BN>
 constexpr bool w4_persist_ok() {
   return EPI != EPI_GELU_BWD && !(EPI == EPI_RESID && BM * BN > 256 * 192);
