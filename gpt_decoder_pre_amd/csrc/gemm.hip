@@ -1432,11 +1432,13 @@ int gemm_resolve_config(int cfg, GemmLayout layout, GemmEpilogue epi, bool bf16_
     // two workgroups per CU (config 22) lets one workgroup's prologue and
     // epilogue run beside the other's k-loop (measured on MI355X: 3-10%
     // faster than config 19 and 5-18% faster than the one-workgroup tiles
-    // for these GEMMs).  The residual add with K = 4C goes to the rate
-    // model (measured on MI355X: 0.3% faster per step than the 128 x 192
-    // tile).  The lm_head product (K = C but 50k columns) keeps the
-    // one-workgroup tiles.
-    const bool heavy_epi = (epi == EPI_ACT && a.bias) || epi == EPI_GELU || epi == EPI_GELU_BWD;
+    // for these GEMMs).  So does the residual add (its fp32 read-modify-
+    // write epilogue; measured on MI355X with K = 4C: 3.8% faster than the
+    // 256 x 192 tile).  The lm_head product (K = C but 50k columns) keeps
+    // the one-workgroup tiles, and so do the long-K input gradients (the
+    // 128 x 192 tile measured 5% slower on the lm_head one).
+    const bool heavy_epi =
+        (epi == EPI_ACT && a.bias) || epi == EPI_GELU || epi == EPI_GELU_BWD || epi == EPI_RESID;
     const bool short_k = a.K <= 1024 && epi != EPI_LOGITS;
     if ((heavy_epi || short_k) && gemm_config_usable(22, layout, a)) cfg = 22;
     else if (heavy_epi && gemm_config_usable(19, layout, a)) cfg = 19;

@@ -293,7 +293,7 @@ def test_bf16_full_gpt2_small_one_sequence():
 # weight-gradient launch.
 BENCH_SITE_CONFIGS = {
     "gemm.fwd.lmhead": 20, "gemm.bwd.lmhead.dx": 21, "gemm.bwd.fc.dx": 21, "gemm.bwd.qkv.dx": 21,
-    "gemm.fwd.fcproj": 21, "gemm.fwd.qkv": 22, "gemm.fwd.fc": 22, "gemm.fwd.proj": 22,
+    "gemm.fwd.fcproj": 22, "gemm.fwd.qkv": 22, "gemm.fwd.fc": 22, "gemm.fwd.proj": 22,
     "gemm.bwd.fcproj.dx": 22, "gemm.bwd.proj.dx": 22, "gemm.bwd.dw": -2,
 }
 
