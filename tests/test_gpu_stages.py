@@ -1,7 +1,10 @@
 """Each forward kernel of the bf16 path against a plain PyTorch fp32 reference
 of the same op, fed with the kernel's own (bf16) inputs read back from the
 workspace; this localises a fault to one kernel.  Shapes span several tiles
-and a ragged tail (T = 200 is not a multiple of the 64/128 tiles)."""
+and a ragged tail (T = 200 is not a multiple of the 64/128 tiles); 17 x 1,000
+tokens is a launch large enough for the persistent GEMM grid (several tiles
+per workgroup) with a partial last tile row, and partial last tile columns
+in the lm_head product."""
 
 import numpy as np
 import pytest
@@ -17,7 +20,7 @@ def _max_rel(got, want):
     return d / max(want.abs().max().item(), 1e-30)
 
 
-@pytest.mark.parametrize("C,NH,T,B", [(768, 12, 200, 2), (1600, 25, 128, 1)])
+@pytest.mark.parametrize("C,NH,T,B", [(768, 12, 200, 2), (1600, 25, 128, 1), (768, 12, 1000, 17)])
 def test_bf16_forward_stages_against_torch_fp32(C, NH, T, B):
     import torch
     import torch.nn.functional as F
