@@ -241,70 +241,100 @@ void embed_sort(const int32_t* idx, int M, int vocab, int id_bits, int32_t* keys
 constexpr int kRun = 64;
 
 // Runs: within each chunk of 64 sorted entries, consecutive equal ids form a run;
-// the run's row sum is stored at the index of its first entry.
+// the run's row sum is stored at the index of its first entry.  The rows go
+// out eight at a time (their loads in flight together) and are added in
+// sorted order.
 __global__ __launch_bounds__(256) void run_sum_kernel(const int32_t* __restrict__ sid,
                                                       const int32_t* __restrict__ spos,
                                                       const float* __restrict__ dx, float* __restrict__ runs,
                                                       int M, int C) {
+  constexpr int U = 8;
   const int base = blockIdx.x * kRun, end = min(M, base + kRun);
   const int C4 = C >> 2;
   for (int c4 = threadIdx.x; c4 < C4; c4 += blockDim.x) {
     float acc[4] = {0.f, 0.f, 0.f, 0.f};
     int start = base;
-    for (int i = base; i < end; ++i) {
-      float v[4];
-      load4(dx + (int64_t)spos[i] * C + 4 * c4, v);
+    for (int i0 = base; i0 < end; i0 += U) {
+      float v[U][4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) acc[e] += v[e];
-      if (i + 1 == end || sid[i + 1] != sid[i]) {
-        store4(runs + (int64_t)start * C + 4 * c4, acc);
+      for (int u = 0; u < U; ++u)
+        if (i0 + u < end) load4(dx + (int64_t)spos[i0 + u] * C + 4 * c4, v[u]);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) acc[e] = 0.f;
-        start = i + 1;
+      for (int u = 0; u < U; ++u) {
+        const int i = i0 + u;
+        if (i >= end) break;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[e] += v[u][e];
+        if (i + 1 == end || sid[i + 1] != sid[i]) {
+          store4(runs + (int64_t)start * C + 4 * c4, acc);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[e] = 0.f;
+          start = i + 1;
+        }
       }
     }
   }
 }
 
 // One wavefront per sorted entry; entries that start a segment add the
-// segment's runs (in order) into their wte row.
+// segment's runs (in order) into their wte row.  A lane takes up to three
+// 4-column groups at once and the runs of a long segment come eight at a
+// time, so that a frequent token's row costs a few round trips to memory
+// instead of one per run; the additions keep the run order.
 __global__ __launch_bounds__(256) void segment_add_kernel(const int32_t* __restrict__ sid,
                                                           const float* __restrict__ runs, float* __restrict__ dwte,
                                                           int M, int C) {
+  constexpr int U = 8, NB = 3;
   const int i = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (i >= M) return;
   const int id = sid[i];
   if (i > 0 && sid[i - 1] == id) return;
   const int C4 = C >> 2;
-  for (int c4 = lane; c4 < C4; c4 += 64) {
-    float s[4];
-    load4(runs + (int64_t)i * C + 4 * c4, s);
-    // the segment's later runs, four at a time (loads together, adds in order)
+  for (int cb = 0; cb < C4; cb += 64 * NB) {
+    float s[NB][4];
+    bool col[NB];
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      const int c4 = cb + b * 64 + lane;
+      col[b] = c4 < C4;
+      if (col[b]) load4(runs + (int64_t)i * C + 4 * c4, s[b]);
+    }
+    // the segment's later runs (the first entry of each later chunk)
     int j = (i / kRun + 1) * kRun;
     while (j < M && sid[j] == id) {
-      float v[4][4];
-      bool in[4];
+      float v[U][NB][4];
+      bool in[U];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
+      for (int u = 0; u < U; ++u) {
         const int jj = j + u * kRun;
         in[u] = jj < M && sid[jj] == id && (u == 0 || in[u - 1]);
-        if (in[u]) load4(runs + (int64_t)jj * C + 4 * c4, v[u]);
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+          if (in[u] && col[b]) load4(runs + (int64_t)jj * C + 4 * (cb + b * 64 + lane), v[u][b]);
       }
 #pragma unroll
-      for (int u = 0; u < 4; ++u)
+      for (int u = 0; u < U; ++u)
         if (in[u]) {
 #pragma unroll
-          for (int e = 0; e < 4; ++e) s[e] += v[u][e];
-        }
-      j += 4 * kRun;
-    }
-    float* o = dwte + (int64_t)id * C + 4 * c4;
-    float a[4];
-    load4(o, a);
+          for (int b = 0; b < NB; ++b)
+            if (col[b]) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) a[e] += s[e];
-    store4(o, a);
+              for (int e = 0; e < 4; ++e) s[b][e] += v[u][b][e];
+            }
+        }
+      j += U * kRun;
+    }
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+      if (col[b]) {
+        float* o = dwte + (int64_t)id * C + 4 * (cb + b * 64 + lane);
+        float a4[4];
+        load4(o, a4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) a4[e] += s[b][e];
+        store4(o, a4);
+      }
   }
 }
 
