@@ -137,9 +137,17 @@ bool decode_attn(const TA* qkv, const TA* cache, TA* y, int B, int n_keys, int T
 // 16 for long K) take every NW-th 16-wide k-step, one v_mfma_f32_32x32x16_bf16
 // each (rows past M and columns past N read as zero), then add their 32 x 32
 // partial products in LDS in wave order and apply the epilogue.  The weights
-// stream from HBM once; the rows of A stay in L2.
-template <int EPI, int NW>
-__global__ __launch_bounds__(64 * NW) void skinny_gemm_kernel(GemmArgs a) {
+// stream from HBM once; the rows of A stay in L2.  KV (the QKV product of a
+// decoding step): the key and value columns [C, 3C) of output row m also go to
+// row (m, pos) of the layer's (B, Tmax, 2C) cache, so the step needs no
+// separate cache store.
+struct SkinnyKv {
+  bf16* cache;
+  int Tmax, pos, C;
+};
+
+template <int EPI, int NW, bool KV>
+__global__ __launch_bounds__(64 * NW) void skinny_gemm_kernel(GemmArgs a, SkinnyKv kv) {
   __shared__ float red[NW][32 * 33];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n0 = blockIdx.x * 32;
@@ -182,7 +190,11 @@ __global__ __launch_bounds__(64 * NW) void skinny_gemm_kernel(GemmArgs a) {
     const float bias = a.bias ? a.bias[n] : 0.f;
     const int64_t idx = (int64_t)m * a.ldc + n;
     if constexpr (EPI == EPI_ACT) {
-      reinterpret_cast<bf16*>(a.C)[idx] = (bf16)(v + bias);
+      const bf16 out = (bf16)(v + bias);
+      reinterpret_cast<bf16*>(a.C)[idx] = out;
+      if constexpr (KV) {
+        if (n >= kv.C) kv.cache[((int64_t)m * kv.Tmax + kv.pos) * 2 * kv.C + (n - kv.C)] = out;
+      }
     } else if constexpr (EPI == EPI_F32) {
       reinterpret_cast<float*>(a.C)[idx] = v + bias;
     } else if constexpr (EPI == EPI_RESID) {
@@ -197,23 +209,30 @@ __global__ __launch_bounds__(64 * NW) void skinny_gemm_kernel(GemmArgs a) {
 }
 
 template <int NW>
-bool skinny_launch(GemmEpilogue epi, const GemmArgs& a, hipStream_t s) {
+bool skinny_launch(GemmEpilogue epi, const GemmArgs& a, const SkinnyKv& kv, hipStream_t s) {
   const unsigned grid = (unsigned)((a.N + 31) / 32);
+  if (kv.cache) {
+    if (epi != EPI_ACT) return false;
+    skinny_gemm_kernel<EPI_ACT, NW, true><<<grid, 64 * NW, 0, s>>>(a, kv);
+    return true;
+  }
   switch (epi) {
-    case EPI_ACT: skinny_gemm_kernel<EPI_ACT, NW><<<grid, 64 * NW, 0, s>>>(a); return true;
-    case EPI_F32: skinny_gemm_kernel<EPI_F32, NW><<<grid, 64 * NW, 0, s>>>(a); return true;
-    case EPI_RESID: skinny_gemm_kernel<EPI_RESID, NW><<<grid, 64 * NW, 0, s>>>(a); return true;
-    case EPI_GELU: skinny_gemm_kernel<EPI_GELU, NW><<<grid, 64 * NW, 0, s>>>(a); return true;
+    case EPI_ACT: skinny_gemm_kernel<EPI_ACT, NW, false><<<grid, 64 * NW, 0, s>>>(a, kv); return true;
+    case EPI_F32: skinny_gemm_kernel<EPI_F32, NW, false><<<grid, 64 * NW, 0, s>>>(a, kv); return true;
+    case EPI_RESID: skinny_gemm_kernel<EPI_RESID, NW, false><<<grid, 64 * NW, 0, s>>>(a, kv); return true;
+    case EPI_GELU: skinny_gemm_kernel<EPI_GELU, NW, false><<<grid, 64 * NW, 0, s>>>(a, kv); return true;
     default: return false;
   }
 }
 
-bool gemm_skinny(GemmEpilogue epi, const GemmArgs& a, hipStream_t s) {
+bool gemm_skinny(GemmEpilogue epi, const GemmArgs& a, hipStream_t s, bf16* cache, int Tmax, int pos, int C) {
   if (a.M < 1 || a.M > 32 || a.N < 1 || a.K < 16 || a.K % 16 || a.lda % 8 || a.ldb % 8) return false;
+  if (cache && (epi != EPI_ACT || a.N != 3 * C || pos < 0 || pos >= Tmax)) return false;
+  const SkinnyKv kv{cache, Tmax, pos, C};
   // long K over few columns (the MLP's output projection): sixteen waves share
   // the k-steps, so that a workgroup's chain of dependent steps stays short
-  if (a.K > 1024 && a.N <= 4096) return skinny_launch<16>(epi, a, s);
-  return skinny_launch<4>(epi, a, s);
+  if (a.K > 1024 && a.N <= 4096) return skinny_launch<16>(epi, a, kv, s);
+  return skinny_launch<4>(epi, a, kv, s);
 }
 
 // ---------------------------------------------------------------- sampling ----

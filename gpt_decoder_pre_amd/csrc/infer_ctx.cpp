@@ -119,10 +119,14 @@ int forward(gpt2_infer* c, int B, int T, bool decode, float* d_logits) {
     layernorm_fwd<TA>(xa, c->P("ln1_w", l), c->P("ln1_b", l), ln, c->mean, c->rstd, M, C, s);
     GemmArgs g = args(ln, C, c->W("qkv_w", l), C, M, 3 * C, C, qkv, 3 * C);
     g.bias = c->has("qkv_b") ? c->P("qkv_b", l) : nullptr;
-    if (!product(c, EPI_ACT, g, s)) return GPT2_ERR_ARG;
     TA* cache = (TA*)c->cache_l(l);
+    // a bf16 decoding step stores the new keys and values from the QKV
+    // product's epilogue
+    const bool kv_fused =
+        decode && bf && M <= 32 && gemm_skinny(EPI_ACT, g, s, (bf16*)cache, c->Tmax, c->len, C);
+    if (!kv_fused && !product(c, EPI_ACT, g, s)) return GPT2_ERR_ARG;
     if (decode) {
-      kv_store<TA>(qkv, cache, B, 1, c->len, c->Tmax, C, s);
+      if (!kv_fused) kv_store<TA>(qkv, cache, B, 1, c->len, c->Tmax, C, s);
       if (!decode_attn<TA>(qkv, cache, atty, B, c->len + 1, c->Tmax, C, c->NH, s)) return GPT2_ERR_ARG;
     } else {
       kv_store<TA>(qkv, cache, B, T, 0, c->Tmax, C, s);

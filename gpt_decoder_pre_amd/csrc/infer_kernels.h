@@ -24,8 +24,11 @@ bool decode_attn(const TA* qkv, const TA* cache, TA* y, int B, int n_keys, int T
 // one-token decoding step); epilogues EPI_ACT, EPI_F32, EPI_RESID (C fp32 =
 // resid + acc + bias, resid with C's row stride) and EPI_GELU.  Returns false
 // (nothing launched) for shapes it does not take: M > 32, K % 16, unaligned
-// rows.
-bool gemm_skinny(GemmEpilogue epi, const GemmArgs& a, hipStream_t s);
+// rows.  With a cache (EPI_ACT, N = 3C: the QKV product of a decoding step)
+// the key and value columns of output row m also go to row (m, pos) of that
+// (B, Tmax, 2C) cache.
+bool gemm_skinny(GemmEpilogue epi, const GemmArgs& a, hipStream_t s, bf16* cache = nullptr, int Tmax = 0,
+                 int pos = 0, int C = 0);
 // out[b] = a column of logits row b (fp32, row stride ld) among [0, V):
 // temperature <= 0 or top_k == 1: the first largest; else z = logits / T,
 // columns below the k-th largest z dropped (top_k > 0), p = softmax(z),
