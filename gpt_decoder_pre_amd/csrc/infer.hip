@@ -236,12 +236,21 @@ bool gemm_skinny(GemmEpilogue epi, const GemmArgs& a, hipStream_t s, bf16* cache
 }
 
 // ---------------------------------------------------------------- sampling ----
-// One workgroup of 1024 threads per row; thread t holds the NPT consecutive
-// columns [t NPT, (t + 1) NPT) in registers.  Thresholds are found by a
-// bitwise search over ordered 32-bit keys (exact: 32 counting or summing
-// passes), so no sort is needed.
+// One workgroup of 1024 threads (16 waves) per row.  Loads are coalesced:
+// lane l of wave w holds the columns 4096 w + 64 i + l, i = 0 .. 63, so column
+// order is (wave, i, lane).  Thresholds are found by bitwise searches over
+// ordered 32-bit keys or float bit patterns (exact), so nothing is sorted.
+//
+// Top-k with 2 <= k <= 1024 first bounds the k-th largest value from below by
+// the k-th largest of the 1024 per-thread maxima (k threads each hold a value
+// at least that large).  When at most 1024 columns reach the bound, they are
+// gathered in column order into LDS and one wave finishes the row -- the
+// exact k-th value, the softmax, top-p and the inverse CDF -- with no block
+// barrier.  Otherwise the block works on the whole row in registers.
 constexpr int kSampleThreads = 1024;
-constexpr int kSampleNPT = 64;  // columns per thread: vocabularies up to 65,536
+constexpr int kSampleNPT = 64;                     // columns per thread: vocabularies up to 65,536
+constexpr int kSampleWaveCols = 64 * kSampleNPT;   // consecutive columns of one wave
+constexpr int kSampleCand = 1024;                  // gathered candidates of the top-k path
 
 // block-wide integer sum with one barrier: consecutive calls alternate between
 // the two halves of scratch (32 entries), so a half is rewritten only after
@@ -273,30 +282,6 @@ DEVI int block_excl_scan(int v, int* scratch) {
   return off + incl - v;
 }
 
-// order-preserving map of a float to an unsigned key (-inf lowest), and back.
-// Without -0 and NaN among the values, key(x) >= K  <=>  x >= key_float(K) for
-// every K the threshold search visits.
-DEVI uint32_t order_key(float f) {
-  const uint32_t u = __float_as_uint(f);
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
-DEVI float key_float(uint32_t k) { return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k); }
-
-// inclusive prefix sum of a float over the block's threads in thread order
-DEVI float block_incl_scan(float v, float* scratch) {
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  for (int o = 1; o < 64; o <<= 1) {
-    const float u = __shfl_up(v, o, 64);
-    if (lane >= o) v += u;
-  }
-  __syncthreads();
-  if (lane == 63) scratch[w] = v;
-  __syncthreads();
-  float off = 0.f;
-  for (int i = 0; i < w; ++i) off += scratch[i];
-  return off + v;
-}
-
 // block-wide integer sum (every thread gets it)
 DEVI int block_count(int v, int* scratch) {
   for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
@@ -308,6 +293,155 @@ DEVI int block_count(int v, int* scratch) {
   return r;
 }
 
+// order-preserving map of a float to an unsigned key (-inf lowest), and back.
+// Without -0 and NaN among the values, key(x) >= K  <=>  x >= key_float(K) for
+// every K the threshold search visits.
+DEVI uint32_t order_key(float f) {
+  const uint32_t u = __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+DEVI float key_float(uint32_t k) { return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k); }
+
+// inclusive prefix sum of a float over the wave's lanes
+DEVI float wave_incl_scan(float v) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const float u = __shfl_up(v, o, 64);
+    if (lane >= o) v += u;
+  }
+  return v;
+}
+
+// wave sum, the same bits in every lane: DPP exchanges inside rows of 16
+// lanes (each lane adds the same pairs), then the four row sums in a fixed order
+DEVI float read_lane(float v, int l) { return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l)); }
+DEVI int read_lane(int v, int l) { return __builtin_amdgcn_readlane(v, l); }
+template <int CTRL>
+DEVI float dpp_mov(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+template <int CTRL>
+DEVI int dpp_mov(int v) {
+  return __builtin_amdgcn_mov_dpp(v, CTRL, 0xF, 0xF, false);
+}
+template <typename T>
+DEVI T wave_sum_rows(T v) {
+  v += dpp_mov<0xB1>(v);   // quad_perm [1,0,3,2]: lane ^ 1
+  v += dpp_mov<0x4E>(v);   // quad_perm [2,3,0,1]: lane ^ 2
+  v += dpp_mov<0x141>(v);  // row_half_mirror: the other quad of each eight
+  v += dpp_mov<0x140>(v);  // row_mirror: the other eight of each sixteen
+  const T r0 = read_lane(v, 0), r1 = read_lane(v, 16), r2 = read_lane(v, 32), r3 = read_lane(v, 48);
+  return (r0 + r1) + (r2 + r3);
+}
+
+DEVI int lanes_below(uint64_t m) {
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+}
+
+// the thread's columns c0 + 64 i of one row (-inf past V), coalesced; with
+// SCALE each is divided by the temperature as z inv_t + 0 (the + 0 turns -0
+// into +0)
+template <bool SCALE>
+DEVI void load_row(float (&z)[kSampleNPT], const float* row, int c0, int w, int V, float inv_t) {
+  if ((w + 1) * kSampleWaveCols <= V) {  // the wave's columns all lie below V
+#pragma unroll
+    for (int i = 0; i < kSampleNPT; ++i) {
+      const float v = row[c0 + 64 * i];
+      z[i] = SCALE ? v * inv_t + 0.0f : v;
+    }
+  } else {  // branch-free: clamped addresses, then -inf past the end
+#pragma unroll
+    for (int i = 0; i < kSampleNPT; ++i) {
+      float v = row[min(c0 + 64 * i, V - 1)];
+      if (SCALE) v = v * inv_t + 0.0f;
+      z[i] = c0 + 64 * i < V ? v : -INFINITY;
+    }
+  }
+}
+
+// The top-k row finished by wave 0 on n <= 64 NC candidates cv (values after
+// the temperature) and ci (their columns), both in column order; candidate j
+// sits in lane j % 64 of chunk j / 64.
+template <int NC>
+DEVI void sample_candidates(const float* cv, const int* ci, int n, int top_k, float top_p, float u, int32_t* out) {
+  const int lane = threadIdx.x & 63;
+  float x[NC];
+  uint32_t kx[NC];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    const int j = 64 * c + lane;
+    x[c] = j < n ? cv[j] : -INFINITY;
+    kx[c] = j < n ? order_key(x[c]) : 0u;  // key 0 lies below every key the search visits
+  }
+  // the exact k-th largest key: every column at or above it is a candidate
+  uint32_t kth = 0;
+  for (int bit = 31; bit >= 0; --bit) {
+    const uint32_t cand = kth | (1u << bit);
+    int cnt = 0;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) cnt += __popcll(__ballot(kx[c] >= cand));
+    if (cnt >= top_k) kth = cand;
+  }
+  float mx = -INFINITY;
+#pragma unroll
+  for (int c = 0; c < NC; ++c) mx = fmaxf(mx, x[c]);
+  mx = wave_max(mx);
+  float e[NC], part = 0.f;
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    e[c] = kx[c] >= kth ? expf(x[c] - mx) : 0.f;
+    part += e[c];
+  }
+  if (top_p > 0.f && top_p < 1.f) {
+    // the largest e-threshold whose kept mass reaches top_p Z (e <= 1: bit 30 is clear)
+    const float need = top_p * wave_sum_rows(part);
+    uint32_t thr = 0;
+    for (int bit = 29; bit >= 0; --bit) {
+      const uint32_t cand = thr | (1u << bit);
+      const float cf = __uint_as_float(cand);
+      float sp = 0.f;
+#pragma unroll
+      for (int c = 0; c < NC; ++c) sp += e[c] >= cf ? e[c] : 0.f;
+      if (wave_sum_rows(sp) >= need) thr = cand;
+    }
+    const float cf = __uint_as_float(thr);
+#pragma unroll
+    for (int c = 0; c < NC; ++c) e[c] = e[c] >= cf ? e[c] : 0.f;
+  }
+  // inverse CDF in column order: per-chunk scans chained by their last lanes
+  float cum[NC], carry = 0.f;
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    cum[c] = carry + wave_incl_scan(e[c]);
+    carry = read_lane(cum[c], 63);
+  }
+  const float target = u * carry;
+  int sel = -1;
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    const uint64_t m = __ballot(cum[c] > target && e[c] > 0.f);
+    if (sel < 0 && m) sel = 64 * c + __builtin_ctzll(m);
+  }
+  if (sel < 0) {  // the target fell at or past the rounded total: the last kept column
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      const uint64_t m = __ballot(e[c] > 0.f);
+      if (m) sel = 64 * c + 63 - __builtin_clzll(m);
+    }
+  }
+  if (lane == 0) *out = ci[sel >= 0 ? sel : 0];  // sel < 0 only for NaN input
+}
+
+// bitwise OR over the wave, the same in every lane
+DEVI uint32_t wave_or(uint32_t v) {
+  v |= (uint32_t)dpp_mov<0xB1>((int)v);
+  v |= (uint32_t)dpp_mov<0x4E>((int)v);
+  v |= (uint32_t)dpp_mov<0x141>((int)v);
+  v |= (uint32_t)dpp_mov<0x140>((int)v);
+  return (uint32_t)(read_lane((int)v, 0) | read_lane((int)v, 16) | read_lane((int)v, 32) | read_lane((int)v, 48));
+}
+
 __global__ __launch_bounds__(kSampleThreads) void sample_kernel(const float* __restrict__ logits, int64_t ld, int V,
                                                                 float temperature, int top_k, float top_p,
                                                                 const float* __restrict__ uniform,
@@ -315,45 +449,130 @@ __global__ __launch_bounds__(kSampleThreads) void sample_kernel(const float* __r
   __shared__ float redf[16];
   __shared__ int redi[16];
   __shared__ int redi2[32];
-  __shared__ float scan[kSampleThreads];
-  __shared__ int pick;
-  const int b = blockIdx.x, t = threadIdx.x;
+  __shared__ uint32_t bound_key;
+  // 64 rows of 65: a wave's 4096 columns transposed (padded against bank
+  // conflicts); its front also holds the gathered candidates
+  __shared__ float big[kSampleNPT * 65];
+  const int b = blockIdx.x, t = threadIdx.x, lane = t & 63, w = t >> 6;
   const float* row = logits + (int64_t)b * ld;
-  const int c0 = t * kSampleNPT;
+  const int c0 = w * kSampleWaveCols + lane;  // column of z[i]: c0 + 64 i
   float z[kSampleNPT];
-#pragma unroll
-  for (int i = 0; i < kSampleNPT; ++i) z[i] = (c0 + i < V) ? row[c0 + i] : -INFINITY;
-
   if (temperature <= 0.f || top_k == 1) {  // greedy: the first largest logit
+    load_row<false>(z, row, c0, w, V, 1.0f);
+    const int nv = c0 < V ? (V - c0 + 63) >> 6 : 0;  // this thread's columns below V
     float best = -INFINITY;
     int bi = V;  // past the end: no candidate yet
 #pragma unroll
     for (int i = 0; i < kSampleNPT; ++i)
-      if (c0 + i < V && (z[i] > best || bi == V)) {
+      if (i < nv && (z[i] > best || bi == V)) {
         best = z[i];
-        bi = c0 + i;
+        bi = c0 + 64 * i;
       }
     // block arg-max with the lowest index on ties
     const float m = block_max(best, redf);
     int cand = (best == m) ? bi : V;
     for (int o = 32; o >= 1; o >>= 1) cand = min(cand, __shfl_xor(cand, o, 64));
     __syncthreads();
-    if ((t & 63) == 0) redi[t >> 6] = cand;
+    if (lane == 0) redi[w] = cand;
     __syncthreads();
     if (t == 0) {
       int r = V;
-      for (int w = 0; w < kSampleThreads / 64; ++w) r = min(r, redi[w]);
+      for (int v = 0; v < kSampleThreads / 64; ++v) r = min(r, redi[v]);
       out[b] = r;
     }
     return;
   }
   const float inv_t = 1.0f / temperature;
+  if (top_k > 1 && top_k <= kSampleCand && top_k < V) {
+    load_row<true>(z, row, c0, w, V, inv_t);
+    // lower bound: the k-th largest of the per-thread maxima
+    float tmax = -INFINITY;
 #pragma unroll
-  for (int i = 0; i < kSampleNPT; ++i) z[i] = z[i] * inv_t + 0.0f;  // + 0 turns -0 into +0
+    for (int i = 0; i < kSampleNPT; ++i) tmax = fmaxf(tmax, z[i]);
+    uint32_t* tkey = reinterpret_cast<uint32_t*>(big + 2 * kSampleCand);
+    tkey[t] = order_key(tmax);
+    __syncthreads();
+    if (w == 0) {
+      uint32_t k16[kSampleThreads / 64];
+#pragma unroll
+      for (int c = 0; c < kSampleThreads / 64; ++c) k16[c] = tkey[64 * c + lane];
+      // the top 16 bits of the k-th largest key, the rest zero: still a lower bound
+      uint32_t lb = 0;
+      for (int bit = 31; bit >= 16; --bit) {
+        const uint32_t cand = lb | (1u << bit);
+        int cnt = 0;
+#pragma unroll
+        for (int c = 0; c < kSampleThreads / 64; ++c) cnt += __popcll(__ballot(k16[c] >= cand));
+        if (cnt >= top_k) lb = cand;
+      }
+      if (lane == 0) bound_key = lb;
+    }
+    __syncthreads();
+    // a bound of -inf (fewer than k threads hold a finite value) leaves the
+    // whole row (its truncated key reads as NaN); otherwise the padded
+    // columns (-inf) fall below it.  mk: bit i set when column c0 + 64 i is a
+    // candidate.
+    const float lbf = key_float(bound_key);
+    uint64_t mk = 0;
+    int wc = kSampleCand + 1;
+    if (lbf > -INFINITY) {
+#pragma unroll
+      for (int i = 0; i < kSampleNPT; ++i) mk |= (uint64_t)(z[i] >= lbf ? 1 : 0) << i;
+      wc = wave_sum_rows((int)__popcll(mk));
+    }
+    if (lane == 0) redi[w] = wc;
+    __syncthreads();
+    int n = 0, off = 0;
+    for (int v = 0; v < kSampleThreads / 64; ++v) {
+      if (v == w) off = n;
+      n += redi[v];
+    }
+    if (n <= kSampleCand) {
+      float* cv = big;
+      int* ci = reinterpret_cast<int*>(big + kSampleCand);
+      // the columns i with a candidate in some lane of the wave
+      const uint64_t any = ((uint64_t)wave_or((uint32_t)(mk >> 32)) << 32) | wave_or((uint32_t)mk);
+      // a copy of c0 the compiler cannot match with the load addresses, so
+      // that it recomputes each column here instead of keeping 64 of them
+      int cb = c0;
+      asm volatile("" : "+v"(cb));
+#pragma unroll
+      for (int i = 0; i < kSampleNPT; ++i) {
+        if ((any >> i) & 1) {
+          const bool p = (mk >> i) & 1;
+          const uint64_t m = __ballot(p);
+          if (p) {
+            const int j = off + lanes_below(m);
+            cv[j] = z[i];
+            ci[j] = cb + 64 * i;
+          }
+          off += __popcll(m);
+        }
+      }
+      __syncthreads();
+      if (w == 0) {
+        const float ub = uniform[b];
+        if (n <= 64) sample_candidates<1>(cv, ci, n, top_k, top_p, ub, out + b);
+        else if (n <= 128) sample_candidates<2>(cv, ci, n, top_k, top_p, ub, out + b);
+        else if (n <= 256) sample_candidates<4>(cv, ci, n, top_k, top_p, ub, out + b);
+        else if (n <= 512) sample_candidates<8>(cv, ci, n, top_k, top_p, ub, out + b);
+        else sample_candidates<16>(cv, ci, n, top_k, top_p, ub, out + b);
+      }
+      return;
+    }
+    __syncthreads();  // redi is reused below
+  }
+
+  // the whole row.  It is loaded again (from L2): the registers of the first
+  // load are then free over this part, which needs more of them.
+  {
+    const float* again = row;
+    asm volatile("" : "+s"(again));  // a pointer the compiler cannot match with row
+    load_row<true>(z, again, c0, w, V, inv_t);
+  }
   // top-k: the k-th largest key; columns below it drop out
   uint32_t kth = 0;
   if (top_k > 0 && top_k < V) {
-    __syncthreads();
     for (int bit = 31; bit >= 0; --bit) {
       const uint32_t cand = kth | (1u << bit);
       const float cf = key_float(cand);
@@ -367,7 +586,7 @@ __global__ __launch_bounds__(kSampleThreads) void sample_kernel(const float* __r
   const float kth_f = key_float(kth);
 #pragma unroll
   for (int i = 0; i < kSampleNPT; ++i) {
-    if (z[i] < kth_f || c0 + i >= V) z[i] = -INFINITY;
+    if (z[i] < kth_f) z[i] = -INFINITY;  // the padded columns hold -inf already
     mx = fmaxf(mx, z[i]);
   }
   mx = block_max(mx, redf);
@@ -382,14 +601,15 @@ __global__ __launch_bounds__(kSampleThreads) void sample_kernel(const float* __r
   // top-p: the largest e-threshold whose kept mass reaches top_p Z
   if (top_p > 0.f && top_p < 1.f) {
     const float need = top_p * Z;
-    // few columns left (top-k): gather them in column order and give each
-    // its mass at or above it, S(e) = sum of the kept e' >= e; the threshold
-    // is the largest e with S(e) >= need
+    // few columns left: gather them and give each its mass at or above it,
+    // S(e) = sum of the kept e' >= e; the threshold is the largest e with
+    // S(e) >= need
     int mine_n = 0;
 #pragma unroll
     for (int i = 0; i < kSampleNPT; ++i) mine_n += z[i] > 0.f ? 1 : 0;
     const int nk = block_count(mine_n, redi);
     if (nk <= kSampleThreads) {
+      float* scan = big;
       int pos = block_excl_scan(mine_n, redi);
 #pragma unroll
       for (int i = 0; i < kSampleNPT; ++i)
@@ -405,69 +625,87 @@ __global__ __launch_bounds__(kSampleThreads) void sample_kernel(const float* __r
       const float c = block_max(thr_e, redf);
 #pragma unroll
       for (int i = 0; i < kSampleNPT; ++i) z[i] = z[i] >= c ? z[i] : 0.f;
-      __syncthreads();  // scan[] is reused below
-      top_p = 1.f;      // done
+      __syncthreads();  // big[] is reused below
+    } else {
+      uint32_t thr = 0;
+      for (int bit = 29; bit >= 0; --bit) {  // e <= 1: bit 30 is clear
+        const uint32_t cand = thr | (1u << bit);
+        const float c = __uint_as_float(cand);
+        float sp = 0.f;
+#pragma unroll
+        for (int i = 0; i < kSampleNPT; ++i) sp += z[i] >= c ? z[i] : 0.f;
+        if (block_sum(sp, redf) >= need) thr = cand;
+      }
+      const float c = __uint_as_float(thr);
+#pragma unroll
+      for (int i = 0; i < kSampleNPT; ++i) z[i] = z[i] >= c ? z[i] : 0.f;
     }
   }
-  if (top_p > 0.f && top_p < 1.f) {
-    const float need = top_p * Z;
-    uint32_t thr = 0;
-    for (int bit = 30; bit >= 0; --bit) {
-      const uint32_t cand = thr | (1u << bit);
-      const float c = __uint_as_float(cand);
-      float sp = 0.f;
-#pragma unroll
-      for (int i = 0; i < kSampleNPT; ++i) sp += z[i] >= c ? z[i] : 0.f;
-      if (block_sum(sp, redf) >= need) thr = cand;
-    }
-    const float c = __uint_as_float(thr);
-#pragma unroll
-    for (int i = 0; i < kSampleNPT; ++i) z[i] = z[i] >= c ? z[i] : 0.f;
-  }
-  // inverse CDF in column order: thread sums, an exclusive scan, then the
-  // thread whose range holds u * total walks its columns
+  // inverse CDF in column order.  A fixed-order scan over the 16 wave sums
+  // (each wave covers consecutive columns) finds the wave whose range holds
+  // u * total; that wave transposes its columns through LDS so that lane l
+  // holds the 64 consecutive ones 64 l .. 64 l + 63, scans the lanes' sums and
+  // the lane holding the target walks its columns.
   float mine = 0.f;
 #pragma unroll
   for (int i = 0; i < kSampleNPT; ++i) mine += z[i];
-  if (t == 0) pick = -1;
-  scan[t] = block_incl_scan(mine, redf);
+  const float ws = wave_sum(mine);
   __syncthreads();
-  const float total = scan[kSampleThreads - 1];
+  if (lane == 0) redf[w] = ws;
+  __syncthreads();
+  float before = 0.f, total = 0.f;
+  for (int v = 0; v < kSampleThreads / 64; ++v) {
+    if (v == w) before = total;
+    total += redf[v];
+  }
   const float target = uniform[b] * total;
-  const float before = t > 0 ? scan[t - 1] : 0.f;
-  if (mine > 0.f && target >= before && target < scan[t]) {
-    float c = before;
-    int sel = -1;
+  if (target < total) {
+    if (target >= before && target < before + ws) {  // this wave (the same for all its lanes)
 #pragma unroll
-    for (int i = 0; i < kSampleNPT; ++i) {
-      if (z[i] > 0.f && sel < 0) {
-        c += z[i];
-        if (target < c) sel = c0 + i;
+      for (int i = 0; i < kSampleNPT; ++i) big[65 * i + lane] = z[i];
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      const float* mycols = big + 65 * lane;  // columns w 4096 + 64 lane + m
+      float ls = 0.f;
+      for (int m = 0; m < kSampleNPT; ++m) ls += mycols[m];
+      const float incl = wave_incl_scan(ls);
+      float excl = __shfl_up(incl, 1, 64);
+      if (lane == 0) excl = 0.f;
+      uint64_t hit = __ballot(before + incl > target && ls > 0.f);
+      const bool walk_all = hit == 0;  // rounding at the wave's end: its last kept column
+      if (walk_all) hit = __ballot(ls > 0.f);
+      const int L = walk_all ? 63 - __builtin_clzll(hit) : __builtin_ctzll(hit);
+      if (lane == L) {
+        int sel = -1, last = -1;
+        float c = before + excl;
+        for (int m = 0; m < kSampleNPT; ++m) {
+          const float e = mycols[m];
+          if (e > 0.f) {
+            last = m;
+            if (sel < 0 && !walk_all) {
+              c += e;
+              if (target < c) sel = m;
+            }
+          }
+        }
+        out[b] = w * kSampleWaveCols + 64 * L + (sel >= 0 ? sel : last);
       }
     }
-    if (sel < 0) {  // rounding of the thread's own sum: its last kept column
-#pragma unroll
-      for (int i = 0; i < kSampleNPT; ++i)
-        if (z[i] > 0.f) sel = c0 + i;
-    }
-    pick = sel;
-  }
-  __syncthreads();
-  if (pick >= 0) {
-    if (t == 0) out[b] = pick;
     return;
   }
   // the target fell at or past the rounded total: the last kept column
-  int last = -1;
+  int li = -1;
 #pragma unroll
   for (int i = 0; i < kSampleNPT; ++i)
-    if (z[i] > 0.f) last = c0 + i;
+    if (z[i] > 0.f) li = i;
+  int last = li >= 0 ? c0 + 64 * li : -1;
   for (int o = 32; o >= 1; o >>= 1) last = max(last, __shfl_xor(last, o, 64));
-  if ((t & 63) == 0) redi[t >> 6] = last;
+  if (lane == 0) redi[w] = last;
   __syncthreads();
   if (t == 0) {
     int r = -1;
-    for (int w = 0; w < kSampleThreads / 64; ++w) r = max(r, redi[w]);
+    for (int v = 0; v < kSampleThreads / 64; ++v) r = max(r, redi[v]);
     out[b] = r;
   }
 }

@@ -132,6 +132,59 @@ def test_sampler_alone_matches_oracle(temperature, top_k, top_p):
     say(f"  {B - close}/{B} equal, {close} within rounding of a boundary")
 
 
+
+def _sampler_rows(case, rng):
+    """(logits rows, vocabulary size, padded width) of one sampler path."""
+    if case == "ties":  # 1500 columns share the top value: too many top-k candidates to gather
+        V, Vp = 50257, 50304
+        z = (rng.standard_normal((8, Vp)) * 2).astype(np.float32)
+        for r in range(8):
+            z[r, rng.choice(V, 1500, replace=False)] = z[r].max() + 1.0
+    elif case == "few_finite":  # 30 finite logits, the rest masked to -inf
+        V, Vp = 50257, 50304
+        z = np.full((8, Vp), -np.inf, np.float32)
+        for r in range(8):
+            z[r, rng.choice(V, 30, replace=False)] = rng.standard_normal(30) * 3
+    elif case == "masked":  # 30% of the vocabulary masked to -inf
+        V, Vp = 50257, 50304
+        z = (rng.standard_normal((8, Vp)) * 3).astype(np.float32)
+        z[rng.random((8, Vp)) < 0.3] = -np.inf
+    elif case == "small":  # one ragged wave of columns
+        V, Vp = 100, 128
+        z = (rng.standard_normal((8, Vp)) * 2).astype(np.float32)
+    else:  # "ragged_wave": the second wave's range ends inside it
+        V, Vp = 4097, 4104
+        z = (rng.standard_normal((8, Vp)) * 2).astype(np.float32)
+    return z, V, Vp
+
+
+@pytest.mark.parametrize("case,temperature,top_k,top_p", [
+    ("ties", 1.0, 40, 1.0), ("ties", 1.0, 40, 0.9), ("few_finite", 0.8, 40, 0.9), ("few_finite", 1.0, 0, 0.7),
+    ("masked", 0.9, 50, 0.95), ("masked", 1.0, 2000, 0.5), ("small", 1.0, 80, 0.9), ("small", 1.0, 10, 1.0),
+    ("small", 0.0, 0, 1.0), ("ragged_wave", 1.0, 1024, 0.8), ("ragged_wave", 1.0, 0, 1.0)])
+def test_sampler_paths_match_oracle(case, temperature, top_k, top_p):
+    """Each of the sampler's paths -- the gathered top-k candidates, the whole
+    row when the candidates overflow or the bound is -inf, top-p over few or
+    many kept columns, masked and padded columns -- against the oracle."""
+    import torch
+
+    from gpt_decoder_pre_amd.lib import sample
+    say(f"sampler {case} T={temperature} k={top_k} p={top_p}")
+    rng = np.random.default_rng(21)
+    z, V, Vp = _sampler_rows(case, rng)
+    u = rng.random(z.shape[0]).astype(np.float32)
+    got = sample(torch.tensor(z, device="cuda"), torch.tensor(u, device="cuda"), V, temperature, top_k,
+                 top_p).cpu().numpy()
+    close = 0
+    for b in range(z.shape[0]):
+        want = gen.sample(z[b], V, temperature, top_k, top_p, float(u[b]))
+        if got[b] != want:
+            close += 1
+            assert _sampler_margin(z[b], V, temperature, top_k, top_p, float(u[b])) < 1e-5, (b, got[b], want)
+        if not (temperature <= 0 or top_k == 1):
+            assert gen.filtered_probs(z[b], V, temperature, top_k, top_p)[got[b]] > 0  # a kept token
+    say(f"  {z.shape[0] - close}/{z.shape[0]} equal, {close} within rounding of a boundary")
+
 def test_decode_error_codes():
     import torch
 
