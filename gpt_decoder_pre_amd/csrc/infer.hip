@@ -45,10 +45,11 @@ void last_rows(const TA* src, TA* dst, int B, int T, int C, hipStream_t s) {
 
 // One new query per sequence against its n_keys cached keys (the query's own
 // key and value are the last of them): workgroup (head, sequence).  A key's
-// row is read by TPK threads, 16 bytes each, so 256 / TPK keys are in flight
-// per pass: their scores go to LDS, then the block's softmax, then the same
-// threads sum p_j v_j for every KP-th key and the KP partial rows are added
-// in order.
+// row is read by TPK threads, 16 bytes each, so a pass covers KP = 256 / TPK
+// keys; each thread issues the loads of KR passes before it uses any of them,
+// so that a round trip to memory is paid once per KR passes.  The scores go
+// to LDS, then the block's softmax, then the same threads sum p_j v_j for
+// every KP-th key and the KP partial rows are added in order.
 template <typename TA>
 __global__ __launch_bounds__(256) void decode_attn_kernel(const TA* __restrict__ qkv, const TA* __restrict__ cache,
                                                           TA* __restrict__ y, int n_keys, int Tmax, int C, int NH,
@@ -68,20 +69,29 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(const TA* __restrict__
     unpack16<TA>(raw, q);
   }
   const TA* kb = cache + (int64_t)b * Tmax * 2 * C + h * hd + sub * V;
+  constexpr int KR = 16;  // passes whose rows are loaded together
+  const u32x4 zero = {0u, 0u, 0u, 0u};
   float mx = -INFINITY;
-  for (int j0 = 0; j0 < n_keys; j0 += kp) {
-    const int j = j0 + kq;
-    float part = 0.f;
-    if (j < n_keys) {
+  for (int j0 = 0; j0 < n_keys; j0 += KR * kp) {
+    u32x4 raw[KR];
+#pragma unroll
+    for (int r = 0; r < KR; ++r) {
+      const int j = j0 + r * kp + kq;
+      raw[r] = j < n_keys ? *reinterpret_cast<const u32x4*>(kb + (int64_t)j * 2 * C) : zero;
+    }
+#pragma unroll
+    for (int r = 0; r < KR; ++r) {
+      const int j = j0 + r * kp + kq;
       float k[V];
-      unpack16<TA>(*reinterpret_cast<const u32x4*>(kb + (int64_t)j * 2 * C), k);
+      unpack16<TA>(raw[r], k);
+      float part = 0.f;
 #pragma unroll
       for (int e = 0; e < V; ++e) part = fmaf(q[e], k[e], part);
-    }
-    for (int o = tpk / 2; o >= 1; o >>= 1) part += __shfl_xor(part, o, 64);
-    if (j < n_keys && sub == 0) {
-      sm[j] = part * scale;
-      mx = fmaxf(mx, part * scale);
+      for (int o = tpk / 2; o >= 1; o >>= 1) part += __shfl_xor(part, o, 64);
+      if (j < n_keys && sub == 0) {
+        sm[j] = part * scale;
+        mx = fmaxf(mx, part * scale);
+      }
     }
   }
   mx = block_max(mx, red);
@@ -96,12 +106,24 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(const TA* __restrict__
   float acc[V];
 #pragma unroll
   for (int e = 0; e < V; ++e) acc[e] = 0.f;
-  for (int j = kq; j < n_keys; j += kp) {
-    float v[V];
-    unpack16<TA>(*reinterpret_cast<const u32x4*>(kb + C + (int64_t)j * 2 * C), v);
-    const float pj = sm[j];
+  for (int j0 = 0; j0 < n_keys; j0 += KR * kp) {
+    u32x4 raw[KR];
 #pragma unroll
-    for (int e = 0; e < V; ++e) acc[e] = fmaf(pj, v[e], acc[e]);
+    for (int r = 0; r < KR; ++r) {
+      const int j = j0 + r * kp + kq;
+      raw[r] = j < n_keys ? *reinterpret_cast<const u32x4*>(kb + C + (int64_t)j * 2 * C) : zero;
+    }
+#pragma unroll
+    for (int r = 0; r < KR; ++r) {
+      const int j = j0 + r * kp + kq;
+      if (j < n_keys) {
+        float v[V];
+        unpack16<TA>(raw[r], v);
+        const float pj = sm[j];
+#pragma unroll
+        for (int e = 0; e < V; ++e) acc[e] = fmaf(pj, v[e], acc[e]);
+      }
+    }
   }
   float* part = sm + n_keys;
 #pragma unroll
