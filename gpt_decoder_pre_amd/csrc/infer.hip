@@ -168,6 +168,29 @@ struct SkinnyKv {
   int Tmax, pos, C;
 };
 
+// output (m, n) = v plus the bias, through the epilogue
+template <int EPI, bool KV>
+DEVI void skinny_store(const GemmArgs& a, const SkinnyKv& kv, int m, int n, float v) {
+  const float bias = a.bias ? a.bias[n] : 0.f;
+  const int64_t idx = (int64_t)m * a.ldc + n;
+  if constexpr (EPI == EPI_ACT) {
+    const bf16 out = (bf16)(v + bias);
+    reinterpret_cast<bf16*>(a.C)[idx] = out;
+    if constexpr (KV) {
+      if (n >= kv.C) kv.cache[((int64_t)m * kv.Tmax + kv.pos) * 2 * kv.C + (n - kv.C)] = out;
+    }
+  } else if constexpr (EPI == EPI_F32) {
+    reinterpret_cast<float*>(a.C)[idx] = v + bias;
+  } else if constexpr (EPI == EPI_RESID) {
+    reinterpret_cast<float*>(a.C)[idx] = a.resid[idx] + (v + bias);
+  } else if constexpr (EPI == EPI_GELU) {
+    float g, d;
+    gelu_and_grad(v + bias, g, d);
+    reinterpret_cast<bf16*>(a.C)[idx] = (bf16)d;
+    reinterpret_cast<bf16*>(a.C2)[idx] = (bf16)g;
+  }
+}
+
 template <int EPI, int NW, bool KV>
 __global__ __launch_bounds__(64 * NW) void skinny_gemm_kernel(GemmArgs a, SkinnyKv kv) {
   __shared__ float red[NW][32 * 33];
@@ -209,40 +232,74 @@ __global__ __launch_bounds__(64 * NW) void skinny_gemm_kernel(GemmArgs a, Skinny
     float v = red[0][m * 33 + c];
 #pragma unroll
     for (int w = 1; w < NW; ++w) v += red[w][m * 33 + c];
-    const float bias = a.bias ? a.bias[n] : 0.f;
-    const int64_t idx = (int64_t)m * a.ldc + n;
-    if constexpr (EPI == EPI_ACT) {
-      const bf16 out = (bf16)(v + bias);
-      reinterpret_cast<bf16*>(a.C)[idx] = out;
-      if constexpr (KV) {
-        if (n >= kv.C) kv.cache[((int64_t)m * kv.Tmax + kv.pos) * 2 * kv.C + (n - kv.C)] = out;
-      }
-    } else if constexpr (EPI == EPI_F32) {
-      reinterpret_cast<float*>(a.C)[idx] = v + bias;
-    } else if constexpr (EPI == EPI_RESID) {
-      reinterpret_cast<float*>(a.C)[idx] = a.resid[idx] + (v + bias);
-    } else if constexpr (EPI == EPI_GELU) {
-      float g, d;
-      gelu_and_grad(v + bias, g, d);
-      reinterpret_cast<bf16*>(a.C)[idx] = (bf16)d;
-      reinterpret_cast<bf16*>(a.C2)[idx] = (bf16)g;
-    }
+    skinny_store<EPI, KV>(a, kv, m, n, v);
   }
+}
+
+// The same product for at most 16 rows on v_mfma_f32_16x16x32_bf16: a
+// workgroup owns 16 output columns (twice the workgroups of the 32-row form,
+// none of the MFMA rows wasted when a decoding batch has 16 sequences).  Each
+// wave takes every NW-th 32-wide k-step and issues the loads of all its steps
+// (up to U) before the first product.
+template <int EPI, int NW, bool KV>
+__global__ __launch_bounds__(64 * NW) void skinny16_gemm_kernel(GemmArgs a, SkinnyKv kv) {
+  constexpr int U = 6;
+  __shared__ float red[NW][16 * 17];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n0 = blockIdx.x * 16;
+  const int col = lane & 15, kq = lane >> 4;
+  const bf16* A = reinterpret_cast<const bf16*>(a.A);
+  const bf16* B = reinterpret_cast<const bf16*>(a.B);
+  const bool row_ok = col < a.M, col_ok = n0 + col < a.N;
+  const bf16* ar = A + (int64_t)(row_ok ? col : 0) * a.lda + 8 * kq;
+  const bf16* br = B + (int64_t)(col_ok ? n0 + col : 0) * a.ldb + 8 * kq;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  const int steps = a.K / 32;
+  for (int ks0 = wave; ks0 < steps; ks0 += U * NW) {
+    bf16x8 af[U], bfr[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int ks = ks0 + NW * u;
+      af[u] = __builtin_bit_cast(bf16x8, ld16_or_zero(ar + 32 * ks, row_ok && ks < steps));
+      bfr[u] = __builtin_bit_cast(bf16x8, ld16_or_zero(br + 32 * ks, col_ok && ks < steps));
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[u], bfr[u], acc, 0, 0, 0);
+  }
+  // acc[r] = partial C[row 4 kq + r][column n0 + col]
+#pragma unroll
+  for (int r = 0; r < 4; ++r) red[wave][(4 * kq + r) * 17 + col] = acc[r];
+  __syncthreads();
+  for (int o = tid; o < 16 * 16; o += 64 * NW) {
+    const int m = o >> 4, c = o & 15, n = n0 + c;
+    if (m >= a.M || n >= a.N) continue;
+    float v = red[0][m * 17 + c];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) v += red[w][m * 17 + c];
+    skinny_store<EPI, KV>(a, kv, m, n, v);
+  }
+}
+
+template <int EPI, int NW, bool KV>
+void skinny_go(const GemmArgs& a, const SkinnyKv& kv, hipStream_t s) {
+  if (a.M <= 16 && a.K % 32 == 0)
+    skinny16_gemm_kernel<EPI, NW, KV><<<(unsigned)((a.N + 15) / 16), 64 * NW, 0, s>>>(a, kv);
+  else
+    skinny_gemm_kernel<EPI, NW, KV><<<(unsigned)((a.N + 31) / 32), 64 * NW, 0, s>>>(a, kv);
 }
 
 template <int NW>
 bool skinny_launch(GemmEpilogue epi, const GemmArgs& a, const SkinnyKv& kv, hipStream_t s) {
-  const unsigned grid = (unsigned)((a.N + 31) / 32);
   if (kv.cache) {
     if (epi != EPI_ACT) return false;
-    skinny_gemm_kernel<EPI_ACT, NW, true><<<grid, 64 * NW, 0, s>>>(a, kv);
+    skinny_go<EPI_ACT, NW, true>(a, kv, s);
     return true;
   }
   switch (epi) {
-    case EPI_ACT: skinny_gemm_kernel<EPI_ACT, NW, false><<<grid, 64 * NW, 0, s>>>(a, kv); return true;
-    case EPI_F32: skinny_gemm_kernel<EPI_F32, NW, false><<<grid, 64 * NW, 0, s>>>(a, kv); return true;
-    case EPI_RESID: skinny_gemm_kernel<EPI_RESID, NW, false><<<grid, 64 * NW, 0, s>>>(a, kv); return true;
-    case EPI_GELU: skinny_gemm_kernel<EPI_GELU, NW, false><<<grid, 64 * NW, 0, s>>>(a, kv); return true;
+    case EPI_ACT: skinny_go<EPI_ACT, NW, false>(a, kv, s); return true;
+    case EPI_F32: skinny_go<EPI_F32, NW, false>(a, kv, s); return true;
+    case EPI_RESID: skinny_go<EPI_RESID, NW, false>(a, kv, s); return true;
+    case EPI_GELU: skinny_go<EPI_GELU, NW, false>(a, kv, s); return true;
     default: return false;
   }
 }
