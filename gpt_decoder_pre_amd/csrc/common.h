@@ -91,6 +91,9 @@ DEVI void gelu_and_grad(float u, float& g, float& d) {
   d = fmaf(g * (1.0f - s), dz, s);
 }
 
+// LayerNorm's epsilon inside the square root
+constexpr float kLnEps = 1e-5f;
+
 // ---- wave / block reductions ---------------------------------------------------
 DEVI float wave_sum(float v) {
 #pragma unroll

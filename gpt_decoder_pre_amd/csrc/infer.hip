@@ -167,6 +167,14 @@ struct SkinnyKv {
   bf16* cache;
   int Tmax, pos, C;
 };
+// A of a product formed as LayerNorm(x) in the prologue (skinny16)
+struct SkinnyLnA {
+  const float* x;
+  const float* w;
+  const float* b;
+};
+constexpr int kSkinnyU = 6;      // k-steps per wave whose loads are issued together
+constexpr int kSkinnyULn16 = 4;  // the same for the sixteen-wave LayerNorm form
 
 // output (m, n) = v plus the bias, through the epilogue
 template <int EPI, bool KV>
@@ -241,9 +249,19 @@ __global__ __launch_bounds__(64 * NW) void skinny_gemm_kernel(GemmArgs a, Skinny
 // none of the MFMA rows wasted when a decoding batch has 16 sequences).  Each
 // wave takes every NW-th 32-wide k-step and issues the loads of all its steps
 // (up to U) before the first product.
-template <int EPI, int NW, bool KV>
-__global__ __launch_bounds__(64 * NW) void skinny16_gemm_kernel(GemmArgs a, SkinnyKv kv) {
-  constexpr int U = 6;
+//
+// LNA: A = LayerNorm(x) (fp32 rows, K <= 32 U NW).  The workgroup's A loads
+// then cover its M rows whole: lane (row, kq) holds eight columns of each of
+// its wave's steps, so the row sums (then the sums of squared deviations) are
+// added over the lane's steps, the four lanes of the row and the waves in
+// LDS, and the lane normalises its values in registers as
+// (x - mean) rstd w + b, rounded to bf16 for the MFMA.
+template <int EPI, int NW, bool KV, bool LNA = false>
+__global__ __launch_bounds__(64 * NW) void skinny16_gemm_kernel(GemmArgs a, SkinnyKv kv, SkinnyLnA ln = {}) {
+  // sixteen waves have 128 registers each: fewer steps per wave, and the
+  // LayerNorm's gain and shift loaded after the statistics
+  constexpr int U = (LNA && NW > 4) ? kSkinnyULn16 : kSkinnyU;
+  constexpr bool PRE = NW <= 4;
   __shared__ float red[NW][16 * 17];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n0 = blockIdx.x * 16;
@@ -251,11 +269,81 @@ __global__ __launch_bounds__(64 * NW) void skinny16_gemm_kernel(GemmArgs a, Skin
   const bf16* A = reinterpret_cast<const bf16*>(a.A);
   const bf16* B = reinterpret_cast<const bf16*>(a.B);
   const bool row_ok = col < a.M, col_ok = n0 + col < a.N;
-  const bf16* ar = A + (int64_t)(row_ok ? col : 0) * a.lda + 8 * kq;
   const bf16* br = B + (int64_t)(col_ok ? n0 + col : 0) * a.ldb + 8 * kq;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   const int steps = a.K / 32;
-  for (int ks0 = wave; ks0 < steps; ks0 += U * NW) {
+  if constexpr (LNA) {
+    __shared__ float stat[2][NW][16];
+    const float* xr = ln.x + (int64_t)(row_ok ? col : 0) * a.lda + 8 * kq;
+    float xv[U][8], ww[U][8], bb[U][8];
+    bf16x8 bfr[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int ks = wave + NW * u;
+      bfr[u] = __builtin_bit_cast(bf16x8, ld16_or_zero(br + 32 * ks, col_ok && ks < steps));
+#pragma unroll
+      for (int e = 0; e < 8; ++e) xv[u][e] = ww[u][e] = bb[u][e] = 0.f;
+      if (row_ok && ks < steps) {
+        load4(xr + 32 * ks, xv[u]);
+        load4(xr + 32 * ks + 4, xv[u] + 4);
+      }
+      if (PRE && ks < steps) {  // the gain and shift come with the rows, not after the statistics
+        load4(ln.w + 32 * ks + 8 * kq, ww[u]);
+        load4(ln.w + 32 * ks + 8 * kq + 4, ww[u] + 4);
+        load4(ln.b + 32 * ks + 8 * kq, bb[u]);
+        load4(ln.b + 32 * ks + 8 * kq + 4, bb[u] + 4);
+      }
+    }
+    float sum = 0.f;
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      sum += ((xv[u][0] + xv[u][1]) + (xv[u][2] + xv[u][3])) + ((xv[u][4] + xv[u][5]) + (xv[u][6] + xv[u][7]));
+    sum += __shfl_xor(sum, 16, 64);
+    sum += __shfl_xor(sum, 32, 64);
+    if (kq == 0) stat[0][wave][col] = sum;
+    __syncthreads();
+    float mean = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) mean += stat[0][w][col];
+    mean /= (float)a.K;
+    float sq = 0.f;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (wave + NW * u < steps) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float d = xv[u][e] - mean;
+          sq += d * d;
+        }
+      }
+    }
+    sq += __shfl_xor(sq, 16, 64);
+    sq += __shfl_xor(sq, 32, 64);
+    if (kq == 0) stat[1][wave][col] = sq;
+    __syncthreads();
+    float var = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) var += stat[1][w][col];
+    const float rs = 1.0f / sqrtf(var / (float)a.K + kLnEps);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int ks = wave + NW * u;
+      if (ks < steps) {
+        if (!PRE) {
+          load4(ln.w + 32 * ks + 8 * kq, ww[u]);
+          load4(ln.w + 32 * ks + 8 * kq + 4, ww[u] + 4);
+          load4(ln.b + 32 * ks + 8 * kq, bb[u]);
+          load4(ln.b + 32 * ks + 8 * kq + 4, bb[u] + 4);
+        }
+        bf16x8 af;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) af[e] = (bf16)((xv[u][e] - mean) * rs * ww[u][e] + bb[u][e]);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bfr[u], acc, 0, 0, 0);
+      }
+    }
+  }
+  const bf16* ar = A + (int64_t)(row_ok ? col : 0) * a.lda + 8 * kq;
+  for (int ks0 = wave; !LNA && ks0 < steps; ks0 += U * NW) {
     bf16x8 af[U], bfr[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -302,6 +390,35 @@ bool skinny_launch(GemmEpilogue epi, const GemmArgs& a, const SkinnyKv& kv, hipS
     case EPI_GELU: skinny_go<EPI_GELU, NW, false>(a, kv, s); return true;
     default: return false;
   }
+}
+
+template <int NW>
+bool skinny_ln_launch(GemmEpilogue epi, const GemmArgs& a, const SkinnyKv& kv, const SkinnyLnA& ln, hipStream_t s) {
+  const unsigned grid = (unsigned)((a.N + 15) / 16);
+  if (kv.cache) {
+    if (epi != EPI_ACT) return false;
+    skinny16_gemm_kernel<EPI_ACT, NW, true, true><<<grid, 64 * NW, 0, s>>>(a, kv, ln);
+    return true;
+  }
+  switch (epi) {
+    case EPI_ACT: skinny16_gemm_kernel<EPI_ACT, NW, false, true><<<grid, 64 * NW, 0, s>>>(a, kv, ln); return true;
+    case EPI_F32: skinny16_gemm_kernel<EPI_F32, NW, false, true><<<grid, 64 * NW, 0, s>>>(a, kv, ln); return true;
+    case EPI_GELU: skinny16_gemm_kernel<EPI_GELU, NW, false, true><<<grid, 64 * NW, 0, s>>>(a, kv, ln); return true;
+    default: return false;
+  }
+}
+
+bool gemm_skinny_ln(GemmEpilogue epi, const GemmArgs& a, const float* x, const float* w, const float* b,
+                    hipStream_t s, bf16* cache, int Tmax, int pos, int C) {
+  if (a.M < 1 || a.M > 16 || a.N < 1 || a.K < 32 || a.K % 32 || a.lda % 4 || a.ldb % 8 || !x || !w || !b)
+    return false;
+  if (cache && (epi != EPI_ACT || a.N != 3 * C || pos < 0 || pos >= Tmax)) return false;
+  const SkinnyKv kv{cache, Tmax, pos, C};
+  const SkinnyLnA ln{x, w, b};
+  const int steps = a.K / 32;
+  if (steps <= kSkinnyU * 4) return skinny_ln_launch<4>(epi, a, kv, ln, s);
+  if (steps <= kSkinnyULn16 * 16) return skinny_ln_launch<16>(epi, a, kv, ln, s);
+  return false;
 }
 
 bool gemm_skinny(GemmEpilogue epi, const GemmArgs& a, hipStream_t s, bf16* cache, int Tmax, int pos, int C) {

@@ -115,16 +115,22 @@ int forward(gpt2_infer* c, int B, int T, bool decode, float* d_logits) {
   TA* ln = (TA*)c->ln;
   TA* qkv = (TA*)c->qkv;
   TA* atty = (TA*)c->atty;
+  // a bf16 decoding step of at most 16 sequences forms each LayerNorm in the
+  // prologue of the product that reads it, from the fp32 residual rows
+  const bool ln_pro = decode && bf && M <= 16;
   for (int l = 0; l < c->L; ++l) {
-    layernorm_fwd<TA>(xa, c->P("ln1_w", l), c->P("ln1_b", l), ln, c->mean, c->rstd, M, C, s);
     GemmArgs g = args(ln, C, c->W("qkv_w", l), C, M, 3 * C, C, qkv, 3 * C);
     g.bias = c->has("qkv_b") ? c->P("qkv_b", l) : nullptr;
     TA* cache = (TA*)c->cache_l(l);
     // a bf16 decoding step stores the new keys and values from the QKV
     // product's epilogue
-    const bool kv_fused =
-        decode && bf && M <= 32 && gemm_skinny(EPI_ACT, g, s, (bf16*)cache, c->Tmax, c->len, C);
-    if (!kv_fused && !product(c, EPI_ACT, g, s)) return GPT2_ERR_ARG;
+    bool kv_fused = ln_pro && gemm_skinny_ln(EPI_ACT, g, xa, c->P("ln1_w", l), c->P("ln1_b", l), s, (bf16*)cache,
+                                             c->Tmax, c->len, C);
+    if (!kv_fused) {
+      layernorm_fwd<TA>(xa, c->P("ln1_w", l), c->P("ln1_b", l), ln, c->mean, c->rstd, M, C, s);
+      kv_fused = decode && bf && M <= 32 && gemm_skinny(EPI_ACT, g, s, (bf16*)cache, c->Tmax, c->len, C);
+      if (!kv_fused && !product(c, EPI_ACT, g, s)) return GPT2_ERR_ARG;
+    }
     if (decode) {
       if (!kv_fused) kv_store<TA>(qkv, cache, B, 1, c->len, c->Tmax, C, s);
       if (!decode_attn<TA>(qkv, cache, atty, B, c->len + 1, c->Tmax, C, c->NH, s)) return GPT2_ERR_ARG;
@@ -137,23 +143,28 @@ int forward(gpt2_infer* c, int B, int T, bool decode, float* d_logits) {
     g.bias = c->P("proj_b", l);
     g.resid = xa;
     if (!product(c, EPI_RESID, g, s)) return GPT2_ERR_ARG;
-    layernorm_fwd<TA>(xb, c->P("ln2_w", l), c->P("ln2_b", l), ln, c->mean, c->rstd, M, C, s);
     g = args(ln, C, c->W("fc_w", l), C, M, 4 * C, C, c->fcgd, 4 * C);
     g.bias = c->P("fc_b", l);
     g.C2 = c->fcg;
-    if (!product(c, EPI_GELU, g, s)) return GPT2_ERR_ARG;
+    if (!(ln_pro && gemm_skinny_ln(EPI_GELU, g, xb, c->P("ln2_w", l), c->P("ln2_b", l), s))) {
+      layernorm_fwd<TA>(xb, c->P("ln2_w", l), c->P("ln2_b", l), ln, c->mean, c->rstd, M, C, s);
+      if (!product(c, EPI_GELU, g, s)) return GPT2_ERR_ARG;
+    }
     g = args(c->fcg, 4 * C, c->W("fcproj_w", l), 4 * C, M, C, 4 * C, xa, C);
     g.bias = c->P("fcproj_b", l);
     g.resid = xb;
     if (!product(c, EPI_RESID, g, s)) return GPT2_ERR_ARG;
   }
+  // the final LayerNorm stays a launch of its own: lm_head's thousands of
+  // workgroups would each re-read and normalise the rows
+  const void* head_w = c->W(c->has("lm_head") ? "lm_head" : "wte");
   layernorm_fwd<TA>(xa, c->P("lnf_w"), c->P("lnf_b"), (TA*)c->lnf, c->mean, c->rstd, M, C, s);
   const void* hrows = c->lnf;
   if (!decode && T > 1) {
     last_rows<TA>((const TA*)c->lnf, (TA*)c->last, B, T, C, s);
     hrows = c->last;
   }
-  GemmArgs g = args(hrows, C, c->W(c->has("lm_head") ? "lm_head" : "wte"), C, B, c->Vp, C, d_logits, c->Vp);
+  GemmArgs g = args(hrows, C, head_w, C, B, c->Vp, C, d_logits, c->Vp);
   if (!product(c, EPI_F32, g, s)) return GPT2_ERR_ARG;
   return hip_ok();
 }

@@ -13,8 +13,6 @@
 
 namespace gpt2k {
 
-constexpr float kLnEps = 1e-5f;
-
 // Eight consecutive values of a row: two float4 loads; eight outputs in one
 // 16-byte store (bf16) or two (fp32).
 DEVI void store8(float* p, const float o[8]) {

@@ -81,14 +81,17 @@ def test_decode_bf16_untied_variant():
     _decode_case(s, "bf16", 2, 64, 4, 1.0, 0, 0.9, 2e-2)
 
 
-def test_decode_equals_prefill_of_the_longer_prompt():
+@pytest.mark.parametrize("L,NH,C", [(2, 12, 768), (1, 25, 1600)])
+def test_decode_equals_prefill_of_the_longer_prompt(L, NH, C):
     """The cached step's logits against a prefill of the whole sequence (the
-    same kernels except the attention path)."""
+    same weights; the decoding step's own products, LayerNorms in their
+    prologues and attention).  Width 1600 takes the sixteen-wave forms of the
+    decoding products and several k-rounds in the MLP's output product."""
     import torch
 
     from gpt_decoder_pre_amd.lib import Decoder
-    s = shape("gpt2-124m-L2", 2, 12, 768, 1024, 50257, 50304)
-    say("decode vs prefill of the longer prompt (bf16)")
+    s = shape(f"width{C}-L{L}", L, NH, C, 1024, 50257, 50304)
+    say(f"decode vs prefill of the longer prompt (bf16, C={C})")
     p = init_params(s, 4)
     st = gpu_step(s, "bf16", 1, p)
     a, b = Decoder(st, 2), Decoder(st, 2)
