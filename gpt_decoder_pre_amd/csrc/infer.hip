@@ -50,7 +50,7 @@ void last_rows(const TA* src, TA* dst, int B, int T, int C, hipStream_t s) {
 // so that a round trip to memory is paid once per KR passes.  The scores go
 // to LDS, then the block's softmax, then the same threads sum p_j v_j for
 // every KP-th key and the KP partial rows are added in order.
-template <typename TA>
+template <typename TA, int TPK>
 __global__ __launch_bounds__(256) void decode_attn_kernel(const TA* __restrict__ qkv, const TA* __restrict__ cache,
                                                           TA* __restrict__ y, int n_keys, int Tmax, int C, int NH,
                                                           float scale) {
@@ -58,9 +58,9 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(const TA* __restrict__
   __shared__ float red[16];
   constexpr int V = 16 / sizeof(TA);  // elements per 16-byte chunk
   const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
-  const int hd = C / NH;
-  const int tpk = hd / V;        // threads per key row (a power of two)
-  const int kp = 256 / tpk;      // keys per pass
+  constexpr int hd = TPK * V;
+  constexpr int tpk = TPK;       // threads per key row (a power of two)
+  constexpr int kp = 256 / tpk;  // keys per pass
   const int sub = tid % tpk, kq = tid / tpk;
   float q[V];
   {
@@ -131,6 +131,7 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(const TA* __restrict__
   __syncthreads();
   if (tid < hd) {
     float sum = 0.f;
+#pragma unroll
     for (int i = 0; i < kp; ++i) sum += part[i * hd + tid];
     y[(int64_t)b * C + h * hd + tid] = from_f32<TA>(sum / l);
   }
@@ -146,8 +147,19 @@ bool decode_attn(const TA* qkv, const TA* cache, TA* y, int B, int n_keys, int T
   const int kp = 256 / tpk;
   const size_t lds = (size_t)(n_keys + kp * hd) * sizeof(float);
   if (lds > 60 * 1024) return false;
-  decode_attn_kernel<TA><<<dim3(NH, B), 256, lds, s>>>(qkv, cache, y, n_keys, Tmax, C, NH,
-                                                       1.0f / sqrtf((float)hd));
+  const dim3 grid(NH, B);
+  const float scale = 1.0f / sqrtf((float)hd);
+#define GPT2_DECODE_ATTN(T) decode_attn_kernel<TA, T><<<grid, 256, lds, s>>>(qkv, cache, y, n_keys, Tmax, C, NH, scale)
+  switch (tpk) {
+    case 1: GPT2_DECODE_ATTN(1); break;
+    case 2: GPT2_DECODE_ATTN(2); break;
+    case 4: GPT2_DECODE_ATTN(4); break;
+    case 8: GPT2_DECODE_ATTN(8); break;
+    case 16: GPT2_DECODE_ATTN(16); break;
+    case 32: GPT2_DECODE_ATTN(32); break;
+    default: GPT2_DECODE_ATTN(64); break;
+  }
+#undef GPT2_DECODE_ATTN
   return true;
 }
 
