@@ -10,11 +10,14 @@
 // to match the accumulator layout (the contraction order is free), so P never
 // leaves registers; V is stored transposed in LDS for that product.
 // Backward recomputes P from the saved log-sum-exp: one kernel per query tile
-// computes D = rowsum(dO o O) and accumulates dQ over key tiles, then one per
-// key tile accumulates dK and dV over query tiles (no atomics).
+// computes D = rowsum(dO o O) (stored with the log-sum-exp in the exp2 domain
+// for the next kernel) and accumulates dQ over key tiles, then one per key
+// tile accumulates dK and dV over query tiles (no atomics).
 //
 // fp32 path: one wavefront per query (forward, dQ) or key (dK, dV) row with the
 // scores of the row in LDS; plain fp32 arithmetic for the exact-mode step.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 #include "lds_tile.h"
@@ -346,8 +349,8 @@ __global__ __launch_bounds__(256, 3) void flash_fwd_kernel(const bf16* __restric
 // Workgroup: 128 keys of one (sequence, head); wave w owns keys key0 + 32 w +
 // lane%32 and accumulates dK^T and dV^T over the query tiles (64 queries)
 // that can see them.  Q and dO tiles stream from HBM straight into a
-// three-stage LDS ring; the tile's log-sum-exp (in the exp2 domain) and D
-// rows are staged beside them by waves 0 and 1 through registers.
+// three-stage LDS ring, and the tile's log-sum-exp (exp2 domain) and D rows
+// beside them (written by the dQ kernel).
 __global__ __launch_bounds__(256, 2) void flash_bwd_dkdv_kernel(const bf16* __restrict__ qkv,
                                                                 const bf16* __restrict__ dy,
                                                                 const float* __restrict__ lse,
@@ -368,7 +371,6 @@ __global__ __launch_bounds__(256, 2) void flash_bwd_dkdv_kernel(const bf16* __re
   const bf16* K = Q + C;
   const bf16* V = Q + 2 * C;
   const bf16* G = dy + (int64_t)b * T * C + h * HD;
-  const float* lse_b = lse + ((int64_t)b * NH + h) * T;
   const float* D_b = Dd + ((int64_t)b * NH + h) * T;
   const uint32_t lds0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void*)smem);
 
@@ -376,22 +378,17 @@ __global__ __launch_bounds__(256, 2) void flash_bwd_dkdv_kernel(const bf16* __re
   AttnTileLoader tlq, tlg;  // Q rows are 3C apart, dO rows C apart
   tlq.init(ld, wave, lane);
   tlg.init(C, wave, lane);
-  // waves 0 and 1 carry the lse / D rows of a query tile in a register
-  float rv = 0.f;
+  // waves 0 and 1 bring the tile's lse (exp2 domain) and D rows into LDS
+  // beside it, one 4-byte element per lane
+  const float* L2_b = Dd + (int64_t)(gridDim.x / ((T + 127) / 128)) * T + ((int64_t)b * NH + h) * T;
+  const uint32_t rows0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void*)&rowv[0][0][0]);
   auto load = [&](int it, int stg) {
     const int q0 = key0 + it * 64;
     const uint32_t base = lds0 + stg * (ASTAGE * 2);
     tlq.issue(Q, q0, T, base, wave, lane);
     tlg.issue(G, q0, T, base + ATILE * 2, wave, lane);
-    if (wave < 2) {
-      const int q = min(q0 + lane, T - 1);
-      rv = wave == 0 ? lse_b[q] * kLog2e : D_b[q];
-    }
+    if (wave < 2) dma4((wave == 0 ? L2_b : D_b) + min(q0 + lane, T - 1), rows0 + (stg * 2 + wave) * 256);
   };
-  auto stage_rows = [&](int stg) {  // after the register loads landed
-    if (wave < 2) rowv[stg][wave][lane] = rv;
-  };
-
   bf16x8 kf[4], vf[4];
 #pragma unroll
   for (int kk = 0; kk < 4; ++kk) {
@@ -402,22 +399,22 @@ __global__ __launch_bounds__(256, 2) void flash_bwd_dkdv_kernel(const bf16* __re
 #pragma unroll
   for (int r = 0; r < 16; ++r) dk[0][r] = dk[1][r] = dv[0][r] = dv[1][r] = 0.f;
 
-  // Prologue: tiles 0 and 1 in flight; tile 0's rows staged.
+  // Prologue: tiles 0 and 1 in flight.  Step it waits for tile it (tile
+  // it+1's loads stay in flight), barrier (tile it resident for every wave,
+  // every wave past step it-1), loads tile it+2 into the stage tile it-1
+  // used, then uses tile it.
   load(0, 0);
-  wait_vmcnt<0>();
-  stage_rows(0);
   if (nqt > 1) load(1, 1);
-  // Iteration it: wait for tile it+1 and stage its rows, barrier (tile it
-  // complete everywhere, every wave past iteration it-1), load tile it+2 into
-  // the stage tile it-1 used, then use tile it.
-  int stg = 0;
-  for (int it = 0; it < nqt; ++it) {
-    const int stg1 = stg == 2 ? 0 : stg + 1, stg2 = stg1 == 2 ? 0 : stg1 + 1;
+  auto step = [&](int it, auto stgc) {
+    constexpr int stg = decltype(stgc)::value;
+    constexpr int stg2 = (stg + 2) % 3;
     if (it + 1 < nqt) {
+      if (wave < 2) wait_vmcnt<5>();
+      else wait_vmcnt<4>();
+    } else {
       wait_vmcnt<0>();
-      stage_rows(stg1);
     }
-    __syncthreads();
+    lds_barrier();
     if (it + 2 < nqt) load(it + 2, stg2);
     const int q0 = key0 + it * 64;
     const bf16* Qs = smem + stg * ASTAGE;
@@ -471,7 +468,11 @@ __global__ __launch_bounds__(256, 2) void flash_bwd_dkdv_kernel(const bf16* __re
         }
       }
     }
-    stg = stg1;
+  };
+  for (int it = 0; it < nqt; it += 3) {
+    step(it, std::integral_constant<int, 0>{});
+    if (it + 1 < nqt) step(it + 1, std::integral_constant<int, 1>{});
+    if (it + 2 < nqt) step(it + 2, std::integral_constant<int, 2>{});
   }
   if (mykey < T) {
     bf16* o = dqkv + ((int64_t)b * T + mykey) * ld + h * HD;
@@ -547,7 +548,11 @@ __global__ __launch_bounds__(256, 3) void flash_bwd_dq_kernel(const bf16* __rest
   }
   // D for the dK / dV kernel (launched after this one) and for this one
   const float Dq = halves_sum(dsum);
-  if (qok && hl == 0) Dd[((int64_t)b * NH + h) * T + myq] = Dq;
+  if (qok && hl == 0) {
+    const int64_t rows = (int64_t)(gridDim.x / ((T + 127) / 128)) * T;  // B NH T
+    Dd[((int64_t)b * NH + h) * T + myq] = Dq;
+    Dd[rows + ((int64_t)b * NH + h) * T + myq] = lse2;
+  }
   f32x16 dq[2];
 #pragma unroll
   for (int r = 0; r < 16; ++r) dq[0][r] = dq[1][r] = 0.f;
@@ -563,7 +568,7 @@ __global__ __launch_bounds__(256, 3) void flash_bwd_dq_kernel(const bf16* __rest
     const int k0 = kt * 64;
     const bf16* Ks = smem + stg * ASTAGE;
     const bf16* Vs = Ks + ATILE;
-    if (k0 <= wq0 + 31) {
+    {  // a key tile past every query of the wave is masked whole (adds zeros)
       const bool diag = k0 + 63 > wq0 || k0 + 64 > T;
       f32x16 dS[2];
 #pragma unroll

@@ -587,7 +587,7 @@ int64_t plan_workspace(gpt2_ctx* c, Plan& p, bool assign) {
   c->dbig = at(slots * M * 4 * C * A);
   c->dqkv = at(slots * M * 3 * C * A);
   c->dy = at(M * C * A);
-  c->attnD = (float*)at(M * NH * 4);
+  c->attnD = (float*)at(2 * M * NH * 4);  // D, then the exp2-domain log-sum-exp (bf16 backward)
   c->splitk_elems = std::max<int64_t>(16 * 4 * C * C, 2 * Vp * C);
   c->splitk = (float*)at(c->splitk_elems * 4);
   // one region per column-partial producer of a backward pass: 2L + 1

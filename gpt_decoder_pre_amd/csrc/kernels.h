@@ -157,7 +157,8 @@ int colsum_partials(const TA* x, int M, int N, float* part, hipStream_t s);
 void attn_fwd_bf16(const void* qkv, void* y, float* lse, int B, int T, int NH, int C, hipStream_t s);
 // colsum (or null): column sums of dqkv per 64-token chunk, fp32 [M/64][3C],
 // each chunk's tokens added in ascending order; formed only when T % 64 == 0
-// (the return value says whether they were).
+// (the return value says whether they were).  Dbuf: 2 B NH T floats of
+// scratch (D = rowsum(dO o O), then the log-sum-exp in the exp2 domain).
 bool attn_bwd_bf16(const void* qkv, const void* y, const void* dy, const float* lse, float* Dbuf, void* dqkv,
                    int B, int T, int NH, int C, float* colsum, hipStream_t s);
 void attn_fwd_f32(const float* qkv, float* y, float* lse, int B, int T, int NH, int C, hipStream_t s);

@@ -65,6 +65,12 @@ DEVI void dma16s(const void* sbase, uint32_t voff, uint32_t lds_base) {
                : "memory", "m0");
 }
 
+// One global_load_lds_dword: each lane moves 4 bytes from gptr to LDS address
+// m0 + 4 * lane (dma16 with 4-byte elements).
+DEVI void dma4(const void* gptr, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, off" ::"s"(lds_base), "v"(gptr) : "memory", "m0");
+}
+
 // A pointer the compiler can keep in SGPRs (the value must be wave-uniform).
 template <typename T>
 DEVI const T* uniform_ptr(const T* q) {
