@@ -29,12 +29,12 @@ constexpr int HD = 64;
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
-DEVI bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+DEVI h16x8 as_h16x8(u32x4 v) { return __builtin_bit_cast(h16x8, v); }
 
-DEVI bf16x8 pack8(const f32x16& v, int base) {
-  bf16x8 r;
+DEVI h16x8 pack8(const f32x16& v, int base) {
+  h16x8 r;
 #pragma unroll
-  for (int e = 0; e < 8; ++e) r[e] = (bf16)v[base + e];
+  for (int e = 0; e < 8; ++e) r[e] = (h16)v[base + e];
   return r;
 }
 
@@ -85,9 +85,9 @@ struct AttnTileLoader {
       off[j] = (uint32_t)(2 * ((int64_t)r * ld + c8));
     }
   }
-  DEVI void issue(const bf16* g, int r0, int T, uint32_t lds_tile, int wave, int lane) const {
+  DEVI void issue(const h16* g, int r0, int T, uint32_t lds_tile, int wave, int lane) const {
     if (r0 + 64 <= T) {
-      const bf16* b = uniform_ptr(g + (int64_t)r0 * ld);
+      const h16* b = uniform_ptr(g + (int64_t)r0 * ld);
 #pragma unroll
       for (int j = 0; j < 2; ++j) dma16s(b, off[j], lds_tile + (2 * wave + j) * 1024);
     } else {
@@ -102,10 +102,10 @@ struct AttnTileLoader {
 };
 
 // MFMA operand rows row0 + lane%32 of a tile, dims 16 kk + 8 hl .. + 7.
-DEVI bf16x8 row_frag(const bf16* tile, int row0, int kk, int lane) {
+DEVI h16x8 row_frag(const h16* tile, int row0, int kk, int lane) {
   const int r = row0 + (lane & 31);
   const int c = 2 * kk + (lane >> 5);
-  return *reinterpret_cast<const bf16x8*>(tile + r * 64 + 8 * (c ^ bswz(r)));
+  return *reinterpret_cast<const h16x8*>(tile + r * 64 + 8 * (c ^ bswz(r)));
 }
 
 // A operand of a product over the tile's rows, read transposed: rows
@@ -114,7 +114,7 @@ DEVI bf16x8 row_frag(const bf16* tile, int row0, int kk, int lane) {
 // kbase + 8 + 4 hl + {0..3}.  ds_read_b64_tr_b16 hands lane j of each 16-lane
 // group element i of source lane 4i + j/4's 8-byte row, so source lane 4i + q
 // points at (row kb + i, dims m16 + 4q .. + 3).
-DEVI bf16x8 tr_frag_keys(const bf16* tile, int kbase, int mbase, int lane) {
+DEVI h16x8 tr_frag_keys(const h16* tile, int kbase, int mbase, int lane) {
   const int g = lane >> 4, s = lane & 15;
   const int k = kbase + 4 * (g >> 1) + (s >> 2);
   const int m = mbase + 16 * (g & 1) + 4 * (s & 3);
@@ -124,17 +124,16 @@ DEVI bf16x8 tr_frag_keys(const bf16* tile, int kbase, int mbase, int lane) {
       __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(tile + (k + 8) * 64 + 8 * (c ^ bswz(k + 8)) + o));
   const u32x2 ua = __builtin_bit_cast(u32x2, a), ub = __builtin_bit_cast(u32x2, b);
   u32x4 r = {ua[0], ua[1], ub[0], ub[1]};
-  return as_bf16x8(r);
+  return as_h16x8(r);
 }
 
-// acc + the sum of eight bf16 values (four v_dot2c_f32_bf16 against ones)
-DEVI float sum_bf16x8(bf16x8 v, float acc) {
-  typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
-  const bf16x2v one = {(bf16)1.0f, (bf16)1.0f};
+// acc + the sum of eight 16-bit values (four dot2 against ones)
+DEVI float sum_h16x8(h16x8 v, float acc) {
+  const h16x2 one = {(h16)1.0f, (h16)1.0f};
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
-    const bf16x2v pair = {v[2 * e], v[2 * e + 1]};
-    acc = __builtin_amdgcn_fdot2_f32_bf16(pair, one, acc, false);
+    const h16x2 pair = {v[2 * e], v[2 * e + 1]};
+    acc = dot2(pair, one, acc);
   }
   return acc;
 }
@@ -173,7 +172,7 @@ DEVI void chunk_colsums(const f32x16 (&acc)[2], float scale, bool tok_ok, float*
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int d = t * 32 + 8 * (r >> 2) + 4 * hl + (r & 3);
-      red[(wave * 64 + d) * 33 + lc] = tok_ok ? (float)(bf16)(acc[t][r] * scale) : 0.f;
+      red[(wave * 64 + d) * 33 + lc] = tok_ok ? (float)(h16)(acc[t][r] * scale) : 0.f;
     }
   __syncthreads();
   if (tid < 128) {
@@ -199,10 +198,10 @@ DEVI float halves_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-__global__ __launch_bounds__(256, 3) void flash_fwd_kernel(const bf16* __restrict__ qkv, bf16* __restrict__ y,
+__global__ __launch_bounds__(256, 3) void flash_fwd_kernel(const h16* __restrict__ qkv, h16* __restrict__ y,
                                                            float* __restrict__ lse, int T, int NH, int C,
                                                            float sl2) {
-  __shared__ __attribute__((aligned(1024))) bf16 smem[3 * ASTAGE];  // [stage][K | V]
+  __shared__ __attribute__((aligned(1024))) h16 smem[3 * ASTAGE];  // [stage][K | V]
   int qt, h, b;
   attn_block(T, NH, qt, h, b);
   qt = (T + 127) / 128 - 1 - qt;  // tile 0: the most key tiles
@@ -212,9 +211,9 @@ __global__ __launch_bounds__(256, 3) void flash_fwd_kernel(const bf16* __restric
   const int wq0 = q0 + wave * 32;
   const int myq = wq0 + lc;
   const int64_t ld = 3 * (int64_t)C;
-  const bf16* Q = qkv + (int64_t)b * T * ld + h * HD;
-  const bf16* K = Q + C;
-  const bf16* V = Q + 2 * C;
+  const h16* Q = qkv + (int64_t)b * T * ld + h * HD;
+  const h16* K = Q + C;
+  const h16* V = Q + 2 * C;
   const uint32_t lds0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void*)smem);
 
   const int nkt = (min(T, q0 + 128) + 63) / 64;            // key tiles of the workgroup
@@ -228,20 +227,20 @@ __global__ __launch_bounds__(256, 3) void flash_fwd_kernel(const bf16* __restric
   load(0, 0);
   if (nkt > 1) load(1, 1);
 
-  bf16x8 qf[4];
+  h16x8 qf[4];
 #pragma unroll
-  for (int kk = 0; kk < 4; ++kk) qf[kk] = as_bf16x8(ld16_or_zero(Q + (int64_t)myq * ld + kk * 16 + hl * 8, myq < T));
+  for (int kk = 0; kk < 4; ++kk) qf[kk] = as_h16x8(ld16_or_zero(Q + (int64_t)myq * ld + kk * 16 + hl * 8, myq < T));
 
   // S^T = K Q^T for tile j: s[js][r] is key 64 j + 32 js + 8 (r/4) + 4 hl + r%4, query myq
   auto scores = [&](int stg, f32x16 (&s)[2]) {
-    const bf16* Ks = smem + stg * ASTAGE;
+    const h16* Ks = smem + stg * ASTAGE;
 #pragma unroll
     for (int js = 0; js < 2; ++js) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) s[js][r] = 0.f;
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk)
-        s[js] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag(Ks, js * 32, kk, lane), qf[kk], s[js], 0, 0, 0);
+        s[js] = mfma32(row_frag(Ks, js * 32, kk, lane), qf[kk], s[js]);
     }
   };
 
@@ -298,14 +297,14 @@ __global__ __launch_bounds__(256, 3) void flash_fwd_kernel(const bf16* __restric
     for (int js = 0; js < 2; ++js)
 #pragma unroll
       for (int r = 0; r < 16; ++r) cur[js][r] = exp2_fast(fmaf(cur[js][r], sl2, -mrow));
-    const bf16* Vs = smem + stg * ASTAGE + ATILE;
+    const h16* Vs = smem + stg * ASTAGE + ATILE;
 #pragma unroll
     for (int st = 0; st < 4; ++st) {
-      const bf16x8 pf = pack8(cur[st >> 1], 8 * (st & 1));
+      const h16x8 pf = pack8(cur[st >> 1], 8 * (st & 1));
 #pragma unroll
       for (int i = 0; i < 2; ++i)
-        o[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag_keys(Vs, st * 16, i * 32, lane), pf, o[i], 0, 0, 0);
-      lrow = sum_bf16x8(pf, lrow);
+        o[i] = mfma32(tr_frag_keys(Vs, st * 16, i * 32, lane), pf, o[i]);
+      lrow = sum_h16x8(pf, lrow);
     }
     // the eight score MFMAs of tile j+1 spread over the exponentials of tile j
 #pragma unroll
@@ -333,7 +332,7 @@ __global__ __launch_bounds__(256, 3) void flash_fwd_kernel(const bf16* __restric
   const float ltot = halves_sum(lrow);
   if (myq < T) {
     const float inv = 1.0f / ltot;
-    bf16* yr = y + ((int64_t)b * T + myq) * C + h * HD;
+    h16* yr = y + ((int64_t)b * T + myq) * C + h * HD;
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -351,13 +350,13 @@ __global__ __launch_bounds__(256, 3) void flash_fwd_kernel(const bf16* __restric
 // that can see them.  Q and dO tiles stream from HBM straight into a
 // three-stage LDS ring, and the tile's log-sum-exp (exp2 domain) and D rows
 // beside them (written by the dQ kernel).
-__global__ __launch_bounds__(256, 2) void flash_bwd_dkdv_kernel(const bf16* __restrict__ qkv,
-                                                                const bf16* __restrict__ dy,
+__global__ __launch_bounds__(256, 2) void flash_bwd_dkdv_kernel(const h16* __restrict__ qkv,
+                                                                const h16* __restrict__ dy,
                                                                 const float* __restrict__ lse,
                                                                 const float* __restrict__ Dd,
-                                                                bf16* __restrict__ dqkv, int T, int NH, int C,
+                                                                h16* __restrict__ dqkv, int T, int NH, int C,
                                                                 float sl2, float scale, float* __restrict__ colsum) {
-  __shared__ __attribute__((aligned(1024))) bf16 smem[3 * ASTAGE];  // [stage][Q | dO]
+  __shared__ __attribute__((aligned(1024))) h16 smem[3 * ASTAGE];  // [stage][Q | dO]
   __shared__ __attribute__((aligned(16))) float rowv[3][2][64];     // [stage][lse log2e | D]
   int kt, h, b;
   attn_block(T, NH, kt, h, b);
@@ -367,10 +366,10 @@ __global__ __launch_bounds__(256, 2) void flash_bwd_dkdv_kernel(const bf16* __re
   const int wk0 = key0 + wave * 32;
   const int mykey = wk0 + lc;
   const int64_t ld = 3 * (int64_t)C;
-  const bf16* Q = qkv + (int64_t)b * T * ld + h * HD;
-  const bf16* K = Q + C;
-  const bf16* V = Q + 2 * C;
-  const bf16* G = dy + (int64_t)b * T * C + h * HD;
+  const h16* Q = qkv + (int64_t)b * T * ld + h * HD;
+  const h16* K = Q + C;
+  const h16* V = Q + 2 * C;
+  const h16* G = dy + (int64_t)b * T * C + h * HD;
   const float* D_b = Dd + ((int64_t)b * NH + h) * T;
   const uint32_t lds0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void*)smem);
 
@@ -389,11 +388,11 @@ __global__ __launch_bounds__(256, 2) void flash_bwd_dkdv_kernel(const bf16* __re
     tlg.issue(G, q0, T, base + ATILE * 2, wave, lane);
     if (wave < 2) dma4((wave == 0 ? L2_b : D_b) + min(q0 + lane, T - 1), rows0 + (stg * 2 + wave) * 256);
   };
-  bf16x8 kf[4], vf[4];
+  h16x8 kf[4], vf[4];
 #pragma unroll
   for (int kk = 0; kk < 4; ++kk) {
-    kf[kk] = as_bf16x8(ld16_or_zero(K + (int64_t)mykey * ld + kk * 16 + hl * 8, mykey < T));
-    vf[kk] = as_bf16x8(ld16_or_zero(V + (int64_t)mykey * ld + kk * 16 + hl * 8, mykey < T));
+    kf[kk] = as_h16x8(ld16_or_zero(K + (int64_t)mykey * ld + kk * 16 + hl * 8, mykey < T));
+    vf[kk] = as_h16x8(ld16_or_zero(V + (int64_t)mykey * ld + kk * 16 + hl * 8, mykey < T));
   }
   f32x16 dk[2], dv[2];
 #pragma unroll
@@ -417,8 +416,8 @@ __global__ __launch_bounds__(256, 2) void flash_bwd_dkdv_kernel(const bf16* __re
     lds_barrier();
     if (it + 2 < nqt) load(it + 2, stg2);
     const int q0 = key0 + it * 64;
-    const bf16* Qs = smem + stg * ASTAGE;
-    const bf16* Gs = Qs + ATILE;
+    const h16* Qs = smem + stg * ASTAGE;
+    const h16* Gs = Qs + ATILE;
     if (q0 + 63 >= wk0) {  // some query of the tile sees a key of this wave
       const bool diag = q0 < wk0 + 31 || q0 + 64 > T;
       f32x16 P[2], dS[2];
@@ -429,8 +428,8 @@ __global__ __launch_bounds__(256, 2) void flash_bwd_dkdv_kernel(const bf16* __re
         for (int r = 0; r < 16; ++r) sv[r] = dp[r] = 0.f;
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
-          sv = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag(Qs, i * 32, kk, lane), kf[kk], sv, 0, 0, 0);
-          dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag(Gs, i * 32, kk, lane), vf[kk], dp, 0, 0, 0);
+          sv = mfma32(row_frag(Qs, i * 32, kk, lane), kf[kk], sv);
+          dp = mfma32(row_frag(Gs, i * 32, kk, lane), vf[kk], dp);
         }
         // sv[r]: query q0 + 32 i + 8 (r/4) + 4 hl + r%4, key mykey.  Queries
         // before the key or past T get score -inf (probability exactly 0).
@@ -459,12 +458,12 @@ __global__ __launch_bounds__(256, 2) void flash_bwd_dkdv_kernel(const bf16* __re
       // dV^T += dO^T P, dK^T += Q^T dS (transposed operands read from the natural tiles)
 #pragma unroll
       for (int st = 0; st < 4; ++st) {
-        const bf16x8 pb = pack8(P[st >> 1], 8 * (st & 1));
-        const bf16x8 sb = pack8(dS[st >> 1], 8 * (st & 1));
+        const h16x8 pb = pack8(P[st >> 1], 8 * (st & 1));
+        const h16x8 sb = pack8(dS[st >> 1], 8 * (st & 1));
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
-          dv[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag_keys(Gs, st * 16, t * 32, lane), pb, dv[t], 0, 0, 0);
-          dk[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag_keys(Qs, st * 16, t * 32, lane), sb, dk[t], 0, 0, 0);
+          dv[t] = mfma32(tr_frag_keys(Gs, st * 16, t * 32, lane), pb, dv[t]);
+          dk[t] = mfma32(tr_frag_keys(Qs, st * 16, t * 32, lane), sb, dk[t]);
         }
       }
     }
@@ -475,7 +474,7 @@ __global__ __launch_bounds__(256, 2) void flash_bwd_dkdv_kernel(const bf16* __re
     if (it + 2 < nqt) step(it + 2, std::integral_constant<int, 2>{});
   }
   if (mykey < T) {
-    bf16* o = dqkv + ((int64_t)b * T + mykey) * ld + h * HD;
+    h16* o = dqkv + ((int64_t)b * T + mykey) * ld + h * HD;
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
@@ -502,13 +501,13 @@ __global__ __launch_bounds__(256, 2) void flash_bwd_dkdv_kernel(const bf16* __re
 // for them from the dO and O rows (and stores it for the dK / dV kernel), and
 // accumulates dQ^T over the key tiles (64 keys) it sees; K and V tiles stream
 // into a three-stage LDS ring as in the forward kernel.
-__global__ __launch_bounds__(256, 3) void flash_bwd_dq_kernel(const bf16* __restrict__ qkv,
-                                                              const bf16* __restrict__ y,
-                                                              const bf16* __restrict__ dy,
+__global__ __launch_bounds__(256, 3) void flash_bwd_dq_kernel(const h16* __restrict__ qkv,
+                                                              const h16* __restrict__ y,
+                                                              const h16* __restrict__ dy,
                                                               const float* __restrict__ lse, float* __restrict__ Dd,
-                                                              bf16* __restrict__ dqkv, int T, int NH, int C, float sl2,
+                                                              h16* __restrict__ dqkv, int T, int NH, int C, float sl2,
                                                               float scale, float* __restrict__ colsum) {
-  __shared__ __attribute__((aligned(1024))) bf16 smem[3 * ASTAGE];  // [stage][K | V]
+  __shared__ __attribute__((aligned(1024))) h16 smem[3 * ASTAGE];  // [stage][K | V]
   int qt, h, b;
   attn_block(T, NH, qt, h, b);
   qt = (T + 127) / 128 - 1 - qt;  // tile 0: the most key tiles
@@ -518,10 +517,10 @@ __global__ __launch_bounds__(256, 3) void flash_bwd_dq_kernel(const bf16* __rest
   const int wq0 = q0 + wave * 32;
   const int myq = wq0 + lc;
   const int64_t ld = 3 * (int64_t)C;
-  const bf16* Q = qkv + (int64_t)b * T * ld + h * HD;
-  const bf16* K = Q + C;
-  const bf16* V = Q + 2 * C;
-  const bf16* G = dy + (int64_t)b * T * C + h * HD;
+  const h16* Q = qkv + (int64_t)b * T * ld + h * HD;
+  const h16* K = Q + C;
+  const h16* V = Q + 2 * C;
+  const h16* G = dy + (int64_t)b * T * C + h * HD;
   const uint32_t lds0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void*)smem);
   const int nkt = (min(T, q0 + 128) + 63) / 64;
   AttnTileLoader tl;
@@ -536,13 +535,13 @@ __global__ __launch_bounds__(256, 3) void flash_bwd_dq_kernel(const bf16* __rest
 
   const bool qok = myq < T;
   const float lse2 = qok ? lse[((int64_t)b * NH + h) * T + myq] * kLog2e : 0.f;
-  bf16x8 qf[4], gf[4];
+  h16x8 qf[4], gf[4];
   float dsum = 0.f;  // this lane's half of D = sum_d dO O for its query
 #pragma unroll
   for (int kk = 0; kk < 4; ++kk) {
-    qf[kk] = as_bf16x8(ld16_or_zero(Q + (int64_t)myq * ld + kk * 16 + hl * 8, qok));
-    gf[kk] = as_bf16x8(ld16_or_zero(G + (int64_t)myq * C + kk * 16 + hl * 8, qok));
-    const bf16x8 of = as_bf16x8(ld16_or_zero(y + ((int64_t)b * T + myq) * C + h * HD + kk * 16 + hl * 8, qok));
+    qf[kk] = as_h16x8(ld16_or_zero(Q + (int64_t)myq * ld + kk * 16 + hl * 8, qok));
+    gf[kk] = as_h16x8(ld16_or_zero(G + (int64_t)myq * C + kk * 16 + hl * 8, qok));
+    const h16x8 of = as_h16x8(ld16_or_zero(y + ((int64_t)b * T + myq) * C + h * HD + kk * 16 + hl * 8, qok));
 #pragma unroll
     for (int e = 0; e < 8; ++e) dsum = fmaf((float)gf[kk][e], (float)of[e], dsum);
   }
@@ -566,8 +565,8 @@ __global__ __launch_bounds__(256, 3) void flash_bwd_dq_kernel(const bf16* __rest
     lds_barrier();
     if (kt + 2 < nkt) load(kt + 2, stg2);
     const int k0 = kt * 64;
-    const bf16* Ks = smem + stg * ASTAGE;
-    const bf16* Vs = Ks + ATILE;
+    const h16* Ks = smem + stg * ASTAGE;
+    const h16* Vs = Ks + ATILE;
     {  // a key tile past every query of the wave is masked whole (adds zeros)
       const bool diag = k0 + 63 > wq0 || k0 + 64 > T;
       f32x16 dS[2];
@@ -578,8 +577,8 @@ __global__ __launch_bounds__(256, 3) void flash_bwd_dq_kernel(const bf16* __rest
         for (int r = 0; r < 16; ++r) sv[r] = dp[r] = 0.f;
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
-          sv = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag(Ks, js * 32, kk, lane), qf[kk], sv, 0, 0, 0);
-          dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag(Vs, js * 32, kk, lane), gf[kk], dp, 0, 0, 0);
+          sv = mfma32(row_frag(Ks, js * 32, kk, lane), qf[kk], sv);
+          dp = mfma32(row_frag(Vs, js * 32, kk, lane), gf[kk], dp);
         }
         // sv[r]: key k0 + 32 js + 8 (r/4) + 4 hl + r%4, query myq; keys past
         // the query get score -inf (probability exactly 0)
@@ -597,16 +596,16 @@ __global__ __launch_bounds__(256, 3) void flash_bwd_dq_kernel(const bf16* __rest
       // dQ^T += K^T dS^T (K read transposed, keys in the accumulator order)
 #pragma unroll
       for (int st = 0; st < 4; ++st) {
-        const bf16x8 sb = pack8(dS[st >> 1], 8 * (st & 1));
+        const h16x8 sb = pack8(dS[st >> 1], 8 * (st & 1));
 #pragma unroll
         for (int t = 0; t < 2; ++t)
-          dq[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag_keys(Ks, st * 16, t * 32, lane), sb, dq[t], 0, 0, 0);
+          dq[t] = mfma32(tr_frag_keys(Ks, st * 16, t * 32, lane), sb, dq[t]);
       }
     }
     stg = stg1;
   }
   if (qok) {
-    bf16* o = dqkv + ((int64_t)b * T + myq) * ld + h * HD;
+    h16* o = dqkv + ((int64_t)b * T + myq) * ld + h * HD;
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
@@ -626,7 +625,7 @@ __global__ __launch_bounds__(256, 3) void flash_bwd_dq_kernel(const bf16* __rest
 void attn_fwd_bf16(const void* qkv, void* y, float* lse, int B, int T, int NH, int C, hipStream_t s) {
   const float scale = 1.0f / sqrtf((float)HD);
   const unsigned grid = (unsigned)((T + 127) / 128 * NH * B);
-  flash_fwd_kernel<<<grid, 256, 0, s>>>(reinterpret_cast<const bf16*>(qkv), reinterpret_cast<bf16*>(y), lse, T, NH,
+  flash_fwd_kernel<<<grid, 256, 0, s>>>(reinterpret_cast<const h16*>(qkv), reinterpret_cast<h16*>(y), lse, T, NH,
                                         C, scale * kLog2e);
 }
 
@@ -636,11 +635,11 @@ bool attn_bwd_bf16(const void* qkv, const void* y, const void* dy, const float* 
   const float scale = 1.0f / sqrtf((float)HD);
   const unsigned grid = (unsigned)((T + 127) / 128 * NH * B);
   // dQ first: it also writes D = rowsum(dO o O), which dK / dV reads
-  flash_bwd_dq_kernel<<<grid, 256, 0, s>>>(reinterpret_cast<const bf16*>(qkv), reinterpret_cast<const bf16*>(y),
-                                           reinterpret_cast<const bf16*>(dy), lse, Dbuf,
-                                           reinterpret_cast<bf16*>(dqkv), T, NH, C, scale * kLog2e, scale, colsum);
-  flash_bwd_dkdv_kernel<<<grid, 256, 0, s>>>(reinterpret_cast<const bf16*>(qkv), reinterpret_cast<const bf16*>(dy),
-                                             lse, Dbuf, reinterpret_cast<bf16*>(dqkv), T, NH, C, scale * kLog2e,
+  flash_bwd_dq_kernel<<<grid, 256, 0, s>>>(reinterpret_cast<const h16*>(qkv), reinterpret_cast<const h16*>(y),
+                                           reinterpret_cast<const h16*>(dy), lse, Dbuf,
+                                           reinterpret_cast<h16*>(dqkv), T, NH, C, scale * kLog2e, scale, colsum);
+  flash_bwd_dkdv_kernel<<<grid, 256, 0, s>>>(reinterpret_cast<const h16*>(qkv), reinterpret_cast<const h16*>(dy),
+                                             lse, Dbuf, reinterpret_cast<h16*>(dqkv), T, NH, C, scale * kLog2e,
                                              scale, colsum);
   return colsum != nullptr;
 }

@@ -4,10 +4,22 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-typedef __bf16 bf16;
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+// h16: the 16-bit operand type of the MFMA kernels (GEMM operands,
+// attention operands, the activations kept for the backward, logits).  It is
+// bfloat16, except in the translation units compiled for the fp16 mode
+// (GPT2_OPS_F16 defined, namespace gpt2k_f16), where it is IEEE binary16.
+#ifdef GPT2_OPS_F16
+typedef _Float16 h16;
+#else
+typedef __bf16 h16;
+#endif
+typedef h16 h16x8 __attribute__((ext_vector_type(8)));
+typedef h16 h16x4 __attribute__((ext_vector_type(4)));
+typedef h16 h16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -18,31 +30,50 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 // ---- conversions -----------------------------------------------------------
 DEVI float to_f32(float x) { return x; }
-DEVI float to_f32(bf16 x) { return (float)x; }
+DEVI float to_f32(h16 x) { return (float)x; }
 template <typename T> DEVI T from_f32(float x);
 template <> DEVI float from_f32<float>(float x) { return x; }
-template <> DEVI bf16 from_f32<bf16>(float x) { return (bf16)x; }  // RNE (v_cvt_pk_bf16_f32)
+template <> DEVI h16 from_f32<h16>(float x) { return (h16)x; }  // round to nearest even
 
 // Load / store four consecutive elements as fp32.
 DEVI void load4(const float* p, float v[4]) {
   f32x4 t = *reinterpret_cast<const f32x4*>(p);
   v[0] = t[0]; v[1] = t[1]; v[2] = t[2]; v[3] = t[3];
 }
-DEVI void load4(const bf16* p, float v[4]) {
-  bf16x4 t = *reinterpret_cast<const bf16x4*>(p);
+DEVI void load4(const h16* p, float v[4]) {
+  h16x4 t = *reinterpret_cast<const h16x4*>(p);
   v[0] = (float)t[0]; v[1] = (float)t[1]; v[2] = (float)t[2]; v[3] = (float)t[3];
 }
 DEVI void store4(float* p, const float v[4]) {
   f32x4 t = {v[0], v[1], v[2], v[3]};
   *reinterpret_cast<f32x4*>(p) = t;
 }
-DEVI void store4(bf16* p, const float v[4]) {
-  bf16x4 t = {(bf16)v[0], (bf16)v[1], (bf16)v[2], (bf16)v[3]};
-  *reinterpret_cast<bf16x4*>(p) = t;
+DEVI void store4(h16* p, const float v[4]) {
+  h16x4 t = {(h16)v[0], (h16)v[1], (h16)v[2], (h16)v[3]};
+  *reinterpret_cast<h16x4*>(p) = t;
 }
 
-// Sixteen bytes as fp32 values: four floats, or eight bf16 (element 2i in the
-// low half of word i).
+// The two 16-bit values of a 32-bit word (element 0 in the low half) as fp32.
+DEVI float lo16_f32(uint32_t w) {
+  if constexpr (__is_same(h16, __bf16)) return __builtin_bit_cast(float, w << 16);
+  else return (float)__builtin_bit_cast(h16, (uint16_t)(w & 0xffffu));
+}
+DEVI float hi16_f32(uint32_t w) {
+  if constexpr (__is_same(h16, __bf16)) return __builtin_bit_cast(float, w & 0xffff0000u);
+  else return (float)__builtin_bit_cast(h16, (uint16_t)(w >> 16));
+}
+
+// c + a b on the 32 x 32 x 16 MFMA of the operand type (v_mfma_f32_32x32x16_bf16
+// or _f16; fp32 accumulation either way).
+DEVI f32x16 mfma32(bf16x8_t a, bf16x8_t b, f32x16 c) { return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0); }
+DEVI f32x16 mfma32(f16x8_t a, f16x8_t b, f32x16 c) { return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0); }
+
+// acc + a0 b0 + a1 b1 in fp32 (v_dot2c_f32_bf16 / v_dot2_f32_f16)
+DEVI float dot2(bf16x2_t a, bf16x2_t b, float acc) { return __builtin_amdgcn_fdot2_f32_bf16(a, b, acc, false); }
+DEVI float dot2(f16x2_t a, f16x2_t b, float acc) { return __builtin_amdgcn_fdot2(a, b, acc, false); }
+
+// Sixteen bytes as fp32 values: four floats, or eight 16-bit values (element
+// 2i in the low half of word i).
 template <typename T> DEVI void unpack16(u32x4 v, float* f);
 template <> DEVI void unpack16<float>(u32x4 v, float* f) {
 #pragma unroll
@@ -53,11 +84,12 @@ template <> DEVI void unpack16<float>(u32x4 v, float* f) {
     f[i] = __builtin_bit_cast(float, u);
   }
 }
-template <> DEVI void unpack16<bf16>(u32x4 v, float* f) {
+template <> DEVI void unpack16<h16>(u32x4 v, float* f) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    f[2 * i] = __builtin_bit_cast(float, v[i] << 16);
-    f[2 * i + 1] = __builtin_bit_cast(float, v[i] & 0xffff0000u);
+    const uint32_t u = v[i];
+    f[2 * i] = lo16_f32(u);
+    f[2 * i + 1] = hi16_f32(u);
   }
 }
 
@@ -134,7 +166,7 @@ DEVI float block_max(float v, float* scratch) {
   return r;
 }
 
-// ---- 8x8 bf16 transpose in registers ------------------------------------------
+// ---- 8x8 16-bit transpose in registers ------------------------------------------
 // in[j] holds 8 bf16 of row j (elements 0..7 of that row).  out[e] receives
 // the 8 bf16 of column e (element j from row j).
 DEVI void transpose8x8(const u32x4 in[8], u32x4 out[8]) {

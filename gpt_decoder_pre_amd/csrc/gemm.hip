@@ -105,7 +105,7 @@ struct TileLoader {
   static constexpr int REGS = KMAJ ? PER : PER * 8;
   u32x4 r[REGS];
 
-  DEVI void load(const bf16* g, int64_t ld, int r0, int rmax, int k0, int kend, int tid) {
+  DEVI void load(const h16* g, int64_t ld, int r0, int rmax, int k0, int kend, int tid) {
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
       const int c = tid + i * NT;
@@ -130,7 +130,7 @@ struct TileLoader {
       }
     }
   }
-  DEVI void store(bf16* s, int tid) {
+  DEVI void store(h16* s, int tid) {
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
       const int c = tid + i * NT;
@@ -190,7 +190,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_bf16_kernel(GemmArgs p
   constexpr int WTM = BM / WGM, WTN = BN / WGN;
   constexpr int FM = WTM / 32, FN = WTN / 32;
   static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile is a multiple of 32");
-  __shared__ __attribute__((aligned(16))) bf16 smem[2 * (BM + BN) * LDS];
+  __shared__ __attribute__((aligned(16))) h16 smem[2 * (BM + BN) * LDS];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / WGN, wn = wave % WGN;
@@ -202,13 +202,13 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_bf16_kernel(GemmArgs p
   const int kbeg = split * p.k_per_split;
   const int kend = min(p.K, kbeg + p.k_per_split);
   const int nkt = kend > kbeg ? (kend - kbeg + BK - 1) / BK : 0;
-  const bf16* A = reinterpret_cast<const bf16*>(p.A);
-  const bf16* B = reinterpret_cast<const bf16*>(p.B);
+  const h16* A = reinterpret_cast<const h16*>(p.A);
+  const h16* B = reinterpret_cast<const h16*>(p.B);
 
-  bf16* sA0 = smem;
-  bf16* sB0 = smem + BM * LDS;
-  bf16* sA1 = smem + (BM + BN) * LDS;
-  bf16* sB1 = sA1 + BM * LDS;
+  h16* sA0 = smem;
+  h16* sB0 = smem + BM * LDS;
+  h16* sA1 = smem + (BM + BN) * LDS;
+  h16* sB1 = sA1 + BM * LDS;
 
   f32x16 acc[FM][FN];
 #pragma unroll
@@ -234,21 +234,21 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_bf16_kernel(GemmArgs p
       la.load(A, p.lda, m0, p.M, kbeg + (kt + 1) * BK, kend, tid);
       lb.load(B, p.ldb, n0, p.N, kbeg + (kt + 1) * BK, kend, tid);
     }
-    const bf16* a_s = ((kt & 1) ? sA1 : sA0) + (wm * WTM + lc) * LDS + hl * 8;
-    const bf16* b_s = ((kt & 1) ? sB1 : sB0) + (wn * WTN + lc) * LDS + hl * 8;
+    const h16* a_s = ((kt & 1) ? sA1 : sA0) + (wm * WTM + lc) * LDS + hl * 8;
+    const h16* b_s = ((kt & 1) ? sB1 : sB0) + (wn * WTN + lc) * LDS + hl * 8;
 #pragma unroll
     for (int kk = 0; kk < BK / 16; ++kk) {
-      bf16x8 af[FM], bfr[FN];
+      h16x8 af[FM], bfr[FN];
 #pragma unroll
-      for (int i = 0; i < FM; ++i) af[i] = *reinterpret_cast<const bf16x8*>(a_s + i * 32 * LDS + kk * 16);
+      for (int i = 0; i < FM; ++i) af[i] = *reinterpret_cast<const h16x8*>(a_s + i * 32 * LDS + kk * 16);
 #pragma unroll
-      for (int j = 0; j < FN; ++j) bfr[j] = *reinterpret_cast<const bf16x8*>(b_s + j * 32 * LDS + kk * 16);
+      for (int j = 0; j < FN; ++j) bfr[j] = *reinterpret_cast<const h16x8*>(b_s + j * 32 * LDS + kk * 16);
 #pragma unroll
       for (int i = 0; i < FM; ++i)
 #pragma unroll
         for (int j = 0; j < FN; ++j)
           // first operand supplies the output rows (n), second the columns (m)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[j], af[i], acc[i][j], 0, 0, 0);
+          acc[i][j] = mfma32(bfr[j], af[i], acc[i][j]);
     }
     if (more) {
       la.store((kt & 1) ? sA0 : sA1, tid);
@@ -269,7 +269,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_bf16_kernel(GemmArgs p
         const int n = n0 + wn * WTN + j * 32 + 8 * q + 4 * hl;
         if (n < p.N) {
           float v[4] = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
-          epi_store4<EPI, bf16>(p, m, n, v, split);
+          epi_store4<EPI, h16>(p, m, n, v, split);
         }
       }
     }
@@ -300,11 +300,11 @@ struct DirectLoader {
   // wave); surplus loads repeat the tile's last chunk (same bytes, same place)
   static constexpr int PER_WAVE = (INSTR + NW - 1) / NW;
   static_assert(BYTES % 1024 == 0, "whole 1 KB wave loads");
-  const bf16* src[PER_WAVE];
+  const h16* src[PER_WAVE];
   uint32_t lds[PER_WAVE];
   int64_t kstep;  // elements between consecutive k-tiles
 
-  DEVI void init(const bf16* g, int64_t ld, int r0, int rmax, int kbeg, const bf16* lds_tile, int wave, int lane) {
+  DEVI void init(const h16* g, int64_t ld, int r0, int rmax, int kbeg, const h16* lds_tile, int wave, int lane) {
 #pragma unroll
     for (int j = 0; j < PER_WAVE; ++j) {
       const int J = min(wave * PER_WAVE + j, INSTR - 1);
@@ -348,7 +348,7 @@ constexpr bool epi_staged() {
 // aux_pre (EPI_GELU_BWD, staged, or null): this wave's aux tile already in
 // registers, chunk `it` of the staging loop below in aux_pre[it].
 template <int EPI, int FM, int FN, bool STAGED, int RB = 32 * FM>
-DEVI void gemm_epilogue(const GemmArgs& p, f32x16 (&acc)[FM][FN], bf16* region, int mb, int nb, int lane, int split,
+DEVI void gemm_epilogue(const GemmArgs& p, f32x16 (&acc)[FM][FN], h16* region, int mb, int nb, int lane, int split,
                         const u32x4* aux_pre = nullptr) {
   constexpr int WTM = 32 * FM, WTN = 32 * FN;
   const int lc = lane & 31, hl = lane >> 5;
@@ -368,7 +368,7 @@ DEVI void gemm_epilogue(const GemmArgs& p, f32x16 (&acc)[FM][FN], bf16* region, 
       const int mi = mb + RB * pb;
       if constexpr (EPI == EPI_GELU_BWD) {
         // the gelu'(u) rows come in whole row segments too
-        const bf16* aux = reinterpret_cast<const bf16*>(p.aux);
+        const h16* aux = reinterpret_cast<const h16*>(p.aux);
 #pragma unroll
         for (int it = 0; it < ITB; ++it) {
           const int q = it * 64 + lane;
@@ -428,7 +428,7 @@ DEVI void gemm_epilogue(const GemmArgs& p, f32x16 (&acc)[FM][FN], bf16* region, 
         }
         __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's LDS writes are done
         __builtin_amdgcn_wave_barrier();
-        bf16* out = reinterpret_cast<bf16*>(o == 0 ? p.C : p.C2);
+        h16* out = reinterpret_cast<h16*>(o == 0 ? p.C : p.C2);
 #pragma unroll
         for (int it = 0; it < ITB; ++it) {
           const int q = it * 64 + lane;
@@ -446,12 +446,12 @@ DEVI void gemm_epilogue(const GemmArgs& p, f32x16 (&acc)[FM][FN], bf16* region, 
           if (p.colsum && lane < WTN / 2) {
             const int n = nb + 2 * lane;
             auto sum_rows = [&](int r0, int rows) {
-              const bf16* col = region + r0 * SLD + 2 * lane;
+              const h16* col = region + r0 * SLD + 2 * lane;
 #pragma unroll 8
               for (int r = 0; r < rows; ++r) {
                 const uint32_t w = *reinterpret_cast<const uint32_t*>(col + r * SLD);
-                cs0 += __uint_as_float(w << 16);
-                cs1 += __uint_as_float(w & 0xffff0000u);
+                cs0 += lo16_f32(w);
+                cs1 += hi16_f32(w);
               }
             };
             auto flush = [&](int c0) {  // chunk of rows c0 .. c0 + 63
@@ -524,7 +524,7 @@ DEVI void gemm_epilogue(const GemmArgs& p, f32x16 (&acc)[FM][FN], bf16* region, 
           const int n = nb + j * 32 + 8 * q + 4 * hl;
           if (n < p.N) {
             float v[4] = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
-            epi_store4<EPI, bf16>(p, m, n, v, split);
+            epi_store4<EPI, h16>(p, m, n, v, split);
           }
         }
         __builtin_amdgcn_sched_barrier(0);
@@ -545,10 +545,10 @@ __global__ __launch_bounds__(64 * WGM * WGN, OCC) void gemm_lds_kernel(GemmArgs 
   constexpr int LPW = LA::PER_WAVE + LB::PER_WAVE;  // loads per wave per tile
   // One array per stage: every LDS access names its stage at compile time, so
   // the compiler can tell the reads of stage s from the loads into the others.
-  __shared__ __attribute__((aligned(1024))) bf16 st0[STAGE];
-  __shared__ __attribute__((aligned(1024))) bf16 st1[STAGE];
-  __shared__ __attribute__((aligned(1024))) bf16 st2[NST > 2 ? STAGE : 1];
-  __shared__ __attribute__((aligned(1024))) bf16 st3[NST > 3 ? STAGE : 1];
+  __shared__ __attribute__((aligned(1024))) h16 st0[STAGE];
+  __shared__ __attribute__((aligned(1024))) h16 st1[STAGE];
+  __shared__ __attribute__((aligned(1024))) h16 st2[NST > 2 ? STAGE : 1];
+  __shared__ __attribute__((aligned(1024))) h16 st3[NST > 3 ? STAGE : 1];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -560,10 +560,10 @@ __global__ __launch_bounds__(64 * WGM * WGN, OCC) void gemm_lds_kernel(GemmArgs 
   const int kbeg = split * p.k_per_split;
   const int kend = min(p.K, kbeg + p.k_per_split);
   const int nkt = kend > kbeg ? (kend - kbeg) / BK : 0;
-  const bf16* A = reinterpret_cast<const bf16*>(p.A);
-  const bf16* B = reinterpret_cast<const bf16*>(p.B);
+  const h16* A = reinterpret_cast<const h16*>(p.A);
+  const h16* B = reinterpret_cast<const h16*>(p.B);
 
-  auto stage = [&](auto S) -> bf16* {
+  auto stage = [&](auto S) -> h16* {
     constexpr int s = decltype(S)::value;
     if constexpr (s == 0) return st0;
     else if constexpr (s == 1) return st1;
@@ -617,11 +617,11 @@ __global__ __launch_bounds__(64 * WGM * WGN, OCC) void gemm_lds_kernel(GemmArgs 
     }
     lds_barrier();  // every wave's loads of tile kt landed; the stage of tile kt-1 is free
     if (kt + NST - 1 < nkt) issue(std::integral_constant<int, (s + NST - 1) % NST>{}, kt + NST - 1);
-    const bf16* sa = stage(S);
-    const bf16* sb = sa + BM * BK;
+    const h16* sa = stage(S);
+    const h16* sb = sa + BM * BK;
 #pragma unroll
     for (int kk = 0; kk < BK / 16; ++kk) {
-      bf16x8 af[FM], bfr[FN];
+      h16x8 af[FM], bfr[FN];
 #pragma unroll
       for (int i = 0; i < FM; ++i) af[i] = frag<A_K, BM, BK>(sa, wm * WTM + i * 32, kk, lane);
 #pragma unroll
@@ -630,7 +630,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, OCC) void gemm_lds_kernel(GemmArgs 
       for (int i = 0; i < FM; ++i)
 #pragma unroll
         for (int j = 0; j < FN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[j], af[i], acc[i][j], 0, 0, 0);
+          acc[i][j] = mfma32(bfr[j], af[i], acc[i][j]);
     }
   };
 
@@ -654,7 +654,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, OCC) void gemm_lds_kernel(GemmArgs 
   constexpr int WPA = (NW + 1) / 2;  // waves per stage array
   if constexpr (epi_staged<EPI>() && WPA * WTM * SLD <= STAGE) {
     __syncthreads();  // all waves are done reading the operand stages
-    bf16* region = (wave < WPA ? st0 : st1) + (wave % WPA) * WTM * SLD;
+    h16* region = (wave < WPA ? st0 : st1) + (wave % WPA) * WTM * SLD;
     gemm_epilogue<EPI, FM, FN, true>(pe, acc, region, m0 + wm * WTM, n0 + wn * WTN, lane, split);
   } else {
     gemm_epilogue<EPI, FM, FN, false>(pe, acc, nullptr, m0 + wm * WTM, n0 + wn * WTN, lane, split);
@@ -686,13 +686,13 @@ struct SaddrLoader {
   static constexpr int INSTR = R * 64 * 2 / 1024;  // 1 KB wave instructions per k-tile
   static constexpr int PER_WAVE = INSTR / NW;
   static_assert(INSTR % NW == 0, "whole instructions per wave");
-  const bf16* base;
+  const h16* base;
   uint32_t voff[PER_WAVE];
   uint32_t lds[PER_WAVE];
   int64_t kstep;
 
   // Rows past rmax are clamped to the last row (their outputs are discarded).
-  DEVI void init(const bf16* g, int64_t ld, int r0, int rmax, int kbeg, const bf16* lds_tile, int wave, int lane) {
+  DEVI void init(const h16* g, int64_t ld, int r0, int rmax, int kbeg, const h16* lds_tile, int wave, int lane) {
     base = uniform_ptr(KMAJ ? g + (int64_t)r0 * ld + kbeg : g + (int64_t)kbeg * ld + r0);
 #pragma unroll
     for (int j = 0; j < PER_WAVE; ++j) {
@@ -736,7 +736,7 @@ constexpr int w4_lds_elems() {
 // epilogue of the current one (which stages through the other stage), so
 // that their latency is spent storing instead of waiting.
 template <bool A_K, bool B_K, int BM, int BN, int EPI, bool PERSIST, int NW, class Next>
-DEVI void w4_tiles(const GemmArgs& p, bf16* smem, Next next) {
+DEVI void w4_tiles(const GemmArgs& p, h16* smem, Next next) {
   constexpr int BK = 64;
   constexpr int WTM = BM / (NW / 2), WTN = BN / 2;  // NW / 2 x 2 waves
   static_assert(NW == 4 || NW == 8, "four or eight waves");
@@ -764,8 +764,8 @@ DEVI void w4_tiles(const GemmArgs& p, bf16* smem, Next next) {
     kbeg = split * p.k_per_split;
     const int kend = min(p.K, kbeg + p.k_per_split);
     nkt = kend > kbeg ? (kend - kbeg) / BK : 0;
-    la.init(reinterpret_cast<const bf16*>(p.A), p.lda, m0, p.M, kbeg, smem, wave, lane);
-    lb.init(reinterpret_cast<const bf16*>(p.B), p.ldb, n0, p.N, kbeg, smem + BM * BK, wave, lane);
+    la.init(reinterpret_cast<const h16*>(p.A), p.lda, m0, p.M, kbeg, smem, wave, lane);
+    lb.init(reinterpret_cast<const h16*>(p.B), p.ldb, n0, p.N, kbeg, smem + BM * BK, wave, lane);
   };
   constexpr uint32_t kStageBytes = STAGE * 2;
   // direct load number d (A loads first) of k-tile kt into the stage at stage_off
@@ -776,11 +776,11 @@ DEVI void w4_tiles(const GemmArgs& p, bf16* smem, Next next) {
 
   constexpr bool kBiasInit = EPI == EPI_ACT || EPI == EPI_GELU || EPI == EPI_RESID;
   f32x16 acc[FM][FN];
-  bf16x8 fa[2][FM], fb[2][FN];
-  auto read_a = [&](int buf, int i, const bf16* st, int kk) {
+  h16x8 fa[2][FM], fb[2][FN];
+  auto read_a = [&](int buf, int i, const h16* st, int kk) {
     fa[buf][i] = frag<A_K, BM, BK>(st, wm * WTM + i * 32, kk, lane);
   };
-  auto read_b = [&](int buf, int j, const bf16* st, int kk) {
+  auto read_b = [&](int buf, int j, const h16* st, int kk) {
     fb[buf][j] = frag<B_K, BN, BK>(st + BM * BK, wn * WTN + j * 32, kk, lane);
   };
 
@@ -794,7 +794,7 @@ DEVI void w4_tiles(const GemmArgs& p, bf16* smem, Next next) {
   auto aux_load = [&](int j) {
     const int q = j * 64 + lane, r = q / CPR, c = q % CPR;
     const int m = m0 + wm * WTM + r, n = n0 + wn * WTN + 8 * c;
-    auxr[j] = ld16_or_zero(reinterpret_cast<const bf16*>(p.aux) + (int64_t)m * p.ldc + n, m < p.M && n < p.N);
+    auxr[j] = ld16_or_zero(reinterpret_cast<const h16*>(p.aux) + (int64_t)m * p.ldc + n, m < p.M && n < p.N);
   };
   auto aux_share = [&](int kt) {  // k-tiles 0 .. nkt-2 each load their share
     const int lo = kt * NA / (nkt - 1), hi = (kt + 1) * NA / (nkt - 1);
@@ -825,8 +825,8 @@ DEVI void w4_tiles(const GemmArgs& p, bf16* smem, Next next) {
   // wave is past the barrier).
   auto ktile = [&](auto next_c, auto load_c, int kt) {
     constexpr bool NEXT = decltype(next_c)::value, LOAD = decltype(load_c)::value;
-    const bf16* cur = smem + (kt & 1) * STAGE;
-    const bf16* nxt = smem + ((kt + 1) & 1) * STAGE;
+    const h16* cur = smem + (kt & 1) * STAGE;
+    const h16* nxt = smem + ((kt + 1) & 1) * STAGE;
     const uint32_t cur_off = (kt & 1) * kStageBytes, nxt_off = ((kt + 1) & 1) * kStageBytes;
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
@@ -841,7 +841,7 @@ DEVI void w4_tiles(const GemmArgs& p, bf16* smem, Next next) {
 #pragma unroll
       for (int g = 0; g < G; ++g) {
         const int i = g / FN, j = g % FN;
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[cb][j], fa[cb][i], acc[i][j], 0, 0, 0);
+        acc[i][j] = mfma32(fb[cb][j], fa[cb][i], acc[i][j]);
         if (kk < 3) {
           if (g < FM) read_a(cb ^ 1, g, cur, kk + 1);
           else if (g < FM + FN) read_b(cb ^ 1, g - FM, cur, kk + 1);
@@ -952,7 +952,7 @@ struct OneTile {
 
 template <bool A_K, bool B_K, int BM, int BN, int EPI, int OCC = 1, int NW = 4>
 __global__ __launch_bounds__(64 * NW, OCC) void gemm_w4_kernel(GemmArgs p) {
-  __shared__ __attribute__((aligned(1024))) bf16 smem[w4_lds_elems<BM, BN, false, NW>()];
+  __shared__ __attribute__((aligned(1024))) h16 smem[w4_lds_elems<BM, BN, false, NW>()];
   const int tiles_m = (p.M + BM - 1) / BM, tiles_n = (p.N + BN - 1) / BN;
   int tm, tn, split;
   tile_coords(p, tiles_m, tiles_n, blockIdx.x + blockIdx.y * gridDim.x, gridDim.x * gridDim.y, tm, tn, split);
@@ -966,7 +966,7 @@ __global__ __launch_bounds__(64 * NW, OCC) void gemm_w4_kernel(GemmArgs p) {
 // neighbouring tiles as the one-tile-per-workgroup grid does.
 template <bool A_K, bool B_K, int BM, int BN, int EPI, int OCC = 1, int NW = 4>
 __global__ __launch_bounds__(64 * NW, OCC) void gemm_w4p_kernel(GemmArgs p) {
-  __shared__ __attribute__((aligned(1024))) bf16 smem[w4_lds_elems<BM, BN, true, NW>()];
+  __shared__ __attribute__((aligned(1024))) h16 smem[w4_lds_elems<BM, BN, true, NW>()];
   const int tiles_m = (p.M + BM - 1) / BM, tiles_n = (p.N + BN - 1) / BN;
   const int total = tiles_m * tiles_n;
   constexpr int NX = 8;
@@ -1027,7 +1027,7 @@ DEVI void group_tile(const GemmGroup& grp, int t, GemmArgs& p, int& tm, int& tn)
 
 template <int BM, int BN>
 __global__ __launch_bounds__(64 * kGroupWaves, 1) void gemm_w4_group_kernel(GemmGroup grp) {
-  __shared__ __attribute__((aligned(1024))) bf16 smem[w4_lds_elems<BM, BN, false, kGroupWaves>()];
+  __shared__ __attribute__((aligned(1024))) h16 smem[w4_lds_elems<BM, BN, false, kGroupWaves>()];
   // block b runs on XCD b % 8 as that XCD's idx-th workgroup: its whole
   // tiles first, then the K halves of its split tail tiles
   const int x = blockIdx.x % kGroupXcds, idx = blockIdx.x / kGroupXcds;
@@ -1044,8 +1044,8 @@ __global__ __launch_bounds__(64 * kGroupWaves, 1) void gemm_w4_group_kernel(Gemm
     // operands are stored [K][rows]), its half's partial into a dense
     // BM x BN block of its slot
     const int64_t slot = (int64_t)x * kGroupTailMax + (u >> 1);
-    p.A = reinterpret_cast<const bf16*>(p.A) + (int64_t)tm * BM;
-    p.B = reinterpret_cast<const bf16*>(p.B) + (int64_t)tn * BN;
+    p.A = reinterpret_cast<const h16*>(p.A) + (int64_t)tm * BM;
+    p.B = reinterpret_cast<const h16*>(p.B) + (int64_t)tn * BN;
     p.M = min(BM, p.M - tm * BM);
     p.N = min(BN, p.N - tn * BN);
     p.splits = 2;
@@ -1482,7 +1482,7 @@ bool gemm_cfg(int cfg, GemmLayout layout, GemmEpilogue epi, bool bf16_mode, cons
       break;
   }
   if (colsum && !fused_colsum) {
-    if (bf16_mode) colsum_partials<bf16>(reinterpret_cast<const bf16*>(a.C), a.M, a.N, colsum, s);
+    if (bf16_mode) colsum_partials<h16>(reinterpret_cast<const h16*>(a.C), a.M, a.N, colsum, s);
     else colsum_partials<float>(reinterpret_cast<const float*>(a.C), a.M, a.N, colsum, s);
   }
   return true;

@@ -108,7 +108,7 @@ struct gpt2_ctx {
   hipStream_t stream;
   TensorDesc t[T_COUNT];
   int64_t n_params;
-  bool bf16;
+  bool ops16;  // 16-bit MFMA operands (bf16, or fp16 in the fp16 build)
   int64_t act;  // bytes per activation element
   int64_t Mmax;
   int L, C, NH, Vp, V;
@@ -171,7 +171,7 @@ struct gpt2_ctx {
   char* layer_act(char* base, int l, int64_t cols) const { return base + (int64_t)l * Mmax * cols * act; }
   const void* W(int id, int l = 0) const {
     const int64_t o = t[id].off + (int64_t)l * t[id].per_layer;
-    return bf16 ? (const void*)((const char*)buf.params_bf16 + o * 2) : (const void*)(buf.params + o);
+    return ops16 ? (const void*)((const char*)buf.params_bf16 + o * 2) : (const void*)(buf.params + o);
   }
   const float* P(int id, int l = 0) const { return buf.params + t[id].off + (int64_t)l * t[id].per_layer; }
   float* G(int id, int l = 0) const { return buf.grads + t[id].off + (int64_t)l * t[id].per_layer; }
@@ -229,8 +229,8 @@ struct Timed {
 
 bool gemm_site(gpt2_ctx* c, const char* site, GemmLayout lay, GemmEpilogue epi, const GemmArgs& a, double bytes) {
   Timed tm(c, site, 2.0 * a.M * (double)a.N * a.K, bytes,
-           c->timing ? gemm_resolve_config(-1, lay, epi, c->bf16, a) : -1);
-  return gemm(lay, epi, c->bf16, a, c->stream);
+           c->timing ? gemm_resolve_config(-1, lay, epi, c->ops16, a) : -1);
+  return gemm(lay, epi, c->ops16, a, c->stream);
 }
 
 GemmArgs gargs(const void* A, int64_t lda, const void* B, int64_t ldb, int M, int N, int K, void* C, int64_t ldc) {
@@ -260,7 +260,7 @@ bool weight_grad(gpt2_ctx* c, const char* site, float* out, const void* A, int64
   const int64_t outn = (int64_t)Mo * N;
   GemmArgs a = gargs(A, lda, B, ldb, Mo, N, K, out, N);
   int best_cfg = -1, best_splits = 1, best_kps = K;
-  if (c->bf16) {
+  if (c->ops16) {
     double best = 1e30;
     for (int cfg = 0; cfg < kGemmConfigs; ++cfg) {
       for (int sp = 1; sp <= 16; sp *= 2) {
@@ -292,10 +292,10 @@ bool weight_grad(gpt2_ctx* c, const char* site, float* out, const void* A, int64
     best_kps = sp > 1 ? kps : K;
   }
   const double bytes = (double)c->act * ((double)K * Mo + (double)K * N) + 8.0 * outn;
-  if (!c->bf16) best_cfg = kGemmCfgF32;
+  if (!c->ops16) best_cfg = kGemmCfgF32;
   if (best_splits == 1) {
     Timed tm(c, site, 2.0 * a.M * (double)a.N * a.K, bytes, best_cfg);
-    return gemm_cfg(best_cfg, LAYOUT_TN, EPI_F32_ACC, c->bf16, a, c->stream);
+    return gemm_cfg(best_cfg, LAYOUT_TN, EPI_F32_ACC, c->ops16, a, c->stream);
   }
   a.C = c->splitk;
   a.splits = best_splits;
@@ -303,7 +303,7 @@ bool weight_grad(gpt2_ctx* c, const char* site, float* out, const void* A, int64
   a.split_stride = outn;
   {
     Timed tm(c, site, 2.0 * a.M * (double)a.N * a.K, bytes, best_cfg);
-    if (!gemm_cfg(best_cfg, LAYOUT_TN, EPI_PARTIAL, c->bf16, a, c->stream)) return false;
+    if (!gemm_cfg(best_cfg, LAYOUT_TN, EPI_PARTIAL, c->ops16, a, c->stream)) return false;
   }
   splitk_reduce_add(out, c->splitk, best_splits, outn, outn, c->stream);
   return true;
@@ -348,7 +348,7 @@ int forward_impl(gpt2_ctx* c, const int32_t* d_idx, const int32_t* d_tgt, int B,
     {
       Timed tm(c, "attn.fwd", 4.0 * B * c->NH * ((double)T * (T + 1) / 2) * (C / c->NH),
                a * (4.0 * M * C) + 4.0 * M * c->NH);
-      if (c->bf16) attn_fwd_bf16(qkv, atty, lse, B, T, c->NH, C, s);
+      if (c->ops16) attn_fwd_bf16(qkv, atty, lse, B, T, c->NH, C, s);
       else attn_fwd_f32((const float*)qkv, (float*)atty, lse, B, T, c->NH, C, s);
     }
     g = gargs(atty, C, c->W(T_PROJW, l), C, M, C, C, x_mid, C);
@@ -411,7 +411,7 @@ int backward_impl(gpt2_ctx* c) {
   // Weight gradients: in bf16 mode with whole 64-token k-tiles they are
   // collected and run as one grouped launch at the end of the pass (enough
   // output tiles to fill the GPU without split-K); otherwise each runs here.
-  const bool group_dw = c->bf16 && M % 64 == 0;
+  const bool group_dw = c->ops16 && M % 64 == 0;
   std::vector<GemmProblem> dw;
   auto wgrad = [&](const char* site, float* out, const void* A, int64_t lda, const void* Bop, int64_t ldb, int Mo,
                    int N) -> bool {
@@ -426,7 +426,7 @@ int backward_impl(gpt2_ctx* c) {
   };
   // residual-gradient slots (bf16 copy): 2L + 1 is the lm_head side, 2l + 1
   // the gradient at x_mid of block l, 2l the gradient at x_in of block l
-  const bool per_layer = c->bf16;
+  const bool per_layer = c->ops16;
   auto dres_slot = [&](int i) -> TA* {
     return (TA*)(c->dres_act + (per_layer ? (int64_t)i * c->Mmax * C * c->act : 0));
   };
@@ -492,7 +492,7 @@ int backward_impl(gpt2_ctx* c) {
                a * (9.0 * M * C) + 8.0 * M * c->NH);
       // the qkv bias gradient partials come from the attention kernels when
       // they can form them (64-token chunks within a sequence)
-      if (c->bf16)
+      if (c->ops16)
         fused = attn_bwd_bf16(qkv, atty, dy, lse, c->attnD, dqkv, B, T, c->NH, C, c->qkv_bias ? part : nullptr, s);
       else attn_bwd_f32((const float*)qkv, (const float*)atty, (const float*)dy, lse, c->attnD, (float*)dqkv, B, T,
                         c->NH, C, s);
@@ -548,7 +548,7 @@ int check_bt(const gpt2_ctx* c, int B, int T) {
   if (T > c->cfg.block_size) return GPT2_ERR_SEQ_TOO_LONG;
   if (B < 1 || T < 1 || B > c->cfg.max_batch) return GPT2_ERR_BATCH;
   // bf16 weight gradients contract over the B*T tokens in 16-byte rows
-  if (c->bf16 && ((int64_t)B * T) % 8) return GPT2_ERR_BATCH;
+  if (c->ops16 && ((int64_t)B * T) % 8) return GPT2_ERR_BATCH;
   return GPT2_OK;
 }
 
@@ -581,7 +581,7 @@ int64_t plan_workspace(gpt2_ctx* c, Plan& p, bool assign) {
   // bf16: the gradients the weight-gradient GEMMs read stay until the end of
   // the backward pass (one grouped launch there): 2L + 1 residual-gradient
   // slots, L slots of du and of dqkv.  fp32: one of each.
-  const int64_t slots = c->bf16 ? L : 1;
+  const int64_t slots = c->ops16 ? L : 1;
   c->dres_act = at((2 * slots + 1) * M * C * A);
   c->dh = (float*)at(M * C * 4);
   c->dbig = at(slots * M * 4 * C * A);
@@ -610,8 +610,8 @@ void fill_layout(gpt2_ctx* c, const gpt2_config& cfg) {
   c->cfg = cfg;
   tensor_table(cfg, c->t);
   c->n_params = total_params(c->t);
-  c->bf16 = cfg.precision == GPT2_BF16;
-  c->act = c->bf16 ? 2 : 4;
+  c->ops16 = cfg.precision == GPT2_BF16;
+  c->act = c->ops16 ? 2 : 4;
   c->Mmax = (int64_t)cfg.max_batch * cfg.block_size;
   c->L = cfg.n_layer;
   c->C = cfg.n_embd;
@@ -639,17 +639,17 @@ int gpt2_init(const gpt2_config* cfg, const gpt2_buffers* bufs, void* hip_stream
   if (sizes) {
     sizes->n_params = probe.n_params;
     sizes->workspace_bytes = ws;
-    sizes->params_bf16_bytes = probe.bf16 ? probe.n_params * 2 : 0;
+    sizes->params_bf16_bytes = probe.ops16 ? probe.n_params * 2 : 0;
   }
   if (!bufs) return GPT2_OK;
   if (!out || !bufs->params || !bufs->grads || !bufs->adam_m || !bufs->adam_v || !bufs->workspace)
     return GPT2_ERR_ARG;
-  if (probe.bf16 && !bufs->params_bf16) return GPT2_ERR_ARG;
+  if (probe.ops16 && !bufs->params_bf16) return GPT2_ERR_ARG;
   if (((uintptr_t)bufs->workspace) % 256) return GPT2_ERR_ARG;
   gpt2_ctx* c = new gpt2_ctx();
   fill_layout(c, *cfg);
   c->buf = *bufs;
-  if (!c->bf16) c->buf.params_bf16 = nullptr;
+  if (!c->ops16) c->buf.params_bf16 = nullptr;
   c->stream = (hipStream_t)hip_stream;
   Plan p2;
   plan_workspace(c, p2, true);
@@ -657,7 +657,7 @@ int gpt2_init(const gpt2_config* cfg, const gpt2_buffers* bufs, void* hip_stream
   fill_f32(c->buf.adam_m, c->n_params, 0.f, c->stream);
   fill_f32(c->buf.adam_v, c->n_params, 0.f, c->stream);
   fill_f32((float*)c->err_flag, 1, 0.f, c->stream);
-  if (c->bf16) to_bf16(c->buf.params, c->buf.params_bf16, c->n_params, c->stream);
+  if (c->ops16) to_bf16(c->buf.params, c->buf.params_bf16, c->n_params, c->stream);
   const int st = hip_status();
   if (st != GPT2_OK) {
     delete c;
@@ -672,14 +672,14 @@ int gpt2_forward_loss(gpt2_ctx* c, const int32_t* d_idx, const int32_t* d_target
   if (!c || !d_idx || !d_targets || !d_loss) return GPT2_ERR_ARG;
   const int e = check_bt(c, B, T);
   if (e != GPT2_OK) return e;
-  return c->bf16 ? forward_impl<bf16>(c, d_idx, d_targets, B, T, loss_scale, d_loss, false)
+  return c->ops16 ? forward_impl<h16>(c, d_idx, d_targets, B, T, loss_scale, d_loss, false)
                  : forward_impl<float>(c, d_idx, d_targets, B, T, loss_scale, d_loss, false);
 }
 
 int gpt2_backward(gpt2_ctx* c) {
   if (!c) return GPT2_ERR_ARG;
   if (!c->have_fwd) return GPT2_ERR_STATE;
-  return c->bf16 ? backward_impl<bf16>(c) : backward_impl<float>(c);
+  return c->ops16 ? backward_impl<h16>(c) : backward_impl<float>(c);
 }
 
 int gpt2_accumulate(gpt2_ctx* c, const int32_t* d_idx, const int32_t* d_targets, int k, int B, int T,
@@ -699,7 +699,7 @@ int gpt2_accumulate(gpt2_ctx* c, const int32_t* d_idx, const int32_t* d_targets,
       batched = embed_sort_batch(d_idx + i * stride, (int)stride, std::min(kSortBatch, k - i), c->V, c->sort_ka,
                                  c->sort_va, c->stream);
     }
-    e = c->bf16 ? forward_impl<bf16>(c, d_idx + i * stride, d_targets + i * stride, B, T, 1.0f / k, d_mean_loss,
+    e = c->ops16 ? forward_impl<h16>(c, d_idx + i * stride, d_targets + i * stride, B, T, 1.0f / k, d_mean_loss,
                                      i > 0)
                 : forward_impl<float>(c, d_idx + i * stride, d_targets + i * stride, B, T, 1.0f / k, d_mean_loss,
                                       i > 0);
@@ -807,7 +807,7 @@ int gpt2_sync_status(gpt2_ctx* c) {
 
 int gpt2_sync_params(gpt2_ctx* c) {
   if (!c) return GPT2_ERR_ARG;
-  if (c->bf16) to_bf16(c->buf.params, c->buf.params_bf16, c->n_params, c->stream);
+  if (c->ops16) to_bf16(c->buf.params, c->buf.params_bf16, c->n_params, c->stream);
   return hip_status();
 }
 
@@ -843,7 +843,7 @@ int gpt2_tensor_info(const gpt2_config* cfg, int index, const char** name, int64
 int gpt2_activation(gpt2_ctx* c, const char* name, int layer, void** ptr, int64_t* numel, int32_t* dtype) {
   if (!c || !name || !ptr || !numel || !dtype) return GPT2_ERR_ARG;
   const int64_t M = (int64_t)c->B * c->T, C = c->C;
-  const int32_t at = c->bf16 ? 1 : 0;
+  const int32_t at = c->ops16 ? 1 : 0;
   const bool lay_ok = layer >= 0 && layer < c->L;
   auto ret = [&](void* p, int64_t n, int32_t d) {
     *ptr = p;
@@ -995,7 +995,7 @@ int gpt2_checkpoint_load(gpt2_ctx* c, const char* path, int64_t* extra, int* n_e
   const int nx = (int)std::min<int64_t>(head[2], *n_extra);
   for (int i = 0; i < nx; ++i) extra[i] = ex[i];
   *n_extra = nx;
-  if (c->bf16) to_bf16(c->buf.params, c->buf.params_bf16, c->n_params, c->stream);
+  if (c->ops16) to_bf16(c->buf.params, c->buf.params_bf16, c->n_params, c->stream);
   return hip_status();
 }
 

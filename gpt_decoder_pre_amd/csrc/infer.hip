@@ -176,7 +176,7 @@ bool decode_attn(const TA* qkv, const TA* cache, TA* y, int B, int n_keys, int T
 // row (m, pos) of the layer's (B, Tmax, 2C) cache, so the step needs no
 // separate cache store.
 struct SkinnyKv {
-  bf16* cache;
+  h16* cache;
   int Tmax, pos, C;
 };
 // A of a product formed as LayerNorm(x) in the prologue (skinny16)
@@ -194,8 +194,8 @@ DEVI void skinny_store(const GemmArgs& a, const SkinnyKv& kv, int m, int n, floa
   const float bias = a.bias ? a.bias[n] : 0.f;
   const int64_t idx = (int64_t)m * a.ldc + n;
   if constexpr (EPI == EPI_ACT) {
-    const bf16 out = (bf16)(v + bias);
-    reinterpret_cast<bf16*>(a.C)[idx] = out;
+    const h16 out = (h16)(v + bias);
+    reinterpret_cast<h16*>(a.C)[idx] = out;
     if constexpr (KV) {
       if (n >= kv.C) kv.cache[((int64_t)m * kv.Tmax + kv.pos) * 2 * kv.C + (n - kv.C)] = out;
     }
@@ -206,8 +206,8 @@ DEVI void skinny_store(const GemmArgs& a, const SkinnyKv& kv, int m, int n, floa
   } else if constexpr (EPI == EPI_GELU) {
     float g, d;
     gelu_and_grad(v + bias, g, d);
-    reinterpret_cast<bf16*>(a.C)[idx] = (bf16)d;
-    reinterpret_cast<bf16*>(a.C2)[idx] = (bf16)g;
+    reinterpret_cast<h16*>(a.C)[idx] = (h16)d;
+    reinterpret_cast<h16*>(a.C2)[idx] = (h16)g;
   }
 }
 
@@ -217,29 +217,29 @@ __global__ __launch_bounds__(64 * NW) void skinny_gemm_kernel(GemmArgs a, Skinny
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n0 = blockIdx.x * 32;
   const int col = lane & 31, kh = lane >> 5;
-  const bf16* A = reinterpret_cast<const bf16*>(a.A);
-  const bf16* B = reinterpret_cast<const bf16*>(a.B);
+  const h16* A = reinterpret_cast<const h16*>(a.A);
+  const h16* B = reinterpret_cast<const h16*>(a.B);
   const bool row_ok = col < a.M, col_ok = n0 + col < a.N;
-  const bf16* ar = A + (int64_t)(row_ok ? col : 0) * a.lda + 8 * kh;
-  const bf16* br = B + (int64_t)(col_ok ? n0 + col : 0) * a.ldb + 8 * kh;
+  const h16* ar = A + (int64_t)(row_ok ? col : 0) * a.lda + 8 * kh;
+  const h16* br = B + (int64_t)(col_ok ? n0 + col : 0) * a.ldb + 8 * kh;
   f32x16 acc;
 #pragma unroll
   for (int r = 0; r < 16; ++r) acc[r] = 0.f;
   const int steps = a.K / 16;
   int ks = wave;
   for (; ks + 3 * NW < steps; ks += 4 * NW) {  // four steps per round, their loads first
-    bf16x8 af[4], bfr[4];
+    h16x8 af[4], bfr[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      af[u] = __builtin_bit_cast(bf16x8, ld16_or_zero(ar + 16 * (ks + NW * u), row_ok));
-      bfr[u] = __builtin_bit_cast(bf16x8, ld16_or_zero(br + 16 * (ks + NW * u), col_ok));
+      af[u] = __builtin_bit_cast(h16x8, ld16_or_zero(ar + 16 * (ks + NW * u), row_ok));
+      bfr[u] = __builtin_bit_cast(h16x8, ld16_or_zero(br + 16 * (ks + NW * u), col_ok));
     }
 #pragma unroll
     for (int u = 0; u < 4; ++u) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[u], bfr[u], acc, 0, 0, 0);
   }
   for (; ks < steps; ks += NW) {
-    const bf16x8 af = __builtin_bit_cast(bf16x8, ld16_or_zero(ar + 16 * ks, row_ok));
-    const bf16x8 bfr = __builtin_bit_cast(bf16x8, ld16_or_zero(br + 16 * ks, col_ok));
+    const h16x8 af = __builtin_bit_cast(h16x8, ld16_or_zero(ar + 16 * ks, row_ok));
+    const h16x8 bfr = __builtin_bit_cast(h16x8, ld16_or_zero(br + 16 * ks, col_ok));
     acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, bfr, acc, 0, 0, 0);
   }
   // acc[r] = partial C[row 8 (r / 4) + 4 kh + r % 4][column n0 + col]
@@ -278,21 +278,21 @@ __global__ __launch_bounds__(64 * NW) void skinny16_gemm_kernel(GemmArgs a, Skin
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n0 = blockIdx.x * 16;
   const int col = lane & 15, kq = lane >> 4;
-  const bf16* A = reinterpret_cast<const bf16*>(a.A);
-  const bf16* B = reinterpret_cast<const bf16*>(a.B);
+  const h16* A = reinterpret_cast<const h16*>(a.A);
+  const h16* B = reinterpret_cast<const h16*>(a.B);
   const bool row_ok = col < a.M, col_ok = n0 + col < a.N;
-  const bf16* br = B + (int64_t)(col_ok ? n0 + col : 0) * a.ldb + 8 * kq;
+  const h16* br = B + (int64_t)(col_ok ? n0 + col : 0) * a.ldb + 8 * kq;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   const int steps = a.K / 32;
   if constexpr (LNA) {
     __shared__ float stat[2][NW][16];
     const float* xr = ln.x + (int64_t)(row_ok ? col : 0) * a.lda + 8 * kq;
     float xv[U][8], ww[U][8], bb[U][8];
-    bf16x8 bfr[U];
+    h16x8 bfr[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int ks = wave + NW * u;
-      bfr[u] = __builtin_bit_cast(bf16x8, ld16_or_zero(br + 32 * ks, col_ok && ks < steps));
+      bfr[u] = __builtin_bit_cast(h16x8, ld16_or_zero(br + 32 * ks, col_ok && ks < steps));
 #pragma unroll
       for (int e = 0; e < 8; ++e) xv[u][e] = ww[u][e] = bb[u][e] = 0.f;
       if (row_ok && ks < steps) {
@@ -347,21 +347,21 @@ __global__ __launch_bounds__(64 * NW) void skinny16_gemm_kernel(GemmArgs a, Skin
           load4(ln.b + 32 * ks + 8 * kq, bb[u]);
           load4(ln.b + 32 * ks + 8 * kq + 4, bb[u] + 4);
         }
-        bf16x8 af;
+        h16x8 af;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) af[e] = (bf16)((xv[u][e] - mean) * rs * ww[u][e] + bb[u][e]);
+        for (int e = 0; e < 8; ++e) af[e] = (h16)((xv[u][e] - mean) * rs * ww[u][e] + bb[u][e]);
         acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bfr[u], acc, 0, 0, 0);
       }
     }
   }
-  const bf16* ar = A + (int64_t)(row_ok ? col : 0) * a.lda + 8 * kq;
+  const h16* ar = A + (int64_t)(row_ok ? col : 0) * a.lda + 8 * kq;
   for (int ks0 = wave; !LNA && ks0 < steps; ks0 += U * NW) {
-    bf16x8 af[U], bfr[U];
+    h16x8 af[U], bfr[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int ks = ks0 + NW * u;
-      af[u] = __builtin_bit_cast(bf16x8, ld16_or_zero(ar + 32 * ks, row_ok && ks < steps));
-      bfr[u] = __builtin_bit_cast(bf16x8, ld16_or_zero(br + 32 * ks, col_ok && ks < steps));
+      af[u] = __builtin_bit_cast(h16x8, ld16_or_zero(ar + 32 * ks, row_ok && ks < steps));
+      bfr[u] = __builtin_bit_cast(h16x8, ld16_or_zero(br + 32 * ks, col_ok && ks < steps));
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[u], bfr[u], acc, 0, 0, 0);
@@ -421,7 +421,7 @@ bool skinny_ln_launch(GemmEpilogue epi, const GemmArgs& a, const SkinnyKv& kv, c
 }
 
 bool gemm_skinny_ln(GemmEpilogue epi, const GemmArgs& a, const float* x, const float* w, const float* b,
-                    hipStream_t s, bf16* cache, int Tmax, int pos, int C) {
+                    hipStream_t s, h16* cache, int Tmax, int pos, int C) {
   if (a.M < 1 || a.M > 16 || a.N < 1 || a.K < 32 || a.K % 32 || a.lda % 4 || a.ldb % 8 || !x || !w || !b)
     return false;
   if (cache && (epi != EPI_ACT || a.N != 3 * C || pos < 0 || pos >= Tmax)) return false;
@@ -433,7 +433,7 @@ bool gemm_skinny_ln(GemmEpilogue epi, const GemmArgs& a, const float* x, const f
   return false;
 }
 
-bool gemm_skinny(GemmEpilogue epi, const GemmArgs& a, hipStream_t s, bf16* cache, int Tmax, int pos, int C) {
+bool gemm_skinny(GemmEpilogue epi, const GemmArgs& a, hipStream_t s, h16* cache, int Tmax, int pos, int C) {
   if (a.M < 1 || a.M > 32 || a.N < 1 || a.K < 16 || a.K % 16 || a.lda % 8 || a.ldb % 8) return false;
   if (cache && (epi != EPI_ACT || a.N != 3 * C || pos < 0 || pos >= Tmax)) return false;
   const SkinnyKv kv{cache, Tmax, pos, C};
@@ -926,10 +926,10 @@ bool sample(const float* logits, int64_t ld, int B, int V, float temperature, in
 }
 
 template void kv_store<float>(const float*, float*, int, int, int, int, int, hipStream_t);
-template void kv_store<bf16>(const bf16*, bf16*, int, int, int, int, int, hipStream_t);
+template void kv_store<h16>(const h16*, h16*, int, int, int, int, int, hipStream_t);
 template void last_rows<float>(const float*, float*, int, int, int, hipStream_t);
-template void last_rows<bf16>(const bf16*, bf16*, int, int, int, hipStream_t);
+template void last_rows<h16>(const h16*, h16*, int, int, int, hipStream_t);
 template bool decode_attn<float>(const float*, const float*, float*, int, int, int, int, int, hipStream_t);
-template bool decode_attn<bf16>(const bf16*, const bf16*, bf16*, int, int, int, int, int, hipStream_t);
+template bool decode_attn<h16>(const h16*, const h16*, h16*, int, int, int, int, int, hipStream_t);
 
 }  // namespace gpt2k

@@ -18,7 +18,7 @@ using namespace gpt2k;
 
 struct gpt2_infer {
   gpt2_config cfg;
-  bool bf16;
+  bool ops16;  // 16-bit MFMA operands and activations (bf16; decoding has no fp16 mode)
   int L, C, NH, V, Vp, Bmax, Tmax;
   int64_t act;
   const float* params;
@@ -38,7 +38,7 @@ struct gpt2_infer {
   const float* P(const char* n, int l = 0) const { return params + off.at(n) + (int64_t)l * per.at(n); }
   const void* W(const char* n, int l = 0) const {
     const int64_t o = off.at(n) + (int64_t)l * per.at(n);
-    return bf16 ? (const void*)(pbf16 + 2 * o) : (const void*)(params + o);
+    return ops16 ? (const void*)(pbf16 + 2 * o) : (const void*)(params + o);
   }
   char* cache_l(int l) const { return cache + (int64_t)l * Bmax * Tmax * 2 * C * act; }
 };
@@ -99,8 +99,8 @@ int hip_ok() {
 // A product of the forward pass: the skinny kernel for the few rows of a
 // decoding step in bf16 mode, else the step's GEMM.
 bool product(gpt2_infer* c, GemmEpilogue epi, const GemmArgs& g, hipStream_t s) {
-  if (c->bf16 && g.M <= 32 && gemm_skinny(epi, g, s)) return true;
-  return gemm(LAYOUT_NT, epi, c->bf16, g, s);
+  if (c->ops16 && g.M <= 32 && gemm_skinny(epi, g, s)) return true;
+  return gemm(LAYOUT_NT, epi, c->ops16, g, s);
 }
 
 // The blocks, final LayerNorm and lm_head over M = B T rows (prefill, T > 1
@@ -109,7 +109,7 @@ template <typename TA>
 int forward(gpt2_infer* c, int B, int T, bool decode, float* d_logits) {
   hipStream_t s = c->stream;
   const int C = c->C, M = B * T;
-  const bool bf = c->bf16;
+  const bool bf = c->ops16;
   float* xa = c->x0;
   float* xb = c->x1;
   TA* ln = (TA*)c->ln;
@@ -124,11 +124,11 @@ int forward(gpt2_infer* c, int B, int T, bool decode, float* d_logits) {
     TA* cache = (TA*)c->cache_l(l);
     // a bf16 decoding step stores the new keys and values from the QKV
     // product's epilogue
-    bool kv_fused = ln_pro && gemm_skinny_ln(EPI_ACT, g, xa, c->P("ln1_w", l), c->P("ln1_b", l), s, (bf16*)cache,
+    bool kv_fused = ln_pro && gemm_skinny_ln(EPI_ACT, g, xa, c->P("ln1_w", l), c->P("ln1_b", l), s, (h16*)cache,
                                              c->Tmax, c->len, C);
     if (!kv_fused) {
       layernorm_fwd<TA>(xa, c->P("ln1_w", l), c->P("ln1_b", l), ln, c->mean, c->rstd, M, C, s);
-      kv_fused = decode && bf && M <= 32 && gemm_skinny(EPI_ACT, g, s, (bf16*)cache, c->Tmax, c->len, C);
+      kv_fused = decode && bf && M <= 32 && gemm_skinny(EPI_ACT, g, s, (h16*)cache, c->Tmax, c->len, C);
       if (!kv_fused && !product(c, EPI_ACT, g, s)) return GPT2_ERR_ARG;
     }
     if (decode) {
@@ -181,8 +181,8 @@ int gpt2_infer_init(const gpt2_config* cfg, const float* d_params, const void* d
   if (cfg->n_embd / cfg->n_head > 256) return GPT2_ERR_ARG;
   gpt2_infer probe;
   probe.cfg = *cfg;
-  probe.bf16 = cfg->precision == GPT2_BF16;
-  probe.act = probe.bf16 ? 2 : 4;
+  probe.ops16 = cfg->precision == GPT2_BF16;
+  probe.act = probe.ops16 ? 2 : 4;
   probe.L = cfg->n_layer;
   probe.C = cfg->n_embd;
   probe.NH = cfg->n_head;
@@ -197,7 +197,7 @@ int gpt2_infer_init(const gpt2_config* cfg, const float* d_params, const void* d
     sizes->workspace_bytes = ws;
   }
   if (!d_cache) return GPT2_OK;
-  if (!out || !d_params || !d_workspace || (probe.bf16 && !d_params_bf16)) return GPT2_ERR_ARG;
+  if (!out || !d_params || !d_workspace || (probe.ops16 && !d_params_bf16)) return GPT2_ERR_ARG;
   gpt2_infer* c = new gpt2_infer(probe);
   c->params = d_params;
   c->pbf16 = (const char*)d_params_bf16;
@@ -231,7 +231,7 @@ int gpt2_infer_prefill(gpt2_infer* c, const int32_t* d_idx, int B, int T, float*
   if (B < 1 || B > c->Bmax || T < 1) return GPT2_ERR_BATCH;
   embed_fwd(d_idx, c->P("wte"), c->P("wpe"), c->x0, c->ids, B * T, T, c->C, c->V, c->err, c->stream);
   c->len = 0;
-  const int e = c->bf16 ? forward<bf16>(c, B, T, false, d_logits) : forward<float>(c, B, T, false, d_logits);
+  const int e = c->ops16 ? forward<h16>(c, B, T, false, d_logits) : forward<float>(c, B, T, false, d_logits);
   if (e != GPT2_OK) {
     c->len = -1;
     return e;
@@ -249,7 +249,7 @@ int gpt2_infer_decode(gpt2_infer* c, const int32_t* d_tokens, float* d_logits) {
   // one position: wpe row len for every sequence
   embed_fwd(d_tokens, c->P("wte"), c->P("wpe") + (int64_t)c->len * c->C, c->x0, c->ids, B, 1, c->C, c->V, c->err,
             c->stream);
-  const int e = c->bf16 ? forward<bf16>(c, B, 1, true, d_logits) : forward<float>(c, B, 1, true, d_logits);
+  const int e = c->ops16 ? forward<h16>(c, B, 1, true, d_logits) : forward<float>(c, B, 1, true, d_logits);
   if (e != GPT2_OK) return e;
   c->len += 1;
   return GPT2_OK;

@@ -27,7 +27,7 @@ bool decode_attn(const TA* qkv, const TA* cache, TA* y, int B, int n_keys, int T
 // rows.  With a cache (EPI_ACT, N = 3C: the QKV product of a decoding step)
 // the key and value columns of output row m also go to row (m, pos) of that
 // (B, Tmax, 2C) cache.
-bool gemm_skinny(GemmEpilogue epi, const GemmArgs& a, hipStream_t s, bf16* cache = nullptr, int Tmax = 0,
+bool gemm_skinny(GemmEpilogue epi, const GemmArgs& a, hipStream_t s, h16* cache = nullptr, int Tmax = 0,
                  int pos = 0, int C = 0);
 // The same product for M <= 16 rows with A = LayerNorm(x): x fp32 (M x K, row
 // stride a.lda), gain w and shift b (K); each row normalised as
@@ -35,7 +35,7 @@ bool gemm_skinny(GemmEpilogue epi, const GemmArgs& a, hipStream_t s, bf16* cache
 // Epilogues EPI_ACT (with the cache as above), EPI_F32 and EPI_GELU.  Returns
 // false (nothing launched) for shapes it does not take (M > 16, K % 32, K > 2048).
 bool gemm_skinny_ln(GemmEpilogue epi, const GemmArgs& a, const float* x, const float* w, const float* b,
-                    hipStream_t s, bf16* cache = nullptr, int Tmax = 0, int pos = 0, int C = 0);
+                    hipStream_t s, h16* cache = nullptr, int Tmax = 0, int pos = 0, int C = 0);
 // out[b] = a column of logits row b (fp32, row stride ld) among [0, V):
 // temperature <= 0 or top_k == 1: the first largest; else z = logits / T,
 // columns below the k-th largest z dropped (top_k > 0), p = softmax(z),

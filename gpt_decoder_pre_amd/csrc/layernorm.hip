@@ -19,11 +19,11 @@ DEVI void store8(float* p, const float o[8]) {
   store4(p, o);
   store4(p + 4, o + 4);
 }
-DEVI void store8(bf16* p, const float o[8]) {
-  bf16x8 t;
+DEVI void store8(h16* p, const float o[8]) {
+  h16x8 t;
 #pragma unroll
-  for (int e = 0; e < 8; ++e) t[e] = (bf16)o[e];
-  *reinterpret_cast<bf16x8*>(p) = t;
+  for (int e = 0; e < 8; ++e) t[e] = (h16)o[e];
+  *reinterpret_cast<h16x8*>(p) = t;
 }
 
 // Each wavefront normalises R rows together (their loads in flight at once,
@@ -132,7 +132,7 @@ void layernorm_fwd(const float* x, const float* w, const float* b, TA* y, float*
 }
 template void layernorm_fwd<float>(const float*, const float*, const float*, float*, float*, float*, int, int,
                                    hipStream_t);
-template void layernorm_fwd<bf16>(const float*, const float*, const float*, bf16*, float*, float*, int, int,
+template void layernorm_fwd<h16>(const float*, const float*, const float*, h16*, float*, float*, int, int,
                                   hipStream_t);
 
 // dx = rstd (dxhat - mean(dxhat) - xhat mean(dxhat xhat)), dxhat = dy w.
@@ -288,8 +288,8 @@ int layernorm_bwd(const TA* dy, const float* x, const float* mean, const float* 
 }
 template int layernorm_bwd<float>(const float*, const float*, const float*, const float*, const float*, float*,
                                   bool, float*, float*, int, int, hipStream_t);
-template int layernorm_bwd<bf16>(const bf16*, const float*, const float*, const float*, const float*, float*,
-                                 bool, bf16*, float*, int, int, hipStream_t);
+template int layernorm_bwd<h16>(const h16*, const float*, const float*, const float*, const float*, float*,
+                                 bool, h16*, float*, int, int, hipStream_t);
 
 // Many column-partial reductions in one launch: block b belongs to the job j
 // with jobs.first[j] <= b < jobs.first[j + 1] and reduces 256 of that job's
@@ -386,6 +386,6 @@ int colsum_partials(const TA* x, int M, int N, float* part, hipStream_t s) {
   return chunks;
 }
 template int colsum_partials<float>(const float*, int, int, float*, hipStream_t);
-template int colsum_partials<bf16>(const bf16*, int, int, float*, hipStream_t);
+template int colsum_partials<h16>(const h16*, int, int, float*, hipStream_t);
 
 }  // namespace gpt2k

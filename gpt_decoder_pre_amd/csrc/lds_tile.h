@@ -89,23 +89,23 @@ DEVI void wait_vmcnt() {
 
 // Fragment (eight consecutive k of one row, rows = lane % 32) for the 16-k step kk.
 template <bool KMAJ, int R, int BK>
-DEVI bf16x8 frag(const bf16* tile, int row0, int kk, int lane) {
+DEVI h16x8 frag(const h16* tile, int row0, int kk, int lane) {
   if constexpr (KMAJ) {
     const int r = row0 + (lane & 31);
     const int c = 2 * kk + (lane >> 5);
-    return *reinterpret_cast<const bf16x8*>(tile + r * BK + 8 * (c ^ kswz<BK>(r)));
+    return *reinterpret_cast<const h16x8*>(tile + r * BK + 8 * (c ^ kswz<BK>(r)));
   } else {
     const int g = lane >> 4, s = lane & 15;
     const int k = 16 * kk + 8 * (g >> 1) + (s >> 2);
     const int m = row0 + 16 * (g & 1) + 4 * (s & 3);
     const int c = m >> 3, o = m & 7;
-    const bf16* p1 = tile + k * R + 8 * (c ^ tswz<R>(k)) + o;
-    const bf16* p2 = tile + (k + 4) * R + 8 * (c ^ tswz<R>(k + 4)) + o;
+    const h16* p1 = tile + k * R + 8 * (c ^ tswz<R>(k)) + o;
+    const h16* p2 = tile + (k + 4) * R + 8 * (c ^ tswz<R>(k + 4)) + o;
     const i16x4g a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4g*)p1);
     const i16x4g b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4g*)p2);
     const u32x2 ua = __builtin_bit_cast(u32x2, a), ub = __builtin_bit_cast(u32x2, b);
     u32x4 v = {ua[0], ua[1], ub[0], ub[1]};
-    return __builtin_bit_cast(bf16x8, v);
+    return __builtin_bit_cast(h16x8, v);
   }
 }
 

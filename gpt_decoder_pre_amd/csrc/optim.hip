@@ -24,20 +24,20 @@ void fill_f32(float* p, int64_t n, float v, hipStream_t s) {
   fill_kernel<<<(unsigned)((work + 255) / 256), 256, 0, s>>>(p, n, v);
 }
 
-__global__ void to_bf16_kernel(const float* __restrict__ src, bf16* __restrict__ dst, int64_t n) {
+__global__ void to_bf16_kernel(const float* __restrict__ src, h16* __restrict__ dst, int64_t n) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (4 * i + 3 < n) {
     float v[4];
     load4(src + 4 * i, v);
     store4(dst + 4 * i, v);
   } else {
-    for (int64_t j = 4 * i; j < n; ++j) dst[j] = (bf16)src[j];
+    for (int64_t j = 4 * i; j < n; ++j) dst[j] = (h16)src[j];
   }
 }
 
 void to_bf16(const float* src, void* dst, int64_t n, hipStream_t s) {
   const int64_t work = (n + 3) / 4;
-  to_bf16_kernel<<<(unsigned)((work + 255) / 256), 256, 0, s>>>(src, reinterpret_cast<bf16*>(dst), n);
+  to_bf16_kernel<<<(unsigned)((work + 255) / 256), 256, 0, s>>>(src, reinterpret_cast<h16*>(dst), n);
 }
 
 constexpr int kNormBlocks = 1024;
@@ -103,7 +103,7 @@ void clip_finalize(const double* part, int nblk, float max_norm, float* d_norm, 
 template <bool BF16>
 __global__ __launch_bounds__(256) void adamw_kernel(float* __restrict__ p, const float* __restrict__ g,
                                                     float* __restrict__ m, float* __restrict__ v,
-                                                    bf16* __restrict__ pb, int64_t n4, DecaySegments seg,
+                                                    h16* __restrict__ pb, int64_t n4, DecaySegments seg,
                                                     const float* __restrict__ grad_scale, float lr, float beta1,
                                                     float beta2, float eps, float wd, float inv_bc1,
                                                     float inv_bc2) {
@@ -140,7 +140,7 @@ void adamw(float* p, const float* g, float* m, float* v, void* p_bf16, int64_t n
   const int64_t n4 = n / 4;
   const unsigned grid = (unsigned)((n4 + 255) / 256);
   if (p_bf16)
-    adamw_kernel<true><<<grid, 256, 0, s>>>(p, g, m, v, reinterpret_cast<bf16*>(p_bf16), n4, seg, grad_scale, lr,
+    adamw_kernel<true><<<grid, 256, 0, s>>>(p, g, m, v, reinterpret_cast<h16*>(p_bf16), n4, seg, grad_scale, lr,
                                             beta1, beta2, eps, wd, inv_bc1, inv_bc2);
   else
     adamw_kernel<false><<<grid, 256, 0, s>>>(p, g, m, v, nullptr, n4, seg, grad_scale, lr, beta1, beta2, eps, wd,

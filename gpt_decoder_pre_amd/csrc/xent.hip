@@ -78,14 +78,14 @@ __global__ __launch_bounds__(256) void xent_kernel(TA* __restrict__ logits, cons
 // The register budget (64 VGPRs) keeps two rows resident per CU, so one row's
 // loads overlap the other's arithmetic and stores.
 template <int NCH, int NT>
-__global__ __launch_bounds__(NT, 8 * NT / 1024) void xent_bf16_resident_kernel(bf16* __restrict__ logits,
+__global__ __launch_bounds__(NT, 8 * NT / 1024) void xent_bf16_resident_kernel(h16* __restrict__ logits,
                                                                  const int32_t* __restrict__ targets,
                                                                  float* __restrict__ row_loss, int V, int vocab,
                                                                  float grad_scale, int* __restrict__ err) {
   __shared__ float red[16];
   __shared__ float red2[16];
   const int row = blockIdx.x;
-  bf16* z = logits + (int64_t)row * V;
+  h16* z = logits + (int64_t)row * V;
   int y = targets[row];
   if (y < 0 || y >= vocab) {
     if (threadIdx.x == 0) *err = 1;
@@ -103,7 +103,7 @@ __global__ __launch_bounds__(NT, 8 * NT / 1024) void xent_bf16_resident_kernel(b
   for (int i = 0; i < NCH; ++i) {
     const int c = threadIdx.x + i * NT;
     if (c < nchunk) {
-      const bf16x8 v = __builtin_bit_cast(bf16x8, r[i]);
+      const h16x8 v = __builtin_bit_cast(h16x8, r[i]);
 #pragma unroll
       for (int e = 0; e < 8; ++e) m = fmaxf(m, (float)v[e]);
     }
@@ -114,7 +114,7 @@ __global__ __launch_bounds__(NT, 8 * NT / 1024) void xent_bf16_resident_kernel(b
   for (int i = 0; i < NCH; ++i) {
     const int c = threadIdx.x + i * NT;
     if (c < nchunk) {
-      const bf16x8 v = __builtin_bit_cast(bf16x8, r[i]);
+      const h16x8 v = __builtin_bit_cast(h16x8, r[i]);
 #pragma unroll
       for (int e = 0; e < 8; ++e) s += exp2_fast(((float)v[e] - M) * kLog2e);
     }
@@ -126,7 +126,7 @@ __global__ __launch_bounds__(NT, 8 * NT / 1024) void xent_bf16_resident_kernel(b
 #pragma unroll
     for (int i = 0; i < NCH; ++i) {
       if (i == (y / 8) / NT) {
-        const bf16x8 v = __builtin_bit_cast(bf16x8, r[i]);
+        const h16x8 v = __builtin_bit_cast(h16x8, r[i]);
 #pragma unroll
         for (int e = 0; e < 8; ++e)
           if (e == y % 8) zy = (float)v[e];
@@ -139,14 +139,14 @@ __global__ __launch_bounds__(NT, 8 * NT / 1024) void xent_bf16_resident_kernel(b
   for (int i = 0; i < NCH; ++i) {
     const int c = threadIdx.x + i * NT;
     if (c < nchunk) {
-      const bf16x8 v = __builtin_bit_cast(bf16x8, r[i]);
-      bf16x8 o;
+      const h16x8 v = __builtin_bit_cast(h16x8, r[i]);
+      h16x8 o;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const float p = exp2_fast((float)v[e] * kLog2e - l2);
-        o[e] = (bf16)((p - (8 * c + e == y ? 1.f : 0.f)) * grad_scale);
+        o[e] = (h16)((p - (8 * c + e == y ? 1.f : 0.f)) * grad_scale);
       }
-      *reinterpret_cast<bf16x8*>(z + 8 * c) = o;
+      *reinterpret_cast<h16x8*>(z + 8 * c) = o;
     }
   }
 }
@@ -173,7 +173,7 @@ void xent_fwd_bwd(TA* logits, const int32_t* targets, float* row_loss, int M, in
   else xent_kernel<TA, 1><<<M, 256, 0, s>>>(logits, targets, row_loss, V, vocab, grad_scale, err);
 }
 template void xent_fwd_bwd<float>(float*, const int32_t*, float*, int, int, int, float, int*, hipStream_t);
-template void xent_fwd_bwd<bf16>(bf16*, const int32_t*, float*, int, int, int, float, int*, hipStream_t);
+template void xent_fwd_bwd<h16>(h16*, const int32_t*, float*, int, int, int, float, int*, hipStream_t);
 
 __global__ __launch_bounds__(1024) void loss_reduce_kernel(const float* __restrict__ row_loss, int M, float scale,
                                                            int accumulate, float* out) {
