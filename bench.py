@@ -15,6 +15,7 @@ region), and the fp64 oracle timed on the host cores as a CPU baseline.
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import json
 import os
 import sys
@@ -39,6 +40,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", default="gpt2-124m")
+    ap.add_argument("--precision", default=None, choices=["fp32", "bf16", "fp16"],
+                    help="override the config's precision (fp16: IEEE half operands with dynamic loss scaling)")
     ap.add_argument("--site", default=None, help="launch site timed for the roofline (default: the one that "
                     "takes the most time per step in a per-site record of one untimed step)")
     ap.add_argument("--cpu-toy", action="store_true", help="also time the oracle on the toy step")
@@ -219,6 +222,8 @@ def main():
     from gpt_decoder_pre_amd.lib import GPT2Step
 
     run = RUNS[args.config]
+    if args.precision:
+        run = dataclasses.replace(run, precision=args.precision)
     s = run.shape
     B, T, k = run.micro_batch, run.seq_len, run.grad_accum
     dev = torch.device("cuda:0")
@@ -308,13 +313,15 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if run.precision == "bf16" else "f32",
+        "dtype": {"bf16": "bf16", "fp16": "f16"}.get(run.precision, "f32"),
         "data": "synthetic",
         "config": {"workload": f"{s.name} pre-training step: {s.n_layer} layers, {s.n_head} heads, "
                                f"{s.n_embd} dims, vocab {s.padded_vocab_size} "
                                f"({'tied' if s.tied else 'untied head, no QKV bias'}), Zipf(1.1) token ids",
                    "micro_batch": B, "grad_accum": k, "seq_len": T, "tokens_per_step": k * B * T,
-                   "precision": "bf16 compute, fp32 master weights and AdamW moments"},
+                   "precision": {"bf16": "bf16 compute, fp32 master weights and AdamW moments",
+                                 "fp16": "fp16 compute with dynamic loss scaling, fp32 master weights and AdamW "
+                                         "moments"}.get(run.precision, "fp32")},
         "mfu_pct": round(100 * mfu, 2),
         "mfu_pct_6n_12lct": round(100 * mfu_palm, 2),
         "flops_per_token": f_alg,

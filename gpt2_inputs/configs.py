@@ -42,7 +42,7 @@ class RunConfig:
     micro_batch: int
     grad_accum: int
     seq_len: int
-    precision: str            # "fp32" or "bf16"
+    precision: str            # "fp32", "bf16" or "fp16"
     tokens: str               # "uniform" or "zipf"
     lr: float
     weight_decay: float = 0.1

@@ -23,6 +23,12 @@ LIB_PATH = os.path.join(LIB_DIR, "libgpt2.so")
 ARCH = "gfx950"
 SOURCES = ["gemm.hip", "attention.hip", "layernorm.hip", "embed.hip", "xent.hip", "optim.hip", "infer.hip",
            "gpt2.cpp", "train.cpp", "infer_ctx.cpp"]
+# The sources of the training step are built a second time for the fp16 mode:
+# IEEE half as the 16-bit operand type, in namespace gpt2k_f16, with the C ABI
+# entry points prefixed f16_ (the library's own entry points hand fp16
+# contexts to them).
+F16_SOURCES = ["gemm.hip", "attention.hip", "layernorm.hip", "embed.hip", "xent.hip", "optim.hip", "gpt2.cpp"]
+F16_FLAGS = ["-DGPT2_OPS_F16", "-Dgpt2k=gpt2k_f16"]
 CXXFLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
     # no packed-fp32 instructions in device code
@@ -39,9 +45,10 @@ def _hipcc() -> str:
     raise RuntimeError("hipcc not found: the HIP toolchain is required to build libgpt2.so")
 
 
-def _compile(src: str, hipcc: str) -> str:
-    obj = os.path.join(BUILD_DIR, src.replace(".", "_") + ".o")
-    cmd = [hipcc, *CXXFLAGS, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+def _compile(job: tuple, hipcc: str) -> str:
+    src, f16 = job
+    obj = os.path.join(BUILD_DIR, src.replace(".", "_") + ("_f16" if f16 else "") + ".o")
+    cmd = [hipcc, *CXXFLAGS, *(F16_FLAGS if f16 else []), "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed on {src}:\n{r.stderr}")
@@ -53,8 +60,11 @@ def build(verbose: bool = False) -> str:
     hipcc = _hipcc()
     os.makedirs(BUILD_DIR, exist_ok=True)
     os.makedirs(LIB_DIR, exist_ok=True)
-    with ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
-        objs = list(ex.map(lambda s: _compile(s, hipcc), SOURCES))
+    # the two GEMM builds take longest: start them first
+    jobs = [("gemm.hip", False), ("gemm.hip", True)] + [(s, False) for s in SOURCES if s != "gemm.hip"] + \
+        [(s, True) for s in F16_SOURCES if s != "gemm.hip"]
+    with ThreadPoolExecutor(max_workers=8) as ex:
+        objs = list(ex.map(lambda j: _compile(j, hipcc), jobs))
     tmp = LIB_PATH + ".tmp"
     cmd = [hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)

@@ -17,6 +17,31 @@
 #include "gpt2_train.h"
 #include "kernels.h"
 
+// This file is compiled twice: as the library's C ABI (16-bit operands in
+// bfloat16), and with GPT2_OPS_F16 against the kernels built for IEEE half
+// (namespace gpt2k_f16), where every entry point takes an f16_ prefix.  The
+// ABI entry points hand contexts and configs of the fp16 mode to those.
+#ifdef GPT2_OPS_F16
+#define GPT2_NAME(name) f16_##name
+#define GPT2_API(name) __attribute__((visibility("hidden"))) GPT2_NAME(name)
+#define GPT2_TO_F16(cond, call)
+#else
+#define GPT2_NAME(name) name
+#define GPT2_API(name) name
+#define GPT2_TO_F16(cond, call) \
+  if (cond) return call
+extern "C" {
+int f16_gpt2_init(const gpt2_config*, const gpt2_buffers*, void*, gpt2_sizes*, gpt2_ctx**);
+int f16_gpt2_forward_loss(gpt2_ctx*, const int32_t*, const int32_t*, int, int, float, float*);
+int f16_gpt2_backward(gpt2_ctx*);
+int f16_gpt2_accumulate(gpt2_ctx*, const int32_t*, const int32_t*, int, int, int, float*);
+int f16_gpt2_clip_adamw_step(gpt2_ctx*, float, float, float, float, float, float, float*, int32_t*);
+int f16_gpt2_sync_params(gpt2_ctx*);
+int f16_gpt2_checkpoint_load(gpt2_ctx*, const char*, int64_t*, int*);
+int f16_gpt2_embedding_backward(gpt2_ctx*, const int32_t*, const float*, int, int);
+}
+#endif
+
 using namespace gpt2k;
 
 namespace {
@@ -48,9 +73,9 @@ bool config_ok(const gpt2_config& c) {
   if (c.n_layer < 1 || c.n_head < 1 || c.n_embd < 8 || c.block_size < 1 || c.vocab_size < 1) return false;
   if (c.n_embd % c.n_head || c.n_embd % 8 || c.n_embd > 2048) return false;
   if (c.padded_vocab_size < c.vocab_size || c.max_batch < 1) return false;
-  if (c.precision != GPT2_FP32 && c.precision != GPT2_BF16) return false;
+  if (c.precision != GPT2_FP32 && c.precision != GPT2_BF16 && c.precision != GPT2_FP16) return false;
   if (c.variant & ~(GPT2_UNTIED_HEAD | GPT2_NO_QKV_BIAS)) return false;
-  if (c.precision == GPT2_BF16 && (c.n_embd / c.n_head != 64 || c.padded_vocab_size % 8)) return false;
+  if (c.precision != GPT2_FP32 && (c.n_embd / c.n_head != 64 || c.padded_vocab_size % 8)) return false;
   if (c.precision == GPT2_FP32 && c.n_embd / c.n_head > 256) return false;
   if ((int64_t)c.max_batch * c.block_size > (1 << 26)) return false;
   return true;
@@ -109,6 +134,7 @@ struct gpt2_ctx {
   TensorDesc t[T_COUNT];
   int64_t n_params;
   bool ops16;  // 16-bit MFMA operands (bf16, or fp16 in the fp16 build)
+  bool f16;    // fp16 mode: this context runs on the f16_ build
   int64_t act;  // bytes per activation element
   int64_t Mmax;
   int L, C, NH, Vp, V;
@@ -150,6 +176,17 @@ struct gpt2_ctx {
   double* norm_part;
   float* clip_scale;
   int* err_flag;
+  int32_t* amp_found;  // fp16 mode: 1 when the last step found a non-finite gradient
+
+  // Dynamic loss scaling (fp16 mode): the loss gradient is formed times
+  // amp_scale, so the gradients accumulate scaled; the clip + AdamW step
+  // unscales them, and skips the update (parameters, moments and step count
+  // unchanged) when one is not finite.  Then the scale is multiplied by
+  // amp_backoff after a skipped step and by amp_growth after amp_interval
+  // consecutive good ones.
+  bool amp = false;
+  float amp_scale = 65536.f, amp_growth = 2.f, amp_backoff = 0.5f;
+  int amp_interval = 2000, amp_good = 0, amp_skipped = 0;
 
   // state
   bool have_fwd = false;
@@ -382,7 +419,8 @@ int forward_impl(gpt2_ctx* c, const int32_t* d_idx, const int32_t* d_tgt, int B,
     return GPT2_ERR_ARG;
   {
     Timed tm(c, "xent", 0, 2.0 * a * M * Vp + 8.0 * M);
-    xent_fwd_bwd<TA>((TA*)c->logits, d_tgt, c->row_loss, M, Vp, c->V, loss_scale / (float)M, c->err_flag, s);
+    const float seed = c->amp ? loss_scale * c->amp_scale : loss_scale;  // gradient of the (scaled) loss
+    xent_fwd_bwd<TA>((TA*)c->logits, d_tgt, c->row_loss, M, Vp, c->V, seed / (float)M, c->err_flag, s);
   }
   loss_reduce(c->row_loss, M, loss_scale / (float)M, accumulate, d_loss, s);
   c->have_fwd = true;
@@ -603,6 +641,7 @@ int64_t plan_workspace(gpt2_ctx* c, Plan& p, bool assign) {
   c->norm_part = (double*)at(1024 * 8);
   c->clip_scale = (float*)at(256);
   c->err_flag = (int*)at(256);
+  c->amp_found = (int32_t*)at(256);
   return p.bytes;
 }
 
@@ -610,7 +649,9 @@ void fill_layout(gpt2_ctx* c, const gpt2_config& cfg) {
   c->cfg = cfg;
   tensor_table(cfg, c->t);
   c->n_params = total_params(c->t);
-  c->ops16 = cfg.precision == GPT2_BF16;
+  c->ops16 = cfg.precision != GPT2_FP32;
+  c->f16 = cfg.precision == GPT2_FP16;
+  c->amp = c->f16;
   c->act = c->ops16 ? 2 : 4;
   c->Mmax = (int64_t)cfg.max_batch * cfg.block_size;
   c->L = cfg.n_layer;
@@ -629,9 +670,10 @@ void fill_layout(gpt2_ctx* c, const gpt2_config& cfg) {
 
 extern "C" {
 
-int gpt2_init(const gpt2_config* cfg, const gpt2_buffers* bufs, void* hip_stream, gpt2_sizes* sizes,
-              gpt2_ctx** out) {
+int GPT2_API(gpt2_init)(const gpt2_config* cfg, const gpt2_buffers* bufs, void* hip_stream, gpt2_sizes* sizes,
+                        gpt2_ctx** out) {
   if (!cfg || !config_ok(*cfg)) return GPT2_ERR_ARG;
+  GPT2_TO_F16(cfg->precision == GPT2_FP16, f16_gpt2_init(cfg, bufs, hip_stream, sizes, out));
   gpt2_ctx probe;
   fill_layout(&probe, *cfg);
   Plan plan;
@@ -667,24 +709,27 @@ int gpt2_init(const gpt2_config* cfg, const gpt2_buffers* bufs, void* hip_stream
   return GPT2_OK;
 }
 
-int gpt2_forward_loss(gpt2_ctx* c, const int32_t* d_idx, const int32_t* d_targets, int B, int T, float loss_scale,
-                      float* d_loss) {
+int GPT2_API(gpt2_forward_loss)(gpt2_ctx* c, const int32_t* d_idx, const int32_t* d_targets, int B, int T,
+                                float loss_scale, float* d_loss) {
   if (!c || !d_idx || !d_targets || !d_loss) return GPT2_ERR_ARG;
+  GPT2_TO_F16(c->f16, f16_gpt2_forward_loss(c, d_idx, d_targets, B, T, loss_scale, d_loss));
   const int e = check_bt(c, B, T);
   if (e != GPT2_OK) return e;
   return c->ops16 ? forward_impl<h16>(c, d_idx, d_targets, B, T, loss_scale, d_loss, false)
                  : forward_impl<float>(c, d_idx, d_targets, B, T, loss_scale, d_loss, false);
 }
 
-int gpt2_backward(gpt2_ctx* c) {
+int GPT2_API(gpt2_backward)(gpt2_ctx* c) {
   if (!c) return GPT2_ERR_ARG;
+  GPT2_TO_F16(c->f16, f16_gpt2_backward(c));
   if (!c->have_fwd) return GPT2_ERR_STATE;
   return c->ops16 ? backward_impl<h16>(c) : backward_impl<float>(c);
 }
 
-int gpt2_accumulate(gpt2_ctx* c, const int32_t* d_idx, const int32_t* d_targets, int k, int B, int T,
-                    float* d_mean_loss) {
+int GPT2_API(gpt2_accumulate)(gpt2_ctx* c, const int32_t* d_idx, const int32_t* d_targets, int k, int B, int T,
+                              float* d_mean_loss) {
   if (!c || !d_idx || !d_targets || !d_mean_loss) return GPT2_ERR_ARG;
+  GPT2_TO_F16(c->f16, f16_gpt2_accumulate(c, d_idx, d_targets, k, B, T, d_mean_loss));
   if (k < 1) return GPT2_ERR_BATCH;
   int e = check_bt(c, B, T);
   if (e != GPT2_OK) return e;
@@ -705,7 +750,7 @@ int gpt2_accumulate(gpt2_ctx* c, const int32_t* d_idx, const int32_t* d_targets,
                                       i > 0);
     if (e != GPT2_OK) return e;
     c->presorted = batched ? i % kSortBatch : -1;
-    e = gpt2_backward(c);
+    e = GPT2_NAME(gpt2_backward)(c);
     c->presorted = -1;
     if (e != GPT2_OK) return e;
   }
@@ -714,7 +759,7 @@ int gpt2_accumulate(gpt2_ctx* c, const int32_t* d_idx, const int32_t* d_targets,
 
 namespace {
 
-DecaySegments decay_segments(const TensorDesc t[T_COUNT], int64_t n_params) {
+static DecaySegments decay_segments(const TensorDesc t[T_COUNT], int64_t n_params) {
   DecaySegments seg;
   memset(&seg, 0, sizeof(seg));
   for (int i = 0; i < T_COUNT; ++i) {
@@ -731,35 +776,54 @@ DecaySegments decay_segments(const TensorDesc t[T_COUNT], int64_t n_params) {
 
 // Norm, clip decision and AdamW at step t on the flat vectors of bufs, with
 // the norm partials and the clip factor in (norm_part, clip_scale).
-void clip_adamw_launch(gpt2_ctx* c, const gpt2_buffers& b, int64_t n_params, const DecaySegments& seg, int64_t t,
-                       double* norm_part, float* clip_scale, float lr, float beta1, float beta2, float eps,
-                       float weight_decay, float max_norm, float* d_norm, int32_t* d_clipped, hipStream_t s) {
+static void clip_adamw_launch(gpt2_ctx* c, const gpt2_buffers& b, int64_t n_params, const DecaySegments& seg,
+                              int64_t t, double* norm_part, float* clip_scale, float lr, float beta1, float beta2,
+                              float eps, float weight_decay, float max_norm, float* d_norm, int32_t* d_clipped,
+                              hipStream_t s) {
   {
     Timed tm(c, "norm", 0, 4.0 * n_params);
     const int nblk = sumsq_partials(b.grads, n_params, norm_part, s);
-    clip_finalize(norm_part, nblk, max_norm, d_norm, d_clipped, clip_scale, s);
+    clip_finalize(norm_part, nblk, max_norm, d_norm, d_clipped, clip_scale, c->amp ? 1.0f / c->amp_scale : 1.0f,
+                  c->amp ? c->amp_found : nullptr, s);
   }
   const double bc1 = 1.0 - std::pow((double)beta1, (double)t);
   const double bc2 = 1.0 - std::pow((double)beta2, (double)t);
   {
     Timed tm(c, "adamw", 0, (b.params_bf16 ? 30.0 : 28.0) * n_params);
-    adamw(b.params, b.grads, b.adam_m, b.adam_v, b.params_bf16, n_params, seg, clip_scale, lr, beta1, beta2, eps,
-          weight_decay, (float)(1.0 / bc1), (float)(1.0 / bc2), s);
+    adamw(b.params, b.grads, b.adam_m, b.adam_v, b.params_bf16, n_params, seg, clip_scale,
+          c->amp ? c->amp_found : nullptr, lr, beta1, beta2, eps, weight_decay, (float)(1.0 / bc1),
+          (float)(1.0 / bc2), s);
   }
 }
 
 }  // namespace
 
-int gpt2_clip_adamw_step(gpt2_ctx* c, float lr, float beta1, float beta2, float eps, float weight_decay,
+int GPT2_API(gpt2_clip_adamw_step)(gpt2_ctx* c, float lr, float beta1, float beta2, float eps, float weight_decay,
                          float max_norm, float* d_norm, int32_t* d_clipped) {
   if (!c || !d_norm || !d_clipped) return GPT2_ERR_ARG;
+  GPT2_TO_F16(c->f16, f16_gpt2_clip_adamw_step(c, lr, beta1, beta2, eps, weight_decay, max_norm, d_norm, d_clipped));
   c->step += 1;
   clip_adamw_launch(c, c->buf, c->n_params, decay_segments(c->t, c->n_params), c->step, c->norm_part, c->clip_scale,
                     lr, beta1, beta2, eps, weight_decay, max_norm, d_norm, d_clipped, c->stream);
+  if (c->amp) {  // the scale update needs the device's verdict on this step
+    int32_t found = 0;
+    if (hipMemcpyAsync(&found, c->amp_found, sizeof(found), hipMemcpyDeviceToHost, c->stream) != hipSuccess ||
+        hipStreamSynchronize(c->stream) != hipSuccess)
+      return GPT2_ERR_HIP;
+    c->amp_skipped = found ? 1 : 0;
+    if (found) {
+      c->step -= 1;
+      c->amp_scale *= c->amp_backoff;
+      c->amp_good = 0;
+    } else if (++c->amp_good >= c->amp_interval) {
+      c->amp_scale *= c->amp_growth;
+      c->amp_good = 0;
+    }
+  }
   return hip_status();
 }
 
-int gpt2_clip_adamw_step_static(const gpt2_config* cfg, const gpt2_buffers* bufs, void* hip_stream, int64_t t,
+int GPT2_API(gpt2_clip_adamw_step_static)(const gpt2_config* cfg, const gpt2_buffers* bufs, void* hip_stream, int64_t t,
                                 float lr, float beta1, float beta2, float eps, float weight_decay, float max_norm,
                                 float* d_norm, int32_t* d_clipped) {
   if (!cfg || !config_ok(*cfg) || !bufs || !bufs->params || !bufs->grads || !bufs->adam_m || !bufs->adam_v ||
@@ -773,6 +837,7 @@ int gpt2_clip_adamw_step_static(const gpt2_config* cfg, const gpt2_buffers* bufs
             (long long)kStaticMaxParams);
     return GPT2_ERR_ARG;
   }
+  if (cfg->precision == GPT2_FP16) return GPT2_ERR_ARG;  // loss scaling needs the context's scaler
   gpt2_buffers b = *bufs;
   if (cfg->precision != GPT2_BF16) b.params_bf16 = nullptr;
   else if (!b.params_bf16) return GPT2_ERR_ARG;
@@ -786,13 +851,13 @@ int gpt2_clip_adamw_step_static(const gpt2_config* cfg, const gpt2_buffers* bufs
   return hip_status();
 }
 
-void gpt2_destroy(gpt2_ctx* c) {
+void GPT2_API(gpt2_destroy)(gpt2_ctx* c) {
   if (!c) return;
   for (hipEvent_t e : c->ev) (void)hipEventDestroy(e);
   delete c;
 }
 
-int gpt2_sync_status(gpt2_ctx* c) {
+int GPT2_API(gpt2_sync_status)(gpt2_ctx* c) {
   if (!c) return GPT2_ERR_ARG;
   if (hipStreamSynchronize(c->stream) != hipSuccess) return GPT2_ERR_HIP;
   int flag = 0;
@@ -805,21 +870,22 @@ int gpt2_sync_status(gpt2_ctx* c) {
   return hip_status();
 }
 
-int gpt2_sync_params(gpt2_ctx* c) {
+int GPT2_API(gpt2_sync_params)(gpt2_ctx* c) {
   if (!c) return GPT2_ERR_ARG;
+  GPT2_TO_F16(c->f16, f16_gpt2_sync_params(c));
   if (c->ops16) to_bf16(c->buf.params, c->buf.params_bf16, c->n_params, c->stream);
   return hip_status();
 }
 
-int64_t gpt2_get_step(const gpt2_ctx* c) { return c ? c->step : -1; }
+int64_t GPT2_API(gpt2_get_step)(const gpt2_ctx* c) { return c ? c->step : -1; }
 
-int gpt2_set_step(gpt2_ctx* c, int64_t t) {
+int GPT2_API(gpt2_set_step)(gpt2_ctx* c, int64_t t) {
   if (!c || t < 0) return GPT2_ERR_ARG;
   c->step = t;
   return GPT2_OK;
 }
 
-int gpt2_tensor_info(const gpt2_config* cfg, int index, const char** name, int64_t* offset, int64_t* numel,
+int GPT2_API(gpt2_tensor_info)(const gpt2_config* cfg, int index, const char** name, int64_t* offset, int64_t* numel,
                      int32_t* ndim, int64_t* dims) {
   if (!cfg || !config_ok(*cfg) || index < 0) return GPT2_ERR_ARG;
   TensorDesc t[T_COUNT];
@@ -840,10 +906,11 @@ int gpt2_tensor_info(const gpt2_config* cfg, int index, const char** name, int64
   return GPT2_OK;
 }
 
-int gpt2_activation(gpt2_ctx* c, const char* name, int layer, void** ptr, int64_t* numel, int32_t* dtype) {
+int GPT2_API(gpt2_activation)(gpt2_ctx* c, const char* name, int layer, void** ptr, int64_t* numel,
+                              int32_t* dtype) {
   if (!c || !name || !ptr || !numel || !dtype) return GPT2_ERR_ARG;
   const int64_t M = (int64_t)c->B * c->T, C = c->C;
-  const int32_t at = c->ops16 ? 1 : 0;
+  const int32_t at = c->f16 ? 3 : c->ops16 ? 1 : 0;
   const bool lay_ok = layer >= 0 && layer < c->L;
   auto ret = [&](void* p, int64_t n, int32_t d) {
     *ptr = p;
@@ -872,7 +939,7 @@ int gpt2_activation(gpt2_ctx* c, const char* name, int layer, void** ptr, int64_
   return GPT2_ERR_ARG;
 }
 
-int gpt2_timing_enable(gpt2_ctx* c, const char* site) {
+int GPT2_API(gpt2_timing_enable)(gpt2_ctx* c, const char* site) {
   if (!c) return GPT2_ERR_ARG;
   c->ev_used = 0;
   c->ev_overflow = false;
@@ -885,7 +952,7 @@ int gpt2_timing_enable(gpt2_ctx* c, const char* site) {
   return GPT2_OK;
 }
 
-int gpt2_timing_read(gpt2_ctx* c, double* total_ms, int64_t* launches, double* flops, double* bytes) {
+int GPT2_API(gpt2_timing_read)(gpt2_ctx* c, double* total_ms, int64_t* launches, double* flops, double* bytes) {
   if (!c || !total_ms || !launches || !flops || !bytes) return GPT2_ERR_ARG;
   if (hipStreamSynchronize(c->stream) != hipSuccess) return GPT2_ERR_HIP;
   double ms = 0, f = 0, b = 0;
@@ -911,23 +978,27 @@ constexpr char kCkptMagic[8] = {'G', 'P', 'T', '2', 'C', 'K', 'P', '1'};
 constexpr int kCkptExtraMax = 16;
 constexpr int64_t kCkptChunk = (int64_t)1 << 24;  // floats per staged copy
 
-bool same_model(const gpt2_config& a, const gpt2_config& b) {
+static bool same_model(const gpt2_config& a, const gpt2_config& b) {
   return a.n_layer == b.n_layer && a.n_head == b.n_head && a.n_embd == b.n_embd && a.block_size == b.block_size &&
          a.vocab_size == b.vocab_size && a.padded_vocab_size == b.padded_vocab_size && a.precision == b.precision &&
          a.variant == b.variant;
 }
 }  // namespace
 
-int gpt2_checkpoint_save(gpt2_ctx* c, const char* path, const int64_t* extra, int n_extra) {
+int GPT2_API(gpt2_checkpoint_save)(gpt2_ctx* c, const char* path, const int64_t* extra, int n_extra) {
   if (!c || !path || n_extra < 0 || n_extra > kCkptExtraMax || (n_extra > 0 && !extra)) return GPT2_ERR_ARG;
   if (hipStreamSynchronize(c->stream) != hipSuccess) return GPT2_ERR_HIP;
   const std::string tmp = std::string(path) + ".tmp";
   FILE* f = fopen(tmp.c_str(), "wb");
   if (!f) return GPT2_ERR_IO;
   const int64_t head[3] = {c->step, c->n_params, (int64_t)n_extra};
+  uint32_t scale_bits;
+  memcpy(&scale_bits, &c->amp_scale, 4);
+  const int64_t amp_words[2] = {(int64_t)scale_bits, (int64_t)c->amp_good};  // fp16 mode: the loss scaler
   bool ok = fwrite(kCkptMagic, 1, 8, f) == 8 && fwrite(&c->cfg, sizeof(gpt2_config), 1, f) == 1 &&
             fwrite(head, sizeof(int64_t), 3, f) == 3 &&
-            (n_extra == 0 || fwrite(extra, sizeof(int64_t), n_extra, f) == (size_t)n_extra);
+            (n_extra == 0 || fwrite(extra, sizeof(int64_t), n_extra, f) == (size_t)n_extra) &&
+            (!c->amp || fwrite(amp_words, sizeof(int64_t), 2, f) == 2);
   std::vector<float> stage((size_t)std::min<int64_t>(kCkptChunk, c->n_params));
   const float* src[3] = {c->buf.params, c->buf.adam_m, c->buf.adam_v};
   int err = GPT2_ERR_IO;
@@ -950,8 +1021,9 @@ int gpt2_checkpoint_save(gpt2_ctx* c, const char* path, const int64_t* extra, in
   return GPT2_OK;
 }
 
-int gpt2_checkpoint_load(gpt2_ctx* c, const char* path, int64_t* extra, int* n_extra) {
+int GPT2_API(gpt2_checkpoint_load)(gpt2_ctx* c, const char* path, int64_t* extra, int* n_extra) {
   if (!c || !path || !n_extra || *n_extra < 0 || (*n_extra > 0 && !extra)) return GPT2_ERR_ARG;
+  GPT2_TO_F16(c->f16, f16_gpt2_checkpoint_load(c, path, extra, n_extra));
   FILE* f = fopen(path, "rb");
   if (!f) return GPT2_ERR_IO;
   char magic[8];
@@ -966,8 +1038,9 @@ int gpt2_checkpoint_load(gpt2_ctx* c, const char* path, int64_t* extra, int* n_e
     fclose(f);
     return GPT2_ERR_ARG;
   }
-  int64_t ex[kCkptExtraMax];
-  if (head[2] > 0 && fread(ex, sizeof(int64_t), head[2], f) != (size_t)head[2]) {
+  int64_t ex[kCkptExtraMax], amp_words[2] = {0, 0};
+  if ((head[2] > 0 && fread(ex, sizeof(int64_t), head[2], f) != (size_t)head[2]) ||
+      (c->amp && fread(amp_words, sizeof(int64_t), 2, f) != 2)) {
     fclose(f);
     return GPT2_ERR_IO;
   }
@@ -992,6 +1065,11 @@ int gpt2_checkpoint_load(gpt2_ctx* c, const char* path, int64_t* extra, int* n_e
   }
   fclose(f);
   c->step = head[0];
+  if (c->amp) {
+    const uint32_t scale_bits = (uint32_t)amp_words[0];
+    memcpy(&c->amp_scale, &scale_bits, 4);
+    c->amp_good = (int)amp_words[1];
+  }
   const int nx = (int)std::min<int64_t>(head[2], *n_extra);
   for (int i = 0; i < nx; ++i) extra[i] = ex[i];
   *n_extra = nx;
@@ -999,8 +1077,9 @@ int gpt2_checkpoint_load(gpt2_ctx* c, const char* path, int64_t* extra, int* n_e
   return hip_status();
 }
 
-int gpt2_embedding_backward(gpt2_ctx* c, const int32_t* d_idx, const float* d_dx0, int B, int T) {
+int GPT2_API(gpt2_embedding_backward)(gpt2_ctx* c, const int32_t* d_idx, const float* d_dx0, int B, int T) {
   if (!c || !d_idx || !d_dx0) return GPT2_ERR_ARG;
+  GPT2_TO_F16(c->f16, f16_gpt2_embedding_backward(c, d_idx, d_dx0, B, T));
   if (T > c->cfg.block_size) return GPT2_ERR_SEQ_TOO_LONG;
   if (B < 1 || T < 1 || B > c->cfg.max_batch) return GPT2_ERR_BATCH;
   hipStream_t s = c->stream;
@@ -1012,7 +1091,7 @@ int gpt2_embedding_backward(gpt2_ctx* c, const int32_t* d_idx, const float* d_dx
   return hip_status();
 }
 
-int gpt2_timing_site(gpt2_ctx* c, int index, const char** site, double* total_ms, int64_t* launches,
+int GPT2_API(gpt2_timing_site)(gpt2_ctx* c, int index, const char** site, double* total_ms, int64_t* launches,
                      double* flops, double* bytes, int32_t* gemm_cfg) {
   if (!c || index < 0 || !site || !total_ms || !launches || !flops || !bytes || !gemm_cfg) return GPT2_ERR_ARG;
   if (hipStreamSynchronize(c->stream) != hipSuccess) return GPT2_ERR_HIP;
@@ -1043,6 +1122,29 @@ int gpt2_timing_site(gpt2_ctx* c, int index, const char** site, double* total_ms
   *flops = f;
   *bytes = b;
   *gemm_cfg = cfg;
+  return GPT2_OK;
+}
+
+int GPT2_API(gpt2_loss_scaler)(gpt2_ctx* c, float scale, float growth_factor, float backoff_factor,
+                               int32_t growth_interval, int32_t good_steps) {
+  if (!c || !c->amp) return GPT2_ERR_STATE;
+  if (!(scale > 0.f) || !std::isfinite(scale) || !(growth_factor >= 1.f) || !(backoff_factor > 0.f) ||
+      !(backoff_factor <= 1.f) || growth_interval < 1 || good_steps < 0 || good_steps >= growth_interval)
+    return GPT2_ERR_ARG;
+  c->amp_scale = scale;
+  c->amp_growth = growth_factor;
+  c->amp_backoff = backoff_factor;
+  c->amp_interval = growth_interval;
+  c->amp_good = good_steps;
+  return GPT2_OK;
+}
+
+int GPT2_API(gpt2_loss_scaler_state)(const gpt2_ctx* c, float* scale, int32_t* good_steps, int32_t* skipped) {
+  if (!c || !scale || !good_steps || !skipped) return GPT2_ERR_ARG;
+  if (!c->amp) return GPT2_ERR_STATE;
+  *scale = c->amp_scale;
+  *good_steps = c->amp_good;
+  *skipped = c->amp_skipped;
   return GPT2_OK;
 }
 

@@ -179,6 +179,7 @@ int gpt2_infer_init(const gpt2_config* cfg, const float* d_params, const void* d
   gpt2_sizes ps;
   if (gpt2_init(cfg, nullptr, nullptr, &ps, nullptr) != GPT2_OK) return GPT2_ERR_ARG;
   if (cfg->n_embd / cfg->n_head > 256) return GPT2_ERR_ARG;
+  if (cfg->precision == GPT2_FP16) return GPT2_ERR_ARG;  // decoding runs in fp32 or bf16
   gpt2_infer probe;
   probe.cfg = *cfg;
   probe.ops16 = cfg->precision == GPT2_BF16;

@@ -179,8 +179,11 @@ void to_bf16(const float* src, void* dst, int64_t n, hipStream_t s);
 // Sum of squares into nblk fp64 partials; returns nblk.
 int sumsq_partials(const float* g, int64_t n, double* part, hipStream_t s);
 // norm = sqrt(sum part); coef = max_norm / (norm + 1e-6); clipped = coef < 1.
+// With gradients held times a loss scale S (inv_loss_scale = 1/S, else 1) the
+// norm is that of the unscaled gradients, scale_out includes 1/S, and
+// found_inf (or null) is set to whether the norm is finite.
 void clip_finalize(const double* part, int nblk, float max_norm, float* d_norm, int32_t* d_clipped,
-                   float* scale_out, hipStream_t s);
+                   float* scale_out, float inv_loss_scale, int32_t* found_inf, hipStream_t s);
 struct DecaySegments {
   int n;
   int64_t start[24];  // segment i covers [start[i], start[i+1]) (start[n] = total)
@@ -190,8 +193,9 @@ struct DecaySegments {
 // sumsq_partials of any n (nblk of them) and one clip factor.  Returns 0, or
 // -1 if the device address cannot be found.
 int static_scratch(double** partials, float** clip_scale, int* nblk);
+// skip (or null): when *skip is nonzero the update is skipped (nothing written).
 void adamw(float* p, const float* g, float* m, float* v, void* p_bf16, int64_t n, const DecaySegments& seg,
-           const float* grad_scale, float lr, float beta1, float beta2, float eps, float wd, float inv_bc1,
-           float inv_bc2, hipStream_t s);
+           const float* grad_scale, const int32_t* skip, float lr, float beta1, float beta2, float eps, float wd,
+           float inv_bc1, float inv_bc2, hipStream_t s);
 
 }  // namespace gpt2k

@@ -80,35 +80,43 @@ int sumsq_partials(const float* g, int64_t n, double* part, hipStream_t s) {
 
 __global__ __launch_bounds__(256) void clip_finalize_kernel(const double* __restrict__ part, int nblk,
                                                             float max_norm, float* d_norm, int32_t* d_clipped,
-                                                            float* scale_out) {
+                                                            float* scale_out, float inv_loss_scale,
+                                                            int32_t* found_inf) {
   __shared__ double red[16];
   double s = 0.0;
   for (int i = threadIdx.x; i < nblk; i += blockDim.x) s += part[i];
   s = block_sum(s, red);
   if (threadIdx.x == 0) {
-    const double norm = sqrt(s);
+    // gradients held times the loss scale: the norm of the true gradients is
+    // the scaled norm over the scale, and the update multiplies by both
+    // factors (the clip factor, then the unscale)
+    const double norm = sqrt(s) * (double)inv_loss_scale;
     const double coef = (double)max_norm / (norm + 1e-6);
     const bool clip = coef < 1.0;
     *d_norm = (float)norm;
     *d_clipped = clip ? 1 : 0;
-    *scale_out = clip ? (float)coef : 1.0f;
+    *scale_out = (clip ? (float)coef : 1.0f) * inv_loss_scale;
+    if (found_inf) *found_inf = isfinite(norm) ? 0 : 1;
   }
 }
 
 void clip_finalize(const double* part, int nblk, float max_norm, float* d_norm, int32_t* d_clipped,
-                   float* scale_out, hipStream_t s) {
-  clip_finalize_kernel<<<1, 256, 0, s>>>(part, nblk, max_norm, d_norm, d_clipped, scale_out);
+                   float* scale_out, float inv_loss_scale, int32_t* found_inf, hipStream_t s) {
+  clip_finalize_kernel<<<1, 256, 0, s>>>(part, nblk, max_norm, d_norm, d_clipped, scale_out, inv_loss_scale,
+                                         found_inf);
 }
 
 template <bool BF16>
 __global__ __launch_bounds__(256) void adamw_kernel(float* __restrict__ p, const float* __restrict__ g,
                                                     float* __restrict__ m, float* __restrict__ v,
                                                     h16* __restrict__ pb, int64_t n4, DecaySegments seg,
-                                                    const float* __restrict__ grad_scale, float lr, float beta1,
+                                                    const float* __restrict__ grad_scale,
+                                                    const int32_t* __restrict__ skip, float lr, float beta1,
                                                     float beta2, float eps, float wd, float inv_bc1,
                                                     float inv_bc2) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= n4) return;
+  if (skip && *skip) return;  // a skipped step (non-finite gradient under loss scaling)
   const int64_t e0 = 4 * i;
   int decay = 0;
   for (int k = 0; k < seg.n; ++k)
@@ -131,20 +139,28 @@ __global__ __launch_bounds__(256) void adamw_kernel(float* __restrict__ p, const
   store4(p + e0, pp);
   store4(m + e0, mm);
   store4(v + e0, vv);
-  if constexpr (BF16) store4(pb + e0, pp);
+  if constexpr (BF16) {
+    // the 16-bit copy rounds the stored fp32 value, as to_bf16 does (for
+    // fp16 the compiler would otherwise fuse the rounding into the update's
+    // fma, v_fma_mix, and a copy rebuilt from the fp32 weights, as after a
+    // checkpoint, would differ from it)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) asm volatile("" : "+v"(pp[e]));
+    store4(pb + e0, pp);
+  }
 }
 
 void adamw(float* p, const float* g, float* m, float* v, void* p_bf16, int64_t n, const DecaySegments& seg,
-           const float* grad_scale, float lr, float beta1, float beta2, float eps, float wd, float inv_bc1,
-           float inv_bc2, hipStream_t s) {
+           const float* grad_scale, const int32_t* skip, float lr, float beta1, float beta2, float eps, float wd,
+           float inv_bc1, float inv_bc2, hipStream_t s) {
   const int64_t n4 = n / 4;
   const unsigned grid = (unsigned)((n4 + 255) / 256);
   if (p_bf16)
-    adamw_kernel<true><<<grid, 256, 0, s>>>(p, g, m, v, reinterpret_cast<h16*>(p_bf16), n4, seg, grad_scale, lr,
-                                            beta1, beta2, eps, wd, inv_bc1, inv_bc2);
+    adamw_kernel<true><<<grid, 256, 0, s>>>(p, g, m, v, reinterpret_cast<h16*>(p_bf16), n4, seg, grad_scale, skip,
+                                            lr, beta1, beta2, eps, wd, inv_bc1, inv_bc2);
   else
-    adamw_kernel<false><<<grid, 256, 0, s>>>(p, g, m, v, nullptr, n4, seg, grad_scale, lr, beta1, beta2, eps, wd,
-                                             inv_bc1, inv_bc2);
+    adamw_kernel<false><<<grid, 256, 0, s>>>(p, g, m, v, nullptr, n4, seg, grad_scale, skip, lr, beta1, beta2,
+                                             eps, wd, inv_bc1, inv_bc2);
 }
 
 // ---- scratch in device memory that nothing allocates ----------------------------

@@ -25,6 +25,8 @@ GPT2_ERR_HIP = -6
 GPT2_ERR_IO = -7
 GPT2_FP32 = 0
 GPT2_BF16 = 1
+GPT2_FP16 = 2
+PRECISIONS = {"fp32": GPT2_FP32, "bf16": GPT2_BF16, "fp16": GPT2_FP16}
 GPT2_UNTIED_HEAD = 1
 GPT2_NO_QKV_BIAS = 2
 
@@ -38,7 +40,7 @@ ERROR_NAMES = {
 EXPORTS = ("gpt2_init", "gpt2_forward_loss", "gpt2_backward", "gpt2_accumulate", "gpt2_clip_adamw_step",
            "gpt2_destroy", "gpt2_sync_status", "gpt2_sync_params", "gpt2_get_step", "gpt2_set_step",
            "gpt2_tensor_info", "gpt2_activation", "gpt2_timing_enable", "gpt2_timing_read", "gpt2_timing_site",
-           "gpt2_embedding_backward", "gpt2_clip_adamw_step_static",
+           "gpt2_embedding_backward", "gpt2_clip_adamw_step_static", "gpt2_loss_scaler", "gpt2_loss_scaler_state",
            "gpt2_lr_at", "gpt2_loader_open", "gpt2_loader_next", "gpt2_loader_next_host", "gpt2_loader_state",
            "gpt2_loader_seek", "gpt2_loader_close", "gpt2_checkpoint_save", "gpt2_checkpoint_load",
            "gpt2_infer_init", "gpt2_infer_prefill", "gpt2_infer_decode", "gpt2_infer_length", "gpt2_sample",
@@ -122,6 +124,9 @@ def load_library() -> ctypes.CDLL:
         "gpt2_checkpoint_load": (I, [P, ctypes.c_char_p, ctypes.POINTER(I64), ctypes.POINTER(ctypes.c_int)]),
         "gpt2_clip_adamw_step_static": (I, [ctypes.POINTER(gpt2_config), ctypes.POINTER(gpt2_buffers), P, I64,
                                             F, F, F, F, F, F, P, P]),
+        "gpt2_loss_scaler": (I, [P, F, F, F, ctypes.c_int32, ctypes.c_int32]),
+        "gpt2_loss_scaler_state": (I, [P, ctypes.POINTER(F), ctypes.POINTER(ctypes.c_int32),
+                                       ctypes.POINTER(ctypes.c_int32)]),
         "gpt2_infer_init": (I, [ctypes.POINTER(gpt2_config), P, P, P, P, P, ctypes.POINTER(gpt2_infer_sizes),
                                 ctypes.POINTER(P)]),
         "gpt2_infer_prefill": (I, [P, P, I, I, P]),
@@ -151,7 +156,7 @@ def make_config(shape, precision: str, max_batch: int) -> gpt2_config:
     variant = (0 if getattr(shape, "tied", True) else GPT2_UNTIED_HEAD) | \
               (0 if getattr(shape, "qkv_bias", True) else GPT2_NO_QKV_BIAS)
     return gpt2_config(shape.n_layer, shape.n_head, shape.n_embd, shape.block_size, shape.vocab_size,
-                       shape.padded_vocab_size, GPT2_BF16 if precision == "bf16" else GPT2_FP32, max_batch, variant)
+                       shape.padded_vocab_size, PRECISIONS[precision], max_batch, variant)
 
 
 def query_sizes(cfg: gpt2_config) -> gpt2_sizes:
@@ -198,7 +203,9 @@ class GPT2Step:
         self.grads = torch.empty(n, dtype=torch.float32, device=dev)
         self.m = torch.empty(n, dtype=torch.float32, device=dev)
         self.v = torch.empty(n, dtype=torch.float32, device=dev)
-        self.params_bf16 = (torch.empty(n, dtype=torch.bfloat16, device=dev) if precision == "bf16" else None)
+        # the 16-bit copy of the weights (bf16, or fp16 in the fp16 mode)
+        h16 = {"bf16": torch.bfloat16, "fp16": torch.float16}.get(precision)
+        self.params_bf16 = torch.empty(n, dtype=h16, device=dev) if h16 is not None else None
         ws = self.sizes.workspace_bytes
         self.workspace = torch.empty(ws + 256, dtype=torch.uint8, device=dev)
         base = self.workspace.data_ptr()
@@ -325,12 +332,25 @@ class GPT2Step:
         ptr, numel, dt = ctypes.c_void_p(), ctypes.c_int64(), ctypes.c_int32()
         _check(self.lib.gpt2_activation(self.ctx, name.encode(), layer, ctypes.byref(ptr), ctypes.byref(numel),
                                         ctypes.byref(dt)), f"gpt2_activation({name})")
-        dtype = {0: torch.float32, 1: torch.bfloat16, 2: torch.int32}[dt.value]
-        esz = {0: 4, 1: 2, 2: 4}[dt.value]
+        dtype = {0: torch.float32, 1: torch.bfloat16, 2: torch.int32, 3: torch.float16}[dt.value]
+        esz = {0: 4, 1: 2, 2: 4, 3: 2}[dt.value]
         base = self.workspace.data_ptr()
         off = ptr.value - base
         raw = self.workspace[off:off + numel.value * esz]
         return raw.view(dtype)
+
+    def loss_scaler(self, scale: float, growth_factor: float = 2.0, backoff_factor: float = 0.5,
+                    growth_interval: int = 2000, good_steps: int = 0) -> None:
+        """Sets the dynamic loss scaler of an fp16 context."""
+        _check(self.lib.gpt2_loss_scaler(self.ctx, scale, growth_factor, backoff_factor, growth_interval, good_steps),
+               "gpt2_loss_scaler")
+
+    def loss_scaler_state(self):
+        """(scale, good_steps, skipped) of an fp16 context's loss scaler."""
+        sc, good, sk = ctypes.c_float(), ctypes.c_int32(), ctypes.c_int32()
+        _check(self.lib.gpt2_loss_scaler_state(self.ctx, ctypes.byref(sc), ctypes.byref(good), ctypes.byref(sk)),
+               "gpt2_loss_scaler_state")
+        return sc.value, good.value, sk.value
 
     def timing_enable(self, site) -> None:
         _check(self.lib.gpt2_timing_enable(self.ctx, site.encode() if site is not None else None),

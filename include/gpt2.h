@@ -72,6 +72,12 @@ extern "C" {
 #define GPT2_BF16 1  /* bf16 GEMM/attention operands and activations, fp32
                         residual stream, statistics, loss, grads, master
                         weights and AdamW moments                              */
+#define GPT2_FP16 2  /* as GPT2_BF16 with IEEE half (fp16) in place of bf16,
+                        and dynamic loss scaling (gpt2_loss_scaler): the
+                        Genesis model card's "Mixed Precision (AMP) -- FP16"
+                        ("Training Features"), which bf16 does without (AxonLM
+                        README, "Key Features": bfloat16 AMP needs no loss
+                        scaling).  params_bf16 holds the fp16 copy.          */
 
 typedef struct {
   int32_t n_layer;            /* L                                             */
@@ -81,7 +87,8 @@ typedef struct {
   int32_t vocab_size;         /* ids and targets lie in [0, vocab_size)        */
   int32_t padded_vocab_size;  /* Vp >= vocab_size: rows of wte, softmax width;
                                  Vp % 8 == 0 in BF16 mode                      */
-  int32_t precision;          /* GPT2_FP32 or GPT2_BF16; BF16 needs C/NH == 64 */
+  int32_t precision;          /* GPT2_FP32, GPT2_BF16 or GPT2_FP16; the 16-bit
+                                 modes need C/NH == 64                         */
   int32_t max_batch;          /* largest micro-batch B the workspace holds     */
   int32_t variant;            /* 0 (GPT-2), or GPT2_UNTIED_HEAD and/or
                                  GPT2_NO_QKV_BIAS                              */
@@ -177,11 +184,38 @@ int gpt2_accumulate(gpt2_ctx *ctx, const int32_t *d_idx, const int32_t *d_target
  *   and the bf16 copy of params is refreshed (BF16 mode).
  * *d_norm (device fp32) receives n; *d_clipped (device int32) 1 iff scaled.
  * grads are left unscaled.
+ * FP16 mode: the gradients hold S times the true gradients (S the loss scale
+ * the accumulation used); n is that of the true gradients and the update
+ * uses g / S.  If n is not finite the step is skipped: params, moments, the
+ * fp16 copy and t are left as they were.  Then S is updated as
+ * gpt2_loss_scaler describes.  The call waits for the stream (the scale
+ * update needs the step's verdict).
  * Errors: GPT2_ERR_ARG for NULL pointers.
  */
 int gpt2_clip_adamw_step(gpt2_ctx *ctx, float lr, float beta1, float beta2, float eps,
                          float weight_decay, float max_norm, float *d_norm,
                          int32_t *d_clipped);
+
+/*
+ * Dynamic loss scaling of an FP16 context (the fp16 AMP of the Genesis model
+ * card, "Training Features"; the pages give no constants, so a context starts
+ * with those of PyTorch's GradScaler: scale 65536, growth factor 2, backoff
+ * factor 0.5, growth interval 2000).  Every forward of the context forms the
+ * gradient of loss_scale * scale * loss; gpt2_clip_adamw_step unscales, and
+ * after it the scale becomes scale * backoff_factor if the step was skipped
+ * (a gradient was not finite), or scale * growth_factor once growth_interval
+ * consecutive steps were not skipped (good_steps counts them).
+ * gpt2_loss_scaler sets the whole state (also to restore it);
+ * gpt2_loss_scaler_state reads it, with skipped = 1 iff the last step was
+ * skipped.  Host only.
+ * Errors: GPT2_ERR_STATE unless ctx is an FP16 context; GPT2_ERR_ARG for a
+ * scale that is not finite and positive, growth_factor < 1, backoff_factor
+ * outside (0, 1], growth_interval < 1 or good_steps outside
+ * [0, growth_interval), or NULL pointers.
+ */
+int gpt2_loss_scaler(gpt2_ctx *ctx, float scale, float growth_factor, float backoff_factor,
+                     int32_t growth_interval, int32_t good_steps);
+int gpt2_loss_scaler_state(const gpt2_ctx *ctx, float *scale, int32_t *good_steps, int32_t *skipped);
 
 /*
  * gpt2_clip_adamw_step without a context or workspace, for callers that
@@ -195,7 +229,8 @@ int gpt2_clip_adamw_step(gpt2_ctx *ctx, float lr, float beta1, float beta2, floa
  * of a workspace; the call allocates nothing.  Calls that overlap on one GPU
  * (two streams, or two threads) share that array and race: serialise them.
  * The device current on the calling thread must be the stream's device.
- * Errors: GPT2_ERR_ARG for an invalid config, NULL pointers, t < 1 or more
+ * Errors: GPT2_ERR_ARG for an invalid config, an FP16 config (its loss
+ * scaler lives in a context), NULL pointers, t < 1 or more
  * than 2^40 parameters; GPT2_ERR_HIP if the scratch address cannot be found
  * or a launch fails.
  */
@@ -233,7 +268,7 @@ int gpt2_tensor_info(const gpt2_config *cfg, int index, const char **name,
    "emb_sorted_pos", "dresid"}; layer selects the block (for "resid", the
    index 0..2L of the residual stream).  "fcgd" is gelu'(u) and "fcg" gelu(u)
    for the MLP pre-activation u (u itself is not kept).  dtype: 0 fp32,
-   1 bf16, 2 int32. */
+   1 bf16, 2 int32, 3 fp16. */
 int gpt2_activation(gpt2_ctx *ctx, const char *name, int layer, void **ptr,
                     int64_t *numel, int32_t *dtype);
 

@@ -38,7 +38,8 @@ typedef struct {
  * copy (BF16 mode; NULL in FP32 mode).  cfg->max_batch is the number of
  * sequences decoded together.  The parameters are read, never written; they
  * must stay valid while the context is used.
- * Errors: GPT2_ERR_ARG (bad config, NULL buffers, head dim above 256). */
+ * Errors: GPT2_ERR_ARG (bad config, an FP16 config, NULL buffers, head dim
+ * above 256). */
 int gpt2_infer_init(const gpt2_config *cfg, const float *d_params, const void *d_params_bf16, void *d_cache,
                     void *d_workspace, void *hip_stream, gpt2_infer_sizes *sizes, gpt2_infer **out);
 

@@ -90,15 +90,17 @@ void gpt2_loader_close(gpt2_loader *ld);
 
 /* ---- checkpoints -------------------------------------------------------------- */
 /* Writes the training state of ctx to `path`: the config, the AdamW step
- * counter, n_extra caller words (e.g. the loader position; at most 16), and
- * the fp32 params, adam_m and adam_v (12 bytes per parameter).  Waits for the
+ * counter, n_extra caller words (e.g. the loader position; at most 16), the
+ * loss scale and its growth counter (FP16 contexts only), and the fp32
+ * params, adam_m and adam_v (12 bytes per parameter).  Waits for the
  * work queued on the context's stream, then writes `path`.tmp and renames it
  * over `path`, so a crash never leaves a partial file under that name.
  * Errors: GPT2_ERR_ARG, GPT2_ERR_IO, GPT2_ERR_HIP. */
 int gpt2_checkpoint_save(gpt2_ctx *ctx, const char *path, const int64_t *extra, int n_extra);
 
 /* Restores a checkpoint written by gpt2_checkpoint_save into ctx: params,
- * adam_m, adam_v, the step counter and the bf16 copy of params (grads are
+ * adam_m, adam_v, the step counter, the loss scaler's scale and growth
+ * counter (FP16), and the 16-bit copy of params (grads are
  * left as they are).  *n_extra: in, room in extra (at most 16); out, the
  * words restored.  Errors: GPT2_ERR_IO (unreadable or not a checkpoint),
  * GPT2_ERR_ARG (its model config differs from the context's: every field but

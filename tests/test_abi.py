@@ -103,3 +103,29 @@ def test_null_arguments_are_rejected_without_touching_the_gpu(lib):
     assert lib.gpt2_clip_adamw_step(None, 1e-3, 0.9, 0.95, 1e-8, 0.1, 1.0, None, None) == L.GPT2_ERR_ARG
     assert lib.gpt2_get_step(None) == -1
     lib.gpt2_destroy(None)
+
+
+def test_fp16_mode_sizes_and_refusals(lib):
+    """The fp16 mode has the bf16 mode's layout and constraints; the entry
+    point without a context and the decoding context refuse it (its loss
+    scaler lives in a training context); the scaler calls refuse a NULL or
+    non-fp16 context.  None of these touches the GPU."""
+    s = SHAPES["gpt2-124m"]
+    a = L.query_sizes(L.make_config(s, "bf16", 2))
+    h = L.query_sizes(L.make_config(s, "fp16", 2))
+    assert (h.n_params, h.workspace_bytes, h.params_bf16_bytes) == (a.n_params, a.workspace_bytes,
+                                                                    a.params_bf16_bytes)
+    cfg = L.make_config(ModelShape("x", 2, 4, 128, 64, 65, 72), "fp16", 1)  # head dim 32
+    sz = L.gpt2_sizes()
+    assert lib.gpt2_init(ctypes.byref(cfg), None, None, ctypes.byref(sz), None) == L.GPT2_ERR_ARG
+    cfg = L.make_config(s, "fp16", 1)
+    one = ctypes.c_void_p(256)  # never dereferenced: the config is refused first
+    bufs = L.gpt2_buffers(one, one, one, one, one, one)
+    assert lib.gpt2_clip_adamw_step_static(ctypes.byref(cfg), ctypes.byref(bufs), None, 1, 1e-3, 0.9, 0.95, 1e-8,
+                                           0.1, 1.0, one, one) == L.GPT2_ERR_ARG
+    isz = L.gpt2_infer_sizes()
+    assert lib.gpt2_infer_init(ctypes.byref(cfg), None, None, None, None, None, ctypes.byref(isz),
+                               None) == L.GPT2_ERR_ARG
+    f, i = ctypes.c_float(), ctypes.c_int32()
+    assert lib.gpt2_loss_scaler(None, 1.0, 2.0, 0.5, 10, 0) == L.GPT2_ERR_STATE
+    assert lib.gpt2_loss_scaler_state(None, ctypes.byref(f), ctypes.byref(i), ctypes.byref(i)) == L.GPT2_ERR_ARG

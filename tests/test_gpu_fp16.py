@@ -1,0 +1,133 @@
+"""GPU: the fp16 mode (IEEE half operands and activations, fp32 master
+weights, dynamic loss scaling) through the C ABI against the fp64 oracle.
+
+Tolerances: fp16 carries 11 significant bits against bf16's 8, over a range
+that the loss scale keeps the gradients inside, so the bf16 gates (gradient
+cosine >= 0.99 per tensor, update relative L2 <= 2e-2, loss within 2e-2) are
+tightened by the ratio of the unit roundoffs (8x for the relative errors,
+64x for 1 - cosine, a second-order quantity): loss within 5e-3, cosine >=
+0.9995, update relative L2 <= 5e-3.  The loss scaler (skip on a non-finite
+gradient, backoff, growth) is compared exactly with oracle.amp.
+"""
+
+import numpy as np
+import pytest
+
+from gpt2_inputs import init_params
+from oracle import amp
+from oracle import gpt2 as ref
+from tests.gpu_helpers import batches_for, cos, gpu_step, host, per_tensor, rel, say, shape, to_dev, warm_state
+from tests.test_gpu_parity import _f32, _oracle_step, _run
+
+pytestmark = pytest.mark.gpu
+
+FP16_LOSS_ABS = 5e-3
+FP16_GRAD_COS = 0.9995
+FP16_UPDATE_REL = 5e-3
+
+
+def _gate_fp16(p, r, g):
+    say(f"  loss gpu {g['loss']:.6f} ref {r['loss']:.6f}; norm gpu {g['norm']:.5f} ref {r['norm']:.5f}")
+    assert abs(g["loss"] - r["loss"]) < FP16_LOSS_ABS
+    G, RG = per_tensor(g["grads"]), per_tensor(r["grads"])
+    worst = min((cos(G[k], RG[k]), k) for k in G)
+    say(f"  worst gradient cosine {worst[0]:.6f} {worst[1]} over {len(G)} tensors")
+    for k in G:
+        assert cos(G[k], RG[k]) >= FP16_GRAD_COS, (k, cos(G[k], RG[k]))
+    assert abs(g["norm"] - r["norm"]) / r["norm"] < 5e-3
+    assert bool(g["clipped"]) == r["clipped"]
+    P0, P1, R1 = per_tensor(p), per_tensor(g["params"]), per_tensor(_f32(r["params"]))
+    worst = max((rel(P1[k] - P0[k], R1[k] - P0[k]), k) for k in P0)
+    say(f"  worst update rel err {worst[0]:.5f} {worst[1]}")
+    for k in P0:
+        e = rel(P1[k] - P0[k], R1[k] - P0[k])
+        assert e <= FP16_UPDATE_REL, (k, e)
+
+
+def _fp16_case(s, B, T, k, lr=6e-4, scale=None):
+    say(f"fp16 step {s.name}: L={s.n_layer} C={s.n_embd} NH={s.n_head} B={B} T={T} k={k}")
+    p = init_params(s, 0)
+    batches = batches_for(s, B, T, k, kind="zipf")
+    loss_r, g_r = ref.accumulate(p, batches, s.n_head)
+    m0, v0 = warm_state(g_r)
+    r = _oracle_step(p, batches, s.n_head, m0, v0, 11, lr=lr, accumulated=(loss_r, g_r))
+    g = _run(s, "fp16", p, batches, warm=(m0, v0, 10), lr=lr)
+    # the GPU's gradient buffer holds the scaled gradients: unscale for the gate
+    S = amp.INIT_SCALE
+    g["grads"] = {n: a / S for n, a in g["grads"].items()}
+    _gate_fp16(p, r, g)
+
+
+def test_fp16_gpt2_small_width_two_layers():
+    _fp16_case(shape("gpt2-124m-L2", 2, 12, 768, 1024, 50257, 50304), 1, 1024, 2)
+
+
+def test_fp16_ragged_sequence_length():
+    _fp16_case(shape("gpt2-124m-L1", 1, 12, 768, 1024, 50257, 50304), 2, 200, 1)
+
+
+def test_fp16_overflow_skips_the_step_then_recovers():
+    """A scale of 2^40 overflows the fp16 logit gradient (its largest entries
+    are about S / (B T) = 2^33 > 65,504): the step is skipped with everything
+    unchanged and the scale halved.  Then at a workable scale the step runs,
+    its unscaled gradients match the oracle's, and the scaler counts it."""
+    import torch
+    s = shape("gpt2-124m-L1", 1, 12, 768, 1024, 50257, 50304)
+    B, T = 1, 128
+    p = init_params(s, 0)
+    batches = batches_for(s, B, T, 1, kind="zipf")
+    st = gpu_step(s, "fp16", B, p)
+    x, y = to_dev(batches)
+    say("fp16 overflow: scale 2^40")
+    st.loss_scaler(2.0 ** 40, growth_interval=3)
+    before = [t.clone() for t in (st.params, st.m, st.v, st.params_bf16)]
+    st.accumulate(x, y)
+    norm, _ = st.clip_adamw_step(1e-3)
+    torch.cuda.synchronize()
+    assert st.sync_status() == 0
+    scale, good, skipped = st.loss_scaler_state()
+    say(f"  after: scale 2^{np.log2(scale):.0f}, good {good}, skipped {skipped}, norm {norm.item()}")
+    assert skipped == 1 and good == 0 and scale == 2.0 ** 39
+    assert (scale, good) == amp.scaler_update(2.0 ** 40, 0, True, growth_interval=3)
+    assert not np.isfinite(norm.item())
+    assert st.step_count() == 0
+    for a, b in zip(before, (st.params, st.m, st.v, st.params_bf16)):
+        assert torch.equal(a, b)
+    say("fp16 recovery: scale 2^10")
+    st.loss_scaler(2.0 ** 10, growth_interval=3)
+    loss = st.accumulate(x, y)
+    torch.cuda.synchronize()
+    G = {n: a / 2.0 ** 10 for n, a in host(st.to_dict(st.grads)).items()}
+    st.clip_adamw_step(1e-3)
+    torch.cuda.synchronize()
+    scale, good, skipped = st.loss_scaler_state()
+    assert skipped == 0 and good == 1 and scale == 2.0 ** 10 and st.step_count() == 1
+    loss_r, g_r = ref.accumulate(p, batches, s.n_head)
+    assert abs(loss.item() - loss_r) < FP16_LOSS_ABS
+    Gt, Rt = per_tensor(G), per_tensor(g_r)
+    worst = min((cos(Gt[k], Rt[k]), k) for k in Gt)
+    say(f"  loss {loss.item():.5f} (oracle {loss_r:.5f}); worst gradient cosine {worst[0]:.6f} {worst[1]}")
+    assert worst[0] >= FP16_GRAD_COS
+    assert not torch.equal(before[0], st.params)
+    st.close()
+
+
+def test_fp16_scale_grows_after_the_interval():
+    import torch
+    s = shape("gpt2-124m-L1", 1, 12, 768, 1024, 50257, 50304)
+    B, T = 1, 64
+    p = init_params(s, 0)
+    st = gpu_step(s, "fp16", B, p)
+    st.loss_scaler(1024.0, growth_factor=2.0, backoff_factor=0.5, growth_interval=2)
+    want = (1024.0, 0)
+    for i in range(5):
+        x, y = to_dev(batches_for(s, B, T, 1, kind="zipf", seed=10 + i))
+        st.accumulate(x, y)
+        st.clip_adamw_step(1e-4)
+        torch.cuda.synchronize()
+        scale, good, skipped = st.loss_scaler_state()
+        want = amp.scaler_update(*want, bool(skipped), growth_interval=2)
+        say(f"  step {i}: scale {scale} good {good} skipped {skipped}")
+        assert skipped == 0 and (scale, good) == want
+    assert st.step_count() == 5 and want == (4096.0, 1)
+    st.close()

@@ -28,7 +28,7 @@ def _toy_run(k=2):
     return RunConfig("toy-k", r.shape, 4, k, 64, "fp32", "uniform", 1e-3)
 
 
-@pytest.mark.parametrize("precision", ["fp32", "bf16"])
+@pytest.mark.parametrize("precision", ["fp32", "bf16", "fp16"])
 def test_checkpoint_resume_is_bitwise(tmp_path, precision):
     import torch
 
@@ -38,7 +38,7 @@ def test_checkpoint_resume_is_bitwise(tmp_path, precision):
     else:
         from tests.gpu_helpers import shape
         s = shape("gpt2-124m-L1", 1, 12, 768, 1024, 50257, 50304)
-        run = RunConfig("l1", s, 2, 2, 128, "bf16", "zipf", 6e-4)
+        run = RunConfig("l1", s, 2, 2, 128, precision, "zipf", 6e-4)
     say(f"checkpoint / resume {precision}")
     s = run.shape
     paths = _shards(tmp_path, 9 * run.tokens_per_step, s.vocab_size, 3, kind=run.tokens)
@@ -48,6 +48,7 @@ def test_checkpoint_resume_is_bitwise(tmp_path, precision):
     a.train(5)
     torch.cuda.synchronize()
     want = [t.clone() for t in (a.step.params, a.step.m, a.step.v)]
+    want_scaler = a.step.loss_scaler_state()[:2] if precision == "fp16" else None
     a.close()
     p = latest_checkpoint(ck)
     assert p.endswith("step_00000003.ckpt") and not os.path.exists(p + ".tmp")
@@ -59,6 +60,8 @@ def test_checkpoint_resume_is_bitwise(tmp_path, precision):
     assert b.t == 5
     for x, y in zip(want, (b.step.params, b.step.m, b.step.v)):
         assert torch.equal(x, y)
+    if precision == "fp16":  # the loss scaler came back with the checkpoint
+        assert b.step.loss_scaler_state()[:2] == want_scaler
     # a checkpoint of another model is refused
     from gpt_decoder_pre_amd.lib import GPT2_ERR_ARG, GPT2Step, Gpt2Error
     from gpt2_inputs import ModelShape
