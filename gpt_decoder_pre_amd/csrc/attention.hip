@@ -318,8 +318,11 @@ __global__ __launch_bounds__(256, 4) void flash_fwd_kernel(const h16* __restrict
 // lane%32 and accumulates dK^T and dV^T over the query tiles (64 queries)
 // that can see them, one 32-query half at a time (scores, P and dS of that
 // half, then its dV / dK products), which keeps the kernel at 168 VGPRs and
-// three workgroups per CU (measured on MI355X: 3-4% faster than two with
-// both halves' P and dS held; the same products in the same order).  Q and dO tiles stream from HBM straight into a
+// three workgroups per CU.  Q / dO tiles and their LSE / D rows go through a
+// two-stage LDS ring, two q-tiles per loop trip (compile-time stage offsets).
+// Measured on MI355X (dQ + dK/dV at 16 x 12 x 1024 x 64): two workgroups per
+// CU with both halves' P and dS held 142-144 us, three with a three-stage
+// ring 138.5, three with two stages 130; the same products in the same order.  Q and dO tiles stream from HBM straight into a
 // three-stage LDS ring, and the tile's log-sum-exp (exp2 domain) and D rows
 // beside them (written by the dQ kernel).
 __global__ __launch_bounds__(256, 3) void flash_bwd_dkdv_kernel(const h16* __restrict__ qkv,
@@ -328,8 +331,9 @@ __global__ __launch_bounds__(256, 3) void flash_bwd_dkdv_kernel(const h16* __res
                                                                 const float* __restrict__ Dd,
                                                                 h16* __restrict__ dqkv, int T, int NH, int C,
                                                                 float sl2, float scale, float* __restrict__ colsum) {
-  __shared__ __attribute__((aligned(1024))) h16 smem[3 * ASTAGE];  // [stage][Q | dO]
-  __shared__ __attribute__((aligned(16))) float rowv[3][2][64];     // [stage][lse log2e | D]
+  // [stage][Q | dO], two stages; sized for the column sums' staging after the loop (33 KB)
+  __shared__ __attribute__((aligned(1024))) h16 smem[(4 * 64 * 33 * 4 + 1) / 2 > 2 * ASTAGE ? (4 * 64 * 33 * 4 + 1) / 2 : 2 * ASTAGE];
+  __shared__ __attribute__((aligned(16))) float rowv[2][2][64];     // [stage][lse log2e | D]
   int kt, h, b;
   attn_block(T, NH, kt, h, b);
   const int tid = threadIdx.x, lane = tid & 63, lc = lane & 31, hl = lane >> 5;
@@ -370,23 +374,15 @@ __global__ __launch_bounds__(256, 3) void flash_bwd_dkdv_kernel(const h16* __res
 #pragma unroll
   for (int r = 0; r < 16; ++r) dk[0][r] = dk[1][r] = dv[0][r] = dv[1][r] = 0.f;
 
-  // Prologue: tiles 0 and 1 in flight.  Step it waits for tile it (tile
-  // it+1's loads stay in flight), barrier (tile it resident for every wave,
-  // every wave past step it-1), loads tile it+2 into the stage tile it-1
-  // used, then uses tile it.
+  // Prologue: tile 0 in flight.  Step it waits for tile it, barrier (tile it
+  // resident for every wave, every wave past step it-1), loads tile it+1
+  // into the stage tile it-1 used, then uses tile it.
   load(0, 0);
-  if (nqt > 1) load(1, 1);
   auto step = [&](int it, auto stgc) {
     constexpr int stg = decltype(stgc)::value;
-    constexpr int stg2 = (stg + 2) % 3;
-    if (it + 1 < nqt) {
-      if (wave < 2) wait_vmcnt<5>();
-      else wait_vmcnt<4>();
-    } else {
-      wait_vmcnt<0>();
-    }
+    wait_vmcnt<0>();
     lds_barrier();
-    if (it + 2 < nqt) load(it + 2, stg2);
+    if (it + 1 < nqt) load(it + 1, stg ^ 1);
     const int q0 = key0 + it * 64;
     const h16* Qs = smem + stg * ASTAGE;
     const h16* Gs = Qs + ATILE;
@@ -442,10 +438,9 @@ __global__ __launch_bounds__(256, 3) void flash_bwd_dkdv_kernel(const h16* __res
       }
     }
   };
-  for (int it = 0; it < nqt; it += 3) {
+  for (int it = 0; it < nqt; it += 2) {
     step(it, std::integral_constant<int, 0>{});
     if (it + 1 < nqt) step(it + 1, std::integral_constant<int, 1>{});
-    if (it + 2 < nqt) step(it + 2, std::integral_constant<int, 2>{});
   }
   if (mykey < T) {
     h16* o = dqkv + ((int64_t)b * T + mykey) * ld + h * HD;
