@@ -469,14 +469,18 @@ __global__ __launch_bounds__(256, 3) void flash_bwd_dkdv_kernel(const h16* __res
 // Workgroup: 128 queries; wave w owns queries q0 + 32 w + lane%32, forms D
 // for them from the dO and O rows (and stores it for the dK / dV kernel), and
 // accumulates dQ^T over the key tiles (64 keys) it sees; K and V tiles stream
-// into a three-stage LDS ring as in the forward kernel.
+// into a two-stage LDS ring as in the forward kernel, two tiles per loop trip.
+// A key tile past every query of a wave is computed fully masked (it adds
+// zeros) rather than branched around: the branch made the compiler copy the
+// dQ accumulators between register sets every tile.
 __global__ __launch_bounds__(256, 3) void flash_bwd_dq_kernel(const h16* __restrict__ qkv,
                                                               const h16* __restrict__ y,
                                                               const h16* __restrict__ dy,
                                                               const float* __restrict__ lse, float* __restrict__ Dd,
                                                               h16* __restrict__ dqkv, int T, int NH, int C, float sl2,
                                                               float scale, float* __restrict__ colsum) {
-  __shared__ __attribute__((aligned(1024))) h16 smem[3 * ASTAGE];  // [stage][K | V]
+  // [stage][K | V], two stages; sized for the column sums' staging after the loop (33 KB)
+  __shared__ __attribute__((aligned(1024))) h16 smem[(4 * 64 * 33 * 4 + 1) / 2 > 2 * ASTAGE ? (4 * 64 * 33 * 4 + 1) / 2 : 2 * ASTAGE];
   int qt, h, b;
   attn_block(T, NH, qt, h, b);
   qt = (T + 127) / 128 - 1 - qt;  // tile 0: the most key tiles
@@ -500,7 +504,6 @@ __global__ __launch_bounds__(256, 3) void flash_bwd_dq_kernel(const h16* __restr
     tl.issue(V, j * 64, T, base + ATILE * 2, wave, lane);
   };
   load(0, 0);
-  if (nkt > 1) load(1, 1);
 
   const bool qok = myq < T;
   const float lse2 = qok ? lse[((int64_t)b * NH + h) * T + myq] * kLog2e : 0.f;
@@ -526,19 +529,19 @@ __global__ __launch_bounds__(256, 3) void flash_bwd_dq_kernel(const h16* __restr
   for (int r = 0; r < 16; ++r) dq[0][r] = dq[1][r] = 0.f;
   const int qlim = min(myq, T - 1);
 
-  int stg = 0;
-  for (int kt = 0; kt < nkt; ++kt) {
-    const int stg1 = stg == 2 ? 0 : stg + 1, stg2 = stg1 == 2 ? 0 : stg1 + 1;
-    if (kt + 1 < nkt) wait_vmcnt<4>();  // this wave's loads of tile kt landed (tile kt+1's four may be in flight)
-    else wait_vmcnt<0>();
+  // Key tile kt: wait for its loads, barrier (every wave past tile kt-1,
+  // whose stage the loads of tile kt+1 then take), then use it.
+  auto step = [&](int kt, auto stgc) {
+    constexpr int stg = decltype(stgc)::value;
+    wait_vmcnt<0>();
     lds_barrier();
-    if (kt + 2 < nkt) load(kt + 2, stg2);
+    if (kt + 1 < nkt) load(kt + 1, stg ^ 1);
     const int k0 = kt * 64;
     const h16* Ks = smem + stg * ASTAGE;
     const h16* Vs = Ks + ATILE;
     {  // a key tile past every query of the wave is masked whole (adds zeros)
       const bool diag = k0 + 63 > wq0 || k0 + 64 > T;
-      f32x16 dS[2];
+      h16x8 sb[4];  // dS^T in bf16, 16-key steps st = 0..3
 #pragma unroll
       for (int js = 0; js < 2; ++js) {
         f32x16 sv, dp;
@@ -549,29 +552,31 @@ __global__ __launch_bounds__(256, 3) void flash_bwd_dq_kernel(const h16* __restr
           sv = mfma32(row_frag(Ks, js * 32, kk, lane), qf[kk], sv);
           dp = mfma32(row_frag(Vs, js * 32, kk, lane), gf[kk], dp);
         }
-        // sv[r]: key k0 + 32 js + 8 (r/4) + 4 hl + r%4, query myq; keys past
-        // the query get score -inf (probability exactly 0)
         if (diag) {
           const int lim = qlim - (k0 + 32 * js + 4 * hl);
 #pragma unroll
           for (int r = 0; r < 16; ++r) sv[r] = (8 * (r >> 2) + (r & 3) <= lim) ? sv[r] : -INFINITY;
         }
+        f32x16 ds;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const float p = exp2_fast(fmaf(sv[r], sl2, -lse2));
-          dS[js][r] = p * (dp[r] - Dq);
+          ds[r] = p * (dp[r] - Dq);
         }
+        sb[2 * js] = pack8(ds, 0);
+        sb[2 * js + 1] = pack8(ds, 8);
       }
       // dQ^T += K^T dS^T (K read transposed, keys in the accumulator order)
 #pragma unroll
       for (int st = 0; st < 4; ++st) {
-        const h16x8 sb = pack8(dS[st >> 1], 8 * (st & 1));
 #pragma unroll
-        for (int t = 0; t < 2; ++t)
-          dq[t] = mfma32(tr_frag_keys(Ks, st * 16, t * 32, lane), sb, dq[t]);
+        for (int t = 0; t < 2; ++t) dq[t] = mfma32(tr_frag_keys(Ks, st * 16, t * 32, lane), sb[st], dq[t]);
       }
     }
-    stg = stg1;
+  };
+  for (int kt = 0; kt < nkt; kt += 2) {
+    step(kt, std::integral_constant<int, 0>{});
+    if (kt + 1 < nkt) step(kt + 1, std::integral_constant<int, 1>{});
   }
   if (qok) {
     h16* o = dqkv + ((int64_t)b * T + myq) * ld + h * HD;
