@@ -816,7 +816,9 @@ int GPT2_API(gpt2_clip_adamw_step)(gpt2_ctx* c, float lr, float beta1, float bet
       c->amp_scale *= c->amp_backoff;
       c->amp_good = 0;
     } else if (++c->amp_good >= c->amp_interval) {
-      c->amp_scale *= c->amp_growth;
+      // a growth that would overflow fp32 is not taken (an infinite scale
+      // could never back off again)
+      if (std::isfinite(c->amp_scale * c->amp_growth)) c->amp_scale *= c->amp_growth;
       c->amp_good = 0;
     }
   }

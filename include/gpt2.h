@@ -204,7 +204,8 @@ int gpt2_clip_adamw_step(gpt2_ctx *ctx, float lr, float beta1, float beta2, floa
  * gradient of loss_scale * scale * loss; gpt2_clip_adamw_step unscales, and
  * after it the scale becomes scale * backoff_factor if the step was skipped
  * (a gradient was not finite), or scale * growth_factor once growth_interval
- * consecutive steps were not skipped (good_steps counts them).
+ * consecutive steps were not skipped (good_steps counts them; a growth that
+ * would overflow fp32 is not taken).
  * gpt2_loss_scaler sets the whole state (also to restore it);
  * gpt2_loss_scaler_state reads it, with skipped = 1 iff the last step was
  * skipped.  Host only.
