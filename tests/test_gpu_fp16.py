@@ -131,3 +131,40 @@ def test_fp16_scale_grows_after_the_interval():
         assert skipped == 0 and (scale, good) == want
     assert st.step_count() == 5 and want == (4096.0, 1)
     st.close()
+
+
+def test_fp16_training_loop_lowers_the_loss(tmp_path):
+    """Twenty fp16 steps of a one-block GPT-2-width model through the training
+    loop (loader, schedule, accumulation, clip + AdamW with the scaler) on a
+    repeating two-window stream: the loss falls well below ln V, no step is
+    skipped at the default scale, and the step count and scale follow the
+    scaler's rule."""
+    import math
+
+    from gpt2_inputs import RunConfig
+    from gpt_decoder_pre_amd.train import Trainer
+    from tests.test_gpu_train import _shards
+    s = shape("gpt2-124m-L1", 1, 12, 768, 1024, 50257, 50304)
+    run = RunConfig("l1-fp16", s, 2, 1, 128, "fp16", "zipf", 6e-4)
+    say("fp16 training loop")
+    paths = _shards(tmp_path, 2 * run.tokens_per_step + 1, s.vocab_size, 11, kind="zipf", parts=1)
+    log = str(tmp_path / "log.csv")
+    tr = Trainer(run, paths, max_lr=3e-3, min_lr=3e-4, warmup=3, max_steps=20, log_path=log)
+    tr.step.loss_scaler(amp.INIT_SCALE, growth_interval=8)
+    tr.train(20)
+    scale, good, skipped = tr.step.loss_scaler_state()
+    t = tr.t
+    tr.close()
+    rows = [l.split(",") for l in open(log).read().splitlines()[1:]]
+    loss = [float(r[1]) for r in rows]
+    found = [not math.isfinite(float(r[3])) for r in rows]  # a skipped step reports a non-finite norm
+    want = (amp.INIT_SCALE, 0)
+    for f in found:
+        want = amp.scaler_update(*want, f, growth_interval=8)
+    say(f"  loss {loss[0]:.4f} -> {loss[-1]:.4f}; scale {scale}, good {good}, skipped {skipped}, t {t}, "
+        f"skipped steps {sum(found)}")
+    assert len(rows) == 20 and t == 20 - sum(found)
+    assert (scale, good) == want and skipped == int(found[-1])
+    assert sum(found) <= 2  # the default scale is workable for this model
+    assert abs(loss[0] - math.log(50304)) < 0.3
+    assert loss[-1] < loss[0] - 2.0
