@@ -168,3 +168,13 @@ def test_fp16_training_loop_lowers_the_loss(tmp_path):
     assert sum(found) <= 2  # the default scale is workable for this model
     assert abs(loss[0] - math.log(50304)) < 0.3
     assert loss[-1] < loss[0] - 2.0
+
+
+def test_fp16_xl_width():
+    # C = 1600 and NH = 25: partial GEMM tiles and a 25-head attention grid in fp16
+    _fp16_case(shape("gpt2-1558m-L1", 1, 25, 1600, 1024, 50257, 50304), 1, 256, 2)
+
+
+def test_fp16_untied_variant_gpt2_width():
+    from gpt2_inputs import ModelShape
+    _fp16_case(ModelShape("genesis-L1", 1, 12, 768, 1024, 50257, 50304, tied=False, qkv_bias=False), 2, 256, 2)
