@@ -99,14 +99,36 @@ def _seq_loss_grads_dx0(params, x, y, n_head, scale):
     return loss, g, cache["dx0"]
 
 
-def oracle_accumulate_per_sequence(params, x, y, n_head, workers=None, with_dx0=False):
+_SEQ_MEMO = {}
+
+
+def _digest(params, x, y, n_head):
+    import hashlib
+    h = hashlib.blake2b(digest_size=16)
+    for n in sorted(params):
+        h.update(n.encode())
+        h.update(np.ascontiguousarray(params[n]).tobytes())
+    h.update(np.ascontiguousarray(x).tobytes())
+    h.update(np.ascontiguousarray(y).tobytes())
+    h.update(str(n_head).encode())
+    return h.hexdigest()
+
+
+def oracle_accumulate_per_sequence(params, x, y, n_head, workers=None, with_dx0=False, memo=False):
     """The oracle's accumulation with every sequence of the (B, T) batch as its
     own micro-batch (loss scale 1/B): equal to the one batch of B sequences
     (the accumulation pin).  The sequences run on a thread pool (numpy
     releases the GIL inside its loops and BLAS calls) with single-threaded
     BLAS: concurrent calls into a multi-threaded OpenBLAS from several
     threads return corrupted products.  The sums are taken in sequence order.
-    Returns (mean loss, grads)."""
+    Returns (mean loss, grads).  With memo, the result is kept for the rest
+    of the session under a digest of (params, x, y, n_head), so two tests of
+    the same batch share one oracle run (the caller must not modify it)."""
+    if memo:
+        key = (_digest(params, x, y, n_head), with_dx0)
+        if key not in _SEQ_MEMO:
+            _SEQ_MEMO[key] = oracle_accumulate_per_sequence(params, x, y, n_head, workers, with_dx0)
+        return _SEQ_MEMO[key]
     import os
     from concurrent.futures import ThreadPoolExecutor
 

@@ -16,8 +16,9 @@ import pytest
 from gpt2_inputs import init_params
 from oracle import amp
 from oracle import gpt2 as ref
-from tests.gpu_helpers import batches_for, cos, gpu_step, host, per_tensor, rel, say, shape, to_dev, warm_state
-from tests.test_gpu_parity import _f32, _oracle_step, _run
+from tests.gpu_helpers import (batches_for, cos, gpu_step, host, oracle_accumulate_per_sequence, per_tensor, rel, say,
+                               shape, to_dev, warm_state)
+from tests.test_gpu_parity import BENCH_SITE_CONFIGS, _f32, _oracle_step, _run
 
 pytestmark = pytest.mark.gpu
 
@@ -178,3 +179,51 @@ def test_fp16_xl_width():
 def test_fp16_untied_variant_gpt2_width():
     from gpt2_inputs import ModelShape
     _fp16_case(ModelShape("genesis-L1", 1, 12, 768, 1024, 50257, 50304, tied=False, qkv_bias=False), 2, 256, 2)
+
+
+def test_fp16_bench_launch_shape_two_layers():
+    """The benchmarked launch shapes in fp16 (micro-batch 16 x 1024 tokens at
+    GPT-2 124M width, two layers, one micro-batch, the default scale 2^16):
+    every GEMM runs the benchmark's tile configuration, and the unscaled
+    gradients and the update from a warm state pass the fp16 gates per layer
+    and tensor against the oracle (accumulated sequence by sequence)."""
+    import torch
+    s = shape("gpt2-124m-L2", 2, 12, 768, 1024, 50257, 50304)
+    B, T, lr = 16, 1024, 6e-4
+    say(f"fp16 bench launch shape: L=2 C=768 B={B} T={T}")
+    p = init_params(s, 0)
+    batches = batches_for(s, B, T, 1, kind="zipf")
+    g = _run(s, "fp16", p, batches, warm=None, lr=lr, sites=True)
+    for site, want in BENCH_SITE_CONFIGS.items():
+        got = g["sites"][site]["gemm_cfg"]
+        assert got == want, (site, got, want)
+    x, y = batches[0]
+    loss_r, g_r, dx0 = oracle_accumulate_per_sequence(p, x, y, s.n_head, with_dx0=True, memo=True)
+    gdx0 = g["dx0"].reshape(B, T, -1)  # scaled by 2^16: the cosine does not see it
+    worst = min((cos(gdx0[b], dx0[b]), b) for b in range(B))
+    say(f"  dx0 worst sequence cosine {worst[0]:.6f} (sequence {worst[1]})")
+    assert worst[0] >= FP16_GRAD_COS
+    seen = np.zeros(s.padded_vocab_size, bool)
+    seen[np.unique(x)] = True
+    seen[np.unique(y)] = True
+    for name, rows in (("in batch", seen), ("not in batch (lm_head product only)", ~seen)):
+        c = cos(g["grads"]["wte"][rows], g_r["wte"][rows])
+        say(f"  wte rows {name}: cosine {c:.6f}")
+        assert c >= FP16_GRAD_COS, (name, c)
+    m0, v0 = warm_state(g_r)
+    # the update from the warm state, on the GPU's own (scaled) gradients
+    st = gpu_step(s, "fp16", B, p)
+    st.load_state(m0, v0, 10)
+    for n, a in st.to_dict(st.grads).items():
+        a.copy_(torch.as_tensor(g["grads"][n], dtype=torch.float32))
+    st.clip_adamw_step(lr, 0.9, 0.95, 1e-8, 0.1, 1.0)
+    torch.cuda.synchronize()
+    assert st.sync_status() == 0
+    assert st.loss_scaler_state() == (amp.INIT_SCALE, 1, 0)
+    g["params"] = host(st.to_dict(st.params))
+    g["norm"] = float(st.d_norm.item())
+    g["clipped"] = int(st.d_clipped.item())
+    st.close()
+    g["grads"] = {n: a / amp.INIT_SCALE for n, a in g["grads"].items()}
+    r = _oracle_step(p, None, s.n_head, m0, v0, 11, lr=lr, accumulated=(loss_r, g_r))
+    _gate_fp16(p, r, g)

@@ -315,7 +315,7 @@ def test_bf16_bench_launch_shape_two_layers():
         say(f"  {site}: config {got}")
         assert got == want, (site, got, want)
     x, y = batches[0]
-    loss_r, g_r, dx0 = oracle_accumulate_per_sequence(p, x, y, s.n_head, with_dx0=True)
+    loss_r, g_r, dx0 = oracle_accumulate_per_sequence(p, x, y, s.n_head, with_dx0=True, memo=True)
     # the gradient at the embedding output, per sequence, and the wte rows of
     # tokens in the batch (lm_head part + scatter) and not in it (lm_head only)
     gdx0 = g["dx0"].reshape(B, T, -1)
