@@ -362,20 +362,38 @@ DEVI void gemm_epilogue(const GemmArgs& p, f32x16 (&acc)[FM][FN], h16* region, i
     constexpr int ITB = RB * CPR / 64;  // 16-byte chunks per lane for one pass
     static_assert(RB % 32 == 0 && WTM % RB == 0, "whole 32-row blocks per pass");
     static_assert(WTN / 2 <= 64, "one column pair per lane for the column sums");
+    // The 16-byte chunk it * 64 + lane of a pass is row q / CPR, chunk q % CPR
+    // of the staged rows.  That pattern repeats every PER iterations, RPP rows
+    // further down, so the divisions are taken once for the first PER
+    // iterations and the rest add a constant row step: RPP rows of the
+    // staging region (an immediate) and of the output (one 32-bit add).
+    constexpr int G = (CPR & -CPR) < 64 ? (CPR & -CPR) : 64;  // gcd(64, CPR): CPR's power-of-two part
+    constexpr int PER = CPR / G, RPP = 64 / G;
+    static_assert(ITB % PER == 0 && RB % RPP == 0, "whole periods per pass");
+    int rb[PER], cb[PER];
+    uint32_t ob[PER];  // element offset of chunk b from the pass's first output element
+#pragma unroll
+    for (int b = 0; b < PER; ++b) {
+      rb[b] = (b * 64 + lane) / CPR;
+      cb[b] = (b * 64 + lane) % CPR;
+      ob[b] = (uint32_t)rb[b] * (uint32_t)p.ldc + 8u * (uint32_t)cb[b];
+    }
+    const uint32_t ostep = (uint32_t)RPP * (uint32_t)p.ldc;  // RPP output rows, wave-uniform
+    auto row_of = [&](int it) { return (it / PER) * RPP + rb[it % PER]; };
+    auto chunk_of = [&](int it) { return cb[it % PER]; };
+    auto goff = [&](int it) { return ob[it % PER] + (uint32_t)(it / PER) * ostep; };
     float cs0 = 0.f, cs1 = 0.f;  // GELU', 32-row passes: this lane's column pair, current 64-row chunk
 #pragma unroll
     for (int pb = 0; pb < WTM / RB; ++pb) {
       const int mi = mb + RB * pb;
       if constexpr (EPI == EPI_GELU_BWD) {
         // the gelu'(u) rows come in whole row segments too
-        const h16* aux = reinterpret_cast<const h16*>(p.aux);
+        const h16* aux = reinterpret_cast<const h16*>(p.aux) + (mi * p.ldc + nb);
 #pragma unroll
         for (int it = 0; it < ITB; ++it) {
-          const int q = it * 64 + lane;
-          const int r = q / CPR, c = q % CPR;
-          const int m = mi + r, n = nb + 8 * c;
+          const int r = row_of(it), c = chunk_of(it);
           *reinterpret_cast<u32x4*>(region + r * SLD + 8 * c) =
-              aux_pre ? aux_pre[pb * ITB + it] : ld16_or_zero(aux + (int64_t)m * p.ldc + n, m < p.M && n < p.N);
+              aux_pre ? aux_pre[pb * ITB + it] : ld16_or_zero(aux + goff(it), mi + r < p.M && nb + 8 * c < p.N);
           if (it % 8 == 7) __builtin_amdgcn_sched_barrier(0);  // bounded loads in flight
         }
         __builtin_amdgcn_s_waitcnt(0xc07f);
@@ -428,15 +446,12 @@ DEVI void gemm_epilogue(const GemmArgs& p, f32x16 (&acc)[FM][FN], h16* region, i
         }
         __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's LDS writes are done
         __builtin_amdgcn_wave_barrier();
-        h16* out = reinterpret_cast<h16*>(o == 0 ? p.C : p.C2);
+        h16* out = reinterpret_cast<h16*>(o == 0 ? p.C : p.C2) + (mi * p.ldc + nb);
 #pragma unroll
         for (int it = 0; it < ITB; ++it) {
-          const int q = it * 64 + lane;
-          const int r = q / CPR, c = q % CPR;
-          const int m = mi + r, n = nb + 8 * c;
-          if (m < p.M && n < p.N)
-            *reinterpret_cast<u32x4*>(out + (int64_t)m * p.ldc + n) =
-                *reinterpret_cast<const u32x4*>(region + r * SLD + 8 * c);
+          const int r = row_of(it), c = chunk_of(it);
+          if (mi + r < p.M && nb + 8 * c < p.N)
+            *reinterpret_cast<u32x4*>(out + goff(it)) = *reinterpret_cast<const u32x4*>(region + r * SLD + 8 * c);
         }
         if constexpr (EPI == EPI_GELU_BWD && WTM % 64 == 0) {
           // column sums of the staged (bf16) rows per 64-row chunk: the bias
@@ -1403,6 +1418,9 @@ bool gemm_config_usable(int cfg, GemmLayout layout, const GemmArgs& a) {
     // gives each tile the same number of k-steps)
     if (a.K % kCfgBK[cfg] || a.k_per_split % kCfgBK[cfg]) return false;
     if (a.splits > 1 && a.K != a.splits * a.k_per_split) return false;
+    // the staged epilogue addresses a pass of at most 256 output rows with
+    // 32-bit element offsets
+    if (a.ldc >= (int64_t(1) << 24)) return false;
   }
   return true;
 }
