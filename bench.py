@@ -50,6 +50,9 @@ def parse():
                          "sequence per step with top-k / top-p sampling) and print its own JSON line")
     ap.add_argument("--prompt", type=int, default=128, help="prompt length for --decode")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--hbm-ceiling", action="store_true",
+                    help="instead of the training step, time plain HBM streams (read only, write only, copy, "
+                         "add) of 1 GiB fp32 buffers with PyTorch's own kernels and print their rates")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run a plain 1 GiB device-to-device copy (scale reference for HBM byte counters)")
     return ap.parse_args()
@@ -203,8 +206,68 @@ def decode_bench(args):
     print(json.dumps(out), flush=True)
 
 
+def hbm_ceiling_bench(args):
+    """What this part sustains for plain streams, as a reference for the
+    HBM-bound kernels of the step: the library's stream probes (read only,
+    write only, copy) and PyTorch's own reduction, fill, copy and add kernels
+    over 1 GiB fp32 buffers (4x the last-level cache), each timed with HIP
+    events on torch's stream over `steps` back-to-back calls after `warmup`
+    untimed ones.  Rates are the bytes each op must move (read + written)
+    over its time."""
+    import torch
+
+    from gpt_decoder_pre_amd import lib as L
+    dev = torch.device("cuda:0")
+    n = 1 << 28  # 1 GiB of fp32
+    g = torch.Generator(device=dev).manual_seed(3)
+    x = torch.rand(n, generator=g, device=dev)
+    x2 = torch.rand(n, generator=g, device=dev)
+    y = torch.empty_like(x)
+    acc = torch.empty((), device=dev)
+    part = torch.empty(L.probe_partials(n), device=dev)
+    nb = 4 * n
+    ops = [("probe: read only", lambda: L.stream_probe(L.PROBE_READ, x, part), nb),
+           ("probe: write only", lambda: L.stream_probe(L.PROBE_WRITE, None, y), nb),
+           ("probe: copy", lambda: L.stream_probe(L.PROBE_COPY, x, y), 2 * nb),
+           ("torch: read only (sum)", lambda: torch.sum(x, dim=0, out=acc), nb),
+           ("torch: write only (fill)", lambda: y.fill_(0.5), nb),
+           ("torch: copy (one read, one write)", lambda: y.copy_(x), 2 * nb),
+           ("torch: add (two reads, one write)", lambda: torch.add(x, x2, out=y), 3 * nb)]
+    steps, warm = max(args.steps, 10), max(args.warmup, 3)
+    rows = []
+    for name, fn, byt in ops:
+        for _ in range(warm):
+            fn()
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0.record()
+        for _ in range(steps):
+            fn()
+        t1.record()
+        torch.cuda.synchronize()
+        us = t0.elapsed_time(t1) * 1e3 / steps
+        if name == "probe: read only":  # the partial sums add up to the buffer's sum
+            want = float(torch.sum(x.double()))
+            got = float(torch.sum(part.double()))
+            if abs(got - want) > 1e-3 * abs(want):
+                raise RuntimeError(f"read probe sum {got} != {want}")
+        if name == "probe: write only" and not bool((y == 0.5).all()):
+            raise RuntimeError("write probe result")
+        if name == "probe: copy" and not torch.equal(y, x):
+            raise RuntimeError("copy probe result")
+        gbs = byt / (us * 1e-6) / 1e9
+        rows.append({"stream": name, "bytes": byt, "us": round(us, 1), "GB/s": round(gbs, 1),
+                     "frac": round(gbs / PEAK_HBM_GBS, 4)})
+    if not torch.equal(y, x + x2):
+        raise RuntimeError("add stream result")
+    print(json.dumps({"metric": "HBM stream rates of plain kernels (1 GiB fp32 buffers)", "unit": "GB/s",
+                      "peak": PEAK_HBM_GBS, "steps": steps, "warmup": warm, "rows": rows}), flush=True)
+
+
 def main():
     args = parse()
+    if args.hbm_ceiling:
+        hbm_ceiling_bench(args)
+        return
     if args.decode:
         if args.gpus != 1:
             print("bench.py runs on one GPU only", file=sys.stderr)

@@ -22,7 +22,7 @@ LIB_PATH = os.path.join(LIB_DIR, "libgpt2.so")
 
 ARCH = "gfx950"
 SOURCES = ["gemm.hip", "attention.hip", "layernorm.hip", "embed.hip", "xent.hip", "optim.hip", "infer.hip",
-           "gpt2.cpp", "train.cpp", "infer_ctx.cpp"]
+           "gpt2.cpp", "train.cpp", "infer_ctx.cpp", "probe.hip"]
 # The sources of the training step are built a second time for the fp16 mode:
 # IEEE half as the 16-bit operand type, in namespace gpt2k_f16, with the C ABI
 # entry points prefixed f16_ (the library's own entry points hand fp16

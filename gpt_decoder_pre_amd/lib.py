@@ -44,7 +44,7 @@ EXPORTS = ("gpt2_init", "gpt2_forward_loss", "gpt2_backward", "gpt2_accumulate",
            "gpt2_lr_at", "gpt2_loader_open", "gpt2_loader_next", "gpt2_loader_next_host", "gpt2_loader_state",
            "gpt2_loader_seek", "gpt2_loader_close", "gpt2_checkpoint_save", "gpt2_checkpoint_load",
            "gpt2_infer_init", "gpt2_infer_prefill", "gpt2_infer_decode", "gpt2_infer_length", "gpt2_sample",
-           "gpt2_infer_sync_status", "gpt2_infer_destroy")
+           "gpt2_infer_sync_status", "gpt2_infer_destroy", "gpt2_stream_probe")
 
 
 class Gpt2Error(RuntimeError):
@@ -135,6 +135,7 @@ def load_library() -> ctypes.CDLL:
         "gpt2_sample": (I, [P, I64, I, I, F, I, F, P, P, P]),
         "gpt2_infer_sync_status": (I, [P]),
         "gpt2_infer_destroy": (None, [P]),
+        "gpt2_stream_probe": (I, [I, P, P, I64, P]),
         "gpt2_timing_site": (I, [P, I, ctypes.POINTER(ctypes.c_char_p), ctypes.POINTER(ctypes.c_double),
                                  ctypes.POINTER(I64), ctypes.POINTER(ctypes.c_double),
                                  ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int32)]),
@@ -558,3 +559,34 @@ def sample(logits, uniform, vocab_size, temperature=1.0, top_k=0, top_p=1.0, str
                            ctypes.c_void_p(uniform.data_ptr()), ctypes.c_void_p(out.data_ptr()),
                            ctypes.c_void_p(st.cuda_stream)), "gpt2_sample")
     return out
+
+
+# gpt2_stream_probe modes
+PROBE_READ, PROBE_WRITE, PROBE_COPY = 0, 1, 2
+
+
+def probe_partials(n: int) -> int:
+    """Floats the read probe writes for n input floats (one per wave of 64
+    threads, eight 16-byte loads each)."""
+    return 4 * ((n + 8191) // 8192)
+
+
+def stream_probe(mode, src, dst, stream=None):
+    """gpt2_stream_probe: one launch of a plain HBM stream over fp32 device
+    tensors (src unused for PROBE_WRITE; for PROBE_READ, dst receives the
+    per-wave partial sums and must hold probe_partials(n) floats)."""
+    import torch
+    lib = load_library()
+    n = (src if mode != PROBE_WRITE else dst).numel()
+    for t in (src, dst):
+        if t is not None and (t.dtype != torch.float32 or not t.is_contiguous() or not t.is_cuda):
+            raise ValueError("stream_probe: contiguous fp32 device tensors")
+    if mode == PROBE_READ and dst.numel() < probe_partials(n):
+        raise ValueError(f"stream_probe: the read probe writes {probe_partials(n)} partial sums")
+    if mode == PROBE_COPY and dst.numel() < n:
+        raise ValueError("stream_probe: dst smaller than src")
+    dev = dst.device
+    st = stream if stream is not None else torch.cuda.current_stream(dev)
+    _check(lib.gpt2_stream_probe(mode, ctypes.c_void_p(src.data_ptr() if src is not None else 0),
+                                 ctypes.c_void_p(dst.data_ptr()), n, ctypes.c_void_p(st.cuda_stream)),
+           "gpt2_stream_probe")

@@ -305,6 +305,20 @@ int gpt2_timing_read(gpt2_ctx *ctx, double *total_ms, int64_t *launches,
 int gpt2_timing_site(gpt2_ctx *ctx, int index, const char **site, double *total_ms,
                      int64_t *launches, double *flops, double *bytes, int32_t *gemm_cfg);
 
+/* HBM stream probe: one launch of a plain fp32 stream on `stream` (NULL: the
+   default stream), the reference rate that the HBM-bound kernels of the step
+   are measured against; not a step of the method.  Each workgroup streams
+   one contiguous range once.  mode 0 reads n floats of d_src (eight 16-byte
+   loads in flight per thread) and writes one partial sum per wave to d_dst,
+   which must hold at least 4 ceil(n / 8192) floats (their total is the sum
+   of the n floats); mode 1
+   writes 0.5 to n floats of d_dst (d_src unused, may be NULL); mode 2 copies
+   n floats from d_src to d_dst.  Device pointers, 16-byte aligned, the
+   caller's memory; n > 0 and a multiple of 4.  Asynchronous.
+   Errors: GPT2_ERR_ARG for a bad mode, size, NULL or misaligned pointer;
+   GPT2_ERR_HIP if the launch fails. */
+int gpt2_stream_probe(int mode, const float *d_src, float *d_dst, int64_t n, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

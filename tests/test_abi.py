@@ -129,3 +129,13 @@ def test_fp16_mode_sizes_and_refusals(lib):
     f, i = ctypes.c_float(), ctypes.c_int32()
     assert lib.gpt2_loss_scaler(None, 1.0, 2.0, 0.5, 10, 0) == L.GPT2_ERR_STATE
     assert lib.gpt2_loss_scaler_state(None, ctypes.byref(f), ctypes.byref(i), ctypes.byref(i)) == L.GPT2_ERR_ARG
+
+
+def test_stream_probe_refuses_bad_arguments_before_any_launch(lib):
+    # every case below is refused by the argument checks, before a HIP call
+    assert lib.gpt2_stream_probe(3, None, None, 4, None) == L.GPT2_ERR_ARG            # no such mode
+    assert lib.gpt2_stream_probe(0, None, ctypes.c_void_p(256), 4, None) == L.GPT2_ERR_ARG  # read without src
+    assert lib.gpt2_stream_probe(1, None, None, 4, None) == L.GPT2_ERR_ARG            # write without dst
+    assert lib.gpt2_stream_probe(2, ctypes.c_void_p(256), ctypes.c_void_p(264), 4, None) == L.GPT2_ERR_ARG  # misaligned
+    assert lib.gpt2_stream_probe(1, None, ctypes.c_void_p(256), 6, None) == L.GPT2_ERR_ARG  # n % 4
+    assert lib.gpt2_stream_probe(1, None, ctypes.c_void_p(256), 0, None) == L.GPT2_ERR_ARG  # empty
