@@ -756,6 +756,9 @@ DEVI void w4_tiles(const GemmArgs& p, h16* smem, Next next) {
   constexpr int WTM = BM / (NW / 2), WTN = BN / 2;  // NW / 2 x 2 waves
   static_assert(NW == 4 || NW == 8, "four or eight waves");
   static_assert(WTM % 32 == 0 && WTN % 32 == 0, "whole 32 x 32 accumulator blocks");
+  // 64-row tiles (one accumulator row block per wave) computed a wrong step
+  // in the residual epilogue and are not supported
+  static_assert(BM >= 128, "tiles of at least 128 rows");
   constexpr int FM = WTM / 32, FN = WTN / 32;
   constexpr int STAGE = (BM + BN) * BK;  // elements
   constexpr int SLD = WTN + 8;           // staged epilogue row stride
