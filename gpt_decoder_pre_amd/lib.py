@@ -577,6 +577,8 @@ def stream_probe(mode, src, dst, stream=None):
     per-wave partial sums and must hold probe_partials(n) floats)."""
     import torch
     lib = load_library()
+    if mode not in (PROBE_READ, PROBE_WRITE, PROBE_COPY) or dst is None or (mode != PROBE_WRITE and src is None):
+        raise ValueError("stream_probe: mode PROBE_READ / PROBE_WRITE / PROBE_COPY, dst, and src unless writing")
     n = (src if mode != PROBE_WRITE else dst).numel()
     for t in (src, dst):
         if t is not None and (t.dtype != torch.float32 or not t.is_contiguous() or not t.is_cuda):
