@@ -805,7 +805,7 @@ int GPT2_API(gpt2_clip_adamw_step)(gpt2_ctx* c, float lr, float beta1, float bet
   c->step += 1;
   clip_adamw_launch(c, c->buf, c->n_params, decay_segments(c->t, c->n_params), c->step, c->norm_part, c->clip_scale,
                     lr, beta1, beta2, eps, weight_decay, max_norm, d_norm, d_clipped, c->stream);
-  if (c->amp) {  // the scale update needs the device's verdict on this step
+  if (c->amp) {  // the scale update needs the device's overflow flag of this step
     int32_t found = 0;
     if (hipMemcpyAsync(&found, c->amp_found, sizeof(found), hipMemcpyDeviceToHost, c->stream) != hipSuccess ||
         hipStreamSynchronize(c->stream) != hipSuccess)

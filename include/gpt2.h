@@ -189,7 +189,7 @@ int gpt2_accumulate(gpt2_ctx *ctx, const int32_t *d_idx, const int32_t *d_target
  * uses g / S.  If n is not finite the step is skipped: params, moments, the
  * fp16 copy and t are left as they were.  Then S is updated as
  * gpt2_loss_scaler describes.  The call waits for the stream (the scale
- * update needs the step's verdict).
+ * update needs the step's overflow flag).
  * Errors: GPT2_ERR_ARG for NULL pointers.
  */
 int gpt2_clip_adamw_step(gpt2_ctx *ctx, float lr, float beta1, float beta2, float eps,
